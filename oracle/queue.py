@@ -1,0 +1,228 @@
+"""Host tile-instruction queue builder, re-implemented from the written queue rules.
+
+Follows the lowering described on the MegaRTP page, section 4 ("OpGraph -> per-op
+tile expansion -> TaskGraph -> KernelPlan -> instruction tensor + event counters +
+operand pointer table"):
+
+* each op expands into tile tasks (row tiles for norms, output-row tiles for the
+  skinny projections, (request, kv head, KV split) tiles for attention);
+* a (producer op, consumer op) pair turns into events: a counter plus a threshold
+  equal to the number of producer tasks writing (or reducing into) the region the
+  consumer reads ("whole", "tile_cover", "tile_reduce");
+* tasks are numbered in topological order and dealt round-robin onto the worker
+  queues, which are padded with NoOp to a common length [W, L, 32];
+* each instruction is 32 uint32 words: opcode, wait count, signal count, operand
+  row, spec id, task id, four (event, threshold) waits, two (event, increment,
+  publication id) signals, then the tile payload.
+
+Deadlock freedom (handbook, megakernel section and its exercise 3): every wait
+names an event whose producers all have smaller task ids, and all workers are
+co-resident, so the smallest unfinished task can always run.
+
+Reductions whose result a consumer reads once (the split-KV combine, the global
+argmax) use an arrival group instead of an extra wave of finalize tasks: each
+producer records its arrival; the one that completes the group finalises and then
+issues the instruction's signals.  The arrival group id, its size and the
+producer's rank in it are part of the payload.
+"""
+from __future__ import annotations
+
+from typing import Dict, List
+
+import numpy as np
+
+OP_NOOP, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = 0, 1, 2, 3, 4, 5, 6
+NONE = 0xFFFFFFFF
+LEASE_BYTES = 65536  # largest LDS lease of one instruction
+
+
+def _pow2floor(x: int) -> int:
+    p = 1
+    while p * 2 <= x:
+        p *= 2
+    return p
+
+
+def _pow2ceil(x: int) -> int:
+    p = 1
+    while p < x:
+        p *= 2
+    return p
+
+
+def _largest_divisor_le(n: int, cap: int) -> int:
+    cap = max(1, min(n, cap))
+    for r in range(cap, 0, -1):
+        if n % r == 0:
+            return r
+    return 1
+
+
+def tile_params(cfg, W: int, ctx_lens) -> Dict[str, int]:
+    H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
+    Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
+    R = cfg.n_requests
+    elem = 1 if cfg.weight_fp8 else 2
+    n_qkv = (Hq + 2 * Hkv) * d
+
+    def cap_rows(k: int, nmat: int) -> int:
+        return max(1, LEASE_BYTES // (k * elem * nmat))
+
+    p = {}
+    p["r_qkv"] = _pow2floor(min(d, max(1, n_qkv // W), cap_rows(H, 1)))
+    p["r_o"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(Hq * d, 1)))
+    p["r_gu"] = _largest_divisor_le(I, min(max(1, I // W), cap_rows(H, 2)))
+    p["r_down"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(I, 1)))
+    p["r_lm"] = min(cfg.vocab, cap_rows(H, 1)) if cfg.workload == "qwen3_step" else 0
+    ctx_max = int(max(ctx_lens))
+    want = -(-(R * ctx_max * Hkv) // W)
+    p["s_tok"] = max(4, min(LEASE_BYTES // (4 * d), _pow2ceil(max(1, want))))
+    p["spec"] = 0 if cfg.m == 1 else 1
+    return p
+
+
+class _Builder:
+    def __init__(self):
+        self.tasks: List[np.ndarray] = []
+        self.thresholds: List[int] = []
+        self.n_arrivals = 0
+        self.n_ops = 0
+
+    def event(self, threshold: int) -> int:
+        self.thresholds.append(int(threshold))
+        return len(self.thresholds) - 1
+
+    def arrival_group(self) -> int:
+        self.n_arrivals += 1
+        return self.n_arrivals - 1
+
+    def op_row(self) -> int:
+        self.n_ops += 1
+        return self.n_ops - 1
+
+    def task(self, opcode, op_row, spec, waits, signals, payload) -> int:
+        tid = len(self.tasks)
+        w = np.zeros(32, dtype=np.uint32)
+        w[0], w[1], w[2], w[3], w[4], w[5] = opcode, len(waits), len(signals), op_row, spec, tid
+        assert len(waits) <= 4 and len(signals) <= 2 and len(payload) <= 12
+        for i, (e, t) in enumerate(waits):
+            w[6 + 2 * i], w[7 + 2 * i] = e, t
+        for i, (e, inc) in enumerate(signals):
+            w[14 + 3 * i], w[15 + 3 * i], w[16 + 3 * i] = e, inc, tid
+        for i, v in enumerate(payload):
+            w[20 + i] = np.uint32(v & 0xFFFFFFFF)
+        self.tasks.append(w)
+        return tid
+
+
+def _qwen3(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
+    H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
+    Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
+    g = Hq // Hkv
+    R = cfg.n_requests
+    spec = p["spec"]
+    n_qkv = (Hq + 2 * Hkv) * d
+    rq, ro, rgu, rd, st = p["r_qkv"], p["r_o"], p["r_gu"], p["r_down"], p["s_tok"]
+    n_qkv_t, n_o_t, n_gu_t, n_d_t = n_qkv // rq, H // ro, I // rgu, H // rd
+    prev_down = None
+    for l in range(cfg.num_layers):
+        row_qkv, row_attn, row_o, row_gu, row_d = (b.op_row() for _ in range(5))
+        ev_qkv = [b.event((g + 2) * d // rq) for _ in range(Hkv)]
+        ev_oready = b.event(R * Hkv)
+        ev_o = b.event(n_o_t)
+        ev_gu = b.event(n_gu_t)
+        ev_down = b.event(n_d_t)
+        # QKV row tiles; a tile lies inside one head, whose kv group is its event
+        for j in range(n_qkv_t):
+            n0 = j * rq
+            if n0 < Hq * d:
+                grp = (n0 // d) // g
+            elif n0 < (Hq + Hkv) * d:
+                grp = (n0 - Hq * d) // d
+            else:
+                grp = (n0 - (Hq + Hkv) * d) // d
+            waits = [] if prev_down is None else [(prev_down, n_d_t)]
+            b.task(OP_QKV, row_qkv, spec, waits, [(ev_qkv[grp], 1)], [l, n0, rq, 0, H])
+        # split-KV attention tiles: (request, kv head, split); arrival group per (request, kv head)
+        for r in range(R):
+            ctx = int(ctx_lens[r])
+            ns = -(-ctx // st)
+            for hk in range(Hkv):
+                grp = b.arrival_group()
+                for s in range(ns):
+                    t0, t1 = s * st, min(ctx, (s + 1) * st)
+                    b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk], (g + 2) * d // rq)], [(ev_oready, 1)],
+                           [l, r, hk, s, t0, t1, grp, ns, s])
+        for j in range(n_o_t):
+            b.task(OP_OPROJ, row_o, spec, [(ev_oready, R * Hkv)], [(ev_o, 1)], [l, j * ro, ro, 0, Hq * d])
+        for j in range(n_gu_t):
+            b.task(OP_GATEUP, row_gu, spec, [(ev_o, n_o_t)], [(ev_gu, 1)], [l, j * rgu, rgu, 0, H])
+        for j in range(n_d_t):
+            b.task(OP_DOWN, row_d, spec, [(ev_gu, n_gu_t)], [(ev_down, 1)], [l, j * rd, rd, 0, I])
+        prev_down = ev_down
+    if cfg.workload == "qwen3_step":
+        row_lm = b.op_row()
+        rl = p["r_lm"]
+        n_lm = -(-cfg.vocab // rl)
+        grp = b.arrival_group()
+        for j in range(n_lm):
+            n0 = j * rl
+            b.task(OP_LMHEAD, row_lm, spec, [(prev_down, n_d_t)], [],
+                   [cfg.num_layers, n0, min(rl, cfg.vocab - n0), 0, H, 0, grp, n_lm, j])
+
+
+def build_queue(cfg, W: int, ctx_lens=None) -> Dict[str, np.ndarray]:
+    """Returns {'queue': uint32 [W, L, 32], 'thresholds': uint32 [E], 'n_tasks', 'n_ops',
+    'n_arrivals', 'params'}."""
+    if ctx_lens is None:
+        ctx_lens = [cfg.context] * cfg.n_requests
+    b = _Builder()
+    p = tile_params(cfg, W, ctx_lens)
+    if cfg.workload in ("qwen3_layer", "qwen3_step"):
+        _qwen3(cfg, W, ctx_lens, b, p)
+    else:
+        raise NotImplementedError(cfg.workload)
+    T = len(b.tasks)
+    L = -(-T // W)
+    q = np.zeros((W, L, 32), dtype=np.uint32)
+    for tid, words in enumerate(b.tasks):
+        q[tid % W, tid // W] = words
+    return {"queue": q, "thresholds": np.array(b.thresholds, dtype=np.uint32), "n_tasks": T,
+            "n_ops": b.n_ops, "n_arrivals": b.n_arrivals, "params": p}
+
+
+def check_invariants(plan) -> None:
+    """Every task appears once; waits name events whose producers all precede the waiter;
+    each event's threshold equals the increments its producers issue per run."""
+    q = plan["queue"]
+    W, L, _ = q.shape
+    thr = plan["thresholds"]
+    produced = np.zeros(len(thr), dtype=np.int64)
+    last_producer = np.full(len(thr), -1, dtype=np.int64)
+    tasks = {}
+    for w in range(W):
+        for i in range(L):
+            words = q[w, i]
+            if words[0] == OP_NOOP:
+                assert not words.any()
+                continue
+            tid = int(words[5])
+            assert tid not in tasks and tid % W == w and tid // W == i
+            tasks[tid] = words
+    assert sorted(tasks) == list(range(plan["n_tasks"]))
+    for tid in range(plan["n_tasks"]):
+        words = tasks[tid]
+        for k in range(int(words[1])):
+            e, t = int(words[6 + 2 * k]), int(words[7 + 2 * k])
+            assert t == thr[e] and last_producer[e] < tid
+        for k in range(int(words[2])):
+            e, inc = int(words[14 + 3 * k]), int(words[15 + 3 * k])
+            arrival_total = int(words[27])
+            # a finalised signal is issued once per arrival group, by its last producer
+            if arrival_total:
+                if int(words[28]) == arrival_total - 1:
+                    produced[e] += inc
+            else:
+                produced[e] += inc
+            last_producer[e] = tid
+    assert np.array_equal(produced, thr.astype(np.int64)), "threshold != increments"
