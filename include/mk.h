@@ -1,0 +1,151 @@
+/*
+ * mk.h -- C ABI of the persistent tile-instruction decode megakernel for MI355X (gfx950).
+ *
+ * The library lowers a decode workload into tile instructions, queues them per worker and
+ * runs them either inside one persistent kernel (one worker block per compute unit) or as
+ * one standalone kernel per op inside a hipGraph.  This follows the MegaRTP page
+ * ("Kernel-Mega-PDL", section 4): a host-built instruction tensor, event counters with
+ * thresholds, and an operand pointer table that keeps addresses out of the instructions,
+ * so that new tensor addresses only rebind the table.
+ *
+ * Conventions
+ *   - Every entry point returns mk_status; nothing throws across the ABI.  On failure
+ *     mk_last_error() returns a thread-local message.
+ *   - Device pointers are plain addresses of caller-owned device memory (allocated by the
+ *     caller, e.g. through PyTorch).  Host pointers are marked host_.  The library owns the
+ *     plan and everything it allocates (device queue, counters, pointer tables, RoPE table,
+ *     captured graphs); mk_plan_destroy frees them.
+ *   - Work is enqueued on the caller's HIP stream (hipStream_t passed as void*); the graph
+ *     baseline forks internal streams from it with events and joins back.
+ *   - Layouts are row-major.  Weight matrices are [N, K] with K contiguous, stacked on a
+ *     leading layer axis for multi-layer workloads.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MK_OK = 0,
+  MK_ERR_INVALID = -1,     /* bad argument, shape or alignment: nothing was launched */
+  MK_ERR_UNSUPPORTED = -2, /* valid but not built in this library (e.g. workload variant) */
+  MK_ERR_HIP = -3,         /* a HIP runtime call failed */
+  MK_ERR_NOMEM = -4,       /* library-side allocation failed */
+  MK_ERR_TIMEOUT = -5      /* device watchdog: a counter wait did not complete */
+} mk_status;
+
+typedef enum {
+  MK_QWEN3_LAYER = 0,   /* one Qwen3-shaped decode layer, returns (y, r2) */
+  MK_QWEN3_STEP = 1,    /* num_layers chained layers + final RMSNorm + lm_head + greedy argmax */
+  MK_INDEXER_FRONT = 2  /* A0 -> {B0, C0, B1} -> D1 -> E1 indexer front (MegaRTP page, section 4) */
+} mk_workload;
+
+enum {
+  MK_FLAG_NO_PREFETCH = 1u << 0, /* megakernel: no weight prefetch across instructions (ablation) */
+  MK_FLAG_NOOP_ONLY = 1u << 1,   /* megakernel: run the queue shape with every op body skipped */
+  MK_FLAG_TRACE = 1u << 2        /* megakernel: record per-instruction timestamps */
+};
+
+/* Plain data, caller-owned, copied by mk_build_queue. */
+typedef struct {
+  int32_t workload;            /* mk_workload */
+  int32_t weight_fp8, act_fp8; /* FP8 e4m3 weights with 128x128 fp32 block scales / FP8 activations */
+  int32_t hidden, inter, n_q_heads, n_kv_heads, head_dim, num_layers, vocab;
+  int32_t n_requests, tokens_per_request; /* M = n_requests * tokens_per_request rows */
+  int32_t page_size, max_pages_per_req, num_phys_pages;
+  int32_t idx_q_rank, idx_heads, idx_head_dim;
+  float rms_eps, rope_theta;
+  int32_t num_workers; /* 0 => one worker per compute unit of the current device */
+  uint32_t flags;      /* MK_FLAG_* */
+} mk_config;
+
+/* Device addresses in a fixed order per workload (MK_T_* below); n = number used. */
+#define MK_MAX_TENSORS 32
+typedef struct {
+  uint64_t ptr[MK_MAX_TENSORS];
+  int32_t n;
+} mk_tensors;
+
+/* Tensor order for MK_QWEN3_LAYER / MK_QWEN3_STEP (L = num_layers, M rows, d = head_dim):
+ *   W_QKV   [L, (Hq+2Hkv)d, H] bf16      W_O     [L, H, Hq d] bf16
+ *   W_GU    [L, 2I, H] bf16 (rows [0,I) gate, [I,2I) up)     W_DOWN [L, H, I] bf16
+ *   G_ATTN, G_MLP [L, H] bf16;  G_Q, G_K [L, d] bf16  (RMSNorm gains)
+ *   K_CACHE, V_CACHE [L, pages, P, Hkv, d] bf16 (updated in place at slot ctx-1 of each request)
+ *   BLOCK_TABLE [R, max_pages_per_req] int32;  CONTEXT_LENS [R] int32 (include the new token)
+ *   X [M, H] bf16;  R_IN [M, H] fp32 (residual stream)
+ *   Y_OUT [M, H] bf16;  R2_OUT [M, H] fp32       (layer workload outputs; for the step: last layer)
+ *   WORKSPACE  mk_plan_workspace_bytes() bytes, 256-byte aligned, contents need not be preserved
+ *   step only: G_FINAL [H] bf16; W_LM [V, H] bf16; LOGITS_OUT [M, V] fp32; TOKEN_OUT [M] int32 */
+enum {
+  MK_T_W_QKV = 0, MK_T_W_O, MK_T_W_GU, MK_T_W_DOWN,
+  MK_T_G_ATTN, MK_T_G_MLP, MK_T_G_Q, MK_T_G_K,
+  MK_T_K_CACHE, MK_T_V_CACHE, MK_T_BLOCK_TABLE, MK_T_CONTEXT_LENS,
+  MK_T_X, MK_T_R_IN, MK_T_Y_OUT, MK_T_R2_OUT, MK_T_WORKSPACE,
+  MK_T_G_FINAL, MK_T_W_LM, MK_T_LOGITS_OUT, MK_T_TOKEN_OUT,
+  MK_T_COUNT_QWEN3
+};
+
+typedef struct mk_plan mk_plan; /* opaque, library-owned */
+
+/* Lower a workload into tile tasks, events and per-worker queues, and upload the queue,
+ * zeroed counters and tables to the current device.  host_context_lens: n_requests
+ * entries (context length per request including the new token).  The plan fixes tile
+ * counts and thresholds, so a new plan is needed only when shapes, context lengths or the
+ * worker count change (MegaRTP page, section 4: "only M/KV changes need a new plan").
+ * Without a HIP device the plan is built on the host only (num_workers must then be > 0):
+ * its queue, events and info can be read, and the run entry points return MK_ERR_INVALID.
+ * Errors: MK_ERR_INVALID for inconsistent shapes; MK_ERR_UNSUPPORTED for variants not built. */
+mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens, mk_plan** out);
+
+/* Host view of the queue: uint32 [W, L, 32], 32 words per instruction:
+ *   w0 opcode, w1 wait count, w2 signal count, w3 operand row, w4 spec id, w5 task id,
+ *   w6..w13 four (event id, threshold) waits, w14..w19 two (event id, increment,
+ *   publication id) signals, w20..w31 payload (layer, tile coordinates, arrival group id,
+ *   arrival group size, rank in group).  Padding slots are NoOp (32 zero words).
+ * The pointer stays valid until mk_plan_destroy. */
+mk_status mk_plan_queue(const mk_plan* plan, const uint32_t** host_instr, int32_t* W, int32_t* L);
+
+/* Event thresholds: uint32 [num_events]; each equals the increments its producers issue per run. */
+mk_status mk_plan_events(const mk_plan* plan, const uint32_t** host_thresholds, int32_t* num_events);
+
+/* Plan facts: n_tasks, n_ops (rows of the operand pointer table), n_arrivals. */
+mk_status mk_plan_info(const mk_plan* plan, int32_t* n_tasks, int32_t* n_ops, int32_t* n_arrivals);
+
+/* Bytes of scratch the caller passes as MK_T_WORKSPACE. */
+mk_status mk_plan_workspace_bytes(const mk_plan* plan, size_t* bytes);
+
+/* Byte offset and size of a named intermediate inside the workspace ("qkv" fp32 [M, N_qkv],
+ * "o" bf16 [M, Hq d], "m" bf16 [M, I], "r2a"/"r2b" fp32, "ya"/"yb" bf16) for inspection. */
+mk_status mk_plan_workspace_region(const mk_plan* plan, const char* name, size_t* offset, size_t* bytes);
+
+/* Run the plan once as ONE persistent kernel launch on `hip_stream` (asynchronous).
+ * Workers wait on event counters (polled with a bounded-time watchdog) and signal them
+ * after their outputs are stored.  Not capturable into a graph (the run epoch is a launch
+ * argument).  Runs on one plan must be issued on one stream. */
+mk_status mk_run_layer(mk_plan* plan, const mk_tensors* tensors, void* hip_stream);
+
+/* Run the same op bodies as one standalone kernel per op (one tile per block) inside a
+ * hipGraph captured on first use per tensor set; multistream = 0: one stream in topological
+ * order; 1: independent branches on forked streams joined by events.  Asynchronous. */
+mk_status mk_run_graph_baseline(mk_plan* plan, const mk_tensors* tensors, int32_t multistream, void* hip_stream);
+
+/* Wait for the plan's last run on its stream and report the device error record:
+ * MK_ERR_TIMEOUT if a worker's watchdog expired (counters are then reset). */
+mk_status mk_sync(mk_plan* plan, void* hip_stream);
+
+/* Copy the trace (uint32 [W, L, 4]: visible, input-ready, done timestamps of the 100 MHz
+ * realtime clock, and the poll-wait cycles) of the last MK_FLAG_TRACE run into host memory. */
+mk_status mk_read_trace(const mk_plan* plan, uint32_t* host_out, size_t n_words);
+
+const char* mk_last_error(void);
+void mk_plan_destroy(mk_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

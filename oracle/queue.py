@@ -73,7 +73,7 @@ def tile_params(cfg, W: int, ctx_lens) -> Dict[str, int]:
     p["r_o"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(Hq * d, 1)))
     p["r_gu"] = _largest_divisor_le(I, min(max(1, I // W), cap_rows(H, 2)))
     p["r_down"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(I, 1)))
-    p["r_lm"] = min(cfg.vocab, cap_rows(H, 1)) if cfg.workload == "qwen3_step" else 0
+    p["r_lm"] = min(cfg.vocab, cap_rows(H, 1), 64) if cfg.workload == "qwen3_step" else 0
     ctx_max = int(max(ctx_lens))
     want = -(-(R * ctx_max * Hkv) // W)
     p["s_tok"] = max(4, min(LEASE_BYTES // (4 * d), _pow2ceil(max(1, want))))
@@ -165,10 +165,14 @@ def _qwen3(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
         rl = p["r_lm"]
         n_lm = -(-cfg.vocab // rl)
         grp = b.arrival_group()
+        # a worker keeps a running max over its lm_head tiles and publishes it with its last
+        # one: the last min(W, n_lm) tiles publish, each into its own slot of the group
+        n_pub = min(W, n_lm)
         for j in range(n_lm):
             n0 = j * rl
+            slot = j - (n_lm - n_pub) if j >= n_lm - n_pub else NONE
             b.task(OP_LMHEAD, row_lm, spec, [(prev_down, n_d_t)], [],
-                   [cfg.num_layers, n0, min(rl, cfg.vocab - n0), 0, H, 0, grp, n_lm, j])
+                   [cfg.num_layers, n0, min(rl, cfg.vocab - n0), 0, H, 0, grp, n_pub, slot])
 
 
 def build_queue(cfg, W: int, ctx_lens=None) -> Dict[str, np.ndarray]:

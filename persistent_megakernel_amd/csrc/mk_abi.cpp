@@ -1,0 +1,457 @@
+// C ABI of the decode-layer megakernel: plan construction and upload, operand pointer
+// tables (rebinding without replanning), the persistent launch, the hipGraph baseline, and
+// error reporting.  The operand pointer table keeps tensor addresses out of the
+// instructions, so a new set of tensors only needs a new table (MegaRTP page, section 4,
+// OperandPtrTable).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "mk_device.hpp"
+
+namespace {
+thread_local std::string g_err;
+
+mk_status fail(mk_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+#define HIP_TRY(x)                                                                         \
+  do {                                                                                     \
+    hipError_t _e = (x);                                                                   \
+    if (_e != hipSuccess) return fail(MK_ERR_HIP, std::string(#x ": ") + hipGetErrorString(_e)); \
+  } while (0)
+
+struct GraphEntry {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+}  // namespace
+
+struct mk_plan {
+  mk::HostPlan hp;
+  mk::Shapes sh{};
+  int device = 0;
+  int cus = 0;
+  uint32_t* d_queue = nullptr;
+  uint32_t* d_tasks = nullptr;
+  uint32_t* d_events = nullptr;
+  uint32_t* d_arrivals = nullptr;
+  uint32_t* d_err = nullptr;
+  float* d_rope = nullptr;
+  uint32_t* d_trace = nullptr;
+  size_t events_bytes = 0, arrivals_bytes = 0;
+  uint32_t epoch = 0;
+  bool occupancy_checked = false;
+  bool host_only = false;  // planned without a device: queue inspection only
+  std::map<std::vector<uint64_t>, uint64_t*> tables;
+  std::map<std::vector<uint64_t>, GraphEntry> graphs;
+  std::vector<hipStream_t> streams;
+  std::vector<hipEvent_t> events;
+};
+
+namespace {
+
+bool aligned16(uint64_t p) { return (p & 15u) == 0; }
+
+mk_status check_tensors(const mk_plan* p, const mk_tensors* t) {
+  if (!t) return fail(MK_ERR_INVALID, "null tensors");
+  const mk_config& c = p->hp.cfg;
+  const int need = c.workload == MK_QWEN3_STEP ? MK_T_COUNT_QWEN3 : MK_T_WORKSPACE + 1;
+  if (t->n < need) return fail(MK_ERR_INVALID, "too few tensors for this workload");
+  for (int i = 0; i < need; ++i) {
+    if (t->ptr[i] == 0) return fail(MK_ERR_INVALID, "null tensor at index " + std::to_string(i));
+    if (!aligned16(t->ptr[i])) return fail(MK_ERR_INVALID, "tensor " + std::to_string(i) + " is not 16-byte aligned");
+  }
+  if (t->ptr[MK_T_WORKSPACE] & 255u) return fail(MK_ERR_INVALID, "workspace must be 256-byte aligned");
+  return MK_OK;
+}
+
+size_t region_off(const mk::HostPlan& hp, const char* name) {
+  for (auto& r : hp.regions)
+    if (r.name == name) return r.offset;
+  return 0;
+}
+
+// one row of 16 slots per op instance, layer-offset addresses
+void fill_table(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& tab) {
+  using namespace mk;
+  const mk::HostPlan& hp = p->hp;
+  const mk_config& c = hp.cfg;
+  const uint64_t H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const uint64_t nqkv = (Hq + 2 * Hkv) * d;
+  const uint64_t welem = c.weight_fp8 ? 1 : 2;
+  const uint64_t cache_layer = (uint64_t)c.num_phys_pages * c.page_size * Hkv * d * 2;
+  const uint64_t ws = t->ptr[MK_T_WORKSPACE];
+  const int L = c.num_layers;
+  auto r2buf = [&](int l) -> uint64_t {
+    if (l == L - 1) return t->ptr[MK_T_R2_OUT];
+    return ws + region_off(hp, (l & 1) ? "r2b" : "r2a");
+  };
+  auto ybuf = [&](int l) -> uint64_t {
+    if (l == L - 1) return t->ptr[MK_T_Y_OUT];
+    return ws + region_off(hp, (l & 1) ? "yb" : "ya");
+  };
+  auto xin = [&](int l) { return l == 0 ? t->ptr[MK_T_X] : ybuf(l - 1); };
+  auto rin = [&](int l) { return l == 0 ? t->ptr[MK_T_R_IN] : r2buf(l - 1); };
+  tab.assign(hp.ops.size() * kTableSlots, 0);
+  for (size_t row = 0; row < hp.ops.size(); ++row) {
+    uint64_t* s = &tab[row * kTableSlots];
+    const int l = hp.ops[row].layer;
+    switch (hp.ops[row].opcode) {
+      case OP_QKV:
+        s[QKV_W] = t->ptr[MK_T_W_QKV] + l * nqkv * H * welem;
+        s[QKV_GAMMA] = t->ptr[MK_T_G_ATTN] + l * H * 2;
+        s[QKV_X] = xin(l);
+        s[QKV_RIN] = rin(l);
+        s[QKV_OUT] = ws + region_off(hp, "qkv");
+        break;
+      case OP_ATTN:
+        s[ATT_QKV] = ws + region_off(hp, "qkv");
+        s[ATT_GQ] = t->ptr[MK_T_G_Q] + l * d * 2;
+        s[ATT_GK] = t->ptr[MK_T_G_K] + l * d * 2;
+        s[ATT_KC] = t->ptr[MK_T_K_CACHE] + l * cache_layer;
+        s[ATT_VC] = t->ptr[MK_T_V_CACHE] + l * cache_layer;
+        s[ATT_BT] = t->ptr[MK_T_BLOCK_TABLE];
+        s[ATT_PART] = ws + region_off(hp, "part");
+        s[ATT_O] = ws + region_off(hp, "o");
+        s[ATT_ROPE] = (uint64_t)p->d_rope;
+        break;
+      case OP_OPROJ:
+        s[O_W] = t->ptr[MK_T_W_O] + l * H * Hq * d * welem;
+        s[O_IN] = ws + region_off(hp, "o");
+        s[O_X] = xin(l);
+        s[O_RIN] = rin(l);
+        s[O_R2] = r2buf(l);
+        break;
+      case OP_GATEUP:
+        s[GU_W] = t->ptr[MK_T_W_GU] + l * 2 * I * H * welem;
+        s[GU_GAMMA] = t->ptr[MK_T_G_MLP] + l * H * 2;
+        s[GU_R2] = r2buf(l);
+        s[GU_M] = ws + region_off(hp, "m");
+        break;
+      case OP_DOWN:
+        s[DN_W] = t->ptr[MK_T_W_DOWN] + l * H * I * welem;
+        s[DN_M] = ws + region_off(hp, "m");
+        s[DN_Y] = ybuf(l);
+        break;
+      case OP_LMHEAD:
+        s[LM_W] = t->ptr[MK_T_W_LM];
+        s[LM_GAMMA] = t->ptr[MK_T_G_FINAL];
+        s[LM_Y] = ybuf(L - 1);
+        s[LM_R2] = r2buf(L - 1);
+        s[LM_LOGITS] = t->ptr[MK_T_LOGITS_OUT];
+        s[LM_PART] = ws + region_off(hp, "lm_part");
+        s[LM_TOKEN] = t->ptr[MK_T_TOKEN_OUT];
+        break;
+      default: break;
+    }
+  }
+}
+
+mk_status get_table(mk_plan* p, const mk_tensors* t, uint64_t** out) {
+  std::vector<uint64_t> key(t->ptr, t->ptr + t->n);
+  auto it = p->tables.find(key);
+  if (it != p->tables.end()) {
+    *out = it->second;
+    return MK_OK;
+  }
+  std::vector<uint64_t> tab;
+  fill_table(p, t, tab);
+  uint64_t* d = nullptr;
+  HIP_TRY(hipMalloc(&d, tab.size() * sizeof(uint64_t)));
+  HIP_TRY(hipMemcpy(d, tab.data(), tab.size() * sizeof(uint64_t), hipMemcpyHostToDevice));
+  p->tables[key] = d;
+  *out = d;
+  return MK_OK;
+}
+
+mk_status check_runnable(mk_plan* p) {
+  if (p->host_only) return fail(MK_ERR_INVALID, "plan was built without a device");
+  const mk::HostPlan& hp = p->hp;
+  const mk_config& c = hp.cfg;
+  if (hp.tp.spec != 0 || c.weight_fp8 || c.act_fp8)
+    return fail(MK_ERR_UNSUPPORTED, "only the bf16 single-token (M = 1) op bodies are built");
+  if (c.hidden > 8192 || c.inter > 8192 || c.n_q_heads * c.head_dim > 8192 ||
+      hp.max_splits * (c.n_q_heads / c.n_kv_heads) > 2048)
+    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden, inter, q width <= 8192; KV splits x GQA group <= 2048)");
+  if (!p->occupancy_checked) {
+    int per_cu = 0;
+    HIP_TRY(hipSetDevice(p->device));
+    HIP_TRY(mk::worker_occupancy(&per_cu));
+    if (per_cu < 1) return fail(MK_ERR_UNSUPPORTED, "worker block does not fit on a compute unit");
+    if (hp.W > p->cus * per_cu) return fail(MK_ERR_INVALID, "more workers than co-resident blocks: the persistent kernel could deadlock");
+    p->occupancy_checked = true;
+  }
+  return MK_OK;
+}
+
+mk::KArgs base_args(const mk_plan* p, const uint64_t* table) {
+  mk::KArgs a{};
+  a.table = table;
+  a.events = p->d_events;
+  a.arrivals = p->d_arrivals;
+  a.err = p->d_err;
+  a.trace = p->d_trace;
+  a.epoch = p->epoch;
+  a.flags = p->hp.cfg.flags;
+  a.sh = p->sh;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_last_error(void) { return g_err.c_str(); }
+
+mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens, mk_plan** out) {
+  if (!cfg || !host_context_lens || !out) return fail(MK_ERR_INVALID, "null argument");
+  *out = nullptr;
+  auto p = std::make_unique<mk_plan>();
+  // without a device (host-only planning, e.g. to inspect queues) the worker count must be given
+  bool have_device = hipGetDevice(&p->device) == hipSuccess;
+  if (have_device) {
+    hipDeviceProp_t prop;
+    have_device = hipGetDeviceProperties(&prop, p->device) == hipSuccess;
+    if (have_device) p->cus = prop.multiProcessorCount;
+  }
+  if (!have_device) {
+    (void)hipGetLastError();
+    if (cfg->num_workers <= 0) return fail(MK_ERR_HIP, "no HIP device: give num_workers to plan on the host only");
+  }
+  const int W = cfg->num_workers > 0 ? cfg->num_workers : p->cus;
+  std::string err;
+  mk_status st = mk::plan_build(*cfg, host_context_lens, W, p->hp, err);
+  if (st != MK_OK) return fail(st, err);
+  p->host_only = !have_device;
+  const mk::HostPlan& hp = p->hp;
+  const mk_config& c = hp.cfg;
+  if (p->host_only) {
+    *out = p.release();
+    return MK_OK;
+  }
+  p->sh = mk::Shapes{c.hidden, c.inter, c.n_q_heads, c.n_kv_heads, c.n_q_heads / c.n_kv_heads,
+                     (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, c.page_size, c.max_pages_per_req,
+                     hp.max_splits, c.vocab, c.rms_eps, 1.0f / std::sqrt((float)c.head_dim)};
+  HIP_TRY(hipMalloc(&p->d_queue, hp.queue.size() * 4));
+  HIP_TRY(hipMemcpy(p->d_queue, hp.queue.data(), hp.queue.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(hipMalloc(&p->d_tasks, hp.tasks.size() * 4));
+  HIP_TRY(hipMemcpy(p->d_tasks, hp.tasks.data(), hp.tasks.size() * 4, hipMemcpyHostToDevice));
+  p->events_bytes = std::max<size_t>(1, hp.thresholds.size()) * mk::kEvStride * 4;
+  p->arrivals_bytes = std::max(1, hp.n_arrivals) * mk::kSubStride * 4;
+  HIP_TRY(hipMalloc(&p->d_events, p->events_bytes));
+  HIP_TRY(hipMemset(p->d_events, 0, p->events_bytes));
+  HIP_TRY(hipMalloc(&p->d_arrivals, p->arrivals_bytes));
+  HIP_TRY(hipMemset(p->d_arrivals, 0, p->arrivals_bytes));
+  HIP_TRY(hipMalloc(&p->d_err, 64));
+  HIP_TRY(hipMemset(p->d_err, 0, 64));
+  // RoPE table: per request row, (cos, sin) of pos * theta^(-2i/d) for i < d/2, pos = ctx - 1
+  const int half = c.head_dim / 2;
+  std::vector<float> rope((size_t)c.n_requests * half * 2);
+  for (int r = 0; r < c.n_requests; ++r) {
+    const double pos = host_context_lens[r] - 1;
+    for (int i = 0; i < half; ++i) {
+      const double ang = pos * std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
+      rope[((size_t)r * half + i) * 2] = (float)std::cos(ang);
+      rope[((size_t)r * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  }
+  HIP_TRY(hipMalloc(&p->d_rope, rope.size() * 4));
+  HIP_TRY(hipMemcpy(p->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
+  if (c.flags & MK_FLAG_TRACE) {
+    HIP_TRY(hipMalloc(&p->d_trace, (size_t)hp.W * hp.L * 16));
+    HIP_TRY(hipMemset(p->d_trace, 0, (size_t)hp.W * hp.L * 16));
+  }
+  *out = p.release();
+  return MK_OK;
+}
+
+mk_status mk_plan_queue(const mk_plan* p, const uint32_t** q, int32_t* W, int32_t* L) {
+  if (!p || !q || !W || !L) return fail(MK_ERR_INVALID, "null argument");
+  *q = p->hp.queue.data();
+  *W = p->hp.W;
+  *L = p->hp.L;
+  return MK_OK;
+}
+
+mk_status mk_plan_events(const mk_plan* p, const uint32_t** thr, int32_t* n) {
+  if (!p || !thr || !n) return fail(MK_ERR_INVALID, "null argument");
+  *thr = p->hp.thresholds.data();
+  *n = (int32_t)p->hp.thresholds.size();
+  return MK_OK;
+}
+
+mk_status mk_plan_info(const mk_plan* p, int32_t* n_tasks, int32_t* n_ops, int32_t* n_arrivals) {
+  if (!p) return fail(MK_ERR_INVALID, "null plan");
+  if (n_tasks) *n_tasks = p->hp.T;
+  if (n_ops) *n_ops = (int32_t)p->hp.ops.size();
+  if (n_arrivals) *n_arrivals = p->hp.n_arrivals;
+  return MK_OK;
+}
+
+mk_status mk_plan_workspace_bytes(const mk_plan* p, size_t* bytes) {
+  if (!p || !bytes) return fail(MK_ERR_INVALID, "null argument");
+  *bytes = p->hp.workspace_bytes;
+  return MK_OK;
+}
+
+mk_status mk_plan_workspace_region(const mk_plan* p, const char* name, size_t* offset, size_t* bytes) {
+  if (!p || !name || !offset || !bytes) return fail(MK_ERR_INVALID, "null argument");
+  for (auto& r : p->hp.regions)
+    if (r.name == name) {
+      *offset = r.offset;
+      *bytes = r.bytes;
+      return MK_OK;
+    }
+  return fail(MK_ERR_INVALID, std::string("no workspace region ") + name);
+}
+
+mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
+  if (!p) return fail(MK_ERR_INVALID, "null plan");
+  mk_status st = check_tensors(p, t);
+  if (st != MK_OK) return st;
+  if ((st = check_runnable(p)) != MK_OK) return st;
+  uint64_t* table = nullptr;
+  if ((st = get_table(p, t, &table)) != MK_OK) return st;
+  mk::KArgs a = base_args(p, table);
+  a.instrs = p->d_queue;
+  a.L = p->hp.L;
+  a.first_task = 0;
+  HIP_TRY(mk::launch_worker(a, p->hp.W, (hipStream_t)stream));
+  p->epoch++;
+  return MK_OK;
+}
+
+mk_status mk_run_graph_baseline(mk_plan* p, const mk_tensors* t, int32_t multistream, void* stream_) {
+  if (!p) return fail(MK_ERR_INVALID, "null plan");
+  mk_status st = check_tensors(p, t);
+  if (st != MK_OK) return st;
+  if ((st = check_runnable(p)) != MK_OK) return st;
+  hipStream_t stream = (hipStream_t)stream_;
+  std::vector<uint64_t> key(t->ptr, t->ptr + t->n);
+  key.push_back(multistream ? 1 : 0);
+  auto it = p->graphs.find(key);
+  if (it == p->graphs.end()) {
+    uint64_t* table = nullptr;
+    if ((st = get_table(p, t, &table)) != MK_OK) return st;
+    const auto& ops = p->hp.ops;
+    // stream per op: an op continues the stream of its first dependency unless another
+    // consumer already continued it (independent branches then fork onto new streams)
+    std::vector<int> op_stream(ops.size(), 0);
+    std::vector<bool> continued(ops.size(), false);
+    int n_streams = 1;
+    if (multistream) {
+      for (size_t k = 0; k < ops.size(); ++k) {
+        const auto& deps = ops[k].deps;
+        if (!deps.empty() && !continued[deps[0]]) {
+          op_stream[k] = op_stream[deps[0]];
+          continued[deps[0]] = true;
+        } else if (!deps.empty() || k > 0) {
+          op_stream[k] = deps.empty() ? 0 : n_streams++;
+        }
+      }
+    }
+    // capture on library streams (the caller's stream may be the legacy null stream, which
+    // cannot be captured); the instantiated graph is then launched on the caller's stream
+    while ((int)p->streams.size() < n_streams) {
+      hipStream_t s;
+      HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+      p->streams.push_back(s);
+    }
+    while (p->events.size() < ops.size() + 1) {
+      hipEvent_t e;
+      HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+      p->events.push_back(e);
+    }
+    auto sget = [&](int i) { return p->streams[i]; };
+    hipStream_t cap = p->streams[0];
+    GraphEntry ge;
+    HIP_TRY(hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal));
+    hipEvent_t fork = p->events[ops.size()];
+    HIP_TRY(hipEventRecord(fork, cap));
+    std::vector<bool> started(n_streams, false);
+    started[0] = true;
+    for (size_t k = 0; k < ops.size(); ++k) {
+      hipStream_t s = sget(op_stream[k]);
+      if (!started[op_stream[k]]) {
+        HIP_TRY(hipStreamWaitEvent(s, fork, 0));
+        started[op_stream[k]] = true;
+      }
+      for (int dep : ops[k].deps)
+        if (op_stream[dep] != op_stream[k]) HIP_TRY(hipStreamWaitEvent(s, p->events[dep], 0));
+      mk::KArgs a = base_args(p, table);
+      a.flags = (a.flags & ~(uint32_t)(MK_FLAG_TRACE)) | mk::kModeGraph;
+      a.instrs = p->d_tasks;
+      a.first_task = ops[k].first_task;
+      a.L = ops[k].n_tasks;
+      const int grid = std::min(ops[k].n_tasks, p->hp.W);
+      HIP_TRY(mk::launch_worker(a, grid, s));
+      HIP_TRY(hipEventRecord(p->events[k], s));
+    }
+    for (int i = 1; i < n_streams; ++i) {  // join every forked stream back
+      int last = -1;
+      for (size_t k = 0; k < ops.size(); ++k)
+        if (op_stream[k] == i) last = (int)k;
+      if (last >= 0) HIP_TRY(hipStreamWaitEvent(cap, p->events[last], 0));
+    }
+    HIP_TRY(hipStreamEndCapture(cap, &ge.graph));
+    HIP_TRY(hipGraphInstantiate(&ge.exec, ge.graph, nullptr, nullptr, 0));
+    it = p->graphs.emplace(key, ge).first;
+  }
+  HIP_TRY(hipGraphLaunch(it->second.exec, stream));
+  return MK_OK;
+}
+
+mk_status mk_sync(mk_plan* p, void* stream) {
+  if (!p) return fail(MK_ERR_INVALID, "null plan");
+  if (p->host_only) return fail(MK_ERR_INVALID, "plan was built without a device");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  uint32_t e[8];
+  HIP_TRY(hipMemcpy(e, p->d_err, sizeof(e), hipMemcpyDeviceToHost));
+  if (e[0]) {
+    HIP_TRY(hipMemset(p->d_events, 0, p->events_bytes));
+    HIP_TRY(hipMemset(p->d_arrivals, 0, p->arrivals_bytes));
+    HIP_TRY(hipMemset(p->d_err, 0, 64));
+    HIP_TRY(hipDeviceSynchronize());
+    p->epoch = 0;
+    return fail(MK_ERR_TIMEOUT, "watchdog: worker " + std::to_string(e[1]) + " task " + std::to_string(e[2]) +
+                                    " event " + std::to_string(e[3]) + " value " + std::to_string(e[4]) +
+                                    " target " + std::to_string(e[5]));
+  }
+  return MK_OK;
+}
+
+mk_status mk_read_trace(const mk_plan* p, uint32_t* out, size_t n_words) {
+  if (!p || !out) return fail(MK_ERR_INVALID, "null argument");
+  if (!p->d_trace) return fail(MK_ERR_INVALID, "plan was not built with MK_FLAG_TRACE");
+  const size_t have = (size_t)p->hp.W * p->hp.L * 4;
+  HIP_TRY(hipMemcpy(out, p->d_trace, std::min(have, n_words) * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+void mk_plan_destroy(mk_plan* p) {
+  if (!p) return;
+  for (auto& kv : p->graphs) {
+    if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
+    if (kv.second.graph) (void)hipGraphDestroy(kv.second.graph);
+  }
+  for (auto& kv : p->tables) (void)hipFree(kv.second);
+  for (auto s : p->streams) (void)hipStreamDestroy(s);
+  for (auto e : p->events) (void)hipEventDestroy(e);
+  (void)hipFree(p->d_queue);
+  (void)hipFree(p->d_tasks);
+  (void)hipFree(p->d_events);
+  (void)hipFree(p->d_arrivals);
+  (void)hipFree(p->d_err);
+  (void)hipFree(p->d_rope);
+  if (p->d_trace) (void)hipFree(p->d_trace);
+  delete p;
+}
+
+}  // extern "C"

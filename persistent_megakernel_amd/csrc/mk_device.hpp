@@ -1,0 +1,64 @@
+// Kernel-side constants and the launch argument block shared by the device code and the
+// host launcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.hpp"
+
+namespace mk {
+
+struct Shapes {
+  int H, I, Hq, Hkv, g, n_qkv, P, maxp, max_splits, V;
+  float eps, inv_sqrt_d;
+};
+
+struct KArgs {
+  const uint32_t* instrs;  // megakernel: queue [W, L, 32]; graph: task list [T, 32]
+  int L;                   // megakernel: queue length per worker; graph: tasks of the op
+  int first_task;          // graph: task id of block 0
+  const uint64_t* table;   // operand pointer table [n_ops, 16]
+  uint32_t* events;        // [E][kNSub sub-counters, kSubStride words apart]
+  uint32_t* arrivals;      // [A], kSubStride words apart, self re-arming
+  uint32_t* err;           // device error record: flag, worker, task, event, value, target
+  uint32_t* trace;         // [W, L, 4] or null
+  uint32_t epoch;          // runs of this plan so far: a wait on threshold t targets (epoch+1)*t
+  uint32_t flags;          // MK_FLAG_* | kModeGraph
+  Shapes sh;
+};
+
+constexpr uint32_t kModeGraph = 1u << 16;
+constexpr int kNSub = 16;                  // sub-counters per event (spreads the atomics)
+constexpr int kSubStride = 32;             // words between sub-counters (128 bytes)
+constexpr int kEvStride = kNSub * kSubStride;
+constexpr unsigned long long kWatchdogTicks = 200000000ull;  // 2 s of the 100 MHz clock
+
+namespace dev {
+constexpr int kThreads = 512;  // 8 waves: controller + 7 loader/compute waves
+constexpr int kNCW = 7;
+constexpr int kNPages = 8;     // LDS ring of 8 x 16 KiB pages
+constexpr int kRingOff = 0;
+constexpr int kActOff = kNPages * 16384;   // activation staging
+constexpr int kActBytes = 22528;
+constexpr int kOutOff = kActOff + kActBytes;  // compute results
+constexpr int kOutBytes = 8192;
+constexpr int kCtrlOff = kOutOff + kOutBytes;  // abort flag + per-wave lease tables
+constexpr int kCtrlBytes = 1024;
+constexpr int kLdsBytes = kCtrlOff + kCtrlBytes;  // 162816 of 163840: one block per CU
+// attention sub-areas of the activation staging area
+constexpr int kActQ = 0;       // bf16 [g <= 8][128]
+constexpr int kActK = 2048;    // bf16 [128] new key
+constexpr int kActV = 2304;    // bf16 [128] new value
+constexpr int kActS = 2560;    // fp32 [g][kSStride] scores / probabilities
+constexpr int kSStride = 132;
+constexpr int kActStat = 6784;  // fp32 [g][2] max, sum
+constexpr int kActRed = 7168;   // fp32 [TG][g][128] PV partials (<= 14336 bytes)
+static_assert(kActRed + 14336 <= kActBytes, "attention staging overflows");
+static_assert(kLdsBytes <= 163840, "LDS budget");
+}  // namespace dev
+
+hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream);
+hipError_t worker_occupancy(int* blocks_per_cu);
+
+}  // namespace mk

@@ -1,0 +1,85 @@
+// Internal host-side definitions shared by the planner, the launch code and the C ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+
+namespace mk {
+
+enum Opcode : uint32_t {
+  OP_NOOP = 0,
+  OP_QKV = 1,     // fused add + RMSNorm prologue, QKV projection rows
+  OP_ATTN = 2,    // QK-norm + RoPE + cache write + split-KV attention partial; last arrival combines
+  OP_OPROJ = 3,   // O projection rows + residual add
+  OP_GATEUP = 4,  // RMSNorm prologue, gate and up rows, SiLU-mul epilogue
+  OP_DOWN = 5,    // down projection rows
+  OP_LMHEAD = 6   // final add + RMSNorm prologue, lm_head rows, tile max; last arrival takes the argmax
+};
+
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+constexpr int kWords = 32;
+constexpr int kLeaseBytes = 65536;  // largest LDS lease of one instruction
+
+// instruction word positions
+enum Word : int {
+  W_OPCODE = 0, W_NWAIT = 1, W_NSIG = 2, W_ROW = 3, W_SPEC = 4, W_TASK = 5,
+  W_WAIT0 = 6,    // (event, threshold) x 4
+  W_SIG0 = 14,    // (event, increment, publication id) x 2
+  W_LAYER = 20,
+  W_P1 = 21,      // n0 | request
+  W_P2 = 22,      // rows | kv head
+  W_P3 = 23,      // k0 | split
+  W_P4 = 24,      // k length | token start
+  W_P5 = 25,      // token end (exclusive)
+  W_ARR_ID = 26,  // arrival group
+  W_ARR_N = 27,   // arrival group size (0: no arrival group)
+  W_ARR_RANK = 28 // rank of this task in its group
+};
+
+// operand pointer table: 16 slots per op row
+constexpr int kTableSlots = 16;
+enum QkvSlot { QKV_W = 0, QKV_GAMMA, QKV_X, QKV_RIN, QKV_OUT };
+enum AttnSlot { ATT_QKV = 0, ATT_GQ, ATT_GK, ATT_KC, ATT_VC, ATT_BT, ATT_PART, ATT_O, ATT_ROPE };
+enum OSlot { O_W = 0, O_IN, O_X, O_RIN, O_R2 };
+enum GuSlot { GU_W = 0, GU_GAMMA, GU_R2, GU_M };
+enum DownSlot { DN_W = 0, DN_M, DN_Y };
+enum LmSlot { LM_W = 0, LM_GAMMA, LM_Y, LM_R2, LM_LOGITS, LM_PART, LM_TOKEN };
+
+struct TileParams {
+  int r_qkv = 0, r_o = 0, r_gu = 0, r_down = 0, r_lm = 0, s_tok = 0, spec = 0;
+};
+
+struct OpInfo {      // one row of the operand table = one op instance
+  uint32_t opcode;
+  int layer;
+  int first_task, n_tasks;
+  std::vector<int> deps;  // op rows this op waits on (graph edges)
+};
+
+struct WorkspaceRegion {
+  std::string name;
+  size_t offset, bytes;
+};
+
+struct HostPlan {
+  mk_config cfg{};
+  std::vector<int32_t> ctx;
+  int W = 0, L = 0, T = 0;
+  TileParams tp;
+  std::vector<uint32_t> queue;       // [W, L, 32]
+  std::vector<uint32_t> tasks;       // [T, 32] in task order (graph baseline)
+  std::vector<uint32_t> thresholds;  // [E]
+  int n_arrivals = 0;
+  std::vector<OpInfo> ops;           // indexed by operand row
+  int max_splits = 0;                // largest number of KV splits of any (request, kv head)
+  std::vector<WorkspaceRegion> regions;
+  size_t workspace_bytes = 0;
+};
+
+// planner.cpp
+mk_status plan_build(const mk_config& cfg, const int32_t* ctx, int W, HostPlan& out, std::string& err);
+
+}  // namespace mk

@@ -1,0 +1,274 @@
+// Host planner: workload template -> tile tasks -> events -> round-robin worker queues.
+//
+// The lowering follows the MegaRTP page ("Kernel-Mega-PDL", section 4): each op expands
+// into tile tasks; each (producer op, consumer op) pair becomes events whose threshold is
+// the number of producer tasks writing the region the consumer reads; tasks are numbered in
+// topological order and dealt round-robin onto fixed worker queues padded with NoOp, giving
+// an instruction tensor [W, L, 32] of uint32.  Deadlock freedom needs only that every wait
+// names events produced by smaller task ids and that all workers are co-resident (handbook
+// megakernel section, exercise 3); the builder checks the first, the launcher the second.
+#include <algorithm>
+#include <cstring>
+
+#include "mk_internal.hpp"
+
+namespace mk {
+namespace {
+
+int pow2floor(int x) {
+  int p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+int pow2ceil(int x) {
+  int p = 1;
+  while (p < x) p *= 2;
+  return p;
+}
+int largest_divisor_le(int n, int cap) {
+  cap = std::max(1, std::min(n, cap));
+  for (int r = cap; r > 0; --r)
+    if (n % r == 0) return r;
+  return 1;
+}
+
+struct Builder {
+  std::vector<uint32_t> tasks;
+  std::vector<uint32_t> thr;
+  int n_arrivals = 0;
+  std::vector<OpInfo> ops;
+
+  int event(uint32_t threshold) {
+    thr.push_back(threshold);
+    return (int)thr.size() - 1;
+  }
+  int op_row(uint32_t opcode, int layer, std::vector<int> deps) {
+    ops.push_back(OpInfo{opcode, layer, (int)(tasks.size() / kWords), 0, std::move(deps)});
+    return (int)ops.size() - 1;
+  }
+  int task(uint32_t opcode, int row, int spec, std::initializer_list<std::pair<int, uint32_t>> waits,
+           std::initializer_list<std::pair<int, uint32_t>> sigs, std::initializer_list<int64_t> payload) {
+    int tid = (int)(tasks.size() / kWords);
+    size_t base = tasks.size();
+    tasks.resize(base + kWords, 0u);
+    uint32_t* w = tasks.data() + base;
+    w[W_OPCODE] = opcode;
+    w[W_NWAIT] = (uint32_t)waits.size();
+    w[W_NSIG] = (uint32_t)sigs.size();
+    w[W_ROW] = (uint32_t)row;
+    w[W_SPEC] = (uint32_t)spec;
+    w[W_TASK] = (uint32_t)tid;
+    int i = 0;
+    for (auto& e : waits) {
+      w[W_WAIT0 + 2 * i] = (uint32_t)e.first;
+      w[W_WAIT0 + 2 * i + 1] = e.second;
+      ++i;
+    }
+    i = 0;
+    for (auto& s : sigs) {
+      w[W_SIG0 + 3 * i] = (uint32_t)s.first;
+      w[W_SIG0 + 3 * i + 1] = s.second;
+      w[W_SIG0 + 3 * i + 2] = (uint32_t)tid;
+      ++i;
+    }
+    i = 0;
+    for (int64_t v : payload) w[W_LAYER + i++] = (uint32_t)(v & 0xFFFFFFFFll);
+    if (ops[row].n_tasks == 0) ops[row].first_task = tid;
+    ops[row].n_tasks++;
+    return tid;
+  }
+};
+
+bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, std::string& err) {
+  const int H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int R = c.n_requests;
+  const int elem = c.weight_fp8 ? 1 : 2;
+  const int n_qkv = (Hq + 2 * Hkv) * d;
+  auto cap_rows = [&](int k, int nmat) { return std::max(1, kLeaseBytes / (k * elem * nmat)); };
+  p.r_qkv = pow2floor(std::min({d, std::max(1, n_qkv / W), cap_rows(H, 1)}));
+  p.r_o = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(Hq * d, 1)));
+  p.r_gu = largest_divisor_le(I, std::min(std::max(1, I / W), cap_rows(H, 2)));
+  p.r_down = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(I, 1)));
+  p.r_lm = c.workload == MK_QWEN3_STEP ? std::min({c.vocab, cap_rows(H, 1), 64}) : 0;
+  int ctx_max = 0;
+  for (int r = 0; r < R; ++r) ctx_max = std::max(ctx_max, (int)ctx[r]);
+  long long want = ((long long)R * ctx_max * Hkv + W - 1) / W;
+  p.s_tok = std::max(4, std::min(kLeaseBytes / (4 * d), pow2ceil((int)std::max(1ll, want))));
+  p.spec = (R * c.tokens_per_request == 1) ? 0 : 1;
+  (void)err;
+  return true;
+}
+
+}  // namespace
+
+mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& out, std::string& err) {
+  if (c.workload != MK_QWEN3_LAYER && c.workload != MK_QWEN3_STEP) {
+    err = "workload not built in this library";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const int H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int R = c.n_requests, P = c.page_size;
+  if (W < 1 || H < 1 || I < 1 || d < 2 || Hq < 1 || Hkv < 1 || Hq % Hkv || c.num_layers < 1 || R < 1) {
+    err = "invalid shape";
+    return MK_ERR_INVALID;
+  }
+  if (c.tokens_per_request != 1) {
+    err = "the decode-layer workloads take one new token per request";
+    return MK_ERR_INVALID;
+  }
+  if (d != 128 || H % 8 || I % 8 || P < 4 || P % 4 || Hq / Hkv > 8) {
+    err = "unsupported shape: head_dim must be 128, hidden/inter multiples of 8, page size a multiple of 4, GQA group <= 8";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (c.workload == MK_QWEN3_STEP && c.vocab < 1) {
+    err = "vocab must be positive";
+    return MK_ERR_INVALID;
+  }
+  for (int r = 0; r < R; ++r) {
+    if (ctx[r] < 1 || ctx[r] > c.max_pages_per_req * P) {
+      err = "context length out of range of the block table";
+      return MK_ERR_INVALID;
+    }
+  }
+  out = HostPlan{};
+  out.cfg = c;
+  out.ctx.assign(ctx, ctx + R);
+  out.W = W;
+  TileParams& p = out.tp;
+  if (!tile_params(c, W, ctx, p, err)) return MK_ERR_INVALID;
+
+  Builder b;
+  const int g = Hq / Hkv;
+  const int n_qkv = (Hq + 2 * Hkv) * d;
+  const int rq = p.r_qkv, ro = p.r_o, rgu = p.r_gu, rd = p.r_down, st = p.s_tok;
+  const int n_qkv_t = n_qkv / rq, n_o_t = H / ro, n_gu_t = I / rgu, n_d_t = H / rd;
+  const uint32_t thr_grp = (uint32_t)((g + 2) * d / rq);
+  int prev_down = -1, prev_down_row = -1;
+  int max_splits = 0;
+  for (int l = 0; l < c.num_layers; ++l) {
+    int row_qkv = b.op_row(OP_QKV, l, prev_down_row >= 0 ? std::vector<int>{prev_down_row} : std::vector<int>{});
+    int row_attn = b.op_row(OP_ATTN, l, {row_qkv});
+    int row_o = b.op_row(OP_OPROJ, l, {row_attn});
+    int row_gu = b.op_row(OP_GATEUP, l, {row_o});
+    int row_d = b.op_row(OP_DOWN, l, {row_gu});
+    std::vector<int> ev_qkv(Hkv);
+    for (int hk = 0; hk < Hkv; ++hk) ev_qkv[hk] = b.event(thr_grp);
+    int ev_oready = b.event((uint32_t)(R * Hkv));
+    int ev_o = b.event((uint32_t)n_o_t);
+    int ev_gu = b.event((uint32_t)n_gu_t);
+    int ev_down = b.event((uint32_t)n_d_t);
+    for (int j = 0; j < n_qkv_t; ++j) {
+      int n0 = j * rq, grp;
+      if (n0 < Hq * d) grp = (n0 / d) / g;
+      else if (n0 < (Hq + Hkv) * d) grp = (n0 - Hq * d) / d;
+      else grp = (n0 - (Hq + Hkv) * d) / d;
+      if (prev_down < 0)
+        b.task(OP_QKV, row_qkv, p.spec, {}, {{ev_qkv[grp], 1u}}, {l, n0, rq, 0, H});
+      else
+        b.task(OP_QKV, row_qkv, p.spec, {{prev_down, (uint32_t)n_d_t}}, {{ev_qkv[grp], 1u}}, {l, n0, rq, 0, H});
+    }
+    int grp_id = 0;
+    for (int r = 0; r < R; ++r) {
+      int cx = ctx[r], ns = (cx + st - 1) / st;
+      max_splits = std::max(max_splits, ns);
+      for (int hk = 0; hk < Hkv; ++hk) {
+        grp_id = b.n_arrivals++;
+        for (int s = 0; s < ns; ++s) {
+          int t0 = s * st, t1 = std::min(cx, (s + 1) * st);
+          b.task(OP_ATTN, row_attn, p.spec, {{ev_qkv[hk], thr_grp}}, {{ev_oready, 1u}},
+                 {l, r, hk, s, t0, t1, grp_id, ns, s});
+        }
+      }
+    }
+    for (int j = 0; j < n_o_t; ++j)
+      b.task(OP_OPROJ, row_o, p.spec, {{ev_oready, (uint32_t)(R * Hkv)}}, {{ev_o, 1u}}, {l, j * ro, ro, 0, Hq * d});
+    for (int j = 0; j < n_gu_t; ++j)
+      b.task(OP_GATEUP, row_gu, p.spec, {{ev_o, (uint32_t)n_o_t}}, {{ev_gu, 1u}}, {l, j * rgu, rgu, 0, H});
+    for (int j = 0; j < n_d_t; ++j)
+      b.task(OP_DOWN, row_d, p.spec, {{ev_gu, (uint32_t)n_gu_t}}, {{ev_down, 1u}}, {l, j * rd, rd, 0, I});
+    prev_down = ev_down;
+    prev_down_row = row_d;
+  }
+  if (c.workload == MK_QWEN3_STEP) {
+    int row_lm = b.op_row(OP_LMHEAD, c.num_layers, {prev_down_row});
+    int rl = p.r_lm, n_lm = (c.vocab + rl - 1) / rl;
+    int grp = b.n_arrivals++;
+    // each worker keeps a running max over its lm_head tiles and publishes it with its last
+    // one: the last min(W, n_lm) tiles publish, each into its own slot of the arrival group
+    const int n_pub = std::min(W, n_lm);
+    for (int j = 0; j < n_lm; ++j) {
+      int n0 = j * rl;
+      int64_t slot = j >= n_lm - n_pub ? (int64_t)(j - (n_lm - n_pub)) : (int64_t)kNone;
+      b.task(OP_LMHEAD, row_lm, p.spec, {{prev_down, (uint32_t)n_d_t}}, {},
+             {c.num_layers, n0, std::min(rl, c.vocab - n0), 0, H, 0, grp, n_pub, slot});
+    }
+  }
+  out.T = (int)(b.tasks.size() / kWords);
+  out.L = (out.T + W - 1) / W;
+  out.queue.assign((size_t)W * out.L * kWords, 0u);
+  for (int t = 0; t < out.T; ++t)
+    std::memcpy(&out.queue[((size_t)(t % W) * out.L + t / W) * kWords], &b.tasks[(size_t)t * kWords],
+                kWords * sizeof(uint32_t));
+  out.tasks = std::move(b.tasks);
+  out.thresholds = std::move(b.thr);
+  out.n_arrivals = b.n_arrivals;
+  out.ops = std::move(b.ops);
+  out.max_splits = max_splits;
+
+  // each op's tasks form one contiguous run of task ids (the graph baseline launches it)
+  for (size_t r = 0; r < out.ops.size(); ++r) {
+    const OpInfo& op = out.ops[r];
+    for (int t = op.first_task; t < op.first_task + op.n_tasks; ++t)
+      if (out.tasks[(size_t)t * kWords + W_ROW] != (uint32_t)r) {
+        err = "planner invariant violated (op tasks not contiguous)";
+        return MK_ERR_INVALID;
+      }
+  }
+
+  // workspace regions (256-byte aligned)
+  size_t off = 0;
+  const int M = R * c.tokens_per_request;
+  auto region = [&](const char* name, size_t bytes) {
+    out.regions.push_back({name, off, bytes});
+    off += (bytes + 255) / 256 * 256;
+  };
+  region("qkv", (size_t)M * n_qkv * 4);
+  region("part", (size_t)R * Hkv * max_splits * g * (d + 1) * 4);
+  region("o", (size_t)M * Hq * d * 2);
+  region("m", (size_t)M * I * 2);
+  region("r2a", (size_t)M * H * 4);
+  region("r2b", (size_t)M * H * 4);
+  region("ya", (size_t)M * H * 2);
+  region("yb", (size_t)M * H * 2);
+  if (c.workload == MK_QWEN3_STEP) region("lm_part", (size_t)((c.vocab + p.r_lm - 1) / p.r_lm) * 8);
+  out.workspace_bytes = off;
+
+  // invariants: every wait names an event whose producers precede the waiter; thresholds equal
+  // the increments issued per run
+  std::vector<long long> produced(out.thresholds.size(), 0);
+  std::vector<int> last_prod(out.thresholds.size(), -1);
+  for (int t = 0; t < out.T; ++t) {
+    const uint32_t* w = &out.tasks[(size_t)t * kWords];
+    for (uint32_t k = 0; k < w[W_NWAIT]; ++k) {
+      uint32_t e = w[W_WAIT0 + 2 * k];
+      if (e >= out.thresholds.size() || w[W_WAIT0 + 2 * k + 1] != out.thresholds[e] || last_prod[e] >= t) {
+        err = "planner invariant violated (wait)";
+        return MK_ERR_INVALID;
+      }
+    }
+    for (uint32_t k = 0; k < w[W_NSIG]; ++k) {
+      uint32_t e = w[W_SIG0 + 3 * k];
+      bool fires = w[W_ARR_N] == 0 || w[W_ARR_RANK] == w[W_ARR_N] - 1;
+      if (fires) produced[e] += w[W_SIG0 + 3 * k + 1];
+      last_prod[e] = t;
+    }
+  }
+  for (size_t e = 0; e < produced.size(); ++e)
+    if (produced[e] != (long long)out.thresholds[e]) {
+      err = "planner invariant violated (threshold != increments)";
+      return MK_ERR_INVALID;
+    }
+  return MK_OK;
+}
+
+}  // namespace mk

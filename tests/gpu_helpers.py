@@ -1,0 +1,48 @@
+"""Device-side setup shared by the GPU tests: upload seeded inputs, allocate outputs and the
+workspace, build the mk_tensors block."""
+import numpy as np
+import torch
+
+import persistent_megakernel_amd as mk
+
+
+def to_device(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    b = t.detach().cpu().numpy().view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+class QwenRun:
+    """Inputs, outputs and workspace of one Qwen3 layer / step plan on cuda:0."""
+
+    def __init__(self, cfg, inp, num_workers=0, flags=0, ctx=None):
+        self.cfg = cfg
+        self.step = cfg.workload == "qwen3_step"
+        self.plan = mk.Plan(cfg, context_lens=ctx, num_workers=num_workers, flags=flags)
+        M, H = cfg.m, cfg.hidden
+        t = {k: to_device(v) for k, v in inp.items() if k in mk.QWEN3_TENSORS or k in ("x", "r_in")}
+        t["y_out"] = torch.zeros(M * H, dtype=torch.int16, device="cuda")
+        t["r2_out"] = torch.zeros(M * H, dtype=torch.float32, device="cuda")
+        t["workspace"] = torch.zeros(self.plan.workspace_bytes() + 256, dtype=torch.uint8, device="cuda")
+        if self.step:
+            t["logits_out"] = torch.zeros(M * cfg.vocab, dtype=torch.float32, device="cuda")
+            t["token_out"] = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+        self.t = t
+        self.tensors = mk.qwen3_pointers(t, self.step)
+
+    def region(self, name, dtype):
+        off, n = self.plan.region(name)
+        return self.t["workspace"][off:off + n].view(dtype)
+
+    def run(self, mode="mk", multistream=False):
+        if mode == "mk":
+            self.plan.run(self.tensors)
+        else:
+            self.plan.run_graph(self.tensors, multistream=multistream)
+        self.plan.sync()
+        torch.cuda.synchronize()

@@ -1,0 +1,135 @@
+"""GPU parity of the Qwen3 decode-layer path (megakernel and graph baselines) against the
+CPU oracle, called through the C ABI.
+
+Tolerance: max abs error 2e-2 on bf16 outputs, compared with the oracle value before its
+final output rounding.  Cache writes: the written slot set is exact (every other byte of
+both caches is unchanged bit for bit) and the written rows match the oracle within the
+tolerance.  Greedy token: the GPU index must attain the oracle maximum within 2e-2."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import model
+from oracle.numerics import bf16_bits_to_f64
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _check_layer(run, inp, ref, k_before, v_before, tag):
+    from gpu_helpers import bf16_to_f64
+    cfg = run.cfg
+    y = bf16_to_f64(run.t["y_out"]).reshape(cfg.m, cfg.hidden)
+    r2 = run.t["r2_out"].cpu().numpy().astype(np.float64).reshape(cfg.m, cfg.hidden)
+    ey = np.max(np.abs(y - ref["y_pre"]))
+    er = np.max(np.abs(r2 - ref["r2"]))
+    assert ey <= TOL and er <= TOL, f"{tag}: y err {ey}, r2 err {er}"
+    # cache: only the oracle's slot changed; its rows match
+    kc = run.t["k_cache"].cpu().numpy().view(np.uint16)[0]
+    vc = run.t["v_cache"].cpu().numpy().view(np.uint16)[0]
+    mask = np.ones(kc.shape[:2], dtype=bool)
+    for mi in range(cfg.m):
+        page, off = ref["slot_page"][mi], ref["slot_off"][mi]
+        mask[page, off] = False
+        assert np.max(np.abs(bf16_bits_to_f64(kc[page, off]) - ref["k_pre"][mi])) <= TOL, tag
+        assert np.max(np.abs(bf16_bits_to_f64(vc[page, off]) - ref["v_pre"][mi])) <= TOL, tag
+    assert np.array_equal(kc[mask], k_before[mask]) and np.array_equal(vc[mask], v_before[mask]), tag
+
+
+def _layer_case(cfg, W=0, ctx=None, seed=0):
+    from gpu_helpers import QwenRun
+    inp = make_inputs(cfg, seed=seed)
+    if ctx is not None:
+        inp["context_lens"] = np.array(ctx, dtype=np.int32)
+    ref = model.run_qwen3_layer(cfg, inp)
+    run = QwenRun(cfg, inp, num_workers=W, ctx=ctx)
+    return inp, ref, run
+
+
+def test_small_layer_megakernel_and_intermediates():
+    cfg = get_config("qwen3_0p6b_layer")
+    _say("case: qwen3_0p6b_layer megakernel W=all")
+    inp, ref, run = _layer_case(cfg)
+    k0, v0 = inp["k_cache"][0].copy(), inp["v_cache"][0].copy()
+    run.run("mk")
+    qkv = run.region("qkv", torch.float32).cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(qkv - ref["qkv"].reshape(-1))) <= TOL
+    o = bf16_bits_to_f64(run.region("o", torch.int16).cpu().numpy().view(np.uint16))
+    assert np.max(np.abs(o - ref["o_pre"].reshape(-1))) <= TOL
+    m = bf16_bits_to_f64(run.region("m", torch.int16).cpu().numpy().view(np.uint16))
+    assert np.max(np.abs(m - ref["m_pre"].reshape(-1))) <= TOL
+    _check_layer(run, inp, ref, k0, v0, "mk")
+
+
+def test_small_layer_graph_baselines_match_megakernel_bitwise():
+    cfg = get_config("qwen3_0p6b_layer")
+    inp, ref, run = _layer_case(cfg)
+    k0, v0 = inp["k_cache"][0].copy(), inp["v_cache"][0].copy()
+    outs = []
+    for mode, ms in (("mk", False), ("graph", False), ("graph", True), ("mk", False), ("graph", False)):
+        _say(f"case: qwen3_0p6b_layer {mode} multistream={ms}")
+        run.t["y_out"].zero_()
+        run.t["r2_out"].zero_()
+        run.run(mode, ms)
+        _check_layer(run, inp, ref, k0, v0, f"{mode}/{ms}")
+        outs.append((run.t["y_out"].clone(), run.t["r2_out"].clone()))
+    for y, r in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(r, outs[0][1])
+
+
+@pytest.mark.parametrize("W,ctx", [(7, [37]), (64, [1]), (256, [513]), (13, [200])])
+def test_ragged_small_shapes(W, ctx):
+    cfg = dataclasses.replace(get_config("qwen3_0p6b_layer"), hidden=512, inter=1536, n_q_heads=8, n_kv_heads=2,
+                              context=max(ctx[0], 1), page_size=16)
+    _say(f"case: small layer W={W} ctx={ctx}")
+    inp, ref, run = _layer_case(cfg, W=W, ctx=ctx, seed=W)
+    k0, v0 = inp["k_cache"][0].copy(), inp["v_cache"][0].copy()
+    run.run("mk")
+    _check_layer(run, inp, ref, k0, v0, "mk")
+    run.run("graph")
+    _check_layer(run, inp, ref, k0, v0, "graph")
+
+
+def _check_step(run, res, tag):
+    cfg = run.cfg
+    logits = run.t["logits_out"].cpu().numpy().astype(np.float64)
+    el = np.max(np.abs(logits - res["logits_pre"][0]))
+    assert el <= TOL, f"{tag}: logits err {el}"
+    tok = int(run.t["token_out"].cpu().numpy()[0])
+    assert res["logits_pre"][0][tok] >= np.max(res["logits_pre"][0]) - TOL, tag
+
+
+def test_reduced_step_all_modes():
+    cfg = dataclasses.replace(get_config("qwen3_0p6b_step"), num_layers=3, vocab=3000, context=300)
+    inp = make_inputs(cfg, seed=7)
+    res = model.run_qwen3_step(cfg, inp)
+    from gpu_helpers import QwenRun
+    for W in (0, 9):
+        run = QwenRun(cfg, inp, num_workers=W)
+        for mode, ms in (("mk", False), ("graph", False), ("graph", True)):
+            _say(f"case: reduced step W={W} {mode} ms={ms}")
+            run.run(mode, ms)
+            _check_step(run, res, f"W={W} {mode}")
+
+
+def test_full_step_28_layers():
+    cfg = get_config("qwen3_0p6b_step")
+    _say("case: full 28-layer step, oracle on host")
+    inp = make_inputs(cfg, seed=0)
+    res = model.run_qwen3_step(cfg, inp)
+    from gpu_helpers import QwenRun
+    run = QwenRun(cfg, inp)
+    for mode in ("mk", "graph"):
+        _say(f"case: full step {mode}")
+        run.run(mode)
+        _check_step(run, res, mode)
+        y = np.asarray(bf16_bits_to_f64(run.t["y_out"].cpu().numpy().view(np.uint16)))
+        assert np.max(np.abs(y - res["layers"][-1]["y_pre"][0])) <= TOL
