@@ -1,0 +1,183 @@
+"""Benchmark: microseconds per decode layer-step and achieved HBM bandwidth on one MI355X.
+
+Default workload: the Qwen3-0.6B-shaped full decode step (28 layers, batch 1, context
+2048 in 16-token pages, final RMSNorm, lm_head over 151936 rows, greedy argmax) with
+seeded synthetic bf16 weights and caches, run as ONE persistent megakernel launch per
+step.  The same op bodies are also timed as a single-stream and a multi-stream hipGraph
+(one kernel per op), without cross-instruction prefetch, and with every op body skipped
+(the framework alone).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_0p6b_step", choices=["qwen3_0p6b_step", "qwen3_0p6b_layer"])
+    ap.add_argument("--rotate", type=int, default=0, help="copies of weights/caches cycled per run (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the decode chain on a single MI355X "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import persistent_megakernel_amd as mk
+    from gpu_helpers import to_device
+    from workloads import algorithmic_bytes, get_config, make_inputs
+
+    cfg = get_config(args.workload)
+    rotate = args.rotate or (1 if cfg.workload == "qwen3_step" else 16)
+    _log(f"bench: workload {cfg.name}, rotate {rotate}, generating inputs")
+    t0 = time.time()
+    inp = make_inputs(cfg, seed=0)
+    _log(f"bench: inputs generated in {time.time() - t0:.1f}s")
+    step = cfg.workload == "qwen3_step"
+    stream = torch.cuda.Stream()
+    M, H = cfg.m, cfg.hidden
+
+    def device_set(seed_shift: int):
+        t = {k: to_device(v) for k, v in inp.items()}
+        if seed_shift:  # a distinct copy: same values, other addresses (defeats cache residency)
+            t = {k: v.clone() for k, v in t.items()}
+        return t
+
+    base = device_set(0)
+    sets = [base] + [device_set(i) for i in range(1, rotate)]
+    plans = {}
+
+    def plan(flags=0):
+        if flags not in plans:
+            plans[flags] = mk.Plan(cfg, flags=flags)
+        return plans[flags]
+
+    p0 = plan(0)
+    ws_bytes = p0.workspace_bytes() + 256
+    tensor_sets = []
+    for s in sets:
+        s = dict(s)
+        s["y_out"] = torch.zeros(M * H, dtype=torch.int16, device="cuda")
+        s["r2_out"] = torch.zeros(M * H, dtype=torch.float32, device="cuda")
+        s["workspace"] = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+        if step:
+            s["logits_out"] = torch.zeros(M * cfg.vocab, dtype=torch.float32, device="cuda")
+            s["token_out"] = torch.zeros(M, dtype=torch.int32, device="cuda")
+        tensor_sets.append(mk.qwen3_pointers(s, step))
+    torch.cuda.synchronize()
+
+    def timed(fn, p, steps, warmup):
+        for i in range(warmup):
+            fn(p, tensor_sets[i % rotate])
+        p.sync(stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(p, tensor_sets[i % rotate])
+        e1.record(stream)
+        p.sync(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per run
+
+    run_mk = lambda p, t: p.run(t, stream)
+    run_g1 = lambda p, t: p.run_graph(t, False, stream)
+    run_gm = lambda p, t: p.run_graph(t, True, stream)
+
+    _log("bench: megakernel")
+    with torch.cuda.stream(stream):
+        ms = timed(run_mk, p0, args.steps, args.warmup)
+    variants = {}
+    if not args.no_variants:
+        for name, fn, flags in (("graph_single_stream", run_g1, 0), ("graph_multi_stream", run_gm, 0),
+                                ("megakernel_no_prefetch", run_mk, mk.MK_FLAG_NO_PREFETCH),
+                                ("megakernel_empty_framework", run_mk, mk.MK_FLAG_NOOP_ONLY)):
+            _log(f"bench: {name}")
+            with torch.cuda.stream(stream):
+                variants[name] = round(timed(fn, plan(flags), max(10, args.steps // 2), 3) * 1000.0, 3)
+    ab = algorithmic_bytes(cfg)
+    nbytes = ab["total"]
+    step_us = ms * 1000.0
+    layers = cfg.num_layers
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "us per decode layer-step and achieved HBM GB/s (% of MI355X peak)",
+        "value": round(step_us / layers, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random weights and KV caches of the workload's shapes)",
+        "config": {"workload": cfg.name, "layers": layers, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "batch": cfg.n_requests, "context": cfg.context, "page_size": cfg.page_size,
+                   "vocab": cfg.vocab, "rotation_copies": rotate, "workers": int(p0.queue().shape[0])},
+        "step_us": round(step_us, 3),
+        "achieved_GBps": round(achieved, 1),
+        "hbm_frac_of_8TBps": round(achieved / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "mk_worker (persistent megakernel, one launch per step)"},
+        "variants_us_per_step": variants,
+    }
+    if variants:
+        out["gain_split_us"] = {
+            "branch_parallelism": round(variants["graph_single_stream"] - variants["graph_multi_stream"], 3),
+            "in_kernel_scheduling": round(variants["graph_multi_stream"] - step_us, 3),
+            "prefetch": round(variants["megakernel_no_prefetch"] - step_us, 3),
+        }
+    if not args.no_cpu_baseline:
+        _log("bench: CPU oracle baseline")
+        from oracle import model as omodel
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = os.cpu_count() or 1
+        t0 = time.perf_counter()
+        if step:
+            omodel.run_qwen3_step(cfg, inp)
+        else:
+            omodel.run_qwen3_layer(cfg, inp)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(dt * 1e6 / layers, 1), "unit": "us/layer-step", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"one full pass of {cfg.name} ({layers} layer(s){' + lm_head' if step else ''}) "
+                                         f"in float64 NumPy, {dt:.1f} s wall, host cpu_count {os.cpu_count()}"}
+    print(json.dumps(out), flush=True)
+    for p in plans.values():
+        p.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

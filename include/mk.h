@@ -138,8 +138,11 @@ mk_status mk_run_graph_baseline(mk_plan* plan, const mk_tensors* tensors, int32_
  * MK_ERR_TIMEOUT if a worker's watchdog expired (counters are then reset). */
 mk_status mk_sync(mk_plan* plan, void* hip_stream);
 
-/* Copy the trace (uint32 [W, L, 4]: visible, input-ready, done timestamps of the 100 MHz
- * realtime clock, and the poll-wait cycles) of the last MK_FLAG_TRACE run into host memory. */
+/* Copy the trace of the last MK_FLAG_TRACE megakernel run into host memory: uint32 [W, L, 16]
+ * per instruction: low 32 bits of the 100 MHz realtime clock when the controller saw it, when
+ * its waits were met, when its activations were staged, after the compute start / end
+ * barriers, when its outputs were acknowledged, when its arrival resolved (0 if none), when it
+ * was done; word 8 holds the ticks spent polling; the rest are zero. */
 mk_status mk_read_trace(const mk_plan* plan, uint32_t* host_out, size_t n_words);
 
 const char* mk_last_error(void);

@@ -7,10 +7,6 @@ microseconds; launching kernel by kernel without a graph costs 5 us of CPU time 
 kernel.  The per-layer kernel list fuses residual-add + RMSNorm and QK-norm + RoPE,
 as vLLM does; the tail is final norm, lm_head and sampling.
 
-``algorithmic_bytes`` is what one pass of the path must move at least: every weight,
-scale and norm gain once, the prior KV (or indexer keys) once, the new cache rows,
-the layer's external inputs and outputs.  Intermediates and redundant re-reads are
-excluded.
 """
 from __future__ import annotations
 
@@ -60,41 +56,3 @@ def decode_estimate(model_name: str, batch: int, context: int, gaps_us=(0.5, 1.0
            "small_kernels": sum(1 for _, b in ks if b / bw * 1e6 < 1.0),
            "mean_kernel_us": t_data / n}
     return res
-
-
-def algorithmic_bytes(cfg) -> Dict[str, int]:
-    """Minimum bytes one pass of the workload moves (see module docstring)."""
-    parts: Dict[str, int] = {}
-    if cfg.workload in ("qwen3_layer", "qwen3_step"):
-        H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
-        nq, nkv = cfg.n_q_heads * d, cfg.n_kv_heads * d
-        L, M = cfg.num_layers, cfg.m
-        wel = 1 if cfg.weight_fp8 else 2
-        mats = [(nq + 2 * nkv, H), (H, nq), (2 * I, H), (H, I)]
-        parts["weights"] = L * sum(n * k * wel for n, k in mats)
-        if cfg.weight_fp8:
-            parts["scales"] = L * sum((-(-n // 128)) * (-(-k // 128)) * 4 for n, k in mats)
-        parts["norms"] = L * (2 * H + 2 * d) * 2
-        prior = cfg.n_requests * (cfg.context - 1)
-        parts["kv_read"] = L * prior * 2 * nkv * 2
-        parts["kv_write"] = L * cfg.n_requests * 2 * nkv * 2
-        parts["act_in"] = M * H * (2 + 4)
-        if cfg.workload == "qwen3_step":
-            parts["lm_head"] = cfg.vocab * H * 2 + H * 2
-            parts["logits_out"] = M * cfg.vocab * 4 + M * 4
-        else:
-            parts["act_out"] = M * H * (2 + 4)
-    elif cfg.workload == "indexer_front":
-        H, qr, nh, hd = cfg.hidden, cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
-        mats = [(qr, H), (nh, H), (hd, H), (nh * hd, qr)]
-        parts["weights"] = sum(n * k for n, k in mats)
-        parts["scales"] = sum((-(-n // 128)) * (-(-k // 128)) * 4 for n, k in mats)
-        parts["norms"] = (H + qr) * 2
-        M = cfg.m
-        prior = cfg.n_requests * (cfg.context - cfg.tokens_per_request)
-        parts["keys_read"] = prior * (hd + 4)
-        parts["keys_write"] = M * (hd + 4)
-        parts["act_in"] = M * H * (2 + 4)
-        parts["score_out"] = M * cfg.context * 4
-    parts["total"] = sum(parts.values())
-    return parts

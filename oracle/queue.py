@@ -65,17 +65,21 @@ def tile_params(cfg, W: int, ctx_lens) -> Dict[str, int]:
     elem = 1 if cfg.weight_fp8 else 2
     n_qkv = (Hq + 2 * Hkv) * d
 
-    def cap_rows(k: int, nmat: int) -> int:
-        return max(1, LEASE_BYTES // (k * elem * nmat))
+    # rows of one tile: the LDS lease (weights, plus the 1 KiB-rounded norm gain of the fused
+    # add + RMSNorm ops) stays within LEASE_BYTES
+    gain = -(-2 * H // 1024) * 1024
+
+    def cap_rows(k: int, nmat: int, extra: int) -> int:
+        return max(1, (LEASE_BYTES - extra) // (k * elem * nmat))
 
     p = {}
-    p["r_qkv"] = _pow2floor(min(d, max(1, n_qkv // W), cap_rows(H, 1)))
-    p["r_o"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(Hq * d, 1)))
-    p["r_gu"] = _largest_divisor_le(I, min(max(1, I // W), cap_rows(H, 2)))
-    p["r_down"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(I, 1)))
-    p["r_lm"] = min(cfg.vocab, cap_rows(H, 1), 64) if cfg.workload == "qwen3_step" else 0
+    p["r_qkv"] = _pow2floor(min(d, max(1, n_qkv // W), cap_rows(H, 1, gain)))
+    p["r_o"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(Hq * d, 1, 0)))
+    p["r_gu"] = _largest_divisor_le(I, min(max(1, I // W), cap_rows(H, 2, gain + 1024)))
+    p["r_down"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(I, 1, 0)))
+    p["r_lm"] = min(cfg.vocab, cap_rows(H, 1, gain), 64) if cfg.workload == "qwen3_step" else 0
     ctx_max = int(max(ctx_lens))
-    want = -(-(R * ctx_max * Hkv) // W)
+    want = -(-(2 * R * ctx_max * Hkv) // W)  # about W/2 attention tasks
     p["s_tok"] = max(4, min(LEASE_BYTES // (4 * d), _pow2ceil(max(1, want))))
     p["spec"] = 0 if cfg.m == 1 else 1
     return p

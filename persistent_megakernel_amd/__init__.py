@@ -165,7 +165,7 @@ class Plan:
     def read_trace(self) -> np.ndarray:
         q = self.queue()
         W, L = q.shape[:2]
-        out = np.zeros((W, L, 4), dtype=np.uint32)
+        out = np.zeros((W, L, 16), dtype=np.uint32)
         _check(_lib.mk_read_trace(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), out.size),
                "mk_read_trace")
         return out

@@ -177,9 +177,9 @@ mk_status check_runnable(mk_plan* p) {
   const mk_config& c = hp.cfg;
   if (hp.tp.spec != 0 || c.weight_fp8 || c.act_fp8)
     return fail(MK_ERR_UNSUPPORTED, "only the bf16 single-token (M = 1) op bodies are built");
-  if (c.hidden > 8192 || c.inter > 8192 || c.n_q_heads * c.head_dim > 8192 ||
-      hp.max_splits * (c.n_q_heads / c.n_kv_heads) > 2048)
-    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden, inter, q width <= 8192; KV splits x GQA group <= 2048)");
+  if (c.hidden > 3072 || c.inter > 8192 || c.n_q_heads * c.head_dim > 8192 || hp.tp.r_o > 256 ||
+      c.n_q_heads / c.n_kv_heads > mk::dev::kMaxG)
+    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 3072; inter, q width <= 8192; GQA group <= 5)");
   if (!p->occupancy_checked) {
     int per_cu = 0;
     HIP_TRY(hipSetDevice(p->device));
@@ -265,8 +265,8 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
   HIP_TRY(hipMalloc(&p->d_rope, rope.size() * 4));
   HIP_TRY(hipMemcpy(p->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
   if (c.flags & MK_FLAG_TRACE) {
-    HIP_TRY(hipMalloc(&p->d_trace, (size_t)hp.W * hp.L * 16));
-    HIP_TRY(hipMemset(p->d_trace, 0, (size_t)hp.W * hp.L * 16));
+    HIP_TRY(hipMalloc(&p->d_trace, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
+    HIP_TRY(hipMemset(p->d_trace, 0, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
   }
   *out = p.release();
   return MK_OK;
@@ -430,7 +430,7 @@ mk_status mk_sync(mk_plan* p, void* stream) {
 mk_status mk_read_trace(const mk_plan* p, uint32_t* out, size_t n_words) {
   if (!p || !out) return fail(MK_ERR_INVALID, "null argument");
   if (!p->d_trace) return fail(MK_ERR_INVALID, "plan was not built with MK_FLAG_TRACE");
-  const size_t have = (size_t)p->hp.W * p->hp.L * 4;
+  const size_t have = (size_t)p->hp.W * p->hp.L * mk::kTraceWords;
   HIP_TRY(hipMemcpy(out, p->d_trace, std::min(have, n_words) * 4, hipMemcpyDeviceToHost));
   return MK_OK;
 }

@@ -22,13 +22,14 @@ struct KArgs {
   uint32_t* events;        // [E][kNSub sub-counters, kSubStride words apart]
   uint32_t* arrivals;      // [A], kSubStride words apart, self re-arming
   uint32_t* err;           // device error record: flag, worker, task, event, value, target
-  uint32_t* trace;         // [W, L, 4] or null
+  uint32_t* trace;         // [W, L, kTraceWords] or null
   uint32_t epoch;          // runs of this plan so far: a wait on threshold t targets (epoch+1)*t
   uint32_t flags;          // MK_FLAG_* | kModeGraph
   Shapes sh;
 };
 
 constexpr uint32_t kModeGraph = 1u << 16;
+constexpr int kTraceWords = 16;  // per instruction: visible, ready, prologue, A, B, stored, arrived, done, poll
 constexpr int kNSub = 16;                  // sub-counters per event (spreads the atomics)
 constexpr int kSubStride = 32;             // words between sub-counters (128 bytes)
 constexpr int kEvStride = kNSub * kSubStride;
@@ -40,21 +41,26 @@ constexpr int kNCW = 7;
 constexpr int kNPages = 8;     // LDS ring of 8 x 16 KiB pages
 constexpr int kRingOff = 0;
 constexpr int kActOff = kNPages * 16384;   // activation staging
-constexpr int kActBytes = 22528;
+constexpr int kActBytes = 27648;
+constexpr int kActStageBytes = kActBytes;  // largest staged block (a 1 KiB multiple)
 constexpr int kOutOff = kActOff + kActBytes;  // compute results
-constexpr int kOutBytes = 8192;
+constexpr int kOutBytes = 4096;  // g*128 + g floats of an attention partial: GQA group <= 7
 constexpr int kCtrlOff = kOutOff + kOutBytes;  // abort flag + per-wave lease tables
 constexpr int kCtrlBytes = 1024;
-constexpr int kLdsBytes = kCtrlOff + kCtrlBytes;  // 162816 of 163840: one block per CU
+constexpr int kLdsBytes = kCtrlOff + kCtrlBytes;  // all 160 KiB: one block per CU
 // attention sub-areas of the activation staging area
-constexpr int kActQ = 0;       // bf16 [g <= 8][128]
+constexpr int kMaxG = 5;       // GQA group (q heads per kv head) of the M = 1 attention body
+constexpr int kActQ = 0;       // bf16 [g][128] rotated q heads
 constexpr int kActK = 2048;    // bf16 [128] new key
 constexpr int kActV = 2304;    // bf16 [128] new value
-constexpr int kActS = 2560;    // fp32 [g][kSStride] scores / probabilities
-constexpr int kSStride = 132;
-constexpr int kActStat = 6784;  // fp32 [g][2] max, sum
-constexpr int kActRed = 7168;   // fp32 [TG][g][128] PV partials (<= 14336 bytes)
-static_assert(kActRed + 14336 <= kActBytes, "attention staging overflows");
+constexpr int kActMerge = 2560;  // fp32 [7 waves][g][130] per-wave softmax states (<= 18200 bytes)
+constexpr int kAttQraw = 21504;  // fp32 staging of the raw q heads (4 KiB), k and v (1 KiB each)
+constexpr int kAttKraw = 25600;
+constexpr int kAttVraw = 26624;
+constexpr int kActR1 = 16384;   // O projection: fp32 r_in + x of the tile's rows (<= 256)
+static_assert(kActMerge + 7 * kMaxG * 130 * 4 <= kAttQraw, "attention staging overlaps");
+static_assert(kAttVraw + 1024 <= kActBytes, "attention staging overflows");
+static_assert(kLdsBytes == 163840, "LDS budget");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 }  // namespace dev
 

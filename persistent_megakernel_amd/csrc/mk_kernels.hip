@@ -41,17 +41,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 // ---------------------------------------------------------------------------------------
 // small helpers
 DEV uint32_t lane() { return __lane_id(); }
+// a value every lane of the wave holds (e.g. read back from a per-wave LDS table), made uniform
+DEV uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 DEV unsigned long long rtc() { return __builtin_amdgcn_s_memrealtime(); }
 
 DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-DEV uint32_t f2bf(float f) {  // round to nearest even
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 // bf16 pair view of a 32-bit word.  (A bit_cast of an ext-vector element is taken from
 // element 0 by this compiler, so the word is copied out first.)
+// two fp32 to packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32 on gfx950)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+DEV uint32_t pack_bf2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  const bf16x2 h = __builtin_convertvector(v, bf16x2);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
 DEV bf16x2 as_bf2(uint32_t v) {
   bf16x2 r;
   __builtin_memcpy(&r, &v, 4);
@@ -65,13 +70,17 @@ DEV float dot8(u32x4 w, u32x4 x, float acc) {
   return acc;
 }
 
-// Wave reductions: DPP within rows of 16 lanes (quad xor 1, quad xor 2, half-row mirror,
-// row mirror leave every lane of a row holding the row total), ds_swizzle xor 16 for pairs of
-// rows, then the two 32-lane halves through readlane.
+// Wave reductions without the LDS pipe: DPP within rows of 16 lanes (quad xor 1, quad xor 2,
+// half-row mirror, row mirror leave every lane of a row holding the row total), then
+// row_bcast:15 / row_bcast:31 accumulate the four rows into lane 63.
 template <int CTRL>
 DEV float dppf(float v) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false)); }
 template <int CTRL>
 DEV int dppi(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
+template <int CTRL, int ROWS>
+DEV float dpp_rows(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
 DEV float row16_sum(float v) {
   v += dppf<0xB1>(v);
   v += dppf<0x4E>(v);
@@ -81,18 +90,31 @@ DEV float row16_sum(float v) {
 }
 DEV float wave_sum(float v) {
   v = row16_sum(v);
-  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  v += dpp_rows<0x142, 0xA>(0.f, v);
+  v += dpp_rows<0x143, 0xC>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 DEV float wave_max(float v) {
   v = fmaxf(v, dppf<0xB1>(v));
   v = fmaxf(v, dppf<0x4E>(v));
   v = fmaxf(v, dppf<0x141>(v));
   v = fmaxf(v, dppf<0x140>(v));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
-  return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
-               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
+  v = fmaxf(v, dpp_rows<0x142, 0xA>(v, v));
+  v = fmaxf(v, dpp_rows<0x143, 0xC>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// the same lane position summed over the four 16-lane rows (gfx950 cross-row lane swaps)
+DEV float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float p = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+DEV float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float p = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 DEV uint32_t wave_sum_u32(uint32_t v) {
   int x = (int)v;
@@ -100,28 +122,21 @@ DEV uint32_t wave_sum_u32(uint32_t v) {
   x += dppi<0x4E>(x);
   x += dppi<0x141>(x);
   x += dppi<0x140>(x);
-  x += __builtin_amdgcn_ds_swizzle(x, 0x401F);
-  return (uint32_t)(__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 32));
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
 }
 
-// Scalar loads of data that no one writes during a run (queue, pointer table, block table):
-// they go through the scalar cache and the lgkm counter, leaving the vector-memory counter
-// to the prefetch accounting.
-DEV uint32_t s_ld32(const void* p) {
-  uint32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
+// Loads of data that no one writes during a run (queue, pointer table, block table) go through
+// the constant address space: uniform addresses become scalar loads (scalar cache, lgkm
+// counter), which leaves the vector-memory counter to the prefetch accounting.
+template <typename T>
+DEV T c_ld(const void* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
 }
-DEV uint64_t s_ld64(const void* p) {
-  uint64_t v;
-  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
-DEV u32x8 s_ld256(const void* p) {
-  u32x8 v;
-  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
+DEV uint32_t s_ld32(const void* p) { return c_ld<uint32_t>(p); }
+DEV uint64_t s_ld64(const void* p) { return c_ld<uint64_t>(p); }
+DEV u32x8 s_ld256(const void* p) { return c_ld<u32x8>(p); }
 
 struct Instr {
   uint32_t w[32];
@@ -220,276 +235,323 @@ DEV void wait_vm_le(uint32_t n) {
   }
 }
 
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.  Written
+// as inline assembly so that the compiler does not track these loads: it cannot tell which
+// LDS pages they write and would otherwise wait for every outstanding prefetch before any
+// LDS read.  The per-wave issue counts and wait_vm_le() order them instead.
+// M0 (the LDS base of the transfer, read at issue) is saved and restored around it.
+DEV void lds_dma16(const void* src, uint32_t lds_base) {
+  lds_base = uni(lds_base);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds_base), "v"(src)
+               : "memory");
+}
+
 DEV uint32_t ring_off(uint32_t lease, uint32_t off) {
   return (((lease + (off >> 14)) & (kNPages - 1)) << 14) | (off & 16383u);
 }
 
 // ---------------------------------------------------------------------------------------
 // prefetch descriptors: what an instruction streams into its LDS lease, in 1 KiB blocks
+// An instruction's lease holds up to five spans, each starting on a 1 KiB block:
+//   QKV, LM_HEAD: weight rows | norm gain       GATE_UP: gate rows | up rows | norm gain
+//   O_PROJ, DOWN: weight rows                   ATTN: K rows | V rows | q gain | k gain | RoPE row
+// Attention K / V spans are gathered token by token through the block table.
+constexpr int kMaxSpans = 5;
 struct Pf {
-  const char* s0;  // span 0 base (or K cache base)
-  const char* s1;  // span 1 base (or V cache base)
-  uint32_t len0, len1, nb0, nblk;
+  const char* src[kMaxSpans];
+  uint32_t len[kMaxSpans];
+  uint32_t blk[kMaxSpans + 1];  // first block of each span; blk[n] = total blocks
+  int n;
+  bool attn;
   const int32_t* bt;  // attention: block-table row of the request
   int t0, nk, hk;
-  bool attn;
 };
 DEV uint32_t blocks_of(uint32_t bytes) { return (bytes + 1023u) >> 10; }
+
+// span k of the descriptor (k is a compile-time constant at every call: no indexed registers)
+template <int K>
+DEV void pf_set(Pf& pf, const void* src, uint32_t bytes) {
+  pf.src[K] = (const char*)src;
+  pf.len[K] = bytes;
+  pf.blk[K + 1] = pf.blk[K] + blocks_of(bytes);
+  pf.n = K + 1;
+}
 
 DEV void pf_desc(const KArgs& a, const Instr& in, Pf& pf) {
   const uint32_t op = in.w[W_OPCODE];
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const Shapes& sh = a.sh;
-  pf.attn = false;
-  pf.s1 = nullptr;
-  pf.len1 = 0;
-  if (op == OP_ATTN) {
+  pf.blk[0] = 0;
+  pf.attn = op == OP_ATTN;
+  if (pf.attn) {
     const int r = in.w[W_P1], hk = in.w[W_P2], s = in.w[W_P3];
     const int t0 = in.w[W_P4], t1 = in.w[W_P5];
     const bool last = s == (int)in.w[W_ARR_N] - 1;
-    pf.attn = true;
-    pf.s0 = (const char*)s_ld64(row + ATT_KC);
-    pf.s1 = (const char*)s_ld64(row + ATT_VC);
     pf.bt = (const int32_t*)s_ld64(row + ATT_BT) + (size_t)r * sh.maxp;
     pf.t0 = t0;
     pf.hk = hk;
     pf.nk = (last ? t1 - 1 : t1) - t0;
-    pf.len0 = (uint32_t)pf.nk * 256u;
-    pf.nb0 = blocks_of(pf.len0);
-    pf.nblk = 2 * pf.nb0;
+    pf_set<0>(pf, (const void*)s_ld64(row + ATT_KC), (uint32_t)pf.nk * 256u);
+    pf_set<1>(pf, (const void*)s_ld64(row + ATT_VC), (uint32_t)pf.nk * 256u);
+    pf_set<2>(pf, (const void*)s_ld64(row + ATT_GQ), 256u);
+    pf_set<3>(pf, (const void*)s_ld64(row + ATT_GK), 256u);
+    pf_set<4>(pf, (const float*)s_ld64(row + ATT_ROPE) + (size_t)r * 128, 512u);
     return;
   }
   const char* w = (const char*)s_ld64(row + 0);
   const uint32_t n0 = in.w[W_P1], nr = in.w[W_P2], K = in.w[W_P4];
   const uint32_t rowb = K * 2u;
-  pf.s0 = w + (size_t)n0 * rowb;
-  pf.len0 = nr * rowb;
-  pf.nb0 = blocks_of(pf.len0);
-  pf.nblk = pf.nb0;
+  pf_set<0>(pf, w + (size_t)n0 * rowb, nr * rowb);
   if (op == OP_GATEUP) {
-    pf.s1 = w + (size_t)(sh.I + n0) * rowb;
-    pf.len1 = pf.len0;
-    pf.nblk = pf.nb0 + blocks_of(pf.len1);
+    pf_set<1>(pf, w + (size_t)(sh.I + n0) * rowb, nr * rowb);
+    pf_set<2>(pf, (const void*)s_ld64(row + GU_GAMMA), 2u * (uint32_t)sh.H);
+  } else if (op == OP_QKV || op == OP_LMHEAD) {
+    pf_set<1>(pf, (const void*)s_ld64(row + (op == OP_QKV ? QKV_GAMMA : LM_GAMMA)), 2u * (uint32_t)sh.H);
   }
 }
 
 // issue this wave's share (blocks b = cw mod 7) of an instruction's prefetch into its lease
 DEV void pf_issue(const KArgs& a, const Pf& pf, uint32_t lease, int cw, uint32_t& issued, char* smem) {
   const uint32_t ln = lane();
-  for (uint32_t b = cw; b < pf.nblk; b += kNCW) {
+  const uint32_t nblk = pf.blk[0] + 0u;
+  uint32_t total = pf.blk[1];
+#pragma unroll
+  for (int q = 2; q <= kMaxSpans; ++q)
+    if (q <= pf.n) total = pf.blk[q];
+  (void)nblk;
+  for (uint32_t b = cw; b < total; b += kNCW) {
+    int k = 0;
+    const char* base = pf.src[0];
+    uint32_t b0 = 0, len = pf.len[0];
+#pragma unroll
+    for (int q = 1; q < kMaxSpans; ++q)
+      if (q < pf.n && b >= pf.blk[q]) {
+        k = q;
+        base = pf.src[q];
+        b0 = pf.blk[q];
+        len = pf.len[q];
+      }
+    const uint32_t bb = b - b0;
     const char* src;
-    if (pf.attn) {
-      const bool isv = b >= pf.nb0;
-      const uint32_t bb = isv ? b - pf.nb0 : b;
+    if (pf.attn && k < 2) {
       uint32_t u = bb * 4u + (ln >> 4);
       if (u >= (uint32_t)pf.nk) u = 4u * bb;  // beyond the tile: reload the block's first row
       const int t = pf.t0 + (int)(4u * bb);
       const int page = (int)s_ld32(pf.bt + t / a.sh.P);
       const int tt = pf.t0 + (int)u;
       const size_t rowi = ((size_t)page * a.sh.P + (tt % a.sh.P)) * a.sh.Hkv + pf.hk;
-      src = (isv ? pf.s1 : pf.s0) + rowi * 256u + (ln & 15u) * 16u;
+      src = base + rowi * 256u + (ln & 15u) * 16u;
     } else {
-      const bool sp1 = b >= pf.nb0;
-      const uint32_t bb = sp1 ? b - pf.nb0 : b;
       uint32_t off = bb * 1024u + ln * 16u;
-      const uint32_t len = sp1 ? pf.len1 : pf.len0;
       if (off >= len) off = bb * 1024u;
-      src = (sp1 ? pf.s1 : pf.s0) + off;
+      src = base + off;
     }
-    lds_void* dst = (lds_void*)(smem + kRingOff + ring_off(lease, b * 1024u));
-    __builtin_amdgcn_global_load_lds((const void*)src, dst, 16, 0, 0);
+    lds_dma16(src, (uint32_t)(uintptr_t)(lds_void*)(smem + kRingOff + ring_off(lease, b * 1024u)));
     ++issued;
   }
 }
 
+// total blocks of a descriptor
+DEV uint32_t pf_blocks(const Pf& pf) {
+  uint32_t total = pf.blk[1];
+#pragma unroll
+  for (int q = 2; q <= kMaxSpans; ++q)
+    if (q <= pf.n) total = pf.blk[q];
+  return total;
+}
+
 // ---------------------------------------------------------------------------------------
 // controller prologues (activation staging into LDS)
+//
+// Activations are staged with device-scope direct-to-LDS loads: one short loop issues every
+// 1 KiB block, then a single wait -- one memory round trip, no registers, little code.
 
-// act[e] = bf16(RMSNorm(r + x)[e] * gamma[e]) for the M = 1 row; x may be null.
-DEV void norm_prologue(const uint16_t* x, const float* r, const uint16_t* gamma, int H, float eps, char* act) {
-  constexpr int MAXC = 16;  // hidden <= 8192
+DEV void lds_dma16_sc1(const void* src, uint32_t lds_base) {
+  lds_base = uni(lds_base);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off sc1\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds_base), "v"(src)
+               : "memory");
+}
+// copy `bytes` (16-byte aligned source) into LDS at `dst`; the destination region must extend to
+// the next 1 KiB boundary (lanes past the end reload the block's first 16 bytes there)
+DEV void stage(const void* src, uint32_t bytes, char* dst) {
   const uint32_t ln = lane();
-  const int nch = (H + 511) / 512;
-  __amdgpu_buffer_rsrc_t rx = rsrc(x), rr = rsrc(r), rg = rsrc(gamma);
-  float v[MAXC][8];
-  float ss = 0.f;
+  for (uint32_t b = 0; b < bytes; b += 1024u) {
+    uint32_t off = b + ln * 16u;
+    if (off >= bytes) off = b;
+    lds_dma16_sc1((const char*)src + off, (uint32_t)(uintptr_t)(lds_void*)(dst + b));
+  }
+}
+DEV uint32_t kb_round(uint32_t bytes) { return (bytes + 1023u) & ~1023u; }
+
+// fused add + RMSNorm inputs: x (bf16, may be null) at act[0, 2H), the residual r (fp32) at
+// act + kb_round(2H); the compute waves normalise with the gain from their prefetch
+DEV void norm_stage(const uint16_t* x, const float* r, int H, char* act) {
+  if (x) stage(x, 2u * H, act);
+  stage(r, 4u * H, act + kb_round(2u * H));
+  wait_vm0();
+}
+
+// O projection: act = o (bf16), and r1 = r_in + x of the tile's rows at act + kActR1 (fp32);
+// the few residual values ride in the same round trip as the staging
+DEV void oproj_prologue(const Instr& in, const uint64_t* row, int n, char* act) {
+  const int n0 = in.w[W_P1], nr = in.w[W_P2];
+  stage((const void*)s_ld64(row + O_IN), 2u * n, act);
+  __amdgpu_buffer_rsrc_t rx = rsrc((const void*)s_ld64(row + O_X));
+  __amdgpu_buffer_rsrc_t rr = rsrc((const void*)s_ld64(row + O_RIN));
+  float xr[4], rv[4];
 #pragma unroll
-  for (int k = 0; k < MAXC; ++k) {
-    const int e = 512 * k + 8 * (int)ln;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[k][j] = 0.f;
-    if (k < nch && e < H) {
-      u32x4 ra = ld128(rr, e * 4), rb = ld128(rr, e * 4 + 16);
-      float rv[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
-                     __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
-      if (x) {
-        u32x4 xv = ld128(rx, e * 2);
-        uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          rv[2 * j] += bf2f(xs[j] & 0xffffu);
-          rv[2 * j + 1] += bf2f(xs[j] >> 16);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v[k][j] = rv[j];
-        ss += rv[j] * rv[j];
-      }
+  for (int q = 0; q < 4; ++q) {
+    const int jj = (int)lane() + 64 * q;
+    if (jj < nr) {
+      xr[q] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rx, (uint32_t)(n0 + jj) * 2u, 0, SC1));
+      rv[q] = __uint_as_float(ld32(rr, (uint32_t)(n0 + jj) * 4u));
     }
   }
-  ss = wave_sum(ss);
-  const float inv = rsqrtf(ss / (float)H + eps);
+  wait_vm0();
+  float* r1 = (float*)(act + kActR1);
 #pragma unroll
-  for (int k = 0; k < MAXC; ++k) {
-    const int e = 512 * k + 8 * (int)ln;
-    if (k < nch && e < H) {
-      u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(rg, e * 2, 0, 0);
-      uint32_t gs[4] = {gv.x, gv.y, gv.z, gv.w};
-      u32x4 o;
-      uint32_t os[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float h0 = v[k][2 * j] * inv * bf2f(gs[j] & 0xffffu);
-        const float h1 = v[k][2 * j + 1] * inv * bf2f(gs[j] >> 16);
-        os[j] = f2bf(h0) | (f2bf(h1) << 16);
-      }
-      o.x = os[0]; o.y = os[1]; o.z = os[2]; o.w = os[3];
-      *(u32x4*)(act + e * 2) = o;
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int jj = (int)lane() + 64 * q;
+    if (jj < nr) r1[jj] = rv[q] + xr[q];
   }
 }
 
-// act[0 .. n) = bf16 vector copied from device memory (n <= 8192); all loads issue first
-DEV void copy_prologue(const uint16_t* src, int n, char* act) {
-  constexpr int MAXC = 16;
-  __amdgpu_buffer_rsrc_t rs = rsrc(src);
-  u32x4 v[MAXC];
-#pragma unroll
-  for (int k = 0; k < MAXC; ++k) {
-    const int e = 512 * k + 8 * (int)lane();
-    if (e < n) v[k] = ld128(rs, e * 2);
-  }
-#pragma unroll
-  for (int k = 0; k < MAXC; ++k) {
-    const int e = 512 * k + 8 * (int)lane();
-    if (e < n) *(u32x4*)(act + e * 2) = v[k];
-  }
-}
-
-// attention: QK-norm + RoPE of the group's q heads and k head, bf16 q / k / v into LDS; the
-// last split also writes the new k / v row into the paged caches.
-DEV void attn_prologue(const KArgs& a, const Instr& in, char* act) {
+// attention: the raw (fp32) q heads of the group and its k / v heads into LDS
+DEV void attn_stage(const KArgs& a, const Instr& in, char* act) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
-  const int r = in.w[W_P1], hk = in.w[W_P2], s = in.w[W_P3], t1 = in.w[W_P5];
-  const bool last = s == (int)in.w[W_ARR_N] - 1;
+  const int r = in.w[W_P1], hk = in.w[W_P2];
   const float* qkv = (const float*)s_ld64(row + ATT_QKV) + (size_t)r * sh.n_qkv;
-  const uint16_t* gq = (const uint16_t*)s_ld64(row + ATT_GQ);
-  const uint16_t* gk = (const uint16_t*)s_ld64(row + ATT_GK);
-  const float* rope = (const float*)s_ld64(row + ATT_ROPE) + (size_t)r * 128;
-  __amdgpu_buffer_rsrc_t rq = rsrc(qkv), rgq = rsrc(gq), rgk = rsrc(gk), rro = rsrc(rope);
-  const uint32_t i = lane();  // dims i and i + 64
-  const float c = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rro, i * 8, 0, 0));
-  const float sn = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rro, i * 8 + 4, 0, 0));
-  uint16_t* qs = (uint16_t*)(act + kActQ);
-  // vectors j < g: the group's q heads; j == g: its k head; j == g + 1: its v head
-  float x0v[10], x1v[10];
-#pragma unroll
-  for (int j = 0; j < 10; ++j) {
-    if (j <= sh.g + 1) {
-      const int col = j < sh.g ? (hk * sh.g + j) * 128 : (j == sh.g ? (sh.Hq + hk) * 128 : (sh.Hq + sh.Hkv + hk) * 128);
-      x0v[j] = __uint_as_float(ld32(rq, (col + i) * 4));
-      x1v[j] = __uint_as_float(ld32(rq, (col + i + 64) * 4));
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 9; ++j) {
-    if (j > sh.g) break;
-    const bool isk = j == sh.g;
-    const float x0 = x0v[j], x1 = x1v[j];
-    const float ss = wave_sum(x0 * x0 + x1 * x1);
-    const float inv = rsqrtf(ss / 128.f + sh.eps);
-    __amdgpu_buffer_rsrc_t rg = isk ? rgk : rgq;
-    const uint32_t g01 = __builtin_amdgcn_raw_buffer_load_b16(rg, i * 2, 0, 0);
-    const uint32_t g23 = __builtin_amdgcn_raw_buffer_load_b16(rg, (i + 64) * 2, 0, 0);
-    const float n0 = x0 * inv * bf2f(g01), n1 = x1 * inv * bf2f(g23);
-    const float o0 = n0 * c - n1 * sn, o1 = n1 * c + n0 * sn;
-    uint16_t* dst = isk ? (uint16_t*)(act + kActK) : qs + j * 128;
-    dst[i] = (uint16_t)f2bf(o0);
-    dst[i + 64] = (uint16_t)f2bf(o1);
-  }
-  {
-    uint16_t* dv = (uint16_t*)(act + kActV);
-    float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 10; ++j)
-      if (j == sh.g + 1) {
-        v0 = x0v[j];
-        v1 = x1v[j];
-      }
-    dv[i] = (uint16_t)f2bf(v0);
-    dv[i + 64] = (uint16_t)f2bf(v1);
-  }
-  if (last) {
-    const int p = t1 - 1;
-    const int32_t* bt = (const int32_t*)s_ld64(row + ATT_BT) + (size_t)r * sh.maxp;
-    const int page = (int)s_ld32(bt + p / sh.P);
-    const size_t rowi = ((size_t)page * sh.P + (p % sh.P)) * sh.Hkv + hk;
-    uint16_t* kc = (uint16_t*)s_ld64(row + ATT_KC) + rowi * 128;
-    uint16_t* vc = (uint16_t*)s_ld64(row + ATT_VC) + rowi * 128;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS writes above are done
-    const uint16_t* kl = (const uint16_t*)(act + kActK);
-    const uint16_t* vl = (const uint16_t*)(act + kActV);
-    __amdgpu_buffer_rsrc_t rk = rsrc(kc), rv = rsrc(vc);
-    st16(rk, i * 2, kl[i]);
-    st16(rk, (i + 64) * 2, kl[i + 64]);
-    st16(rv, i * 2, vl[i]);
-    st16(rv, (i + 64) * 2, vl[i + 64]);
-  }
+  stage(qkv + (size_t)hk * sh.g * 128, (uint32_t)sh.g * 512u, act + kAttQraw);
+  stage(qkv + (size_t)(sh.Hq + hk) * 128, 512u, act + kAttKraw);
+  stage(qkv + (size_t)(sh.Hq + sh.Hkv + hk) * 128, 512u, act + kAttVraw);
+  wait_vm0();
 }
 
 // ---------------------------------------------------------------------------------------
 // compute bodies (waves 1..7; cw = 0..6)
 
 // out[j] = sum_k act[k] * W[row j][k]; rows [0, nr0) at j * rowb, rows [nr0, nrows) at off1.
-DEV void gemv(const char* smem, uint32_t lease, int nrows, int nr0, uint32_t off1, int K, int cw, float* out) {
+// Fused add + RMSNorm of the staged inputs: h = bf16(RMSNorm(r + x) * gamma) into LDS at hoff.
+// Every wave takes the full sum of squares (cheap), then the waves split the chunks of h.
+// The caller follows with a barrier before the projection reads h.
+// HAS_X = false (the MLP norm, whose input is the residual alone) never touches the x area,
+// which nothing has staged for such a tile.
+template <bool HAS_X>
+DEV void norm_h(const char* smem, uint32_t lease, uint32_t goff, int H, float eps, int cw, uint32_t hoff) {
+  const int ln = (int)lane();
+  const int nk8 = H / 8;
+  const char* act = smem + kActOff;
+  const char* ring = smem + kRingOff;
+  const uint32_t R0 = kb_round(2u * H);
+  float ss = 0.f;
+#pragma unroll 2
+  for (int c = ln; c < nk8; c += 64) {
+    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
+    float rv[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
+                   __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
+    if constexpr (HAS_X) {
+      const u32x4 xv = *(const u32x4*)(act + c * 16);
+      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rv[2 * q] += bf2f(xs[q] & 0xffffu);
+        rv[2 * q + 1] += bf2f(xs[q] >> 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ss += rv[q] * rv[q];
+  }
+  const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
+  for (int c = cw * 64 + ln; c < nk8; c += kNCW * 64) {
+    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
+    const u32x4 gv = *(const u32x4*)(ring + ring_off(lease, goff + (uint32_t)c * 16u));
+    float rv[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
+                   __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
+    if constexpr (HAS_X) {
+      const u32x4 xv = *(const u32x4*)(act + c * 16);
+      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rv[2 * q] += bf2f(xs[q] & 0xffffu);
+        rv[2 * q + 1] += bf2f(xs[q] >> 16);
+      }
+    }
+    const uint32_t gs[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t os[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      os[q] = pack_bf2(rv[2 * q] * inv * bf2f(gs[q] & 0xffffu), rv[2 * q + 1] * inv * bf2f(gs[q] >> 16));
+    u32x4 o;
+    o.x = os[0]; o.y = os[1]; o.z = os[2]; o.w = os[3];
+    *(u32x4*)(smem + kActOff + hoff + c * 16) = o;
+  }
+}
+
+// out[j] = sum_k h[k] * W[row j][k] with h the bf16 vector at act + hoff; rows [0, nr0) at
+// j * rowb, rows [nr0, nrows) at off1.  Rows go in groups of four consecutive rows, groups
+// round-robin over the waves; inside a group the loop body has no branches (a short last group
+// repeats its last row), so every LDS read of an iteration is in flight together.
+DEV void gemv(const char* smem, uint32_t lease, int nrows, int nr0, uint32_t off1, int K, int cw, float* out,
+              uint32_t hoff) {
   const int ln = (int)lane();
   const uint32_t rowb = (uint32_t)K * 2u;
   const int nk8 = K / 8;
-  const char* act = smem + kActOff;
+  const char* act = smem + kActOff + hoff;
   const char* ring = smem + kRingOff;
-  for (int r0 = cw; r0 < nrows; r0 += kNCW * 4) {
+  for (int r0 = cw * 4; r0 < nrows; r0 += kNCW * 4) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     uint32_t rb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = r0 + kNCW * j;
+      const int r = min(r0 + j, nrows - 1);
       rb[j] = r < nr0 ? (uint32_t)r * rowb : off1 + (uint32_t)(r - nr0) * rowb;
     }
+#pragma unroll 2
     for (int c = ln; c < nk8; c += 64) {
       const u32x4 x = *(const u32x4*)(act + c * 16);
+      u32x4 wv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (r0 + kNCW * j < nrows) {
-          const u32x4 wv = *(const u32x4*)(ring + ring_off(lease, rb[j] + (uint32_t)c * 16u));
-          acc[j] = dot8(wv, x, acc[j]);
-        }
-      }
+      for (int j = 0; j < 4; ++j) wv[j] = *(const u32x4*)(ring + ring_off(lease, rb[j] + (uint32_t)c * 16u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = dot8(wv[j], x, acc[j]);
     }
+    float sm[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = r0 + kNCW * j;
-      if (r < nrows) {
-        const float s = wave_sum(acc[j]);
-        if (ln == 0) out[r] = s;
-      }
+    for (int j = 0; j < 4; ++j) sm[j] = wave_sum(acc[j]);
+    if (ln == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (r0 + j < nrows) out[r0 + j] = sm[j];
     }
   }
 }
 
-// split-KV attention partial for one (request, kv head, split): g query heads.
-// inner barriers: 3 (scores | softmax | PV partials | reduce)
+// split-KV attention partial for one (request, kv head, split) over its g query heads.
+// Each 16-lane row walks its own tokens (row R of 28 takes tokens R, R + 28, ...) with an
+// online softmax (running max, sum and rescaled output, 8 dims per lane); the four rows of a
+// wave merge by lane exchange, the seven waves through LDS after one barrier.  Output: the
+// split's normalised O [g][128] and lse [g] in the output area.
+// QK-norm (RMSNorm over the 128 dims of a head, gain gn) then rotate-half RoPE of one raw fp32
+// head vector, by one wave: lane i holds the rotation pair (i, i + 64); bf16 result into dst
+DEV void qk_norm_rope(const float* raw, const char* gn, const char* rope, float eps, char* dst) {
+  const int i = (int)lane();
+  const float x0 = raw[i], x1 = raw[i + 64];
+  const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / 128.f + eps);
+  const float g0 = bf2f(*(const uint16_t*)(gn + i * 2)), g1 = bf2f(*(const uint16_t*)(gn + (i + 64) * 2));
+  const float c = *(const float*)(rope + i * 8), sn = *(const float*)(rope + i * 8 + 4);
+  const float n0 = x0 * inv * g0, n1 = x1 * inv * g1;
+  const uint32_t o = pack_bf2(n0 * c - n1 * sn, n1 * c + n0 * sn);
+  ((uint16_t*)dst)[i] = (uint16_t)(o & 0xffffu);
+  ((uint16_t*)dst)[i + 64] = (uint16_t)(o >> 16);
+}
+
 DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
   const Shapes& sh = a.sh;
   const int g = sh.g;
@@ -497,84 +559,105 @@ DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* a
   const bool last = s == (int)in.w[W_ARR_N] - 1;
   const int ntok = t1 - t0;
   const int nk = last ? ntok - 1 : ntok;
-  const uint32_t voff = blocks_of((uint32_t)nk * 256u) * 1024u;
+  const uint32_t nbk = blocks_of((uint32_t)nk * 256u);
+  const uint32_t voff = nbk * 1024u, gqoff = 2u * nbk * 1024u;  // lease: K | V | q gain | k gain | RoPE
   const char* ring = smem + kRingOff;
   const int ln = (int)lane();
-  const int gl = cw * 64 + ln;  // 0..447
-  float* sc = (float*)(act + kActS);      // [g][kSStride]
-  float* st = (float*)(act + kActStat);   // [g][2]: max, sum
-  float* red = (float*)(act + kActRed);   // [TG][g][128]
+  const int sub = ln & 15, rowid = cw * 4 + (ln >> 4);  // 28 token rows
   const float scale = sh.inv_sqrt_d;
-  // 1) scores: one (head, token) pair per 16-lane row
-  {
-    const int grp = gl >> 4, sub = ln & 15;
-    for (int pidx = grp; pidx < g * ntok; pidx += kNCW * 4) {
-      const int j = pidx / ntok, u = pidx % ntok;
-      const u32x4 qv = *(const u32x4*)(act + kActQ + j * 256 + sub * 16);
-      u32x4 kv;
-      if (u < nk) kv = *(const u32x4*)(ring + ring_off(lease, (uint32_t)u * 256u + sub * 16u));
-      else kv = *(const u32x4*)(act + kActK + sub * 16);
-      float d = row16_sum(dot8(kv, qv, 0.f));
-      if (sub == 0) sc[j * kSStride + u] = d * scale;
-    }
+  // QK-norm + RoPE once per head: wave j < g takes q head j, wave g the new key, wave g + 1 the
+  // new value (bf16); the results (also the new cache row) go to LDS before one barrier
+  if (cw < g) {
+    qk_norm_rope((const float*)(act + kAttQraw) + cw * 128, ring + ring_off(lease, gqoff),
+                 ring + ring_off(lease, gqoff + 2048u), sh.eps, act + kActQ + cw * 256);
+  } else if (cw == g) {
+    qk_norm_rope((const float*)(act + kAttKraw), ring + ring_off(lease, gqoff + 1024u),
+                 ring + ring_off(lease, gqoff + 2048u), sh.eps, act + kActK);
+  } else if (cw == g + 1) {
+    const float* vr = (const float*)(act + kAttVraw);
+    ((uint32_t*)(act + kActV))[ln] = pack_bf2(vr[2 * ln], vr[2 * ln + 1]);
   }
   lds_barrier();
-  // 2) softmax statistics per head, p = exp(s - max) in place
-  for (int j = cw; j < g; j += kNCW) {
-    float m = -INFINITY;
-    for (int u = ln; u < ntok; u += 64) m = fmaxf(m, sc[j * kSStride + u]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int u = ln; u < ntok; u += 64) {
-      const float e = __expf(sc[j * kSStride + u] - m);
-      sc[j * kSStride + u] = e;
-      l += e;
-    }
-    l = wave_sum(l);
-    if (ln == 0) {
-      st[2 * j] = m;
-      st[2 * j + 1] = l;
-    }
+  u32x4 qv[kMaxG];
+#pragma unroll
+  for (int j = 0; j < kMaxG; ++j)
+    if (j < g) qv[j] = *(const u32x4*)(act + kActQ + j * 256 + sub * 16);
+  const u32x4 knew = *(const u32x4*)(act + kActK + sub * 16);
+  const u32x4 vnew = *(const u32x4*)(act + kActV + sub * 16);
+  float m[kMaxG], l[kMaxG], acc[kMaxG][8];
+#pragma unroll
+  for (int j = 0; j < kMaxG; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[j][q] = 0.f;
   }
-  lds_barrier();
-  // 3) PV partials: unit = (head, 8 dims); TG token groups
-  {
-    const int units = g * 16;
-    const int TG = (kNCW * 64) / units;
-    const int unit = gl % units, tg = gl / units;
-    if (tg < TG) {
-      const int j = unit >> 4, c8 = unit & 15;
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int u = tg; u < ntok; u += TG) {
-        const float p = sc[j * kSStride + u];
-        u32x4 vv;
-        if (u < nk) vv = *(const u32x4*)(ring + ring_off(lease, voff + (uint32_t)u * 256u + c8 * 16u));
-        else vv = *(const u32x4*)(act + kActV + c8 * 16);
-        const uint32_t vs[4] = {vv.x, vv.y, vv.z, vv.w};
+  for (int u = rowid; u < ntok; u += kNCW * 4) {
+    u32x4 kv, vv;
+    if (u < nk) {
+      kv = *(const u32x4*)(ring + ring_off(lease, (uint32_t)u * 256u + sub * 16u));
+      vv = *(const u32x4*)(ring + ring_off(lease, voff + (uint32_t)u * 256u + sub * 16u));
+    } else {
+      kv = knew;
+      vv = vnew;
+    }
+    const uint32_t vs[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int j = 0; j < kMaxG; ++j) {
+      if (j < g) {
+        const float sc = row16_sum(dot8(kv, qv[j], 0.f)) * scale;
+        const float mn = fmaxf(m[j], sc);
+        const float c = __expf(m[j] - mn), p = __expf(sc - mn);
+        l[j] = l[j] * c + p;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += p * bf2f(vs[q] & 0xffffu);
-          acc[2 * q + 1] += p * bf2f(vs[q] >> 16);
+          acc[j][2 * q] = acc[j][2 * q] * c + p * bf2f(vs[q] & 0xffffu);
+          acc[j][2 * q + 1] = acc[j][2 * q + 1] * c + p * bf2f(vs[q] >> 16);
         }
+        m[j] = mn;
       }
-      float* dst = red + ((size_t)tg * g + j) * 128 + c8 * 8;
+    }
+  }
+  // merge the wave's four rows (lane exchange across rows), then publish per wave
+  float* mrg = (float*)(act + kActMerge);  // [wave][g][130]: m, l, O[128] (unnormalised)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dst[q] = acc[q];
+  for (int j = 0; j < kMaxG; ++j) {
+    if (j < g) {
+      // rescale every row to the wave's maximum, then sum the rows lane by lane
+      const float M = rows_max(m[j]);
+      const float e = (M == -INFINITY || m[j] == -INFINITY) ? 0.f : __expf(m[j] - M);
+      l[j] = rows_sum(l[j] * e);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[j][q] = rows_sum(acc[j][q] * e);
+      m[j] = M;
+      float* slot = mrg + ((size_t)cw * g + j) * 130;
+      if (ln < 16) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) slot[2 + sub * 8 + q] = acc[j][q];
+      }
+      if (ln == 0) {
+        slot[0] = m[j];
+        slot[1] = l[j];
+      }
     }
   }
   lds_barrier();
-  // 4) reduce token groups -> normalised O and lse into the output area
-  {
-    const int units = g * 16;
-    const int TG = (kNCW * 64) / units;
-    float* out = (float*)(smem + kOutOff);
-    for (int o = gl; o < g * 128; o += kNCW * 64) {
-      const int j = o >> 7;
-      float acc = 0.f;
-      for (int tg = 0; tg < TG; ++tg) acc += red[((size_t)tg * g + j) * 128 + (o & 127)];
-      out[o] = acc / st[2 * j + 1];
+  float* out = (float*)(smem + kOutOff);
+  for (int o = cw * 64 + ln; o < g * 128; o += kNCW * 64) {
+    const int j = o >> 7, i = o & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kNCW; ++w) M = fmaxf(M, mrg[((size_t)w * g + j) * 130]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNCW; ++w) {
+      const float* slot = mrg + ((size_t)w * g + j) * 130;
+      const float e = slot[0] == -INFINITY ? 0.f : __expf(slot[0] - M);
+      L += slot[1] * e;
+      O += slot[2 + i] * e;
     }
-    if (gl < g) out[g * 128 + gl] = st[2 * gl] + __logf(st[2 * gl + 1]);
+    out[o] = O / L;
+    if (i == 0) out[g * 128 + j] = M + __logf(L);
   }
 }
 
@@ -605,76 +688,108 @@ DEV bool arrive(const KArgs& a, const Instr& in) {
   return last;
 }
 
-DEV void attn_epilogue(const KArgs& a, const Instr& in, const char* smem) {
+// controller timestamps of one instruction (trace build)
+struct Stamps {
+  unsigned long long ack, arr;
+};
+
+DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) {
   const Shapes& sh = a.sh;
   const int g = sh.g;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int r = in.w[W_P1], hk = in.w[W_P2], s = in.w[W_P3];
   const int ns = in.w[W_ARR_N];
-  const uint32_t pstride = (uint32_t)g * 129u;  // floats per split: g*128 O + g lse
+  const uint32_t pstride = (uint32_t)g * 128u + 8u;  // floats per split: g*128 O, g lse, padding
   const uint32_t gbase = ((uint32_t)(r * sh.Hkv + hk) * (uint32_t)sh.max_splits) * pstride;
   float* part = (float*)s_ld64(row + ATT_PART);
   __amdgpu_buffer_rsrc_t rp = rsrc(part);
   const float* out = (const float*)(smem + kOutOff);
-  for (int e = (int)lane(); e < (int)pstride; e += 64)
+  for (int e = (int)lane(); e < g * 129; e += 64)
     st32(rp, (gbase + (uint32_t)s * pstride + e) * 4u, __float_as_uint(out[e]));
+  if (s == ns - 1) {  // the split holding the new token writes its K / V row into the paged caches
+    const int p = (int)in.w[W_P5] - 1;
+    const int32_t* bt = (const int32_t*)s_ld64(row + ATT_BT) + (size_t)r * sh.maxp;
+    const int page = (int)s_ld32(bt + p / sh.P);
+    const size_t rowi = ((size_t)page * sh.P + (p % sh.P)) * sh.Hkv + hk;
+    const uint32_t* kl = (const uint32_t*)(smem + kActOff + kActK);
+    const uint32_t* vl = (const uint32_t*)(smem + kActOff + kActV);
+    st32(rsrc((uint16_t*)s_ld64(row + ATT_KC) + rowi * 128), lane() * 4u, kl[lane()]);
+    st32(rsrc((uint16_t*)s_ld64(row + ATT_VC) + rowi * 128), lane() * 4u, vl[lane()]);
+  }
   wait_vm0();
-  if (!arrive(a, in)) return;
-  // combine the group's splits: o = sum_i exp(lse_i - lse) O_i, lse = log sum_i exp(lse_i)
-  uint16_t* o = (uint16_t*)s_ld64(row + ATT_O) + (size_t)r * sh.Hq * 128;
-  __amdgpu_buffer_rsrc_t ro = rsrc(o);
+  if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
+  const bool last = arrive(a, in);
+  if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
+  if (!last) return;
+  // combine the group's splits, o = sum_i exp(lse_i - lse) O_i with lse = log sum_i exp(lse_i),
+  // online over chunks of splits staged into LDS: lanes over splits take the statistics,
+  // lanes over 4-dim units accumulate the outputs
+  char* act = smem + kActOff;
+  float* wts = (float*)(smem + kOutOff);          // [64][kMaxG] weights of the chunk's splits
+  float* hst = (float*)(smem + kOutOff) + 64 * kMaxG;  // [kMaxG][3]: running max, sum, chunk rescale
+  const uint32_t chunk = min(64u, (uint32_t)kActStageBytes / (pstride * 4u));
   const int ln = (int)lane();
-  float* wts = (float*)(smem + kOutOff);  // [ns][g] combine weights (this split's output is stored)
+  float acc[4][4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= g) break;
-    float mx = -INFINITY;
-    for (int t0 = 0; t0 < ns; t0 += 64) {
-      const int t = t0 + ln;
-      const float l = t < ns ? __uint_as_float(ld32(rp, (gbase + t * pstride + g * 128 + j) * 4u)) : -INFINITY;
-      if (t < ns) wts[t * g + j] = l;
-      mx = fmaxf(mx, l);
-    }
-    mx = wave_max(mx);
-    float den = 0.f;
-    for (int t0 = 0; t0 < ns; t0 += 64) {
-      const int t = t0 + ln;
-      if (t < ns) {
-        const float w = __expf(wts[t * g + j] - mx);
-        wts[t * g + j] = w;
-        den += w;
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[u][q] = 0.f;
+  if (ln < g) {
+    hst[ln * 3] = -INFINITY;
+    hst[ln * 3 + 1] = 0.f;
+  }
+  for (int t0 = 0; t0 < ns; t0 += (int)chunk) {
+    const int nc = min((int)chunk, ns - t0);
+    stage(part + gbase + (uint32_t)t0 * pstride, (uint32_t)nc * pstride * 4u, act);
+    wait_vm0();
+    const float* pl = (const float*)act;
+    for (int j = 0; j < g; ++j) {
+      const float lv = ln < nc ? pl[ln * pstride + g * 128 + j] : -INFINITY;
+      const float mo = hst[j * 3];
+      const float mn = fmaxf(mo, wave_max(lv));
+      const float w = ln < nc ? __expf(lv - mn) : 0.f;
+      const float ws = wave_sum(w);
+      const float sc = __expf(mo - mn);
+      wts[ln * kMaxG + j] = w;
+      if (ln == 0) {
+        hst[j * 3] = mn;
+        hst[j * 3 + 1] = hst[j * 3 + 1] * sc + ws;
+        hst[j * 3 + 2] = sc;
       }
     }
-    den = wave_sum(den);
-    const float inv = 1.f / den;
-    for (int t0 = 0; t0 < ns; t0 += 64) {
-      const int t = t0 + ln;
-      if (t < ns) wts[t * g + j] *= inv;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  for (int u = ln; u < g * 32; u += 64) {  // unit = (head j, 4 dims)
-    const int j = u >> 5, c4 = u & 31;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int t0 = 0; t0 < ns; t0 += 16) {
-      u32x4 v[16];
+    __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (t0 + q < ns) v[q] = ld128(rp, (gbase + (t0 + q) * pstride + j * 128 + c4 * 4) * 4u);
+    for (int u = 0; u < 4; ++u) {
+      const int unit = ln + 64 * u;
+      if (unit < g * 32) {
+        const int j = unit >> 5, c4 = unit & 31;
+        const float sc = hst[j * 3 + 2];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (t0 + q < ns) {
-          const float w = wts[(t0 + q) * g + j];
-          acc[0] += w * __uint_as_float(v[q].x);
-          acc[1] += w * __uint_as_float(v[q].y);
-          acc[2] += w * __uint_as_float(v[q].z);
-          acc[3] += w * __uint_as_float(v[q].w);
+        for (int q = 0; q < 4; ++q) acc[u][q] *= sc;
+#pragma unroll 8
+        for (int t = 0; t < nc; ++t) {
+          const float w = wts[t * kMaxG + j];
+          const u32x4 ov = *(const u32x4*)(pl + t * pstride + j * 128 + c4 * 4);
+          acc[u][0] += w * __uint_as_float(ov.x);
+          acc[u][1] += w * __uint_as_float(ov.y);
+          acc[u][2] += w * __uint_as_float(ov.z);
+          acc[u][3] += w * __uint_as_float(ov.w);
         }
       }
     }
-    const uint32_t col = (uint32_t)(hk * g + j) * 128u + c4 * 4u;
-    st32(ro, col * 2u, f2bf(acc[0]) | (f2bf(acc[1]) << 16));
-    st32(ro, col * 2u + 4u, f2bf(acc[2]) | (f2bf(acc[3]) << 16));
+  }
+  uint16_t* o = (uint16_t*)s_ld64(row + ATT_O) + (size_t)r * sh.Hq * 128;
+  __amdgpu_buffer_rsrc_t ro = rsrc(o);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int unit = ln + 64 * u;
+    if (unit < g * 32) {
+      const int j = unit >> 5, c4 = unit & 31;
+      const float inv = 1.f / hst[j * 3 + 1];
+      const uint32_t col = (uint32_t)(hk * g + j) * 128u + c4 * 4u;
+      st32(ro, col * 2u, pack_bf2(acc[u][0] * inv, acc[u][1] * inv));
+      st32(ro, col * 2u + 4u, pack_bf2(acc[u][2] * inv, acc[u][3] * inv));
+    }
   }
   wait_vm0();
   signal_all(a, in);
@@ -697,7 +812,7 @@ struct LmState {
   int idx;
 };
 
-DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmState& lm) {
+DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmState& lm, Stamps& st) {
   const uint32_t op = in.w[W_OPCODE];
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int n0 = in.w[W_P1], nr = in.w[W_P2];
@@ -707,26 +822,21 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
     __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + QKV_OUT));
     for (int jj = j; jj < nr; jj += 64) st32(ro, (uint32_t)(n0 + jj) * 4u, __float_as_uint(out[jj]));
   } else if (op == OP_OPROJ) {
-    __amdgpu_buffer_rsrc_t rx = rsrc((const void*)s_ld64(row + O_X));
-    __amdgpu_buffer_rsrc_t rr = rsrc((const void*)s_ld64(row + O_RIN));
     __amdgpu_buffer_rsrc_t r2 = rsrc((const void*)s_ld64(row + O_R2));
+    const float* r1 = (const float*)(smem + kActOff + kActR1);
     for (int jj = j; jj < nr; jj += 64) {
-      const uint32_t n = (uint32_t)(n0 + jj);
-      const float av = bf2f(f2bf(out[jj]));
-      const float xv = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rx, n * 2u, 0, SC1));
-      const float rin = __uint_as_float(ld32(rr, n * 4u));
-      const float r1 = rin + xv;
-      st32(r2, n * 4u, __float_as_uint(r1 + av));
+      const float av = bf2f(pack_bf2(out[jj], 0.f) & 0xffffu);
+      st32(r2, (uint32_t)(n0 + jj) * 4u, __float_as_uint(r1[jj] + av));
     }
   } else if (op == OP_GATEUP) {
     __amdgpu_buffer_rsrc_t rm = rsrc((const void*)s_ld64(row + GU_M));
     for (int jj = j; jj < nr; jj += 64) {
       const float gv = out[jj], uv = out[nr + jj];
-      st16(rm, (uint32_t)(n0 + jj) * 2u, f2bf(gv / (1.f + __expf(-gv)) * uv));
+      st16(rm, (uint32_t)(n0 + jj) * 2u, pack_bf2(gv / (1.f + __expf(-gv)) * uv, 0.f));
     }
   } else if (op == OP_DOWN) {
     __amdgpu_buffer_rsrc_t ry = rsrc((const void*)s_ld64(row + DN_Y));
-    for (int jj = j; jj < nr; jj += 64) st16(ry, (uint32_t)(n0 + jj) * 2u, f2bf(out[jj]));
+    for (int jj = j; jj < nr; jj += 64) st16(ry, (uint32_t)(n0 + jj) * 2u, pack_bf2(out[jj], 0.f));
   } else if (op == OP_LMHEAD) {
     __amdgpu_buffer_rsrc_t rl = rsrc((const void*)s_ld64(row + LM_LOGITS));
     __amdgpu_buffer_rsrc_t rp = rsrc((const void*)s_ld64(row + LM_PART));
@@ -752,7 +862,10 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
       st32(rp, slot * 8u + 4u, (uint32_t)lm.idx);
     }
     wait_vm0();
-    if (!arrive(a, in)) return;
+    if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
+    const bool last = arrive(a, in);
+    if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
+    if (!last) return;
     const uint32_t n = in.w[W_ARR_N];
     best = -INFINITY;
     bi = 0x7fffffff;
@@ -782,21 +895,29 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
     return;
   }
   wait_vm0();
+  if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
   signal_all(a, in);
 }
 
 // ---------------------------------------------------------------------------------------
 // the two roles
 
-DEV int inner_barriers(uint32_t op) { return op == OP_ATTN ? 3 : 0; }
+// barriers between the compute-start and compute-end barriers: attention (QK-norm / RoPE, wave
+// merge), the fused norm of QKV / GATE_UP / LM_HEAD
+DEV int inner_barriers(uint32_t op) { return op == OP_ATTN ? 2 : ((op == OP_QKV || op == OP_GATEUP || op == OP_LMHEAD) ? 1 : 0); }
 
 // returns false when the watchdog expired or another worker aborted
-DEV bool wait_events(const KArgs& a, const Instr& in, uint32_t& poll_ticks) {
+struct WaitCache {  // the last (event, threshold) wait found satisfied in this run
+  uint32_t e, thr;
+};
+
+DEV bool wait_events(const KArgs& a, const Instr& in, uint32_t& poll_ticks, WaitCache& wc) {
   const uint32_t ln = lane();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if ((uint32_t)k >= in.w[W_NWAIT]) break;
     const uint32_t e = in.w[W_WAIT0 + 2 * k], thr = in.w[W_WAIT0 + 2 * k + 1];
+    if (e == wc.e && thr == wc.thr) continue;  // counters only grow within a run
     const uint32_t target = (a.epoch + 1u) * thr;
     const uint32_t* base = a.events + (size_t)e * kEvStride;
     const unsigned long long t_start = rtc();
@@ -827,55 +948,58 @@ DEV bool wait_events(const KArgs& a, const Instr& in, uint32_t& poll_ticks) {
       __builtin_amdgcn_s_sleep(1);
     }
     poll_ticks += (uint32_t)(rtc() - t_start);
+    wc.e = e;
+    wc.thr = thr;
   }
   asm volatile("" ::: "memory");
   return true;
 }
 
 DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride, char* smem) {
-  volatile uint32_t* ctrl = (volatile uint32_t*)(smem + kCtrlOff);
+  uint32_t* ctrl = (uint32_t*)(smem + kCtrlOff);  // LDS; read and written only across barriers
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
   const bool graph = a.flags & kModeGraph;
   uint32_t last_row = 0xFFFFFFFFu;
   LmState lm{-INFINITY, 0x7fffffff};
+  WaitCache wc{0xFFFFFFFFu, 0u};
   for (int i = 0; i < count; ++i) {
     Instr in;
     fetch(base + (size_t)i * stride, in);
     const uint32_t op = in.w[W_OPCODE];
     if (op == OP_NOOP) continue;
-    const unsigned long long t_vis = rtc();
+    const bool tracing = a.flags & MK_FLAG_TRACE;
+    const unsigned long long t_vis = tracing ? rtc() : 0;
     uint32_t poll = 0;
-    bool ok = graph ? true : wait_events(a, in, poll);
-    const unsigned long long t_ready = rtc();
+    bool ok = graph ? true : wait_events(a, in, poll, wc);
+    const unsigned long long t_ready = tracing ? rtc() : 0;
+    Stamps st{0, 0};
     if (ok && !noop_only) {
       const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
       char* act = smem + kActOff;
-      switch (op) {
-        case OP_QKV:
-          norm_prologue((const uint16_t*)s_ld64(row + QKV_X), (const float*)s_ld64(row + QKV_RIN),
-                        (const uint16_t*)s_ld64(row + QKV_GAMMA), a.sh.H, a.sh.eps, act);
-          break;
-        case OP_ATTN: attn_prologue(a, in, act); break;
-        case OP_OPROJ: copy_prologue((const uint16_t*)s_ld64(row + O_IN), a.sh.Hq * 128, act); break;
-        case OP_GATEUP:
-          norm_prologue(nullptr, (const float*)s_ld64(row + GU_R2), (const uint16_t*)s_ld64(row + GU_GAMMA),
-                        a.sh.H, a.sh.eps, act);
-          break;
-        case OP_DOWN: copy_prologue((const uint16_t*)s_ld64(row + DN_M), a.sh.I, act); break;
-        case OP_LMHEAD:
-          if (last_row != in.w[W_ROW])
-            norm_prologue((const uint16_t*)s_ld64(row + LM_Y), (const float*)s_ld64(row + LM_R2),
-                          (const uint16_t*)s_ld64(row + LM_GAMMA), a.sh.H, a.sh.eps, act);
-          break;
-        default: break;
+      if (op == OP_ATTN) {
+        attn_stage(a, in, act);
+      } else if (op == OP_OPROJ) {
+        oproj_prologue(in, row, a.sh.Hq * 128, act);
+      } else if (op == OP_DOWN) {
+        stage((const void*)s_ld64(row + DN_M), 2u * a.sh.I, act);
+        wait_vm0();
+      } else if (op != OP_LMHEAD || last_row != in.w[W_ROW]) {  // inputs of the fused add + RMSNorm
+        const int sx = op == OP_QKV ? QKV_X : LM_Y, sr = op == OP_QKV ? QKV_RIN : (op == OP_GATEUP ? GU_R2 : LM_R2);
+        norm_stage(op == OP_GATEUP ? nullptr : (const uint16_t*)s_ld64(row + sx), (const float*)s_ld64(row + sr),
+                   a.sh.H, act);
       }
       last_row = in.w[W_ROW];
     }
     if (!ok && lane() == 0) ctrl[0] = 1u;
+    const unsigned long long t_pro = tracing ? rtc() : 0;
     lds_barrier();  // A: activations staged, prefetch of this instruction landed
+    const unsigned long long t_a = tracing ? rtc() : 0;
+    const unsigned long long c_a = tracing ? __builtin_readcyclecounter() : 0;
     if (!ok) break;
     for (int b = 0; b < inner_barriers(op); ++b) lds_barrier();
     lds_barrier();  // B: compute done, results in the output area
+    const unsigned long long t_b = tracing ? rtc() : 0;
+    const unsigned long long c_b = tracing ? __builtin_readcyclecounter() : 0;
     if (noop_only) {
       if (op == OP_ATTN || op == OP_LMHEAD) {
         if (arrive(a, in) && op == OP_ATTN) signal_all(a, in);
@@ -883,22 +1007,28 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
         signal_all(a, in);
       }
     } else if (op == OP_ATTN) {
-      attn_epilogue(a, in, smem);
+      attn_epilogue(a, in, smem, st);
     } else {
-      gemv_epilogue(a, in, smem, lm);
+      gemv_epilogue(a, in, smem, lm, st);
     }
-    if ((a.flags & MK_FLAG_TRACE) && a.trace && lane() == 0) {
-      uint32_t* tr = a.trace + ((size_t)blockIdx.x * a.L + i) * 4;
+    if (tracing && a.trace && lane() == 0) {
+      uint32_t* tr = a.trace + ((size_t)blockIdx.x * a.L + i) * kTraceWords;
       tr[0] = (uint32_t)t_vis;
       tr[1] = (uint32_t)t_ready;
-      tr[2] = (uint32_t)rtc();
-      tr[3] = poll;
+      tr[2] = (uint32_t)t_pro;
+      tr[3] = (uint32_t)t_a;
+      tr[4] = (uint32_t)t_b;
+      tr[5] = (uint32_t)st.ack;
+      tr[6] = (uint32_t)st.arr;
+      tr[7] = (uint32_t)rtc();
+      tr[8] = poll;
+      tr[9] = (uint32_t)(c_b - c_a);  // shader clock cycles between the two compute barriers
     }
   }
 }
 
 DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, int cw, char* smem) {
-  volatile uint32_t* ctrl = (volatile uint32_t*)(smem + kCtrlOff);
+  const uint32_t* ctrl = (const uint32_t*)(smem + kCtrlOff);  // LDS abort flag
   uint32_t* lease_tab = (uint32_t*)(smem + kCtrlOff + 64) + cw * 32;  // [16] lease, [16] issued_end
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
   const int lookahead = (a.flags & MK_FLAG_NO_PREFETCH) ? 0 : 15;
@@ -914,7 +1044,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
     }
     if (!noop_only) {
       // pages of every instruction before i are free now
-      const uint32_t freed = (pf_i > i) ? lease_tab[i & 15] : head;
+      const uint32_t freed = (pf_i > i) ? uni(lease_tab[i & 15]) : head;
       if (pf_i < i) pf_i = i;
       while (pf_i < count && pf_i <= i + lookahead) {
         Instr nx;
@@ -927,7 +1057,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
         }
         Pf pf;
         pf_desc(a, nx, pf);
-        const uint32_t npg = (pf.nblk + 15u) >> 4;
+        const uint32_t npg = (pf_blocks(pf) + 15u) >> 4;
         if (head + npg - freed > (uint32_t)kNPages) break;
         pf_issue(a, pf, head, cw, issued, smem);
         lease_tab[pf_i & 15] = head;
@@ -935,20 +1065,30 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
         head += npg;
         ++pf_i;
       }
-      wait_vm_le(issued - lease_tab[16 + (i & 15)]);
+      wait_vm_le(issued - uni(lease_tab[16 + (i & 15)]));
     }
     lds_barrier();  // A
-    if (ctrl[0]) break;
+    if (uni(ctrl[0])) break;
     if (!noop_only) {
-      const uint32_t lease = lease_tab[i & 15];
+      const uint32_t lease = uni(lease_tab[i & 15]);
       char* act = smem + kActOff;
       float* out = (float*)(smem + kOutOff);
       if (op == OP_ATTN) {
         attn_compute(a, in, smem, act, lease, cw);
       } else {
         const int nr = in.w[W_P2], K = in.w[W_P4];
-        if (op == OP_GATEUP) gemv(smem, lease, 2 * nr, nr, blocks_of((uint32_t)nr * K * 2u) * 1024u, K, cw, out);
-        else gemv(smem, lease, nr, nr, 0, K, cw, out);
+        const uint32_t wblk = blocks_of((uint32_t)nr * K * 2u);
+        uint32_t hoff = 0;
+        if (op == OP_QKV || op == OP_GATEUP || op == OP_LMHEAD) {
+          const uint32_t goff = (op == OP_GATEUP ? 2u : 1u) * wblk * 1024u;
+          hoff = kb_round(2u * K) + kb_round(4u * K);  // after the staged x and r
+          if (op == OP_GATEUP)
+            norm_h<false>(smem, lease, goff, K, a.sh.eps, cw, hoff);
+          else
+            norm_h<true>(smem, lease, goff, K, a.sh.eps, cw, hoff);
+          lds_barrier();
+        }
+        gemv(smem, lease, op == OP_GATEUP ? 2 * nr : nr, nr, wblk * 1024u, K, cw, out, hoff);
       }
     } else {
       for (int b = 0; b < inner_barriers(op); ++b) lds_barrier();
@@ -974,7 +1114,7 @@ __global__ void __launch_bounds__(dev::kThreads, 1) mk_worker(KArgs a) {
     count = a.L;
     stride = kWords;
   }
-  if (threadIdx.x == 0) *(volatile uint32_t*)(smem + dev::kCtrlOff) = 0u;
+  if (threadIdx.x == 0) *(uint32_t*)(smem + dev::kCtrlOff) = 0u;
   __syncthreads();
   if (wave == 0) dev::controller(a, base, count, stride, smem);
   else dev::compute(a, base, count, stride, wave - 1, smem);

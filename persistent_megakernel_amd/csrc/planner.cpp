@@ -84,15 +84,19 @@ bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, s
   const int R = c.n_requests;
   const int elem = c.weight_fp8 ? 1 : 2;
   const int n_qkv = (Hq + 2 * Hkv) * d;
-  auto cap_rows = [&](int k, int nmat) { return std::max(1, kLeaseBytes / (k * elem * nmat)); };
-  p.r_qkv = pow2floor(std::min({d, std::max(1, n_qkv / W), cap_rows(H, 1)}));
-  p.r_o = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(Hq * d, 1)));
-  p.r_gu = largest_divisor_le(I, std::min(std::max(1, I / W), cap_rows(H, 2)));
-  p.r_down = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(I, 1)));
-  p.r_lm = c.workload == MK_QWEN3_STEP ? std::min({c.vocab, cap_rows(H, 1), 64}) : 0;
+  // rows of one tile: the lease (weights, plus the 1 KiB-rounded norm gain of the fused
+  // add + RMSNorm ops) stays within kLeaseBytes
+  const int gain = (2 * H + 1023) / 1024 * 1024;
+  auto cap_rows = [&](int k, int nmat, int extra) { return std::max(1, (kLeaseBytes - extra) / (k * elem * nmat)); };
+  p.r_qkv = pow2floor(std::min({d, std::max(1, n_qkv / W), cap_rows(H, 1, gain)}));
+  p.r_o = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(Hq * d, 1, 0)));
+  p.r_gu = largest_divisor_le(I, std::min(std::max(1, I / W), cap_rows(H, 2, gain + 1024)));
+  p.r_down = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(I, 1, 0)));
+  p.r_lm = c.workload == MK_QWEN3_STEP ? std::min({c.vocab, cap_rows(H, 1, gain), 64}) : 0;
   int ctx_max = 0;
   for (int r = 0; r < R; ++r) ctx_max = std::max(ctx_max, (int)ctx[r]);
-  long long want = ((long long)R * ctx_max * Hkv + W - 1) / W;
+  // about W/2 attention tasks: fewer splits keep the combine short; the KV is prefetched anyway
+  long long want = (2ll * R * ctx_max * Hkv + W - 1) / W;
   p.s_tok = std::max(4, std::min(kLeaseBytes / (4 * d), pow2ceil((int)std::max(1ll, want))));
   p.spec = (R * c.tokens_per_request == 1) ? 0 : 1;
   (void)err;
@@ -233,7 +237,7 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
     off += (bytes + 255) / 256 * 256;
   };
   region("qkv", (size_t)M * n_qkv * 4);
-  region("part", (size_t)R * Hkv * max_splits * g * (d + 1) * 4);
+  region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);  // per split: g*d O, g lse, padding
   region("o", (size_t)M * Hq * d * 2);
   region("m", (size_t)M * I * 2);
   region("r2a", (size_t)M * H * 4);

@@ -44,8 +44,8 @@ def test_small_kernel_line_and_exercise():
 
 
 def test_algorithmic_bytes_small_layer():
-    from workloads import get_config
-    b = ob.algorithmic_bytes(get_config("qwen3_0p6b_layer"))
+    from workloads import algorithmic_bytes, get_config
+    b = algorithmic_bytes(get_config("qwen3_0p6b_layer"))
     # weights: (4096 + 1024*2048/1024 ...) spelled out per matrix
     assert b["weights"] == 2 * (4096 * 1024 + 1024 * 2048 + 6144 * 1024 + 1024 * 3072)
     assert b["kv_read"] == 511 * 2 * 8 * 128 * 2

@@ -21,9 +21,9 @@ def test_invariants(name, W):
 def test_small_layer_counts():
     plan = oq.build_queue(get_config("qwen3_0p6b_layer"), 256)
     p = plan["params"]
-    assert (p["r_qkv"], p["r_o"], p["r_gu"], p["r_down"], p["s_tok"]) == (16, 4, 12, 4, 16)
-    # 256 QKV + 8 heads x 32 splits + 256 + 256 + 256
-    assert plan["n_tasks"] == 1280 and plan["queue"].shape == (256, 5, 32)
+    assert (p["r_qkv"], p["r_o"], p["r_gu"], p["r_down"], p["s_tok"]) == (16, 4, 12, 4, 32)
+    # 256 QKV + 8 heads x 16 splits + 256 + 256 + 256
+    assert plan["n_tasks"] == 1152 and plan["queue"].shape == (256, 5, 32)
     assert list(plan["thresholds"]) == [32] * 8 + [8, 256, 256, 256]
 
 

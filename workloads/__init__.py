@@ -23,7 +23,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-__all__ = ["Config", "CONFIGS", "get_config", "make_inputs", "f32_to_bf16_bits_trunc"]
+__all__ = ["Config", "CONFIGS", "get_config", "make_inputs", "f32_to_bf16_bits_trunc", "algorithmic_bytes"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -215,3 +215,43 @@ def make_inputs(cfg: Config, seed: int = 0, layers: Optional[int] = None) -> Dic
     else:
         raise ValueError(cfg.workload)
     return out
+
+
+def algorithmic_bytes(cfg) -> Dict[str, int]:
+    """Bytes one pass of the workload must move at least: every weight, scale and norm gain
+    once, the prior KV cache (or indexer keys) once, the new cache rows, and the external
+    inputs and outputs.  Intermediates and redundant re-reads are excluded."""
+    parts: Dict[str, int] = {}
+    if cfg.workload in ("qwen3_layer", "qwen3_step"):
+        H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
+        nq, nkv = cfg.n_q_heads * d, cfg.n_kv_heads * d
+        L, M = cfg.num_layers, cfg.m
+        wel = 1 if cfg.weight_fp8 else 2
+        mats = [(nq + 2 * nkv, H), (H, nq), (2 * I, H), (H, I)]
+        parts["weights"] = L * sum(n * k * wel for n, k in mats)
+        if cfg.weight_fp8:
+            parts["scales"] = L * sum((-(-n // 128)) * (-(-k // 128)) * 4 for n, k in mats)
+        parts["norms"] = L * (2 * H + 2 * d) * 2
+        prior = cfg.n_requests * (cfg.context - 1)
+        parts["kv_read"] = L * prior * 2 * nkv * 2
+        parts["kv_write"] = L * cfg.n_requests * 2 * nkv * 2
+        parts["act_in"] = M * H * (2 + 4)
+        if cfg.workload == "qwen3_step":
+            parts["lm_head"] = cfg.vocab * H * 2 + H * 2
+            parts["logits_out"] = M * cfg.vocab * 4 + M * 4
+        else:
+            parts["act_out"] = M * H * (2 + 4)
+    elif cfg.workload == "indexer_front":
+        H, qr, nh, hd = cfg.hidden, cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
+        mats = [(qr, H), (nh, H), (hd, H), (nh * hd, qr)]
+        parts["weights"] = sum(n * k for n, k in mats)
+        parts["scales"] = sum((-(-n // 128)) * (-(-k // 128)) * 4 for n, k in mats)
+        parts["norms"] = (H + qr) * 2
+        M = cfg.m
+        prior = cfg.n_requests * (cfg.context - cfg.tokens_per_request)
+        parts["keys_read"] = prior * (hd + 4)
+        parts["keys_write"] = M * (hd + 4)
+        parts["act_in"] = M * H * (2 + 4)
+        parts["score_out"] = M * cfg.context * 4
+    parts["total"] = sum(parts.values())
+    return parts
