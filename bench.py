@@ -26,6 +26,33 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 HBM_PEAK_GBPS = 8000.0
 
 
+def _kernel_source_sha16() -> str:
+    import hashlib
+    d = os.path.join(ROOT, "persistent_megakernel_amd", "csrc")
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(d)):
+        with open(os.path.join(d, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_traffic(workload: str):
+    """HBM bytes per launch from the committed profiler counter summary of this workload, or
+    None when there is none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"mk_worker_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            k, sep, v = line.partition(":")
+            if sep and k.strip() in ("source_sha16", "traffic_bytes_per_launch"):
+                fields[k.strip()] = v.strip().strip("()`")
+    if fields.get("source_sha16") != _kernel_source_sha16() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -39,6 +66,9 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=0, help="copies of weights/caches cycled per run (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="time a plain device-to-device copy of this many bytes instead (calibrates the "
+                         "HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the decode chain on a single MI355X "
@@ -47,6 +77,9 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_bytes:
+        return copy_calibration(args, torch)
 
     import persistent_megakernel_amd as mk
     from gpu_helpers import to_device
@@ -145,7 +178,7 @@ def main() -> int:
         "hbm_frac_of_8TBps": round(achieved / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _counter_traffic(cfg.name),
                      "kernel": "mk_worker (persistent megakernel, one launch per step)"},
         "variants_us_per_step": variants,
     }
@@ -176,6 +209,27 @@ def main() -> int:
     print(json.dumps(out), flush=True)
     for p in plans.values():
         p.close()
+    return 0
+
+
+def copy_calibration(args, torch) -> int:
+    """Plain copy of a known size: its profiler byte counters give the scale factor that turns
+    counter readings of the megakernel into HBM bytes."""
+    n = args.copy_bytes // 16 * 16
+    src = torch.empty(n // 4, dtype=torch.int32, device="cuda").random_()
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n, "ms_per_copy": round(ms, 5),
+                      "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
     return 0
 
 

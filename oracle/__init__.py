@@ -13,7 +13,7 @@ Modules
             indexer score)
   model     the workloads: one Qwen3-shaped layer, the full decode step, the indexer front
   queue     the host tile-instruction queue builder (tiles -> events -> round-robin queues)
-  bytes     the decode byte / gap estimate model and the algorithmic-byte counts
+  bytes     the decode byte / gap estimate model of the handbook
 
 Pages cited: "Kernel-Mega-PDL" (MegaRTP; qingkeai.online), the handbook chapter on
 PDL and megakernels (anrans.github.io), the Hazy/MPK/MegaMoE survey
