@@ -178,8 +178,10 @@ mk_status check_runnable(mk_plan* p) {
   if (hp.tp.spec != 0 || c.weight_fp8 || c.act_fp8)
     return fail(MK_ERR_UNSUPPORTED, "only the bf16 single-token (M = 1) op bodies are built");
   if (c.hidden > 3072 || c.inter > 8192 || c.n_q_heads * c.head_dim > 8192 || hp.tp.r_o > 256 ||
-      c.n_q_heads / c.n_kv_heads > mk::dev::kMaxG)
-    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 3072; inter, q width <= 8192; GQA group <= 5)");
+      c.n_q_heads / c.n_kv_heads > mk::dev::kMaxG || c.hidden % 512 || c.inter % 512 ||
+      (c.n_q_heads * c.head_dim) % 512)
+    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 3072; inter, q width <= 8192; "
+                                    "hidden, inter and q width multiples of 512; GQA group <= 5)");
   if (!p->occupancy_checked) {
     int per_cu = 0;
     HIP_TRY(hipSetDevice(p->device));

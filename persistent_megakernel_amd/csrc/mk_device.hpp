@@ -38,6 +38,7 @@ constexpr unsigned long long kWatchdogTicks = 200000000ull;  // 2 s of the 100 M
 namespace dev {
 constexpr int kThreads = 512;  // 8 waves: controller + 7 loader/compute waves
 constexpr int kNCW = 7;
+constexpr int kNW = 8;     // waves of a projection tile: the seven compute waves and the controller
 constexpr int kNPages = 8;     // LDS ring of 8 x 16 KiB pages
 constexpr int kRingOff = 0;
 constexpr int kActOff = kNPages * 16384;   // activation staging
@@ -47,18 +48,24 @@ constexpr int kOutOff = kActOff + kActBytes;  // compute results
 constexpr int kOutBytes = 4096;  // g*128 + g floats of an attention partial: GQA group <= 7
 constexpr int kCtrlOff = kOutOff + kOutBytes;  // abort flag + per-wave lease tables
 constexpr int kCtrlBytes = 1024;
+constexpr int kLeaseTabOff = 64;   // in the control area: [7 waves][32] lease tables
+constexpr int kInvOff = 8;         // in the control area: the fused norm's rsqrt(mean square + eps)
+static_assert(kLeaseTabOff + 7 * 32 * 4 <= kCtrlBytes, "control area");
 constexpr int kLdsBytes = kCtrlOff + kCtrlBytes;  // all 160 KiB: one block per CU
 // attention sub-areas of the activation staging area
 constexpr int kMaxG = 5;       // GQA group (q heads per kv head) of the M = 1 attention body
 constexpr int kActQ = 0;       // bf16 [g][128] rotated q heads
 constexpr int kActK = 2048;    // bf16 [128] new key
 constexpr int kActV = 2304;    // bf16 [128] new value
-constexpr int kActMerge = 2560;  // fp32 [7 waves][g][130] per-wave softmax states (<= 18200 bytes)
+constexpr int kActMerge = 2560;  // fp32 [7 waves][g][128] per-wave partial P V (<= 17920 bytes)
 constexpr int kAttQraw = 21504;  // fp32 staging of the raw q heads (4 KiB), k and v (1 KiB each)
 constexpr int kAttKraw = 25600;
 constexpr int kAttVraw = 26624;
+constexpr int kAttS = kAttQraw;  // fp32 [g][128] scores, once QK-norm / RoPE consumed the raw q
+constexpr int kAttP = kAttS + kMaxG * 512;  // fp32 [7 waves][g][20] exponentials of each wave's tokens
 constexpr int kActR1 = 16384;   // O projection: fp32 r_in + x of the tile's rows (<= 256)
-static_assert(kActMerge + 7 * kMaxG * 130 * 4 <= kAttQraw, "attention staging overlaps");
+static_assert(kActMerge + 7 * kMaxG * 128 * 4 <= kAttQraw, "attention staging overlaps");
+static_assert(kAttP + 7 * kMaxG * 20 * 4 <= kActBytes, "attention exponentials overflow the staging area");
 static_assert(kAttVraw + 1024 <= kActBytes, "attention staging overflows");
 static_assert(kLdsBytes == 163840, "LDS budget");
 static_assert(kLdsBytes <= 163840, "LDS budget");

@@ -50,6 +50,7 @@ DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 // element 0 by this compiler, so the word is copied out first.)
 // two fp32 to packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32 on gfx950)
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 DEV uint32_t pack_bf2(float lo, float hi) {
   const f32x2 v = {lo, hi};
   const bf16x2 h = __builtin_convertvector(v, bf16x2);
@@ -389,12 +390,68 @@ DEV void stage(const void* src, uint32_t bytes, char* dst) {
 }
 DEV uint32_t kb_round(uint32_t bytes) { return (bytes + 1023u) & ~1023u; }
 
-// fused add + RMSNorm inputs: x (bf16, may be null) at act[0, 2H), the residual r (fp32) at
-// act + kb_round(2H); the compute waves normalise with the gain from their prefetch
-DEV void norm_stage(const uint16_t* x, const float* r, int H, char* act) {
+// Fused add + RMSNorm, first half, by the controller: stage x (bf16, may be null) at act[0, 2H)
+// and the residual r (fp32) at act + kb_round(2H) in one round trip, then
+// inv = rsqrt(mean((r + x)^2) + eps) into the control area for norm_h.
+DEV void norm_stage(const uint16_t* x, const float* r, int H, float eps, char* act, char* smem) {
+  const uint32_t R0 = kb_round(2u * H);
   if (x) stage(x, 2u * H, act);
-  stage(r, 4u * H, act + kb_round(2u * H));
+  stage(r, 4u * H, act + R0);
   wait_vm0();
+  const int ln = (int)lane(), nk8 = H / 8;
+  const bool has_x = x != nullptr;
+  float ss = 0.f;
+#pragma unroll 2
+  for (int c = ln; c < nk8; c += 64) {
+    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
+    float v[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
+                  __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
+    if (has_x) {
+      const u32x4 xv = *(const u32x4*)(act + c * 16);
+      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] += bf2f(xs[q] & 0xffffu);
+        v[2 * q + 1] += bf2f(xs[q] >> 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ss += v[q] * v[q];
+  }
+  const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
+  if (ln == 0) *(float*)(smem + kCtrlOff + kInvOff) = inv;
+}
+
+// Fused add + RMSNorm, second half, by all eight waves (wave wv): h = bf16((r + x) * inv * gain)
+// over act[0, 2H), 8 elements per lane, the gain from the instruction's lease at goff.  The
+// caller follows with a barrier before the projection reads h.
+DEV void norm_h(const char* smem, uint32_t lease, uint32_t goff, int H, bool has_x, int wv) {
+  char* act = (char*)smem + kActOff;
+  const uint32_t R0 = kb_round(2u * H);
+  const float inv = *(const float*)(smem + kCtrlOff + kInvOff);
+  const int nk8 = H / 8;
+  for (int c = wv * 64 + (int)lane(); c < nk8; c += kNW * 64) {
+    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
+    const u32x4 gv = *(const u32x4*)(smem + kRingOff + ring_off(lease, goff + (uint32_t)c * 16u));
+    float v[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
+                  __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
+    if (has_x) {
+      const u32x4 xv = *(const u32x4*)(act + c * 16);
+      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] += bf2f(xs[q] & 0xffffu);
+        v[2 * q + 1] += bf2f(xs[q] >> 16);
+      }
+    }
+    const uint32_t gs[4] = {gv.x, gv.y, gv.z, gv.w};
+    u32x4 o;
+    o.x = pack_bf2(v[0] * inv * bf2f(gs[0] & 0xffffu), v[1] * inv * bf2f(gs[0] >> 16));
+    o.y = pack_bf2(v[2] * inv * bf2f(gs[1] & 0xffffu), v[3] * inv * bf2f(gs[1] >> 16));
+    o.z = pack_bf2(v[4] * inv * bf2f(gs[2] & 0xffffu), v[5] * inv * bf2f(gs[2] >> 16));
+    o.w = pack_bf2(v[6] * inv * bf2f(gs[3] & 0xffffu), v[7] * inv * bf2f(gs[3] >> 16));
+    *(u32x4*)(act + c * 16) = o;
+  }
 }
 
 // O projection: act = o (bf16), and r1 = r_in + x of the tile's rows at act + kActR1 (fp32);
@@ -437,107 +494,78 @@ DEV void attn_stage(const KArgs& a, const Instr& in, char* act) {
 // ---------------------------------------------------------------------------------------
 // compute bodies (waves 1..7; cw = 0..6)
 
-// out[j] = sum_k act[k] * W[row j][k]; rows [0, nr0) at j * rowb, rows [nr0, nrows) at off1.
-// Fused add + RMSNorm of the staged inputs: h = bf16(RMSNorm(r + x) * gamma) into LDS at hoff.
-// Every wave takes the full sum of squares (cheap), then the waves split the chunks of h.
-// The caller follows with a barrier before the projection reads h.
-// HAS_X = false (the MLP norm, whose input is the residual alone) never touches the x area,
-// which nothing has staged for such a tile.
-template <bool HAS_X>
-DEV void norm_h(const char* smem, uint32_t lease, uint32_t goff, int H, float eps, int cw, uint32_t hoff) {
-  const int ln = (int)lane();
-  const int nk8 = H / 8;
-  const char* act = smem + kActOff;
-  const char* ring = smem + kRingOff;
-  const uint32_t R0 = kb_round(2u * H);
-  float ss = 0.f;
-#pragma unroll 2
-  for (int c = ln; c < nk8; c += 64) {
-    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
-    float rv[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
-                   __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
-    if constexpr (HAS_X) {
-      const u32x4 xv = *(const u32x4*)(act + c * 16);
-      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rv[2 * q] += bf2f(xs[q] & 0xffffu);
-        rv[2 * q + 1] += bf2f(xs[q] >> 16);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) ss += rv[q] * rv[q];
-  }
-  const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
-  for (int c = cw * 64 + ln; c < nk8; c += kNCW * 64) {
-    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
-    const u32x4 gv = *(const u32x4*)(ring + ring_off(lease, goff + (uint32_t)c * 16u));
-    float rv[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
-                   __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
-    if constexpr (HAS_X) {
-      const u32x4 xv = *(const u32x4*)(act + c * 16);
-      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rv[2 * q] += bf2f(xs[q] & 0xffffu);
-        rv[2 * q + 1] += bf2f(xs[q] >> 16);
-      }
-    }
-    const uint32_t gs[4] = {gv.x, gv.y, gv.z, gv.w};
-    uint32_t os[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      os[q] = pack_bf2(rv[2 * q] * inv * bf2f(gs[q] & 0xffffu), rv[2 * q + 1] * inv * bf2f(gs[q] >> 16));
-    u32x4 o;
-    o.x = os[0]; o.y = os[1]; o.z = os[2]; o.w = os[3];
-    *(u32x4*)(smem + kActOff + hoff + c * 16) = o;
-  }
+// Projection tile on all eight waves: part[Q] = sum over quad Q of h[k] * W[r][k], for the tile's
+// R rows of K elements cut into quads of 512 (Q = r * KQ + kq, KQ = K / 512); rows [0, nr0) sit
+// at r * rowb in the lease, rows [nr0, R) at off1 + (r - nr0) * rowb; h (bf16) is at the start of
+// the activation area.  Wave w takes quads w, w + 8, ...; inside a quad, 16-lane row rho takes
+// the 128 elements [kq * 512 + 128 rho, + 128), lane `sub` eight of them.  Four quads at a time
+// are summed over the 16 lanes of each row by a transposing butterfly (about four instructions
+// per quad), then over the four rows by cross-row lane swaps.  Every address is wave-uniform
+// but for a per-lane constant.  The epilogue adds a row's KQ quad sums in order.
+DEV float butterfly4(float a0, float a1, float a2, float a3, int sub) {
+  const bool lo8 = sub < 8, lo4 = (sub & 4) == 0;
+  // partner 15 - sub (row mirror): lanes < 8 keep blocks 0, 1 and hand over 2, 3
+  float k0 = lo8 ? a0 : a2, k1 = lo8 ? a1 : a3;
+  const float s0 = lo8 ? a2 : a0, s1 = lo8 ? a3 : a1;
+  k0 += dppf<0x140>(s0);
+  k1 += dppf<0x140>(s1);
+  // partner 7 - sub within the half row: lanes with bit 2 clear keep k0
+  float k = lo4 ? k0 : k1;
+  const float t = lo4 ? k1 : k0;
+  k += dppf<0x141>(t);
+  // the quad's four lanes hold the same block: finish over the quad
+  k += dppf<0x4E>(k);
+  k += dppf<0xB1>(k);
+  return k;  // lanes 4i .. 4i + 3 of the row hold block i
 }
 
-// out[j] = sum_k h[k] * W[row j][k] with h the bf16 vector at act + hoff; rows [0, nr0) at
-// j * rowb, rows [nr0, nrows) at off1.  Rows go in groups of four consecutive rows, groups
-// round-robin over the waves; inside a group the loop body has no branches (a short last group
-// repeats its last row), so every LDS read of an iteration is in flight together.
-DEV void gemv(const char* smem, uint32_t lease, int nrows, int nr0, uint32_t off1, int K, int cw, float* out,
-              uint32_t hoff) {
-  const int ln = (int)lane();
+DEV void gemv(const char* smem, uint32_t lease, int R, int nr0, uint32_t off1, int K, int wv, float* part) {
+  const int ln = (int)lane(), sub = ln & 15;
+  const uint32_t KQ = (uint32_t)K >> 9, NQ = (uint32_t)R * KQ;
   const uint32_t rowb = (uint32_t)K * 2u;
-  const int nk8 = K / 8;
-  const char* act = smem + kActOff + hoff;
-  const char* ring = smem + kRingOff;
-  for (int r0 = cw * 4; r0 < nrows; r0 += kNCW * 4) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    uint32_t rb[4];
+  const uint32_t magic = (65536u + KQ - 1u) / KQ;  // Q / KQ == (Q * magic) >> 16 for Q < 2^16 / KQ
+  const uint32_t up = off1 - (uint32_t)nr0 * rowb;  // rows past nr0 start at off1
+  const char* act = smem + kActOff;
+  const uint32_t lbase = (lease << 14) + (uint32_t)(ln >> 4) * 256u + (uint32_t)sub * 16u;
+  const uint32_t xlane = (uint32_t)ln * 16u;  // row rho, lane sub: rho * 256 + sub * 16
+  for (uint32_t q0 = (uint32_t)wv; q0 < NQ; q0 += 4u * kNW) {
+    u32x4 w[4], x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = min(r0 + j, nrows - 1);
-      rb[j] = r < nr0 ? (uint32_t)r * rowb : off1 + (uint32_t)(r - nr0) * rowb;
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t Q = min(q0 + (uint32_t)m * kNW, NQ - 1u);  // wave-uniform: scalar arithmetic
+      const uint32_t r = (Q * magic) >> 16, kq = Q - r * KQ;
+      const uint32_t wo = r * rowb + (r >= (uint32_t)nr0 ? up : 0u) + kq * 1024u;
+      w[m] = *(const u32x4*)(smem + kRingOff + ((lbase + wo) & (uint32_t)(kNPages * 16384 - 1)));
+      x[m] = *(const u32x4*)(act + kq * 1024u + xlane);
     }
-#pragma unroll 2
-    for (int c = ln; c < nk8; c += 64) {
-      const u32x4 x = *(const u32x4*)(act + c * 16);
-      u32x4 wv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wv[j] = *(const u32x4*)(ring + ring_off(lease, rb[j] + (uint32_t)c * 16u));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = dot8(wv[j], x, acc[j]);
-    }
-    float sm[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sm[j] = wave_sum(acc[j]);
-    if (ln == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (r0 + j < nrows) out[r0 + j] = sm[j];
-    }
+    const float v = rows_sum(butterfly4(dot8(w[0], x[0], 0.f), dot8(w[1], x[1], 0.f), dot8(w[2], x[2], 0.f),
+                                        dot8(w[3], x[3], 0.f), sub));
+    const uint32_t Q = q0 + (uint32_t)(sub >> 2) * kNW;  // lanes 4i hold quad q0 + 8 i
+    if (ln < 16 && (sub & 3) == 0 && Q < NQ) part[Q] = v;
   }
 }
 
-// split-KV attention partial for one (request, kv head, split) over its g query heads.
-// Each 16-lane row walks its own tokens (row R of 28 takes tokens R, R + 28, ...) with an
-// online softmax (running max, sum and rescaled output, 8 dims per lane); the four rows of a
-// wave merge by lane exchange, the seven waves through LDS after one barrier.  Output: the
-// split's normalised O [g][128] and lse [g] in the output area.
+// a row of a projection tile: its KQ quad sums in order
+DEV float row_sum(const float* part, int r, int KQ) {
+  const float* p = part + r * KQ;
+  float s = p[0];
+  for (int k = 1; k < KQ; ++k) s += p[k];
+  return s;
+}
+
+// the projection body of one instruction on one wave (wv 0..6 compute waves, 7 the controller):
+// the second half of a fused norm (then a barrier), then the tile's quad sums into the output area
+DEV void proj_body(const KArgs& a, const Instr& in, const char* smem, uint32_t lease, bool fused_norm, int wv) {
+  const uint32_t op = in.w[W_OPCODE];
+  const int nr = in.w[W_P2], K = in.w[W_P4];
+  const uint32_t wblk = blocks_of((uint32_t)nr * K * 2u);
+  if (fused_norm) {
+    norm_h(smem, lease, (op == OP_GATEUP ? 2u : 1u) * wblk * 1024u, K, op != OP_GATEUP, wv);
+    lds_barrier();
+  }
+  gemv(smem, lease, op == OP_GATEUP ? 2 * nr : nr, nr, wblk * 1024u, K, wv, (float*)(smem + kOutOff));
+}
+
 // QK-norm (RMSNorm over the 128 dims of a head, gain gn) then rotate-half RoPE of one raw fp32
 // head vector, by one wave: lane i holds the rotation pair (i, i + 64); bf16 result into dst
 DEV void qk_norm_rope(const float* raw, const char* gn, const char* rope, float eps, char* dst) {
@@ -552,112 +580,140 @@ DEV void qk_norm_rope(const float* raw, const char* gn, const char* rope, float 
   ((uint16_t*)dst)[i + 64] = (uint16_t)(o >> 16);
 }
 
-DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
+// split-KV attention partial for one (request, kv head, split) over its G query heads, in three
+// phases separated by block barriers:
+//   1. scores: 16-lane rows over the split's tokens (row R takes tokens R, R + 28, ...), lane
+//      `sub` holding dims [8 sub, 8 sub + 8); four tokens of a row are summed over its lanes at
+//      once by the transposing butterfly;
+//   2. per head, the maximum and the sum of exponentials (every wave), and the exponentials of
+//      the wave's own phase-3 tokens into a wave-private table;
+//   3. P V: lanes over dimension pairs, waves over tokens (wave w takes tokens w, w + 7, ...),
+//      then the sum of the seven waves' partial outputs.
+// Output: the split's normalised O [G][128] and its lse [G] in the output area.
+template <int G>
+DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
   const Shapes& sh = a.sh;
-  const int g = sh.g;
   const int s = in.w[W_P3], t0 = in.w[W_P4], t1 = in.w[W_P5];
   const bool last = s == (int)in.w[W_ARR_N] - 1;
-  const int ntok = t1 - t0;
-  const int nk = last ? ntok - 1 : ntok;
+  const int ntok = t1 - t0;               // 1 .. 128
+  const int nk = last ? ntok - 1 : ntok;  // tokens read from the cache; the last split adds the new one
   const uint32_t nbk = blocks_of((uint32_t)nk * 256u);
   const uint32_t voff = nbk * 1024u, gqoff = 2u * nbk * 1024u;  // lease: K | V | q gain | k gain | RoPE
   const char* ring = smem + kRingOff;
   const int ln = (int)lane();
-  const int sub = ln & 15, rowid = cw * 4 + (ln >> 4);  // 28 token rows
   const float scale = sh.inv_sqrt_d;
-  // QK-norm + RoPE once per head: wave j < g takes q head j, wave g the new key, wave g + 1 the
-  // new value (bf16); the results (also the new cache row) go to LDS before one barrier
-  if (cw < g) {
+  // phase 0: QK-norm + RoPE once per head: wave j < G takes q head j, wave G the new key, wave
+  // G + 1 the new value (bf16); the results (also the new cache row) go to LDS
+  if (cw < G) {
     qk_norm_rope((const float*)(act + kAttQraw) + cw * 128, ring + ring_off(lease, gqoff),
                  ring + ring_off(lease, gqoff + 2048u), sh.eps, act + kActQ + cw * 256);
-  } else if (cw == g) {
+  } else if (cw == G) {
     qk_norm_rope((const float*)(act + kAttKraw), ring + ring_off(lease, gqoff + 1024u),
                  ring + ring_off(lease, gqoff + 2048u), sh.eps, act + kActK);
-  } else if (cw == g + 1) {
+  } else if (cw == G + 1) {
     const float* vr = (const float*)(act + kAttVraw);
     ((uint32_t*)(act + kActV))[ln] = pack_bf2(vr[2 * ln], vr[2 * ln + 1]);
   }
   lds_barrier();
-  u32x4 qv[kMaxG];
+  // phase 1: scores into LDS (the raw q area is free now)
+  float* sc = (float*)(act + kAttS);  // [G][128]
+  {
+    const int sub = ln & 15, rowid = cw * 4 + (ln >> 4);
+    u32x4 qv[G], kv[5];
 #pragma unroll
-  for (int j = 0; j < kMaxG; ++j)
-    if (j < g) qv[j] = *(const u32x4*)(act + kActQ + j * 256 + sub * 16);
-  const u32x4 knew = *(const u32x4*)(act + kActK + sub * 16);
-  const u32x4 vnew = *(const u32x4*)(act + kActV + sub * 16);
-  float m[kMaxG], l[kMaxG], acc[kMaxG][8];
+    for (int j = 0; j < G; ++j) qv[j] = *(const u32x4*)(act + kActQ + j * 256 + sub * 16);
 #pragma unroll
-  for (int j = 0; j < kMaxG; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[j][q] = 0.f;
-  }
-  for (int u = rowid; u < ntok; u += kNCW * 4) {
-    u32x4 kv, vv;
-    if (u < nk) {
-      kv = *(const u32x4*)(ring + ring_off(lease, (uint32_t)u * 256u + sub * 16u));
-      vv = *(const u32x4*)(ring + ring_off(lease, voff + (uint32_t)u * 256u + sub * 16u));
-    } else {
-      kv = knew;
-      vv = vnew;
+    for (int it = 0; it < 5; ++it) {  // 5 * 28 >= 128 tokens; a row past the end reloads the last
+      const int u = min(rowid + it * kNCW * 4, ntok - 1);
+      kv[it] = *(const u32x4*)(u < nk ? ring + ring_off(lease, (uint32_t)u * 256u + sub * 16u) : act + kActK + sub * 16);
     }
-    const uint32_t vs[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-    for (int j = 0; j < kMaxG; ++j) {
-      if (j < g) {
-        const float sc = row16_sum(dot8(kv, qv[j], 0.f)) * scale;
-        const float mn = fmaxf(m[j], sc);
-        const float c = __expf(m[j] - mn), p = __expf(sc - mn);
-        l[j] = l[j] * c + p;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[j][2 * q] = acc[j][2 * q] * c + p * bf2f(vs[q] & 0xffffu);
-          acc[j][2 * q + 1] = acc[j][2 * q + 1] * c + p * bf2f(vs[q] >> 16);
-        }
-        m[j] = mn;
-      }
-    }
-  }
-  // merge the wave's four rows (lane exchange across rows), then publish per wave
-  float* mrg = (float*)(act + kActMerge);  // [wave][g][130]: m, l, O[128] (unnormalised)
-#pragma unroll
-  for (int j = 0; j < kMaxG; ++j) {
-    if (j < g) {
-      // rescale every row to the wave's maximum, then sum the rows lane by lane
-      const float M = rows_max(m[j]);
-      const float e = (M == -INFINITY || m[j] == -INFINITY) ? 0.f : __expf(m[j] - M);
-      l[j] = rows_sum(l[j] * e);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[j][q] = rows_sum(acc[j][q] * e);
-      m[j] = M;
-      float* slot = mrg + ((size_t)cw * g + j) * 130;
-      if (ln < 16) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) slot[2 + sub * 8 + q] = acc[j][q];
-      }
-      if (ln == 0) {
-        slot[0] = m[j];
-        slot[1] = l[j];
-      }
+    for (int j = 0; j < G; ++j) {
+      const float v = butterfly4(dot8(kv[0], qv[j], 0.f), dot8(kv[1], qv[j], 0.f), dot8(kv[2], qv[j], 0.f),
+                                 dot8(kv[3], qv[j], 0.f), sub);
+      const int u = rowid + (sub >> 2) * kNCW * 4;  // lanes 4i.. hold the row's token i
+      if ((sub & 3) == 0 && u < ntok) sc[j * 128 + u] = v * scale;
+      const float v4 = row16_sum(dot8(kv[4], qv[j], 0.f));
+      const int u4 = rowid + 4 * kNCW * 4;
+      if (sub == 0 && u4 < ntok) sc[j * 128 + u4] = v4 * scale;
     }
   }
   lds_barrier();
-  float* out = (float*)(smem + kOutOff);
-  for (int o = cw * 64 + ln; o < g * 128; o += kNCW * 64) {
-    const int j = o >> 7, i = o & 127;
-    float M = -INFINITY;
+  // phase 2: per-head maximum and sum of exponentials (wave-uniform), then the exponentials of
+  // this wave's tokens t = cw + 7 i (lane i < 20) into pw[cw][j][i] (0 past the end)
+  float mh[G], lh[G];
+  float* pw = (float*)(act + kAttP) + cw * G * 20;
+  {
+    const bool in0 = ln < ntok, in1 = ln + 64 < ntok;
+    const int tw = cw + kNCW * ln;
 #pragma unroll
-    for (int w = 0; w < kNCW; ++w) M = fmaxf(M, mrg[((size_t)w * g + j) * 130]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNCW; ++w) {
-      const float* slot = mrg + ((size_t)w * g + j) * 130;
-      const float e = slot[0] == -INFINITY ? 0.f : __expf(slot[0] - M);
-      L += slot[1] * e;
-      O += slot[2 + i] * e;
+    for (int j = 0; j < G; ++j) {
+      const float a0 = in0 ? sc[j * 128 + ln] : -INFINITY, a1 = in1 ? sc[j * 128 + 64 + ln] : -INFINITY;
+      mh[j] = wave_max(fmaxf(a0, a1));
+      lh[j] = wave_sum((in0 ? __expf(a0 - mh[j]) : 0.f) + (in1 ? __expf(a1 - mh[j]) : 0.f));
+      if (ln < 20) pw[j * 20 + ln] = tw < ntok ? __expf(sc[j * 128 + min(tw, 127)] - mh[j]) : 0.f;
     }
-    out[o] = O / L;
-    if (i == 0) out[g * 128 + j] = M + __logf(L);
+  }
+  // phase 3: this wave's tokens, four at a time; lane ln owns dims 2 ln, 2 ln + 1
+  float acc[G][2];
+#pragma unroll
+  for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = 0.f;
+  const int nw = ntok > cw ? (ntok - cw + kNCW - 1) / kNCW : 0;
+  for (int i = 0; i < nw; i += 4) {
+    uint32_t vw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = min(cw + kNCW * (i + k), ntok - 1);  // past the end: any valid token, weight 0
+      vw[k] = *(const uint32_t*)(t < nk ? ring + ring_off(lease, voff + (uint32_t)t * 256u + ln * 4u) : act + kActV + ln * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const f32x4 pj = *(const f32x4*)(pw + j * 20 + i);
+      const float pk[4] = {pj.x, pj.y, pj.z, pj.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[j][0] += pk[k] * bf2f(vw[k] & 0xffffu);
+        acc[j][1] += pk[k] * bf2f(vw[k] >> 16);
+      }
+    }
+  }
+  float* mrg = (float*)(act + kActMerge);  // [wave][G][128] partial P V
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const f32x2 v = {acc[j][0], acc[j][1]};
+    *(f32x2*)(mrg + (cw * G + j) * 128 + 2 * ln) = v;
+  }
+  lds_barrier();
+  float* out = (float*)(smem + kOutOff);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    // output o = j * 128 + d of head j by flat lane cw * 64 + ln < 128 ... spread over the waves
+    for (int d = cw * 64 + ln; d < 128; d += kNCW * 64) {
+      float O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNCW; ++w) O += mrg[(w * G + j) * 128 + d];
+      out[j * 128 + d] = O / lh[j];
+    }
+  }
+  if (cw == kNCW - 1 && ln < G) {
+    float M = mh[0], L = lh[0];
+#pragma unroll
+    for (int jj = 1; jj < G; ++jj)
+      if (jj == ln) {
+        M = mh[jj];
+        L = lh[jj];
+      }
+    out[G * 128 + ln] = M + __logf(L);
+  }
+}
+
+DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
+  switch (a.sh.g) {
+    case 1: attn_body<1>(a, in, smem, act, lease, cw); break;
+    case 2: attn_body<2>(a, in, smem, act, lease, cw); break;
+    case 3: attn_body<3>(a, in, smem, act, lease, cw); break;
+    case 4: attn_body<4>(a, in, smem, act, lease, cw); break;
+    default: attn_body<5>(a, in, smem, act, lease, cw); break;
   }
 }
 
@@ -690,7 +746,7 @@ DEV bool arrive(const KArgs& a, const Instr& in) {
 
 // controller timestamps of one instruction (trace build)
 struct Stamps {
-  unsigned long long ack, arr;
+  unsigned long long ack, arr, c1, c2;  // c1 / c2: split combine staged / computed
 };
 
 DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) {
@@ -721,10 +777,45 @@ DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
   const bool last = arrive(a, in);
   if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
   if (!last) return;
-  // combine the group's splits, o = sum_i exp(lse_i - lse) O_i with lse = log sum_i exp(lse_i),
-  // online over chunks of splits staged into LDS: lanes over splits take the statistics,
-  // lanes over 4-dim units accumulate the outputs
+  // combine the group's splits, o = sum_i exp(lse_i - lse) O_i with lse = log sum_i exp(lse_i)
   char* act = smem + kActOff;
+  uint16_t* o = (uint16_t*)s_ld64(row + ATT_O) + (size_t)r * sh.Hq * 128;
+  __amdgpu_buffer_rsrc_t ro = rsrc(o);
+  if ((uint32_t)ns * pstride * 4u <= (uint32_t)kActStageBytes && ns <= 64) {
+    // every split at once: lane t < ns takes the weights of split t, then lanes over 4-dim units
+    // accumulate the outputs in split order
+    stage(part + gbase, (uint32_t)ns * pstride * 4u, act);
+    wait_vm0();
+    if (a.flags & MK_FLAG_TRACE) st.c1 = rtc();
+    const float* pl = (const float*)act;
+    float* wts = (float*)(smem + kOutOff);  // [64][kMaxG] normalised weights
+    const int ln = (int)lane();
+    for (int j = 0; j < g; ++j) {
+      const float lv = ln < ns ? pl[ln * pstride + g * 128 + j] : -INFINITY;
+      const float M = wave_max(lv);
+      const float e = ln < ns ? __expf(lv - M) : 0.f;
+      const float S = wave_sum(e);
+      if (ln < ns) wts[ln * kMaxG + j] = e / S;
+    }
+    for (int u = 0; u * 256 < g * 128; ++u) {
+      const int oi = u * 256 + 4 * ln;
+      if (oi < g * 128) {
+        const int j = oi >> 7;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int t = 0; t < ns; ++t) acc += wts[t * kMaxG + j] * *(const f32x4*)(pl + t * pstride + oi);
+        const uint32_t col = (uint32_t)hk * g * 128u + (uint32_t)oi;
+        st32(ro, col * 2u, pack_bf2(acc.x, acc.y));
+        st32(ro, col * 2u + 4u, pack_bf2(acc.z, acc.w));
+      }
+    }
+    if (a.flags & MK_FLAG_TRACE) st.c2 = rtc();
+    wait_vm0();
+    signal_all(a, in);
+    return;
+  }
+  // many splits: online over chunks of splits staged into LDS: lanes over splits take the
+  // statistics, lanes over 4-dim units accumulate the outputs
   float* wts = (float*)(smem + kOutOff);          // [64][kMaxG] weights of the chunk's splits
   float* hst = (float*)(smem + kOutOff) + 64 * kMaxG;  // [kMaxG][3]: running max, sum, chunk rescale
   const uint32_t chunk = min(64u, (uint32_t)kActStageBytes / (pstride * 4u));
@@ -742,6 +833,7 @@ DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
     const int nc = min((int)chunk, ns - t0);
     stage(part + gbase + (uint32_t)t0 * pstride, (uint32_t)nc * pstride * 4u, act);
     wait_vm0();
+    if ((a.flags & MK_FLAG_TRACE) && t0 == 0) st.c1 = rtc();
     const float* pl = (const float*)act;
     for (int j = 0; j < g; ++j) {
       const float lv = ln < nc ? pl[ln * pstride + g * 128 + j] : -INFINITY;
@@ -778,8 +870,7 @@ DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
       }
     }
   }
-  uint16_t* o = (uint16_t*)s_ld64(row + ATT_O) + (size_t)r * sh.Hq * 128;
-  __amdgpu_buffer_rsrc_t ro = rsrc(o);
+  if (a.flags & MK_FLAG_TRACE) st.c2 = rtc();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int unit = ln + 64 * u;
@@ -816,34 +907,35 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
   const uint32_t op = in.w[W_OPCODE];
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int n0 = in.w[W_P1], nr = in.w[W_P2];
-  const float* out = (const float*)(smem + kOutOff);
+  const float* part = (const float*)(smem + kOutOff);  // block sums of the tile
+  const int KB = (int)in.w[W_P4] >> 9;  // quads per row
   const int j = (int)lane();
   if (op == OP_QKV) {
     __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + QKV_OUT));
-    for (int jj = j; jj < nr; jj += 64) st32(ro, (uint32_t)(n0 + jj) * 4u, __float_as_uint(out[jj]));
+    for (int jj = j; jj < nr; jj += 64) st32(ro, (uint32_t)(n0 + jj) * 4u, __float_as_uint(row_sum(part, jj, KB)));
   } else if (op == OP_OPROJ) {
     __amdgpu_buffer_rsrc_t r2 = rsrc((const void*)s_ld64(row + O_R2));
     const float* r1 = (const float*)(smem + kActOff + kActR1);
     for (int jj = j; jj < nr; jj += 64) {
-      const float av = bf2f(pack_bf2(out[jj], 0.f) & 0xffffu);
+      const float av = bf2f(pack_bf2(row_sum(part, jj, KB), 0.f) & 0xffffu);
       st32(r2, (uint32_t)(n0 + jj) * 4u, __float_as_uint(r1[jj] + av));
     }
   } else if (op == OP_GATEUP) {
     __amdgpu_buffer_rsrc_t rm = rsrc((const void*)s_ld64(row + GU_M));
     for (int jj = j; jj < nr; jj += 64) {
-      const float gv = out[jj], uv = out[nr + jj];
+      const float gv = row_sum(part, jj, KB), uv = row_sum(part, nr + jj, KB);
       st16(rm, (uint32_t)(n0 + jj) * 2u, pack_bf2(gv / (1.f + __expf(-gv)) * uv, 0.f));
     }
   } else if (op == OP_DOWN) {
     __amdgpu_buffer_rsrc_t ry = rsrc((const void*)s_ld64(row + DN_Y));
-    for (int jj = j; jj < nr; jj += 64) st16(ry, (uint32_t)(n0 + jj) * 2u, pack_bf2(out[jj], 0.f));
+    for (int jj = j; jj < nr; jj += 64) st16(ry, (uint32_t)(n0 + jj) * 2u, pack_bf2(row_sum(part, jj, KB), 0.f));
   } else if (op == OP_LMHEAD) {
     __amdgpu_buffer_rsrc_t rl = rsrc((const void*)s_ld64(row + LM_LOGITS));
     __amdgpu_buffer_rsrc_t rp = rsrc((const void*)s_ld64(row + LM_PART));
     float best = -INFINITY;
     int bi = 0x7fffffff;
     for (int jj = j; jj < nr; jj += 64) {
-      const float v = out[jj];
+      const float v = row_sum(part, jj, KB);
       st32(rl, (uint32_t)(n0 + jj) * 4u, __float_as_uint(v));
       if (v > best) {
         best = v;
@@ -902,9 +994,11 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
 // ---------------------------------------------------------------------------------------
 // the two roles
 
-// barriers between the compute-start and compute-end barriers: attention (QK-norm / RoPE, wave
-// merge), the fused norm of QKV / GATE_UP / LM_HEAD
-DEV int inner_barriers(uint32_t op) { return op == OP_ATTN ? 2 : ((op == OP_QKV || op == OP_GATEUP || op == OP_LMHEAD) ? 1 : 0); }
+// barriers between the compute-start and compute-end barriers: attention (QK-norm / RoPE,
+// scores, P V)
+// (the fused norm's barrier of a projection is taken inside proj_body; with every op body
+// skipped, no wave takes any)
+DEV int inner_barriers(uint32_t op, bool noop_only) { return op == OP_ATTN && !noop_only ? 3 : 0; }
 
 // returns false when the watchdog expired or another worker aborted
 struct WaitCache {  // the last (event, threshold) wait found satisfied in this run
@@ -969,10 +1063,11 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     if (op == OP_NOOP) continue;
     const bool tracing = a.flags & MK_FLAG_TRACE;
     const unsigned long long t_vis = tracing ? rtc() : 0;
+    const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
     uint32_t poll = 0;
     bool ok = graph ? true : wait_events(a, in, poll, wc);
     const unsigned long long t_ready = tracing ? rtc() : 0;
-    Stamps st{0, 0};
+    Stamps st{0, 0, 0, 0};
     if (ok && !noop_only) {
       const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
       char* act = smem + kActOff;
@@ -983,10 +1078,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       } else if (op == OP_DOWN) {
         stage((const void*)s_ld64(row + DN_M), 2u * a.sh.I, act);
         wait_vm0();
-      } else if (op != OP_LMHEAD || last_row != in.w[W_ROW]) {  // inputs of the fused add + RMSNorm
+      } else if (fused_norm) {  // fused add + RMSNorm (once per lm_head run)
         const int sx = op == OP_QKV ? QKV_X : LM_Y, sr = op == OP_QKV ? QKV_RIN : (op == OP_GATEUP ? GU_R2 : LM_R2);
         norm_stage(op == OP_GATEUP ? nullptr : (const uint16_t*)s_ld64(row + sx), (const float*)s_ld64(row + sr),
-                   a.sh.H, act);
+                   a.sh.H, a.sh.eps, act, smem);
       }
       last_row = in.w[W_ROW];
     }
@@ -996,7 +1091,12 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     const unsigned long long t_a = tracing ? rtc() : 0;
     const unsigned long long c_a = tracing ? __builtin_readcyclecounter() : 0;
     if (!ok) break;
-    for (int b = 0; b < inner_barriers(op); ++b) lds_barrier();
+    if (op != OP_ATTN && !noop_only) {  // the controller is the eighth wave of a projection tile
+      const uint32_t lease = uni(((const uint32_t*)(smem + kCtrlOff + kLeaseTabOff))[i & 15]);  // compute wave 0's table
+      proj_body(a, in, smem, lease, fused_norm, kNW - 1);
+    } else {
+      for (int b = 0; b < inner_barriers(op, noop_only); ++b) lds_barrier();
+    }
     lds_barrier();  // B: compute done, results in the output area
     const unsigned long long t_b = tracing ? rtc() : 0;
     const unsigned long long c_b = tracing ? __builtin_readcyclecounter() : 0;
@@ -1023,16 +1123,19 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       tr[7] = (uint32_t)rtc();
       tr[8] = poll;
       tr[9] = (uint32_t)(c_b - c_a);  // shader clock cycles between the two compute barriers
+      tr[10] = (uint32_t)st.c1;
+      tr[11] = (uint32_t)st.c2;
     }
   }
 }
 
 DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, int cw, char* smem) {
   const uint32_t* ctrl = (const uint32_t*)(smem + kCtrlOff);  // LDS abort flag
-  uint32_t* lease_tab = (uint32_t*)(smem + kCtrlOff + 64) + cw * 32;  // [16] lease, [16] issued_end
+  uint32_t* lease_tab = (uint32_t*)(smem + kCtrlOff + kLeaseTabOff) + cw * 32;  // [16] lease, [16] issued_end
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
   const int lookahead = (a.flags & MK_FLAG_NO_PREFETCH) ? 0 : 15;
   uint32_t head = 0, issued = 0;
+  uint32_t last_row = 0xFFFFFFFFu;  // as in the controller: the lm_head norm runs once per worker
   int pf_i = 0;
   for (int i = 0; i < count; ++i) {
     Instr in;
@@ -1042,6 +1145,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       if (pf_i <= i) pf_i = i + 1;
       continue;
     }
+    const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
     if (!noop_only) {
       // pages of every instruction before i are free now
       const uint32_t freed = (pf_i > i) ? uni(lease_tab[i & 15]) : head;
@@ -1072,26 +1176,14 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
     if (!noop_only) {
       const uint32_t lease = uni(lease_tab[i & 15]);
       char* act = smem + kActOff;
-      float* out = (float*)(smem + kOutOff);
       if (op == OP_ATTN) {
         attn_compute(a, in, smem, act, lease, cw);
       } else {
-        const int nr = in.w[W_P2], K = in.w[W_P4];
-        const uint32_t wblk = blocks_of((uint32_t)nr * K * 2u);
-        uint32_t hoff = 0;
-        if (op == OP_QKV || op == OP_GATEUP || op == OP_LMHEAD) {
-          const uint32_t goff = (op == OP_GATEUP ? 2u : 1u) * wblk * 1024u;
-          hoff = kb_round(2u * K) + kb_round(4u * K);  // after the staged x and r
-          if (op == OP_GATEUP)
-            norm_h<false>(smem, lease, goff, K, a.sh.eps, cw, hoff);
-          else
-            norm_h<true>(smem, lease, goff, K, a.sh.eps, cw, hoff);
-          lds_barrier();
-        }
-        gemv(smem, lease, op == OP_GATEUP ? 2 * nr : nr, nr, wblk * 1024u, K, cw, out, hoff);
+        proj_body(a, in, smem, lease, fused_norm, cw);
       }
+      last_row = in.w[W_ROW];
     } else {
-      for (int b = 0; b < inner_barriers(op); ++b) lds_barrier();
+      for (int b = 0; b < inner_barriers(op, noop_only); ++b) lds_barrier();
     }
     lds_barrier();  // B
   }
