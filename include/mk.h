@@ -47,7 +47,8 @@ typedef enum {
 
 enum {
   MK_FLAG_NO_PREFETCH = 1u << 0, /* megakernel: no weight prefetch across instructions (ablation) */
-  MK_FLAG_NOOP_ONLY = 1u << 1,   /* megakernel: run the queue shape with every op body skipped */
+  MK_FLAG_NOOP_ONLY = 1u << 1,   /* megakernel: run the queue with every op body skipped: the waits,
+                                    stagings and output stores remain, weights are not read */
   MK_FLAG_TRACE = 1u << 2        /* megakernel: record per-instruction timestamps */
 };
 
@@ -119,14 +120,22 @@ mk_status mk_plan_info(const mk_plan* plan, int32_t* n_tasks, int32_t* n_ops, in
 /* Bytes of scratch the caller passes as MK_T_WORKSPACE. */
 mk_status mk_plan_workspace_bytes(const mk_plan* plan, size_t* bytes);
 
-/* Byte offset and size of a named intermediate inside the workspace ("qkv" fp32 [M, N_qkv],
- * "o" bf16 [M, Hq d], "m" bf16 [M, I], "r2a"/"r2b" fp32, "ya"/"yb" bf16) for inspection. */
+/* Byte offset and size of a named intermediate inside the workspace, for inspection.  Vectors
+ * written inside a run are tagged records of 8 bytes {uint32 payload, uint32 tag}, the tag being
+ * epoch * 1024 + layer + 1 of the run and layer that wrote them (epoch = runs of this plan
+ * before): "qkv" fp32 [M, N_qkv], "o" bf16 pairs [M, Hq d / 2], "m" bf16 pairs [M, I / 2],
+ * "r2" fp32 [M, H] (residual after attention), "r1" fp32 [M, H] (r2 + y, the next layer's
+ * residual input).  "part" holds the split-KV partials as plain fp32, "lm_part" the lm_head
+ * tile maxima. */
 mk_status mk_plan_workspace_region(const mk_plan* plan, const char* name, size_t* offset, size_t* bytes);
 
 /* Run the plan once as ONE persistent kernel launch on `hip_stream` (asynchronous).
- * Workers wait on event counters (polled with a bounded-time watchdog) and signal them
- * after their outputs are stored.  Not capturable into a graph (the run epoch is a launch
- * argument).  Runs on one plan must be issued on one stream. */
+ * An instruction's waits are realised on the data: producers store tagged records (see
+ * mk_plan_workspace_region), and a consumer stages the records it needs until all carry the
+ * run's tag -- the event reaches its threshold when every producer tile's records are current.
+ * Polls are bounded by a watchdog.  The split-KV combine and the argmax use arrival counters.
+ * Not capturable into a graph (the run epoch is a launch argument).  Runs on one plan must be
+ * issued on one stream. */
 mk_status mk_run_layer(mk_plan* plan, const mk_tensors* tensors, void* hip_stream);
 
 /* Run the same op bodies as one standalone kernel per op (one tile per block) inside a

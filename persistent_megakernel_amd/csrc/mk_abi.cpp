@@ -5,6 +5,8 @@
 // OperandPtrTable).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -46,7 +48,8 @@ struct mk_plan {
   float* d_rope = nullptr;
   uint32_t* d_trace = nullptr;
   size_t events_bytes = 0, arrivals_bytes = 0;
-  uint32_t epoch = 0;
+  uint32_t epoch = 0;  // megakernel runs so far; never reset (record tags must not repeat)
+  uint32_t salt = 0;   // per-plan record tag base, a multiple of 1024
   bool occupancy_checked = false;
   bool host_only = false;  // planned without a device: queue inspection only
   std::map<std::vector<uint64_t>, uint64_t*> tables;
@@ -89,16 +92,8 @@ void fill_table(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& ta
   const uint64_t cache_layer = (uint64_t)c.num_phys_pages * c.page_size * Hkv * d * 2;
   const uint64_t ws = t->ptr[MK_T_WORKSPACE];
   const int L = c.num_layers;
-  auto r2buf = [&](int l) -> uint64_t {
-    if (l == L - 1) return t->ptr[MK_T_R2_OUT];
-    return ws + region_off(hp, (l & 1) ? "r2b" : "r2a");
-  };
-  auto ybuf = [&](int l) -> uint64_t {
-    if (l == L - 1) return t->ptr[MK_T_Y_OUT];
-    return ws + region_off(hp, (l & 1) ? "yb" : "ya");
-  };
-  auto xin = [&](int l) { return l == 0 ? t->ptr[MK_T_X] : ybuf(l - 1); };
-  auto rin = [&](int l) { return l == 0 ? t->ptr[MK_T_R_IN] : r2buf(l - 1); };
+  const uint64_t qkv = ws + region_off(hp, "qkv"), ob = ws + region_off(hp, "o"), mb = ws + region_off(hp, "m");
+  const uint64_t r2b = ws + region_off(hp, "r2"), r1b = ws + region_off(hp, "r1");
   tab.assign(hp.ops.size() * kTableSlots, 0);
   for (size_t row = 0; row < hp.ops.size(); ++row) {
     uint64_t* s = &tab[row * kTableSlots];
@@ -107,44 +102,48 @@ void fill_table(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& ta
       case OP_QKV:
         s[QKV_W] = t->ptr[MK_T_W_QKV] + l * nqkv * H * welem;
         s[QKV_GAMMA] = t->ptr[MK_T_G_ATTN] + l * H * 2;
-        s[QKV_X] = xin(l);
-        s[QKV_RIN] = rin(l);
-        s[QKV_OUT] = ws + region_off(hp, "qkv");
+        s[QKV_X] = l == 0 ? t->ptr[MK_T_X] : 0;
+        s[QKV_RIN] = l == 0 ? t->ptr[MK_T_R_IN] : 0;
+        s[QKV_OUT] = qkv;
+        s[QKV_R1] = l == 0 ? 0 : r1b;
         break;
       case OP_ATTN:
-        s[ATT_QKV] = ws + region_off(hp, "qkv");
+        s[ATT_QKV] = qkv;
         s[ATT_GQ] = t->ptr[MK_T_G_Q] + l * d * 2;
         s[ATT_GK] = t->ptr[MK_T_G_K] + l * d * 2;
         s[ATT_KC] = t->ptr[MK_T_K_CACHE] + l * cache_layer;
         s[ATT_VC] = t->ptr[MK_T_V_CACHE] + l * cache_layer;
         s[ATT_BT] = t->ptr[MK_T_BLOCK_TABLE];
         s[ATT_PART] = ws + region_off(hp, "part");
-        s[ATT_O] = ws + region_off(hp, "o");
+        s[ATT_O] = ob;
         s[ATT_ROPE] = (uint64_t)p->d_rope;
         break;
       case OP_OPROJ:
         s[O_W] = t->ptr[MK_T_W_O] + l * H * Hq * d * welem;
-        s[O_IN] = ws + region_off(hp, "o");
-        s[O_X] = xin(l);
-        s[O_RIN] = rin(l);
-        s[O_R2] = r2buf(l);
+        s[O_IN] = ob;
+        s[O_X] = l == 0 ? t->ptr[MK_T_X] : 0;
+        s[O_RIN] = l == 0 ? t->ptr[MK_T_R_IN] : 0;
+        s[O_R2] = r2b;
+        s[O_R1] = l == 0 ? 0 : r1b;
+        s[O_R2OUT] = l == L - 1 ? t->ptr[MK_T_R2_OUT] : 0;
         break;
       case OP_GATEUP:
         s[GU_W] = t->ptr[MK_T_W_GU] + l * 2 * I * H * welem;
         s[GU_GAMMA] = t->ptr[MK_T_G_MLP] + l * H * 2;
-        s[GU_R2] = r2buf(l);
-        s[GU_M] = ws + region_off(hp, "m");
+        s[GU_R2] = r2b;
+        s[GU_M] = mb;
         break;
       case OP_DOWN:
         s[DN_W] = t->ptr[MK_T_W_DOWN] + l * H * I * welem;
-        s[DN_M] = ws + region_off(hp, "m");
-        s[DN_Y] = ybuf(l);
+        s[DN_M] = mb;
+        s[DN_Y] = l == L - 1 ? t->ptr[MK_T_Y_OUT] : 0;
+        s[DN_R2] = r2b;
+        s[DN_R1] = r1b;
         break;
       case OP_LMHEAD:
         s[LM_W] = t->ptr[MK_T_W_LM];
         s[LM_GAMMA] = t->ptr[MK_T_G_FINAL];
-        s[LM_Y] = ybuf(L - 1);
-        s[LM_R2] = r2buf(L - 1);
+        s[LM_R1] = r1b;
         s[LM_LOGITS] = t->ptr[MK_T_LOGITS_OUT];
         s[LM_PART] = ws + region_off(hp, "lm_part");
         s[LM_TOKEN] = t->ptr[MK_T_TOKEN_OUT];
@@ -177,11 +176,11 @@ mk_status check_runnable(mk_plan* p) {
   const mk_config& c = hp.cfg;
   if (hp.tp.spec != 0 || c.weight_fp8 || c.act_fp8)
     return fail(MK_ERR_UNSUPPORTED, "only the bf16 single-token (M = 1) op bodies are built");
-  if (c.hidden > 3072 || c.inter > 8192 || c.n_q_heads * c.head_dim > 8192 || hp.tp.r_o > 256 ||
-      c.n_q_heads / c.n_kv_heads > mk::dev::kMaxG || c.hidden % 512 || c.inter % 512 ||
-      (c.n_q_heads * c.head_dim) % 512)
-    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 3072; inter, q width <= 8192; "
-                                    "hidden, inter and q width multiples of 512; GQA group <= 5)");
+  if (c.hidden > 2048 || c.inter > 6144 || c.n_q_heads * c.head_dim > 6144 || hp.tp.r_o > 128 ||
+      hp.tp.r_down > 128 || hp.tp.r_gu % 2 || c.n_q_heads / c.n_kv_heads > mk::dev::kMaxG || c.hidden % 512 ||
+      c.inter % 512 || (c.n_q_heads * c.head_dim) % 512)
+    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 2048; inter, q width <= 6144; "
+                                    "hidden, inter and q width multiples of 512; even gate/up tiles; GQA group <= 5)");
   if (!p->occupancy_checked) {
     int per_cu = 0;
     HIP_TRY(hipSetDevice(p->device));
@@ -200,7 +199,7 @@ mk::KArgs base_args(const mk_plan* p, const uint64_t* table) {
   a.arrivals = p->d_arrivals;
   a.err = p->d_err;
   a.trace = p->d_trace;
-  a.epoch = p->epoch;
+  a.tag0 = p->salt + p->epoch * 1024u;
   a.flags = p->hp.cfg.flags;
   a.sh = p->sh;
   return a;
@@ -216,6 +215,12 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
   if (!cfg || !host_context_lens || !out) return fail(MK_ERR_INVALID, "null argument");
   *out = nullptr;
   auto p = std::make_unique<mk_plan>();
+  {  // record tag base of this plan: a plan count and the clock mixed (multiplicative hashing)
+    static std::atomic<uint32_t> plans{0};
+    const uint64_t ns = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    uint32_t h = (plans.fetch_add(1) + 1u) * 0x9E3779B1u ^ (uint32_t)(ns ^ (ns >> 32)) * 0x85EBCA77u;
+    p->salt = h & ~1023u;
+  }
   // without a device (host-only planning, e.g. to inspect queues) the worker count must be given
   bool have_device = hipGetDevice(&p->device) == hipSuccess;
   if (have_device) {
@@ -320,7 +325,10 @@ mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
   if (st != MK_OK) return st;
   if ((st = check_runnable(p)) != MK_OK) return st;
   uint64_t* table = nullptr;
+  const bool new_set = p->tables.find(std::vector<uint64_t>(t->ptr, t->ptr + t->n)) == p->tables.end();
   if ((st = get_table(p, t, &table)) != MK_OK) return st;
+  if (new_set)  // a workspace first seen by this plan: no stale record may carry one of its tags
+    HIP_TRY(hipMemsetAsync((void*)t->ptr[MK_T_WORKSPACE], 0, p->hp.workspace_bytes, (hipStream_t)stream));
   mk::KArgs a = base_args(p, table);
   a.instrs = p->d_queue;
   a.L = p->hp.L;
@@ -421,10 +429,9 @@ mk_status mk_sync(mk_plan* p, void* stream) {
     HIP_TRY(hipMemset(p->d_arrivals, 0, p->arrivals_bytes));
     HIP_TRY(hipMemset(p->d_err, 0, 64));
     HIP_TRY(hipDeviceSynchronize());
-    p->epoch = 0;
     return fail(MK_ERR_TIMEOUT, "watchdog: worker " + std::to_string(e[1]) + " task " + std::to_string(e[2]) +
-                                    " event " + std::to_string(e[3]) + " value " + std::to_string(e[4]) +
-                                    " target " + std::to_string(e[5]));
+                                    " waited for tag " + std::to_string(e[3]) + " over " + std::to_string(e[4]) +
+                                    " polls");
   }
   return MK_OK;
 }

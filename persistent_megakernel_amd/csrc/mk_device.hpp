@@ -23,7 +23,7 @@ struct KArgs {
   uint32_t* arrivals;      // [A], kSubStride words apart, self re-arming
   uint32_t* err;           // device error record: flag, worker, task, event, value, target
   uint32_t* trace;         // [W, L, kTraceWords] or null
-  uint32_t epoch;          // runs of this plan so far: a wait on threshold t targets (epoch+1)*t
+  uint32_t tag0;           // megakernel: this run's record tag base (plan salt + runs so far * 1024)
   uint32_t flags;          // MK_FLAG_* | kModeGraph
   Shapes sh;
 };
@@ -58,15 +58,15 @@ constexpr int kActQ = 0;       // bf16 [g][128] rotated q heads
 constexpr int kActK = 2048;    // bf16 [128] new key
 constexpr int kActV = 2304;    // bf16 [128] new value
 constexpr int kActMerge = 2560;  // fp32 [7 waves][g][128] per-wave partial P V (<= 17920 bytes)
-constexpr int kAttQraw = 21504;  // fp32 staging of the raw q heads (4 KiB), k and v (1 KiB each)
-constexpr int kAttKraw = 25600;
-constexpr int kAttVraw = 26624;
-constexpr int kAttS = kAttQraw;  // fp32 [g][128] scores, once QK-norm / RoPE consumed the raw q
+constexpr int kAttQraw = 4096;   // tagged records of the raw q heads (g KiB), k and v (1 KiB each);
+constexpr int kAttKraw = kAttQraw + kMaxG * 1024;  // consumed before the merge area is written
+constexpr int kAttVraw = kAttKraw + 1024;
+constexpr int kAttS = 21504;     // fp32 [g][128] scores
 constexpr int kAttP = kAttS + kMaxG * 512;  // fp32 [7 waves][g][20] exponentials of each wave's tokens
-constexpr int kActR1 = 16384;   // O projection: fp32 r_in + x of the tile's rows (<= 256)
-static_assert(kActMerge + 7 * kMaxG * 128 * 4 <= kAttQraw, "attention staging overlaps");
+constexpr int kActR1 = kActBytes - 1024;    // O projection / down: residual rows of the tile as records (<= 128)
+static_assert(kActMerge + 7 * kMaxG * 128 * 4 <= kAttS, "attention merge area overlaps the scores");
+static_assert(kAttVraw + 1024 <= kAttS, "attention staging overlaps the scores");
 static_assert(kAttP + 7 * kMaxG * 20 * 4 <= kActBytes, "attention exponentials overflow the staging area");
-static_assert(kAttVraw + 1024 <= kActBytes, "attention staging overflows");
 static_assert(kLdsBytes == 163840, "LDS budget");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 }  // namespace dev

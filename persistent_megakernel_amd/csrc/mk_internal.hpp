@@ -41,12 +41,15 @@ enum Word : int {
 
 // operand pointer table: 16 slots per op row
 constexpr int kTableSlots = 16;
-enum QkvSlot { QKV_W = 0, QKV_GAMMA, QKV_X, QKV_RIN, QKV_OUT };
+// Workspace vectors written inside a run (qkv, o, m, r2, r1) hold tagged 8-byte records
+// {payload, tag}; X / RIN are the caller's first-layer inputs, R2OUT / Y the caller's last-layer
+// outputs (0 on other layers).
+enum QkvSlot { QKV_W = 0, QKV_GAMMA, QKV_X, QKV_RIN, QKV_OUT, QKV_R1 };
 enum AttnSlot { ATT_QKV = 0, ATT_GQ, ATT_GK, ATT_KC, ATT_VC, ATT_BT, ATT_PART, ATT_O, ATT_ROPE };
-enum OSlot { O_W = 0, O_IN, O_X, O_RIN, O_R2 };
+enum OSlot { O_W = 0, O_IN, O_X, O_RIN, O_R2, O_R1, O_R2OUT };
 enum GuSlot { GU_W = 0, GU_GAMMA, GU_R2, GU_M };
-enum DownSlot { DN_W = 0, DN_M, DN_Y };
-enum LmSlot { LM_W = 0, LM_GAMMA, LM_Y, LM_R2, LM_LOGITS, LM_PART, LM_TOKEN };
+enum DownSlot { DN_W = 0, DN_M, DN_Y, DN_R2, DN_R1 };
+enum LmSlot { LM_W = 0, LM_GAMMA, LM_R1, LM_LOGITS, LM_PART, LM_TOKEN };
 
 struct TileParams {
   int r_qkv = 0, r_o = 0, r_gu = 0, r_down = 0, r_lm = 0, s_tok = 0, spec = 0;

@@ -17,12 +17,14 @@
 // counter is per wave, the polling wave never issues prefetch loads and the prefetching waves
 // never poll, so each side's waits see only its own loads.
 //
-// Cross-CU visibility.  MI355X has one L2 per XCD and plain cached lines are not coherent
-// across XCDs.  Every access to data produced inside a run (activations, partials, counters)
-// is made at device scope (sc1), producers wait for their stores to complete before the
-// relaxed device-scope counter add, and consumers issue their device-scope loads after the
-// satisfying poll -- the release/acquire pairing of the counter protocol without whole-L2
-// write-back / invalidate.
+// Cross-CU visibility and waits.  MI355X has one L2 per XCD and plain cached lines are not
+// coherent across XCDs.  Every value produced inside a run is stored at device scope (sc1) as an
+// 8-byte record {payload, tag}, the tag naming the plan, the run and the producing layer; an
+// aligned 8-byte store is seen whole or not at all.  An event of the queue is thereby
+// carried by the data itself: a consumer's wait is the staging of the records it needs into LDS,
+// repeated for the 1 KiB blocks whose tags are not current yet -- one memory round trip once the
+// data is there, no acknowledgement wait on the producer side and no separate counter.  Only
+// the split-KV combine and the argmax keep an arrival counter (the last arriver reduces).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -162,6 +164,23 @@ DEV void st32(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) { __builtin_am
 DEV void st16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, SC1);
 }
+
+// tagged records (8 bytes each): one {payload, tag} per store, or two adjacent ones in 16 bytes.
+// A megakernel run tags with tag0 + layer + 1 (tag0 = plan salt + runs * 1024: never 0 in the low
+// ten bits); the graph baseline, whose order comes from the stream, writes tag 0, which no
+// megakernel run waits for.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+DEV uint32_t ll_tag(const KArgs& a, uint32_t layer) { return (a.flags & kModeGraph) ? 0u : a.tag0 + layer + 1u; }
+DEV void ll_put(__amdgpu_buffer_rsrc_t r, uint32_t idx, uint32_t payload, uint32_t tag) {
+  const u32x2 v = {payload, tag};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, idx * 8u, 0, SC1);
+}
+DEV void ll_put2(__amdgpu_buffer_rsrc_t r, uint32_t idx, uint32_t p0, uint32_t p1, uint32_t tag) {
+  const u32x4 v = {p0, tag, p1, tag};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, idx * 8u, 0, SC1);
+}
+// the payload of record k of a vector staged into LDS
+DEV float ll_f32(const char* base, int k) { return *(const float*)(base + 8 * k); }
 
 DEV void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -390,31 +409,107 @@ DEV void stage(const void* src, uint32_t bytes, char* dst) {
 }
 DEV uint32_t kb_round(uint32_t bytes) { return (bytes + 1023u) & ~1023u; }
 
-// Fused add + RMSNorm, first half, by the controller: stage x (bf16, may be null) at act[0, 2H)
-// and the residual r (fp32) at act + kb_round(2H) in one round trip, then
-// inv = rsqrt(mean((r + x)^2) + eps) into the control area for norm_h.
-DEV void norm_stage(const uint16_t* x, const float* r, int H, float eps, char* act, char* smem) {
+// A run of tagged records to stage: `bytes` (8 per record) from global `src` into the activation
+// area at `dst` (1 KiB aligned, room for whole 1 KiB blocks); current when every tag is `tag`.
+struct LlRegion {
+  const char* src;
+  uint32_t bytes, dst, tag;
+};
+
+DEV void record_timeout(const KArgs& a, const Instr& in, uint32_t what, uint32_t value) {
+  if (lane() != 0) return;
+  uint32_t z = 0;
+  if (__hip_atomic_compare_exchange_strong(a.err, &z, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(a.err + 1, blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.err + 2, in.w[W_TASK], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.err + 3, what, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.err + 4, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The wait of an instruction: stage every block of its regions in one round trip; with `verify`
+// (the megakernel), stage again the blocks holding a record whose tag is not current, until all
+// are.  False when the watchdog expired or another worker aborted.
+DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, char* act, bool verify, uint32_t& polls) {
+  const uint32_t ln = lane();
+  uint32_t pend[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < nrg) pend[j] = (1u << blocks_of(rg[j].bytes)) - 1u;  // at most 27 blocks
+  const unsigned long long t0 = rtc();
+  for (uint32_t it = 1;; ++it) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      for (uint32_t m = j < nrg ? pend[j] : 0u; m; m &= m - 1u) {
+        const uint32_t b = (uint32_t)__builtin_ctz(m);
+        uint32_t off = b * 1024u + ln * 16u;
+        if (off >= rg[j].bytes) off = b * 1024u;
+        lds_dma16_sc1(rg[j].src + off, (uint32_t)(uintptr_t)(lds_void*)(act + rg[j].dst + b * 1024u));
+      }
+    }
+    wait_vm0();
+    if (!verify) return true;
+    bool done = true;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      for (uint32_t m = j < nrg ? pend[j] : 0u; m; m &= m - 1u) {
+        const uint32_t b = (uint32_t)__builtin_ctz(m);
+        const uint32_t off = b * 1024u + ln * 16u;
+        bool ok = true;
+        if (off < rg[j].bytes) {
+          const u32x4 v = *(const u32x4*)(act + rg[j].dst + off);
+          ok = v.y == rg[j].tag && (off + 8u >= rg[j].bytes || v.w == rg[j].tag);
+        }
+        if (__builtin_amdgcn_ballot_w64(!ok) == 0) pend[j] &= ~(1u << b);
+        else done = false;
+      }
+    }
+    if (done) return true;
+    ++polls;
+    if ((it & 15u) == 0 && __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
+    if (rtc() - t0 > kWatchdogTicks) {
+      record_timeout(a, in, rg[0].tag, polls);
+      return false;
+    }
+  }
+}
+
+// Fused add + RMSNorm.  The residual r sits at act + kb_round(2H): fp32 as the caller gave it
+// (PLAIN: the first layer, with its x at act[0, 2H)) or as tagged records (later layers, no x).
+// The controller takes the sum of squares once staged; all eight waves then write
+// h = bf16((r + x) * rsqrt(mean((r + x)^2) + eps) * gain) over act[0, 2H).
+template <bool PLAIN>
+DEV void norm_chunk(const char* act, uint32_t R0, int c, float v[8]) {
+  if (PLAIN) {
+    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
+    const u32x4 xv = *(const u32x4*)(act + c * 16);
+    v[0] = __uint_as_float(ra.x) + bf2f(xv.x & 0xffffu);
+    v[1] = __uint_as_float(ra.y) + bf2f(xv.x >> 16);
+    v[2] = __uint_as_float(ra.z) + bf2f(xv.y & 0xffffu);
+    v[3] = __uint_as_float(ra.w) + bf2f(xv.y >> 16);
+    v[4] = __uint_as_float(rb.x) + bf2f(xv.z & 0xffffu);
+    v[5] = __uint_as_float(rb.y) + bf2f(xv.z >> 16);
+    v[6] = __uint_as_float(rb.z) + bf2f(xv.w & 0xffffu);
+    v[7] = __uint_as_float(rb.w) + bf2f(xv.w >> 16);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 rr = *(const u32x4*)(act + R0 + c * 64 + q * 16);
+      v[2 * q] = __uint_as_float(rr.x);
+      v[2 * q + 1] = __uint_as_float(rr.z);
+    }
+  }
+}
+
+template <bool PLAIN>
+DEV void norm_ss(char* act, int H, float eps, char* smem) {
   const uint32_t R0 = kb_round(2u * H);
-  if (x) stage(x, 2u * H, act);
-  stage(r, 4u * H, act + R0);
-  wait_vm0();
   const int ln = (int)lane(), nk8 = H / 8;
-  const bool has_x = x != nullptr;
   float ss = 0.f;
 #pragma unroll 2
   for (int c = ln; c < nk8; c += 64) {
-    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
-    float v[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
-                  __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
-    if (has_x) {
-      const u32x4 xv = *(const u32x4*)(act + c * 16);
-      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] += bf2f(xs[q] & 0xffffu);
-        v[2 * q + 1] += bf2f(xs[q] >> 16);
-      }
-    }
+    float v[8];
+    norm_chunk<PLAIN>(act, R0, c, v);
 #pragma unroll
     for (int q = 0; q < 8; ++q) ss += v[q] * v[q];
   }
@@ -422,28 +517,16 @@ DEV void norm_stage(const uint16_t* x, const float* r, int H, float eps, char* a
   if (ln == 0) *(float*)(smem + kCtrlOff + kInvOff) = inv;
 }
 
-// Fused add + RMSNorm, second half, by all eight waves (wave wv): h = bf16((r + x) * inv * gain)
-// over act[0, 2H), 8 elements per lane, the gain from the instruction's lease at goff.  The
-// caller follows with a barrier before the projection reads h.
-DEV void norm_h(const char* smem, uint32_t lease, uint32_t goff, int H, bool has_x, int wv) {
+template <bool PLAIN>
+DEV void norm_h(const char* smem, uint32_t lease, uint32_t goff, int H, int wv) {
   char* act = (char*)smem + kActOff;
   const uint32_t R0 = kb_round(2u * H);
   const float inv = *(const float*)(smem + kCtrlOff + kInvOff);
   const int nk8 = H / 8;
   for (int c = wv * 64 + (int)lane(); c < nk8; c += kNW * 64) {
-    const u32x4 ra = *(const u32x4*)(act + R0 + c * 32), rb = *(const u32x4*)(act + R0 + c * 32 + 16);
+    float v[8];
+    norm_chunk<PLAIN>(act, R0, c, v);
     const u32x4 gv = *(const u32x4*)(smem + kRingOff + ring_off(lease, goff + (uint32_t)c * 16u));
-    float v[8] = {__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z), __uint_as_float(ra.w),
-                  __uint_as_float(rb.x), __uint_as_float(rb.y), __uint_as_float(rb.z), __uint_as_float(rb.w)};
-    if (has_x) {
-      const u32x4 xv = *(const u32x4*)(act + c * 16);
-      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] += bf2f(xs[q] & 0xffffu);
-        v[2 * q + 1] += bf2f(xs[q] >> 16);
-      }
-    }
     const uint32_t gs[4] = {gv.x, gv.y, gv.z, gv.w};
     u32x4 o;
     o.x = pack_bf2(v[0] * inv * bf2f(gs[0] & 0xffffu), v[1] * inv * bf2f(gs[0] >> 16));
@@ -454,41 +537,82 @@ DEV void norm_h(const char* smem, uint32_t lease, uint32_t goff, int H, bool has
   }
 }
 
-// O projection: act = o (bf16), and r1 = r_in + x of the tile's rows at act + kActR1 (fp32);
-// the few residual values ride in the same round trip as the staging
-DEV void oproj_prologue(const Instr& in, const uint64_t* row, int n, char* act) {
-  const int n0 = in.w[W_P1], nr = in.w[W_P2];
-  stage((const void*)s_ld64(row + O_IN), 2u * n, act);
-  __amdgpu_buffer_rsrc_t rx = rsrc((const void*)s_ld64(row + O_X));
-  __amdgpu_buffer_rsrc_t rr = rsrc((const void*)s_ld64(row + O_RIN));
-  float xr[4], rv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int jj = (int)lane() + 64 * q;
-    if (jj < nr) {
-      xr[q] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rx, (uint32_t)(n0 + jj) * 2u, 0, SC1));
-      rv[q] = __uint_as_float(ld32(rr, (uint32_t)(n0 + jj) * 4u));
-    }
+// QKV, GATE_UP, LM_HEAD (its first tile): stage the norm input and take its sum of squares.
+// First-layer QKV reads the caller's x and r_in; otherwise the tagged residual: r1 of the layer
+// before (QKV, LM_HEAD) or r2 of this layer (GATE_UP).
+DEV bool norm_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, char* smem, bool verify,
+                       bool noop, uint32_t& polls) {
+  const uint32_t op = in.w[W_OPCODE], layer = in.w[W_LAYER];
+  const int H = a.sh.H;
+  const uint32_t R0 = kb_round(2u * H);
+  if (op == OP_QKV && layer == 0) {
+    stage((const void*)s_ld64(row + QKV_X), 2u * H, act);
+    stage((const void*)s_ld64(row + QKV_RIN), 4u * H, act + R0);
+    wait_vm0();
+    if (!noop) norm_ss<true>(act, H, a.sh.eps, smem);
+    return true;
   }
-  wait_vm0();
-  float* r1 = (float*)(act + kActR1);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int jj = (int)lane() + 64 * q;
-    if (jj < nr) r1[jj] = rv[q] + xr[q];
-  }
+  const int slot = op == OP_QKV ? QKV_R1 : (op == OP_GATEUP ? GU_R2 : LM_R1);
+  const LlRegion rg{(const char*)s_ld64(row + slot), 8u * H, R0, ll_tag(a, op == OP_GATEUP ? layer : layer - 1u)};
+  if (!ll_stage(a, in, &rg, 1, act, verify, polls)) return false;
+  if (!noop) norm_ss<false>(act, H, a.sh.eps, smem);
+  return true;
 }
 
-// attention: the raw (fp32) q heads of the group and its k / v heads into LDS
-DEV void attn_stage(const KArgs& a, const Instr& in, char* act) {
+// O projection: the tagged o (bf16 pairs) at act[0, ...), and r1 of the tile's rows as records at
+// act + kActR1 (tagged records of the layer before; the first layer adds the caller's r_in + x)
+DEV bool oproj_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, bool verify, uint32_t& polls) {
+  const uint32_t layer = in.w[W_LAYER];
+  const int n0 = in.w[W_P1], nr = in.w[W_P2];
+  const uint32_t n = (uint32_t)a.sh.Hq * 128u;
+  LlRegion rg[2];
+  rg[0] = LlRegion{(const char*)s_ld64(row + O_IN), 4u * n, 0u, ll_tag(a, layer)};
+  int nrg = 1;
+  if (layer > 0) rg[nrg++] = LlRegion{(const char*)s_ld64(row + O_R1) + (size_t)n0 * 8, 8u * nr, (uint32_t)kActR1,
+                                      ll_tag(a, layer - 1u)};
+  if (!ll_stage(a, in, rg, nrg, act, verify, polls)) return false;
+  if (layer == 0) {
+    __amdgpu_buffer_rsrc_t rx = rsrc((const void*)s_ld64(row + O_X));
+    __amdgpu_buffer_rsrc_t rr = rsrc((const void*)s_ld64(row + O_RIN));
+    float xr[2], rv[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int jj = (int)lane() + 64 * q;
+      if (jj < nr) {
+        xr[q] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rx, (uint32_t)(n0 + jj) * 2u, 0, SC1));
+        rv[q] = __uint_as_float(ld32(rr, (uint32_t)(n0 + jj) * 4u));
+      }
+    }
+    wait_vm0();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int jj = (int)lane() + 64 * q;
+      if (jj < nr) *(float*)(act + kActR1 + 8 * jj) = rv[q] + xr[q];
+    }
+  }
+  return true;
+}
+
+// down projection: the tagged m (bf16 pairs) at act[0, ...) and r2 of the tile's rows at act + kActR1
+DEV bool down_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, bool verify, uint32_t& polls) {
+  const uint32_t tag = ll_tag(a, in.w[W_LAYER]);
+  const int n0 = in.w[W_P1], nr = in.w[W_P2];
+  const LlRegion rg[2] = {{(const char*)s_ld64(row + DN_M), 4u * (uint32_t)a.sh.I, 0u, tag},
+                          {(const char*)s_ld64(row + DN_R2) + (size_t)n0 * 8, 8u * nr, (uint32_t)kActR1, tag}};
+  return ll_stage(a, in, rg, 2, act, verify, polls);
+}
+
+// attention: the tagged raw (fp32) q heads of the group and its k / v heads
+DEV bool attn_stage(const KArgs& a, const Instr& in, char* act, bool verify, uint32_t& polls) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int r = in.w[W_P1], hk = in.w[W_P2];
-  const float* qkv = (const float*)s_ld64(row + ATT_QKV) + (size_t)r * sh.n_qkv;
-  stage(qkv + (size_t)hk * sh.g * 128, (uint32_t)sh.g * 512u, act + kAttQraw);
-  stage(qkv + (size_t)(sh.Hq + hk) * 128, 512u, act + kAttKraw);
-  stage(qkv + (size_t)(sh.Hq + sh.Hkv + hk) * 128, 512u, act + kAttVraw);
-  wait_vm0();
+  const char* qkv = (const char*)s_ld64(row + ATT_QKV) + (size_t)r * sh.n_qkv * 8;
+  const uint32_t tag = ll_tag(a, in.w[W_LAYER]);
+  const LlRegion rg[3] = {{qkv + (size_t)hk * sh.g * 128 * 8, (uint32_t)sh.g * 1024u, (uint32_t)kAttQraw, tag},
+                          {qkv + (size_t)(sh.Hq + hk) * 128 * 8, 1024u, (uint32_t)kAttKraw, tag},
+                          {qkv + (size_t)(sh.Hq + sh.Hkv + hk) * 128 * 8, 1024u, (uint32_t)kAttVraw, tag}};
+  return ll_stage(a, in, rg, 3, act, verify, polls);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -519,6 +643,7 @@ DEV float butterfly4(float a0, float a1, float a2, float a3, int sub) {
   return k;  // lanes 4i .. 4i + 3 of the row hold block i
 }
 
+template <bool LLX>  // x as tagged records (bf16 pairs) rather than plain bf16
 DEV void gemv(const char* smem, uint32_t lease, int R, int nr0, uint32_t off1, int K, int wv, float* part) {
   const int ln = (int)lane(), sub = ln & 15;
   const uint32_t KQ = (uint32_t)K >> 9, NQ = (uint32_t)R * KQ;
@@ -536,7 +661,13 @@ DEV void gemv(const char* smem, uint32_t lease, int R, int nr0, uint32_t off1, i
       const uint32_t r = (Q * magic) >> 16, kq = Q - r * KQ;
       const uint32_t wo = r * rowb + (r >= (uint32_t)nr0 ? up : 0u) + kq * 1024u;
       w[m] = *(const u32x4*)(smem + kRingOff + ((lbase + wo) & (uint32_t)(kNPages * 16384 - 1)));
-      x[m] = *(const u32x4*)(act + kq * 1024u + xlane);
+      if (LLX) {
+        const char* xp = act + 2u * (kq * 1024u + xlane);
+        const u32x4 ra = *(const u32x4*)xp, rb = *(const u32x4*)(xp + 16);
+        x[m] = u32x4{ra.x, ra.z, rb.x, rb.z};
+      } else {
+        x[m] = *(const u32x4*)(act + kq * 1024u + xlane);
+      }
     }
     const float v = rows_sum(butterfly4(dot8(w[0], x[0], 0.f), dot8(w[1], x[1], 0.f), dot8(w[2], x[2], 0.f),
                                         dot8(w[3], x[3], 0.f), sub));
@@ -559,18 +690,27 @@ DEV void proj_body(const KArgs& a, const Instr& in, const char* smem, uint32_t l
   const uint32_t op = in.w[W_OPCODE];
   const int nr = in.w[W_P2], K = in.w[W_P4];
   const uint32_t wblk = blocks_of((uint32_t)nr * K * 2u);
+  float* out = (float*)(smem + kOutOff);
   if (fused_norm) {
-    norm_h(smem, lease, (op == OP_GATEUP ? 2u : 1u) * wblk * 1024u, K, op != OP_GATEUP, wv);
+    const uint32_t goff = (op == OP_GATEUP ? 2u : 1u) * wblk * 1024u;
+    if (op == OP_QKV && in.w[W_LAYER] == 0)
+      norm_h<true>(smem, lease, goff, K, wv);
+    else
+      norm_h<false>(smem, lease, goff, K, wv);
     lds_barrier();
   }
-  gemv(smem, lease, op == OP_GATEUP ? 2 * nr : nr, nr, wblk * 1024u, K, wv, (float*)(smem + kOutOff));
+  if (op == OP_OPROJ || op == OP_DOWN)
+    gemv<true>(smem, lease, nr, nr, 0u, K, wv, out);
+  else
+    gemv<false>(smem, lease, op == OP_GATEUP ? 2 * nr : nr, nr, wblk * 1024u, K, wv, out);
 }
 
 // QK-norm (RMSNorm over the 128 dims of a head, gain gn) then rotate-half RoPE of one raw fp32
-// head vector, by one wave: lane i holds the rotation pair (i, i + 64); bf16 result into dst
-DEV void qk_norm_rope(const float* raw, const char* gn, const char* rope, float eps, char* dst) {
+// head vector (staged tagged records), by one wave: lane i holds the rotation pair (i, i + 64);
+// bf16 result into dst
+DEV void qk_norm_rope(const char* raw, const char* gn, const char* rope, float eps, char* dst) {
   const int i = (int)lane();
-  const float x0 = raw[i], x1 = raw[i + 64];
+  const float x0 = ll_f32(raw, i), x1 = ll_f32(raw, i + 64);
   const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / 128.f + eps);
   const float g0 = bf2f(*(const uint16_t*)(gn + i * 2)), g1 = bf2f(*(const uint16_t*)(gn + (i + 64) * 2));
   const float c = *(const float*)(rope + i * 8), sn = *(const float*)(rope + i * 8 + 4);
@@ -605,14 +745,14 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
   // phase 0: QK-norm + RoPE once per head: wave j < G takes q head j, wave G the new key, wave
   // G + 1 the new value (bf16); the results (also the new cache row) go to LDS
   if (cw < G) {
-    qk_norm_rope((const float*)(act + kAttQraw) + cw * 128, ring + ring_off(lease, gqoff),
-                 ring + ring_off(lease, gqoff + 2048u), sh.eps, act + kActQ + cw * 256);
+    qk_norm_rope(act + kAttQraw + cw * 1024, ring + ring_off(lease, gqoff), ring + ring_off(lease, gqoff + 2048u),
+                 sh.eps, act + kActQ + cw * 256);
   } else if (cw == G) {
-    qk_norm_rope((const float*)(act + kAttKraw), ring + ring_off(lease, gqoff + 1024u),
-                 ring + ring_off(lease, gqoff + 2048u), sh.eps, act + kActK);
+    qk_norm_rope(act + kAttKraw, ring + ring_off(lease, gqoff + 1024u), ring + ring_off(lease, gqoff + 2048u),
+                 sh.eps, act + kActK);
   } else if (cw == G + 1) {
-    const float* vr = (const float*)(act + kAttVraw);
-    ((uint32_t*)(act + kActV))[ln] = pack_bf2(vr[2 * ln], vr[2 * ln + 1]);
+    const char* vr = act + kAttVraw;  // tagged records
+    ((uint32_t*)(act + kActV))[ln] = pack_bf2(ll_f32(vr, 2 * ln), ll_f32(vr, 2 * ln + 1));
   }
   lds_barrier();
   // phase 1: scores into LDS (the raw q area is free now)
@@ -720,18 +860,6 @@ DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* a
 // ---------------------------------------------------------------------------------------
 // controller epilogues
 
-DEV void signal_all(const KArgs& a, const Instr& in) {
-  if (a.flags & kModeGraph) return;
-  if (lane() == 0) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if ((uint32_t)k >= in.w[W_NSIG]) break;
-      uint32_t* ctr = a.events + (size_t)in.w[W_SIG0 + 3 * k] * kEvStride + (blockIdx.x % kNSub) * kSubStride;
-      __hip_atomic_fetch_add(ctr, in.w[W_SIG0 + 3 * k + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
 // record arrival in the instruction's group; true for the producer that completes the group,
 // which also re-arms the counter for the next run
 DEV bool arrive(const KArgs& a, const Instr& in) {
@@ -778,9 +906,10 @@ DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
   if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
   if (!last) return;
   // combine the group's splits, o = sum_i exp(lse_i - lse) O_i with lse = log sum_i exp(lse_i)
+  // o: tagged records of bf16 pairs, [request][Hq * 128 / 2]
   char* act = smem + kActOff;
-  uint16_t* o = (uint16_t*)s_ld64(row + ATT_O) + (size_t)r * sh.Hq * 128;
-  __amdgpu_buffer_rsrc_t ro = rsrc(o);
+  __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + ATT_O));
+  const uint32_t obase = (uint32_t)r * sh.Hq * 64u + (uint32_t)hk * g * 64u, otag = ll_tag(a, in.w[W_LAYER]);
   if ((uint32_t)ns * pstride * 4u <= (uint32_t)kActStageBytes && ns <= 64) {
     // every split at once: lane t < ns takes the weights of split t, then lanes over 4-dim units
     // accumulate the outputs in split order
@@ -804,14 +933,10 @@ DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
         for (int t = 0; t < ns; ++t) acc += wts[t * kMaxG + j] * *(const f32x4*)(pl + t * pstride + oi);
-        const uint32_t col = (uint32_t)hk * g * 128u + (uint32_t)oi;
-        st32(ro, col * 2u, pack_bf2(acc.x, acc.y));
-        st32(ro, col * 2u + 4u, pack_bf2(acc.z, acc.w));
+        ll_put2(ro, obase + (uint32_t)oi / 2u, pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w), otag);
       }
     }
     if (a.flags & MK_FLAG_TRACE) st.c2 = rtc();
-    wait_vm0();
-    signal_all(a, in);
     return;
   }
   // many splits: online over chunks of splits staged into LDS: lanes over splits take the
@@ -877,13 +1002,10 @@ DEV void attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
     if (unit < g * 32) {
       const int j = unit >> 5, c4 = unit & 31;
       const float inv = 1.f / hst[j * 3 + 1];
-      const uint32_t col = (uint32_t)(hk * g + j) * 128u + c4 * 4u;
-      st32(ro, col * 2u, pack_bf2(acc[u][0] * inv, acc[u][1] * inv));
-      st32(ro, col * 2u + 4u, pack_bf2(acc[u][2] * inv, acc[u][3] * inv));
+      ll_put2(ro, obase + (uint32_t)(j * 64 + c4 * 2), pack_bf2(acc[u][0] * inv, acc[u][1] * inv),
+              pack_bf2(acc[u][2] * inv, acc[u][3] * inv), otag);
     }
   }
-  wait_vm0();
-  signal_all(a, in);
 }
 
 // (max, smallest index) over the wave
@@ -910,25 +1032,36 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
   const float* part = (const float*)(smem + kOutOff);  // block sums of the tile
   const int KB = (int)in.w[W_P4] >> 9;  // quads per row
   const int j = (int)lane();
-  if (op == OP_QKV) {
+  const uint32_t tag = ll_tag(a, in.w[W_LAYER]);
+  if (op == OP_QKV) {  // qkv rows as tagged fp32 records
     __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + QKV_OUT));
-    for (int jj = j; jj < nr; jj += 64) st32(ro, (uint32_t)(n0 + jj) * 4u, __float_as_uint(row_sum(part, jj, KB)));
-  } else if (op == OP_OPROJ) {
+    for (int jj = j; jj < nr; jj += 64) ll_put(ro, (uint32_t)(n0 + jj), __float_as_uint(row_sum(part, jj, KB)), tag);
+  } else if (op == OP_OPROJ) {  // r2 = r1 + bf16(a) as tagged records (and the caller's r2 after the last layer)
     __amdgpu_buffer_rsrc_t r2 = rsrc((const void*)s_ld64(row + O_R2));
-    const float* r1 = (const float*)(smem + kActOff + kActR1);
+    const uint64_t out = s_ld64(row + O_R2OUT);
+    const char* r1 = smem + kActOff + kActR1;
     for (int jj = j; jj < nr; jj += 64) {
       const float av = bf2f(pack_bf2(row_sum(part, jj, KB), 0.f) & 0xffffu);
-      st32(r2, (uint32_t)(n0 + jj) * 4u, __float_as_uint(r1[jj] + av));
+      const float v = ll_f32(r1, jj) + av;
+      ll_put(r2, (uint32_t)(n0 + jj), __float_as_uint(v), tag);
+      if (out) st32(rsrc((const void*)out), (uint32_t)(n0 + jj) * 4u, __float_as_uint(v));
     }
-  } else if (op == OP_GATEUP) {
+  } else if (op == OP_GATEUP) {  // m = silu(gate) * up, bf16 pairs as tagged records (nr is even)
     __amdgpu_buffer_rsrc_t rm = rsrc((const void*)s_ld64(row + GU_M));
-    for (int jj = j; jj < nr; jj += 64) {
-      const float gv = row_sum(part, jj, KB), uv = row_sum(part, nr + jj, KB);
-      st16(rm, (uint32_t)(n0 + jj) * 2u, pack_bf2(gv / (1.f + __expf(-gv)) * uv, 0.f));
+    for (int pp = j; pp < nr / 2; pp += 64) {
+      const float g0 = row_sum(part, 2 * pp, KB), u0 = row_sum(part, nr + 2 * pp, KB);
+      const float g1 = row_sum(part, 2 * pp + 1, KB), u1 = row_sum(part, nr + 2 * pp + 1, KB);
+      ll_put(rm, (uint32_t)(n0 / 2 + pp), pack_bf2(g0 / (1.f + __expf(-g0)) * u0, g1 / (1.f + __expf(-g1)) * u1), tag);
     }
-  } else if (op == OP_DOWN) {
-    __amdgpu_buffer_rsrc_t ry = rsrc((const void*)s_ld64(row + DN_Y));
-    for (int jj = j; jj < nr; jj += 64) st16(ry, (uint32_t)(n0 + jj) * 2u, pack_bf2(row_sum(part, jj, KB), 0.f));
+  } else if (op == OP_DOWN) {  // y = bf16(m W^T); r1 of the next layer = r2 + y as tagged records
+    __amdgpu_buffer_rsrc_t r1 = rsrc((const void*)s_ld64(row + DN_R1));
+    const uint64_t yout = s_ld64(row + DN_Y);
+    const char* r2 = smem + kActOff + kActR1;
+    for (int jj = j; jj < nr; jj += 64) {
+      const uint32_t yb = pack_bf2(row_sum(part, jj, KB), 0.f) & 0xffffu;
+      ll_put(r1, (uint32_t)(n0 + jj), __float_as_uint(ll_f32(r2, jj) + bf2f(yb)), tag);
+      if (yout) st16(rsrc((const void*)yout), (uint32_t)(n0 + jj) * 2u, yb);
+    }
   } else if (op == OP_LMHEAD) {
     __amdgpu_buffer_rsrc_t rl = rsrc((const void*)s_ld64(row + LM_LOGITS));
     __amdgpu_buffer_rsrc_t rp = rsrc((const void*)s_ld64(row + LM_PART));
@@ -986,9 +1119,7 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
     wait_vm0();
     return;
   }
-  wait_vm0();
   if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
-  signal_all(a, in);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1000,62 +1131,12 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
 // skipped, no wave takes any)
 DEV int inner_barriers(uint32_t op, bool noop_only) { return op == OP_ATTN && !noop_only ? 3 : 0; }
 
-// returns false when the watchdog expired or another worker aborted
-struct WaitCache {  // the last (event, threshold) wait found satisfied in this run
-  uint32_t e, thr;
-};
-
-DEV bool wait_events(const KArgs& a, const Instr& in, uint32_t& poll_ticks, WaitCache& wc) {
-  const uint32_t ln = lane();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if ((uint32_t)k >= in.w[W_NWAIT]) break;
-    const uint32_t e = in.w[W_WAIT0 + 2 * k], thr = in.w[W_WAIT0 + 2 * k + 1];
-    if (e == wc.e && thr == wc.thr) continue;  // counters only grow within a run
-    const uint32_t target = (a.epoch + 1u) * thr;
-    const uint32_t* base = a.events + (size_t)e * kEvStride;
-    const unsigned long long t_start = rtc();
-    uint32_t it = 0;
-    while (true) {
-      uint32_t v = 0;
-      if (ln < (uint32_t)kNSub) v = __hip_atomic_load(base + ln * kSubStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t sum = wave_sum_u32(v);
-      if ((int32_t)(sum - target) >= 0) break;
-      const unsigned long long now = rtc();
-      if ((++it & 31u) == 0) {
-        const uint32_t abort_flag = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (abort_flag) return false;
-      }
-      if (now - t_start > kWatchdogTicks) {
-        if (ln == 0) {
-          uint32_t z = 0;
-          if (__hip_atomic_compare_exchange_strong(a.err, &z, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-            __hip_atomic_store(a.err + 1, blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.err + 2, in.w[W_TASK], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.err + 3, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.err + 4, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.err + 5, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        return false;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    poll_ticks += (uint32_t)(rtc() - t_start);
-    wc.e = e;
-    wc.thr = thr;
-  }
-  asm volatile("" ::: "memory");
-  return true;
-}
-
 DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride, char* smem) {
   uint32_t* ctrl = (uint32_t*)(smem + kCtrlOff);  // LDS; read and written only across barriers
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
   const bool graph = a.flags & kModeGraph;
   uint32_t last_row = 0xFFFFFFFFu;
   LmState lm{-INFINITY, 0x7fffffff};
-  WaitCache wc{0xFFFFFFFFu, 0u};
   for (int i = 0; i < count; ++i) {
     Instr in;
     fetch(base + (size_t)i * stride, in);
@@ -1064,29 +1145,25 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     const bool tracing = a.flags & MK_FLAG_TRACE;
     const unsigned long long t_vis = tracing ? rtc() : 0;
     const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
+    const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+    char* act = smem + kActOff;
+    // the instruction's wait: its tagged inputs staged into LDS (the graph baseline's stream order
+    // already guarantees them, so it stages without checking tags)
     uint32_t poll = 0;
-    bool ok = graph ? true : wait_events(a, in, poll, wc);
+    bool ok = true;
+    if (op == OP_ATTN)
+      ok = attn_stage(a, in, act, !graph, poll);
+    else if (op == OP_OPROJ)
+      ok = oproj_prologue(a, in, row, act, !graph, poll);
+    else if (op == OP_DOWN)
+      ok = down_prologue(a, in, row, act, !graph, poll);
+    else if (fused_norm)
+      ok = norm_prologue(a, in, row, act, smem, !graph, noop_only, poll);
+    last_row = in.w[W_ROW];
     const unsigned long long t_ready = tracing ? rtc() : 0;
     Stamps st{0, 0, 0, 0};
-    if (ok && !noop_only) {
-      const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
-      char* act = smem + kActOff;
-      if (op == OP_ATTN) {
-        attn_stage(a, in, act);
-      } else if (op == OP_OPROJ) {
-        oproj_prologue(in, row, a.sh.Hq * 128, act);
-      } else if (op == OP_DOWN) {
-        stage((const void*)s_ld64(row + DN_M), 2u * a.sh.I, act);
-        wait_vm0();
-      } else if (fused_norm) {  // fused add + RMSNorm (once per lm_head run)
-        const int sx = op == OP_QKV ? QKV_X : LM_Y, sr = op == OP_QKV ? QKV_RIN : (op == OP_GATEUP ? GU_R2 : LM_R2);
-        norm_stage(op == OP_GATEUP ? nullptr : (const uint16_t*)s_ld64(row + sx), (const float*)s_ld64(row + sr),
-                   a.sh.H, a.sh.eps, act, smem);
-      }
-      last_row = in.w[W_ROW];
-    }
     if (!ok && lane() == 0) ctrl[0] = 1u;
-    const unsigned long long t_pro = tracing ? rtc() : 0;
+    const unsigned long long t_pro = t_ready;
     lds_barrier();  // A: activations staged, prefetch of this instruction landed
     const unsigned long long t_a = tracing ? rtc() : 0;
     const unsigned long long c_a = tracing ? __builtin_readcyclecounter() : 0;
@@ -1100,17 +1177,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     lds_barrier();  // B: compute done, results in the output area
     const unsigned long long t_b = tracing ? rtc() : 0;
     const unsigned long long c_b = tracing ? __builtin_readcyclecounter() : 0;
-    if (noop_only) {
-      if (op == OP_ATTN || op == OP_LMHEAD) {
-        if (arrive(a, in) && op == OP_ATTN) signal_all(a, in);
-      } else {
-        signal_all(a, in);
-      }
-    } else if (op == OP_ATTN) {
+    if (op == OP_ATTN)
       attn_epilogue(a, in, smem, st);
-    } else {
+    else
       gemv_epilogue(a, in, smem, lm, st);
-    }
     if (tracing && a.trace && lane() == 0) {
       uint32_t* tr = a.trace + ((size_t)blockIdx.x * a.L + i) * kTraceWords;
       tr[0] = (uint32_t)t_vis;
@@ -1181,10 +1251,10 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       } else {
         proj_body(a, in, smem, lease, fused_norm, cw);
       }
-      last_row = in.w[W_ROW];
     } else {
       for (int b = 0; b < inner_barriers(op, noop_only); ++b) lds_barrier();
     }
+    last_row = in.w[W_ROW];
     lds_barrier();  // B
   }
   wait_vm0();  // no LDS-bound load may be in flight when the block retires

@@ -236,14 +236,13 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
     out.regions.push_back({name, off, bytes});
     off += (bytes + 255) / 256 * 256;
   };
-  region("qkv", (size_t)M * n_qkv * 4);
-  region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);  // per split: g*d O, g lse, padding
-  region("o", (size_t)M * Hq * d * 2);
-  region("m", (size_t)M * I * 2);
-  region("r2a", (size_t)M * H * 4);
-  region("r2b", (size_t)M * H * 4);
-  region("ya", (size_t)M * H * 2);
-  region("yb", (size_t)M * H * 2);
+  // vectors written inside a run are tagged 8-byte records: fp32 or a bf16 pair per record
+  region("qkv", (size_t)M * n_qkv * 8);
+  region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);  // per split: g*d O, g lse, padding (fp32)
+  region("o", (size_t)M * Hq * d / 2 * 8);
+  region("m", (size_t)M * I / 2 * 8);
+  region("r2", (size_t)M * H * 8);
+  region("r1", (size_t)M * H * 8);
   if (c.workload == MK_QWEN3_STEP) region("lm_part", (size_t)((c.vocab + p.r_lm - 1) / p.r_lm) * 8);
   out.workspace_bytes = off;
 

@@ -39,6 +39,20 @@ class QwenRun:
         off, n = self.plan.region(name)
         return self.t["workspace"][off:off + n].view(dtype)
 
+    def records(self, name):
+        """A workspace vector of tagged records: (payload words uint32, tags uint32)."""
+        w = self.region(name, torch.int32).cpu().numpy().view(np.uint32)
+        return w[0::2].copy(), w[1::2].copy()
+
+    def payload_f32(self, name):
+        return self.records(name)[0].view(np.float32).astype(np.float64)
+
+    def payload_bf16(self, name):
+        """bf16 pairs per record (low half first), as float64."""
+        p = self.records(name)[0]
+        pairs = np.stack([p & 0xFFFF, p >> 16], axis=1).reshape(-1).astype(np.uint32) << 16
+        return pairs.view(np.float32).astype(np.float64)
+
     def run(self, mode="mk", multistream=False):
         if mode == "mk":
             self.plan.run(self.tensors)

@@ -60,13 +60,22 @@ def test_small_layer_megakernel_and_intermediates():
     inp, ref, run = _layer_case(cfg)
     k0, v0 = inp["k_cache"][0].copy(), inp["v_cache"][0].copy()
     run.run("mk")
-    qkv = run.region("qkv", torch.float32).cpu().numpy().astype(np.float64)
+    qkv = run.payload_f32("qkv")
     assert np.max(np.abs(qkv - ref["qkv"].reshape(-1))) <= TOL
-    o = bf16_bits_to_f64(run.region("o", torch.int16).cpu().numpy().view(np.uint16))
+    o = run.payload_bf16("o")
     assert np.max(np.abs(o - ref["o_pre"].reshape(-1))) <= TOL
-    m = bf16_bits_to_f64(run.region("m", torch.int16).cpu().numpy().view(np.uint16))
+    m = run.payload_bf16("m")
     assert np.max(np.abs(m - ref["m_pre"].reshape(-1))) <= TOL
+    r2 = run.payload_f32("r2")
+    assert np.array_equal(r2, run.t["r2_out"].cpu().numpy().astype(np.float64))  # the records hold r2 itself
+    # every record written by the run carries the run's tag: one value, layer 0 -> low bits 1
+    tags = np.concatenate([run.records(n)[1] for n in ("qkv", "o", "m", "r2", "r1")])
+    tag0 = int(tags[0])
+    assert np.all(tags == tag0) and tag0 & 1023 == 1
     _check_layer(run, inp, ref, k0, v0, "mk")
+    run.run("mk")  # the next run rewrites every record with the next run's tag
+    for name in ("qkv", "o", "m", "r2", "r1"):
+        assert np.all(run.records(name)[1] == (tag0 + 1024) % 2**32), name
 
 
 def test_small_layer_graph_baselines_match_megakernel_bitwise():
@@ -80,6 +89,8 @@ def test_small_layer_graph_baselines_match_megakernel_bitwise():
         run.t["r2_out"].zero_()
         run.run(mode, ms)
         _check_layer(run, inp, ref, k0, v0, f"{mode}/{ms}")
+        if mode == "graph":  # stream order replaces the tags: the baseline writes tag 0, never waited for
+            assert all(np.all(run.records(n)[1] == 0) for n in ("qkv", "o", "m", "r2", "r1"))
         outs.append((run.t["y_out"].clone(), run.t["r2_out"].clone()))
     for y, r in outs[1:]:
         assert torch.equal(y, outs[0][0]) and torch.equal(r, outs[0][1])
