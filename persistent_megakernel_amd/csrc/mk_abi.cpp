@@ -177,10 +177,10 @@ mk_status check_runnable(mk_plan* p) {
   if (hp.tp.spec != 0 || c.weight_fp8 || c.act_fp8)
     return fail(MK_ERR_UNSUPPORTED, "only the bf16 single-token (M = 1) op bodies are built");
   if (c.hidden > 2048 || c.inter > 6144 || c.n_q_heads * c.head_dim > 6144 || hp.tp.r_o > 128 ||
-      hp.tp.r_down > 128 || hp.tp.r_gu % 2 || c.n_q_heads / c.n_kv_heads > mk::dev::kMaxG || c.hidden % 512 ||
-      c.inter % 512 || (c.n_q_heads * c.head_dim) % 512)
+      hp.tp.r_down > 128 || hp.tp.r_gu % 2 || (c.n_q_heads / c.n_kv_heads != 1 && c.n_q_heads / c.n_kv_heads != 2 &&
+      c.n_q_heads / c.n_kv_heads != 4) || c.hidden % 512 || c.inter % 512 || (c.n_q_heads * c.head_dim) % 512)
     return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 2048; inter, q width <= 6144; "
-                                    "hidden, inter and q width multiples of 512; even gate/up tiles; GQA group <= 5)");
+                                    "hidden, inter and q width multiples of 512; even gate/up tiles; GQA group 1, 2 or 4)");
   if (!p->occupancy_checked) {
     int per_cu = 0;
     HIP_TRY(hipSetDevice(p->device));

@@ -40,12 +40,17 @@ constexpr int kThreads = 512;  // 8 waves: controller + 7 loader/compute waves
 constexpr int kNCW = 7;
 constexpr int kNW = 8;     // waves of a projection tile: the seven compute waves and the controller
 constexpr int kNPages = 8;     // LDS ring of 8 x 16 KiB pages
+#ifndef MK_LOOKAHEAD_PAGES
+#define MK_LOOKAHEAD_PAGES 8
+#endif
+constexpr int kLookPages = MK_LOOKAHEAD_PAGES;  // prefetch at most this many pages from the current lease
 constexpr int kRingOff = 0;
 constexpr int kActOff = kNPages * 16384;   // activation staging
 constexpr int kActBytes = 27648;
 constexpr int kActStageBytes = kActBytes;  // largest staged block (a 1 KiB multiple)
 constexpr int kOutOff = kActOff + kActBytes;  // compute results
-constexpr int kOutBytes = 4096;  // g*128 + g floats of an attention partial: GQA group <= 7
+constexpr int kOutBytes = 4096;
+constexpr int kMaxKQ = 12;     // projection K <= 12 * 512: quad sums per row  // g*128 + g floats of an attention partial: GQA group <= 7
 constexpr int kCtrlOff = kOutOff + kOutBytes;  // abort flag + per-wave lease tables
 constexpr int kCtrlBytes = 1024;
 constexpr int kLeaseTabOff = 64;   // in the control area: [7 waves][32] lease tables
@@ -64,7 +69,7 @@ constexpr int kAttVraw = kAttKraw + 1024;
 constexpr int kAttS = 21504;     // fp32 [g][128] scores
 constexpr int kAttP = kAttS + kMaxG * 512;  // fp32 [7 waves][g][20] exponentials of each wave's tokens
 constexpr int kActR1 = kActBytes - 1024;    // O projection / down: residual rows of the tile as records (<= 128)
-static_assert(kActMerge + 7 * kMaxG * 128 * 4 <= kAttS, "attention merge area overlaps the scores");
+static_assert(kActMerge + 7 * kMaxG * 130 * 4 <= kAttS, "attention merge area overlaps the scores");
 static_assert(kAttVraw + 1024 <= kAttS, "attention staging overlaps the scores");
 static_assert(kAttP + 7 * kMaxG * 20 * 4 <= kActBytes, "attention exponentials overflow the staging area");
 static_assert(kLdsBytes == 163840, "LDS budget");

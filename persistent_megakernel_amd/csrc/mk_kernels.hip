@@ -430,13 +430,19 @@ DEV void record_timeout(const KArgs& a, const Instr& in, uint32_t what, uint32_t
 // The wait of an instruction: stage every block of its regions in one round trip; with `verify`
 // (the megakernel), stage again the blocks holding a record whose tag is not current, until all
 // are.  False when the watchdog expired or another worker aborted.
-DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, char* act, bool verify, uint32_t& polls) {
+struct StageStamps {  // trace: when the first staging round was issued and when it landed
+  unsigned long long issue, landed;
+};
+
+DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, char* act, bool verify, uint32_t& polls,
+                  StageStamps& ss) {
   const uint32_t ln = lane();
   uint32_t pend[3] = {0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < 3; ++j)
     if (j < nrg) pend[j] = (1u << blocks_of(rg[j].bytes)) - 1u;  // at most 27 blocks
   const unsigned long long t0 = rtc();
+  if (a.flags & MK_FLAG_TRACE) ss.issue = t0;
   for (uint32_t it = 1;; ++it) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -448,6 +454,7 @@ DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, 
       }
     }
     wait_vm0();
+    if ((a.flags & MK_FLAG_TRACE) && it == 1) ss.landed = rtc();
     if (!verify) return true;
     bool done = true;
 #pragma unroll
@@ -541,7 +548,7 @@ DEV void norm_h(const char* smem, uint32_t lease, uint32_t goff, int H, int wv) 
 // First-layer QKV reads the caller's x and r_in; otherwise the tagged residual: r1 of the layer
 // before (QKV, LM_HEAD) or r2 of this layer (GATE_UP).
 DEV bool norm_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, char* smem, bool verify,
-                       bool noop, uint32_t& polls) {
+                       bool noop, uint32_t& polls, StageStamps& ss) {
   const uint32_t op = in.w[W_OPCODE], layer = in.w[W_LAYER];
   const int H = a.sh.H;
   const uint32_t R0 = kb_round(2u * H);
@@ -554,14 +561,15 @@ DEV bool norm_prologue(const KArgs& a, const Instr& in, const uint64_t* row, cha
   }
   const int slot = op == OP_QKV ? QKV_R1 : (op == OP_GATEUP ? GU_R2 : LM_R1);
   const LlRegion rg{(const char*)s_ld64(row + slot), 8u * H, R0, ll_tag(a, op == OP_GATEUP ? layer : layer - 1u)};
-  if (!ll_stage(a, in, &rg, 1, act, verify, polls)) return false;
+  if (!ll_stage(a, in, &rg, 1, act, verify, polls, ss)) return false;
   if (!noop) norm_ss<false>(act, H, a.sh.eps, smem);
   return true;
 }
 
 // O projection: the tagged o (bf16 pairs) at act[0, ...), and r1 of the tile's rows as records at
 // act + kActR1 (tagged records of the layer before; the first layer adds the caller's r_in + x)
-DEV bool oproj_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, bool verify, uint32_t& polls) {
+DEV bool oproj_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, bool verify, uint32_t& polls,
+                        StageStamps& ss) {
   const uint32_t layer = in.w[W_LAYER];
   const int n0 = in.w[W_P1], nr = in.w[W_P2];
   const uint32_t n = (uint32_t)a.sh.Hq * 128u;
@@ -570,7 +578,7 @@ DEV bool oproj_prologue(const KArgs& a, const Instr& in, const uint64_t* row, ch
   int nrg = 1;
   if (layer > 0) rg[nrg++] = LlRegion{(const char*)s_ld64(row + O_R1) + (size_t)n0 * 8, 8u * nr, (uint32_t)kActR1,
                                       ll_tag(a, layer - 1u)};
-  if (!ll_stage(a, in, rg, nrg, act, verify, polls)) return false;
+  if (!ll_stage(a, in, rg, nrg, act, verify, polls, ss)) return false;
   if (layer == 0) {
     __amdgpu_buffer_rsrc_t rx = rsrc((const void*)s_ld64(row + O_X));
     __amdgpu_buffer_rsrc_t rr = rsrc((const void*)s_ld64(row + O_RIN));
@@ -594,16 +602,17 @@ DEV bool oproj_prologue(const KArgs& a, const Instr& in, const uint64_t* row, ch
 }
 
 // down projection: the tagged m (bf16 pairs) at act[0, ...) and r2 of the tile's rows at act + kActR1
-DEV bool down_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, bool verify, uint32_t& polls) {
+DEV bool down_prologue(const KArgs& a, const Instr& in, const uint64_t* row, char* act, bool verify, uint32_t& polls,
+                       StageStamps& ss) {
   const uint32_t tag = ll_tag(a, in.w[W_LAYER]);
   const int n0 = in.w[W_P1], nr = in.w[W_P2];
   const LlRegion rg[2] = {{(const char*)s_ld64(row + DN_M), 4u * (uint32_t)a.sh.I, 0u, tag},
                           {(const char*)s_ld64(row + DN_R2) + (size_t)n0 * 8, 8u * nr, (uint32_t)kActR1, tag}};
-  return ll_stage(a, in, rg, 2, act, verify, polls);
+  return ll_stage(a, in, rg, 2, act, verify, polls, ss);
 }
 
 // attention: the tagged raw (fp32) q heads of the group and its k / v heads
-DEV bool attn_stage(const KArgs& a, const Instr& in, char* act, bool verify, uint32_t& polls) {
+DEV bool attn_stage(const KArgs& a, const Instr& in, char* act, bool verify, uint32_t& polls, StageStamps& ss) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int r = in.w[W_P1], hk = in.w[W_P2];
@@ -612,7 +621,7 @@ DEV bool attn_stage(const KArgs& a, const Instr& in, char* act, bool verify, uin
   const LlRegion rg[3] = {{qkv + (size_t)hk * sh.g * 128 * 8, (uint32_t)sh.g * 1024u, (uint32_t)kAttQraw, tag},
                           {qkv + (size_t)(sh.Hq + hk) * 128 * 8, 1024u, (uint32_t)kAttKraw, tag},
                           {qkv + (size_t)(sh.Hq + sh.Hkv + hk) * 128 * 8, 1024u, (uint32_t)kAttVraw, tag}};
-  return ll_stage(a, in, rg, 3, act, verify, polls);
+  return ll_stage(a, in, rg, 3, act, verify, polls, ss);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -676,11 +685,16 @@ DEV void gemv(const char* smem, uint32_t lease, int R, int nr0, uint32_t off1, i
   }
 }
 
-// a row of a projection tile: its KQ quad sums in order
+// a row of a projection tile: its KQ quad sums in order.  The loads are unconditional (the output
+// area extends past the last row's sums) so that they go out together; entries past KQ add 0.
 DEV float row_sum(const float* part, int r, int KQ) {
   const float* p = part + r * KQ;
-  float s = p[0];
-  for (int k = 1; k < KQ; ++k) s += p[k];
+  float v[kMaxKQ];
+#pragma unroll
+  for (int k = 0; k < kMaxKQ; ++k) v[k] = p[k];
+  float s = v[0];
+#pragma unroll
+  for (int k = 1; k < kMaxKQ; ++k) s += k < KQ ? v[k] : 0.f;
   return s;
 }
 
@@ -725,10 +739,10 @@ DEV void qk_norm_rope(const char* raw, const char* gn, const char* rope, float e
 //   1. scores: 16-lane rows over the split's tokens (row R takes tokens R, R + 28, ...), lane
 //      `sub` holding dims [8 sub, 8 sub + 8); four tokens of a row are summed over its lanes at
 //      once by the transposing butterfly;
-//   2. per head, the maximum and the sum of exponentials (every wave), and the exponentials of
-//      the wave's own phase-3 tokens into a wave-private table;
-//   3. P V: lanes over dimension pairs, waves over tokens (wave w takes tokens w, w + 7, ...),
-//      then the sum of the seven waves' partial outputs.
+//   2. per head and wave, the maximum over the wave's own phase-3 tokens and their exponentials
+//      into a wave-private table;
+//   3. P V: lanes over dimension pairs, waves over tokens (wave w takes tokens w, w + 7, ...);
+//      the seven waves' partial outputs and sums merge with weights exp(m_w - max m_w).
 // Output: the split's normalised O [G][128] and its lse [G] in the output area.
 template <int G>
 DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
@@ -779,25 +793,25 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
     }
   }
   lds_barrier();
-  // phase 2: per-head maximum and sum of exponentials (wave-uniform), then the exponentials of
-  // this wave's tokens t = cw + 7 i (lane i < 20) into pw[cw][j][i] (0 past the end)
-  float mh[G], lh[G];
+  // phase 2: the wave's own tokens t = cw + 7 i (lane i < 20): per head the wave's maximum m_w and
+  // the exponentials exp(s - m_w) into the wave-private table pw[cw][j][i] (0 past the end)
+  float mw[G];
   float* pw = (float*)(act + kAttP) + cw * G * 20;
   {
-    const bool in0 = ln < ntok, in1 = ln + 64 < ntok;
     const int tw = cw + kNCW * ln;
+    const bool mine = ln < 20 && tw < ntok;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const float a0 = in0 ? sc[j * 128 + ln] : -INFINITY, a1 = in1 ? sc[j * 128 + 64 + ln] : -INFINITY;
-      mh[j] = wave_max(fmaxf(a0, a1));
-      lh[j] = wave_sum((in0 ? __expf(a0 - mh[j]) : 0.f) + (in1 ? __expf(a1 - mh[j]) : 0.f));
-      if (ln < 20) pw[j * 20 + ln] = tw < ntok ? __expf(sc[j * 128 + min(tw, 127)] - mh[j]) : 0.f;
+      const float sv = mine ? sc[j * 128 + tw] : -INFINITY;
+      mw[j] = wave_max(sv);  // -inf for a wave without tokens (ntok < 7); its weight is then 0
+      if (ln < 20) pw[j * 20 + ln] = mine ? __expf(sv - mw[j]) : 0.f;
     }
   }
-  // phase 3: this wave's tokens, four at a time; lane ln owns dims 2 ln, 2 ln + 1
-  float acc[G][2];
+  // phase 3: P V over the wave's tokens, four at a time; lane ln owns dims 2 ln, 2 ln + 1; the sum
+  // of the exponentials is wave-uniform
+  float acc[G][2], lw[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = 0.f;
+  for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = lw[j] = 0.f;
   const int nw = ntok > cw ? (ntok - cw + kNCW - 1) / kNCW : 0;
   for (int i = 0; i < nw; i += 4) {
     uint32_t vw[4];
@@ -810,6 +824,7 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
     for (int j = 0; j < G; ++j) {
       const f32x4 pj = *(const f32x4*)(pw + j * 20 + i);
       const float pk[4] = {pj.x, pj.y, pj.z, pj.w};
+      lw[j] += (pk[0] + pk[1]) + (pk[2] + pk[3]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         acc[j][0] += pk[k] * bf2f(vw[k] & 0xffffu);
@@ -817,33 +832,35 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
       }
     }
   }
-  float* mrg = (float*)(act + kActMerge);  // [wave][G][128] partial P V
+  float* mrg = (float*)(act + kActMerge);  // [wave][G][128] partial P V, then [wave][G] (m_w, l_w)
+  float* ml = mrg + kNCW * G * 128;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const f32x2 v = {acc[j][0], acc[j][1]};
     *(f32x2*)(mrg + (cw * G + j) * 128 + 2 * ln) = v;
-  }
-  lds_barrier();
-  float* out = (float*)(smem + kOutOff);
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    // output o = j * 128 + d of head j by flat lane cw * 64 + ln < 128 ... spread over the waves
-    for (int d = cw * 64 + ln; d < 128; d += kNCW * 64) {
-      float O = 0.f;
-#pragma unroll
-      for (int w = 0; w < kNCW; ++w) O += mrg[(w * G + j) * 128 + d];
-      out[j * 128 + d] = O / lh[j];
+    if (ln == 0) {
+      const f32x2 st = {nw > 0 ? mw[j] : -INFINITY, lw[j]};
+      *(f32x2*)(ml + (cw * G + j) * 2) = st;
     }
   }
-  if (cw == kNCW - 1 && ln < G) {
-    float M = mh[0], L = lh[0];
+  lds_barrier();
+  // merge the seven waves: weights exp(m_w - M) with M the largest m_w; lane o = j * 128 + d
+  float* out = (float*)(smem + kOutOff);
+  for (int o = cw * 64 + ln; o < G * 128; o += kNCW * 64) {
+    const int j = o >> 7, d = o & 127;
+    float M = -INFINITY;
 #pragma unroll
-    for (int jj = 1; jj < G; ++jj)
-      if (jj == ln) {
-        M = mh[jj];
-        L = lh[jj];
-      }
-    out[G * 128 + ln] = M + __logf(L);
+    for (int w = 0; w < kNCW; ++w) M = fmaxf(M, ml[(w * G + j) * 2]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNCW; ++w) {
+      const float mv = ml[(w * G + j) * 2];
+      const float e = mv == -INFINITY ? 0.f : __expf(mv - M);
+      O += e * mrg[(w * G + j) * 128 + d];
+      L += e * ml[(w * G + j) * 2 + 1];
+    }
+    out[o] = O / L;
+    if (d == 0) out[G * 128 + j] = M + __logf(L);
   }
 }
 
@@ -851,9 +868,7 @@ DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* a
   switch (a.sh.g) {
     case 1: attn_body<1>(a, in, smem, act, lease, cw); break;
     case 2: attn_body<2>(a, in, smem, act, lease, cw); break;
-    case 3: attn_body<3>(a, in, smem, act, lease, cw); break;
-    case 4: attn_body<4>(a, in, smem, act, lease, cw); break;
-    default: attn_body<5>(a, in, smem, act, lease, cw); break;
+    default: attn_body<4>(a, in, smem, act, lease, cw); break;  // GQA groups 1, 2 and 4 are built
   }
 }
 
@@ -1151,14 +1166,15 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     // already guarantees them, so it stages without checking tags)
     uint32_t poll = 0;
     bool ok = true;
+    StageStamps sst{0, 0};
     if (op == OP_ATTN)
-      ok = attn_stage(a, in, act, !graph, poll);
+      ok = attn_stage(a, in, act, !graph, poll, sst);
     else if (op == OP_OPROJ)
-      ok = oproj_prologue(a, in, row, act, !graph, poll);
+      ok = oproj_prologue(a, in, row, act, !graph, poll, sst);
     else if (op == OP_DOWN)
-      ok = down_prologue(a, in, row, act, !graph, poll);
+      ok = down_prologue(a, in, row, act, !graph, poll, sst);
     else if (fused_norm)
-      ok = norm_prologue(a, in, row, act, smem, !graph, noop_only, poll);
+      ok = norm_prologue(a, in, row, act, smem, !graph, noop_only, poll, sst);
     last_row = in.w[W_ROW];
     const unsigned long long t_ready = tracing ? rtc() : 0;
     Stamps st{0, 0, 0, 0};
@@ -1195,6 +1211,8 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       tr[9] = (uint32_t)(c_b - c_a);  // shader clock cycles between the two compute barriers
       tr[10] = (uint32_t)st.c1;
       tr[11] = (uint32_t)st.c2;
+      tr[12] = (uint32_t)sst.issue;
+      tr[13] = (uint32_t)sst.landed;
     }
   }
 }
@@ -1233,6 +1251,9 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
         pf_desc(a, nx, pf);
         const uint32_t npg = (pf_blocks(pf) + 15u) >> 4;
         if (head + npg - freed > (uint32_t)kNPages) break;
+        // bounded depth: loads in flight queue ahead of the controller's staging in this CU's
+        // memory pipeline, so leases beyond kLookPages pages from instruction i's wait
+        if (pf_i > i && head + npg - uni(lease_tab[i & 15]) > (uint32_t)kLookPages) break;
         pf_issue(a, pf, head, cw, issued, smem);
         lease_tab[pf_i & 15] = head;
         lease_tab[16 + (pf_i & 15)] = issued;
