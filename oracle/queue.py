@@ -32,8 +32,13 @@ from typing import Dict, List
 import numpy as np
 
 OP_NOOP, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = 0, 1, 2, 3, 4, 5, 6
+# multi-row (M = 16) plans: per-row norms, projection tiles over K chunks with explicit finalize
+# tasks, per-row FP8 quantisation of the O and down inputs
+OP_NORM, OP_GEMM, OP_FIN, OP_QUANT = 7, 8, 9, 10
+K_QKV, K_O, K_GU, K_DOWN = 0, 1, 2, 3  # projection kinds
 NONE = 0xFFFFFFFF
 LEASE_BYTES = 65536  # largest LDS lease of one instruction
+M16_ROWS = 64        # weight rows of one multi-row projection tile (gate/up: 32 gate + 32 up)
 
 
 def _pow2floor(x: int) -> int:
@@ -82,6 +87,8 @@ def tile_params(cfg, W: int, ctx_lens) -> Dict[str, int]:
     want = -(-(2 * R * ctx_max * Hkv) // W)  # about W/2 attention tasks
     p["s_tok"] = max(4, min(LEASE_BYTES // (4 * d), _pow2ceil(max(1, want))))
     p["spec"] = 0 if cfg.m == 1 else 1
+    # multi-row projection tiles: M16_ROWS weight rows x kc columns fill one lease
+    p["kc"] = LEASE_BYTES // (M16_ROWS * elem) if p["spec"] == 1 else 0
     return p
 
 
@@ -179,6 +186,93 @@ def _qwen3(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
                    [cfg.num_layers, n0, min(rl, cfg.vocab - n0), 0, H, 0, grp, n_pub, slot])
 
 
+def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
+    """Multi-row (M = R x T rows, M <= 16) layer: row-task norms, projections as
+    (output-row tile, K chunk) tasks writing partial sums, one finalize task per row tile that
+    adds the chunks in K order and applies the epilogue; FP8 plans quantise o and m per row.
+
+    Waits (all "whole" unless stated): NORM_A on the previous layer's down finalizes; QKV tiles
+    on NORM_A; QKV finalize on its tile's chunks ("tile_reduce"); attention on the QKV finalizes of
+    its kv group ("tile_cover"); [QUANT_O on every combine]; O tiles on the combines [or QUANT_O];
+    NORM_B on the O finalizes; gate/up tiles on NORM_B; [QUANT_M on the gate/up finalizes]; down
+    tiles on the gate/up finalizes [or QUANT_M]."""
+    H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
+    Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
+    g = Hq // Hkv
+    R, M = cfg.n_requests, cfg.m
+    spec, kc, st = p["spec"], p["kc"], p["s_tok"]
+    n_qkv = (Hq + 2 * Hkv) * d
+    fp8 = bool(cfg.act_fp8)
+    rt = M16_ROWS
+
+    def proj(kind, l, N, K, rows, wait, fin_signal):
+        row_g, row_f = b.op_row(), b.op_row()
+        nt, nk = N // rows, K // kc
+        parts = [b.event(nk) for _ in range(nt)]
+        for j in range(nt):
+            for c in range(nk):
+                b.task(OP_GEMM, row_g, spec, [wait], [(parts[j], 1)], [l, kind, j, j * rows, rows, c * kc, kc])
+        for j in range(nt):
+            b.task(OP_FIN, row_f, spec, [(parts[j], nk)], [fin_signal(j)], [l, kind, j, j * rows, rows, nk, kc])
+
+    prev = None
+    for l in range(cfg.num_layers):
+        row_na = b.op_row()
+        ev_na = b.event(M)
+        for m in range(M):
+            b.task(OP_NORM, row_na, spec, [] if prev is None else [prev], [(ev_na, 1)], [l, 0, m])
+        # QKV: a 64-row tile lies inside one head; its finalize counts for the head's kv group
+        tiles_per_group = (g + 2) * d // rt
+        ev_qkv = [b.event(tiles_per_group) for _ in range(Hkv)]
+
+        def qkv_group(j):
+            n0 = j * rt
+            if n0 < Hq * d:
+                return (n0 // d) // g
+            if n0 < (Hq + Hkv) * d:
+                return (n0 - Hq * d) // d
+            return (n0 - (Hq + Hkv) * d) // d
+
+        proj(K_QKV, l, n_qkv, H, rt, (ev_na, M), lambda j: (ev_qkv[qkv_group(j)], 1))
+        row_attn = b.op_row()
+        ev_oready = b.event(R * Hkv)
+        for r in range(R):
+            ctx = int(ctx_lens[r])
+            ns = -(-ctx // st)
+            for hk in range(Hkv):
+                grp = b.arrival_group()
+                for s in range(ns):
+                    t0, t1 = s * st, min(ctx, (s + 1) * st)
+                    b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk], tiles_per_group)], [(ev_oready, 1)],
+                           [l, r, hk, s, t0, t1, grp, ns, s])
+        o_wait = (ev_oready, R * Hkv)
+        if fp8:
+            row_qo = b.op_row()
+            ev_oq = b.event(M)
+            for m in range(M):
+                b.task(OP_QUANT, row_qo, spec, [o_wait], [(ev_oq, 1)], [l, 0, m])
+            o_wait = (ev_oq, M)
+        ev_o = b.event(H // rt)
+        proj(K_O, l, H, Hq * d, rt, o_wait, lambda j: (ev_o, 1))
+        row_nb = b.op_row()
+        ev_nb = b.event(M)
+        for m in range(M):
+            b.task(OP_NORM, row_nb, spec, [(ev_o, H // rt)], [(ev_nb, 1)], [l, 1, m])
+        # gate/up: a tile holds rt/2 gate rows and the matching rt/2 up rows
+        ev_gu = b.event(I // (rt // 2))
+        proj(K_GU, l, I, H, rt // 2, (ev_nb, M), lambda j: (ev_gu, 1))
+        m_wait = (ev_gu, I // (rt // 2))
+        if fp8:
+            row_qm = b.op_row()
+            ev_mq = b.event(M)
+            for m in range(M):
+                b.task(OP_QUANT, row_qm, spec, [m_wait], [(ev_mq, 1)], [l, 1, m])
+            m_wait = (ev_mq, M)
+        ev_down = b.event(H // rt)
+        proj(K_DOWN, l, H, I, rt, m_wait, lambda j: (ev_down, 1))
+        prev = (ev_down, H // rt)
+
+
 def build_queue(cfg, W: int, ctx_lens=None) -> Dict[str, np.ndarray]:
     """Returns {'queue': uint32 [W, L, 32], 'thresholds': uint32 [E], 'n_tasks', 'n_ops',
     'n_arrivals', 'params'}."""
@@ -186,7 +280,11 @@ def build_queue(cfg, W: int, ctx_lens=None) -> Dict[str, np.ndarray]:
         ctx_lens = [cfg.context] * cfg.n_requests
     b = _Builder()
     p = tile_params(cfg, W, ctx_lens)
-    if cfg.workload in ("qwen3_layer", "qwen3_step"):
+    if cfg.workload in ("qwen3_layer", "qwen3_step") and p["spec"] == 1:
+        if cfg.workload == "qwen3_step":
+            raise NotImplementedError("multi-row decode step")
+        _qwen3_m16(cfg, W, ctx_lens, b, p)
+    elif cfg.workload in ("qwen3_layer", "qwen3_step"):
         _qwen3(cfg, W, ctx_lens, b, p)
     else:
         raise NotImplementedError(cfg.workload)

@@ -16,8 +16,15 @@ enum Opcode : uint32_t {
   OP_OPROJ = 3,   // O projection rows + residual add
   OP_GATEUP = 4,  // RMSNorm prologue, gate and up rows, SiLU-mul epilogue
   OP_DOWN = 5,    // down projection rows
-  OP_LMHEAD = 6   // final add + RMSNorm prologue, lm_head rows, tile max; last arrival takes the argmax
+  OP_LMHEAD = 6,  // final add + RMSNorm prologue, lm_head rows, tile max; last arrival takes the argmax
+  // multi-row (M = 16) plans
+  OP_NORM = 7,    // one row: (add +) RMSNorm (+ FP8 quantisation) into the projection input layout
+  OP_GEMM = 8,    // one (64-row tile, K chunk) of a projection: MFMA partial sums
+  OP_FIN = 9,     // one row tile: add the K chunks in order, then the projection's epilogue
+  OP_QUANT = 10   // one row of o or m: per-token FP8 quantisation into the projection input layout
 };
+enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3 };
+constexpr int kM16Rows = 64;  // weight rows of a multi-row projection tile (gate/up: 32 + 32)
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 constexpr int kWords = 32;
@@ -53,6 +60,7 @@ enum LmSlot { LM_W = 0, LM_GAMMA, LM_R1, LM_LOGITS, LM_PART, LM_TOKEN };
 
 struct TileParams {
   int r_qkv = 0, r_o = 0, r_gu = 0, r_down = 0, r_lm = 0, s_tok = 0, spec = 0;
+  int kc = 0;  // multi-row plans: K chunk of a projection tile (kM16Rows x kc weights fill a lease)
 };
 
 struct OpInfo {      // one row of the operand table = one op instance

@@ -99,8 +99,102 @@ bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, s
   long long want = (2ll * R * ctx_max * Hkv + W - 1) / W;
   p.s_tok = std::max(4, std::min(kLeaseBytes / (4 * d), pow2ceil((int)std::max(1ll, want))));
   p.spec = (R * c.tokens_per_request == 1) ? 0 : 1;
+  p.kc = p.spec == 1 ? kLeaseBytes / (kM16Rows * elem) : 0;
   (void)err;
   return true;
+}
+
+// Multi-row (M = R x T <= 16) layer: row-task norms, projections as (64-row tile, K chunk) tasks
+// writing partial sums, one finalize task per row tile adding the chunks in K order and applying
+// the epilogue; FP8 plans quantise o and m per row.  The same rules as the oracle's builder.
+void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Builder& b, int& max_splits) {
+  const int H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int g = Hq / Hkv, R = c.n_requests, M = R * c.tokens_per_request;
+  const int spec = p.spec, kc = p.kc, st = p.s_tok, rt = kM16Rows;
+  const int n_qkv = (Hq + 2 * Hkv) * d;
+  const bool fp8 = c.act_fp8 != 0;
+  auto proj = [&](uint32_t kind, int l, int N, int K, int rows, std::pair<int, uint32_t> wait, int dep_row,
+                  auto fin_event) -> int {
+    const int row_g = b.op_row(OP_GEMM, l, {dep_row});
+    const int nt = N / rows, nk = K / kc;
+    std::vector<int> parts(nt);
+    for (int j = 0; j < nt; ++j) parts[j] = b.event((uint32_t)nk);
+    for (int j = 0; j < nt; ++j)
+      for (int ck = 0; ck < nk; ++ck)
+        b.task(OP_GEMM, row_g, spec, {wait}, {{parts[j], 1u}}, {l, kind, j, j * rows, rows, ck * kc, kc});
+    const int row_f = b.op_row(OP_FIN, l, {row_g});
+    for (int j = 0; j < nt; ++j)
+      b.task(OP_FIN, row_f, spec, {{parts[j], (uint32_t)nk}}, {{fin_event(j), 1u}}, {l, kind, j, j * rows, rows, nk, kc});
+    return row_f;
+  };
+  int prev = -1, prev_row = -1;
+  uint32_t prev_thr = 0;
+  for (int l = 0; l < c.num_layers; ++l) {
+    const int row_na = b.op_row(OP_NORM, l, prev_row >= 0 ? std::vector<int>{prev_row} : std::vector<int>{});
+    const int ev_na = b.event((uint32_t)M);
+    for (int m = 0; m < M; ++m) {
+      if (prev < 0)
+        b.task(OP_NORM, row_na, spec, {}, {{ev_na, 1u}}, {l, 0, m});
+      else
+        b.task(OP_NORM, row_na, spec, {{prev, prev_thr}}, {{ev_na, 1u}}, {l, 0, m});
+    }
+    // QKV: a 64-row tile lies inside one head; its finalize counts for the head's kv group
+    const uint32_t tiles_per_group = (uint32_t)((g + 2) * d / rt);
+    std::vector<int> ev_qkv(Hkv);
+    for (int hk = 0; hk < Hkv; ++hk) ev_qkv[hk] = b.event(tiles_per_group);
+    auto qkv_group = [&](int j) {
+      const int n0 = j * rt;
+      if (n0 < Hq * d) return (n0 / d) / g;
+      if (n0 < (Hq + Hkv) * d) return (n0 - Hq * d) / d;
+      return (n0 - (Hq + Hkv) * d) / d;
+    };
+    const int row_qf = proj(K_QKV, l, n_qkv, H, rt, {ev_na, (uint32_t)M}, row_na,
+                            [&](int j) { return ev_qkv[qkv_group(j)]; });
+    const int row_attn = b.op_row(OP_ATTN, l, {row_qf});
+    const int ev_oready = b.event((uint32_t)(R * Hkv));
+    for (int r = 0; r < R; ++r) {
+      const int cx = ctx[r], ns = (cx + st - 1) / st;
+      max_splits = std::max(max_splits, ns);
+      for (int hk = 0; hk < Hkv; ++hk) {
+        const int grp = b.n_arrivals++;
+        for (int s = 0; s < ns; ++s) {
+          const int t0 = s * st, t1 = std::min(cx, (s + 1) * st);
+          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {{ev_oready, 1u}},
+                 {l, r, hk, s, t0, t1, grp, ns, s});
+        }
+      }
+    }
+    std::pair<int, uint32_t> o_wait{ev_oready, (uint32_t)(R * Hkv)};
+    int o_dep = row_attn;
+    if (fp8) {
+      const int row_qo = b.op_row(OP_QUANT, l, {row_attn});
+      const int ev_oq = b.event((uint32_t)M);
+      for (int m = 0; m < M; ++m) b.task(OP_QUANT, row_qo, spec, {o_wait}, {{ev_oq, 1u}}, {l, 0, m});
+      o_wait = {ev_oq, (uint32_t)M};
+      o_dep = row_qo;
+    }
+    const int ev_o = b.event((uint32_t)(H / rt));
+    const int row_of = proj(K_O, l, H, Hq * d, rt, o_wait, o_dep, [&](int) { return ev_o; });
+    const int row_nb = b.op_row(OP_NORM, l, {row_of});
+    const int ev_nb = b.event((uint32_t)M);
+    for (int m = 0; m < M; ++m) b.task(OP_NORM, row_nb, spec, {{ev_o, (uint32_t)(H / rt)}}, {{ev_nb, 1u}}, {l, 1, m});
+    // gate/up: a tile holds rt/2 gate rows and the matching rt/2 up rows
+    const int ev_gu = b.event((uint32_t)(I / (rt / 2)));
+    const int row_gf = proj(K_GU, l, I, H, rt / 2, {ev_nb, (uint32_t)M}, row_nb, [&](int) { return ev_gu; });
+    std::pair<int, uint32_t> m_wait{ev_gu, (uint32_t)(I / (rt / 2))};
+    int m_dep = row_gf;
+    if (fp8) {
+      const int row_qm = b.op_row(OP_QUANT, l, {row_gf});
+      const int ev_mq = b.event((uint32_t)M);
+      for (int m = 0; m < M; ++m) b.task(OP_QUANT, row_qm, spec, {m_wait}, {{ev_mq, 1u}}, {l, 1, m});
+      m_wait = {ev_mq, (uint32_t)M};
+      m_dep = row_qm;
+    }
+    const int ev_down = b.event((uint32_t)(H / rt));
+    prev_row = proj(K_DOWN, l, H, I, rt, m_wait, m_dep, [&](int) { return ev_down; });
+    prev = ev_down;
+    prev_thr = (uint32_t)(H / rt);
+  }
 }
 
 }  // namespace
@@ -149,7 +243,20 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
   const uint32_t thr_grp = (uint32_t)((g + 2) * d / rq);
   int prev_down = -1, prev_down_row = -1;
   int max_splits = 0;
-  for (int l = 0; l < c.num_layers; ++l) {
+  if (p.spec == 1) {
+    if (c.workload == MK_QWEN3_STEP) {
+      err = "the full decode step is planned for one row (M = 1) only";
+      return MK_ERR_UNSUPPORTED;
+    }
+    if ((Hq + 2 * Hkv) * d % kM16Rows || H % kM16Rows || I % (kM16Rows / 2) || H % p.kc || I % p.kc ||
+        (Hq * d) % p.kc || R * c.tokens_per_request > 16) {
+      err = "unsupported multi-row shape: projection sizes must be multiples of the 64-row tile and of the K chunk, "
+            "and at most 16 rows";
+      return MK_ERR_UNSUPPORTED;
+    }
+    build_m16(c, ctx, p, b, max_splits);
+  }
+  for (int l = 0; l < (p.spec == 0 ? c.num_layers : 0); ++l) {
     int row_qkv = b.op_row(OP_QKV, l, prev_down_row >= 0 ? std::vector<int>{prev_down_row} : std::vector<int>{});
     int row_attn = b.op_row(OP_ATTN, l, {row_qkv});
     int row_o = b.op_row(OP_OPROJ, l, {row_attn});

@@ -9,7 +9,7 @@ from oracle import queue as oq
 from workloads import get_config
 
 
-@pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer"])
+@pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_invariants(name, W):
     cfg = get_config(name)
@@ -88,3 +88,53 @@ def test_page_packing_example():
     # the page's 70 events: 16, 16, 16, 48, 64 x 2 (D0 -> D2 pairs), 32, 1
     thr = [16, 16, 16, 48] + [2] * 64 + [32, 1]
     assert len(thr) == 70 and sum(1 for t in thr if t == 2) == 128 // 2
+
+
+def _tasks(plan):
+    q = plan["queue"]
+    return [q[w, i] for i in range(q.shape[1]) for w in range(q.shape[0]) if q[w, i][0] != oq.OP_NOOP]
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_layer", "qwen3_8b_layer_fp8"])
+def test_multi_row_tiles_cover_each_projection_once(name):
+    """Each projection's (row, K) grid is covered exactly once by its GEMM tiles, and its
+    rows exactly once by finalize tasks whose chunk count matches the tiles."""
+    cfg = get_config(name)
+    plan = oq.build_queue(cfg, 256)
+    p = plan["params"]
+    H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
+    shapes = {oq.K_QKV: ((cfg.n_q_heads + 2 * cfg.n_kv_heads) * d, H), oq.K_O: (H, cfg.n_q_heads * d),
+              oq.K_GU: (I, H), oq.K_DOWN: (H, I)}
+    kc = p["kc"]
+    assert kc * (1 if cfg.weight_fp8 else 2) * oq.M16_ROWS == 64 * 1024
+    ops = [int(t[0]) for t in _tasks(plan)]
+    assert set(ops) <= {oq.OP_NORM, oq.OP_GEMM, oq.OP_FIN, oq.OP_QUANT, oq.OP_ATTN}
+    for kind, (N, K) in shapes.items():
+        grid = np.zeros((N, K // kc), dtype=np.int64)
+        fin = np.zeros(N, dtype=np.int64)
+        for t in _tasks(plan):
+            pl = t[20:]  # payload words follow the header
+            if t[0] == oq.OP_GEMM and pl[1] == kind:
+                n0, rows, k0 = int(pl[3]), int(pl[4]), int(pl[5])
+                assert int(pl[6]) == kc and k0 % kc == 0
+                grid[n0:n0 + rows, k0 // kc] += 1
+            if t[0] == oq.OP_FIN and pl[1] == kind:
+                n0, rows, nk = int(pl[3]), int(pl[4]), int(pl[5])
+                assert nk == K // kc
+                fin[n0:n0 + rows] += 1
+        assert (grid == 1).all() and (fin == 1).all(), kind
+    n_norm = ops.count(oq.OP_NORM)
+    n_quant = ops.count(oq.OP_QUANT)
+    assert n_norm == 2 * cfg.m and n_quant == (2 * cfg.m if cfg.act_fp8 else 0)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_multi_row_no_deadlock_random_speeds(fp8):
+    cfg = dataclasses.replace(get_config("qwen3_8b_layer_fp8" if fp8 else "qwen3_8b_layer"),
+                              hidden=512, inter=1024, n_q_heads=4, n_kv_heads=2, n_requests=3,
+                              context=200, num_layers=2)
+    plan = oq.build_queue(cfg, 37)
+    assert plan["params"]["spec"] == 1
+    oq.check_invariants(plan)
+    for seed in range(2):
+        simulate(plan, seed)
