@@ -81,13 +81,18 @@ typedef struct {
  *   X [M, H] bf16;  R_IN [M, H] fp32 (residual stream)
  *   Y_OUT [M, H] bf16;  R2_OUT [M, H] fp32       (layer workload outputs; for the step: last layer)
  *   WORKSPACE  mk_plan_workspace_bytes() bytes, 256-byte aligned, contents need not be preserved
- *   step only: G_FINAL [H] bf16; W_LM [V, H] bf16; LOGITS_OUT [M, V] fp32; TOKEN_OUT [M] int32 */
+ *   step only: G_FINAL [H] bf16; W_LM [V, H] bf16; LOGITS_OUT [M, V] fp32; TOKEN_OUT [M] int32
+ *     (layer workloads leave these four entries 0)
+ *   FP8 weights (weight_fp8 = act_fp8 = 1) only: W_QKV, W_O, W_GU, W_DOWN hold e4m3 codes (OCP
+ *     E4M3FN, one byte per weight, same [N, K] layout) and S_QKV, S_O, S_GU, S_DOWN their fp32
+ *     scales per 128 x 128 block, [L, ceil(N/128), ceil(K/128)] row-major: weight = code * scale */
 enum {
   MK_T_W_QKV = 0, MK_T_W_O, MK_T_W_GU, MK_T_W_DOWN,
   MK_T_G_ATTN, MK_T_G_MLP, MK_T_G_Q, MK_T_G_K,
   MK_T_K_CACHE, MK_T_V_CACHE, MK_T_BLOCK_TABLE, MK_T_CONTEXT_LENS,
   MK_T_X, MK_T_R_IN, MK_T_Y_OUT, MK_T_R2_OUT, MK_T_WORKSPACE,
   MK_T_G_FINAL, MK_T_W_LM, MK_T_LOGITS_OUT, MK_T_TOKEN_OUT,
+  MK_T_S_QKV, MK_T_S_O, MK_T_S_GU, MK_T_S_DOWN,
   MK_T_COUNT_QWEN3
 };
 

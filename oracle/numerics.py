@@ -58,14 +58,22 @@ def round_f32(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
+    """The format definition, code by code: sign, exponent field (bias 7; 0 = subnormal), mantissa."""
+    c = np.asarray(c, dtype=np.int64)
     s = np.where(c >> 7, -1.0, 1.0)
     e = (c >> 3) & 15
     m = c & 7
     mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
     mag = np.where((e == 15) & (m == 7), np.nan, mag)
     return s * mag
+
+
+_E4M3_VALUES = _e4m3_value(np.arange(256))  # all 256 codes, decoded once
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_round(x: np.ndarray) -> np.ndarray:

@@ -25,7 +25,8 @@ MK_FLAG_NO_PREFETCH, MK_FLAG_NOOP_ONLY, MK_FLAG_TRACE = 1, 2, 4
 MK_MAX_TENSORS = 32
 QWEN3_TENSORS = ["w_qkv", "w_o", "w_gu", "w_down", "g_attn", "g_mlp", "g_q", "g_k", "k_cache", "v_cache",
                  "block_table", "context_lens", "x", "r_in", "y_out", "r2_out", "workspace",
-                 "g_final", "w_lm", "logits_out", "token_out"]
+                 "g_final", "w_lm", "logits_out", "token_out",
+                 "s_qkv", "s_o", "s_gu", "s_down"]
 _WORKLOADS = {"qwen3_layer": MK_QWEN3_LAYER, "qwen3_step": MK_QWEN3_STEP, "indexer_front": MK_INDEXER_FRONT}
 
 
@@ -172,9 +173,11 @@ class Plan:
 
 
 def qwen3_pointers(t: Dict[str, "object"], step: bool) -> MkTensors:
-    """mk_tensors in the ABI order from a dict of device tensors (torch) keyed by QWEN3_TENSORS."""
-    names = QWEN3_TENSORS if step else QWEN3_TENSORS[:QWEN3_TENSORS.index("workspace") + 1]
-    return Plan.tensors([t[n].data_ptr() for n in names])
+    """mk_tensors in the ABI order from a dict of device tensors (torch) keyed by QWEN3_TENSORS;
+    entries a workload does not use (the step's tail for a layer, the FP8 scales for bf16) are 0."""
+    fp8 = "s_qkv" in t
+    last = len(QWEN3_TENSORS) if fp8 else QWEN3_TENSORS.index("token_out" if step else "workspace") + 1
+    return Plan.tensors([t[n].data_ptr() if n in t else 0 for n in QWEN3_TENSORS[:last]])
 
 
 def exported_symbols():

@@ -49,6 +49,7 @@ struct mk_plan {
   uint32_t* d_trace = nullptr;
   size_t events_bytes = 0, arrivals_bytes = 0;
   uint32_t epoch = 0;  // megakernel runs so far; never reset (record tags must not repeat)
+  uint32_t cruns = 0;  // megakernel runs since the event counters were last zeroed
   uint32_t salt = 0;   // per-plan record tag base, a multiple of 1024
   bool occupancy_checked = false;
   bool host_only = false;  // planned without a device: queue inspection only
@@ -65,9 +66,12 @@ bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 mk_status check_tensors(const mk_plan* p, const mk_tensors* t) {
   if (!t) return fail(MK_ERR_INVALID, "null tensors");
   const mk_config& c = p->hp.cfg;
-  const int need = c.workload == MK_QWEN3_STEP ? MK_T_COUNT_QWEN3 : MK_T_WORKSPACE + 1;
+  const bool step = c.workload == MK_QWEN3_STEP, fp8 = c.weight_fp8 != 0;
+  const int need = fp8 ? MK_T_COUNT_QWEN3 : step ? MK_T_TOKEN_OUT + 1 : MK_T_WORKSPACE + 1;
   if (t->n < need) return fail(MK_ERR_INVALID, "too few tensors for this workload");
   for (int i = 0; i < need; ++i) {
+    const bool used = i <= MK_T_WORKSPACE || (step && i <= MK_T_TOKEN_OUT) || (fp8 && i >= MK_T_S_QKV);
+    if (!used) continue;
     if (t->ptr[i] == 0) return fail(MK_ERR_INVALID, "null tensor at index " + std::to_string(i));
     if (!aligned16(t->ptr[i])) return fail(MK_ERR_INVALID, "tensor " + std::to_string(i) + " is not 16-byte aligned");
   }
@@ -94,10 +98,65 @@ void fill_table(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& ta
   const int L = c.num_layers;
   const uint64_t qkv = ws + region_off(hp, "qkv"), ob = ws + region_off(hp, "o"), mb = ws + region_off(hp, "m");
   const uint64_t r2b = ws + region_off(hp, "r2"), r1b = ws + region_off(hp, "r1");
+  auto rg = [&](const char* n) { return ws + region_off(hp, n); };
+  const bool fp8 = c.act_fp8 != 0;
+  // multi-row projections by kind: weights, their block scales, N, K, operand-order input,
+  // partial sums, per-token input scales
+  const uint64_t wt[4] = {t->ptr[MK_T_W_QKV], t->ptr[MK_T_W_O], t->ptr[MK_T_W_GU], t->ptr[MK_T_W_DOWN]};
+  const uint64_t st[4] = {t->ptr[MK_T_S_QKV], t->ptr[MK_T_S_O], t->ptr[MK_T_S_GU], t->ptr[MK_T_S_DOWN]};
+  const uint64_t pn[4] = {nqkv, H, 2 * I, H}, pk[4] = {H, Hq * d, H, I};
+  const char* pin[4] = {"h1", fp8 ? "oq" : "o", "h2", fp8 ? "mq" : "m"};
+  const char* pgp[4] = {"gp_qkv", "gp_o", "gp_gu", "gp_down"};
+  const char* psa[4] = {"s1", "so", "s2", "sm"};
   tab.assign(hp.ops.size() * kTableSlots, 0);
   for (size_t row = 0; row < hp.ops.size(); ++row) {
     uint64_t* s = &tab[row * kTableSlots];
     const int l = hp.ops[row].layer;
+    const uint32_t sub = hp.ops[row].sub;
+    const bool spec1 = hp.tp.spec == 1;
+    switch (hp.ops[row].opcode) {
+      case OP_NORM:
+        s[NM_X] = sub == 0 ? (l == 0 ? t->ptr[MK_T_X] : rg("y")) : 0;
+        s[NM_R] = sub == 0 && l == 0 ? t->ptr[MK_T_R_IN] : rg("r2");
+        s[NM_GAIN] = (sub == 0 ? t->ptr[MK_T_G_ATTN] : t->ptr[MK_T_G_MLP]) + l * H * 2;
+        s[NM_R1] = sub == 0 ? r1b : 0;
+        s[NM_H] = rg(sub == 0 ? "h1" : "h2");
+        s[NM_S] = fp8 ? rg(sub == 0 ? "s1" : "s2") : 0;
+        break;
+      case OP_GEMM: {
+        const uint64_t nb = (pn[sub] + 127) / 128, kb = (pk[sub] + 127) / 128;
+        s[GM_W] = wt[sub] + l * pn[sub] * pk[sub] * welem;
+        s[GM_ACT] = rg(pin[sub]);
+        s[GM_PART] = rg(pgp[sub]);
+        s[GM_SW] = fp8 ? st[sub] + l * nb * kb * 4 : 0;
+        break;
+      }
+      case OP_FIN:
+        s[FN_PART] = rg(pgp[sub]);
+        s[FN_SA] = fp8 ? rg(psa[sub]) : 0;
+        s[FN_OUT] = sub == K_QKV ? qkv : sub == K_O ? r2b : sub == K_GU ? mb : rg("y");
+        s[FN_R1] = sub == K_O ? r1b : 0;
+        s[FN_OUT2] = l == L - 1 ? (sub == K_O ? t->ptr[MK_T_R2_OUT] : sub == K_DOWN ? t->ptr[MK_T_Y_OUT] : 0) : 0;
+        break;
+      case OP_ATTN:
+        s[ATT_QKV] = qkv;
+        s[ATT_GQ] = t->ptr[MK_T_G_Q] + l * d * 2;
+        s[ATT_GK] = t->ptr[MK_T_G_K] + l * d * 2;
+        s[ATT_KC] = t->ptr[MK_T_K_CACHE] + l * cache_layer;
+        s[ATT_VC] = t->ptr[MK_T_V_CACHE] + l * cache_layer;
+        s[ATT_BT] = t->ptr[MK_T_BLOCK_TABLE];
+        s[ATT_PART] = ws + region_off(hp, "part");
+        s[ATT_O] = ob;
+        s[ATT_ROPE] = (uint64_t)p->d_rope;
+        break;
+      case OP_QUANT:
+        s[QT_IN] = sub == 0 ? ob : mb;
+        s[QT_OUT] = rg(sub == 0 ? "oq" : "mq");
+        s[QT_S] = rg(sub == 0 ? "so" : "sm");
+        break;
+      default: break;
+    }
+    if (spec1) continue;
     switch (hp.ops[row].opcode) {
       case OP_QKV:
         s[QKV_W] = t->ptr[MK_T_W_QKV] + l * nqkv * H * welem;
@@ -174,13 +233,25 @@ mk_status check_runnable(mk_plan* p) {
   if (p->host_only) return fail(MK_ERR_INVALID, "plan was built without a device");
   const mk::HostPlan& hp = p->hp;
   const mk_config& c = hp.cfg;
-  if (hp.tp.spec != 0 || c.weight_fp8 || c.act_fp8)
-    return fail(MK_ERR_UNSUPPORTED, "only the bf16 single-token (M = 1) op bodies are built");
-  if (c.hidden > 2048 || c.inter > 6144 || c.n_q_heads * c.head_dim > 6144 || hp.tp.r_o > 128 ||
-      hp.tp.r_down > 128 || hp.tp.r_gu % 2 || (c.n_q_heads / c.n_kv_heads != 1 && c.n_q_heads / c.n_kv_heads != 2 &&
-      c.n_q_heads / c.n_kv_heads != 4) || c.hidden % 512 || c.inter % 512 || (c.n_q_heads * c.head_dim) % 512)
-    return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 2048; inter, q width <= 6144; "
-                                    "hidden, inter and q width multiples of 512; even gate/up tiles; GQA group 1, 2 or 4)");
+  const int g = c.n_q_heads / c.n_kv_heads;
+  if (g != 1 && g != 2 && g != 4) return fail(MK_ERR_UNSUPPORTED, "GQA group must be 1, 2 or 4");
+  if (c.weight_fp8 != c.act_fp8) return fail(MK_ERR_UNSUPPORTED, "FP8 weights come with FP8 activations (W8A8) only");
+  if (hp.tp.spec == 0) {
+    if (c.weight_fp8)
+      return fail(MK_ERR_UNSUPPORTED, "the single-token (M = 1) op bodies are built for bf16 weights only");
+    if (c.hidden > 2048 || c.inter > 6144 || c.n_q_heads * c.head_dim > 6144 || hp.tp.r_o > 128 ||
+        hp.tp.r_down > 128 || hp.tp.r_gu % 2 || c.hidden % 512 || c.inter % 512 || (c.n_q_heads * c.head_dim) % 512)
+      return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 2048; inter, q width <= 6144; "
+                                      "hidden, inter and q width multiples of 512; even gate/up tiles)");
+  } else {
+    const int K[3] = {c.hidden, c.n_q_heads * c.head_dim, c.inter};
+    for (int k : K)
+      if (k / hp.tp.kc > mk::kMaxChunks)
+        return fail(MK_ERR_UNSUPPORTED, "multi-row projection with more K chunks than a finalize task adds");
+    if (c.hidden > 8192 || c.inter > 12288 || c.n_q_heads * c.head_dim > 12288 || c.hidden % 512 || c.inter % 512)
+      return fail(MK_ERR_UNSUPPORTED, "shape exceeds the multi-row op bodies (hidden <= 8192, inter and q width "
+                                      "<= 12288, hidden and inter multiples of 512)");
+  }
   if (!p->occupancy_checked) {
     int per_cu = 0;
     HIP_TRY(hipSetDevice(p->device));
@@ -200,6 +271,7 @@ mk::KArgs base_args(const mk_plan* p, const uint64_t* table) {
   a.err = p->d_err;
   a.trace = p->d_trace;
   a.tag0 = p->salt + p->epoch * 1024u;
+  a.run = p->cruns;
   a.flags = p->hp.cfg.flags;
   a.sh = p->sh;
   return a;
@@ -245,7 +317,8 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
   }
   p->sh = mk::Shapes{c.hidden, c.inter, c.n_q_heads, c.n_kv_heads, c.n_q_heads / c.n_kv_heads,
                      (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, c.page_size, c.max_pages_per_req,
-                     hp.max_splits, c.vocab, c.rms_eps, 1.0f / std::sqrt((float)c.head_dim)};
+                     hp.max_splits, c.vocab, c.rms_eps, 1.0f / std::sqrt((float)c.head_dim),
+                     c.n_requests * c.tokens_per_request, hp.tp.kc, c.act_fp8 ? 1 : 0, c.num_layers};
   HIP_TRY(hipMalloc(&p->d_queue, hp.queue.size() * 4));
   HIP_TRY(hipMemcpy(p->d_queue, hp.queue.data(), hp.queue.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipMalloc(&p->d_tasks, hp.tasks.size() * 4));
@@ -335,6 +408,7 @@ mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
   a.first_task = 0;
   HIP_TRY(mk::launch_worker(a, p->hp.W, (hipStream_t)stream));
   p->epoch++;
+  p->cruns++;
   return MK_OK;
 }
 
@@ -425,6 +499,7 @@ mk_status mk_sync(mk_plan* p, void* stream) {
   uint32_t e[8];
   HIP_TRY(hipMemcpy(e, p->d_err, sizeof(e), hipMemcpyDeviceToHost));
   if (e[0]) {
+    p->cruns = 0;
     HIP_TRY(hipMemset(p->d_events, 0, p->events_bytes));
     HIP_TRY(hipMemset(p->d_arrivals, 0, p->arrivals_bytes));
     HIP_TRY(hipMemset(p->d_err, 0, 64));

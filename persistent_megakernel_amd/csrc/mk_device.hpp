@@ -12,6 +12,7 @@ namespace mk {
 struct Shapes {
   int H, I, Hq, Hkv, g, n_qkv, P, maxp, max_splits, V;
   float eps, inv_sqrt_d;
+  int M, kc, fp8, layers;  // multi-row plans: rows, K chunk of a projection tile, W8A8, layers
 };
 
 struct KArgs {
@@ -24,6 +25,7 @@ struct KArgs {
   uint32_t* err;           // device error record: flag, worker, task, event, value, target
   uint32_t* trace;         // [W, L, kTraceWords] or null
   uint32_t tag0;           // megakernel: this run's record tag base (plan salt + runs so far * 1024)
+  uint32_t run;            // megakernel: runs since the event counters were zeroed (targets (run + 1) * threshold)
   uint32_t flags;          // MK_FLAG_* | kModeGraph
   Shapes sh;
 };
@@ -69,6 +71,13 @@ constexpr int kAttVraw = kAttKraw + 1024;
 constexpr int kAttS = 21504;     // fp32 [g][128] scores
 constexpr int kAttP = kAttS + kMaxG * 512;  // fp32 [7 waves][g][20] exponentials of each wave's tokens
 constexpr int kActR1 = kActBytes - 1024;    // O projection / down: residual rows of the tile as records (<= 128)
+// multi-row ops in the activation staging area: a projection tile's input chunk (16 rows x one K
+// chunk in operand order, 16 KiB), the eight waves' 16 x 16 fp32 results, reduction scratch
+constexpr int kActA = 0;
+constexpr int kActABytes = 16384;
+constexpr int kActD = kActA + kActABytes;   // [8 waves][64 lanes][4] fp32
+constexpr int kActRed = kActD + 8192;       // [2][8] fp32 per-wave partial reductions
+static_assert(kActRed + 64 <= kActBytes, "multi-row staging overflows the activation area");
 static_assert(kActMerge + 7 * kMaxG * 130 * 4 <= kAttS, "attention merge area overlaps the scores");
 static_assert(kAttVraw + 1024 <= kAttS, "attention staging overlaps the scores");
 static_assert(kAttP + 7 * kMaxG * 20 * 4 <= kActBytes, "attention exponentials overflow the staging area");

@@ -25,6 +25,7 @@ enum Opcode : uint32_t {
 };
 enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3 };
 constexpr int kM16Rows = 64;  // weight rows of a multi-row projection tile (gate/up: 32 + 32)
+constexpr int kMaxChunks = 24;  // K chunks a multi-row finalize task adds
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 constexpr int kWords = 32;
@@ -57,6 +58,18 @@ enum OSlot { O_W = 0, O_IN, O_X, O_RIN, O_R2, O_R1, O_R2OUT };
 enum GuSlot { GU_W = 0, GU_GAMMA, GU_R2, GU_M };
 enum DownSlot { DN_W = 0, DN_M, DN_Y, DN_R2, DN_R1 };
 enum LmSlot { LM_W = 0, LM_GAMMA, LM_R1, LM_LOGITS, LM_PART, LM_TOKEN };
+// Multi-row plans keep their intermediates plain (no record tags: event counters order them).
+// Projection inputs are stored in the matrix-core operand order, 1 KiB per K step: bf16 steps of
+// 32, lane l = row + 16 * ((k % 32) / 8) holding 8 consecutive k; e4m3 steps of 64, lane
+// l = row + 16 * ((k % 64) / 16) holding 16 consecutive k.  Rows >= M stay 0.
+// NORM: x (0 for the post-attention norm), residual in, gain, r1 out (first norm only), h out, scale out
+enum NormSlot { NM_X = 0, NM_R, NM_GAIN, NM_R1, NM_H, NM_S };
+// GEMM tile: weights, operand-order input, fp32 partial sums [tile][chunk][4 x 64 lanes x 4], weight scales
+enum GemmSlot { GM_W = 0, GM_ACT, GM_PART, GM_SW };
+// FIN: partial sums, per-token input scales (FP8), output, r1 (O projection), caller's output (last layer)
+enum FinSlot { FN_PART = 0, FN_SA, FN_OUT, FN_R1, FN_OUT2 };
+// QUANT: fp32 rows in, e4m3 operand-order rows out, per-token scales out
+enum QuantSlot { QT_IN = 0, QT_OUT, QT_S };
 
 struct TileParams {
   int r_qkv = 0, r_o = 0, r_gu = 0, r_down = 0, r_lm = 0, s_tok = 0, spec = 0;
@@ -65,6 +78,7 @@ struct TileParams {
 
 struct OpInfo {      // one row of the operand table = one op instance
   uint32_t opcode;
+  uint32_t sub;      // GEMM / FIN: projection kind; NORM / QUANT: which (0: first, 1: second)
   int layer;
   int first_task, n_tasks;
   std::vector<int> deps;  // op rows this op waits on (graph edges)

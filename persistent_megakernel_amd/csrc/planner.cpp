@@ -42,8 +42,8 @@ struct Builder {
     thr.push_back(threshold);
     return (int)thr.size() - 1;
   }
-  int op_row(uint32_t opcode, int layer, std::vector<int> deps) {
-    ops.push_back(OpInfo{opcode, layer, (int)(tasks.size() / kWords), 0, std::move(deps)});
+  int op_row(uint32_t opcode, int layer, std::vector<int> deps, uint32_t sub = 0) {
+    ops.push_back(OpInfo{opcode, sub, layer, (int)(tasks.size() / kWords), 0, std::move(deps)});
     return (int)ops.size() - 1;
   }
   int task(uint32_t opcode, int row, int spec, std::initializer_list<std::pair<int, uint32_t>> waits,
@@ -115,14 +115,14 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
   const bool fp8 = c.act_fp8 != 0;
   auto proj = [&](uint32_t kind, int l, int N, int K, int rows, std::pair<int, uint32_t> wait, int dep_row,
                   auto fin_event) -> int {
-    const int row_g = b.op_row(OP_GEMM, l, {dep_row});
+    const int row_g = b.op_row(OP_GEMM, l, {dep_row}, kind);
     const int nt = N / rows, nk = K / kc;
     std::vector<int> parts(nt);
     for (int j = 0; j < nt; ++j) parts[j] = b.event((uint32_t)nk);
     for (int j = 0; j < nt; ++j)
       for (int ck = 0; ck < nk; ++ck)
         b.task(OP_GEMM, row_g, spec, {wait}, {{parts[j], 1u}}, {l, kind, j, j * rows, rows, ck * kc, kc});
-    const int row_f = b.op_row(OP_FIN, l, {row_g});
+    const int row_f = b.op_row(OP_FIN, l, {row_g}, kind);
     for (int j = 0; j < nt; ++j)
       b.task(OP_FIN, row_f, spec, {{parts[j], (uint32_t)nk}}, {{fin_event(j), 1u}}, {l, kind, j, j * rows, rows, nk, kc});
     return row_f;
@@ -130,7 +130,7 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
   int prev = -1, prev_row = -1;
   uint32_t prev_thr = 0;
   for (int l = 0; l < c.num_layers; ++l) {
-    const int row_na = b.op_row(OP_NORM, l, prev_row >= 0 ? std::vector<int>{prev_row} : std::vector<int>{});
+    const int row_na = b.op_row(OP_NORM, l, prev_row >= 0 ? std::vector<int>{prev_row} : std::vector<int>{}, 0);
     const int ev_na = b.event((uint32_t)M);
     for (int m = 0; m < M; ++m) {
       if (prev < 0)
@@ -167,7 +167,7 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
     std::pair<int, uint32_t> o_wait{ev_oready, (uint32_t)(R * Hkv)};
     int o_dep = row_attn;
     if (fp8) {
-      const int row_qo = b.op_row(OP_QUANT, l, {row_attn});
+      const int row_qo = b.op_row(OP_QUANT, l, {row_attn}, 0);
       const int ev_oq = b.event((uint32_t)M);
       for (int m = 0; m < M; ++m) b.task(OP_QUANT, row_qo, spec, {o_wait}, {{ev_oq, 1u}}, {l, 0, m});
       o_wait = {ev_oq, (uint32_t)M};
@@ -175,7 +175,7 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
     }
     const int ev_o = b.event((uint32_t)(H / rt));
     const int row_of = proj(K_O, l, H, Hq * d, rt, o_wait, o_dep, [&](int) { return ev_o; });
-    const int row_nb = b.op_row(OP_NORM, l, {row_of});
+    const int row_nb = b.op_row(OP_NORM, l, {row_of}, 1);
     const int ev_nb = b.event((uint32_t)M);
     for (int m = 0; m < M; ++m) b.task(OP_NORM, row_nb, spec, {{ev_o, (uint32_t)(H / rt)}}, {{ev_nb, 1u}}, {l, 1, m});
     // gate/up: a tile holds rt/2 gate rows and the matching rt/2 up rows
@@ -184,7 +184,7 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
     std::pair<int, uint32_t> m_wait{ev_gu, (uint32_t)(I / (rt / 2))};
     int m_dep = row_gf;
     if (fp8) {
-      const int row_qm = b.op_row(OP_QUANT, l, {row_gf});
+      const int row_qm = b.op_row(OP_QUANT, l, {row_gf}, 1);
       const int ev_mq = b.event((uint32_t)M);
       for (int m = 0; m < M; ++m) b.task(OP_QUANT, row_qm, spec, {m_wait}, {{ev_mq, 1u}}, {l, 1, m});
       m_wait = {ev_mq, (uint32_t)M};
@@ -343,13 +343,42 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
     out.regions.push_back({name, off, bytes});
     off += (bytes + 255) / 256 * 256;
   };
-  // vectors written inside a run are tagged 8-byte records: fp32 or a bf16 pair per record
-  region("qkv", (size_t)M * n_qkv * 8);
-  region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);  // per split: g*d O, g lse, padding (fp32)
-  region("o", (size_t)M * Hq * d / 2 * 8);
-  region("m", (size_t)M * I / 2 * 8);
-  region("r2", (size_t)M * H * 8);
-  region("r1", (size_t)M * H * 8);
+  if (p.spec == 1) {
+    // multi-row: qkv as tagged records (the attention staging reads records), everything else
+    // plain; projection inputs in the matrix-core operand order over 16 row slots
+    const size_t el = c.act_fp8 ? 1 : 2;
+    const size_t kc = (size_t)p.kc;
+    region("qkv", (size_t)M * n_qkv * 8);
+    region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);
+    region("r1", (size_t)M * H * 4);
+    region("r2", (size_t)M * H * 4);
+    region("y", (size_t)M * H * 2);
+    region("h1", (size_t)16 * H * el);
+    region("h2", (size_t)16 * H * el);
+    if (c.act_fp8) {  // attention output and m in fp32 rows, quantised per token into oq / mq
+      region("o", (size_t)M * Hq * d * 4);
+      region("m", (size_t)M * I * 4);
+      region("oq", (size_t)16 * Hq * d);
+      region("mq", (size_t)16 * I);
+      for (const char* s : {"s1", "s2", "so", "sm"}) region(s, 16 * 4);
+    } else {
+      region("o", (size_t)16 * Hq * d * 2);
+      region("m", (size_t)16 * I * 2);
+    }
+    // fp32 partial sums of the projection tiles: [tile][K chunk][16 x 64]
+    region("gp_qkv", (size_t)(n_qkv / kM16Rows) * (H / kc) * 4096);
+    region("gp_o", (size_t)(H / kM16Rows) * (Hq * d / kc) * 4096);
+    region("gp_gu", (size_t)(I / (kM16Rows / 2)) * (H / kc) * 4096);
+    region("gp_down", (size_t)(H / kM16Rows) * (I / kc) * 4096);
+  } else {
+    // vectors written inside a run are tagged 8-byte records: fp32 or a bf16 pair per record
+    region("qkv", (size_t)M * n_qkv * 8);
+    region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);  // per split: g*d O, g lse, padding (fp32)
+    region("o", (size_t)M * Hq * d / 2 * 8);
+    region("m", (size_t)M * I / 2 * 8);
+    region("r2", (size_t)M * H * 8);
+    region("r1", (size_t)M * H * 8);
+  }
   if (c.workload == MK_QWEN3_STEP) region("lm_part", (size_t)((c.vocab + p.r_lm - 1) / p.r_lm) * 8);
   out.workspace_bytes = off;
 

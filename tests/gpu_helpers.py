@@ -12,6 +12,19 @@ def to_device(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |v| (8 significant bits; the smallest normal spacing below)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def bf16_excess(gpu: np.ndarray, pre: np.ndarray, tol: float) -> float:
+    """How far a bf16 output is from being the bf16 rounding of a value within tol of the
+    oracle's value before rounding: max(|gpu - pre| - tol - half ulp), <= 0 when it is."""
+    allow = tol + np.maximum(bf16_half_ulp(gpu), bf16_half_ulp(pre))
+    return float(np.max(np.abs(gpu - pre) - allow)) if gpu.size else 0.0
+
+
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     b = t.detach().cpu().numpy().view(np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)

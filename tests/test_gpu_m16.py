@@ -1,0 +1,192 @@
+"""GPU parity of the multi-row (16-token) decode layer -- bf16 and W8A8 FP8 -- against the CPU
+oracle, through the C ABI: megakernel and both graph baselines.
+
+Tolerances: max abs error 2e-2 (bf16) and 6e-2 (FP8 weights and activations) on the layer outputs
+y and r2 and on the intermediates, against the oracle value before its output rounding; a value
+the layer materialises in bf16 passes when it is the bf16 rounding of a value within that error
+(bf16 spacing alone exceeds 2e-2 from |v| >= 8).  Cache writes: the written slot set is exact
+(every other byte of both caches is unchanged bit for bit).
+At the full sizes the oracle runs on a sample of the requests: the rows of the layer are
+independent requests, so a request's outputs depend only on its own row, its own cache pages and
+the shared weights; the sample's pages are copied into a compact pool with a remapped block table.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import model
+from oracle.numerics import bf16_bits_to_f64, e4m3_decode
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _tol(cfg):
+    return 6e-2 if cfg.act_fp8 else 2e-2
+
+
+def opnd_bf16_rows(buf: np.ndarray, K: int) -> np.ndarray:
+    """[16, K] float64 from the bf16 matrix-core operand order: per K step of 32, lane
+    m + 16 * ((k % 32) // 8) holds 8 consecutive k of row m."""
+    a = buf.view(np.uint16)[:16 * K].reshape(K // 32, 4, 16, 8).transpose(2, 0, 1, 3).reshape(16, K)
+    return bf16_bits_to_f64(a)
+
+
+def opnd_fp8_rows(buf: np.ndarray, K: int) -> np.ndarray:
+    """[16, K] e4m3 codes from the FP8 operand order: per K step of 64, lane
+    m + 16 * ((k % 64) // 16) holds 16 consecutive k of row m."""
+    return buf.view(np.uint8)[:16 * K].reshape(K // 64, 4, 16, 16).transpose(2, 0, 1, 3).reshape(16, K)
+
+
+def _run(cfg, inp, W=0):
+    from gpu_helpers import QwenRun
+    # the plan is built for the inputs' context lengths (tile counts and RoPE positions follow them)
+    return QwenRun(cfg, inp, num_workers=W, ctx=[int(c) for c in inp["context_lens"]])
+
+
+def _ws(run, name, dtype=torch.uint8):
+    return run.region(name, dtype).cpu().numpy()
+
+
+def _check_outputs(run, ref, rows, tag):
+    """y, r2 of the given GPU rows against the oracle rows 0.. of ref."""
+    from gpu_helpers import bf16_excess, bf16_to_f64
+    cfg, tol = run.cfg, _tol(run.cfg)
+    y = bf16_to_f64(run.t["y_out"]).reshape(cfg.m, cfg.hidden)[rows]
+    r2 = run.t["r2_out"].cpu().numpy().astype(np.float64).reshape(cfg.m, cfg.hidden)[rows]
+    ey, er = np.max(np.abs(y - ref["y_pre"])), np.max(np.abs(r2 - ref["r2"]))
+    _say(f"  {tag}: y err {ey:.3e} (max |y| {np.abs(ref['y_pre']).max():.3g}) r2 err {er:.3e}")
+    assert bf16_excess(y, ref["y_pre"], tol) <= 0 and er <= tol, f"{tag}: y err {ey}, r2 err {er}"
+
+
+def _check_cache(run, inp, ref, rows, k_before, v_before, tag):
+    """The written slots are exactly the oracle's; their rows match; nothing else changed."""
+    cfg, tol = run.cfg, _tol(run.cfg)
+    kc = run.t["k_cache"].cpu().numpy().view(np.uint16)[0]
+    vc = run.t["v_cache"].cpu().numpy().view(np.uint16)[0]
+    mask = np.ones(kc.shape[:2], dtype=bool)
+    ctx = inp["context_lens"]
+    for r in range(cfg.n_requests):
+        p = int(ctx[r]) - 1
+        mask[inp["block_table"][r][p // cfg.page_size], p % cfg.page_size] = False
+    assert np.array_equal(kc[mask], k_before[mask]) and np.array_equal(vc[mask], v_before[mask]), tag
+    from gpu_helpers import bf16_excess
+    for i, r in enumerate(rows):
+        p = int(ctx[r]) - 1
+        page, off = inp["block_table"][r][p // cfg.page_size], p % cfg.page_size
+        assert bf16_excess(bf16_bits_to_f64(kc[page, off]), ref["k_pre"][i], tol) <= 0, tag
+        assert bf16_excess(bf16_bits_to_f64(vc[page, off]), ref["v_pre"][i], tol) <= 0, tag
+
+
+def _check_intermediates(run, ref, tag):
+    """Every workspace intermediate of a run covering all rows (reduced shapes)."""
+    cfg, tol = run.cfg, _tol(run.cfg)
+    M, H, I, q = cfg.m, cfg.hidden, cfg.inter, cfg.n_q_heads * cfg.head_dim
+    qkv = run.payload_f32("qkv").reshape(M, -1)
+    assert np.max(np.abs(qkv - ref["qkv"])) <= tol, tag
+    r1 = _ws(run, "r1").view(np.float32).astype(np.float64)[:M * H].reshape(M, H)
+    assert np.max(np.abs(r1 - ref["r1"])) <= 1e-5, tag  # an fp32 add: rounding only
+    r2 = _ws(run, "r2").view(np.float32).astype(np.float64)[:M * H].reshape(M, H)
+    assert np.max(np.abs(r2 - ref["r2"])) <= tol, tag
+    if cfg.act_fp8:
+        for name, K, key in (("h1", H, "h1_pre"), ("h2", H, "h2_pre")):
+            s = _ws(run, "s" + name[1]).view(np.float32)[:M].astype(np.float64)
+            assert np.allclose(s, ref["s" + name[1]], rtol=1e-5), f"{tag} {name} scales"
+            codes = opnd_fp8_rows(_ws(run, name), K)[:M]
+            deq = e4m3_decode(codes) * s[:, None]
+            # one e4m3 step of the row's scale at most (a code at a rounding boundary may flip)
+            assert np.all(np.abs(deq - ref[key]) <= s[:, None] * 32.0 + 1e-12), f"{tag} {name}"
+        o = _ws(run, "o").view(np.float32)[:M * q].astype(np.float64).reshape(M, q)
+        assert np.max(np.abs(o - ref["o_pre"])) <= tol, tag
+        m = _ws(run, "m").view(np.float32)[:M * I].astype(np.float64).reshape(M, I)
+        assert np.max(np.abs(m - ref["m_pre"])) <= tol, tag
+        for name, K, key, skey in (("oq", q, "o_pre", "so"), ("mq", I, "m_pre", "sm")):
+            s = _ws(run, skey).view(np.float32)[:M].astype(np.float64)
+            assert np.allclose(s, ref[skey], rtol=1e-4), f"{tag} {skey}"
+            deq = e4m3_decode(opnd_fp8_rows(_ws(run, name), K)[:M]) * s[:, None]
+            assert np.all(np.abs(deq - ref[key]) <= s[:, None] * 32.0 + 1e-12), f"{tag} {name}"
+        pad = [opnd_fp8_rows(_ws(run, n), K)[M:] for n, K in (("h1", H), ("h2", H), ("oq", q), ("mq", I))]
+    else:
+        from gpu_helpers import bf16_excess
+        for name, K, key in (("h1", H, "h1_pre"), ("h2", H, "h2_pre"), ("o", q, "o_pre"), ("m", I, "m_pre")):
+            v = opnd_bf16_rows(_ws(run, name), K)
+            assert bf16_excess(v[:M], ref[key], tol) <= 0, f"{tag} {name}"
+        pad = [opnd_bf16_rows(_ws(run, n), K)[M:] for n, K in (("h1", H), ("h2", H), ("o", q), ("m", I))]
+    assert all(np.all(p == 0) for p in pad), f"{tag}: padding rows of the operand-order inputs were written"
+
+
+def _reduced(fp8, R, ctx):
+    base = get_config("qwen3_8b_layer_fp8" if fp8 else "qwen3_8b_layer")
+    return dataclasses.replace(base, hidden=1024, inter=2048 if fp8 else 1536, n_q_heads=8, n_kv_heads=2,
+                               n_requests=R, context=max(ctx), page_size=16)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_m16_reduced_layer_all_modes(fp8):
+    ctx = [1, 37, 300, 513, 64]
+    cfg = _reduced(fp8, len(ctx), ctx)
+    inp = make_inputs(cfg, seed=3)
+    inp["context_lens"] = np.array(ctx, dtype=np.int32)
+    ref = model.run_qwen3_layer(cfg, inp)
+    k0, v0 = inp["k_cache"][0].copy(), inp["v_cache"][0].copy()
+    rows = list(range(cfg.m))
+    for W in (0, 37):
+        run = _run(cfg, inp, W)
+        assert run.plan.queue()[0, 0, 4] == 1  # the multi-row plan
+        outs = []
+        for mode, ms in (("mk", False), ("graph", False), ("graph", True), ("mk", False)):
+            _say(f"case: reduced multi-row fp8={fp8} W={W} {mode} multistream={ms}")
+            run.t["y_out"].zero_()
+            run.t["r2_out"].zero_()
+            run.run(mode, ms)
+            _check_outputs(run, ref, rows, f"{mode}/{ms}")
+            _check_cache(run, inp, ref, rows, k0, v0, f"{mode}/{ms}")
+            _check_intermediates(run, ref, f"W={W} {mode}/{ms}")
+            outs.append((run.t["y_out"].clone(), run.t["r2_out"].clone()))
+        # fixed-order reductions: every mode gives the same bits
+        for y, r in outs[1:]:
+            assert torch.equal(y, outs[0][0]) and torch.equal(r, outs[0][1])
+
+
+def _sample_inputs(cfg, inp, rows):
+    """Inputs of a layer restricted to some requests, their cache pages copied into a compact pool."""
+    bt = inp["block_table"][rows]
+    pages = np.unique(bt)
+    remap = np.full(cfg.num_phys_pages, -1, dtype=np.int64)
+    remap[pages] = np.arange(len(pages))
+    sub = dict(inp)
+    sub["block_table"] = remap[bt].astype(np.int32)
+    sub["context_lens"] = inp["context_lens"][rows]
+    sub["x"], sub["r_in"] = inp["x"][rows], inp["r_in"][rows]
+    sub["k_cache"], sub["v_cache"] = inp["k_cache"][:, pages], inp["v_cache"][:, pages]
+    scfg = dataclasses.replace(cfg, n_requests=len(rows))
+    return scfg, sub
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_layer", "qwen3_8b_layer_fp8"])
+def test_m16_full_size_sampled_rows(name):
+    cfg = get_config(name)
+    _say(f"case: {name} full size, inputs")
+    inp = make_inputs(cfg, seed=0)
+    k0, v0 = inp["k_cache"][0].copy(), inp["v_cache"][0].copy()
+    run = _run(cfg, inp)
+    _say(f"case: {name} megakernel W=all")
+    run.run("mk")
+    rows = [0, 9, 15]
+    scfg, sub = _sample_inputs(cfg, inp, rows)
+    _say(f"case: {name} oracle on rows {rows}")
+    ref = model.run_qwen3_layer(scfg, sub)
+    _check_outputs(run, ref, rows, f"{name} mk")
+    _check_cache(run, inp, ref, rows, k0, v0, f"{name} mk")
+    y_mk = run.t["y_out"].clone()
+    _say(f"case: {name} graph multistream")
+    run.t["y_out"].zero_()
+    run.run("graph", True)
+    assert torch.equal(run.t["y_out"], y_mk)

@@ -19,6 +19,7 @@ the handbook's decode byte model (the ``decode_gaps.py`` model table).
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Dict, Optional
 
 import numpy as np
@@ -100,7 +101,7 @@ def get_config(name: str, **overrides) -> Config:
 def f32_to_bf16_bits_trunc(a: np.ndarray) -> np.ndarray:
     """Upper 16 bits of float32 values (round toward zero): the synthetic bf16 draw."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    return (a.view(np.uint32) >> 16).astype(np.uint16)
+    return a.reshape(-1).view(np.uint16)[1::2].reshape(a.shape)  # little-endian: the upper half words
 
 
 def _bf16_normal(rng: np.random.Generator, shape, std: float, mean: float = 0.0) -> np.ndarray:
@@ -113,31 +114,46 @@ def _bf16_normal(rng: np.random.Generator, shape, std: float, mean: float = 0.0)
         v *= np.float32(std)
         if mean:
             v += np.float32(mean)
-        flat[s:s + n] = f32_to_bf16_bits_trunc(v)
+        flat[s:s + n] = v.view(np.uint16)[1::2]  # upper 16 bits (little-endian)
     return out
 
 
-def _fp8_codes(rng: np.random.Generator, shape, exp_mean: float = 9.0, exp_std: float = 1.5) -> np.ndarray:
-    """e4m3 code bytes drawn field by field: sign uniform, exponent field from a rounded
-    normal clipped to [0, 15], mantissa uniform in [0, 7]; the NaN pattern
-    (exponent 15, mantissa 7) is redrawn as mantissa 6."""
+def _binade_probs(sigma: float) -> np.ndarray:
+    """P(|v| falls in the e4m3 binade of exponent field e), e = 0..15, for v ~ N(0, sigma^2) in
+    code units: field 0 holds [0, 2^-6), field e >= 1 holds [2^(e-7), 2^(e-6)), and field 15 also
+    every larger magnitude (the top binade takes the tail)."""
+    edges = [0.0] + [2.0 ** (e - 7) for e in range(1, 16)] + [math.inf]
+    cdf = [math.erf(x / (sigma * math.sqrt(2.0))) if math.isfinite(x) else 1.0 for x in edges]
+    p = np.diff(np.array(cdf))
+    return p / p.sum()
+
+
+def _fp8_codes(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    """e4m3 code bytes drawn field by field so that the decoded values spread like a normal
+    N(0, sigma^2) in code units: sign uniform, exponent field from the normal's binade
+    probabilities, mantissa uniform in [0, 7] (the NaN pattern, exponent 15 with mantissa 7, is
+    drawn as mantissa 6)."""
+    probs = _binade_probs(sigma)
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint8)
     chunk = 1 << 24
     for s in range(0, n, chunk):
         k = min(chunk, n - s)
         sign = rng.integers(0, 2, k, dtype=np.uint8)
-        e = np.clip(np.rint(rng.normal(exp_mean, exp_std, k)), 0, 15).astype(np.uint8)
+        e = rng.choice(16, size=k, p=probs).astype(np.uint8)
         m = rng.integers(0, 8, k, dtype=np.uint8)
         m = np.where((e == 15) & (m == 7), np.uint8(6), m)
         out[s:s + k] = (sign << 7) | (e << 3) | m
     return out.reshape(shape)
 
 
-# FP8 weight codes drawn with exponent field ~ N(9, 1.5) have an RMS decoded magnitude of
-# about 6; this block-scale base makes the effective weights' spread about 0.02.
-_FP8_W_SCALE = 0.02 / 6.0
-_FP8_K_SCALE = 1.0 / 6.0
+# Spread of the codes, as a per-group amax -> 448 mapping of normal values would give them: a
+# 128 x 128 weight block's amax is about 4 standard deviations (codes ~ N(0, 112^2)), a 128-wide
+# key row's about 2.6 (codes ~ N(0, 172^2)).  The scales then make the effective values
+# N(0, 0.02^2) for weights and N(0, 1) for keys.
+_FP8_W_SIGMA, _FP8_K_SIGMA = 112.0, 172.0
+_FP8_W_SCALE = 0.02 / _FP8_W_SIGMA
+_FP8_K_SCALE = 1.0 / _FP8_K_SIGMA
 
 
 def _page_table(rng: np.random.Generator, cfg: Config) -> np.ndarray:
@@ -174,7 +190,7 @@ def make_inputs(cfg: Config, seed: int = 0, layers: Optional[int] = None) -> Dic
         shapes = [("w_qkv", (nq + 2 * nkv, H)), ("w_o", (H, nq)), ("w_gu", (2 * I, H)), ("w_down", (H, I))]
         for name, (n, k) in shapes:
             if cfg.weight_fp8:
-                out[name] = _fp8_codes(rng, (L, n, k))
+                out[name] = _fp8_codes(rng, (L, n, k), _FP8_W_SIGMA)
                 nb, kb = -(-n // 128), -(-k // 128)
                 out["s_" + name[2:]] = (rng.uniform(0.8, 1.25, (L, nb, kb)) * _FP8_W_SCALE).astype(np.float32)
             else:
@@ -201,14 +217,14 @@ def make_inputs(cfg: Config, seed: int = 0, layers: Optional[int] = None) -> Dic
         H = cfg.hidden
         qr, nh, hd = cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
         for name, (n, k) in [("w_qa", (qr, H)), ("w_w", (nh, H)), ("w_k", (hd, H)), ("w_qi", (nh * hd, qr))]:
-            out[name] = _fp8_codes(rng, (n, k))
+            out[name] = _fp8_codes(rng, (n, k), _FP8_W_SIGMA)
             out["s_" + name[2:]] = (rng.uniform(0.8, 1.25, (-(-n // 128), -(-k // 128))) * _FP8_W_SCALE).astype(np.float32)
         out["g_norm"] = _bf16_normal(rng, (H,), 0.02, 1.0)
         out["g_qa"] = _bf16_normal(rng, (qr,), 0.02, 1.0)
         bt = _page_table(rng, cfg)
         out["block_table"] = bt
         out["context_lens"] = np.full(cfg.n_requests, cfg.context, dtype=np.int32)
-        out["key_cache"] = _fp8_codes(rng, (cfg.num_phys_pages, cfg.page_size, hd), exp_mean=7.0)
+        out["key_cache"] = _fp8_codes(rng, (cfg.num_phys_pages, cfg.page_size, hd), _FP8_K_SIGMA)
         out["key_scale"] = (rng.uniform(0.8, 1.25, (cfg.num_phys_pages, cfg.page_size)) * _FP8_K_SCALE).astype(np.float32)
         out["x"] = _bf16_normal(rng, (cfg.m, H), 1.0)
         out["r_in"] = rng.standard_normal((cfg.m, H), dtype=np.float32)
