@@ -62,7 +62,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3_0p6b_step", choices=["qwen3_0p6b_step", "qwen3_0p6b_layer"])
+    ap.add_argument("--workload", default="qwen3_0p6b_step",
+                    choices=["qwen3_0p6b_step", "qwen3_0p6b_layer", "qwen3_8b_layer", "qwen3_8b_layer_fp8"])
     ap.add_argument("--rotate", type=int, default=0, help="copies of weights/caches cycled per run (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
@@ -86,7 +87,9 @@ def main() -> int:
     from workloads import algorithmic_bytes, get_config, make_inputs
 
     cfg = get_config(args.workload)
-    rotate = args.rotate or (1 if cfg.workload == "qwen3_step" else 16)
+    # rotation copies keep the timed runs from being served out of the 256 MiB MALL: the full step
+    # and the 16-token layers are larger than it on their own (two copies for the layers)
+    rotate = args.rotate or (1 if cfg.workload == "qwen3_step" else 2 if cfg.m > 1 else 16)
     _log(f"bench: workload {cfg.name}, rotate {rotate}, generating inputs")
     t0 = time.time()
     inp = make_inputs(cfg, seed=0)
@@ -167,7 +170,7 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 (bf16 MFMA products, fp32 sums)" if cfg.weight_fp8 else "bf16",
         "data": "synthetic (seeded random weights and KV caches of the workload's shapes)",
         "config": {"workload": cfg.name, "layers": layers, "hidden": cfg.hidden, "inter": cfg.inter,
                    "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,

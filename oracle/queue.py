@@ -35,6 +35,7 @@ OP_NOOP, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = 0, 1, 2, 3, 
 # multi-row (M = 16) plans: per-row norms, projection tiles over K chunks with explicit finalize
 # tasks, per-row FP8 quantisation of the O and down inputs
 OP_NORM, OP_GEMM, OP_FIN, OP_QUANT = 7, 8, 9, 10
+OP_COMB = 11  # multi-row: combine the split-KV partials of one (request, kv head)
 K_QKV, K_O, K_GU, K_DOWN = 0, 1, 2, 3  # projection kinds
 NONE = 0xFFFFFFFF
 LEASE_BYTES = 65536  # largest LDS lease of one instruction
@@ -193,7 +194,8 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
 
     Waits (all "whole" unless stated): NORM_A on the previous layer's down finalizes; QKV tiles
     on NORM_A; QKV finalize on its tile's chunks ("tile_reduce"); attention on the QKV finalizes of
-    its kv group ("tile_cover"); [QUANT_O on every combine]; O tiles on the combines [or QUANT_O];
+    its kv group ("tile_cover"); a combine on its group's splits ("tile_reduce"); [QUANT_O on every
+    combine]; O tiles on the combines [or QUANT_O];
     NORM_B on the O finalizes; gate/up tiles on NORM_B; [QUANT_M on the gate/up finalizes]; down
     tiles on the gate/up finalizes [or QUANT_M]."""
     H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
@@ -234,17 +236,25 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
             return (n0 - (Hq + Hkv) * d) // d
 
         proj(K_QKV, l, n_qkv, H, rt, (ev_na, M), lambda j: (ev_qkv[qkv_group(j)], 1))
+        # split-KV partials, one event per (request, kv head) counting its splits; then one combine
+        # task per (request, kv head) -- dealt round-robin like every task, so the combines spread
+        # over the workers instead of landing on whichever split happens to arrive last
         row_attn = b.op_row()
-        ev_oready = b.event(R * Hkv)
+        nsplit = [-(-int(ctx_lens[r]) // st) for r in range(R)]
+        ev_att = [b.event(nsplit[r]) for r in range(R) for _ in range(Hkv)]
         for r in range(R):
-            ctx = int(ctx_lens[r])
-            ns = -(-ctx // st)
+            ctx, ns = int(ctx_lens[r]), nsplit[r]
             for hk in range(Hkv):
-                grp = b.arrival_group()
                 for s in range(ns):
                     t0, t1 = s * st, min(ctx, (s + 1) * st)
-                    b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk], tiles_per_group)], [(ev_oready, 1)],
-                           [l, r, hk, s, t0, t1, grp, ns, s])
+                    b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk], tiles_per_group)], [(ev_att[r * Hkv + hk], 1)],
+                           [l, r, hk, s, t0, t1, 0, 0, 0, ns])
+        row_comb = b.op_row()
+        ev_oready = b.event(R * Hkv)
+        for r in range(R):
+            for hk in range(Hkv):
+                b.task(OP_COMB, row_comb, spec, [(ev_att[r * Hkv + hk], nsplit[r])], [(ev_oready, 1)],
+                       [l, r, hk, nsplit[r]])
         o_wait = (ev_oready, R * Hkv)
         if fp8:
             row_qo = b.op_row()

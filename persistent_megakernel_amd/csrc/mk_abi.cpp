@@ -149,6 +149,10 @@ void fill_table(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& ta
         s[ATT_O] = ob;
         s[ATT_ROPE] = (uint64_t)p->d_rope;
         break;
+      case OP_COMB:
+        s[ATT_PART] = ws + region_off(hp, "part");
+        s[ATT_O] = ob;
+        break;
       case OP_QUANT:
         s[QT_IN] = sub == 0 ? ob : mb;
         s[QT_OUT] = rg(sub == 0 ? "oq" : "mq");
@@ -255,7 +259,7 @@ mk_status check_runnable(mk_plan* p) {
   if (!p->occupancy_checked) {
     int per_cu = 0;
     HIP_TRY(hipSetDevice(p->device));
-    HIP_TRY(mk::worker_occupancy(&per_cu));
+    HIP_TRY(mk::worker_occupancy(&per_cu, hp.tp.spec));
     if (per_cu < 1) return fail(MK_ERR_UNSUPPORTED, "worker block does not fit on a compute unit");
     if (hp.W > p->cus * per_cu) return fail(MK_ERR_INVALID, "more workers than co-resident blocks: the persistent kernel could deadlock");
     p->occupancy_checked = true;
@@ -406,7 +410,7 @@ mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
   a.instrs = p->d_queue;
   a.L = p->hp.L;
   a.first_task = 0;
-  HIP_TRY(mk::launch_worker(a, p->hp.W, (hipStream_t)stream));
+  HIP_TRY(mk::launch_worker(a, p->hp.W, (hipStream_t)stream, p->hp.tp.spec));
   p->epoch++;
   p->cruns++;
   return MK_OK;
@@ -475,7 +479,7 @@ mk_status mk_run_graph_baseline(mk_plan* p, const mk_tensors* t, int32_t multist
       a.first_task = ops[k].first_task;
       a.L = ops[k].n_tasks;
       const int grid = std::min(ops[k].n_tasks, p->hp.W);
-      HIP_TRY(mk::launch_worker(a, grid, s));
+      HIP_TRY(mk::launch_worker(a, grid, s, p->hp.tp.spec));
       HIP_TRY(hipEventRecord(p->events[k], s));
     }
     for (int i = 1; i < n_streams; ++i) {  // join every forked stream back

@@ -65,6 +65,9 @@ constexpr int kActQ = 0;       // bf16 [g][128] rotated q heads
 constexpr int kActK = 2048;    // bf16 [128] new key
 constexpr int kActV = 2304;    // bf16 [128] new value
 constexpr int kActMerge = 2560;  // fp32 [7 waves][g][128] per-wave partial P V (<= 17920 bytes)
+constexpr int kAttGq = 2560;     // q and k norm gains (bf16 [128] each) and the request's RoPE row
+constexpr int kAttGk = 2816;     // (fp32 (cos, sin) [64]): read in the first phase, before the merge
+constexpr int kAttRope = 3072;   // area they share is written
 constexpr int kAttQraw = 4096;   // tagged records of the raw q heads (g KiB), k and v (1 KiB each);
 constexpr int kAttKraw = kAttQraw + kMaxG * 1024;  // consumed before the merge area is written
 constexpr int kAttVraw = kAttKraw + 1024;
@@ -80,12 +83,14 @@ constexpr int kActRed = kActD + 8192;       // [2][8] fp32 per-wave partial redu
 static_assert(kActRed + 64 <= kActBytes, "multi-row staging overflows the activation area");
 static_assert(kActMerge + 7 * kMaxG * 130 * 4 <= kAttS, "attention merge area overlaps the scores");
 static_assert(kAttVraw + 1024 <= kAttS, "attention staging overlaps the scores");
+static_assert(kAttRope + 512 <= kAttQraw, "attention gains overlap the raw q staging");
 static_assert(kAttP + 7 * kMaxG * 20 * 4 <= kActBytes, "attention exponentials overflow the staging area");
 static_assert(kLdsBytes == 163840, "LDS budget");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 }  // namespace dev
 
-hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream);
-hipError_t worker_occupancy(int* blocks_per_cu);
+// spec: the plan's op family (0 single-token bodies, 1 multi-row bodies), one kernel instance each
+hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec);
+hipError_t worker_occupancy(int* blocks_per_cu, int spec);
 
 }  // namespace mk

@@ -21,7 +21,8 @@ enum Opcode : uint32_t {
   OP_NORM = 7,    // one row: (add +) RMSNorm (+ FP8 quantisation) into the projection input layout
   OP_GEMM = 8,    // one (64-row tile, K chunk) of a projection: MFMA partial sums
   OP_FIN = 9,     // one row tile: add the K chunks in order, then the projection's epilogue
-  OP_QUANT = 10   // one row of o or m: per-token FP8 quantisation into the projection input layout
+  OP_QUANT = 10,  // one row of o or m: per-token FP8 quantisation into the projection input layout
+  OP_COMB = 11    // one (request, kv head): combine the split-KV partials into o
 };
 enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3 };
 constexpr int kM16Rows = 64;  // weight rows of a multi-row projection tile (gate/up: 32 + 32)
@@ -44,7 +45,8 @@ enum Word : int {
   W_P5 = 25,      // token end (exclusive)
   W_ARR_ID = 26,  // arrival group
   W_ARR_N = 27,   // arrival group size (0: no arrival group)
-  W_ARR_RANK = 28 // rank of this task in its group
+  W_ARR_RANK = 28, // rank of this task in its group
+  W_NSPLIT = 29   // multi-row attention: splits of the (request, kv head)
 };
 
 // operand pointer table: 16 slots per op row

@@ -277,43 +277,59 @@ DEV uint32_t ring_off(uint32_t lease, uint32_t off) {
 // prefetch descriptors: what an instruction streams into its LDS lease, in 1 KiB blocks
 // An instruction's lease holds up to five spans, each starting on a 1 KiB block:
 //   QKV, LM_HEAD: weight rows | norm gain       GATE_UP: gate rows | up rows | norm gain
-//   O_PROJ, DOWN: weight rows                   ATTN: K rows | V rows | q gain | k gain | RoPE row
+//   O_PROJ, DOWN: weight rows                   ATTN: K rows | V rows
 //   multi-row GEMM: 64 weight rows x one K chunk in matrix-core operand order   NORM: norm gain
 // Attention K / V spans are gathered token by token through the block table.
 constexpr int kMaxSpans = 5;
 enum PfMode : uint32_t { PF_SPANS = 0, PF_ATTN = 1, PF_W_BF16 = 2, PF_W_FP8 = 3 };
-struct Pf {
+// weight fragments (multi-row family only): tile row tr < split is weight row base0 + tr, else
+// base1 + tr; rowb bytes per weight row; k0b byte offset of the K chunk in a row.  The single-token
+// family carries none of it, which keeps its descriptor small enough to stay in registers.
+template <int S>
+struct PfFrag {};
+template <>
+struct PfFrag<1> {
+  uint32_t rowb, k0b, base0, base1, split;
+};
+// Every span is a whole number of 1 KiB blocks (the launcher checks the shapes for it), so a
+// block's 64 lanes always load 1 KiB of the span; no per-span length is kept (selecting one by span
+// index would put the descriptor in private memory).
+template <int S>
+struct Pf : PfFrag<S> {
   const char* src[kMaxSpans];
-  uint32_t len[kMaxSpans];
   uint32_t blk[kMaxSpans + 1];  // first block of each span; blk[n] = total blocks
   int n;
+  uint32_t total;  // blocks of all spans (kept apart from blk so that no access indexes blk by n)
   uint32_t mode;
   const int32_t* bt;  // attention: block-table row of the request
   int t0, nk, hk;
-  // weight fragments: tile row tr < split is weight row base0 + tr, else base1 + tr; rowb bytes per
-  // weight row; k0b byte offset of the K chunk in a row
-  uint32_t rowb, k0b, base0, base1, split;
 };
 DEV uint32_t blocks_of(uint32_t bytes) { return (bytes + 1023u) >> 10; }
 
 // span k of the descriptor (k is a compile-time constant at every call: no indexed registers)
-template <int K>
-DEV void pf_set(Pf& pf, const void* src, uint32_t bytes) {
+template <int K, int S>
+DEV void pf_set(Pf<S>& pf, const void* src, uint32_t bytes) {
   pf.src[K] = (const char*)src;
-  pf.len[K] = bytes;
   pf.blk[K + 1] = pf.blk[K] + blocks_of(bytes);
   pf.n = K + 1;
+  pf.total = pf.blk[K + 1];
 }
 
-DEV void pf_desc(const KArgs& a, const Instr& in, Pf& pf) {
+// splits of an attention instruction's (request, kv head).  S is the op family of the kernel
+// instance: 0 the single-token bodies, 1 the multi-row ones (the plan's spec id, fixed per plan).
+template <int S>
+DEV int attn_splits(const Instr& in) { return (int)in.w[S == 1 ? W_NSPLIT : W_ARR_N]; }
+
+template <int S>
+DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
   const uint32_t op = in.w[W_OPCODE];
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const Shapes& sh = a.sh;
   pf.blk[0] = 0;
-  pf.blk[1] = 0;
   pf.n = 0;
+  pf.total = 0;
   pf.mode = op == OP_ATTN ? PF_ATTN : PF_SPANS;
-  if (op == OP_GEMM) {
+  if constexpr (S == 1) if (op == OP_GEMM) {
     // 64 KiB: block b = 16 nb + q holds 64 bytes of each of the tile rows [16 nb, 16 nb + 16) (K
     // step q: 32 bf16 or 64 e4m3 weights), lane l taking row 16 nb + l % 16, bytes 16 (l / 16) ...
     const uint32_t kind = in.w[W_LAYER + 1], n0 = in.w[W_LAYER + 3], k0 = in.w[W_LAYER + 5];
@@ -328,26 +344,25 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf& pf) {
     pf_set<0>(pf, (const void*)s_ld64(row + GM_W), 65536u);
     return;
   }
-  if (op == OP_NORM) {
+  if (S == 1 && op == OP_NORM) {
     pf_set<0>(pf, (const void*)s_ld64(row + NM_GAIN), 2u * (uint32_t)sh.H);
     return;
   }
-  if (op == OP_FIN || op == OP_QUANT) return;  // nothing to prefetch: inputs are produced in the run
+  if (S == 1 && (op == OP_FIN || op == OP_QUANT)) return;  // nothing to prefetch: inputs are produced in the run
   if (pf.mode == PF_ATTN) {
     const int r = in.w[W_P1], hk = in.w[W_P2], s = in.w[W_P3];
     const int t0 = in.w[W_P4], t1 = in.w[W_P5];
-    const bool last = s == (int)in.w[W_ARR_N] - 1;
+    const bool last = s == attn_splits<S>(in) - 1;
     pf.bt = (const int32_t*)s_ld64(row + ATT_BT) + (size_t)r * sh.maxp;
     pf.t0 = t0;
     pf.hk = hk;
     pf.nk = (last ? t1 - 1 : t1) - t0;
     pf_set<0>(pf, (const void*)s_ld64(row + ATT_KC), (uint32_t)pf.nk * 256u);
     pf_set<1>(pf, (const void*)s_ld64(row + ATT_VC), (uint32_t)pf.nk * 256u);
-    pf_set<2>(pf, (const void*)s_ld64(row + ATT_GQ), 256u);
-    pf_set<3>(pf, (const void*)s_ld64(row + ATT_GK), 256u);
-    pf_set<4>(pf, (const float*)s_ld64(row + ATT_ROPE) + (size_t)r * 128, 512u);
+    (void)r;
     return;
   }
+  if (S == 1 && op == OP_COMB) return;
   const char* w = (const char*)s_ld64(row + 0);
   const uint32_t n0 = in.w[W_P1], nr = in.w[W_P2], K = in.w[W_P4];
   const uint32_t rowb = K * 2u;
@@ -361,32 +376,32 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf& pf) {
 }
 
 // issue this wave's share (blocks b = cw mod 7) of an instruction's prefetch into its lease
-DEV void pf_issue(const KArgs& a, const Pf& pf, uint32_t lease, int cw, uint32_t& issued, char* smem) {
+template <int S>
+DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint32_t& issued, char* smem) {
   const uint32_t ln = lane();
-  const uint32_t nblk = pf.blk[0] + 0u;
-  uint32_t total = pf.blk[1];
-#pragma unroll
-  for (int q = 2; q <= kMaxSpans; ++q)
-    if (q <= pf.n) total = pf.blk[q];
-  (void)nblk;
-  for (uint32_t b = cw; b < total; b += kNCW) {
+  for (uint32_t b = cw; b < pf.total; b += kNCW) {
     int k = 0;
     const char* base = pf.src[0];
-    uint32_t b0 = 0, len = pf.len[0];
+    uint32_t b0 = 0;
 #pragma unroll
     for (int q = 1; q < kMaxSpans; ++q)
       if (q < pf.n && b >= pf.blk[q]) {
         k = q;
         base = pf.src[q];
         b0 = pf.blk[q];
-        len = pf.len[q];
       }
     const uint32_t bb = b - b0;
     const char* src;
-    if (pf.mode >= PF_W_BF16) {
-      const uint32_t tr = (b >> 4) * 16u + (ln & 15u), q = b & 15u;
-      const uint32_t grow = tr < pf.split ? pf.base0 + tr : pf.base1 + tr;
-      src = base + (size_t)grow * pf.rowb + pf.k0b + q * 64u + (ln >> 4) * 16u;
+    bool frag = false;
+    if constexpr (S == 1) {
+      if (pf.mode >= PF_W_BF16) {
+        const uint32_t tr = (b >> 4) * 16u + (ln & 15u), q = b & 15u;
+        const uint32_t grow = tr < pf.split ? pf.base0 + tr : pf.base1 + tr;
+        src = base + (size_t)grow * pf.rowb + pf.k0b + q * 64u + (ln >> 4) * 16u;
+        frag = true;
+      }
+    }
+    if (frag) {
     } else if (pf.mode == PF_ATTN && k < 2) {
       uint32_t u = bb * 4u + (ln >> 4);
       if (u >= (uint32_t)pf.nk) u = 4u * bb;  // beyond the tile: reload the block's first row
@@ -396,9 +411,7 @@ DEV void pf_issue(const KArgs& a, const Pf& pf, uint32_t lease, int cw, uint32_t
       const size_t rowi = ((size_t)page * a.sh.P + (tt % a.sh.P)) * a.sh.Hkv + pf.hk;
       src = base + rowi * 256u + (ln & 15u) * 16u;
     } else {
-      uint32_t off = bb * 1024u + ln * 16u;
-      if (off >= len) off = bb * 1024u;
-      src = base + off;
+      src = base + bb * 1024u + ln * 16u;
     }
     lds_dma16(src, (uint32_t)(uintptr_t)(lds_void*)(smem + kRingOff + ring_off(lease, b * 1024u)));
     ++issued;
@@ -406,12 +419,9 @@ DEV void pf_issue(const KArgs& a, const Pf& pf, uint32_t lease, int cw, uint32_t
 }
 
 // total blocks of a descriptor
-DEV uint32_t pf_blocks(const Pf& pf) {
-  uint32_t total = pf.blk[1];
-#pragma unroll
-  for (int q = 2; q <= kMaxSpans; ++q)
-    if (q <= pf.n) total = pf.blk[q];
-  return total;
+template <int S>
+DEV uint32_t pf_blocks(const Pf<S>& pf) {
+  return pf.total;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -642,11 +652,21 @@ DEV bool down_prologue(const KArgs& a, const Instr& in, const uint64_t* row, cha
   return ll_stage(a, in, rg, 2, act, verify, polls, ss);
 }
 
-// attention: the tagged raw (fp32) q heads of the group and its k / v heads
+// at most 1 KiB (a multiple of 16 bytes) into LDS at dst: only the lanes that carry data write
+DEV void stage_small(const void* src, uint32_t bytes, char* dst) {
+  const uint32_t ln = lane();
+  if (ln * 16u < bytes) lds_dma16_sc1((const char*)src + ln * 16u, (uint32_t)(uintptr_t)(lds_void*)dst);
+}
+
+// attention: the q / k norm gains and the request's RoPE row, then the tagged raw (fp32) q heads of
+// the group and its k / v heads (one round trip: the record staging waits for all of it)
 DEV bool attn_stage(const KArgs& a, const Instr& in, char* act, bool verify, uint32_t& polls, StageStamps& ss) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int r = in.w[W_P1], hk = in.w[W_P2];
+  stage_small((const void*)s_ld64(row + ATT_GQ), 256u, act + kAttGq);
+  stage_small((const void*)s_ld64(row + ATT_GK), 256u, act + kAttGk);
+  stage_small((const float*)s_ld64(row + ATT_ROPE) + (size_t)r * 128, 512u, act + kAttRope);
   const char* qkv = (const char*)s_ld64(row + ATT_QKV) + (size_t)r * sh.n_qkv * 8;
   const uint32_t tag = ll_tag(a, in.w[W_LAYER]);
   const LlRegion rg[3] = {{qkv + (size_t)hk * sh.g * 128 * 8, (uint32_t)sh.g * 1024u, (uint32_t)kAttQraw, tag},
@@ -775,26 +795,24 @@ DEV void qk_norm_rope(const char* raw, const char* gn, const char* rope, float e
 //   3. P V: lanes over dimension pairs, waves over tokens (wave w takes tokens w, w + 7, ...);
 //      the seven waves' partial outputs and sums merge with weights exp(m_w - max m_w).
 // Output: the split's normalised O [G][128] and its lse [G] in the output area.
-template <int G>
+template <int G, int S>
 DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
   const Shapes& sh = a.sh;
   const int s = in.w[W_P3], t0 = in.w[W_P4], t1 = in.w[W_P5];
-  const bool last = s == (int)in.w[W_ARR_N] - 1;
+  const bool last = s == attn_splits<S>(in) - 1;
   const int ntok = t1 - t0;               // 1 .. 128
   const int nk = last ? ntok - 1 : ntok;  // tokens read from the cache; the last split adds the new one
   const uint32_t nbk = blocks_of((uint32_t)nk * 256u);
-  const uint32_t voff = nbk * 1024u, gqoff = 2u * nbk * 1024u;  // lease: K | V | q gain | k gain | RoPE
+  const uint32_t voff = nbk * 1024u;      // lease: K | V
   const char* ring = smem + kRingOff;
   const int ln = (int)lane();
   const float scale = sh.inv_sqrt_d;
   // phase 0: QK-norm + RoPE once per head: wave j < G takes q head j, wave G the new key, wave
   // G + 1 the new value (bf16); the results (also the new cache row) go to LDS
   if (cw < G) {
-    qk_norm_rope(act + kAttQraw + cw * 1024, ring + ring_off(lease, gqoff), ring + ring_off(lease, gqoff + 2048u),
-                 sh.eps, act + kActQ + cw * 256);
+    qk_norm_rope(act + kAttQraw + cw * 1024, act + kAttGq, act + kAttRope, sh.eps, act + kActQ + cw * 256);
   } else if (cw == G) {
-    qk_norm_rope(act + kAttKraw, ring + ring_off(lease, gqoff + 1024u), ring + ring_off(lease, gqoff + 2048u),
-                 sh.eps, act + kActK);
+    qk_norm_rope(act + kAttKraw, act + kAttGk, act + kAttRope, sh.eps, act + kActK);
   } else if (cw == G + 1) {
     const char* vr = act + kAttVraw;  // tagged records
     ((uint32_t*)(act + kActV))[ln] = pack_bf2(ll_f32(vr, 2 * ln), ll_f32(vr, 2 * ln + 1));
@@ -895,11 +913,12 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
   }
 }
 
+template <int S>
 DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
   switch (a.sh.g) {
-    case 1: attn_body<1>(a, in, smem, act, lease, cw); break;
-    case 2: attn_body<2>(a, in, smem, act, lease, cw); break;
-    default: attn_body<4>(a, in, smem, act, lease, cw); break;  // GQA groups 1, 2 and 4 are built
+    case 1: attn_body<1, S>(a, in, smem, act, lease, cw); break;
+    case 2: attn_body<2, S>(a, in, smem, act, lease, cw); break;
+    default: attn_body<4, S>(a, in, smem, act, lease, cw); break;  // GQA groups 1, 2 and 4 are built
   }
 }
 
@@ -1269,6 +1288,57 @@ DEV void quant_row(const KArgs& a, const Instr& in, char* smem, int wv) {
   wait_vm0();
 }
 
+// Combine of one (request, kv head) on the eight waves: thread t takes output element t of the
+// group's g heads x 128 dims, o = sum_s exp(lse_s - L) O_s with L = log sum_s exp(lse_s), over the
+// splits in order, 32 at a time with a running maximum (online rescaling)
+DEV void comb_group(const KArgs& a, const Instr& in, int wv) {
+  const Shapes& sh = a.sh;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t r = in.w[W_LAYER + 1], hk = in.w[W_LAYER + 2], ns = in.w[W_LAYER + 3];
+  const uint32_t g = (uint32_t)sh.g, t = (uint32_t)wv * 64u + lane();
+  const uint32_t pstride = g * 128u + 8u;
+  const uint32_t gbase = ((r * (uint32_t)sh.Hkv + hk) * (uint32_t)sh.max_splits) * pstride;
+  __amdgpu_buffer_rsrc_t rp = rsrc((const float*)s_ld64(row + ATT_PART) + gbase);
+  const uint32_t tt = min(t, g * 128u - 1u), j = tt >> 7;
+  float M = -INFINITY, S = 0.f, acc = 0.f;
+  for (uint32_t s0 = 0; s0 < ns; s0 += 32u) {
+    float lv[32], ov[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t sp = min(s0 + (uint32_t)i, ns - 1u);
+      lv[i] = __uint_as_float(ld32(rp, (sp * pstride + g * 128u + j) * 4u));
+      ov[i] = __uint_as_float(ld32(rp, (sp * pstride + tt) * 4u));
+    }
+    wait_vm0();
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (s0 + (uint32_t)i < ns) mc = fmaxf(mc, lv[i]);
+    const float sc = M == -INFINITY ? 0.f : __expf(M - mc);
+    S *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (s0 + (uint32_t)i < ns) {
+        const float e = __expf(lv[i] - mc);
+        S += e;
+        acc += e * ov[i];
+      }
+    }
+    M = mc;
+  }
+  if (t < g * 128u) {
+    const uint32_t k = hk * g * 128u + t;
+    __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + ATT_O));
+    const float v = acc / S;
+    if (sh.fp8)
+      st32(ro, (r * (uint32_t)sh.Hq * 128u + k) * 4u, __float_as_uint(v));
+    else
+      st16(ro, opnd_bf16(r, k), bf16_bits(v));
+  }
+  wait_vm0();
+}
+
 // the multi-row op body of one instruction on one of the eight waves (ATTN aside)
 DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const uint32_t op = in.w[W_OPCODE];
@@ -1286,6 +1356,8 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
     else fin_tile<kMaxChunks>(a, in, wv);
   } else if (op == OP_QUANT) {
     quant_row(a, in, smem, wv);
+  } else if (op == OP_COMB) {
+    comb_group(a, in, wv);
   }
 }
 
@@ -1325,10 +1397,11 @@ struct Stamps {
 // four consecutive attention-output elements k .. k + 3 of row r: M = 1 plans as tagged records of
 // bf16 pairs; multi-row plans in the O projection's operand order (bf16), or as fp32 rows for the
 // per-token quantisation (W8A8)
+template <int S>
 DEV void o_store(const KArgs& a, const Instr& in, __amdgpu_buffer_rsrc_t ro, uint32_t r, uint32_t k, f32x4 v,
                  uint32_t tag) {
   const uint32_t w = (uint32_t)a.sh.Hq * 128u;
-  if (in.w[W_SPEC] == 0)
+  if (S == 0)
     ll_put2(ro, (r * w + k) / 2u, pack_bf2(v.x, v.y), pack_bf2(v.z, v.w), tag);
   else if (!a.sh.fp8)
     st64(ro, opnd_bf16(r, k), u32x2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)});
@@ -1336,13 +1409,16 @@ DEV void o_store(const KArgs& a, const Instr& in, __amdgpu_buffer_rsrc_t ro, uin
     st128(ro, (r * w + k) * 4u, u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
 }
 
-// true for the worker that completed the group and combined it
+// Store the split's partial (and, for the split holding the new token, the cache rows).  M = 1
+// plans: record arrival; the split completing its group combines it (true for that worker).
+// Multi-row plans: signal the group's event; a combine task reduces it.
+template <int S>
 DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) {
   const Shapes& sh = a.sh;
   const int g = sh.g;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int r = in.w[W_P1], hk = in.w[W_P2], s = in.w[W_P3];
-  const int ns = in.w[W_ARR_N];
+  const int ns = attn_splits<S>(in);
   const uint32_t pstride = (uint32_t)g * 128u + 8u;  // floats per split: g*128 O, g lse, padding
   const uint32_t gbase = ((uint32_t)(r * sh.Hkv + hk) * (uint32_t)sh.max_splits) * pstride;
   float* part = (float*)s_ld64(row + ATT_PART);
@@ -1362,6 +1438,10 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
   }
   wait_vm0();
   if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
+  if (S == 1) {
+    signal_all(a, in);
+    return false;
+  }
   const bool last = arrive(a, in);
   if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
   if (!last) return false;
@@ -1383,8 +1463,8 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
       const float lv = ln < ns ? pl[ln * pstride + g * 128 + j] : -INFINITY;
       const float M = wave_max(lv);
       const float e = ln < ns ? __expf(lv - M) : 0.f;
-      const float S = wave_sum(e);
-      if (ln < ns) wts[ln * kMaxG + j] = e / S;
+      const float sum = wave_sum(e);
+      if (ln < ns) wts[ln * kMaxG + j] = e / sum;
     }
     for (int u = 0; u * 256 < g * 128; ++u) {
       const int oi = u * 256 + 4 * ln;
@@ -1393,7 +1473,7 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
         for (int t = 0; t < ns; ++t) acc += wts[t * kMaxG + j] * *(const f32x4*)(pl + t * pstride + oi);
-        o_store(a, in, ro, (uint32_t)r, kbase + (uint32_t)oi, acc, otag);
+        o_store<S>(a, in, ro, (uint32_t)r, kbase + (uint32_t)oi, acc, otag);
       }
     }
     if (a.flags & MK_FLAG_TRACE) st.c2 = rtc();
@@ -1463,7 +1543,7 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
       const int j = unit >> 5, c4 = unit & 31;
       const float inv = 1.f / hst[j * 3 + 1];
       const f32x4 v = {acc[u][0] * inv, acc[u][1] * inv, acc[u][2] * inv, acc[u][3] * inv};
-      o_store(a, in, ro, (uint32_t)r, kbase + (uint32_t)(j * 128 + c4 * 4), v, otag);
+      o_store<S>(a, in, ro, (uint32_t)r, kbase + (uint32_t)(j * 128 + c4 * 4), v, otag);
     }
   }
   return true;
@@ -1592,6 +1672,7 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
 // skipped, no wave takes any)
 DEV int inner_barriers(uint32_t op, bool noop_only) { return op == OP_ATTN && !noop_only ? 3 : 0; }
 
+template <int S>
 DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride, char* smem) {
   uint32_t* ctrl = (uint32_t*)(smem + kCtrlOff);  // LDS; read and written only across barriers
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
@@ -1605,7 +1686,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     fetch(base + (size_t)i * stride, in);
     const uint32_t op = in.w[W_OPCODE];
     if (op == OP_NOOP) continue;
-    const bool m16 = in.w[W_SPEC] == 1;
+    constexpr bool m16 = S == 1;
     const bool tracing = a.flags & MK_FLAG_TRACE;
     const unsigned long long t_vis = tracing ? rtc() : 0;
     const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
@@ -1616,7 +1697,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     uint32_t poll = 0;
     bool ok = true;
     StageStamps sst{0, 0};
-    if (m16) {
+    if constexpr (m16) {
       // multi-row: wait for the event counters (the graph baseline's stream order guarantees them),
       // then stage what the op reads from LDS
       ok = graph || wait_events(a, in, poll, wc);
@@ -1642,7 +1723,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     if (!ok) break;
     if (op != OP_ATTN && !noop_only) {  // the controller is the eighth wave of a projection tile
       const uint32_t lease = uni(((const uint32_t*)(smem + kCtrlOff + kLeaseTabOff))[i & 15]);  // compute wave 0's table
-      if (m16)
+      if constexpr (m16)
         m16_body(a, in, smem, lease, kNW - 1);
       else
         proj_body(a, in, smem, lease, fused_norm, kNW - 1);
@@ -1653,15 +1734,15 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     const unsigned long long t_b = tracing ? rtc() : 0;
     const unsigned long long c_b = tracing ? __builtin_readcyclecounter() : 0;
     if (op == OP_ATTN) {
-      if (attn_epilogue(a, in, smem, st) && m16) {  // the combining worker signals the group's event
+      if (attn_epilogue<S>(a, in, smem, st) && m16) {  // the combining worker signals the group's event
         wait_vm0();
         signal_all(a, in);
       }
-    } else if (m16) {
+    } else if constexpr (m16) {
       if (op == OP_GEMM)
         gemm_epilogue(a, in, smem);
       else
-        signal_all(a, in);  // norm / finalize / quantise: every wave's stores completed before B
+        signal_all(a, in);  // norm / finalize / quantise / combine: every wave's stores completed before B
     } else {
       gemv_epilogue(a, in, smem, lm, st);
     }
@@ -1685,6 +1766,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
   }
 }
 
+template <int S>
 DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, int cw, char* smem) {
   const uint32_t* ctrl = (const uint32_t*)(smem + kCtrlOff);  // LDS abort flag
   uint32_t* lease_tab = (uint32_t*)(smem + kCtrlOff + kLeaseTabOff) + cw * 32;  // [16] lease, [16] issued_end
@@ -1708,21 +1790,21 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       if (pf_i < i) pf_i = i;
       while (pf_i < count && pf_i <= i + lookahead) {
         Instr nx;
-        fetch(base + (size_t)pf_i * stride, nx);
+        fetch(base + (size_t)uni((uint32_t)pf_i) * stride, nx);  // pf_i is wave-uniform: scalar loads
         if (nx.w[W_OPCODE] == OP_NOOP) {
           lease_tab[pf_i & 15] = head;
           lease_tab[16 + (pf_i & 15)] = issued;
           ++pf_i;
           continue;
         }
-        Pf pf;
-        pf_desc(a, nx, pf);
+        Pf<S> pf;
+        pf_desc<S>(a, nx, pf);
         const uint32_t npg = (pf_blocks(pf) + 15u) >> 4;
         if (head + npg - freed > (uint32_t)kNPages) break;
         // bounded depth: loads in flight queue ahead of the controller's staging in this CU's
         // memory pipeline, so leases beyond kLookPages pages from instruction i's wait
         if (pf_i > i && head + npg - uni(lease_tab[i & 15]) > (uint32_t)kLookPages) break;
-        pf_issue(a, pf, head, cw, issued, smem);
+        pf_issue<S>(a, pf, head, cw, issued, smem);
         lease_tab[pf_i & 15] = head;
         lease_tab[16 + (pf_i & 15)] = issued;
         head += npg;
@@ -1736,8 +1818,8 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       const uint32_t lease = uni(lease_tab[i & 15]);
       char* act = smem + kActOff;
       if (op == OP_ATTN) {
-        attn_compute(a, in, smem, act, lease, cw);
-      } else if (in.w[W_SPEC] == 1) {
+        attn_compute<S>(a, in, smem, act, lease, cw);
+      } else if constexpr (S == 1) {
         m16_body(a, in, smem, lease, cw);
       } else {
         proj_body(a, in, smem, lease, fused_norm, cw);
@@ -1753,6 +1835,9 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
 
 }  // namespace dev
 
+// one kernel per op family: the single-token plans' bodies (S = 0) and the multi-row plans' (S = 1)
+// are compiled separately, so neither family's register allocation carries the other's code
+template <int S>
 __global__ void __launch_bounds__(dev::kThreads, 1) mk_worker(KArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1769,19 +1854,23 @@ __global__ void __launch_bounds__(dev::kThreads, 1) mk_worker(KArgs a) {
   }
   if (threadIdx.x == 0) *(uint32_t*)(smem + dev::kCtrlOff) = 0u;
   __syncthreads();
-  if (wave == 0) dev::controller(a, base, count, stride, smem);
-  else dev::compute(a, base, count, stride, wave - 1, smem);
+  if (wave == 0) dev::controller<S>(a, base, count, stride, smem);
+  else dev::compute<S>(a, base, count, stride, wave - 1, smem);
 }
 
-hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(mk_worker, dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec) {
+  if (spec == 1)
+    hipLaunchKernelGGL(mk_worker<1>, dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+  else
+    hipLaunchKernelGGL(mk_worker<0>, dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
-hipError_t worker_occupancy(int* blocks_per_cu) {
-  hipError_t e = hipFuncSetAttribute((const void*)mk_worker, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
+hipError_t worker_occupancy(int* blocks_per_cu, int spec) {
+  const void* f = spec == 1 ? (const void*)mk_worker<1> : (const void*)mk_worker<0>;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_worker, dev::kThreads, dev::kLdsBytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, dev::kThreads, dev::kLdsBytes);
 }
 
 }  // namespace mk

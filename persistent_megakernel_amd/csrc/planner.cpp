@@ -150,24 +150,33 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
     };
     const int row_qf = proj(K_QKV, l, n_qkv, H, rt, {ev_na, (uint32_t)M}, row_na,
                             [&](int j) { return ev_qkv[qkv_group(j)]; });
+    // split-KV partials signal their (request, kv head) event; one combine task per group, dealt
+    // round-robin like every task (not left to whichever split arrives last)
     const int row_attn = b.op_row(OP_ATTN, l, {row_qf});
-    const int ev_oready = b.event((uint32_t)(R * Hkv));
+    std::vector<int> nsplit(R), ev_att((size_t)R * Hkv);
+    for (int r = 0; r < R; ++r) nsplit[r] = (ctx[r] + st - 1) / st;
+    for (int r = 0; r < R; ++r)
+      for (int hk = 0; hk < Hkv; ++hk) ev_att[(size_t)r * Hkv + hk] = b.event((uint32_t)nsplit[r]);
     for (int r = 0; r < R; ++r) {
-      const int cx = ctx[r], ns = (cx + st - 1) / st;
+      const int cx = ctx[r], ns = nsplit[r];
       max_splits = std::max(max_splits, ns);
-      for (int hk = 0; hk < Hkv; ++hk) {
-        const int grp = b.n_arrivals++;
+      for (int hk = 0; hk < Hkv; ++hk)
         for (int s = 0; s < ns; ++s) {
           const int t0 = s * st, t1 = std::min(cx, (s + 1) * st);
-          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {{ev_oready, 1u}},
-                 {l, r, hk, s, t0, t1, grp, ns, s});
+          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {{ev_att[(size_t)r * Hkv + hk], 1u}},
+                 {l, r, hk, s, t0, t1, 0, 0, 0, ns});
         }
-      }
     }
+    const int row_comb = b.op_row(OP_COMB, l, {row_attn});
+    const int ev_oready = b.event((uint32_t)(R * Hkv));
+    for (int r = 0; r < R; ++r)
+      for (int hk = 0; hk < Hkv; ++hk)
+        b.task(OP_COMB, row_comb, spec, {{ev_att[(size_t)r * Hkv + hk], (uint32_t)nsplit[r]}}, {{ev_oready, 1u}},
+               {l, r, hk, nsplit[r]});
     std::pair<int, uint32_t> o_wait{ev_oready, (uint32_t)(R * Hkv)};
-    int o_dep = row_attn;
+    int o_dep = row_comb;
     if (fp8) {
-      const int row_qo = b.op_row(OP_QUANT, l, {row_attn}, 0);
+      const int row_qo = b.op_row(OP_QUANT, l, {row_comb}, 0);
       const int ev_oq = b.event((uint32_t)M);
       for (int m = 0; m < M; ++m) b.task(OP_QUANT, row_qo, spec, {o_wait}, {{ev_oq, 1u}}, {l, 0, m});
       o_wait = {ev_oq, (uint32_t)M};

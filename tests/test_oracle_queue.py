@@ -108,7 +108,8 @@ def test_multi_row_tiles_cover_each_projection_once(name):
     kc = p["kc"]
     assert kc * (1 if cfg.weight_fp8 else 2) * oq.M16_ROWS == 64 * 1024
     ops = [int(t[0]) for t in _tasks(plan)]
-    assert set(ops) <= {oq.OP_NORM, oq.OP_GEMM, oq.OP_FIN, oq.OP_QUANT, oq.OP_ATTN}
+    assert set(ops) <= {oq.OP_NORM, oq.OP_GEMM, oq.OP_FIN, oq.OP_QUANT, oq.OP_ATTN, oq.OP_COMB}
+    assert ops.count(oq.OP_COMB) == cfg.n_requests * cfg.n_kv_heads
     for kind, (N, K) in shapes.items():
         grid = np.zeros((N, K // kc), dtype=np.int64)
         fin = np.zeros(N, dtype=np.int64)
