@@ -36,6 +36,10 @@ OP_NOOP, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = 0, 1, 2, 3, 
 # tasks, per-row FP8 quantisation of the O and down inputs
 OP_NORM, OP_GEMM, OP_FIN, OP_QUANT = 7, 8, 9, 10
 OP_COMB = 11  # multi-row: combine the split-KV partials of one (request, kv head)
+# indexer front
+OP_KCACHE, OP_SCORE = 12, 13  # key RoPE + per-token e4m3 + cache write; paged indexer score
+K_QA, K_W, K_KI, K_QI = 4, 5, 6, 7  # projection kinds: q_a, head weights, indexer key, indexer q
+SCORE_TOK = 128  # keys per indexer-score task
 K_QKV, K_O, K_GU, K_DOWN = 0, 1, 2, 3  # projection kinds
 NONE = 0xFFFFFFFF
 LEASE_BYTES = 65536  # largest LDS lease of one instruction
@@ -64,7 +68,18 @@ def _largest_divisor_le(n: int, cap: int) -> int:
     return 1
 
 
+def kchunk(K: int) -> int:
+    """K chunk of an e4m3 projection tile: the largest multiple of 128 that divides K and keeps
+    M16_ROWS rows within one lease (1024)."""
+    for kc in range(LEASE_BYTES // M16_ROWS, 0, -128):
+        if K % kc == 0:
+            return kc
+    raise ValueError(K)
+
+
 def tile_params(cfg, W: int, ctx_lens) -> Dict[str, int]:
+    if cfg.workload == "indexer_front":
+        return {"spec": 1, "kc": kchunk(cfg.hidden), "kc_q": kchunk(cfg.idx_q_rank), "s_tok": SCORE_TOK}
     H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
     Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
     R = cfg.n_requests
@@ -283,6 +298,88 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
         prev = (ev_down, H // rt)
 
 
+def _indexer(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
+    """Indexer front (MegaRTP page, section 4: A0 -> {B0, C0, B1}; {B0, C0} -> D1; {D1, B1} -> E1):
+      A0: one NORM row task per token (add + RMSNorm + per-token e4m3)
+      B0 / C0 / B1: e4m3 projection tiles of 64 weight rows x one K chunk, finalize per tile
+        (B0 -> q_a rows, C0 -> head weights, B1 -> key rows); B0's rows then get a NORM row task
+        each (RMSNorm of q_a + per-token e4m3); B1's finalizes feed one key-cache task (RoPE,
+        per-token e4m3, cache write)
+      D1: projection tiles of q_a; one finalize per head (its two 64-row tiles, so that RoPE pairs
+        dimensions i and i + 64)
+      E1: one score task per (request, SCORE_TOK keys)
+    Waits: B0 / C0 / B1 tiles on A0 ("tile_cover"); finalizes on their tiles' chunks
+    ("tile_reduce"); the q_a norms on B0's finalizes; D1 tiles on the q_a norms; the key-cache
+    task on B1's finalizes; E1 on D1's finalizes, C0's finalize and the key-cache task."""
+    H, qr, nh, hd = cfg.hidden, cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
+    R, T = cfg.n_requests, cfg.tokens_per_request
+    M = R * T
+    spec, rt, st = p["spec"], M16_ROWS, p["s_tok"]
+    l = 0
+
+    def tiles(kind, N, K, kc, wait, part_event):
+        row_g = b.op_row()
+        nt, nk = N // rt, K // kc
+        for j in range(nt):
+            for c in range(nk):
+                b.task(OP_GEMM, row_g, spec, [wait], [(part_event(j), 1)], [l, kind, j, j * rt, rt, c * kc, kc])
+        return nt, nk
+
+    def fin(kind, nt, nk, kc, parts, fin_event):
+        row_f = b.op_row()
+        for j in range(nt):
+            b.task(OP_FIN, row_f, spec, [(parts[j], nk)], [(fin_event, 1)], [l, kind, j, j * rt, rt, nk, kc])
+
+    row_a0 = b.op_row()
+    ev_a0 = b.event(M)
+    for m in range(M):
+        b.task(OP_NORM, row_a0, spec, [], [(ev_a0, 1)], [l, 0, m])
+    kc = p["kc"]
+    # B0: q_a, then its per-token RMSNorm + quantisation
+    nt, nk = qr // rt, H // kc
+    parts = [b.event(nk) for _ in range(nt)]
+    tiles(K_QA, qr, H, kc, (ev_a0, M), lambda j: parts[j])
+    ev_b0 = b.event(nt)
+    fin(K_QA, nt, nk, kc, parts, ev_b0)
+    row_qn = b.op_row()
+    ev_qn = b.event(M)
+    for m in range(M):
+        b.task(OP_NORM, row_qn, spec, [(ev_b0, nt)], [(ev_qn, 1)], [l, 2, m])
+    # C0: head weights
+    nt_w = nh // rt
+    parts_w = [b.event(nk) for _ in range(nt_w)]
+    tiles(K_W, nh, H, kc, (ev_a0, M), lambda j: parts_w[j])
+    ev_w = b.event(nt_w)
+    fin(K_W, nt_w, nk, kc, parts_w, ev_w)
+    # B1: indexer key, then RoPE + quantisation + cache write
+    nt_k = hd // rt
+    parts_k = [b.event(nk) for _ in range(nt_k)]
+    tiles(K_KI, hd, H, kc, (ev_a0, M), lambda j: parts_k[j])
+    ev_k = b.event(nt_k)
+    fin(K_KI, nt_k, nk, kc, parts_k, ev_k)
+    row_kc = b.op_row()
+    ev_kc = b.event(1)
+    b.task(OP_KCACHE, row_kc, spec, [(ev_k, nt_k)], [(ev_kc, 1)], [l])
+    # D1: indexer q per head (two tiles each)
+    kcq = p["kc_q"]
+    nk_q = qr // kcq
+    per_head = hd // rt
+    ev_head = [b.event(per_head * nk_q) for _ in range(nh)]
+    tiles(K_QI, nh * hd, qr, kcq, (ev_qn, M), lambda j: ev_head[j // per_head])
+    row_f = b.op_row()
+    ev_qi = b.event(nh)
+    for h in range(nh):
+        b.task(OP_FIN, row_f, spec, [(ev_head[h], per_head * nk_q)], [(ev_qi, 1)],
+               [l, K_QI, h, h * hd, hd, nk_q, kcq])
+    # E1: scores
+    row_e = b.op_row()
+    for r in range(R):
+        ctx = int(ctx_lens[r])
+        for s in range(-(-ctx // st)):
+            b.task(OP_SCORE, row_e, spec, [(ev_qi, nh), (ev_w, nt_w), (ev_kc, 1)], [],
+                   [l, r, s, s * st, min(ctx, (s + 1) * st)])
+
+
 def build_queue(cfg, W: int, ctx_lens=None) -> Dict[str, np.ndarray]:
     """Returns {'queue': uint32 [W, L, 32], 'thresholds': uint32 [E], 'n_tasks', 'n_ops',
     'n_arrivals', 'params'}."""
@@ -290,7 +387,9 @@ def build_queue(cfg, W: int, ctx_lens=None) -> Dict[str, np.ndarray]:
         ctx_lens = [cfg.context] * cfg.n_requests
     b = _Builder()
     p = tile_params(cfg, W, ctx_lens)
-    if cfg.workload in ("qwen3_layer", "qwen3_step") and p["spec"] == 1:
+    if cfg.workload == "indexer_front":
+        _indexer(cfg, W, ctx_lens, b, p)
+    elif cfg.workload in ("qwen3_layer", "qwen3_step") and p["spec"] == 1:
         if cfg.workload == "qwen3_step":
             raise NotImplementedError("multi-row decode step")
         _qwen3_m16(cfg, W, ctx_lens, b, p)

@@ -22,9 +22,13 @@ enum Opcode : uint32_t {
   OP_GEMM = 8,    // one (64-row tile, K chunk) of a projection: MFMA partial sums
   OP_FIN = 9,     // one row tile: add the K chunks in order, then the projection's epilogue
   OP_QUANT = 10,  // one row of o or m: per-token FP8 quantisation into the projection input layout
-  OP_COMB = 11    // one (request, kv head): combine the split-KV partials into o
+  OP_COMB = 11,   // one (request, kv head): combine the split-KV partials into o
+  // indexer front
+  OP_KCACHE = 12, // the new tokens' keys: RoPE, per-token e4m3, key-cache write
+  OP_SCORE = 13   // one (request, key split): paged indexer score
 };
-enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3 };
+enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_QA = 4, K_W = 5, K_KI = 6, K_QI = 7 };
+constexpr int kScoreTok = 128;  // keys per indexer-score task
 constexpr int kM16Rows = 64;  // weight rows of a multi-row projection tile (gate/up: 32 + 32)
 constexpr int kMaxChunks = 24;  // K chunks a multi-row finalize task adds
 
@@ -72,10 +76,16 @@ enum GemmSlot { GM_W = 0, GM_ACT, GM_PART, GM_SW };
 enum FinSlot { FN_PART = 0, FN_SA, FN_OUT, FN_R1, FN_OUT2 };
 // QUANT: fp32 rows in, e4m3 operand-order rows out, per-token scales out
 enum QuantSlot { QT_IN = 0, QT_OUT, QT_S };
+// KCACHE: key rows (fp32 [M][d]), RoPE table, key cache codes, key scales, block table
+enum KcSlot { KC_K = 0, KC_ROPE, KC_CACHE, KC_SCALE, KC_BT };
+// SCORE: q (bf16, score operand order), head weights (fp32 [M][heads]), key cache, key scales,
+// block table, scores out (fp32 [M][max context])
+enum ScSlot { SC_Q = 0, SC_W, SC_CACHE, SC_SCALE, SC_BT, SC_OUT };
 
 struct TileParams {
   int r_qkv = 0, r_o = 0, r_gu = 0, r_down = 0, r_lm = 0, s_tok = 0, spec = 0;
   int kc = 0;  // multi-row plans: K chunk of a projection tile (kM16Rows x kc weights fill a lease)
+  int kc_q = 0;  // indexer front: K chunk of the q projection (K = q rank)
 };
 
 struct OpInfo {      // one row of the operand table = one op instance

@@ -79,7 +79,26 @@ struct Builder {
   }
 };
 
+// K chunk of an e4m3 projection tile: the largest multiple of 128 dividing K with kM16Rows rows
+// within one lease
+int kchunk(int K) {
+  for (int kc = kLeaseBytes / kM16Rows; kc > 0; kc -= 128)
+    if (K % kc == 0) return kc;
+  return 0;
+}
+
 bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, std::string& err) {
+  if (c.workload == MK_INDEXER_FRONT) {
+    p.spec = 1;
+    p.kc = kchunk(c.hidden);
+    p.kc_q = kchunk(c.idx_q_rank);
+    p.s_tok = kScoreTok;
+    if (!p.kc || !p.kc_q) {
+      err = "indexer projections need K a multiple of 128";
+      return false;
+    }
+    return true;
+  }
   const int H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int R = c.n_requests;
   const int elem = c.weight_fp8 ? 1 : 2;
@@ -206,9 +225,189 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
   }
 }
 
+// Indexer front (MegaRTP page, section 4: A0 -> {B0, C0, B1}; {B0, C0} -> D1; {D1, B1} -> E1):
+// row norms, e4m3 projection tiles with per-tile finalizes (per head for D1, so that RoPE pairs
+// dimensions i and i + 64), the q_a norm rows, one key-cache task, per-(request, key split) score
+// tasks.  The same rules as the oracle's builder.
+void build_indexer(const mk_config& c, const int32_t* ctx, const TileParams& p, Builder& b) {
+  const int H = c.hidden, qr = c.idx_q_rank, nh = c.idx_heads, hd = c.idx_head_dim;
+  const int R = c.n_requests, M = R * c.tokens_per_request;
+  const int spec = p.spec, rt = kM16Rows, st = p.s_tok, l = 0;
+  auto tiles = [&](uint32_t kind, int N, int K, int kc, std::pair<int, uint32_t> wait, int dep, auto part_event) {
+    const int row_g = b.op_row(OP_GEMM, l, {dep}, kind);
+    for (int j = 0; j < N / rt; ++j)
+      for (int ck = 0; ck < K / kc; ++ck)
+        b.task(OP_GEMM, row_g, spec, {wait}, {{part_event(j), 1u}}, {l, kind, j, j * rt, rt, ck * kc, kc});
+    return row_g;
+  };
+  auto fin = [&](uint32_t kind, int nt, int nk, int kc, const std::vector<int>& parts, int fin_event, int dep) {
+    const int row_f = b.op_row(OP_FIN, l, {dep}, kind);
+    for (int j = 0; j < nt; ++j)
+      b.task(OP_FIN, row_f, spec, {{parts[j], (uint32_t)nk}}, {{fin_event, 1u}}, {l, kind, j, j * rt, rt, nk, kc});
+    return row_f;
+  };
+  const int row_a0 = b.op_row(OP_NORM, l, {}, 0);
+  const int ev_a0 = b.event((uint32_t)M);
+  for (int m = 0; m < M; ++m) b.task(OP_NORM, row_a0, spec, {}, {{ev_a0, 1u}}, {l, 0, m});
+  const int kc = p.kc, nk = H / kc;
+  // B0
+  const int nt = qr / rt;
+  std::vector<int> parts(nt);
+  for (int j = 0; j < nt; ++j) parts[j] = b.event((uint32_t)nk);
+  const int row_b0 = tiles(K_QA, qr, H, kc, {ev_a0, (uint32_t)M}, row_a0, [&](int j) { return parts[j]; });
+  const int ev_b0 = b.event((uint32_t)nt);
+  const int row_b0f = fin(K_QA, nt, nk, kc, parts, ev_b0, row_b0);
+  const int row_qn = b.op_row(OP_NORM, l, {row_b0f}, 2);
+  const int ev_qn = b.event((uint32_t)M);
+  for (int m = 0; m < M; ++m) b.task(OP_NORM, row_qn, spec, {{ev_b0, (uint32_t)nt}}, {{ev_qn, 1u}}, {l, 2, m});
+  // C0
+  const int nt_w = nh / rt;
+  std::vector<int> parts_w(nt_w);
+  for (int j = 0; j < nt_w; ++j) parts_w[j] = b.event((uint32_t)nk);
+  const int row_c0 = tiles(K_W, nh, H, kc, {ev_a0, (uint32_t)M}, row_a0, [&](int j) { return parts_w[j]; });
+  const int ev_w = b.event((uint32_t)nt_w);
+  const int row_c0f = fin(K_W, nt_w, nk, kc, parts_w, ev_w, row_c0);
+  // B1
+  const int nt_k = hd / rt;
+  std::vector<int> parts_k(nt_k);
+  for (int j = 0; j < nt_k; ++j) parts_k[j] = b.event((uint32_t)nk);
+  const int row_b1 = tiles(K_KI, hd, H, kc, {ev_a0, (uint32_t)M}, row_a0, [&](int j) { return parts_k[j]; });
+  const int ev_k = b.event((uint32_t)nt_k);
+  const int row_b1f = fin(K_KI, nt_k, nk, kc, parts_k, ev_k, row_b1);
+  const int row_kc = b.op_row(OP_KCACHE, l, {row_b1f});
+  const int ev_kc = b.event(1u);
+  b.task(OP_KCACHE, row_kc, spec, {{ev_k, (uint32_t)nt_k}}, {{ev_kc, 1u}}, {l});
+  // D1
+  const int kcq = p.kc_q, nk_q = qr / kcq, per_head = hd / rt;
+  std::vector<int> ev_head(nh);
+  for (int h = 0; h < nh; ++h) ev_head[h] = b.event((uint32_t)(per_head * nk_q));
+  const int row_d1 = tiles(K_QI, nh * hd, qr, kcq, {ev_qn, (uint32_t)M}, row_qn,
+                           [&](int j) { return ev_head[j / per_head]; });
+  const int row_d1f = b.op_row(OP_FIN, l, {row_d1}, K_QI);
+  const int ev_qi = b.event((uint32_t)nh);
+  for (int h = 0; h < nh; ++h)
+    b.task(OP_FIN, row_d1f, spec, {{ev_head[h], (uint32_t)(per_head * nk_q)}}, {{ev_qi, 1u}},
+           {l, K_QI, h, h * hd, hd, nk_q, kcq});
+  // E1
+  const int row_e = b.op_row(OP_SCORE, l, {row_d1f, row_c0f, row_kc});
+  for (int r = 0; r < R; ++r)
+    for (int s2 = 0; s2 < (ctx[r] + st - 1) / st; ++s2)
+      b.task(OP_SCORE, row_e, spec, {{ev_qi, (uint32_t)nh}, {ev_w, (uint32_t)nt_w}, {ev_kc, 1u}}, {},
+             {l, r, s2, s2 * st, std::min((int)ctx[r], (s2 + 1) * st)});
+}
+
+// deal the tasks round-robin onto W queues padded with NoOp; move the builder's tables into the plan
+mk_status pack_plan(Builder& b, int W, int max_splits, HostPlan& out, std::string& err) {
+  out.T = (int)(b.tasks.size() / kWords);
+  out.L = (out.T + W - 1) / W;
+  out.queue.assign((size_t)W * out.L * kWords, 0u);
+  for (int t = 0; t < out.T; ++t)
+    std::memcpy(&out.queue[((size_t)(t % W) * out.L + t / W) * kWords], &b.tasks[(size_t)t * kWords],
+                kWords * sizeof(uint32_t));
+  out.tasks = std::move(b.tasks);
+  out.thresholds = std::move(b.thr);
+  out.n_arrivals = b.n_arrivals;
+  out.ops = std::move(b.ops);
+  out.max_splits = max_splits;
+
+  // each op's tasks form one contiguous run of task ids (the graph baseline launches it)
+  for (size_t r = 0; r < out.ops.size(); ++r) {
+    const OpInfo& op = out.ops[r];
+    for (int t = op.first_task; t < op.first_task + op.n_tasks; ++t)
+      if (out.tasks[(size_t)t * kWords + W_ROW] != (uint32_t)r) {
+        err = "planner invariant violated (op tasks not contiguous)";
+        return MK_ERR_INVALID;
+      }
+  }
+
+  return MK_OK;
+}
+
+mk_status check_events(const HostPlan& out, std::string& err) {
+  // invariants: every wait names an event whose producers precede the waiter; thresholds equal
+  // the increments issued per run
+  std::vector<long long> produced(out.thresholds.size(), 0);
+  std::vector<int> last_prod(out.thresholds.size(), -1);
+  for (int t = 0; t < out.T; ++t) {
+    const uint32_t* w = &out.tasks[(size_t)t * kWords];
+    for (uint32_t k = 0; k < w[W_NWAIT]; ++k) {
+      uint32_t e = w[W_WAIT0 + 2 * k];
+      if (e >= out.thresholds.size() || w[W_WAIT0 + 2 * k + 1] != out.thresholds[e] || last_prod[e] >= t) {
+        err = "planner invariant violated (wait)";
+        return MK_ERR_INVALID;
+      }
+    }
+    for (uint32_t k = 0; k < w[W_NSIG]; ++k) {
+      uint32_t e = w[W_SIG0 + 3 * k];
+      bool fires = w[W_ARR_N] == 0 || w[W_ARR_RANK] == w[W_ARR_N] - 1;
+      if (fires) produced[e] += w[W_SIG0 + 3 * k + 1];
+      last_prod[e] = t;
+    }
+  }
+  for (size_t e = 0; e < produced.size(); ++e)
+    if (produced[e] != (long long)out.thresholds[e]) {
+      err = "planner invariant violated (threshold != increments)";
+      return MK_ERR_INVALID;
+    }
+  return MK_OK;
+}
+
+mk_status plan_indexer(const mk_config& c, const int32_t* ctx, int W, HostPlan& out, std::string& err) {
+  const int H = c.hidden, qr = c.idx_q_rank, nh = c.idx_heads, hd = c.idx_head_dim;
+  const int R = c.n_requests, T = c.tokens_per_request, M = R * T, P = c.page_size;
+  if (W < 1 || R < 1 || T < 1 || H < 1 || qr < 1 || nh < 1 || hd < 1) {
+    err = "invalid shape";
+    return MK_ERR_INVALID;
+  }
+  if (!c.weight_fp8 || !c.act_fp8) {
+    err = "the indexer front is built for e4m3 weights and activations";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (hd != 128 || nh % kM16Rows || qr % kM16Rows || H % 512 || qr % 512 || H > 8192 || qr > 8192 || T > 8 ||
+      M > 16 || P % 8) {
+    err = "unsupported indexer shape: head dim 128, heads a multiple of 64, hidden and q rank multiples of 512 "
+          "(at most 8192), at most 8 tokens per request and 16 rows, page size a multiple of 8";
+    return MK_ERR_UNSUPPORTED;
+  }
+  for (int r = 0; r < R; ++r)
+    if (ctx[r] < T || ctx[r] > c.max_pages_per_req * P) {
+      err = "context length out of range (at least the request's new tokens, at most its block table)";
+      return MK_ERR_INVALID;
+    }
+  out = HostPlan{};
+  out.cfg = c;
+  out.ctx.assign(ctx, ctx + R);
+  out.W = W;
+  if (!tile_params(c, W, ctx, out.tp, err)) return MK_ERR_UNSUPPORTED;
+  Builder b;
+  build_indexer(c, ctx, out.tp, b);
+  if (pack_plan(b, W, 0, out, err) != MK_OK) return MK_ERR_INVALID;
+  size_t off = 0;
+  auto region = [&](const char* name, size_t bytes) {
+    out.regions.push_back({name, off, bytes});
+    off += (bytes + 255) / 256 * 256;
+  };
+  const size_t kc = out.tp.kc, kcq = out.tp.kc_q;
+  region("hq", (size_t)16 * H);          // A0 output, e4m3 operand order
+  region("sh", 16 * 4);
+  region("qa", (size_t)M * qr * 4);      // B0 output, fp32 rows
+  region("qaq", (size_t)16 * qr);        // q_a norm output, e4m3 operand order
+  region("sqa", 16 * 4);
+  region("w", (size_t)M * nh * 4);       // C0 output, fp32 rows
+  region("k", (size_t)M * hd * 4);       // B1 output, fp32 rows
+  region("qi", (size_t)16 * nh * hd * 2);  // D1 output, bf16 in the score operand order
+  region("gp_qa", (size_t)(qr / kM16Rows) * (H / kc) * 4096);
+  region("gp_w", (size_t)(nh / kM16Rows) * (H / kc) * 4096);
+  region("gp_k", (size_t)(hd / kM16Rows) * (H / kc) * 4096);
+  region("gp_qi", (size_t)(nh * hd / kM16Rows) * (qr / kcq) * 4096);
+  out.workspace_bytes = off;
+  return check_events(out, err);
+}
+
 }  // namespace
 
 mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& out, std::string& err) {
+  if (c.workload == MK_INDEXER_FRONT) return plan_indexer(c, ctx, W, out, err);
   if (c.workload != MK_QWEN3_LAYER && c.workload != MK_QWEN3_STEP) {
     err = "workload not built in this library";
     return MK_ERR_UNSUPPORTED;
@@ -323,27 +522,7 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
              {c.num_layers, n0, std::min(rl, c.vocab - n0), 0, H, 0, grp, n_pub, slot});
     }
   }
-  out.T = (int)(b.tasks.size() / kWords);
-  out.L = (out.T + W - 1) / W;
-  out.queue.assign((size_t)W * out.L * kWords, 0u);
-  for (int t = 0; t < out.T; ++t)
-    std::memcpy(&out.queue[((size_t)(t % W) * out.L + t / W) * kWords], &b.tasks[(size_t)t * kWords],
-                kWords * sizeof(uint32_t));
-  out.tasks = std::move(b.tasks);
-  out.thresholds = std::move(b.thr);
-  out.n_arrivals = b.n_arrivals;
-  out.ops = std::move(b.ops);
-  out.max_splits = max_splits;
-
-  // each op's tasks form one contiguous run of task ids (the graph baseline launches it)
-  for (size_t r = 0; r < out.ops.size(); ++r) {
-    const OpInfo& op = out.ops[r];
-    for (int t = op.first_task; t < op.first_task + op.n_tasks; ++t)
-      if (out.tasks[(size_t)t * kWords + W_ROW] != (uint32_t)r) {
-        err = "planner invariant violated (op tasks not contiguous)";
-        return MK_ERR_INVALID;
-      }
-  }
+  if (pack_plan(b, W, max_splits, out, err) != MK_OK) return MK_ERR_INVALID;
 
   // workspace regions (256-byte aligned)
   size_t off = 0;
@@ -391,32 +570,7 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
   if (c.workload == MK_QWEN3_STEP) region("lm_part", (size_t)((c.vocab + p.r_lm - 1) / p.r_lm) * 8);
   out.workspace_bytes = off;
 
-  // invariants: every wait names an event whose producers precede the waiter; thresholds equal
-  // the increments issued per run
-  std::vector<long long> produced(out.thresholds.size(), 0);
-  std::vector<int> last_prod(out.thresholds.size(), -1);
-  for (int t = 0; t < out.T; ++t) {
-    const uint32_t* w = &out.tasks[(size_t)t * kWords];
-    for (uint32_t k = 0; k < w[W_NWAIT]; ++k) {
-      uint32_t e = w[W_WAIT0 + 2 * k];
-      if (e >= out.thresholds.size() || w[W_WAIT0 + 2 * k + 1] != out.thresholds[e] || last_prod[e] >= t) {
-        err = "planner invariant violated (wait)";
-        return MK_ERR_INVALID;
-      }
-    }
-    for (uint32_t k = 0; k < w[W_NSIG]; ++k) {
-      uint32_t e = w[W_SIG0 + 3 * k];
-      bool fires = w[W_ARR_N] == 0 || w[W_ARR_RANK] == w[W_ARR_N] - 1;
-      if (fires) produced[e] += w[W_SIG0 + 3 * k + 1];
-      last_prod[e] = t;
-    }
-  }
-  for (size_t e = 0; e < produced.size(); ++e)
-    if (produced[e] != (long long)out.thresholds[e]) {
-      err = "planner invariant violated (threshold != increments)";
-      return MK_ERR_INVALID;
-    }
-  return MK_OK;
+  return check_events(out, err);
 }
 
 }  // namespace mk

@@ -9,7 +9,8 @@ from oracle import queue as oq
 from workloads import get_config
 
 
-@pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8"])
+@pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
+                                  "indexer_front"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_invariants(name, W):
     cfg = get_config(name)
@@ -139,3 +140,24 @@ def test_multi_row_no_deadlock_random_speeds(fp8):
     oq.check_invariants(plan)
     for seed in range(2):
         simulate(plan, seed)
+
+
+def test_indexer_front_counts_and_no_deadlock():
+    """Indexer front at its configured size: 16 norm rows, tiles of 64 rows x one K chunk for
+    B0 (1536 rows), C0 (64), B1 (128) over K = 6144 (chunk 1024) and D1 (8192 rows) over K = 1536
+    (chunk 768), per-tile finalizes (D1: per head), 16 q_a norm rows, one key-cache task, and
+    one score task per 128 keys of each request."""
+    cfg = get_config("indexer_front")
+    plan = oq.build_queue(cfg, 256)
+    ops = [int(t[0]) for t in _tasks(plan)]
+    assert ops.count(oq.OP_NORM) == 2 * 16
+    assert ops.count(oq.OP_GEMM) == (1536 // 64 + 1 + 2) * 6 + (8192 // 64) * 2
+    assert ops.count(oq.OP_FIN) == 1536 // 64 + 1 + 2 + 64
+    assert ops.count(oq.OP_KCACHE) == 1 and ops.count(oq.OP_SCORE) == 2 * 8192 // 128
+    assert plan["n_tasks"] == 670
+    small = dataclasses.replace(cfg, hidden=1024, idx_q_rank=512, context=300)
+    for W in (3, 64):
+        p = oq.build_queue(small, W)
+        oq.check_invariants(p)
+        for seed in range(2):
+            simulate(p, seed)

@@ -16,7 +16,8 @@ def _both(cfg, W, ctx=None):
     return plan, ref
 
 
-@pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8"])
+@pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
+                                  "indexer_front"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_queue_bit_exact(name, W):
     cfg = get_config(name)
@@ -48,3 +49,15 @@ def test_small_shapes_bit_exact():
         plan, ref = _both(cfg, W)
         assert np.array_equal(plan.queue(), ref["queue"])
         plan.close()
+
+
+def test_indexer_ragged_bit_exact():
+    cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, idx_heads=64,
+                              n_requests=2, tokens_per_request=3, context=300)
+    for ctx in ([300, 3], [129, 256]):
+        for W in (5, 64, 256):
+            plan, ref = _both(cfg, W, ctx)
+            assert np.array_equal(plan.queue(), ref["queue"])
+            assert np.array_equal(plan.thresholds(), ref["thresholds"])
+            oq.check_invariants(ref)
+            plan.close()
