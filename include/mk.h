@@ -96,6 +96,26 @@ enum {
   MK_T_COUNT_QWEN3
 };
 
+/* Tensor order for MK_INDEXER_FRONT (M = n_requests x tokens_per_request rows, request r's rows
+ * r T .. r T + T - 1 are its T new tokens at positions ctx_r - T .. ctx_r - 1; qr = idx_q_rank,
+ * nh = idx_heads, hd = idx_head_dim = 128; e4m3 = OCP E4M3FN code bytes, scales fp32 per 128 x 128
+ * block [ceil(N/128), ceil(K/128)]):
+ *   W_QA [qr, H] e4m3 + S_QA;  W_W [nh, H] e4m3 + S_W;  W_K [hd, H] e4m3 + S_K;
+ *   W_QI [nh hd, qr] e4m3 + S_QI          (rows h hd .. h hd + hd - 1 are head h)
+ *   G_NORM [H] bf16;  G_QA [qr] bf16    (RMSNorm gains)
+ *   KEY_CACHE [pages, P, hd] e4m3;  KEY_SCALE [pages, P] fp32  (written in place at the new positions)
+ *   BLOCK_TABLE [R, max_pages_per_req] int32;  CONTEXT_LENS [R] int32 (include the new tokens)
+ *   X [M, H] bf16;  R_IN [M, H] fp32
+ *   SCORE_OUT [M, S] fp32 with S = the largest context length: row m gets the scores of keys
+ *     t < ctx_r (-inf for t > its position); entries t >= ctx_r are not written
+ *   WORKSPACE  mk_plan_workspace_bytes() bytes, 256-byte aligned */
+enum {
+  MK_TI_W_QA = 0, MK_TI_S_QA, MK_TI_W_W, MK_TI_S_W, MK_TI_W_K, MK_TI_S_K, MK_TI_W_QI, MK_TI_S_QI,
+  MK_TI_G_NORM, MK_TI_G_QA, MK_TI_KEY_CACHE, MK_TI_KEY_SCALE, MK_TI_BLOCK_TABLE, MK_TI_CONTEXT_LENS,
+  MK_TI_X, MK_TI_R_IN, MK_TI_SCORE_OUT, MK_TI_WORKSPACE,
+  MK_TI_COUNT
+};
+
 typedef struct mk_plan mk_plan; /* opaque, library-owned */
 
 /* Lower a workload into tile tasks, events and per-worker queues, and upload the queue,

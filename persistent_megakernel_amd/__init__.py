@@ -27,6 +27,8 @@ QWEN3_TENSORS = ["w_qkv", "w_o", "w_gu", "w_down", "g_attn", "g_mlp", "g_q", "g_
                  "block_table", "context_lens", "x", "r_in", "y_out", "r2_out", "workspace",
                  "g_final", "w_lm", "logits_out", "token_out",
                  "s_qkv", "s_o", "s_gu", "s_down"]
+INDEXER_TENSORS = ["w_qa", "s_qa", "w_w", "s_w", "w_k", "s_k", "w_qi", "s_qi", "g_norm", "g_qa", "key_cache",
+                   "key_scale", "block_table", "context_lens", "x", "r_in", "score_out", "workspace"]
 _WORKLOADS = {"qwen3_layer": MK_QWEN3_LAYER, "qwen3_step": MK_QWEN3_STEP, "indexer_front": MK_INDEXER_FRONT}
 
 
@@ -182,3 +184,8 @@ def qwen3_pointers(t: Dict[str, "object"], step: bool) -> MkTensors:
 
 def exported_symbols():
     return [n for n in dir(_lib) if n.startswith("mk_")]
+
+
+def indexer_pointers(t: Dict[str, "object"]) -> MkTensors:
+    """mk_tensors in the indexer front's ABI order from a dict of device tensors keyed by INDEXER_TENSORS."""
+    return Plan.tensors([t[n].data_ptr() for n in INDEXER_TENSORS])

@@ -45,7 +45,8 @@ struct mk_plan {
   uint32_t* d_events = nullptr;
   uint32_t* d_arrivals = nullptr;
   uint32_t* d_err = nullptr;
-  float* d_rope = nullptr;
+  float* d_rope = nullptr;   // per row: (cos, sin) at the row's position, [M][head_dim / 2][2]
+  int32_t* d_pos = nullptr;  // per row: position of the row's token
   uint32_t* d_trace = nullptr;
   size_t events_bytes = 0, arrivals_bytes = 0;
   uint32_t epoch = 0;  // megakernel runs so far; never reset (record tags must not repeat)
@@ -63,9 +64,20 @@ namespace {
 
 bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 
+int ws_index(const mk_config& c) { return c.workload == MK_INDEXER_FRONT ? (int)MK_TI_WORKSPACE : (int)MK_T_WORKSPACE; }
+
 mk_status check_tensors(const mk_plan* p, const mk_tensors* t) {
   if (!t) return fail(MK_ERR_INVALID, "null tensors");
   const mk_config& c = p->hp.cfg;
+  if (c.workload == MK_INDEXER_FRONT) {
+    if (t->n < MK_TI_COUNT) return fail(MK_ERR_INVALID, "too few tensors for the indexer front");
+    for (int i = 0; i < MK_TI_COUNT; ++i) {
+      if (t->ptr[i] == 0) return fail(MK_ERR_INVALID, "null tensor at index " + std::to_string(i));
+      if (!aligned16(t->ptr[i])) return fail(MK_ERR_INVALID, "tensor " + std::to_string(i) + " is not 16-byte aligned");
+    }
+    if (t->ptr[MK_TI_WORKSPACE] & 255u) return fail(MK_ERR_INVALID, "workspace must be 256-byte aligned");
+    return MK_OK;
+  }
   const bool step = c.workload == MK_QWEN3_STEP, fp8 = c.weight_fp8 != 0;
   const int need = fp8 ? MK_T_COUNT_QWEN3 : step ? MK_T_TOKEN_OUT + 1 : MK_T_WORKSPACE + 1;
   if (t->n < need) return fail(MK_ERR_INVALID, "too few tensors for this workload");
@@ -85,10 +97,71 @@ size_t region_off(const mk::HostPlan& hp, const char* name) {
   return 0;
 }
 
+// indexer front: one row of 16 slots per op instance
+void fill_table_indexer(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& tab) {
+  using namespace mk;
+  const mk::HostPlan& hp = p->hp;
+  const uint64_t ws = t->ptr[MK_TI_WORKSPACE];
+  auto rg = [&](const char* n) { return ws + region_off(hp, n); };
+  const uint64_t wt[8] = {0, 0, 0, 0, t->ptr[MK_TI_W_QA], t->ptr[MK_TI_W_W], t->ptr[MK_TI_W_K], t->ptr[MK_TI_W_QI]};
+  const uint64_t st[8] = {0, 0, 0, 0, t->ptr[MK_TI_S_QA], t->ptr[MK_TI_S_W], t->ptr[MK_TI_S_K], t->ptr[MK_TI_S_QI]};
+  const char* gp[8] = {"", "", "", "", "gp_qa", "gp_w", "gp_k", "gp_qi"};
+  const char* out[8] = {"", "", "", "", "qa", "w", "k", "qi"};
+  tab.assign(hp.ops.size() * kTableSlots, 0);
+  for (size_t row = 0; row < hp.ops.size(); ++row) {
+    uint64_t* s = &tab[row * kTableSlots];
+    const uint32_t sub = hp.ops[row].sub;
+    switch (hp.ops[row].opcode) {
+      case OP_NORM:  // A0 (sub 0) or the q_a norm (sub 2)
+        s[NM_X] = sub == 0 ? t->ptr[MK_TI_X] : 0;
+        s[NM_R] = sub == 0 ? t->ptr[MK_TI_R_IN] : rg("qa");
+        s[NM_GAIN] = sub == 0 ? t->ptr[MK_TI_G_NORM] : t->ptr[MK_TI_G_QA];
+        s[NM_R1] = 0;
+        s[NM_H] = rg(sub == 0 ? "hq" : "qaq");
+        s[NM_S] = rg(sub == 0 ? "sh" : "sqa");
+        break;
+      case OP_GEMM:
+        s[GM_W] = wt[sub];
+        s[GM_ACT] = rg(sub == K_QI ? "qaq" : "hq");
+        s[GM_PART] = rg(gp[sub]);
+        s[GM_SW] = st[sub];
+        break;
+      case OP_FIN:
+        s[FN_PART] = rg(gp[sub]);
+        s[FN_SA] = rg(sub == K_QI ? "sqa" : "sh");
+        s[FN_OUT] = rg(out[sub]);
+        s[FN_R1] = (uint64_t)p->d_rope;  // D1's RoPE
+        break;
+      case OP_KCACHE:
+        s[KC_K] = rg("k");
+        s[KC_ROPE] = (uint64_t)p->d_rope;
+        s[KC_CACHE] = t->ptr[MK_TI_KEY_CACHE];
+        s[KC_SCALE] = t->ptr[MK_TI_KEY_SCALE];
+        s[KC_BT] = t->ptr[MK_TI_BLOCK_TABLE];
+        s[KC_POS] = (uint64_t)p->d_pos;
+        break;
+      case OP_SCORE:
+        s[SC_Q] = rg("qi");
+        s[SC_W] = rg("w");
+        s[SC_CACHE] = t->ptr[MK_TI_KEY_CACHE];
+        s[SC_SCALE] = t->ptr[MK_TI_KEY_SCALE];
+        s[SC_BT] = t->ptr[MK_TI_BLOCK_TABLE];
+        s[SC_OUT] = t->ptr[MK_TI_SCORE_OUT];
+        s[SC_POS] = (uint64_t)p->d_pos;
+        break;
+      default: break;
+    }
+  }
+}
+
 // one row of 16 slots per op instance, layer-offset addresses
 void fill_table(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& tab) {
   using namespace mk;
   const mk::HostPlan& hp = p->hp;
+  if (hp.cfg.workload == MK_INDEXER_FRONT) {
+    fill_table_indexer(p, t, tab);
+    return;
+  }
   const mk_config& c = hp.cfg;
   const uint64_t H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const uint64_t nqkv = (Hq + 2 * Hkv) * d;
@@ -237,7 +310,7 @@ mk_status check_runnable(mk_plan* p) {
   if (p->host_only) return fail(MK_ERR_INVALID, "plan was built without a device");
   const mk::HostPlan& hp = p->hp;
   const mk_config& c = hp.cfg;
-  const int g = c.n_q_heads / c.n_kv_heads;
+  const int g = c.workload == MK_INDEXER_FRONT ? 1 : c.n_q_heads / c.n_kv_heads;
   if (g != 1 && g != 2 && g != 4) return fail(MK_ERR_UNSUPPORTED, "GQA group must be 1, 2 or 4");
   if (c.weight_fp8 != c.act_fp8) return fail(MK_ERR_UNSUPPORTED, "FP8 weights come with FP8 activations (W8A8) only");
   if (hp.tp.spec == 0) {
@@ -247,6 +320,8 @@ mk_status check_runnable(mk_plan* p) {
         hp.tp.r_down > 128 || hp.tp.r_gu % 2 || c.hidden % 512 || c.inter % 512 || (c.n_q_heads * c.head_dim) % 512)
       return fail(MK_ERR_UNSUPPORTED, "shape exceeds the M = 1 op bodies (hidden <= 2048; inter, q width <= 6144; "
                                       "hidden, inter and q width multiples of 512; even gate/up tiles)");
+  } else if (c.workload == MK_INDEXER_FRONT) {
+    if (c.idx_heads != 64) return fail(MK_ERR_UNSUPPORTED, "the indexer score body holds 64 heads");
   } else {
     const int K[3] = {c.hidden, c.n_q_heads * c.head_dim, c.inter};
     for (int k : K)
@@ -319,10 +394,12 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
     *out = p.release();
     return MK_OK;
   }
-  p->sh = mk::Shapes{c.hidden, c.inter, c.n_q_heads, c.n_kv_heads, c.n_q_heads / c.n_kv_heads,
+  p->sh = mk::Shapes{c.hidden, c.inter, c.n_q_heads, c.n_kv_heads, c.n_kv_heads ? c.n_q_heads / c.n_kv_heads : 1,
                      (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, c.page_size, c.max_pages_per_req,
                      hp.max_splits, c.vocab, c.rms_eps, 1.0f / std::sqrt((float)c.head_dim),
-                     c.n_requests * c.tokens_per_request, hp.tp.kc, c.act_fp8 ? 1 : 0, c.num_layers};
+                     c.n_requests * c.tokens_per_request, hp.tp.kc, c.act_fp8 ? 1 : 0, c.num_layers,
+                     c.idx_q_rank, c.idx_heads, c.tokens_per_request, 0};
+  for (int r = 0; r < c.n_requests; ++r) p->sh.smax = std::max(p->sh.smax, (int)host_context_lens[r]);
   HIP_TRY(hipMalloc(&p->d_queue, hp.queue.size() * 4));
   HIP_TRY(hipMemcpy(p->d_queue, hp.queue.data(), hp.queue.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipMalloc(&p->d_tasks, hp.tasks.size() * 4));
@@ -335,19 +412,24 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
   HIP_TRY(hipMemset(p->d_arrivals, 0, p->arrivals_bytes));
   HIP_TRY(hipMalloc(&p->d_err, 64));
   HIP_TRY(hipMemset(p->d_err, 0, 64));
-  // RoPE table: per request row, (cos, sin) of pos * theta^(-2i/d) for i < d/2, pos = ctx - 1
-  const int half = c.head_dim / 2;
-  std::vector<float> rope((size_t)c.n_requests * half * 2);
-  for (int r = 0; r < c.n_requests; ++r) {
-    const double pos = host_context_lens[r] - 1;
+  // RoPE table: per row m (request r = m / T, its token m % T of T new ones), (cos, sin) of
+  // pos * theta^(-2i/d) for i < d/2 with pos = ctx_r - T + m % T
+  const int T = c.tokens_per_request, M = c.n_requests * T;
+  const int hd = c.workload == MK_INDEXER_FRONT ? c.idx_head_dim : c.head_dim, half = hd / 2;
+  std::vector<float> rope((size_t)M * half * 2);
+  std::vector<int32_t> posv(M);
+  for (int m = 0; m < M; ++m) {
+    posv[m] = host_context_lens[m / T] - T + m % T;
     for (int i = 0; i < half; ++i) {
-      const double ang = pos * std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
-      rope[((size_t)r * half + i) * 2] = (float)std::cos(ang);
-      rope[((size_t)r * half + i) * 2 + 1] = (float)std::sin(ang);
+      const double ang = (double)posv[m] * std::pow((double)c.rope_theta, -2.0 * i / hd);
+      rope[((size_t)m * half + i) * 2] = (float)std::cos(ang);
+      rope[((size_t)m * half + i) * 2 + 1] = (float)std::sin(ang);
     }
   }
   HIP_TRY(hipMalloc(&p->d_rope, rope.size() * 4));
   HIP_TRY(hipMemcpy(p->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(hipMalloc(&p->d_pos, posv.size() * 4));
+  HIP_TRY(hipMemcpy(p->d_pos, posv.data(), posv.size() * 4, hipMemcpyHostToDevice));
   if (c.flags & MK_FLAG_TRACE) {
     HIP_TRY(hipMalloc(&p->d_trace, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
     HIP_TRY(hipMemset(p->d_trace, 0, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
@@ -405,7 +487,7 @@ mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
   const bool new_set = p->tables.find(std::vector<uint64_t>(t->ptr, t->ptr + t->n)) == p->tables.end();
   if ((st = get_table(p, t, &table)) != MK_OK) return st;
   if (new_set)  // a workspace first seen by this plan: no stale record may carry one of its tags
-    HIP_TRY(hipMemsetAsync((void*)t->ptr[MK_T_WORKSPACE], 0, p->hp.workspace_bytes, (hipStream_t)stream));
+    HIP_TRY(hipMemsetAsync((void*)t->ptr[ws_index(p->hp.cfg)], 0, p->hp.workspace_bytes, (hipStream_t)stream));
   mk::KArgs a = base_args(p, table);
   a.instrs = p->d_queue;
   a.L = p->hp.L;
@@ -538,6 +620,7 @@ void mk_plan_destroy(mk_plan* p) {
   (void)hipFree(p->d_arrivals);
   (void)hipFree(p->d_err);
   (void)hipFree(p->d_rope);
+  (void)hipFree(p->d_pos);
   if (p->d_trace) (void)hipFree(p->d_trace);
   delete p;
 }

@@ -13,6 +13,7 @@ struct Shapes {
   int H, I, Hq, Hkv, g, n_qkv, P, maxp, max_splits, V;
   float eps, inv_sqrt_d;
   int M, kc, fp8, layers;  // multi-row plans: rows, K chunk of a projection tile, W8A8, layers
+  int qr, nh, T, smax;     // indexer front: q rank, heads, tokens per request, score row stride
 };
 
 struct KArgs {

@@ -76,11 +76,11 @@ enum GemmSlot { GM_W = 0, GM_ACT, GM_PART, GM_SW };
 enum FinSlot { FN_PART = 0, FN_SA, FN_OUT, FN_R1, FN_OUT2 };
 // QUANT: fp32 rows in, e4m3 operand-order rows out, per-token scales out
 enum QuantSlot { QT_IN = 0, QT_OUT, QT_S };
-// KCACHE: key rows (fp32 [M][d]), RoPE table, key cache codes, key scales, block table
-enum KcSlot { KC_K = 0, KC_ROPE, KC_CACHE, KC_SCALE, KC_BT };
+// KCACHE: key rows (fp32 [M][d]), RoPE table, key cache codes, key scales, block table, row positions
+enum KcSlot { KC_K = 0, KC_ROPE, KC_CACHE, KC_SCALE, KC_BT, KC_POS };
 // SCORE: q (bf16, score operand order), head weights (fp32 [M][heads]), key cache, key scales,
-// block table, scores out (fp32 [M][max context])
-enum ScSlot { SC_Q = 0, SC_W, SC_CACHE, SC_SCALE, SC_BT, SC_OUT };
+// block table, scores out (fp32 [M][max context]), row positions
+enum ScSlot { SC_Q = 0, SC_W, SC_CACHE, SC_SCALE, SC_BT, SC_OUT, SC_POS };
 
 struct TileParams {
   int r_qkv = 0, r_o = 0, r_gu = 0, r_down = 0, r_lm = 0, s_tok = 0, spec = 0;

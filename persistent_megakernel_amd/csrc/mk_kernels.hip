@@ -281,7 +281,7 @@ DEV uint32_t ring_off(uint32_t lease, uint32_t off) {
 //   multi-row GEMM: 64 weight rows x one K chunk in matrix-core operand order   NORM: norm gain
 // Attention K / V spans are gathered token by token through the block table.
 constexpr int kMaxSpans = 5;
-enum PfMode : uint32_t { PF_SPANS = 0, PF_ATTN = 1, PF_W_BF16 = 2, PF_W_FP8 = 3 };
+enum PfMode : uint32_t { PF_SPANS = 0, PF_ATTN = 1, PF_W_BF16 = 2, PF_W_FP8 = 3, PF_KEYS = 4 };
 // weight fragments (multi-row family only): tile row tr < split is weight row base0 + tr, else
 // base1 + tr; rowb bytes per weight row; k0b byte offset of the K chunk in a row.  The single-token
 // family carries none of it, which keeps its descriptor small enough to stay in registers.
@@ -289,7 +289,7 @@ template <int S>
 struct PfFrag {};
 template <>
 struct PfFrag<1> {
-  uint32_t rowb, k0b, base0, base1, split;
+  uint32_t rowb, k0b, base0, base1, split, bpn;  // bpn: lease blocks per 16-row block of the tile
 };
 // Every span is a whole number of 1 KiB blocks (the launcher checks the shapes for it), so a
 // block's 64 lanes always load 1 KiB of the span; no per-span length is kept (selecting one by span
@@ -315,6 +315,18 @@ DEV void pf_set(Pf<S>& pf, const void* src, uint32_t bytes) {
   pf.total = pf.blk[K + 1];
 }
 
+// K of a projection kind
+DEV uint32_t proj_k(const Shapes& sh, uint32_t kind) {
+  switch (kind) {
+    case K_O: return (uint32_t)sh.Hq * 128u;
+    case K_DOWN: return (uint32_t)sh.I;
+    case K_QI: return (uint32_t)sh.qr;
+    default: return (uint32_t)sh.H;
+  }
+}
+// row length of a NORM instruction: the hidden size, or the q rank for the indexer's q_a norm
+DEV uint32_t norm_len(const Shapes& sh, const Instr& in) { return in.w[W_LAYER + 1] == 2 ? (uint32_t)sh.qr : (uint32_t)sh.H; }
+
 // splits of an attention instruction's (request, kv head).  S is the op family of the kernel
 // instance: 0 the single-token bodies, 1 the multi-row ones (the plan's spec id, fixed per plan).
 template <int S>
@@ -332,8 +344,8 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
   if constexpr (S == 1) if (op == OP_GEMM) {
     // 64 KiB: block b = 16 nb + q holds 64 bytes of each of the tile rows [16 nb, 16 nb + 16) (K
     // step q: 32 bf16 or 64 e4m3 weights), lane l taking row 16 nb + l % 16, bytes 16 (l / 16) ...
-    const uint32_t kind = in.w[W_LAYER + 1], n0 = in.w[W_LAYER + 3], k0 = in.w[W_LAYER + 5];
-    const uint32_t K = kind == K_O ? (uint32_t)sh.Hq * 128u : kind == K_DOWN ? (uint32_t)sh.I : (uint32_t)sh.H;
+    const uint32_t kind = in.w[W_LAYER + 1], n0 = in.w[W_LAYER + 3], k0 = in.w[W_LAYER + 5], kc = in.w[W_LAYER + 6];
+    const uint32_t K = proj_k(sh, kind);
     const uint32_t el = sh.fp8 ? 1u : 2u;
     pf.mode = sh.fp8 ? PF_W_FP8 : PF_W_BF16;
     pf.rowb = K * el;
@@ -341,14 +353,30 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
     pf.base0 = n0;
     pf.split = kind == K_GU ? 32u : 64u;  // gate/up: 32 gate rows, then the 32 matching up rows
     pf.base1 = kind == K_GU ? (uint32_t)sh.I + n0 - 32u : n0;
-    pf_set<0>(pf, (const void*)s_ld64(row + GM_W), 65536u);
+    pf.bpn = kc * el / 64u;
+    pf_set<0>(pf, (const void*)s_ld64(row + GM_W), 64u * kc * el);
     return;
   }
   if (S == 1 && op == OP_NORM) {
-    pf_set<0>(pf, (const void*)s_ld64(row + NM_GAIN), 2u * (uint32_t)sh.H);
+    pf_set<0>(pf, (const void*)s_ld64(row + NM_GAIN), 2u * norm_len(sh, in));
     return;
   }
-  if (S == 1 && (op == OP_FIN || op == OP_QUANT)) return;  // nothing to prefetch: inputs are produced in the run
+  if (S == 1 && op == OP_SCORE) {
+    // the split's keys from before this step, 8 tokens (1 KiB) per block, and their scales (32 bytes
+    // per key block) in one block after them; the step's own keys are staged after the wait
+    const uint32_t r = in.w[W_LAYER + 1], t0 = in.w[W_LAYER + 3], t1 = in.w[W_LAYER + 4];
+    const uint32_t T = (uint32_t)sh.T;
+    const uint32_t ctx = (uint32_t)c_ld<int32_t>((const int32_t*)s_ld64(row + SC_POS) + r * T + T - 1u) + 1u;
+    const uint32_t lim = min(t1, ctx - T), nko = lim > t0 ? lim - t0 : 0u;
+    pf.mode = PF_KEYS;
+    pf.bt = (const int32_t*)s_ld64(row + SC_BT) + (size_t)r * sh.maxp;
+    pf.t0 = (int)t0;
+    pf.nk = (int)nko;
+    pf_set<0>(pf, (const void*)s_ld64(row + SC_CACHE), nko * 128u);
+    pf_set<1>(pf, (const void*)s_ld64(row + SC_SCALE), nko ? 1024u : 0u);
+    return;
+  }
+  if (S == 1 && (op == OP_FIN || op == OP_QUANT || op == OP_KCACHE)) return;  // nothing to prefetch: inputs are produced in the run
   if (pf.mode == PF_ATTN) {
     const int r = in.w[W_P1], hk = in.w[W_P2], s = in.w[W_P3];
     const int t0 = in.w[W_P4], t1 = in.w[W_P5];
@@ -394,10 +422,24 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
     const char* src;
     bool frag = false;
     if constexpr (S == 1) {
-      if (pf.mode >= PF_W_BF16) {
-        const uint32_t tr = (b >> 4) * 16u + (ln & 15u), q = b & 15u;
+      if (pf.mode == PF_W_BF16 || pf.mode == PF_W_FP8) {
+        const uint32_t nb = b / pf.bpn, q = b - nb * pf.bpn;
+        const uint32_t tr = nb * 16u + (ln & 15u);
         const uint32_t grow = tr < pf.split ? pf.base0 + tr : pf.base1 + tr;
         src = base + (size_t)grow * pf.rowb + pf.k0b + q * 64u + (ln >> 4) * 16u;
+        frag = true;
+      } else if (pf.mode == PF_KEYS) {
+        if (k == 1) break;  // the scale block is filled alongside the key blocks
+        // 8 tokens of one page (8 divides the page size and t0): 1 KiB contiguous in the cache
+        const uint32_t tok = (uint32_t)pf.t0 + 8u * b, P = (uint32_t)a.sh.P;
+        const uint32_t page = (uint32_t)s_ld32(pf.bt + tok / P);
+        const uint32_t slot = page * P + tok % P;
+        const uint32_t lo = 8u * b + (ln >> 3) < (uint32_t)pf.nk ? ln * 16u : 0u;  // past the split: reload the block start
+        src = base + (size_t)slot * 128u + lo;
+        const uint32_t sdst = (uint32_t)(uintptr_t)(lds_void*)(smem + kRingOff + ring_off(lease, pf.blk[1] * 1024u + b * 32u));
+        if (ln < 2u)  // the 8 tokens' scales (32 bytes) into the scale block: one more load of the wave
+          lds_dma16(pf.src[1] + (size_t)slot * 4u + ln * 16u, sdst);
+        ++issued;
         frag = true;
       }
     }
@@ -998,10 +1040,6 @@ DEV bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
   const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
-// K of a projection kind
-DEV uint32_t proj_k(const Shapes& sh, uint32_t kind) {
-  return kind == K_O ? (uint32_t)sh.Hq * 128u : kind == K_DOWN ? (uint32_t)sh.I : (uint32_t)sh.H;
-}
 DEV void st64(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, SC1); }
 DEV void st128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, SC1); }
 DEV uint32_t bf16_bits(float v) { return pack_bf2(v, 0.f) & 0xffffu; }
@@ -1027,7 +1065,8 @@ DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, 
   const char* act = smem + kActOff + kActA;
   const char* ring = smem + kRingOff;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (!FP8) {
+  const uint32_t kc = in.w[W_LAYER + 6];
+  if (!FP8) {  // K chunk 512: 16 steps of 32
 #pragma unroll
     for (uint32_t i = 0; i < 8; ++i) {
       const uint32_t q = kh * 8u + i;
@@ -1042,18 +1081,20 @@ DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, 
     const uint32_t tr0 = nb * 16u;
     const uint32_t grow = kind == K_GU && tr0 >= 32u ? (uint32_t)a.sh.I + n0 + tr0 - 32u : n0 + tr0;
     const float* sw = (const float*)s_ld64(row + GM_SW) + (size_t)(grow >> 7) * nkb + (k0 >> 7);
+    const uint32_t nkh = kc >> 8;  // 128-wide scale blocks per half of the chunk (kc 1024: 4, 768: 3)
 #pragma unroll
-    for (uint32_t kb = 0; kb < 4; ++kb) {  // the wave's four 128-wide scale blocks, two 64-k steps each
+    for (uint32_t kb = 0; kb < 4; ++kb) {  // the wave's scale blocks, two 64-k steps each
+      if (kb >= nkh) break;
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (uint32_t h = 0; h < 2; ++h) {
-        const uint32_t q = kh * 8u + kb * 2u + h;
+        const uint32_t q = kh * 2u * nkh + kb * 2u + h;
         const u32x4 av = *(const u32x4*)(act + q * 1024u + ln * 16u);
-        const u32x4 bv = *(const u32x4*)(ring + ring_off(lease, (nb * 16u + q) * 1024u + ln * 16u));
+        const u32x4 bv = *(const u32x4*)(ring + ring_off(lease, (nb * (kc >> 6) + q) * 1024u + ln * 16u));
         t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av.x, av.y), e4m3x8_bf16(bv.x, bv.y), t, 0, 0, 0);
         t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av.z, av.w), e4m3x8_bf16(bv.z, bv.w), t, 0, 0, 0);
       }
-      acc += c_ld<float>(sw + kh * 4u + kb) * t;
+      acc += c_ld<float>(sw + kh * nkh + kb) * t;
     }
   }
   *(f32x4*)(smem + kActOff + kActD + ((uint32_t)wv * 64u + ln) * 16u) = acc;
@@ -1065,7 +1106,7 @@ DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, 
 DEV void gemm_epilogue(const KArgs& a, const Instr& in, const char* smem) {
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const uint32_t kind = in.w[W_LAYER + 1], j = in.w[W_LAYER + 2], k0 = in.w[W_LAYER + 5];
-  const uint32_t kc = (uint32_t)a.sh.kc, nk = proj_k(a.sh, kind) / kc;
+  const uint32_t kc = in.w[W_LAYER + 6], nk = proj_k(a.sh, kind) / kc;
   float* part = (float*)s_ld64(row + GM_PART) + ((size_t)j * nk + k0 / kc) * 1024;
   __amdgpu_buffer_rsrc_t rp = rsrc(part);
   const char* D = smem + kActOff + kActD;
@@ -1140,6 +1181,10 @@ DEV void fin_tile(const KArgs& a, const Instr& in, int wv) {
       else
         st16(ro, opnd_bf16(m0, n0 + c), bf16_bits(mv));
     }
+  } else if (kind >= K_QA) {  // indexer q_a, head weights, key: fp32 rows
+    const uint32_t w = kind == K_QA ? (uint32_t)sh.qr : kind == K_W ? (uint32_t)sh.nh : 128u;
+    if (m0 < M) st32(ro, (m0 * w + n0 + c) * 4u, __float_as_uint(s0));
+    if (m1 < M) st32(ro, (m1 * w + n0 + c) * 4u, __float_as_uint(s1));
   } else {
     const uint32_t ms[2] = {m0, m1};
     const float vs[2] = {s0, s1};
@@ -1170,7 +1215,7 @@ template <bool FP8>
 DEV void norm_row(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
-  const uint32_t m = in.w[W_LAYER + 2], H = (uint32_t)sh.H, t = (uint32_t)wv * 64u + lane();
+  const uint32_t m = in.w[W_LAYER + 2], H = norm_len(sh, in), t = (uint32_t)wv * 64u + lane();
   const uint64_t xp = s_ld64(row + NM_X), r1p = s_ld64(row + NM_R1);
   __amdgpu_buffer_rsrc_t rr = rsrc((const float*)s_ld64(row + NM_R) + (size_t)m * H);
   __amdgpu_buffer_rsrc_t rx = rsrc((const uint16_t*)xp + (size_t)m * H);
@@ -1339,6 +1384,194 @@ DEV void comb_group(const KArgs& a, const Instr& in, int wv) {
   wait_vm0();
 }
 
+// ---------------------------------------------------------------------------------------
+// indexer front
+
+// byte offset of q element (token m, head h, dim d) in the score's A-operand order: per (token,
+// 16-head block, dim step) 1 KiB, dim step f = 2 (d / 64) + (d % 16) / 8, lane (h % 16) + 16 ((d % 64) / 16)
+// holding 8 consecutive dims -- the order in which a lane's 16 key bytes (dims 64 s + 16 g ..) feed
+// two bf16 matrix-core steps
+DEV uint32_t qi_off(uint32_t m, uint32_t h, uint32_t d, uint32_t nh) {
+  return ((m * (nh >> 4) + (h >> 4)) * 4u + 2u * (d >> 6) + ((d >> 3) & 1u)) * 1024u +
+         ((h & 15u) + 16u * ((d & 63u) >> 4)) * 16u + (d & 7u) * 2u;
+}
+
+// D1 finalize of one head on the eight waves: thread t takes the RoPE pairs (i, i + 64) of tokens
+// m = t / 64 and m + 8, i = t % 64: q = (sum of the head's two tiles' chunks) x the token's q_a scale,
+// rotated at the token's position, then bf16 into the score operand order
+DEV void fin_qi(const KArgs& a, const Instr& in, int wv) {
+  const Shapes& sh = a.sh;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t h = in.w[W_LAYER + 2], nk = in.w[W_LAYER + 5];
+  const uint32_t t = (uint32_t)wv * 64u + lane(), i = t & 63u, M = (uint32_t)sh.M;
+  const uint32_t ms[2] = {t >> 6, (t >> 6) + 8u};
+  __amdgpu_buffer_rsrc_t rp = rsrc((const float*)s_ld64(row + FN_PART) + (size_t)2u * h * nk * 1024);
+  __amdgpu_buffer_rsrc_t rs = rsrc((const void*)s_ld64(row + FN_SA));
+  __amdgpu_buffer_rsrc_t rr = rsrc((const void*)s_ld64(row + FN_R1));
+  float x[2][2][4], sa[2], cs[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t m = min(ms[q], M - 1u);
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t kk = min((uint32_t)k, nk - 1u);
+        x[q][tl][k] = __uint_as_float(ld32(rp, (((uint32_t)tl * nk + kk) * 1024u + part_idx(m, i)) * 4u));
+      }
+    sa[q] = __uint_as_float(ld32(rs, m * 4u));
+    cs[q][0] = __uint_as_float(ld32(rr, (m * 64u + i) * 8u));
+    cs[q][1] = __uint_as_float(ld32(rr, (m * 64u + i) * 8u + 4u));
+  }
+  wait_vm0();
+  __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + FN_OUT));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (ms[q] >= M) continue;
+    float v[2];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+      float acc = x[q][tl][0];
+#pragma unroll
+      for (uint32_t k = 1; k < 4; ++k)
+        if (k < nk) acc += x[q][tl][k];
+      v[tl] = acc * sa[q];
+    }
+    const float y0 = v[0] * cs[q][0] - v[1] * cs[q][1], y1 = v[1] * cs[q][0] + v[0] * cs[q][1];
+    st16(ro, qi_off(ms[q], h, i, (uint32_t)sh.nh), bf16_bits(y0));
+    st16(ro, qi_off(ms[q], h, i + 64u, (uint32_t)sh.nh), bf16_bits(y1));
+  }
+  wait_vm0();
+}
+
+// The step's keys on the eight waves (rows m = wave and wave + 8): RoPE at the row's position (lane i:
+// the pair (i, i + 64)), per-token e4m3 with scale amax / 448, codes and scale into the key cache at
+// (block_table[r][pos / P], pos % P)
+DEV void kcache(const KArgs& a, const Instr& in, int wv) {
+  const Shapes& sh = a.sh;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t i = lane(), M = (uint32_t)sh.M, P = (uint32_t)sh.P;
+  __amdgpu_buffer_rsrc_t rk = rsrc((const void*)s_ld64(row + KC_K));
+  __amdgpu_buffer_rsrc_t rr = rsrc((const void*)s_ld64(row + KC_ROPE));
+  __amdgpu_buffer_rsrc_t rc = rsrc((const void*)s_ld64(row + KC_CACHE));
+  __amdgpu_buffer_rsrc_t rsc = rsrc((const void*)s_ld64(row + KC_SCALE));
+  const int32_t* bt = (const int32_t*)s_ld64(row + KC_BT);
+  const int32_t* pos = (const int32_t*)s_ld64(row + KC_POS);
+  for (uint32_t m = (uint32_t)wv; m < M; m += kNW) {
+    const float x0 = __uint_as_float(ld32(rk, (m * 128u + i) * 4u)), x1 = __uint_as_float(ld32(rk, (m * 128u + i + 64u) * 4u));
+    const float c = __uint_as_float(ld32(rr, (m * 64u + i) * 8u)), sn = __uint_as_float(ld32(rr, (m * 64u + i) * 8u + 4u));
+    wait_vm0();
+    const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
+    const float amax = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
+    const float sc = amax > 0.f ? amax / 448.f : 1.f;
+    const uint32_t p = (uint32_t)c_ld<int32_t>(pos + m), r = m / (uint32_t)sh.T;
+    const uint32_t page = (uint32_t)c_ld<int32_t>(bt + (size_t)r * sh.maxp + p / P);
+    const uint32_t slot = page * P + p % P;
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(e4m3x4(y0 / sc, 0.f, 0.f, 0.f) & 0xffu), rc, slot * 128u + i, 0, SC1);
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(e4m3x4(y1 / sc, 0.f, 0.f, 0.f) & 0xffu), rc, slot * 128u + i + 64u, 0, SC1);
+    if (i == 0) st32(rsc, slot * 4u, __float_as_uint(sc));
+  }
+  wait_vm0();
+}
+
+// controller, score tasks overlapping the step's own keys: those T keys (written by the key-cache
+// task this run) and their scales into the activation area (kScoreNewK, kScoreNewS)
+constexpr int kScoreNewK = 0;     // [T][128] e4m3
+constexpr int kScoreNewS = 1024;  // [T] fp32
+DEV void score_stage(const KArgs& a, const Instr& in, char* act) {
+  const Shapes& sh = a.sh;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t r = in.w[W_LAYER + 1], t1 = in.w[W_LAYER + 4], T = (uint32_t)sh.T, P = (uint32_t)sh.P;
+  const int32_t* pos = (const int32_t*)s_ld64(row + SC_POS);
+  const uint32_t ctx = (uint32_t)c_ld<int32_t>(pos + r * T + T - 1u) + 1u;
+  if (t1 <= ctx - T) return;  // no new key in this split
+  const int32_t* bt = (const int32_t*)s_ld64(row + SC_BT) + (size_t)r * sh.maxp;
+  const char* cache = (const char*)s_ld64(row + SC_CACHE);
+  const float* scale = (const float*)s_ld64(row + SC_SCALE);
+  // lane l: 16 bytes of new token l / 8 and the scale of new token l (per-lane block-table reads:
+  // the new tokens may straddle a page boundary)
+  const uint32_t ln = lane();
+  const uint32_t tk = ctx - T + min(ln >> 3, T - 1u), ts = ctx - T + min(ln, T - 1u);
+  const uint32_t sk_slot = (uint32_t)bt[tk / P] * P + tk % P, ss_slot = (uint32_t)bt[ts / P] * P + ts % P;
+  const float sj = __uint_as_float(ld32(rsrc(scale), ss_slot * 4u));
+  if (ln < 8u * T) lds_dma16_sc1(cache + (size_t)sk_slot * 128u + (ln & 7u) * 16u, (uint32_t)(uintptr_t)(lds_void*)(act + kScoreNewK));
+  wait_vm0();
+  if (ln < T) *(float*)(act + kScoreNewS + ln * 4u) = sj;
+}
+
+// Indexer score of one (request, key split) on the eight waves, wave j taking token m = r T + j:
+// its q (64 heads x 128, bf16) stays in registers as 16 A fragments; per 16 keys, two steps of dims
+// per 64 widen the keys' e4m3 bytes to bf16 for the matrix core (exact products, fp32 sums), then
+// score[t] = sum_h w[m][h] max(0, scale[t] (q_h . k_t)) -- the 4 rows of each 16-head block a lane
+// holds are weighted and added, then the four 16-lane rows -- -inf past the token's position.
+DEV void score_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
+  const Shapes& sh = a.sh;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t r = in.w[W_LAYER + 1], t0 = in.w[W_LAYER + 3], t1 = in.w[W_LAYER + 4];
+  const uint32_t T = (uint32_t)sh.T, nh = (uint32_t)sh.nh;
+  if ((uint32_t)wv >= T) return;
+  const int32_t* pos = (const int32_t*)s_ld64(row + SC_POS);
+  const uint32_t m = r * T + (uint32_t)wv, pm = (uint32_t)c_ld<int32_t>(pos + m);
+  const uint32_t ctx = (uint32_t)c_ld<int32_t>(pos + r * T + T - 1u) + 1u, new0 = ctx - T;
+  const uint32_t lim = min(t1, new0), nko = lim > t0 ? lim - t0 : 0u;
+  const uint32_t kb = (nko + 7u) >> 3;  // key blocks in the lease; the scale block follows
+  const uint32_t ln = lane(), j16 = ln & 15u, g = ln >> 4;
+  __amdgpu_buffer_rsrc_t rq = rsrc((const void*)s_ld64(row + SC_Q));
+  __amdgpu_buffer_rsrc_t rw = rsrc((const void*)s_ld64(row + SC_W));
+  u32x4 qa[4][4];
+  f32x4 wv4[4];
+#pragma unroll
+  for (uint32_t hb = 0; hb < 4; ++hb) {
+#pragma unroll
+    for (uint32_t f = 0; f < 4; ++f) qa[hb][f] = ld128(rq, ((m * (nh >> 4) + hb) * 4u + f) * 1024u + ln * 16u);
+    const u32x4 wq = ld128(rw, (m * nh + hb * 16u + 4u * g) * 4u);
+    wv4[hb] = f32x4{__uint_as_float(wq.x), __uint_as_float(wq.y), __uint_as_float(wq.z), __uint_as_float(wq.w)};
+  }
+  wait_vm0();
+  const char* ring = smem + kRingOff;
+  const char* act = smem + kActOff;
+  __amdgpu_buffer_rsrc_t ro = rsrc((const float*)s_ld64(row + SC_OUT) + (size_t)m * sh.smax);
+  const uint32_t ntok = t1 - t0;
+  for (uint32_t tb = 0; tb * 16u < ntok; ++tb) {
+    const uint32_t tt = t0 + tb * 16u + j16;
+    const uint32_t tc = min(tt, t1 - 1u);  // past the split: any of its keys, not stored
+    const char* kp;
+    float sk;
+    if (tc < new0) {
+      kp = ring + ring_off(lease, (tc - t0) * 128u + 16u * g);
+      sk = *(const float*)(ring + ring_off(lease, kb * 1024u + (tc - t0) * 4u));
+    } else {
+      kp = act + kScoreNewK + (tc - new0) * 128u + 16u * g;
+      sk = *(const float*)(act + kScoreNewS + (tc - new0) * 4u);
+    }
+    f32x4 d[4];
+#pragma unroll
+    for (uint32_t hb = 0; hb < 4; ++hb) d[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (uint32_t s2 = 0; s2 < 2; ++s2) {
+      const u32x4 kv = *(const u32x4*)(kp + 64u * s2);
+      const bf16x8 b0 = e4m3x8_bf16(kv.x, kv.y), b1 = e4m3x8_bf16(kv.z, kv.w);
+#pragma unroll
+      for (uint32_t hb = 0; hb < 4; ++hb) {
+        bf16x8 a0, a1;
+        __builtin_memcpy(&a0, &qa[hb][2u * s2], 16);
+        __builtin_memcpy(&a1, &qa[hb][2u * s2 + 1u], 16);
+        d[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, d[hb], 0, 0, 0);
+        d[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, d[hb], 0, 0, 0);
+      }
+    }
+    float p = 0.f;
+#pragma unroll
+    for (uint32_t hb = 0; hb < 4; ++hb) {
+      p += wv4[hb].x * fmaxf(0.f, sk * d[hb].x) + wv4[hb].y * fmaxf(0.f, sk * d[hb].y);
+      p += wv4[hb].z * fmaxf(0.f, sk * d[hb].z) + wv4[hb].w * fmaxf(0.f, sk * d[hb].w);
+    }
+    const float tot = rows_sum(p);
+    if (g == 0 && tt < t1) st32(ro, tt * 4u, __float_as_uint(tt <= pm ? tot : -INFINITY));
+  }
+  wait_vm0();
+}
+
 // the multi-row op body of one instruction on one of the eight waves (ATTN aside)
 DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const uint32_t op = in.w[W_OPCODE];
@@ -1350,7 +1583,8 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
     else norm_row<false>(a, in, smem, lease, wv);
   } else if (op == OP_FIN) {
     const uint32_t nk = in.w[W_LAYER + 5];
-    if (nk <= 4) fin_tile<4>(a, in, wv);
+    if (in.w[W_LAYER + 1] == K_QI) fin_qi(a, in, wv);
+    else if (nk <= 4) fin_tile<4>(a, in, wv);
     else if (nk <= 8) fin_tile<8>(a, in, wv);
     else if (nk <= 12) fin_tile<12>(a, in, wv);
     else fin_tile<kMaxChunks>(a, in, wv);
@@ -1358,6 +1592,10 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
     quant_row(a, in, smem, wv);
   } else if (op == OP_COMB) {
     comb_group(a, in, wv);
+  } else if (op == OP_KCACHE) {
+    kcache(a, in, wv);
+  } else if (op == OP_SCORE) {
+    score_tile(a, in, smem, lease, wv);
   }
 }
 
@@ -1365,11 +1603,12 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
 // instruction staged the same chunk and nothing has written the area since)
 DEV void gemm_stage(const KArgs& a, const Instr& in, char* act, uint64_t& staged) {
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
-  const uint32_t k0 = in.w[W_LAYER + 5];
+  const uint32_t k0 = in.w[W_LAYER + 5], kc = in.w[W_LAYER + 6];
   const uint32_t off = a.sh.fp8 ? (k0 >> 6) * 1024u : (k0 >> 5) * 1024u;
+  const uint32_t bytes = a.sh.fp8 ? (kc >> 6) * 1024u : (kc >> 5) * 1024u;  // at most kActABytes
   const char* src = (const char*)s_ld64(row + GM_ACT) + off;
   if ((uint64_t)src == staged) return;
-  stage(src, (uint32_t)kActABytes, act + kActA);
+  stage(src, bytes, act + kActA);
   wait_vm0();
   staged = (uint64_t)src;
 }
@@ -1703,6 +1942,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       ok = graph || wait_events(a, in, poll, wc);
       if (ok && op == OP_ATTN) ok = attn_stage(a, in, act, false, poll, sst);
       if (ok && op == OP_GEMM) gemm_stage(a, in, act, staged);
+      if (ok && op == OP_SCORE) score_stage(a, in, act);
       if (op != OP_GEMM) staged = 0;
     } else if (op == OP_ATTN)
       ok = attn_stage(a, in, act, !graph, poll, sst);

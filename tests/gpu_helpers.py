@@ -73,3 +73,30 @@ class QwenRun:
             self.plan.run_graph(self.tensors, multistream=multistream)
         self.plan.sync()
         torch.cuda.synchronize()
+
+
+class IndexerRun:
+    """Inputs, score output and workspace of one indexer-front plan on cuda:0."""
+
+    def __init__(self, cfg, inp, num_workers=0, flags=0):
+        self.cfg = cfg
+        ctx = [int(c) for c in inp["context_lens"]]
+        self.plan = mk.Plan(cfg, context_lens=ctx, num_workers=num_workers, flags=flags)
+        t = {k: to_device(v) for k, v in inp.items() if k in mk.INDEXER_TENSORS}
+        self.smax = max(ctx)
+        t["score_out"] = torch.full((cfg.m * self.smax,), float("nan"), dtype=torch.float32, device="cuda")
+        t["workspace"] = torch.zeros(self.plan.workspace_bytes() + 256, dtype=torch.uint8, device="cuda")
+        self.t = t
+        self.tensors = mk.indexer_pointers(t)
+
+    def region(self, name, dtype):
+        off, n = self.plan.region(name)
+        return self.t["workspace"][off:off + n].view(dtype)
+
+    def run(self, mode="mk", multistream=False):
+        if mode == "mk":
+            self.plan.run(self.tensors)
+        else:
+            self.plan.run_graph(self.tensors, multistream=multistream)
+        self.plan.sync()
+        torch.cuda.synchronize()

@@ -1,0 +1,131 @@
+"""GPU parity of the indexer front (A0 -> {B0, C0, B1} -> D1 -> E1) against the CPU oracle, through
+the C ABI: megakernel and both graph baselines.
+
+Tolerance: max abs error 6e-2 (the FP8 path) on the scores and the fp32 intermediates, against the
+oracle value before its output rounding; bf16 q passes when it is the bf16 rounding of a value within
+that error.  e4m3 codes: the dequantised value is within one code step of the oracle's value (a value
+at a rounding boundary may round the other way).  Key-cache writes: the written slot set is exact
+(every other byte of the cache and its scales is unchanged).  Scores: -inf exactly for keys after a
+token's position; all modes give the same bits.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import model
+from oracle.numerics import e4m3_decode
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+TOL = 6e-2
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def opnd_fp8_rows(buf: np.ndarray, K: int) -> np.ndarray:
+    return buf.view(np.uint8)[:16 * K].reshape(K // 64, 4, 16, 16).transpose(2, 0, 1, 3).reshape(16, K)
+
+
+def qi_rows(buf: np.ndarray, nh: int) -> np.ndarray:
+    """[16, nh, 128] float64 from the score's A-operand order: per (token, 16-head block, step f)
+    1 KiB, lane (h % 16) + 16 g holding dims 64 (f // 2) + 16 g + 8 (f % 2) + 0..7."""
+    a = buf.view(np.uint16)[:16 * nh * 128].reshape(16, nh // 16, 4, 4, 16, 8)  # [m, hb, f, g, hh, e]
+    d = np.arange(128)
+    f, g, e = 2 * (d // 64) + (d % 16) // 8, (d % 64) // 16, d % 8
+    out = a[:, :, f, g, :, e]  # [128 d, 16 m, hb, 16 hh] after advanced indexing
+    out = np.moveaxis(out, 0, -1).reshape(16, nh, 128)
+    return (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _ws(run, name, dtype=torch.uint8):
+    return run.region(name, dtype).cpu().numpy()
+
+
+def _codes_ok(codes, s, pre):
+    """Each dequantised code within one e4m3 step (32 at the top binade) of the oracle's value."""
+    return np.all(np.abs(e4m3_decode(codes) * s[:, None] - pre) <= s[:, None] * 32.0 + 1e-12)
+
+
+def _check(run, inp, ref, tag, intermediates=True):
+    from gpu_helpers import bf16_excess
+    cfg = run.cfg
+    M, H, qr, nh = cfg.m, cfg.hidden, cfg.idx_q_rank, cfg.idx_heads
+    ctx = inp["context_lens"]
+    pos = ref["pos"]
+    score = run.t["score_out"].cpu().numpy().astype(np.float64).reshape(M, run.smax)
+    worst = 0.0
+    for m in range(M):
+        c = int(ctx[m // cfg.tokens_per_request])
+        row, want = score[m, :c], ref["score_pre"][m, :c]
+        fin = np.arange(c) <= pos[m]
+        assert np.all(np.isneginf(row[~fin])), f"{tag}: row {m} keys after the position are not -inf"
+        assert np.all(np.isfinite(row[fin])), f"{tag}: row {m}"
+        worst = max(worst, float(np.max(np.abs(row[fin] - want[fin]))))
+    _say(f"  {tag}: score err {worst:.3e} (max |score| {np.abs(ref['score_pre'][np.isfinite(ref['score_pre'])]).max():.3g})")
+    assert worst <= TOL, f"{tag}: score err {worst}"
+    if not intermediates:
+        return
+    sh = _ws(run, "sh").view(np.float32)[:M].astype(np.float64)
+    assert np.allclose(sh, ref["sh"], rtol=1e-5), tag
+    assert _codes_ok(opnd_fp8_rows(_ws(run, "hq"), H)[:M], sh, ref["h_pre"]), tag
+    qa = _ws(run, "qa").view(np.float32)[:M * qr].astype(np.float64).reshape(M, qr)
+    assert np.max(np.abs(qa - ref["qa"])) <= TOL, tag
+    sqa = _ws(run, "sqa").view(np.float32)[:M].astype(np.float64)
+    assert np.allclose(sqa, ref["sqa"], rtol=1e-4), tag
+    assert _codes_ok(opnd_fp8_rows(_ws(run, "qaq"), qr)[:M], sqa, ref["qa_n"]), tag
+    w = _ws(run, "w").view(np.float32)[:M * nh].astype(np.float64).reshape(M, nh)
+    assert np.max(np.abs(w - ref["w_pre"])) <= TOL, tag
+    k = _ws(run, "k").view(np.float32)[:M * 128].astype(np.float64).reshape(M, 128)
+    assert np.max(np.abs(k - ref["k_lin"])) <= TOL, tag
+    qi = qi_rows(_ws(run, "qi"), nh)
+    assert bf16_excess(qi[:M], ref["qi_pre"], TOL) <= 0, tag
+    assert np.all(qi[M:] == 0), tag
+
+
+def _check_cache(run, inp, ref, kc0, ks0, tag):
+    cfg = run.cfg
+    kc = run.t["key_cache"].cpu().numpy()
+    ks = run.t["key_scale"].cpu().numpy().astype(np.float64)
+    mask = np.ones(kc.shape[:2], dtype=bool)
+    page, off = ref["slot_page"], ref["slot_off"]
+    mask[page, off] = False
+    assert np.array_equal(kc[mask], kc0[mask]) and np.array_equal(ks[mask], ks0[mask]), f"{tag}: other slots changed"
+    assert np.allclose(ks[page, off], ref["sk"], rtol=1e-5), tag
+    assert _codes_ok(kc[page, off], ks[page, off], ref["k_pre"]), tag
+
+
+def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True), ("mk", False)),
+          W=0, intermediates=True):
+    from gpu_helpers import IndexerRun
+    inp = make_inputs(cfg, seed=seed)
+    inp["context_lens"] = np.array(ctx, dtype=np.int32)
+    ref = model.run_indexer_front(cfg, inp)
+    kc0, ks0 = inp["key_cache"].copy(), inp["key_scale"].astype(np.float64).copy()
+    run = IndexerRun(cfg, inp, num_workers=W)
+    outs = []
+    for mode, ms in modes:
+        _say(f"case: {cfg.name} R={cfg.n_requests} T={cfg.tokens_per_request} ctx={ctx} W={W} {mode} ms={ms}")
+        run.t["score_out"].fill_(float("nan"))
+        run.run(mode, ms)
+        _check(run, inp, ref, f"{mode}/{ms}", intermediates)
+        _check_cache(run, inp, ref, kc0, ks0, f"{mode}/{ms}")
+        outs.append(run.t["score_out"].clone())
+    for o in outs[1:]:
+        assert torch.equal(torch.nan_to_num(o), torch.nan_to_num(outs[0]))
+
+
+@pytest.mark.parametrize("R,T,ctx,W", [(2, 8, [300, 133], 0), (3, 5, [64, 196, 5], 37)])
+def test_indexer_reduced(R, T, ctx, W):
+    cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, n_requests=R,
+                              tokens_per_request=T, context=max(ctx))
+    _case(cfg, ctx, seed=11, W=W)
+
+
+def test_indexer_full_size():
+    cfg = get_config("indexer_front")
+    _case(cfg, [cfg.context] * cfg.n_requests, seed=0, modes=(("mk", False), ("graph", True)))
