@@ -63,7 +63,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_0p6b_step",
-                    choices=["qwen3_0p6b_step", "qwen3_0p6b_layer", "qwen3_8b_layer", "qwen3_8b_layer_fp8"])
+                    choices=["qwen3_0p6b_step", "qwen3_0p6b_layer", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
+                             "indexer_front"])
     ap.add_argument("--rotate", type=int, default=0, help="copies of weights/caches cycled per run (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
@@ -89,7 +90,8 @@ def main() -> int:
     cfg = get_config(args.workload)
     # rotation copies keep the timed runs from being served out of the 256 MiB MALL: the full step
     # and the 16-token layers are larger than it on their own (two copies for the layers)
-    rotate = args.rotate or (1 if cfg.workload == "qwen3_step" else 2 if cfg.m > 1 else 16)
+    indexer = cfg.workload == "indexer_front"
+    rotate = args.rotate or (1 if cfg.workload == "qwen3_step" else 20 if indexer else 2 if cfg.m > 1 else 16)
     _log(f"bench: workload {cfg.name}, rotate {rotate}, generating inputs")
     t0 = time.time()
     inp = make_inputs(cfg, seed=0)
@@ -118,6 +120,11 @@ def main() -> int:
     tensor_sets = []
     for s in sets:
         s = dict(s)
+        if indexer:  # scores [M, context] and the workspace
+            s["score_out"] = torch.zeros(M * cfg.context, dtype=torch.float32, device="cuda")
+            s["workspace"] = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+            tensor_sets.append(mk.indexer_pointers(s))
+            continue
         s["y_out"] = torch.zeros(M * H, dtype=torch.int16, device="cuda")
         s["r2_out"] = torch.zeros(M * H, dtype=torch.float32, device="cuda")
         s["workspace"] = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -172,17 +179,21 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "fp8-e4m3 (bf16 MFMA products, fp32 sums)" if cfg.weight_fp8 else "bf16",
         "data": "synthetic (seeded random weights and KV caches of the workload's shapes)",
-        "config": {"workload": cfg.name, "layers": layers, "hidden": cfg.hidden, "inter": cfg.inter,
-                   "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
-                   "batch": cfg.n_requests, "context": cfg.context, "page_size": cfg.page_size,
-                   "vocab": cfg.vocab, "rotation_copies": rotate, "workers": int(p0.queue().shape[0])},
+        "config": ({"workload": cfg.name, "hidden": cfg.hidden, "q_rank": cfg.idx_q_rank, "heads": cfg.idx_heads,
+                    "head_dim": cfg.idx_head_dim, "requests": cfg.n_requests, "tokens_per_request": cfg.tokens_per_request,
+                    "context": cfg.context, "page_size": cfg.page_size, "rotation_copies": rotate,
+                    "workers": int(p0.queue().shape[0])} if indexer else
+                   {"workload": cfg.name, "layers": layers, "hidden": cfg.hidden, "inter": cfg.inter,
+                    "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                    "batch": cfg.n_requests, "context": cfg.context, "page_size": cfg.page_size,
+                    "vocab": cfg.vocab, "rotation_copies": rotate, "workers": int(p0.queue().shape[0])}),
         "step_us": round(step_us, 3),
         "achieved_GBps": round(achieved, 1),
         "hbm_frac_of_8TBps": round(achieved / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _counter_traffic(cfg.name),
-                     "kernel": "mk_worker (persistent megakernel, one launch per step)"},
+                     "kernel": "mk_worker<%d> (persistent megakernel, one launch per step)" % (1 if cfg.m > 1 else 0)},
         "variants_us_per_step": variants,
     }
     if variants:
@@ -202,6 +213,8 @@ def main() -> int:
         t0 = time.perf_counter()
         if step:
             omodel.run_qwen3_step(cfg, inp)
+        elif indexer:
+            omodel.run_indexer_front(cfg, inp)
         else:
             omodel.run_qwen3_layer(cfg, inp)
         dt = time.perf_counter() - t0
