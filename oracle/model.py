@@ -42,15 +42,31 @@ def _w(inp: Dict[str, np.ndarray], name: str, layer: int, cfg) -> np.ndarray:
     return bf16_bits_to_f64(inp[name][layer])
 
 
+def _quant(pre: np.ndarray, key: str, decide) -> tuple:
+    """Per-token e4m3 quantisation of ``pre``, or the (codes, scales) that ``decide[key]`` holds.
+
+    A value within rounding of a code boundary may be coded either way by an evaluation that
+    sums in another order; a code step at the top binade is 1/14 of the row's largest value and
+    reaches every output of the next projection.  ``decide`` lets a caller continue the chain from
+    another evaluation's codes (checked by that caller to lie within one code step of ``pre``), so
+    that the rest of the chain is compared for the same decisions."""
+    if decide is not None and key in decide:
+        codes, s = decide[key]
+        return np.asarray(codes, dtype=np.uint8), np.asarray(s, dtype=np.float64)
+    return quant_per_token(pre)
+
+
 def _w8a8(cfg, inp, name, layer, codes, scale):
     return ops.linear_w8a8(e4m3_decode(codes), scale, e4m3_decode(inp[name][layer]), inp["s_" + name[2:]][layer])
 
 
 def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in: np.ndarray,
-                k_cache: np.ndarray, v_cache: np.ndarray) -> Dict[str, np.ndarray]:
+                k_cache: np.ndarray, v_cache: np.ndarray, decide=None) -> Dict[str, np.ndarray]:
     """One decode layer.  x: decoded bf16 values [M, H]; r_in: fp32 values [M, H].
     k_cache / v_cache: this layer's decoded caches [pages, P, Hkv, d] (updated in place
-    with the new rows).  Rows are requests (one token per request)."""
+    with the new rows).  Rows are requests (one token per request).
+    decide: optional FP8 codes and scales {"h1q", "oq", "h2q", "mq": (codes, s)} taken in place of
+    this layer's own quantisation at those points (see ``_quant``)."""
     H, d = cfg.hidden, cfg.head_dim
     Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
     g = Hq // Hkv
@@ -66,7 +82,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     out["r1"] = r1
     out["h1_pre"] = h1_pre
     if fp8:
-        h1q, s1 = quant_per_token(h1_pre)
+        h1q, s1 = _quant(h1_pre, "h1q", decide)
         out["h1q"], out["s1"] = h1q, s1
         qkv = _w8a8(cfg, inp, "w_qkv", layer, h1q, s1)
     else:
@@ -100,7 +116,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     o_pre = o_pre.reshape(M, Hq * d)
     out["o_pre"] = o_pre
     if fp8:
-        oq, so = quant_per_token(o_pre)
+        oq, so = _quant(o_pre, "oq", decide)
         out["oq"], out["so"] = oq, so
         a_pre = _w8a8(cfg, inp, "w_o", layer, oq, so)
     else:
@@ -115,7 +131,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     out["h2_pre"] = h2_pre
     I = cfg.inter
     if fp8:
-        h2q, s2 = quant_per_token(h2_pre)
+        h2q, s2 = _quant(h2_pre, "h2q", decide)
         out["h2q"], out["s2"] = h2q, s2
         gu = _w8a8(cfg, inp, "w_gu", layer, h2q, s2)
     else:
@@ -125,7 +141,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     m_pre = ops.silu_mul(gu[:, :I], gu[:, I:])
     out["m_pre"] = m_pre
     if fp8:
-        mq, sm = quant_per_token(m_pre)
+        mq, sm = _quant(m_pre, "mq", decide)
         out["mq"], out["sm"] = mq, sm
         y_pre = _w8a8(cfg, inp, "w_down", layer, mq, sm)
     else:
@@ -137,12 +153,12 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     return out
 
 
-def run_qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int = 0) -> Dict[str, np.ndarray]:
+def run_qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int = 0, decide=None) -> Dict[str, np.ndarray]:
     """Single-layer workload: returns the layer outputs and the updated caches (decoded)."""
     k_cache = bf16_bits_to_f64(inp["k_cache"][layer])
     v_cache = bf16_bits_to_f64(inp["v_cache"][layer])
     out = qwen3_layer(cfg, inp, layer, bf16_bits_to_f64(inp["x"]), inp["r_in"].astype(np.float64),
-                      k_cache, v_cache)
+                      k_cache, v_cache, decide)
     out["k_cache"], out["v_cache"] = k_cache, v_cache
     return out
 
@@ -172,7 +188,8 @@ def run_qwen3_step(cfg, inp: Dict[str, np.ndarray], keep_layers: bool = False) -
     return res
 
 
-def run_indexer_front(cfg, inp: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+def run_indexer_front(cfg, inp: Dict[str, np.ndarray], decide=None) -> Dict[str, np.ndarray]:
+    """decide: optional FP8 codes and scales {"hq", "qaq", "kq": (codes, s)} (see ``_quant``)."""
     H, qr, nh, hd = cfg.hidden, cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
     R, T = cfg.n_requests, cfg.tokens_per_request
     M = R * T
@@ -186,12 +203,12 @@ def run_indexer_front(cfg, inp: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
 
     r1 = ops.add_residual(bf16_bits_to_f64(inp["x"]), inp["r_in"].astype(np.float64))
     h_pre = ops.rmsnorm(r1, bf16_bits_to_f64(inp["g_norm"]), cfg.rms_eps)
-    hq, sh = quant_per_token(h_pre)
+    hq, sh = _quant(h_pre, "hq", decide)
     out.update(r1=r1, h_pre=h_pre, hq=hq, sh=sh)
     # B0
     qa = w8a8("w_qa", hq, sh)
     qa_n = ops.rmsnorm(qa, bf16_bits_to_f64(inp["g_qa"]), cfg.rms_eps)
-    qaq, sqa = quant_per_token(qa_n)
+    qaq, sqa = _quant(qa_n, "qaq", decide)
     out.update(qa=qa, qa_n=qa_n, qaq=qaq, sqa=sqa)
     # C0
     w_pre = w8a8("w_w", hq, sh)
@@ -200,7 +217,7 @@ def run_indexer_front(cfg, inp: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     # B1
     k_lin = w8a8("w_k", hq, sh)
     k_pre = ops.rope_neox(k_lin, pos, cfg.rope_theta)
-    kq, sk = quant_per_token(k_pre)
+    kq, sk = _quant(k_pre, "kq", decide)
     out.update(k_lin=k_lin, k_pre=k_pre, kq=kq, sk=sk)
     page, off = ops.cache_slots(inp["block_table"], pos, req, cfg.page_size)
     key_cache = inp["key_cache"].copy()

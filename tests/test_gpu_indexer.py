@@ -3,8 +3,9 @@ the C ABI: megakernel and both graph baselines.
 
 Tolerance: max abs error 6e-2 (the FP8 path) on the scores and the fp32 intermediates, against the
 oracle value before its output rounding; bf16 q passes when it is the bf16 rounding of a value within
-that error.  e4m3 codes: the dequantised value is within one code step of the oracle's value (a value
-at a rounding boundary may round the other way).  Key-cache writes: the written slot set is exact
+that error.  e4m3 codes: each is one of the two codes enclosing the oracle's value (a value at a
+rounding boundary may be coded either way by an evaluation that sums in another order), and the
+oracle then continues from the GPU's codes, so that what follows is compared for the same decisions.  Key-cache writes: the written slot set is exact
 (every other byte of the cache and its scales is unchanged).  Scores: -inf exactly for keys after a
 token's position; all modes give the same bits.
 """
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 from oracle import model
-from oracle.numerics import e4m3_decode
+from oracle.numerics import quant_per_token
 from workloads import get_config, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -47,8 +48,29 @@ def _ws(run, name, dtype=torch.uint8):
 
 
 def _codes_ok(codes, s, pre):
-    """Each dequantised code within one e4m3 step (32 at the top binade) of the oracle's value."""
-    return np.all(np.abs(e4m3_decode(codes) * s[:, None] - pre) <= s[:, None] * 32.0 + 1e-12)
+    from gpu_helpers import e4m3_codes_ok
+    return e4m3_codes_ok(codes, s, pre)
+
+
+def _oracle(run, inp):
+    """The oracle continued from the GPU's codes at hq, qaq and the new keys, each checked to be one of
+    the two codes enclosing the oracle's value there."""
+    cfg = run.cfg
+    M, H, qr = cfg.m, cfg.hidden, cfg.idx_q_rank
+    slots = model.run_indexer_front(cfg, inp)  # cache slots (they depend on no decision)
+    page, off = slots["slot_page"], slots["slot_off"]
+    dec = {"hq": (opnd_fp8_rows(_ws(run, "hq"), H)[:M], _ws(run, "sh").view(np.float32)[:M].astype(np.float64)),
+           "qaq": (opnd_fp8_rows(_ws(run, "qaq"), qr)[:M], _ws(run, "sqa").view(np.float32)[:M].astype(np.float64)),
+           "kq": (run.t["key_cache"].cpu().numpy()[page, off],
+                  run.t["key_scale"].cpu().numpy().astype(np.float64)[page, off])}
+    ref = model.run_indexer_front(cfg, inp, decide=dec)
+    for key, pre in (("hq", "h_pre"), ("qaq", "qa_n"), ("kq", "k_pre")):
+        codes, s = dec[key]
+        own, s_own = quant_per_token(ref[pre])
+        assert np.allclose(s, s_own, rtol=1e-4), f"{key} scales"
+        assert _codes_ok(codes, s, ref[pre]), f"{key}: a code is not one enclosing the oracle's value"
+        _say(f"  {key}: {int(np.sum(codes != own))} of {codes.size} codes on the other side of a boundary")
+    return ref
 
 
 def _check(run, inp, ref, tag, intermediates=True):
@@ -104,14 +126,16 @@ def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True
     from gpu_helpers import IndexerRun
     inp = make_inputs(cfg, seed=seed)
     inp["context_lens"] = np.array(ctx, dtype=np.int32)
-    ref = model.run_indexer_front(cfg, inp)
     kc0, ks0 = inp["key_cache"].copy(), inp["key_scale"].astype(np.float64).copy()
     run = IndexerRun(cfg, inp, num_workers=W)
     outs = []
+    ref = None
     for mode, ms in modes:
         _say(f"case: {cfg.name} R={cfg.n_requests} T={cfg.tokens_per_request} ctx={ctx} W={W} {mode} ms={ms}")
         run.t["score_out"].fill_(float("nan"))
         run.run(mode, ms)
+        if ref is None:  # every mode gives the same bits (checked below)
+            ref = _oracle(run, inp)
         _check(run, inp, ref, f"{mode}/{ms}", intermediates)
         _check_cache(run, inp, ref, kc0, ks0, f"{mode}/{ms}")
         outs.append(run.t["score_out"].clone())

@@ -112,3 +112,28 @@ def test_indexer_front_consistency():
     kq = nu.e4m3_decode(o["kq"][mi]) * o["sk"][mi]
     ref = np.sum(o["w"][mi] * np.maximum(0, o["qi"][mi] @ kq))
     assert abs(o["score"][mi, o["pos"][mi]] - ref) < 1e-3 * max(1, abs(ref))
+
+
+def test_fp8_decisions_taken_from_the_caller():
+    """The FP8 layer continues from codes a caller supplies: its own codes reproduce it exactly, and
+    one code moved to its neighbour changes y by that step times the dequantised down-projection
+    column (the layer is linear in the down projection's input)."""
+    cfg = dataclasses.replace(_small_cfg(), weight_fp8=True, act_fp8=True, hidden=256, inter=512)
+    inp = make_inputs(cfg, seed=9)
+    own = model.run_qwen3_layer(cfg, inp)
+    dec = {k: (own[k], own["s" + n]) for k, n in (("h1q", "1"), ("oq", "o"), ("h2q", "2"), ("mq", "m"))}
+    same = model.run_qwen3_layer(cfg, inp, decide=dec)
+    for key in ("y_pre", "r2", "o_pre", "m_pre", "qkv"):
+        assert np.array_equal(same[key], own[key]), key
+    mq = own["mq"].copy()
+    row, col = 1, int(np.argmax(np.abs(nu.e4m3_decode(own["mq"][1]))))
+    code = int(mq[row, col])
+    mq[row, col] = code - 1 if code & 0x7F else code + 1  # the neighbouring code toward zero (or away from it)
+    dec["mq"] = (mq, own["sm"])
+    moved = model.run_qwen3_layer(cfg, inp, decide=dec)
+    step = (nu.e4m3_decode(np.array([mq[row, col]], np.uint8))[0] - nu.e4m3_decode(np.array([code], np.uint8))[0])
+    w_col = nu.dequant_weight_blocks(inp["w_down"][0], inp["s_down"][0])[:, col]
+    want = own["y_pre"].copy()
+    want[row] += step * own["sm"][row] * w_col
+    assert np.allclose(moved["y_pre"], want, rtol=0, atol=1e-12)
+    assert np.array_equal(moved["y_pre"][0], own["y_pre"][0])  # other rows untouched
