@@ -65,15 +65,14 @@ constexpr int kMaxG = 5;       // GQA group (q heads per kv head) of the M = 1 a
 constexpr int kActQ = 0;       // bf16 [g][128] rotated q heads
 constexpr int kActK = 2048;    // bf16 [128] new key
 constexpr int kActV = 2304;    // bf16 [128] new value
-constexpr int kActMerge = 2560;  // fp32 [7 waves][g][128] per-wave partial P V (<= 17920 bytes)
+constexpr int kActMerge = 2560;  // fp32 [8 waves][g][128] per-wave partial P V, then (m_w, l_w)
 constexpr int kAttGq = 2560;     // q and k norm gains (bf16 [128] each) and the request's RoPE row
 constexpr int kAttGk = 2816;     // (fp32 (cos, sin) [64]): read in the first phase, before the merge
 constexpr int kAttRope = 3072;   // area they share is written
 constexpr int kAttQraw = 4096;   // tagged records of the raw q heads (g KiB), k and v (1 KiB each);
 constexpr int kAttKraw = kAttQraw + kMaxG * 1024;  // consumed before the merge area is written
 constexpr int kAttVraw = kAttKraw + 1024;
-constexpr int kAttS = 21504;     // fp32 [g][128] scores
-constexpr int kAttP = kAttS + kMaxG * 512;  // fp32 [7 waves][g][20] exponentials of each wave's tokens
+constexpr int kAttP = kActMerge + 8 * kMaxG * 130 * 4;  // fp32 [8 waves][g][16] exponentials of each wave's tokens
 constexpr int kActR1 = kActBytes - 1024;    // O projection / down: residual rows of the tile as records (<= 128)
 // multi-row ops in the activation staging area: a projection tile's input chunk (16 rows x one K
 // chunk in operand order, 16 KiB), the eight waves' 16 x 16 fp32 results, reduction scratch
@@ -82,10 +81,9 @@ constexpr int kActABytes = 16384;
 constexpr int kActD = kActA + kActABytes;   // [8 waves][64 lanes][4] fp32
 constexpr int kActRed = kActD + 8192;       // [2][8] fp32 per-wave partial reductions
 static_assert(kActRed + 64 <= kActBytes, "multi-row staging overflows the activation area");
-static_assert(kActMerge + 7 * kMaxG * 130 * 4 <= kAttS, "attention merge area overlaps the scores");
-static_assert(kAttVraw + 1024 <= kAttS, "attention staging overlaps the scores");
+static_assert(kAttVraw + 1024 <= kAttP, "attention staging overlaps the exponentials");
 static_assert(kAttRope + 512 <= kAttQraw, "attention gains overlap the raw q staging");
-static_assert(kAttP + 7 * kMaxG * 20 * 4 <= kActBytes, "attention exponentials overflow the staging area");
+static_assert(kAttP + 8 * kMaxG * 16 * 4 <= kActBytes, "attention exponentials overflow the staging area");
 static_assert(kLdsBytes == 163840, "LDS budget");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 }  // namespace dev

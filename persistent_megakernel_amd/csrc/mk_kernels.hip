@@ -184,6 +184,9 @@ DEV float ll_f32(const char* base, int k) { return *(const float*)(base + 8 * k)
 
 DEV void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// the wave's own LDS writes done, and no LDS access moved across this point (a wave-private
+// exchange between lanes: LDS serves one wave's accesses in order once they are issued)
+DEV void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // wait until at most n vector-memory operations of this wave are outstanding
 DEV void wait_vm_le(uint32_t n) {
@@ -827,18 +830,19 @@ DEV void qk_norm_rope(const char* raw, const char* gn, const char* rope, float e
   ((uint16_t*)dst)[i + 64] = (uint16_t)(o >> 16);
 }
 
-// split-KV attention partial for one (request, kv head, split) over its G query heads, in three
-// phases separated by block barriers:
-//   1. scores: 16-lane rows over the split's tokens (row R takes tokens R, R + 28, ...), lane
-//      `sub` holding dims [8 sub, 8 sub + 8); four tokens of a row are summed over its lanes at
-//      once by the transposing butterfly;
-//   2. per head and wave, the maximum over the wave's own phase-3 tokens and their exponentials
-//      into a wave-private table;
-//   3. P V: lanes over dimension pairs, waves over tokens (wave w takes tokens w, w + 7, ...);
-//      the seven waves' partial outputs and sums merge with weights exp(m_w - max m_w).
+// split-KV attention partial for one (request, kv head, split) over its G query heads, on all eight
+// waves (wv 0..6 the compute waves, 7 the controller: two per SIMD), with two block barriers:
+//   0. QK-norm + RoPE once per head (wave j < G: q head j, wave G: the new key, wave G + 1: the new
+//      value, bf16) into LDS;
+//   1. wave wv takes a contiguous block of at most 16 of the split's tokens: its four 16-lane rows take
+//      one token each at a time for the scores (lane `sub` holding dims [8 sub, 8 sub + 8), a 16-lane
+//      sum); the wave's maximum m_w per head (read from the four rows), the exponentials into a
+//      wave-private table (no block barrier: only this wave reads it), then P V on all 64 lanes, one
+//      token at a time (two dims per lane);
+//   2. the eight waves' (m_w, l_w, O_w) merge with weights exp(m_w - max m_w).
 // Output: the split's normalised O [G][128] and its lse [G] in the output area.
 template <int G, int S>
-DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int cw) {
+DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int wv) {
   const Shapes& sh = a.sh;
   const int s = in.w[W_P3], t0 = in.w[W_P4], t1 = in.w[W_P5];
   const bool last = s == attn_splits<S>(in) - 1;
@@ -848,103 +852,89 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
   const uint32_t voff = nbk * 1024u;      // lease: K | V
   const char* ring = smem + kRingOff;
   const int ln = (int)lane();
-  const float scale = sh.inv_sqrt_d;
-  // phase 0: QK-norm + RoPE once per head: wave j < G takes q head j, wave G the new key, wave
-  // G + 1 the new value (bf16); the results (also the new cache row) go to LDS
-  if (cw < G) {
-    qk_norm_rope(act + kAttQraw + cw * 1024, act + kAttGq, act + kAttRope, sh.eps, act + kActQ + cw * 256);
-  } else if (cw == G) {
+  if (wv < G) {
+    qk_norm_rope(act + kAttQraw + wv * 1024, act + kAttGq, act + kAttRope, sh.eps, act + kActQ + wv * 256);
+  } else if (wv == G) {
     qk_norm_rope(act + kAttKraw, act + kAttGk, act + kAttRope, sh.eps, act + kActK);
-  } else if (cw == G + 1) {
+  } else if (wv == G + 1) {
     const char* vr = act + kAttVraw;  // tagged records
     ((uint32_t*)(act + kActV))[ln] = pack_bf2(ll_f32(vr, 2 * ln), ll_f32(vr, 2 * ln + 1));
   }
   lds_barrier();
-  // phase 1: scores into LDS (the raw q area is free now)
-  float* sc = (float*)(act + kAttS);  // [G][128]
-  {
-    const int sub = ln & 15, rowid = cw * 4 + (ln >> 4);
-    u32x4 qv[G], kv[5];
+  const int sub = ln & 15, rw = ln >> 4;
+  const int per = (ntok + kNW - 1) / kNW;  // <= 16 tokens per wave: four rounds of four rows
+  const int tw0 = min(wv * per, ntok), tw1 = min(tw0 + per, ntok);
+  u32x4 qv[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) qv[j] = *(const u32x4*)(act + kActQ + j * 256 + sub * 16);
+  for (int j = 0; j < G; ++j) qv[j] = *(const u32x4*)(act + kActQ + j * 256 + sub * 16);
+  const float scale = sh.inv_sqrt_d;
+  float sc[4][G];
 #pragma unroll
-    for (int it = 0; it < 5; ++it) {  // 5 * 28 >= 128 tokens; a row past the end reloads the last
-      const int u = min(rowid + it * kNCW * 4, ntok - 1);
-      kv[it] = *(const u32x4*)(u < nk ? ring + ring_off(lease, (uint32_t)u * 256u + sub * 16u) : act + kActK + sub * 16);
-    }
+  for (int k = 0; k < 4; ++k) {
+    const int t = tw0 + 4 * k + rw;
+    const int tc = min(t, ntok - 1);  // past the wave's block: any valid token, masked
+    const u32x4 kv = *(const u32x4*)(tc < nk ? ring + ring_off(lease, (uint32_t)tc * 256u + sub * 16u) : act + kActK + sub * 16);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const float v = butterfly4(dot8(kv[0], qv[j], 0.f), dot8(kv[1], qv[j], 0.f), dot8(kv[2], qv[j], 0.f),
-                                 dot8(kv[3], qv[j], 0.f), sub);
-      const int u = rowid + (sub >> 2) * kNCW * 4;  // lanes 4i.. hold the row's token i
-      if ((sub & 3) == 0 && u < ntok) sc[j * 128 + u] = v * scale;
-      const float v4 = row16_sum(dot8(kv[4], qv[j], 0.f));
-      const int u4 = rowid + 4 * kNCW * 4;
-      if (sub == 0 && u4 < ntok) sc[j * 128 + u4] = v4 * scale;
+      const float v = row16_sum(dot8(kv, qv[j], 0.f)) * scale;
+      sc[k][j] = t < tw1 ? v : -INFINITY;
     }
   }
-  lds_barrier();
-  // phase 2: the wave's own tokens t = cw + 7 i (lane i < 20): per head the wave's maximum m_w and
-  // the exponentials exp(s - m_w) into the wave-private table pw[cw][j][i] (0 past the end)
+  float* pw = (float*)(act + kAttP) + wv * G * 16;  // [G][16] exponentials of the wave's tokens
   float mw[G];
-  float* pw = (float*)(act + kAttP) + cw * G * 20;
-  {
-    const int tw = cw + kNCW * ln;
-    const bool mine = ln < 20 && tw < ntok;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float sv = mine ? sc[j * 128 + tw] : -INFINITY;
-      mw[j] = wave_max(sv);  // -inf for a wave without tokens (ntok < 7); its weight is then 0
-      if (ln < 20) pw[j * 20 + ln] = mine ? __expf(sv - mw[j]) : 0.f;
+  for (int j = 0; j < G; ++j) {
+    float m = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
+    const int mi = __float_as_int(m);
+    mw[j] = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 0)), __int_as_float(__builtin_amdgcn_readlane(mi, 16))),
+                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 32)), __int_as_float(__builtin_amdgcn_readlane(mi, 48))));
+    if (sub == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pw[j * 16 + 4 * k + rw] = sc[k][j] == -INFINITY ? 0.f : __expf(sc[k][j] - mw[j]);
     }
   }
-  // phase 3: P V over the wave's tokens, four at a time; lane ln owns dims 2 ln, 2 ln + 1; the sum
-  // of the exponentials is wave-uniform
+  wave_lds_sync();
   float acc[G][2], lw[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = lw[j] = 0.f;
-  const int nw = ntok > cw ? (ntok - cw + kNCW - 1) / kNCW : 0;
-  for (int i = 0; i < nw; i += 4) {
-    uint32_t vw[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = min(cw + kNCW * (i + k), ntok - 1);  // past the end: any valid token, weight 0
-      vw[k] = *(const uint32_t*)(t < nk ? ring + ring_off(lease, voff + (uint32_t)t * 256u + ln * 4u) : act + kActV + ln * 4);
-    }
+  for (int k = 0; k < 4; ++k) {
+    if (tw0 + 4 * k >= tw1) break;
+    f32x4 pk[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const f32x4 pj = *(const f32x4*)(pw + j * 20 + i);
-      const float pk[4] = {pj.x, pj.y, pj.z, pj.w};
-      lw[j] += (pk[0] + pk[1]) + (pk[2] + pk[3]);
+    for (int j = 0; j < G; ++j) pk[j] = *(const f32x4*)(pw + j * 16 + 4 * k);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[j][0] += pk[k] * bf2f(vw[k] & 0xffffu);
-        acc[j][1] += pk[k] * bf2f(vw[k] >> 16);
+    for (int r = 0; r < 4; ++r) {
+      const int t = min(tw0 + 4 * k + r, ntok - 1);  // past the block: weight 0 from the table
+      const uint32_t vw = *(const uint32_t*)(t < nk ? ring + ring_off(lease, voff + (uint32_t)t * 256u + ln * 4u) : act + kActV + ln * 4);
+      const float v0 = bf2f(vw & 0xffffu), v1 = bf2f(vw >> 16);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float pj = pk[j][r];
+        lw[j] += pj;
+        acc[j][0] += pj * v0;
+        acc[j][1] += pj * v1;
       }
     }
   }
   float* mrg = (float*)(act + kActMerge);  // [wave][G][128] partial P V, then [wave][G] (m_w, l_w)
-  float* ml = mrg + kNCW * G * 128;
+  float* ml = mrg + kNW * G * 128;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const f32x2 v = {acc[j][0], acc[j][1]};
-    *(f32x2*)(mrg + (cw * G + j) * 128 + 2 * ln) = v;
-    if (ln == 0) {
-      const f32x2 st = {nw > 0 ? mw[j] : -INFINITY, lw[j]};
-      *(f32x2*)(ml + (cw * G + j) * 2) = st;
-    }
+    *(f32x2*)(mrg + (wv * G + j) * 128 + 2 * ln) = f32x2{acc[j][0], acc[j][1]};
+    if (ln == 0) *(f32x2*)(ml + (wv * G + j) * 2) = f32x2{tw1 > tw0 ? mw[j] : -INFINITY, lw[j]};
   }
   lds_barrier();
-  // merge the seven waves: weights exp(m_w - M) with M the largest m_w; lane o = j * 128 + d
+  // merge the eight waves: weights exp(m_w - M) with M the largest m_w; lane o = j * 128 + d
   float* out = (float*)(smem + kOutOff);
-  for (int o = cw * 64 + ln; o < G * 128; o += kNCW * 64) {
+  for (int o = wv * 64 + ln; o < G * 128; o += kNW * 64) {
     const int j = o >> 7, d = o & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kNCW; ++w) M = fmaxf(M, ml[(w * G + j) * 2]);
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, ml[(w * G + j) * 2]);
     float O = 0.f, L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNCW; ++w) {
+    for (int w = 0; w < kNW; ++w) {
       const float mv = ml[(w * G + j) * 2];
       const float e = mv == -INFINITY ? 0.f : __expf(mv - M);
       O += e * mrg[(w * G + j) * 128 + d];
@@ -1905,12 +1895,6 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
 // ---------------------------------------------------------------------------------------
 // the two roles
 
-// barriers between the compute-start and compute-end barriers: attention (QK-norm / RoPE,
-// scores, P V)
-// (the fused norm's barrier of a projection is taken inside proj_body; with every op body
-// skipped, no wave takes any)
-DEV int inner_barriers(uint32_t op, bool noop_only) { return op == OP_ATTN && !noop_only ? 3 : 0; }
-
 template <int S>
 DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride, char* smem) {
   uint32_t* ctrl = (uint32_t*)(smem + kCtrlOff);  // LDS; read and written only across barriers
@@ -1961,14 +1945,14 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     const unsigned long long t_a = tracing ? rtc() : 0;
     const unsigned long long c_a = tracing ? __builtin_readcyclecounter() : 0;
     if (!ok) break;
-    if (op != OP_ATTN && !noop_only) {  // the controller is the eighth wave of a projection tile
+    if (!noop_only) {  // the controller is the eighth wave of every op body
       const uint32_t lease = uni(((const uint32_t*)(smem + kCtrlOff + kLeaseTabOff))[i & 15]);  // compute wave 0's table
-      if constexpr (m16)
+      if (op == OP_ATTN)
+        attn_compute<S>(a, in, smem, act, lease, kNW - 1);
+      else if constexpr (m16)
         m16_body(a, in, smem, lease, kNW - 1);
       else
         proj_body(a, in, smem, lease, fused_norm, kNW - 1);
-    } else {
-      for (int b = 0; b < inner_barriers(op, noop_only); ++b) lds_barrier();
     }
     lds_barrier();  // B: compute done, results in the output area
     const unsigned long long t_b = tracing ? rtc() : 0;
@@ -2064,8 +2048,6 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       } else {
         proj_body(a, in, smem, lease, fused_norm, cw);
       }
-    } else {
-      for (int b = 0; b < inner_barriers(op, noop_only); ++b) lds_barrier();
     }
     last_row = in.w[W_ROW];
     lds_barrier();  // B
