@@ -72,7 +72,6 @@ constexpr int kAttRope = 3072;   // area they share is written
 constexpr int kAttQraw = 4096;   // tagged records of the raw q heads (g KiB), k and v (1 KiB each);
 constexpr int kAttKraw = kAttQraw + kMaxG * 1024;  // consumed before the merge area is written
 constexpr int kAttVraw = kAttKraw + 1024;
-constexpr int kAttP = kActMerge + 8 * kMaxG * 130 * 4;  // fp32 [8 waves][g][16] exponentials of each wave's tokens
 constexpr int kActR1 = kActBytes - 1024;    // O projection / down: residual rows of the tile as records (<= 128)
 // multi-row ops in the activation staging area: a projection tile's input chunk (16 rows x one K
 // chunk in operand order, 16 KiB), the eight waves' 16 x 16 fp32 results, reduction scratch
@@ -81,9 +80,8 @@ constexpr int kActABytes = 16384;
 constexpr int kActD = kActA + kActABytes;   // [8 waves][64 lanes][4] fp32
 constexpr int kActRed = kActD + 8192;       // [2][8] fp32 per-wave partial reductions
 static_assert(kActRed + 64 <= kActBytes, "multi-row staging overflows the activation area");
-static_assert(kAttVraw + 1024 <= kAttP, "attention staging overlaps the exponentials");
+static_assert(kActMerge + 8 * kMaxG * 130 * 4 <= kActBytes, "attention merge area overflows the staging area");
 static_assert(kAttRope + 512 <= kAttQraw, "attention gains overlap the raw q staging");
-static_assert(kAttP + 8 * kMaxG * 16 * 4 <= kActBytes, "attention exponentials overflow the staging area");
 static_assert(kLdsBytes == 163840, "LDS budget");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 }  // namespace dev

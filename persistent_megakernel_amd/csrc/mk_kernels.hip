@@ -36,6 +36,9 @@ namespace dev {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // 16x16x32 bf16 matrix-core operand
+typedef short i16x4 __attribute__((ext_vector_type(4)));    // 16x16x16 bf16 matrix-core operand
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 #define DEV __device__ __forceinline__
@@ -454,7 +457,7 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
       const int page = (int)s_ld32(pf.bt + t / a.sh.P);
       const int tt = pf.t0 + (int)u;
       const size_t rowi = ((size_t)page * a.sh.P + (tt % a.sh.P)) * a.sh.Hkv + pf.hk;
-      src = base + rowi * 256u + (ln & 15u) * 16u;
+      src = base + rowi * 256u + (((ln & 15u) ^ ((4u * bb + (ln >> 4)) & 15u)) << 4);  // chunk order of att_pos
     } else {
       src = base + bb * 1024u + ln * 16u;
     }
@@ -830,19 +833,38 @@ DEV void qk_norm_rope(const char* raw, const char* gn, const char* rope, float e
   ((uint16_t*)dst)[i + 64] = (uint16_t)(o >> 16);
 }
 
-// split-KV attention partial for one (request, kv head, split) over its G query heads, on all eight
-// waves (wv 0..6 the compute waves, 7 the controller: two per SIMD), with two block barriers:
+// An attention lease holds the split's K rows, then its V rows (256 bytes each).  Chunk c (16 bytes,
+// dims 8c .. 8c + 7) of lease row u sits at position c ^ (u mod 16) of the row: the 16 rows that one
+// matrix-core operand load reads at the same chunk then fall in 16 different bank groups.
+DEV uint32_t att_pos(uint32_t u, uint32_t c) { return u * 256u + ((c ^ (u & 15u)) << 4); }
+
+// reductions over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48), every lane getting the result
+DEV float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+DEV float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// split-KV attention partial for one (request, kv head, split) over its G (<= 16) query heads, on all
+// eight waves (wv 0..6 the compute waves, 7 the controller: two per SIMD), with two block barriers:
 //   0. QK-norm + RoPE once per head (wave j < G: q head j, wave G: the new key, wave G + 1: the new
 //      value, bf16) into LDS;
-//   1. wave wv takes a contiguous block of at most 16 of the split's tokens: its four 16-lane rows take
-//      one token each at a time for the scores (lane `sub` holding dims [8 sub, 8 sub + 8), a 16-lane
-//      sum); the wave's maximum m_w per head (read from the four rows), the exponentials into a
-//      wave-private table (no block barrier: only this wave reads it), then P V on all 64 lanes, one
-//      token at a time (two dims per lane);
+//   1. wave wv takes a contiguous block of at most 16 of the split's tokens and works on the matrix
+//      cores: S^T = K Q^T (16x16x32 bf16; token rows by key rows, head columns), the wave's maximum
+//      m_w and sum l_w per head over its tokens, P = exp(S - m_w) -- whose result layout is already
+//      the A operand of the next product -- and O_w = P V (16x16x16 bf16 on P's two bf16 parts);
 //   2. the eight waves' (m_w, l_w, O_w) merge with weights exp(m_w - max m_w).
 // Output: the split's normalised O [G][128] and its lse [G] in the output area.
 template <int G, int S>
 DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int wv) {
+  static_assert(G <= 16, "one matrix-core column per query head");
   const Shapes& sh = a.sh;
   const int s = in.w[W_P3], t0 = in.w[W_P4], t1 = in.w[W_P5];
   const bool last = s == attn_splits<S>(in) - 1;
@@ -861,74 +883,91 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
     ((uint32_t*)(act + kActV))[ln] = pack_bf2(ll_f32(vr, 2 * ln), ll_f32(vr, 2 * ln + 1));
   }
   lds_barrier();
-  const int sub = ln & 15, rw = ln >> 4;
-  const int per = (ntok + kNW - 1) / kNW;  // <= 16 tokens per wave: four rounds of four rows
+  const int sub = ln & 15, grp = ln >> 4;
+  const int per = (ntok + kNW - 1) / kNW;  // <= 16 tokens per wave
   const int tw0 = min(wv * per, ntok), tw1 = min(tw0 + per, ntok);
-  u32x4 qv[G];
+  // scores: A row sub = key row tw0 + sub (a row past the block loads a valid row; masked below),
+  // lane group grp holding dims 32 k + 8 grp .. + 8 at step k; B column sub = q head sub (zero past
+  // G).  Result: S[token tw0 + 4 grp + e][head sub] in element e.
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int ua = min(tw0 + sub, ntok - 1);
 #pragma unroll
-  for (int j = 0; j < G; ++j) qv[j] = *(const u32x4*)(act + kActQ + j * 256 + sub * 16);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c = 4u * k + (uint32_t)grp;
+      const bf16x8 kv = *(const bf16x8*)(ua < nk ? ring + ring_off(lease, att_pos((uint32_t)ua, c)) : act + kActK + c * 16u);
+      bf16x8 qv = *(const bf16x8*)(act + kActQ + (sub < G ? sub : 0) * 256 + c * 16u);
+      if (sub >= G) qv = bf16x8{};
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv, sacc, 0, 0, 0);
+    }
+  }
   const float scale = sh.inv_sqrt_d;
-  float sc[4][G];
+  float p[4];
+  float mloc = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int t = tw0 + 4 * k + rw;
-    const int tc = min(t, ntok - 1);  // past the wave's block: any valid token, masked
-    const u32x4 kv = *(const u32x4*)(tc < nk ? ring + ring_off(lease, (uint32_t)tc * 256u + sub * 16u) : act + kActK + sub * 16);
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float v = row16_sum(dot8(kv, qv[j], 0.f)) * scale;
-      sc[k][j] = t < tw1 ? v : -INFINITY;
-    }
+  for (int e = 0; e < 4; ++e) {
+    p[e] = tw0 + 4 * grp + e < tw1 ? sacc[e] * scale : -INFINITY;
+    mloc = fmaxf(mloc, p[e]);
   }
-  float* pw = (float*)(act + kAttP) + wv * G * 16;  // [G][16] exponentials of the wave's tokens
-  float mw[G];
+  const float mw = rows4_max(mloc);  // -inf for a wave without tokens
+  float lloc = 0.f;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float m = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
-    const int mi = __float_as_int(m);
-    mw[j] = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 0)), __int_as_float(__builtin_amdgcn_readlane(mi, 16))),
-                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 32)), __int_as_float(__builtin_amdgcn_readlane(mi, 48))));
-    if (sub == 0) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pw[j * 16 + 4 * k + rw] = sc[k][j] == -INFINITY ? 0.f : __expf(sc[k][j] - mw[j]);
-    }
+  for (int e = 0; e < 4; ++e) {
+    p[e] = p[e] == -INFINITY ? 0.f : __expf(p[e] - mw);
+    lloc += p[e];
   }
-  wave_lds_sync();
-  float acc[G][2], lw[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = lw[j] = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (tw0 + 4 * k >= tw1) break;
-    f32x4 pk[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) pk[j] = *(const f32x4*)(pw + j * 16 + 4 * k);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = min(tw0 + 4 * k + r, ntok - 1);  // past the block: weight 0 from the table
-      const uint32_t vw = *(const uint32_t*)(t < nk ? ring + ring_off(lease, voff + (uint32_t)t * 256u + ln * 4u) : act + kActV + ln * 4);
-      const float v0 = bf2f(vw & 0xffffu), v1 = bf2f(vw >> 16);
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float pj = pk[j][r];
-        lw[j] += pj;
-        acc[j][0] += pj * v0;
-        acc[j][1] += pj * v1;
-      }
-    }
+  const float lw = rows4_sum(lloc);
+  // P V: A = P (lane: head sub, tokens 4 grp + e -- the layout the scores came in) as the sum of two
+  // bf16 parts, P = hi + lo, so the product keeps about 16 bits of P; B fragment c holds
+  // V[token 4 grp + e][dim 8 sub + c], taken from one 16-byte load per token (chunk sub of the row)
+  i16x4 pa, pl;
+  {
+    const u32x2 hw = {pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3])};
+    const u32x2 lw2 = {pack_bf2(p[0] - bf2f(hw[0] & 0xffffu), p[1] - bf2f(hw[0] >> 16)),
+                       pack_bf2(p[2] - bf2f(hw[1] & 0xffffu), p[3] - bf2f(hw[1] >> 16))};
+    __builtin_memcpy(&pa, &hw, 8);
+    __builtin_memcpy(&pl, &lw2, 8);
   }
+  u32x4 vv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int u = min(tw0 + 4 * grp + e, ntok - 1);  // past the block: a valid row, weight 0
+    vv[e] = *(const u32x4*)(u < nk ? ring + ring_off(lease, voff + att_pos((uint32_t)u, (uint32_t)sub)) : act + kActV + sub * 16);
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int w = c >> 1;
+    u32x2 bw;
+    if (c & 1) {
+      bw[0] = (vv[0][w] >> 16) | (vv[1][w] & 0xffff0000u);
+      bw[1] = (vv[2][w] >> 16) | (vv[3][w] & 0xffff0000u);
+    } else {
+      bw[0] = (vv[0][w] & 0xffffu) | (vv[1][w] << 16);
+      bw[1] = (vv[2][w] & 0xffffu) | (vv[3][w] << 16);
+    }
+    i16x4 b;
+    __builtin_memcpy(&b, &bw, 8);
+    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, b, o[c], 0, 0, 0);
+  }
+  // O_w[head 4 grp + i][dim 8 sub + c] is element i of o[c]
   float* mrg = (float*)(act + kActMerge);  // [wave][G][128] partial P V, then [wave][G] (m_w, l_w)
   float* ml = mrg + kNW * G * 128;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    *(f32x2*)(mrg + (wv * G + j) * 128 + 2 * ln) = f32x2{acc[j][0], acc[j][1]};
-    if (ln == 0) *(f32x2*)(ml + (wv * G + j) * 2) = f32x2{tw1 > tw0 ? mw[j] : -INFINITY, lw[j]};
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * grp + i;
+    if (h < G) {
+      *(f32x4*)(mrg + (wv * G + h) * 128 + 8 * sub) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+      *(f32x4*)(mrg + (wv * G + h) * 128 + 8 * sub + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+    }
   }
+  if (grp == 0 && sub < G) *(f32x2*)(ml + (wv * G + sub) * 2) = f32x2{mw, lw};
   lds_barrier();
   // merge the eight waves: weights exp(m_w - M) with M the largest m_w; lane o = j * 128 + d
   float* out = (float*)(smem + kOutOff);
-  for (int o = wv * 64 + ln; o < G * 128; o += kNW * 64) {
-    const int j = o >> 7, d = o & 127;
+  for (int o2 = wv * 64 + ln; o2 < G * 128; o2 += kNW * 64) {
+    const int j = o2 >> 7, d = o2 & 127;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) M = fmaxf(M, ml[(w * G + j) * 2]);
@@ -940,7 +979,7 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
       O += e * mrg[(w * G + j) * 128 + d];
       L += e * ml[(w * G + j) * 2 + 1];
     }
-    out[o] = O / L;
+    out[o2] = O / L;
     if (d == 0) out[G * 128 + j] = M + __logf(L);
   }
 }
@@ -964,8 +1003,6 @@ DEV void attn_compute(const KArgs& a, const Instr& in, const char* smem, char* a
 // Intermediates are plain (untagged) values; projection inputs sit in HBM already in the
 // matrix-core operand order, so a tile's input chunk is one contiguous copy.
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 DEV void signal_all(const KArgs& a, const Instr& in) {
   if (a.flags & kModeGraph) return;
