@@ -409,60 +409,90 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
   }
 }
 
-// issue this wave's share (blocks b = cw mod 7) of an instruction's prefetch into its lease
+// issue this wave's share of an instruction's prefetch into its lease: a contiguous run of blocks
+// (about a seventh of them), span by span, with the per-block address work kept incremental (a
+// block-table entry is read once per page, a weight row address once per 16-row block) so that a
+// wave issues its loads back to back
 template <int S>
 DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint32_t& issued, char* smem) {
   const uint32_t ln = lane();
-  for (uint32_t b = cw; b < pf.total; b += kNCW) {
-    int k = 0;
-    const char* base = pf.src[0];
-    uint32_t b0 = 0;
+  const uint32_t per = (pf.total + kNCW - 1u) / kNCW;
+  const uint32_t lo = min((uint32_t)cw * per, pf.total), hi = min(lo + per, pf.total);
+  const uint32_t ring = (uint32_t)(uintptr_t)(lds_void*)(smem + kRingOff);
 #pragma unroll
-    for (int q = 1; q < kMaxSpans; ++q)
-      if (q < pf.n && b >= pf.blk[q]) {
-        k = q;
-        base = pf.src[q];
-        b0 = pf.blk[q];
-      }
-    const uint32_t bb = b - b0;
-    const char* src;
-    bool frag = false;
+  for (int k = 0; k < kMaxSpans; ++k) {
+    if (k >= pf.n) break;
+    const uint32_t b0 = max(lo, pf.blk[k]), b1 = min(hi, pf.blk[k + 1]);
+    if (b0 >= b1) continue;
+    const char* base = pf.src[k];
     if constexpr (S == 1) {
       if (pf.mode == PF_W_BF16 || pf.mode == PF_W_FP8) {
-        const uint32_t nb = b / pf.bpn, q = b - nb * pf.bpn;
-        const uint32_t tr = nb * 16u + (ln & 15u);
-        const uint32_t grow = tr < pf.split ? pf.base0 + tr : pf.base1 + tr;
-        src = base + (size_t)grow * pf.rowb + pf.k0b + q * 64u + (ln >> 4) * 16u;
-        frag = true;
-      } else if (pf.mode == PF_KEYS) {
+        // block b = 16-row block nb, K step q: lane l takes row 16 nb + l % 16, bytes 16 (l / 16) of the step
+        uint32_t nb = b0 / pf.bpn, q = b0 - nb * pf.bpn;
+        const char* rowp = nullptr;
+        uint32_t rnb = 0xFFFFFFFFu;
+        for (uint32_t b = b0; b < b1; ++b) {
+          if (nb != rnb) {
+            const uint32_t tr = nb * 16u + (ln & 15u);
+            const uint32_t grow = tr < pf.split ? pf.base0 + tr : pf.base1 + tr;
+            rowp = base + (size_t)grow * pf.rowb + pf.k0b + (ln >> 4) * 16u;
+            rnb = nb;
+          }
+          lds_dma16(rowp + q * 64u, ring + ring_off(lease, b * 1024u));
+          ++issued;
+          if (++q == pf.bpn) {
+            q = 0;
+            ++nb;
+          }
+        }
+        continue;
+      }
+      if (pf.mode == PF_KEYS) {
         if (k == 1) break;  // the scale block is filled alongside the key blocks
         // 8 tokens of one page (8 divides the page size and t0): 1 KiB contiguous in the cache
-        const uint32_t tok = (uint32_t)pf.t0 + 8u * b, P = (uint32_t)a.sh.P;
-        const uint32_t page = (uint32_t)s_ld32(pf.bt + tok / P);
-        const uint32_t slot = page * P + tok % P;
-        const uint32_t lo = 8u * b + (ln >> 3) < (uint32_t)pf.nk ? ln * 16u : 0u;  // past the split: reload the block start
-        src = base + (size_t)slot * 128u + lo;
-        const uint32_t sdst = (uint32_t)(uintptr_t)(lds_void*)(smem + kRingOff + ring_off(lease, pf.blk[1] * 1024u + b * 32u));
-        if (ln < 2u)  // the 8 tokens' scales (32 bytes) into the scale block: one more load of the wave
-          lds_dma16(pf.src[1] + (size_t)slot * 4u + ln * 16u, sdst);
-        ++issued;
-        frag = true;
+        const uint32_t P = (uint32_t)a.sh.P;
+        uint32_t pidx = 0xFFFFFFFFu, page = 0;
+        for (uint32_t b = b0; b < b1; ++b) {
+          const uint32_t tok = (uint32_t)pf.t0 + 8u * b;
+          if (tok / P != pidx) {
+            pidx = tok / P;
+            page = (uint32_t)s_ld32(pf.bt + pidx);
+          }
+          const uint32_t slot = page * P + tok % P;
+          const uint32_t off = 8u * b + (ln >> 3) < (uint32_t)pf.nk ? ln * 16u : 0u;  // past the split: reload the block start
+          const uint32_t sdst = ring + ring_off(lease, pf.blk[1] * 1024u + b * 32u);
+          if (ln < 2u)  // the 8 tokens' scales (32 bytes) into the scale block: one more load of the wave
+            lds_dma16(pf.src[1] + (size_t)slot * 4u + ln * 16u, sdst);
+          lds_dma16(base + (size_t)slot * 128u + off, ring + ring_off(lease, b * 1024u));
+          issued += 2u;
+        }
+        continue;
       }
     }
-    if (frag) {
-    } else if (pf.mode == PF_ATTN && k < 2) {
-      uint32_t u = bb * 4u + (ln >> 4);
-      if (u >= (uint32_t)pf.nk) u = 4u * bb;  // beyond the tile: reload the block's first row
-      const int t = pf.t0 + (int)(4u * bb);
-      const int page = (int)s_ld32(pf.bt + t / a.sh.P);
-      const int tt = pf.t0 + (int)u;
-      const size_t rowi = ((size_t)page * a.sh.P + (tt % a.sh.P)) * a.sh.Hkv + pf.hk;
-      src = base + rowi * 256u + (((ln & 15u) ^ ((4u * bb + (ln >> 4)) & 15u)) << 4);  // chunk order of att_pos
-    } else {
-      src = base + bb * 1024u + ln * 16u;
+    if (pf.mode == PF_ATTN && k < 2) {
+      // block bb of the K (or V) span: the split's rows 4 bb .. 4 bb + 3 (one page: 4 divides the page
+      // size and t0), chunk c of row u at position c ^ (u mod 16)
+      const int P = a.sh.P;
+      int pidx = -1, page = 0;
+      for (uint32_t b = b0; b < b1; ++b) {
+        const uint32_t bb = b - pf.blk[k];
+        const int t = pf.t0 + (int)(4u * bb);
+        if (t / P != pidx) {
+          pidx = t / P;
+          page = (int)s_ld32(pf.bt + pidx);
+        }
+        uint32_t u = bb * 4u + (ln >> 4);
+        if (u >= (uint32_t)pf.nk) u = 4u * bb;  // beyond the tile: reload the block's first row
+        const size_t rowi = ((size_t)page * P + ((pf.t0 + (int)u) % P)) * a.sh.Hkv + pf.hk;
+        lds_dma16(base + rowi * 256u + (((ln & 15u) ^ ((4u * bb + (ln >> 4)) & 15u)) << 4), ring + ring_off(lease, b * 1024u));
+        ++issued;
+      }
+      continue;
     }
-    lds_dma16(src, (uint32_t)(uintptr_t)(lds_void*)(smem + kRingOff + ring_off(lease, b * 1024u)));
-    ++issued;
+    for (uint32_t b = b0; b < b1; ++b) {
+      lds_dma16(base + (b - pf.blk[k]) * 1024u + ln * 16u, ring + ring_off(lease, b * 1024u));
+      ++issued;
+    }
   }
 }
 
