@@ -1050,6 +1050,32 @@ struct WaitCache {  // the last (event, threshold) wait found satisfied in this 
   uint32_t e, thr;
 };
 
+// A multi-row instruction's signals, held by the controller from its compute-end barrier until
+// its stores have completed: the completion wait is taken together with the next instruction's
+// staging, or on its own before any wait that has to poll and at the end of the queue.
+struct SigPend {
+  uint32_t n, e0, i0, e1, i1;
+};
+DEV SigPend sig_of(const Instr& in) {
+  return SigPend{in.w[W_NSIG], in.w[W_SIG0], in.w[W_SIG0 + 1], in.w[W_SIG0 + 3], in.w[W_SIG0 + 4]};
+}
+DEV void signal_pend(const KArgs& a, const SigPend& sp) {
+  if (a.flags & kModeGraph) return;
+  if (lane() == 0) {
+    const size_t sub = (blockIdx.x % kNSub) * kSubStride;
+    if (sp.n > 0u) __hip_atomic_fetch_add(a.events + (size_t)sp.e0 * kEvStride + sub, sp.i0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sp.n > 1u) __hip_atomic_fetch_add(a.events + (size_t)sp.e1 * kEvStride + sub, sp.i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+// every wait of the instruction is the one last found satisfied (no polling needed)
+DEV bool waits_cached(const Instr& in, const WaitCache& wc) {
+  bool all = true;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)  // constant indices: the instruction words stay in registers
+    if ((uint32_t)k < in.w[W_NWAIT] && (in.w[W_WAIT0 + 2 * k] != wc.e || in.w[W_WAIT0 + 2 * k + 1] != wc.thr)) all = false;
+  return all;
+}
+
 // false when the watchdog expired or another worker aborted
 DEV bool wait_events(const KArgs& a, const Instr& in, uint32_t& polls, WaitCache& wc) {
   const uint32_t ln = lane();
@@ -1173,8 +1199,6 @@ DEV void gemm_epilogue(const KArgs& a, const Instr& in, const char* smem) {
     const f32x4 v = *(const f32x4*)(D + (nb * 64u + ln) * 16u) + *(const f32x4*)(D + ((nb + 4u) * 64u + ln) * 16u);
     st128(rp, (nb * 64u + ln) * 16u, u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
   }
-  wait_vm0();
-  signal_all(a, in);
 }
 
 // float index of tile element (m, c) in one chunk's partial sums
@@ -1732,12 +1756,9 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
     st32(rsrc((uint16_t*)s_ld64(row + ATT_KC) + rowi * 128), lane() * 4u, kl[lane()]);
     st32(rsrc((uint16_t*)s_ld64(row + ATT_VC) + rowi * 128), lane() * 4u, vl[lane()]);
   }
+  if (S == 1) return false;  // multi-row plans: the controller completes the stores and signals later
   wait_vm0();
   if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
-  if (S == 1) {
-    signal_all(a, in);
-    return false;
-  }
   const bool last = arrive(a, in);
   if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
   if (!last) return false;
@@ -1971,6 +1992,8 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
   LmState lm{-INFINITY, 0x7fffffff};
   WaitCache wc{0xFFFFFFFFu, 0u};
   uint64_t staged = 0;  // multi-row: the projection input chunk held in the activation area
+  SigPend pend{0u, 0u, 0u, 0u, 0u};
+  bool pending = false;  // multi-row: the previous instruction's signals wait for its stores
   for (int i = 0; i < count; ++i) {
     Instr in;
     fetch(base + (size_t)i * stride, in);
@@ -1990,11 +2013,21 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     if constexpr (m16) {
       // multi-row: wait for the event counters (the graph baseline's stream order guarantees them),
       // then stage what the op reads from LDS
+      if (pending && !graph && !waits_cached(in, wc)) {  // a wait that may poll: no signal of ours held back
+        wait_vm0();
+        signal_pend(a, pend);
+        pending = false;
+      }
       ok = graph || wait_events(a, in, poll, wc);
       if (ok && op == OP_ATTN) ok = attn_stage(a, in, act, false, poll, sst);
       if (ok && op == OP_GEMM) gemm_stage(a, in, act, staged);
       if (ok && op == OP_SCORE) score_stage(a, in, act);
       if (op != OP_GEMM) staged = 0;
+      if (pending) {  // the staging above waited for our stores too, when it staged anything
+        wait_vm0();
+        signal_pend(a, pend);
+        pending = false;
+      }
     } else if (op == OP_ATTN)
       ok = attn_stage(a, in, act, !graph, poll, sst);
     else if (op == OP_OPROJ)
@@ -2024,16 +2057,17 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     lds_barrier();  // B: compute done, results in the output area
     const unsigned long long t_b = tracing ? rtc() : 0;
     const unsigned long long c_b = tracing ? __builtin_readcyclecounter() : 0;
-    if (op == OP_ATTN) {
-      if (attn_epilogue<S>(a, in, smem, st) && m16) {  // the combining worker signals the group's event
-        wait_vm0();
-        signal_all(a, in);
-      }
-    } else if constexpr (m16) {
-      if (op == OP_GEMM)
+    if constexpr (m16) {
+      // stores only; norm / finalize / quantise / combine / key-cache / score bodies completed theirs
+      // in every wave before B
+      if (op == OP_ATTN)
+        attn_epilogue<S>(a, in, smem, st);
+      else if (op == OP_GEMM)
         gemm_epilogue(a, in, smem);
-      else
-        signal_all(a, in);  // norm / finalize / quantise / combine: every wave's stores completed before B
+      pend = sig_of(in);
+      pending = true;
+    } else if (op == OP_ATTN) {
+      attn_epilogue<S>(a, in, smem, st);
     } else {
       gemv_epilogue(a, in, smem, lm, st);
     }
@@ -2054,6 +2088,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       tr[12] = (uint32_t)sst.issue;
       tr[13] = (uint32_t)sst.landed;
     }
+  }
+  if (pending) {  // the last instruction's signals
+    wait_vm0();
+    signal_pend(a, pend);
   }
 }
 
