@@ -12,6 +12,11 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
+try:  # PyTorch first: libmk.so then binds to the HIP / HSA runtime PyTorch loaded (one runtime per
+    import torch  # noqa: F401  process); loaded the other way round, PyTorch finds no GPU
+except ImportError:  # pragma: no cover - the library itself does not need PyTorch
+    pass
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 if not os.path.exists(LIB_PATH):
