@@ -332,6 +332,11 @@ DEV uint32_t proj_k(const Shapes& sh, uint32_t kind) {
 }
 // row length of a NORM instruction: the hidden size, or the q rank for the indexer's q_a norm
 DEV uint32_t norm_len(const Shapes& sh, const Instr& in) { return in.w[W_LAYER + 1] == 2 ? (uint32_t)sh.qr : (uint32_t)sh.H; }
+// a NORM adding the caller's x to its r_in (the first norm, waiting on nothing: both are inputs of
+// the launch) gets them through its lease, after the gain: r at 2H bytes, x at 6H bytes
+DEV bool norm_inputs_in_lease(const Instr& in, const uint64_t* row) {
+  return in.w[W_NWAIT] == 0u && in.w[W_LAYER + 1] == 0u && s_ld64(row + NM_X) != 0u;
+}
 
 // splits of an attention instruction's (request, kv head).  S is the op family of the kernel
 // instance: 0 the single-token bodies, 1 the multi-row ones (the plan's spec id, fixed per plan).
@@ -364,7 +369,13 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
     return;
   }
   if (S == 1 && op == OP_NORM) {
-    pf_set<0>(pf, (const void*)s_ld64(row + NM_GAIN), 2u * norm_len(sh, in));
+    const uint32_t H = norm_len(sh, in);
+    pf_set<0>(pf, (const void*)s_ld64(row + NM_GAIN), 2u * H);
+    if (norm_inputs_in_lease(in, row)) {  // the layer's own inputs: stream them in with the gain
+      const uint32_t m = in.w[W_LAYER + 2];
+      pf_set<1>(pf, (const float*)s_ld64(row + NM_R) + (size_t)m * H, 4u * H);
+      pf_set<2>(pf, (const uint16_t*)s_ld64(row + NM_X) + (size_t)m * H, 2u * H);
+    }
     return;
   }
   if (S == 1 && op == OP_SCORE) {
@@ -1302,12 +1313,20 @@ DEV void norm_row(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
   __amdgpu_buffer_rsrc_t rx = rsrc((const uint16_t*)xp + (size_t)m * H);
   float v[2][8];
   u32x4 ra[2], rb[2], xv[2];
+  const bool in_lease = norm_inputs_in_lease(in, row);
+  const char* ring = smem + kRingOff;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint32_t e = min(t + 512u * i, H / 8u - 1u) * 8u;
-    ra[i] = ld128(rr, e * 4u);
-    rb[i] = ld128(rr, e * 4u + 16u);
-    xv[i] = xp ? ld128(rx, e * 2u) : u32x4{0u, 0u, 0u, 0u};
+    if (in_lease) {
+      ra[i] = *(const u32x4*)(ring + ring_off(lease, 2u * H + e * 4u));
+      rb[i] = *(const u32x4*)(ring + ring_off(lease, 2u * H + e * 4u + 16u));
+      xv[i] = *(const u32x4*)(ring + ring_off(lease, 6u * H + e * 2u));
+    } else {
+      ra[i] = ld128(rr, e * 4u);
+      rb[i] = ld128(rr, e * 4u + 16u);
+      xv[i] = xp ? ld128(rx, e * 2u) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   wait_vm0();
   float ss = 0.f;
