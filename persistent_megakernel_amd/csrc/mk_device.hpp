@@ -58,7 +58,15 @@ constexpr int kCtrlOff = kOutOff + kOutBytes;  // abort flag + per-wave lease ta
 constexpr int kCtrlBytes = 1024;
 constexpr int kLeaseTabOff = 64;   // in the control area: [7 waves][32] lease tables
 constexpr int kInvOff = 8;         // in the control area: the fused norm's rsqrt(mean square + eps)
+// multi-row kernel: kLoaders more waves that only stream leases and never take a barrier; the
+// other eight synchronise through an LDS arrival counter instead of s_barrier
+constexpr int kLoaders = 3;
+constexpr int kThreadsM = kThreads + 64 * kLoaders;
+constexpr int kBarOff = 24;        // in the control area: arrivals at the eight waves' barrier
+constexpr int kRetiredOff = 28;    // in the control area: instructions the eight waves have finished
+constexpr int kDoneOff = 32;       // in the control area: [kLoaders] instructions whose lease share landed
 static_assert(kLeaseTabOff + 7 * 32 * 4 <= kCtrlBytes, "control area");
+static_assert(kDoneOff + 4 * kLoaders <= kLeaseTabOff && kLoaders <= 7, "control area");
 constexpr int kLdsBytes = kCtrlOff + kCtrlBytes;  // all 160 KiB: one block per CU
 // attention sub-areas of the activation staging area
 constexpr int kMaxG = 5;       // GQA group (q heads per kv head) of the M = 1 attention body

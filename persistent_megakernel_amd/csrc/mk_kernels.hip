@@ -186,7 +186,38 @@ DEV void ll_put2(__amdgpu_buffer_rsrc_t r, uint32_t idx, uint32_t p0, uint32_t p
 DEV float ll_f32(const char* base, int k) { return *(const float*)(base + 8 * k); }
 
 DEV void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// the kernels' dynamic LDS (the same base as each kernel's own `smem`)
+extern __shared__ __attribute__((aligned(1024))) char mk_lds[];
+
+// Barrier of the eight waves that run the op bodies.  The multi-row kernel also has loader waves
+// that never take a barrier, so there the eight meet on an LDS arrival counter: the arrivals of
+// one barrier are 8k .. 8k + 7, and a wave waits for the count to reach 8(k + 1).  A wait that
+// outlasts the watchdog marks the block aborted (control word 2) and lets the wave go.
+DEV void group_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  uint32_t* cnt = (uint32_t*)(mk_lds + kCtrlOff + kBarOff);
+  uint32_t old = 0;
+  if (__lane_id() == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const uint32_t target = (__builtin_amdgcn_readfirstlane(old) & ~7u) + 8u;
+  for (uint32_t it = 1;; ++it) {
+    const uint32_t now = __builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if ((int32_t)(now - target) >= 0) break;
+    __builtin_amdgcn_s_sleep(1);
+    if ((it & 0xFFFFFu) == 0u) {  // about every 0.1 s: give up once the block has aborted or after ~2 s
+      volatile uint32_t* ctrl = (volatile uint32_t*)(mk_lds + kCtrlOff);
+      if (*ctrl != 0u) break;
+      if (it >= 0x1400000u) {
+        if (__lane_id() == 0) *ctrl = 2u;
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+}
+DEV void lds_barrier() {
+  if (blockDim.x > (uint32_t)kThreads) group_barrier();
+  else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 // the wave's own LDS writes done, and no LDS access moved across this point (a wave-private
 // exchange between lanes: LDS serves one wave's accesses in order once they are issued)
 DEV void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -425,9 +456,9 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
 // block-table entry is read once per page, a weight row address once per 16-row block) so that a
 // wave issues its loads back to back
 template <int S>
-DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint32_t& issued, char* smem) {
+DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint32_t& issued, char* smem, int nw = kNCW) {
   const uint32_t ln = lane();
-  const uint32_t per = (pf.total + kNCW - 1u) / kNCW;
+  const uint32_t per = (pf.total + (uint32_t)nw - 1u) / (uint32_t)nw;
   const uint32_t lo = min((uint32_t)cw * per, pf.total), hi = min(lo + per, pf.total);
   const uint32_t ring = (uint32_t)(uintptr_t)(lds_void*)(smem + kRingOff);
 #pragma unroll
@@ -2002,6 +2033,74 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
 // ---------------------------------------------------------------------------------------
 // the two roles
 
+// Multi-row kernel: loader wave k of kLoaders.  The loaders walk the queue ahead of the eight
+// compute-group waves, lease ring pages to instructions in queue order (each loader keeps the same
+// lease table; loader 0's is the one the compute group reads), stream their share of each lease
+// (a contiguous run of its blocks), and publish in order how many instructions' shares have
+// landed.  Pages of an instruction are reused once the compute group has retired it.  Loaders take
+// no barrier, so a full memory pipeline stalls only them, never the op bodies.
+template <int S>
+DEV void loader(const KArgs& a, const uint32_t* base, int count, int stride, int k, char* smem) {
+  volatile uint32_t* ctrl = (volatile uint32_t*)(smem + kCtrlOff);
+  volatile uint32_t* done = (volatile uint32_t*)(smem + kCtrlOff + kDoneOff) + k;
+  const volatile uint32_t* retired = (const volatile uint32_t*)(smem + kCtrlOff + kRetiredOff);
+  uint32_t* lease_tab = (uint32_t*)(smem + kCtrlOff + kLeaseTabOff) + k * 32;  // [16] lease, [16] issued_end
+  const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
+  const int lookahead = (a.flags & MK_FLAG_NO_PREFETCH) ? 0 : 15;  // lease slots are indexed mod 16
+  uint32_t head = 0, issued = 0;
+  int j = 0;  // next instruction to lease
+  int d = 0;  // instructions whose share has landed
+  uint32_t idle = 0;
+  while (d < count) {
+    const int r = (int)uni(*retired);
+    while (j < count && j <= r + lookahead) {
+      Instr nx;
+      fetch(base + (size_t)uni((uint32_t)j) * stride, nx);
+      uint32_t npg = 0;
+      Pf<S> pf;
+      if (nx.w[W_OPCODE] != OP_NOOP && !noop_only) {
+        pf_desc<S>(a, nx, pf);
+        npg = (pf_blocks(pf) + 15u) >> 4;
+        const uint32_t freed = j > r ? uni(lease_tab[r & 15]) : head;  // pages before instruction r are free
+        if (head + npg - freed > (uint32_t)kNPages) break;
+        if (npg) pf_issue<S>(a, pf, head, k, issued, smem, kLoaders);
+      }
+      lease_tab[j & 15] = head;
+      lease_tab[16 + (j & 15)] = issued;
+      head += npg;
+      ++j;
+    }
+    if (d < j) {  // the oldest leased instruction: wait for this loader's share, then publish it
+      wait_vm_le(issued - uni(lease_tab[16 + (d & 15)]));
+      ++d;
+      if (lane() == 0) *done = (uint32_t)d;
+      idle = 0;
+      continue;
+    }
+    // nothing in flight and nothing that fits: wait for the compute group to retire an instruction
+    __builtin_amdgcn_s_sleep(2);
+    if ((++idle & 0xFFFFu) == 0u && (*ctrl != 0u || idle >= 0x800000u)) {
+      if (lane() == 0 && *ctrl == 0u) *ctrl = 2u;
+      break;
+    }
+  }
+  wait_vm0();  // no LDS-bound load may be in flight when the block retires
+}
+
+// multi-row kernel, controller: wait until every loader has landed its share of instruction i
+DEV bool wait_loaders(const char* smem, int i) {
+  const volatile uint32_t* done = (const volatile uint32_t*)(smem + kCtrlOff + kDoneOff);
+  const volatile uint32_t* ctrl = (const volatile uint32_t*)(smem + kCtrlOff);
+  for (uint32_t it = 1;; ++it) {
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < kLoaders; ++k) all = all && (int)uni(done[k]) > i;
+    if (all) return true;
+    __builtin_amdgcn_s_sleep(1);
+    if ((it & 0xFFFFFu) == 0u && (*ctrl != 0u || it >= 0x1400000u)) return false;
+  }
+}
+
 template <int S>
 DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride, char* smem) {
   uint32_t* ctrl = (uint32_t*)(smem + kCtrlOff);  // LDS; read and written only across barriers
@@ -2017,7 +2116,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     Instr in;
     fetch(base + (size_t)i * stride, in);
     const uint32_t op = in.w[W_OPCODE];
-    if (op == OP_NOOP) continue;
+    if (op == OP_NOOP) {
+      if (S == 1 && lane() == 0) *(volatile uint32_t*)(smem + kCtrlOff + kRetiredOff) = (uint32_t)i + 1u;
+      continue;
+    }
     constexpr bool m16 = S == 1;
     const bool tracing = a.flags & MK_FLAG_TRACE;
     const unsigned long long t_vis = tracing ? rtc() : 0;
@@ -2047,6 +2149,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
         signal_pend(a, pend);
         pending = false;
       }
+      if (ok && !wait_loaders(smem, i)) {  // the loaders' shares of this lease
+        record_timeout(a, in, 0xB0u, 0u);
+        ok = false;
+      }
     } else if (op == OP_ATTN)
       ok = attn_stage(a, in, act, !graph, poll, sst);
     else if (op == OP_OPROJ)
@@ -2064,6 +2170,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     const unsigned long long t_a = tracing ? rtc() : 0;
     const unsigned long long c_a = tracing ? __builtin_readcyclecounter() : 0;
     if (!ok) break;
+    if (m16 && uni(ctrl[0]) != 0u) {  // a barrier or a loader of this block gave up (watchdog)
+      record_timeout(a, in, 0xBAu, 0u);
+      break;
+    }
     if (!noop_only) {  // the controller is the eighth wave of every op body
       const uint32_t lease = uni(((const uint32_t*)(smem + kCtrlOff + kLeaseTabOff))[i & 15]);  // compute wave 0's table
       if (op == OP_ATTN)
@@ -2074,6 +2184,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
         proj_body(a, in, smem, lease, fused_norm, kNW - 1);
     }
     lds_barrier();  // B: compute done, results in the output area
+    if (m16 && lane() == 0) *(volatile uint32_t*)(smem + kCtrlOff + kRetiredOff) = (uint32_t)i + 1u;  // its pages are free
     const unsigned long long t_b = tracing ? rtc() : 0;
     const unsigned long long c_b = tracing ? __builtin_readcyclecounter() : 0;
     if constexpr (m16) {
@@ -2132,7 +2243,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       continue;
     }
     const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
-    if (!noop_only) {
+    if (S == 0 && !noop_only) {
       // pages of every instruction before i are free now
       const uint32_t freed = (pf_i > i) ? uni(lease_tab[i & 15]) : head;
       if (pf_i < i) pf_i = i;
@@ -2163,7 +2274,8 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
     lds_barrier();  // A
     if (uni(ctrl[0])) break;
     if (!noop_only) {
-      const uint32_t lease = uni(lease_tab[i & 15]);
+      // multi-row kernel: loader 0's lease table (the loaders landed this lease before barrier A)
+      const uint32_t lease = S == 1 ? uni(((const uint32_t*)(smem + kCtrlOff + kLeaseTabOff))[i & 15]) : uni(lease_tab[i & 15]);
       char* act = smem + kActOff;
       if (op == OP_ATTN) {
         attn_compute<S>(a, in, smem, act, lease, cw);
@@ -2184,7 +2296,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
 // one kernel per op family: the single-token plans' bodies (S = 0) and the multi-row plans' (S = 1)
 // are compiled separately, so neither family's register allocation carries the other's code
 template <int S>
-__global__ void __launch_bounds__(dev::kThreads, 1) mk_worker(KArgs a) {
+__global__ void __launch_bounds__(S == 1 ? dev::kThreadsM : dev::kThreads, 1) mk_worker(KArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t* base;
@@ -2198,15 +2310,16 @@ __global__ void __launch_bounds__(dev::kThreads, 1) mk_worker(KArgs a) {
     count = a.L;
     stride = kWords;
   }
-  if (threadIdx.x == 0) *(uint32_t*)(smem + dev::kCtrlOff) = 0u;
+  if (threadIdx.x < 16) ((uint32_t*)(smem + dev::kCtrlOff))[threadIdx.x] = 0u;  // abort flag .. loader counts
   __syncthreads();
-  if (wave == 0) dev::controller<S>(a, base, count, stride, smem);
+  if (S == 1 && wave >= dev::kNW) dev::loader<S>(a, base, count, stride, wave - dev::kNW, smem);
+  else if (wave == 0) dev::controller<S>(a, base, count, stride, smem);
   else dev::compute<S>(a, base, count, stride, wave - 1, smem);
 }
 
 hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec) {
   if (spec == 1)
-    hipLaunchKernelGGL(mk_worker<1>, dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+    hipLaunchKernelGGL(mk_worker<1>, dim3(grid), dim3(dev::kThreadsM), dev::kLdsBytes, stream, a);
   else
     hipLaunchKernelGGL(mk_worker<0>, dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
   return hipGetLastError();
@@ -2216,7 +2329,8 @@ hipError_t worker_occupancy(int* blocks_per_cu, int spec) {
   const void* f = spec == 1 ? (const void*)mk_worker<1> : (const void*)mk_worker<0>;
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, dev::kThreads, dev::kLdsBytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, spec == 1 ? dev::kThreadsM : dev::kThreads,
+                                                      dev::kLdsBytes);
 }
 
 }  // namespace mk
