@@ -306,6 +306,11 @@ mk_status get_table(mk_plan* p, const mk_tensors* t, uint64_t** out) {
   return MK_OK;
 }
 
+// Multi-row plans run with loader waves, which keep HBM streaming while the op bodies compute,
+// except the indexer front: its phases are a few tasks per worker, bound by dependency hops,
+// where the loaders' LDS barrier costs more than the streaming gains.
+static bool use_loaders(const mk_plan* p) { return p->hp.tp.spec == 1 && p->hp.cfg.workload != MK_INDEXER_FRONT; }
+
 mk_status check_runnable(mk_plan* p) {
   if (p->host_only) return fail(MK_ERR_INVALID, "plan was built without a device");
   const mk::HostPlan& hp = p->hp;
@@ -492,7 +497,7 @@ mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
   a.instrs = p->d_queue;
   a.L = p->hp.L;
   a.first_task = 0;
-  HIP_TRY(mk::launch_worker(a, p->hp.W, (hipStream_t)stream, p->hp.tp.spec));
+  HIP_TRY(mk::launch_worker(a, p->hp.W, (hipStream_t)stream, p->hp.tp.spec, use_loaders(p)));
   p->epoch++;
   p->cruns++;
   return MK_OK;
@@ -561,7 +566,7 @@ mk_status mk_run_graph_baseline(mk_plan* p, const mk_tensors* t, int32_t multist
       a.first_task = ops[k].first_task;
       a.L = ops[k].n_tasks;
       const int grid = std::min(ops[k].n_tasks, p->hp.W);
-      HIP_TRY(mk::launch_worker(a, grid, s, p->hp.tp.spec));
+      HIP_TRY(mk::launch_worker(a, grid, s, p->hp.tp.spec, use_loaders(p)));
       HIP_TRY(hipEventRecord(p->events[k], s));
     }
     for (int i = 1; i < n_streams; ++i) {  // join every forked stream back

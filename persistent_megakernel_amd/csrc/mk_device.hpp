@@ -95,7 +95,9 @@ static_assert(kLdsBytes <= 163840, "LDS budget");
 }  // namespace dev
 
 // spec: the plan's op family (0 single-token bodies, 1 multi-row bodies), one kernel instance each
-hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec);
+// loaders: the multi-row kernel with its loader waves (kThreadsM threads) rather than the eight
+// waves prefetching for themselves (kThreads)
+hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec, bool loaders);
 hipError_t worker_occupancy(int* blocks_per_cu, int spec);
 
 }  // namespace mk

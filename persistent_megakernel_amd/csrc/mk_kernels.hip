@@ -2101,7 +2101,7 @@ DEV bool wait_loaders(const char* smem, int i) {
   }
 }
 
-template <int S>
+template <int S, bool LD>
 DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride, char* smem) {
   uint32_t* ctrl = (uint32_t*)(smem + kCtrlOff);  // LDS; read and written only across barriers
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
@@ -2149,7 +2149,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
         signal_pend(a, pend);
         pending = false;
       }
-      if (ok && !wait_loaders(smem, i)) {  // the loaders' shares of this lease
+      if (LD && ok && !wait_loaders(smem, i)) {  // the loaders' shares of this lease
         record_timeout(a, in, 0xB0u, 0u);
         ok = false;
       }
@@ -2225,9 +2225,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
   }
 }
 
-template <int S>
+template <int S, bool LD>
 DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, int cw, char* smem) {
   const uint32_t* ctrl = (const uint32_t*)(smem + kCtrlOff);  // LDS abort flag
+  constexpr bool loaders = LD;  // loader waves stream the leases
   uint32_t* lease_tab = (uint32_t*)(smem + kCtrlOff + kLeaseTabOff) + cw * 32;  // [16] lease, [16] issued_end
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
   const int lookahead = (a.flags & MK_FLAG_NO_PREFETCH) ? 0 : 15;
@@ -2243,7 +2244,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       continue;
     }
     const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
-    if (S == 0 && !noop_only) {
+    if (!loaders && !noop_only) {
       // pages of every instruction before i are free now
       const uint32_t freed = (pf_i > i) ? uni(lease_tab[i & 15]) : head;
       if (pf_i < i) pf_i = i;
@@ -2274,8 +2275,8 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
     lds_barrier();  // A
     if (uni(ctrl[0])) break;
     if (!noop_only) {
-      // multi-row kernel: loader 0's lease table (the loaders landed this lease before barrier A)
-      const uint32_t lease = S == 1 ? uni(((const uint32_t*)(smem + kCtrlOff + kLeaseTabOff))[i & 15]) : uni(lease_tab[i & 15]);
+      // with loaders: loader 0's lease table (the loaders landed this lease before barrier A)
+      const uint32_t lease = loaders ? uni(((const uint32_t*)(smem + kCtrlOff + kLeaseTabOff))[i & 15]) : uni(lease_tab[i & 15]);
       char* act = smem + kActOff;
       if (op == OP_ATTN) {
         attn_compute<S>(a, in, smem, act, lease, cw);
@@ -2294,9 +2295,10 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
 }  // namespace dev
 
 // one kernel per op family: the single-token plans' bodies (S = 0) and the multi-row plans' (S = 1)
-// are compiled separately, so neither family's register allocation carries the other's code
-template <int S>
-__global__ void __launch_bounds__(S == 1 ? dev::kThreadsM : dev::kThreads, 1) mk_worker(KArgs a) {
+// are compiled separately, so neither family's register allocation carries the other's code; the
+// multi-row family comes with loader waves (LD) or with the eight waves prefetching for themselves
+template <int S, bool LD>
+__global__ void __launch_bounds__(LD ? dev::kThreadsM : dev::kThreads, 1) mk_worker(KArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t* base;
@@ -2312,23 +2314,30 @@ __global__ void __launch_bounds__(S == 1 ? dev::kThreadsM : dev::kThreads, 1) mk
   }
   if (threadIdx.x < 16) ((uint32_t*)(smem + dev::kCtrlOff))[threadIdx.x] = 0u;  // abort flag .. loader counts
   __syncthreads();
-  if (S == 1 && wave >= dev::kNW) dev::loader<S>(a, base, count, stride, wave - dev::kNW, smem);
-  else if (wave == 0) dev::controller<S>(a, base, count, stride, smem);
-  else dev::compute<S>(a, base, count, stride, wave - 1, smem);
+  if (LD && wave >= dev::kNW) dev::loader<S>(a, base, count, stride, wave - dev::kNW, smem);
+  else if (wave == 0) dev::controller<S, LD>(a, base, count, stride, smem);
+  else dev::compute<S, LD>(a, base, count, stride, wave - 1, smem);
 }
 
-hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec) {
-  if (spec == 1)
-    hipLaunchKernelGGL(mk_worker<1>, dim3(grid), dim3(dev::kThreadsM), dev::kLdsBytes, stream, a);
+hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec, bool loaders) {
+  if (spec == 1 && loaders)
+    hipLaunchKernelGGL((mk_worker<1, true>), dim3(grid), dim3(dev::kThreadsM), dev::kLdsBytes, stream, a);
+  else if (spec == 1)
+    hipLaunchKernelGGL((mk_worker<1, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
   else
-    hipLaunchKernelGGL(mk_worker<0>, dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+    hipLaunchKernelGGL((mk_worker<0, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
 hipError_t worker_occupancy(int* blocks_per_cu, int spec) {
-  const void* f = spec == 1 ? (const void*)mk_worker<1> : (const void*)mk_worker<0>;
+  // the multi-row family's larger block (with loader waves) bounds both of its instances
+  const void* f = spec == 1 ? (const void*)mk_worker<1, true> : (const void*)mk_worker<0, false>;
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
   if (e != hipSuccess) return e;
+  if (spec == 1) {
+    e = hipFuncSetAttribute((const void*)mk_worker<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
+    if (e != hipSuccess) return e;
+  }
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, spec == 1 ? dev::kThreadsM : dev::kThreads,
                                                       dev::kLdsBytes);
 }
