@@ -209,7 +209,7 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
 
     Waits (all "whole" unless stated): NORM_A on the previous layer's down finalizes; QKV tiles
     on NORM_A; QKV finalize on its tile's chunks ("tile_reduce"); attention on the QKV finalizes of
-    its kv group ("tile_cover"); a combine on its group's splits ("tile_reduce"); [QUANT_O on every
+    its kv group ("tile_cover"); a combine on its group's chain partials ("tile_reduce"); [QUANT_O on every
     combine]; O tiles on the combines [or QUANT_O];
     NORM_B on the O finalizes; gate/up tiles on NORM_B; [QUANT_M on the gate/up finalizes]; down
     tiles on the gate/up finalizes [or QUANT_M]."""
@@ -251,25 +251,51 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
             return (n0 - (Hq + Hkv) * d) // d
 
         proj(K_QKV, l, n_qkv, H, rt, (ev_na, M), lambda j: (ev_qkv[qkv_group(j)], 1))
-        # split-KV partials, one event per (request, kv head) counting its splits; then one combine
-        # task per (request, kv head) -- dealt round-robin like every task, so the combines spread
-        # over the workers instead of landing on whichever split happens to arrive last
+        # split-KV attention: the (request, kv head, split) tasks are laid out so that dealing them
+        # round-robin hands each worker a run of consecutive splits of one (request, kv head) -- a
+        # chain, which the worker folds into one running softmax state and writes as one partial.
+        # The splits, pair after pair, fill the columns 0 .. C-1 of the op's rounds of C tasks
+        # (C = min(W, tasks); a column is one worker's share, longer columns first); a chain is a
+        # column's maximal run inside one pair.  One event per pair counts its chains; one
+        # combine task per pair reduces their partials.
         row_attn = b.op_row()
         nsplit = [-(-int(ctx_lens[r]) // st) for r in range(R)]
-        ev_att = [b.event(nsplit[r]) for r in range(R) for _ in range(Hkv)]
-        for r in range(R):
-            ctx, ns = int(ctx_lens[r]), nsplit[r]
-            for hk in range(Hkv):
-                for s in range(ns):
-                    t0, t1 = s * st, min(ctx, (s + 1) * st)
-                    b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk], tiles_per_group)], [(ev_att[r * Hkv + hk], 1)],
-                           [l, r, hk, s, t0, t1, 0, 0, 0, ns])
+        seq = [(r, hk, s) for r in range(R) for hk in range(Hkv) for s in range(nsplit[r])]
+        n = len(seq)
+        C = min(W, n)
+        rounds = -(-n // C)
+        full = n - (rounds - 1) * C
+        lens = [rounds if j < full else rounds - 1 for j in range(C)]
+        starts = [sum(lens[:j]) for j in range(C)]
+        nchain = [0] * (R * Hkv)
+        chain = {}  # seq index -> (flags, slot): bit 0 continues the column's previous task, bit 1 ends a chain
+        for j in range(C):
+            for k in range(lens[j]):
+                i = starts[j] + k
+                pair = seq[i][0] * Hkv + seq[i][1]
+                cont = k > 0 and seq[i - 1][:2] == seq[i][:2]
+                end = k == lens[j] - 1 or seq[i + 1][:2] != seq[i][:2]
+                if not cont:
+                    nchain[pair] += 1
+                chain[i] = (int(cont) | int(end) << 1, nchain[pair] - 1)
+        ev_att = [b.event(nchain[pair]) for pair in range(R * Hkv)]
+        for k in range(rounds):
+            for j in range(C):
+                if k >= lens[j]:
+                    continue
+                i = starts[j] + k
+                r, hk, s = seq[i]
+                flags, slot = chain[i]
+                t0, t1 = s * st, min(int(ctx_lens[r]), (s + 1) * st)
+                b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk], tiles_per_group)],
+                       [(ev_att[r * Hkv + hk], 1)] if flags & 2 else [],
+                       [l, r, hk, s, t0, t1, 0, 0, 0, nsplit[r], flags, slot])
         row_comb = b.op_row()
         ev_oready = b.event(R * Hkv)
         for r in range(R):
             for hk in range(Hkv):
-                b.task(OP_COMB, row_comb, spec, [(ev_att[r * Hkv + hk], nsplit[r])], [(ev_oready, 1)],
-                       [l, r, hk, nsplit[r]])
+                b.task(OP_COMB, row_comb, spec, [(ev_att[r * Hkv + hk], nchain[r * Hkv + hk])], [(ev_oready, 1)],
+                       [l, r, hk, nchain[r * Hkv + hk]])
         o_wait = (ev_oready, R * Hkv)
         if fp8:
             row_qo = b.op_row()

@@ -32,7 +32,7 @@ struct KArgs {
 };
 
 constexpr uint32_t kModeGraph = 1u << 16;
-constexpr int kTraceWords = 16;  // per instruction: visible, ready, prologue, A, B, stored, arrived, done, poll
+constexpr int kTraceWords = 16;  // per instruction: visible, ready, prologue, A, B, stored, arrived, done, poll, ...
 constexpr int kNSub = 16;                  // sub-counters per event (spreads the atomics)
 constexpr int kSubStride = 32;             // words between sub-counters (128 bytes)
 constexpr int kEvStride = kNSub * kSubStride;

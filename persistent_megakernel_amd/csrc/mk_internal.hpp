@@ -50,7 +50,9 @@ enum Word : int {
   W_ARR_ID = 26,  // arrival group
   W_ARR_N = 27,   // arrival group size (0: no arrival group)
   W_ARR_RANK = 28, // rank of this task in its group
-  W_NSPLIT = 29   // multi-row attention: splits of the (request, kv head)
+  W_NSPLIT = 29,  // multi-row attention: splits of the (request, kv head)
+  W_CHAIN = 30,   // multi-row attention: bit 0 continues the worker's previous task's chain, bit 1 ends it
+  W_PSLOT = 31    // multi-row attention: the chain's partial slot in its (request, kv head)
 };
 
 // operand pointer table: 16 slots per op row

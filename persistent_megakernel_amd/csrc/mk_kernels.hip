@@ -513,21 +513,28 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
     }
     if (pf.mode == PF_ATTN && k < 2) {
       // block bb of the K (or V) span: the split's rows 4 bb .. 4 bb + 3 (one page: 4 divides the page
-      // size and t0), chunk c of row u at position c ^ (u mod 16)
-      const int P = a.sh.P;
-      int pidx = -1, page = 0;
-      for (uint32_t b = b0; b < b1; ++b) {
-        const uint32_t bb = b - pf.blk[k];
-        const int t = pf.t0 + (int)(4u * bb);
-        if (t / P != pidx) {
-          pidx = t / P;
-          page = (int)s_ld32(pf.bt + pidx);
-        }
-        uint32_t u = bb * 4u + (ln >> 4);
-        if (u >= (uint32_t)pf.nk) u = 4u * bb;  // beyond the tile: reload the block's first row
-        const size_t rowi = ((size_t)page * P + ((pf.t0 + (int)u) % P)) * a.sh.Hkv + pf.hk;
-        lds_dma16(base + rowi * 256u + (((ln & 15u) ^ ((4u * bb + (ln >> 4)) & 15u)) << 4), ring + ring_off(lease, b * 1024u));
+      // size and t0), chunk c of row u at position c ^ (u mod 16); lane ln takes row 4 bb + ln / 16,
+      // chunk ln mod 16.  Addresses advance row by row inside a page; the block table is read once
+      // per page.
+      const uint32_t P = (uint32_t)a.sh.P, rowb = (uint32_t)a.sh.Hkv * 256u;  // bytes between a head's tokens
+      const uint32_t r16 = ln >> 4, c16 = ln & 15u;
+      uint32_t bb = b0 - pf.blk[k];
+      const uint32_t tok = (uint32_t)pf.t0 + 4u * bb;
+      uint32_t pidx = tok / P, pos = tok - pidx * P;
+      auto page_base = [&](uint32_t pi) {  // the span's head in page pi
+        return base + ((size_t)(uint32_t)s_ld32(pf.bt + pi) * P * (uint32_t)a.sh.Hkv + (uint32_t)pf.hk) * 256u;
+      };
+      const char* pb = page_base(pidx);
+      for (uint32_t b = b0; b < b1; ++b, ++bb) {
+        const uint32_t u = 4u * bb + r16;
+        const uint32_t rp = u < (uint32_t)pf.nk ? pos + r16 : pos;  // beyond the tile: reload the block's first row
+        lds_dma16(pb + rp * rowb + ((c16 ^ (u & 15u)) << 4), ring + ring_off(lease, b * 1024u));
         ++issued;
+        pos += 4u;
+        if (pos == P && b + 1u < b1) {  // the next block starts the next page
+          pos = 0;
+          pb = page_base(++pidx);
+        }
       }
       continue;
     }
@@ -934,6 +941,10 @@ DEV float rows4_sum(float v) {
 //      the A operand of the next product -- and O_w = P V (16x16x16 bf16 on P's two bf16 parts);
 //   2. the eight waves' (m_w, l_w, O_w) merge with weights exp(m_w - max m_w).
 // Output: the split's normalised O [G][128] and its lse [G] in the output area.
+// Multi-row plans deal a worker consecutive splits of one (request, kv head), a chain: step 0 runs
+// on its first split only (q, k and v stay in LDS), each later split's (m_w, l_w, O_w) is folded
+// into the wave's running state in its own merge slots (both rescaled to the larger maximum), and
+// step 2 runs on its last split only, so the chain leaves one partial.
 template <int G, int S>
 DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act, uint32_t lease, int wv) {
   static_assert(G <= 16, "one matrix-core column per query head");
@@ -946,15 +957,21 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
   const uint32_t voff = nbk * 1024u;      // lease: K | V
   const char* ring = smem + kRingOff;
   const int ln = (int)lane();
-  if (wv < G) {
-    qk_norm_rope(act + kAttQraw + wv * 1024, act + kAttGq, act + kAttRope, sh.eps, act + kActQ + wv * 256);
-  } else if (wv == G) {
-    qk_norm_rope(act + kAttKraw, act + kAttGk, act + kAttRope, sh.eps, act + kActK);
-  } else if (wv == G + 1) {
-    const char* vr = act + kAttVraw;  // tagged records
-    ((uint32_t*)(act + kActV))[ln] = pack_bf2(ll_f32(vr, 2 * ln), ll_f32(vr, 2 * ln + 1));
+  // multi-row plans: a chain of splits on this worker folds into each wave's running state; its
+  // first split prepares q, k and v, its last merges the waves (single-token: chains of one)
+  const uint32_t chain = S == 1 ? in.w[W_CHAIN] : 2u;
+  const bool cont = (chain & 1u) != 0u, end = (chain & 2u) != 0u;
+  if (!cont) {
+    if (wv < G) {
+      qk_norm_rope(act + kAttQraw + wv * 1024, act + kAttGq, act + kAttRope, sh.eps, act + kActQ + wv * 256);
+    } else if (wv == G) {
+      qk_norm_rope(act + kAttKraw, act + kAttGk, act + kAttRope, sh.eps, act + kActK);
+    } else if (wv == G + 1) {
+      const char* vr = act + kAttVraw;  // tagged records
+      ((uint32_t*)(act + kActV))[ln] = pack_bf2(ll_f32(vr, 2 * ln), ll_f32(vr, 2 * ln + 1));
+    }
+    lds_barrier();
   }
-  lds_barrier();
   const int sub = ln & 15, grp = ln >> 4;
   const int per = (ntok + kNW - 1) / kNW;  // <= 16 tokens per wave
   const int tw0 = min(wv * per, ntok), tw1 = min(tw0 + per, ntok);
@@ -1026,15 +1043,39 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
   // O_w[head 4 grp + i][dim 8 sub + c] is element i of o[c]
   float* mrg = (float*)(act + kActMerge);  // [wave][G][128] partial P V, then [wave][G] (m_w, l_w)
   float* ml = mrg + kNW * G * 128;
+  float m_w = mw, l_w = lw;
+  float fo[4] = {0.f, 0.f, 0.f, 0.f}, fc[4] = {1.f, 1.f, 1.f, 1.f};  // weights of the state and of this split
+  if (S == 1 && cont) {
+    // the wave's state so far (this wave's own slots, from the chain's previous split): rescale
+    // both parts to the larger maximum; lane sub of row 0 holds head sub's weights
+    const f32x2 so = *(const f32x2*)(ml + (wv * G + (sub < G ? sub : 0)) * 2);
+    m_w = fmaxf(so.x, mw);
+    const float ao = so.x == -INFINITY ? 0.f : __expf(so.x - m_w);
+    const float ac = mw == -INFINITY ? 0.f : __expf(mw - m_w);
+    l_w = ao * so.y + ac * lw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fo[i] = __shfl(ao, 4 * grp + i);
+      fc[i] = __shfl(ac, 4 * grp + i);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * grp + i;
     if (h < G) {
-      *(f32x4*)(mrg + (wv * G + h) * 128 + 8 * sub) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
-      *(f32x4*)(mrg + (wv * G + h) * 128 + 8 * sub + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+      float* po = mrg + (wv * G + h) * 128 + 8 * sub;
+      f32x4 o0 = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]} * fc[i];
+      f32x4 o1 = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]} * fc[i];
+      if (S == 1 && cont) {
+        o0 += *(const f32x4*)po * fo[i];
+        o1 += *(const f32x4*)(po + 4) * fo[i];
+      }
+      *(f32x4*)po = o0;
+      *(f32x4*)(po + 4) = o1;
     }
   }
-  if (grp == 0 && sub < G) *(f32x2*)(ml + (wv * G + sub) * 2) = f32x2{mw, lw};
+  if (grp == 0 && sub < G) *(f32x2*)(ml + (wv * G + sub) * 2) = f32x2{m_w, l_w};
+  if (!end) return;  // the chain goes on: the state stays in this wave's slots
   lds_barrier();
   // merge the eight waves: weights exp(m_w - M) with M the largest m_w; lane o = j * 128 + d
   float* out = (float*)(smem + kOutOff);
@@ -1781,7 +1822,8 @@ DEV void o_store(const KArgs& a, const Instr& in, __amdgpu_buffer_rsrc_t ro, uin
 
 // Store the split's partial (and, for the split holding the new token, the cache rows).  M = 1
 // plans: record arrival; the split completing its group combines it (true for that worker).
-// Multi-row plans: signal the group's event; a combine task reduces it.
+// Multi-row plans: the last split of a chain stores the chain's partial and signals the group's
+// event; a combine task reduces the group's chains.
 template <int S>
 DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) {
   const Shapes& sh = a.sh;
@@ -1794,8 +1836,12 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
   float* part = (float*)s_ld64(row + ATT_PART);
   __amdgpu_buffer_rsrc_t rp = rsrc(part);
   const float* out = (const float*)(smem + kOutOff);
-  for (int e = (int)lane(); e < g * 129; e += 64)
-    st32(rp, (gbase + (uint32_t)s * pstride + e) * 4u, __float_as_uint(out[e]));
+  // multi-row plans: the partial of a chain of splits, by its last split, in the chain's slot
+  if (S == 0 || (in.w[W_CHAIN] & 2u) != 0u) {
+    const uint32_t slot = S == 1 ? in.w[W_PSLOT] : (uint32_t)s;
+    for (int e = (int)lane(); e < g * 129; e += 64)
+      st32(rp, (gbase + slot * pstride + e) * 4u, __float_as_uint(out[e]));
+  }
   if (s == ns - 1) {  // the split holding the new token writes its K / V row into the paged caches
     const int p = (int)in.w[W_P5] - 1;
     const int32_t* bt = (const int32_t*)s_ld64(row + ATT_BT) + (size_t)r * sh.maxp;
@@ -2050,21 +2096,33 @@ DEV void loader(const KArgs& a, const uint32_t* base, int count, int stride, int
   uint32_t head = 0, issued = 0;
   int j = 0;  // next instruction to lease
   int d = 0;  // instructions whose share has landed
+  int have = -1;  // the instruction whose prefetch descriptor pf / npg hold
+  Pf<S> pf;
+  uint32_t npg = 0;
   uint32_t idle = 0;
   while (d < count) {
     const int r = (int)uni(*retired);
     while (j < count && j <= r + lookahead) {
-      Instr nx;
-      fetch(base + (size_t)uni((uint32_t)j) * stride, nx);
-      uint32_t npg = 0;
-      Pf<S> pf;
-      if (nx.w[W_OPCODE] != OP_NOOP && !noop_only) {
-        pf_desc<S>(a, nx, pf);
-        npg = (pf_blocks(pf) + 15u) >> 4;
+      const bool tr0 = (a.flags & MK_FLAG_TRACE) && a.trace && k == 0 && lane() == 0;
+      if (have != j) {  // the descriptor is kept while the instruction waits for free pages
+        if (tr0) a.trace[((size_t)blockIdx.x * a.L + j) * kTraceWords + 11] = (uint32_t)rtc();  // loader 0: first look
+        Instr nx;
+        fetch(base + (size_t)uni((uint32_t)j) * stride, nx);
+        npg = 0;
+        if (nx.w[W_OPCODE] != OP_NOOP && !noop_only) {
+          pf_desc<S>(a, nx, pf);
+          npg = (pf_blocks(pf) + 15u) >> 4;
+        }
+        have = j;
+      }
+      if (npg) {
         const uint32_t freed = j > r ? uni(lease_tab[r & 15]) : head;  // pages before instruction r are free
         if (head + npg - freed > (uint32_t)kNPages) break;
-        if (npg) pf_issue<S>(a, pf, head, k, issued, smem, kLoaders);
+        if (tr0) a.trace[((size_t)blockIdx.x * a.L + j) * kTraceWords + 10] = (uint32_t)rtc();  // its pages are free
+        pf_issue<S>(a, pf, head, k, issued, smem, kLoaders);
       }
+      if ((a.flags & MK_FLAG_TRACE) && a.trace && k == 0 && lane() == 0)  // loader 0: lease issued
+        a.trace[((size_t)blockIdx.x * a.L + j) * kTraceWords + 5] = (uint32_t)rtc();
       lease_tab[j & 15] = head;
       lease_tab[16 + (j & 15)] = issued;
       head += npg;
@@ -2072,6 +2130,8 @@ DEV void loader(const KArgs& a, const uint32_t* base, int count, int stride, int
     }
     if (d < j) {  // the oldest leased instruction: wait for this loader's share, then publish it
       wait_vm_le(issued - uni(lease_tab[16 + (d & 15)]));
+      if ((a.flags & MK_FLAG_TRACE) && a.trace && k == 0 && lane() == 0)  // loader 0: its share landed
+        a.trace[((size_t)blockIdx.x * a.L + d) * kTraceWords + 6] = (uint32_t)rtc();
       ++d;
       if (lane() == 0) *done = (uint32_t)d;
       idle = 0;
@@ -2131,6 +2191,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     uint32_t poll = 0;
     bool ok = true;
     StageStamps sst{0, 0};
+    unsigned long long t_ev = 0, t_ld = 0;  // multi-row trace: events met, staging done
     if constexpr (m16) {
       // multi-row: wait for the event counters (the graph baseline's stream order guarantees them),
       // then stage what the op reads from LDS
@@ -2140,7 +2201,8 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
         pending = false;
       }
       ok = graph || wait_events(a, in, poll, wc);
-      if (ok && op == OP_ATTN) ok = attn_stage(a, in, act, false, poll, sst);
+      if (tracing) t_ev = rtc();
+      if (ok && op == OP_ATTN && (in.w[W_CHAIN] & 1u) == 0u) ok = attn_stage(a, in, act, false, poll, sst);  // a chain's first split
       if (ok && op == OP_GEMM) gemm_stage(a, in, act, staged);
       if (ok && op == OP_SCORE) score_stage(a, in, act);
       if (op != OP_GEMM) staged = 0;
@@ -2149,6 +2211,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
         signal_pend(a, pend);
         pending = false;
       }
+      if (tracing) t_ld = rtc();
       if (LD && ok && !wait_loaders(smem, i)) {  // the loaders' shares of this lease
         record_timeout(a, in, 0xB0u, 0u);
         ok = false;
@@ -2208,15 +2271,21 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       tr[2] = (uint32_t)t_pro;
       tr[3] = (uint32_t)t_a;
       tr[4] = (uint32_t)t_b;
-      tr[5] = (uint32_t)st.ack;
-      tr[6] = (uint32_t)st.arr;
+      if (!LD) {  // with loader waves: loader 0's issue and landing times of this lease
+        tr[5] = (uint32_t)st.ack;
+        tr[6] = (uint32_t)st.arr;
+      }
       tr[7] = (uint32_t)rtc();
       tr[8] = poll;
       tr[9] = (uint32_t)(c_b - c_a);  // shader clock cycles between the two compute barriers
-      tr[10] = (uint32_t)st.c1;
-      tr[11] = (uint32_t)st.c2;
+      if (!LD) {  // with loader waves: loader 0's first look at this lease and when its pages were free
+        tr[10] = (uint32_t)st.c1;
+        tr[11] = (uint32_t)st.c2;
+      }
       tr[12] = (uint32_t)sst.issue;
       tr[13] = (uint32_t)sst.landed;
+      tr[14] = (uint32_t)t_ev;
+      tr[15] = (uint32_t)t_ld;
     }
   }
   if (pending) {  // the last instruction's signals

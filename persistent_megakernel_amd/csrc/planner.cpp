@@ -126,7 +126,7 @@ bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, s
 // Multi-row (M = R x T <= 16) layer: row-task norms, projections as (64-row tile, K chunk) tasks
 // writing partial sums, one finalize task per row tile adding the chunks in K order and applying
 // the epilogue; FP8 plans quantise o and m per row.  The same rules as the oracle's builder.
-void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Builder& b, int& max_splits) {
+void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, int W, Builder& b, int& max_splits) {
   const int H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int g = Hq / Hkv, R = c.n_requests, M = R * c.tokens_per_request;
   const int spec = p.spec, kc = p.kc, st = p.s_tok, rt = kM16Rows;
@@ -169,29 +169,58 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, Buil
     };
     const int row_qf = proj(K_QKV, l, n_qkv, H, rt, {ev_na, (uint32_t)M}, row_na,
                             [&](int j) { return ev_qkv[qkv_group(j)]; });
-    // split-KV partials signal their (request, kv head) event; one combine task per group, dealt
-    // round-robin like every task (not left to whichever split arrives last)
+    // split-KV attention: the (request, kv head, split) tasks are laid out so that dealing them
+    // round-robin hands each worker a run of consecutive splits of one (request, kv head) -- a
+    // chain, folded into one running softmax state on chip and written as one partial.  The
+    // splits, pair after pair, fill columns 0 .. C-1 of the op's rounds of C tasks (C = min(W,
+    // tasks), a column being one worker's share, longer columns first); a chain is a column's
+    // maximal run inside one pair.  One event per pair counts its chains; one combine task per
+    // pair reduces their partials (dealt round-robin, not left to whichever chain ends last).
     const int row_attn = b.op_row(OP_ATTN, l, {row_qf});
-    std::vector<int> nsplit(R), ev_att((size_t)R * Hkv);
-    for (int r = 0; r < R; ++r) nsplit[r] = (ctx[r] + st - 1) / st;
-    for (int r = 0; r < R; ++r)
-      for (int hk = 0; hk < Hkv; ++hk) ev_att[(size_t)r * Hkv + hk] = b.event((uint32_t)nsplit[r]);
+    struct Split {
+      int pair, s;
+    };
+    std::vector<Split> seq;
+    std::vector<int> nsplit(R);
     for (int r = 0; r < R; ++r) {
-      const int cx = ctx[r], ns = nsplit[r];
-      max_splits = std::max(max_splits, ns);
+      nsplit[r] = (ctx[r] + st - 1) / st;
+      max_splits = std::max(max_splits, nsplit[r]);
       for (int hk = 0; hk < Hkv; ++hk)
-        for (int s = 0; s < ns; ++s) {
-          const int t0 = s * st, t1 = std::min(cx, (s + 1) * st);
-          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {{ev_att[(size_t)r * Hkv + hk], 1u}},
-                 {l, r, hk, s, t0, t1, 0, 0, 0, ns});
-        }
+        for (int s = 0; s < nsplit[r]; ++s) seq.push_back({r * Hkv + hk, s});
     }
+    const int n = (int)seq.size(), C = std::min(W, n), rounds = (n + C - 1) / C, full = n - (rounds - 1) * C;
+    std::vector<int> start(C), len(C), flags(n), slot(n), nchain((size_t)R * Hkv, 0);
+    for (int j = 0, at = 0; j < C; ++j) {
+      len[j] = j < full ? rounds : rounds - 1;
+      start[j] = at;
+      at += len[j];
+      for (int k = 0; k < len[j]; ++k) {
+        const int i = start[j] + k;
+        const bool cont = k > 0 && seq[i - 1].pair == seq[i].pair;
+        const bool end = k == len[j] - 1 || seq[i + 1].pair != seq[i].pair;
+        if (!cont) nchain[seq[i].pair]++;
+        flags[i] = (cont ? 1 : 0) | (end ? 2 : 0);
+        slot[i] = nchain[seq[i].pair] - 1;
+      }
+    }
+    std::vector<int> ev_att((size_t)R * Hkv);
+    for (int q = 0; q < R * Hkv; ++q) ev_att[q] = b.event((uint32_t)nchain[q]);
+    for (int k = 0; k < rounds; ++k)
+      for (int j = 0; j < C && k < len[j]; ++j) {
+        const int i = start[j] + k, r = seq[i].pair / Hkv, hk = seq[i].pair % Hkv, s = seq[i].s;
+        const int t0 = s * st, t1 = std::min((int)ctx[r], (s + 1) * st);
+        if (flags[i] & 2)
+          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {{ev_att[seq[i].pair], 1u}},
+                 {l, r, hk, s, t0, t1, 0, 0, 0, nsplit[r], flags[i], slot[i]});
+        else
+          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {},
+                 {l, r, hk, s, t0, t1, 0, 0, 0, nsplit[r], flags[i], slot[i]});
+      }
     const int row_comb = b.op_row(OP_COMB, l, {row_attn});
     const int ev_oready = b.event((uint32_t)(R * Hkv));
-    for (int r = 0; r < R; ++r)
-      for (int hk = 0; hk < Hkv; ++hk)
-        b.task(OP_COMB, row_comb, spec, {{ev_att[(size_t)r * Hkv + hk], (uint32_t)nsplit[r]}}, {{ev_oready, 1u}},
-               {l, r, hk, nsplit[r]});
+    for (int q = 0; q < R * Hkv; ++q)
+      b.task(OP_COMB, row_comb, spec, {{ev_att[q], (uint32_t)nchain[q]}}, {{ev_oready, 1u}},
+             {l, q / Hkv, q % Hkv, nchain[q]});
     std::pair<int, uint32_t> o_wait{ev_oready, (uint32_t)(R * Hkv)};
     int o_dep = row_comb;
     if (fp8) {
@@ -462,7 +491,7 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
             "and at most 16 rows";
       return MK_ERR_UNSUPPORTED;
     }
-    build_m16(c, ctx, p, b, max_splits);
+    build_m16(c, ctx, p, W, b, max_splits);
   }
   for (int l = 0; l < (p.spec == 0 ? c.num_layers : 0); ++l) {
     int row_qkv = b.op_row(OP_QKV, l, prev_down_row >= 0 ? std::vector<int>{prev_down_row} : std::vector<int>{});

@@ -61,3 +61,62 @@ def test_indexer_ragged_bit_exact():
             assert np.array_equal(plan.thresholds(), ref["thresholds"])
             oq.check_invariants(ref)
             plan.close()
+
+
+@pytest.mark.parametrize("W", [3, 7, 100, 256])
+def test_multi_row_attention_chains(W):
+    """Multi-row attention: bit-exact queues with ragged contexts, and the chains of splits they
+    encode.  A task continues a chain exactly when the worker's previous instruction is a split of
+    the same (request, kv head); it ends one exactly when the next is not; only chain ends signal;
+    each pair's chains have slots 0 .. n-1 and cover its splits once; its combine reduces n."""
+    ctx = [700, 1, 129, 384, 513]
+    cfg = dataclasses.replace(get_config("qwen3_8b_layer"), n_requests=len(ctx), context=max(ctx), num_layers=2)
+    plan, ref = _both(cfg, W, ctx)
+    assert np.array_equal(plan.queue(), ref["queue"])
+    assert np.array_equal(plan.thresholds(), ref["thresholds"])
+    plan.close()
+    oq.check_invariants(ref)
+    q, thr = ref["queue"], ref["thresholds"]
+    st = ref["params"]["s_tok"]
+    chains, splits, comb = {}, {}, {}
+    for w in range(q.shape[0]):
+        for i in range(q.shape[1]):
+            t = q[w, i]
+            if t[0] == oq.OP_COMB:
+                comb[tuple(int(v) for v in t[20:23])] = (int(t[23]), int(t[7]))
+            if t[0] != oq.OP_ATTN:
+                continue
+            key = tuple(int(v) for v in t[20:23])
+            same = lambda j: 0 <= j < q.shape[1] and q[w, j][0] == oq.OP_ATTN and tuple(int(v) for v in q[w, j][20:23]) == key
+            flags, slot = int(t[30]), int(t[31])
+            assert bool(flags & 1) == same(i - 1) and bool(flags & 2) == (not same(i + 1))
+            assert int(t[2]) == (1 if flags & 2 else 0)
+            if flags & 2:
+                assert int(t[15]) == 1
+            s, t0, t1 = int(t[23]), int(t[24]), int(t[25])
+            r = key[1]
+            assert (t0, t1) == (s * st, min(ctx[r], (s + 1) * st)) and int(t[29]) == -(-ctx[r] // st)
+            splits.setdefault(key, []).append(s)
+            chains.setdefault(key, set()).add(slot)
+    for key, ss in splits.items():
+        assert sorted(ss) == list(range(-(-ctx[key[1]] // st)))
+        n = len(chains[key])
+        assert chains[key] == set(range(n)) and comb[key] == (n, n)
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_layer", "qwen3_8b_layer_fp8"])
+def test_multi_row_attention_chain_lengths(name):
+    """At the full sizes on 256 workers the splits of each (request, kv head) form chains of equal
+    length covering contiguous token ranges: 4096 / 128 = 32 splits in two chains of 16 (8192: two
+    of 32), one chain per worker."""
+    cfg = get_config(name)
+    ref = oq.build_queue(cfg, 256)
+    q = ref["queue"]
+    ns = -(-cfg.context // ref["params"]["s_tok"])
+    for w in range(256):
+        att = [q[w, i] for i in range(q.shape[1]) if q[w, i][0] == oq.OP_ATTN]
+        assert len(att) == ns // 2
+        assert len({tuple(int(v) for v in t[20:23]) for t in att}) == 1
+        s = [int(t[23]) for t in att]
+        assert s == list(range(s[0], s[0] + ns // 2)) and s[0] % (ns // 2) == 0
+        assert [int(t[30]) for t in att] == [0] + [1] * (ns // 2 - 2) + [3] and len({int(t[31]) for t in att}) == 1
