@@ -65,8 +65,9 @@ constexpr int kThreadsM = kThreads + 64 * kLoaders;
 constexpr int kBarOff = 24;        // in the control area: arrivals at the eight waves' barrier
 constexpr int kRetiredOff = 28;    // in the control area: instructions the eight waves have finished
 constexpr int kDoneOff = 32;       // in the control area: [kLoaders] instructions whose lease share landed
+constexpr int kFetchedOff = 48;    // in the control area: instructions loader 0 has copied into the instruction ring
 static_assert(kLeaseTabOff + 7 * 32 * 4 <= kCtrlBytes, "control area");
-static_assert(kDoneOff + 4 * kLoaders <= kLeaseTabOff && kLoaders <= 7, "control area");
+static_assert(kDoneOff + 4 * kLoaders <= kFetchedOff && kFetchedOff + 4 <= kLeaseTabOff && kLoaders <= 7, "control area");
 constexpr int kLdsBytes = kCtrlOff + kCtrlBytes;  // all 160 KiB: one block per CU
 // attention sub-areas of the activation staging area
 constexpr int kMaxG = 5;       // GQA group (q heads per kv head) of the M = 1 attention body
@@ -88,6 +89,10 @@ constexpr int kActABytes = 16384;
 constexpr int kActD = kActA + kActABytes;   // [8 waves][64 lanes][4] fp32
 constexpr int kActRed = kActD + 8192;       // [2][8] fp32 per-wave partial reductions
 static_assert(kActRed + 64 <= kActBytes, "multi-row staging overflows the activation area");
+// multi-row kernel with loader waves: the next sixteen instructions (128 B each), copied by loader 0
+// as it walks the queue, at the end of the activation area (no multi-row layer op uses it)
+constexpr int kActInstr = kActBytes - 2048;
+static_assert(kActRed + 64 <= kActInstr && kActMerge + 8 * kMaxG * 130 * 4 <= kActInstr, "instruction ring overlaps staging");
 static_assert(kActMerge + 8 * kMaxG * 130 * 4 <= kActBytes, "attention merge area overflows the staging area");
 static_assert(kAttRope + 512 <= kAttQraw, "attention gains overlap the raw q staging");
 static_assert(kLdsBytes == 163840, "LDS budget");

@@ -156,6 +156,27 @@ DEV void fetch(const uint32_t* p, Instr& in) {
   }
 }
 
+// the instruction ring of the multi-row kernel with loader waves: slot i mod 16 of the activation
+// area's last 2 KiB (loader 0 writes it on its first look at instruction i; the controller reads it
+// once loader 0 has published i, instead of a scalar fetch from the queue in memory)
+DEV void put_instr(char* smem, int j, const Instr& in) {
+  if (__lane_id() == 0) {
+    u32x4* d = (u32x4*)(smem + dev::kActOff + dev::kActInstr + (j & 15) * 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d[k] = u32x4{in.w[4 * k], in.w[4 * k + 1], in.w[4 * k + 2], in.w[4 * k + 3]};
+  }
+}
+DEV void get_instr(const char* smem, int i, Instr& in) {
+  asm volatile("" ::: "memory");  // not before the read of the published count (LDS serves a wave in order)
+  const u32x4* s = (const u32x4*)(smem + dev::kActOff + dev::kActInstr + (i & 15) * 128);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4 v = s[k];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) in.w[4 * k + q] = __builtin_amdgcn_readfirstlane(v[q]);
+  }
+}
+
 // Device-scope (sc1) loads and stores through buffer resources; aux bit 4 = sc1 on gfx950.
 DEV __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
@@ -2108,6 +2129,10 @@ DEV void loader(const KArgs& a, const uint32_t* base, int count, int stride, int
         if (tr0) a.trace[((size_t)blockIdx.x * a.L + j) * kTraceWords + 11] = (uint32_t)rtc();  // loader 0: first look
         Instr nx;
         fetch(base + (size_t)uni((uint32_t)j) * stride, nx);
+        if (k == 0) {  // publish the words for the controller
+          put_instr(smem, j, nx);
+          if (lane() == 0) *(volatile uint32_t*)(smem + kCtrlOff + kFetchedOff) = (uint32_t)j + 1u;
+        }
         npg = 0;
         if (nx.w[W_OPCODE] != OP_NOOP && !noop_only) {
           pf_desc<S>(a, nx, pf);
@@ -2174,7 +2199,10 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
   bool pending = false;  // multi-row: the previous instruction's signals wait for its stores
   for (int i = 0; i < count; ++i) {
     Instr in;
-    fetch(base + (size_t)i * stride, in);
+    if (LD && (int)uni(*(volatile uint32_t*)(smem + kCtrlOff + kFetchedOff)) > i)
+      get_instr(smem, i, in);  // loader 0 has copied it into the instruction ring
+    else
+      fetch(base + (size_t)i * stride, in);
     const uint32_t op = in.w[W_OPCODE];
     if (op == OP_NOOP) {
       if (S == 1 && lane() == 0) *(volatile uint32_t*)(smem + kCtrlOff + kRetiredOff) = (uint32_t)i + 1u;
