@@ -93,6 +93,13 @@ static_assert(kActRed + 64 <= kActBytes, "multi-row staging overflows the activa
 // as it walks the queue, at the end of the activation area (no multi-row layer op uses it)
 constexpr int kActInstr = kActBytes - 2048;
 static_assert(kActRed + 64 <= kActInstr && kActMerge + 8 * kMaxG * 130 * 4 <= kActInstr, "instruction ring overlaps staging");
+// single-token kernel: the next eight instructions, copied by compute wave 0 as it prefetches, at the
+// end of the output area (attention output <= 4 x 129 floats, combine weights 64 x kMaxG + kMaxG x 3
+// floats, projection sums <= 128 floats), each slot with its instruction index + 1 in the control area
+constexpr int kOutInstr = kOutBytes - 1024;
+constexpr int kITagOff = 960;
+static_assert(4 * 129 * 4 <= kOutInstr && (64 * kMaxG + 3 * kMaxG) * 4 <= kOutInstr, "instruction ring overlaps outputs");
+static_assert(kLeaseTabOff + 7 * 32 * 4 <= kITagOff && kITagOff + 8 * 4 <= kCtrlBytes, "control area");
 static_assert(kActMerge + 8 * kMaxG * 130 * 4 <= kActBytes, "attention merge area overflows the staging area");
 static_assert(kAttRope + 512 <= kAttQraw, "attention gains overlap the raw q staging");
 static_assert(kLdsBytes == 163840, "LDS budget");

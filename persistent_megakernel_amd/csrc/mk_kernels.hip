@@ -177,6 +177,32 @@ DEV void get_instr(const char* smem, int i, Instr& in) {
   }
 }
 
+// the instruction ring of the single-token kernel: slot i mod 8 of the output area's last KiB, tagged
+// with i + 1; compute wave 0 writes the instructions it prefetches at most seven ahead of its own
+// (so never the slot of one the controller has yet to read)
+DEV void put_instr8(char* smem, int j, const Instr& in) {
+  if (__lane_id() == 0) {
+    u32x4* d = (u32x4*)(smem + dev::kOutOff + dev::kOutInstr + (j & 7) * 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d[k] = u32x4{in.w[4 * k], in.w[4 * k + 1], in.w[4 * k + 2], in.w[4 * k + 3]};
+    *(volatile uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff + (j & 7) * 4) = (uint32_t)j + 1u;
+  }
+}
+DEV bool get_instr8(const char* smem, int i, Instr& in) {
+  if (__builtin_amdgcn_readfirstlane(*(const volatile uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff + (i & 7) * 4)) !=
+      (uint32_t)i + 1u)
+    return false;
+  asm volatile("" ::: "memory");  // the words after their tag (LDS serves a wave in order)
+  const u32x4* s = (const u32x4*)(smem + dev::kOutOff + dev::kOutInstr + (i & 7) * 128);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4 v = s[k];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) in.w[4 * k + q] = __builtin_amdgcn_readfirstlane(v[q]);
+  }
+  return true;
+}
+
 // Device-scope (sc1) loads and stores through buffer resources; aux bit 4 = sc1 on gfx950.
 DEV __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
@@ -2201,7 +2227,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     Instr in;
     if (LD && (int)uni(*(volatile uint32_t*)(smem + kCtrlOff + kFetchedOff)) > i)
       get_instr(smem, i, in);  // loader 0 has copied it into the instruction ring
-    else
+    else if (S == 1 || !get_instr8(smem, i, in))  // single-token: compute wave 0 may have copied it
       fetch(base + (size_t)i * stride, in);
     const uint32_t op = in.w[W_OPCODE];
     if (op == OP_NOOP) {
@@ -2348,6 +2374,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       while (pf_i < count && pf_i <= i + lookahead) {
         Instr nx;
         fetch(base + (size_t)uni((uint32_t)pf_i) * stride, nx);  // pf_i is wave-uniform: scalar loads
+        if (S == 0 && cw == 0 && pf_i - i < 8) put_instr8(smem, pf_i, nx);  // for the controller
         if (nx.w[W_OPCODE] == OP_NOOP) {
           lease_tab[pf_i & 15] = head;
           lease_tab[16 + (pf_i & 15)] = issued;
@@ -2410,6 +2437,7 @@ __global__ void __launch_bounds__(LD ? dev::kThreadsM : dev::kThreads, 1) mk_wor
     stride = kWords;
   }
   if (threadIdx.x < 16) ((uint32_t*)(smem + dev::kCtrlOff))[threadIdx.x] = 0u;  // abort flag .. loader counts
+  if (threadIdx.x < 8) ((uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff))[threadIdx.x] = 0u;  // instruction ring tags
   __syncthreads();
   if (LD && wave >= dev::kNW) dev::loader<S>(a, base, count, stride, wave - dev::kNW, smem);
   else if (wave == 0) dev::controller<S, LD>(a, base, count, stride, smem);
