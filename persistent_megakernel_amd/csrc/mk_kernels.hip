@@ -177,23 +177,30 @@ DEV void get_instr(const char* smem, int i, Instr& in) {
   }
 }
 
-// the instruction ring of the single-token kernel: slot i mod 8 of the output area's last KiB, tagged
-// with i + 1; compute wave 0 writes the instructions it prefetches at most seven ahead of its own
-// (so never the slot of one the controller has yet to read)
+// the instruction ring of the kernels without loader waves: slot i mod 8, tagged with i + 1, of the
+// output area's last KiB (single-token) or of the activation area's ring (multi-row); compute wave 0
+// writes the instructions it prefetches at most seven ahead of its own (so never the slot of one the
+// controller has yet to read)
+template <int S>
+DEV char* ring8_slot(const char* smem, int j) {
+  return (char*)smem + (S == 0 ? dev::kOutOff + dev::kOutInstr : dev::kActOff + dev::kActInstr) + (j & 7) * 128;
+}
+template <int S>
 DEV void put_instr8(char* smem, int j, const Instr& in) {
   if (__lane_id() == 0) {
-    u32x4* d = (u32x4*)(smem + dev::kOutOff + dev::kOutInstr + (j & 7) * 128);
+    u32x4* d = (u32x4*)ring8_slot<S>(smem, j);
 #pragma unroll
     for (int k = 0; k < 8; ++k) d[k] = u32x4{in.w[4 * k], in.w[4 * k + 1], in.w[4 * k + 2], in.w[4 * k + 3]};
     *(volatile uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff + (j & 7) * 4) = (uint32_t)j + 1u;
   }
 }
+template <int S>
 DEV bool get_instr8(const char* smem, int i, Instr& in) {
   if (__builtin_amdgcn_readfirstlane(*(const volatile uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff + (i & 7) * 4)) !=
       (uint32_t)i + 1u)
     return false;
   asm volatile("" ::: "memory");  // the words after their tag (LDS serves a wave in order)
-  const u32x4* s = (const u32x4*)(smem + dev::kOutOff + dev::kOutInstr + (i & 7) * 128);
+  const u32x4* s = (const u32x4*)ring8_slot<S>(smem, i);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const u32x4 v = s[k];
@@ -2225,10 +2232,14 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
   bool pending = false;  // multi-row: the previous instruction's signals wait for its stores
   for (int i = 0; i < count; ++i) {
     Instr in;
-    if (LD && (int)uni(*(volatile uint32_t*)(smem + kCtrlOff + kFetchedOff)) > i)
-      get_instr(smem, i, in);  // loader 0 has copied it into the instruction ring
-    else if (S == 1 || !get_instr8(smem, i, in))  // single-token: compute wave 0 may have copied it
+    if (LD) {
+      if ((int)uni(*(volatile uint32_t*)(smem + kCtrlOff + kFetchedOff)) > i)
+        get_instr(smem, i, in);  // loader 0 has copied it into the instruction ring
+      else
+        fetch(base + (size_t)i * stride, in);
+    } else if (!get_instr8<S>(smem, i, in)) {  // compute wave 0 may have copied it
       fetch(base + (size_t)i * stride, in);
+    }
     const uint32_t op = in.w[W_OPCODE];
     if (op == OP_NOOP) {
       if (S == 1 && lane() == 0) *(volatile uint32_t*)(smem + kCtrlOff + kRetiredOff) = (uint32_t)i + 1u;
@@ -2374,7 +2385,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       while (pf_i < count && pf_i <= i + lookahead) {
         Instr nx;
         fetch(base + (size_t)uni((uint32_t)pf_i) * stride, nx);  // pf_i is wave-uniform: scalar loads
-        if (S == 0 && cw == 0 && pf_i - i < 8) put_instr8(smem, pf_i, nx);  // for the controller
+        if (cw == 0 && pf_i - i < 8) put_instr8<S>(smem, pf_i, nx);  // for the controller
         if (nx.w[W_OPCODE] == OP_NOOP) {
           lease_tab[pf_i & 15] = head;
           lease_tab[16 + (pf_i & 15)] = issued;
