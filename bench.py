@@ -193,7 +193,8 @@ def main() -> int:
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _counter_traffic(cfg.name),
-                     "kernel": "mk_worker<%d> (persistent megakernel, one launch per step)" % (1 if cfg.m > 1 else 0)},
+                     "kernel": "mk_worker<%s> (persistent megakernel, one launch per step)" % (
+                         "0, false" if cfg.m == 1 else "1, false" if indexer else "1, true")},
         "variants_us_per_step": variants,
     }
     if variants:
