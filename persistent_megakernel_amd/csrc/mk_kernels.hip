@@ -2250,6 +2250,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     const unsigned long long t_vis = tracing ? rtc() : 0;
     const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
     const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+    const uint64_t row_touch = s_ld64(row);  // the pointer row into the scalar cache before the epilogue reads it
     char* act = smem + kActOff;
     // the instruction's wait: its tagged inputs staged into LDS (the graph baseline's stream order
     // already guarantees them, so it stages without checking tags)
@@ -2329,6 +2330,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     } else {
       gemv_epilogue(a, in, smem, lm, st);
     }
+    asm volatile("" ::"s"(row_touch));
     if (tracing && a.trace && lane() == 0) {
       uint32_t* tr = a.trace + ((size_t)blockIdx.x * a.L + i) * kTraceWords;
       tr[0] = (uint32_t)t_vis;
