@@ -2272,15 +2272,15 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       if (ok && op == OP_GEMM) gemm_stage(a, in, act, staged);
       if (ok && op == OP_SCORE) score_stage(a, in, act);
       if (op != OP_GEMM) staged = 0;
-      if (pending) {  // the staging above waited for our stores too, when it staged anything
-        wait_vm0();
-        signal_pend(a, pend);
-        pending = false;
-      }
       if (tracing) t_ld = rtc();
       if (LD && ok && !wait_loaders(smem, i)) {  // the loaders' shares of this lease
         record_timeout(a, in, 0xB0u, 0u);
         ok = false;
+      }
+      if (pending) {  // the staging and the loaders' wait above mostly covered our stores' round trip
+        wait_vm0();
+        signal_pend(a, pend);
+        pending = false;
       }
     } else if (op == OP_ATTN)
       ok = attn_stage(a, in, act, !graph, poll, sst);
