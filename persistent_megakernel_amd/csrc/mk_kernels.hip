@@ -1561,8 +1561,7 @@ DEV void quant_row(const KArgs& a, const Instr& in, char* smem, int wv) {
 
 // Combine of one (request, kv head) on the eight waves: thread t takes output element t of the
 // group's g heads x 128 dims, o = sum_s exp(lse_s - L) O_s with L = log sum_s exp(lse_s), over the
-// partials in slot order (one per chain of splits), 32 at a time with a running maximum (online
-// rescaling)
+// splits in order, 32 at a time with a running maximum (online rescaling)
 DEV void comb_group(const KArgs& a, const Instr& in, int wv) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
