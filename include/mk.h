@@ -49,7 +49,9 @@ enum {
   MK_FLAG_NO_PREFETCH = 1u << 0, /* megakernel: no weight prefetch across instructions (ablation) */
   MK_FLAG_NOOP_ONLY = 1u << 1,   /* megakernel: run the queue with every op body skipped: the waits,
                                     stagings and output stores remain, weights are not read */
-  MK_FLAG_TRACE = 1u << 2        /* megakernel: record per-instruction timestamps */
+  MK_FLAG_TRACE = 1u << 2,       /* megakernel: record per-instruction timestamps */
+  MK_FLAG_DEBUG_GATHER = 1u << 3 /* both modes: record the physical cache slot of every K / V row and indexer
+                                    key the run gathers through the block table (mk_read_gather) */
 };
 
 /* Plain data, caller-owned, copied by mk_build_queue. */
@@ -178,6 +180,17 @@ mk_status mk_sync(mk_plan* plan, void* hip_stream);
  * barriers, when its outputs were acknowledged, when its arrival resolved (0 if none), when it
  * was done; word 8 holds the ticks spent polling; the rest are zero. */
 mk_status mk_read_trace(const mk_plan* plan, uint32_t* host_out, size_t n_words);
+
+/* Copy the gather record of the last run of an MK_FLAG_DEBUG_GATHER plan into host memory (synchronous).
+ * Each entry is the physical cache slot page * P + offset a run fetched for one token through the
+ * block table (the page walk of the MegaRTP page's E1 operand row: block_table and context_lens),
+ * or -1 where nothing was fetched (every run first sets all entries to -1):
+ *   MK_QWEN3_LAYER / MK_QWEN3_STEP: int32 [layers][n_requests][n_kv_heads][2 (K, V)][max_pages_per_req * P];
+ *     the tokens t < ctx_r - 1 of request r (the new token's row comes from the run itself)
+ *   MK_INDEXER_FRONT: int32 [n_requests][max_pages_per_req * P]; the keys t < ctx_r - T written before the run
+ * n_words: capacity of host_out in int32 entries (extra entries are left untouched).
+ * Errors: MK_ERR_INVALID when the plan was built without the flag. */
+mk_status mk_read_gather(const mk_plan* plan, int32_t* host_out, size_t n_words);
 
 const char* mk_last_error(void);
 void mk_plan_destroy(mk_plan* plan);

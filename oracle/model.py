@@ -31,8 +31,8 @@ from typing import Dict
 import numpy as np
 
 from . import ops
-from .numerics import (bf16_bits_to_f64, dequant_per_token, dequant_weight_blocks, e4m3_decode,
-                       f64_to_bf16_bits, quant_per_token, round_bf16, round_f32)
+from .numerics import (bf16_bits_to_f64, dequant_per_token, dequant_weight_blocks, e4m3_ambiguous, e4m3_decode,
+                       e4m3_other_code, f64_to_bf16_bits, quant_per_token, round_bf16, round_f32)
 
 
 def _w(inp: Dict[str, np.ndarray], name: str, layer: int, cfg) -> np.ndarray:
@@ -42,18 +42,28 @@ def _w(inp: Dict[str, np.ndarray], name: str, layer: int, cfg) -> np.ndarray:
     return bf16_bits_to_f64(inp[name][layer])
 
 
-def _quant(pre: np.ndarray, key: str, decide) -> tuple:
-    """Per-token e4m3 quantisation of ``pre``, or the (codes, scales) that ``decide[key]`` holds.
+def _quant(pre: np.ndarray, key: str, ties, out: Dict[str, np.ndarray]) -> tuple:
+    """Per-token e4m3 quantisation of ``pre`` (round to nearest even in the fp32 ratio pre / s).
 
-    A value within rounding of a code boundary may be coded either way by an evaluation that
-    sums in another order; a code step at the top binade is 1/14 of the row's largest value and
-    reaches every output of the next projection.  ``decide`` lets a caller continue the chain from
-    another evaluation's codes (checked by that caller to lie within one code step of ``pre``), so
-    that the rest of the chain is compared for the same decisions."""
-    if decide is not None and key in decide:
-        codes, s = decide[key]
-        return np.asarray(codes, dtype=np.uint8), np.asarray(s, dtype=np.float64)
-    return quant_per_token(pre)
+    ``ties`` (optional) resolves the oracle's own ambiguous decisions and nothing else.  A
+    value that lies within delta of the midpoint between two e4m3 codes may be coded either way
+    by an evaluation that reproduces it only to within delta (an fp32 evaluation that sums in
+    another order); one code step at the top binade is 1/14 of the row's largest value and
+    reaches every output of the next projection.  The oracle marks those elements itself:
+    ``ties.delta(key)`` gives (delta_rel, delta_abs) in code units and the ambiguous set is
+    {|v - midpoint| <= delta_rel |v| + delta_abs}.  ``ties.choose(key, v, codes, s, ambiguous)``
+    returns where to take the other code of the enclosing pair; a choice outside the ambiguous
+    set is an error.  Without ``ties`` every decision is the oracle's own."""
+    codes, s = quant_per_token(pre)
+    if ties is None:
+        return codes, s
+    v = round_f32(pre / s[..., None])
+    amb = e4m3_ambiguous(v, *ties.delta(key))
+    other = np.asarray(ties.choose(key, v, codes, s, amb), dtype=bool)
+    if np.any(other & ~amb):
+        raise ValueError(f"{key}: a code choice outside the oracle's ambiguity set")
+    out[key + "_ambiguous"] = amb
+    return np.where(other, e4m3_other_code(v, codes), codes), s
 
 
 def _w8a8(cfg, inp, name, layer, codes, scale):
@@ -61,12 +71,11 @@ def _w8a8(cfg, inp, name, layer, codes, scale):
 
 
 def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in: np.ndarray,
-                k_cache: np.ndarray, v_cache: np.ndarray, decide=None) -> Dict[str, np.ndarray]:
+                k_cache: np.ndarray, v_cache: np.ndarray, ties=None) -> Dict[str, np.ndarray]:
     """One decode layer.  x: decoded bf16 values [M, H]; r_in: fp32 values [M, H].
     k_cache / v_cache: this layer's decoded caches [pages, P, Hkv, d] (updated in place
     with the new rows).  Rows are requests (one token per request).
-    decide: optional FP8 codes and scales {"h1q", "oq", "h2q", "mq": (codes, s)} taken in place of
-    this layer's own quantisation at those points (see ``_quant``)."""
+    ties: optional resolution of ambiguous FP8 decisions at "h1q", "oq", "h2q", "mq" (``_quant``)."""
     H, d = cfg.hidden, cfg.head_dim
     Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
     g = Hq // Hkv
@@ -82,7 +91,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     out["r1"] = r1
     out["h1_pre"] = h1_pre
     if fp8:
-        h1q, s1 = _quant(h1_pre, "h1q", decide)
+        h1q, s1 = _quant(h1_pre, "h1q", ties, out)
         out["h1q"], out["s1"] = h1q, s1
         qkv = _w8a8(cfg, inp, "w_qkv", layer, h1q, s1)
     else:
@@ -116,7 +125,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     o_pre = o_pre.reshape(M, Hq * d)
     out["o_pre"] = o_pre
     if fp8:
-        oq, so = _quant(o_pre, "oq", decide)
+        oq, so = _quant(o_pre, "oq", ties, out)
         out["oq"], out["so"] = oq, so
         a_pre = _w8a8(cfg, inp, "w_o", layer, oq, so)
     else:
@@ -131,7 +140,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     out["h2_pre"] = h2_pre
     I = cfg.inter
     if fp8:
-        h2q, s2 = _quant(h2_pre, "h2q", decide)
+        h2q, s2 = _quant(h2_pre, "h2q", ties, out)
         out["h2q"], out["s2"] = h2q, s2
         gu = _w8a8(cfg, inp, "w_gu", layer, h2q, s2)
     else:
@@ -141,7 +150,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     m_pre = ops.silu_mul(gu[:, :I], gu[:, I:])
     out["m_pre"] = m_pre
     if fp8:
-        mq, sm = _quant(m_pre, "mq", decide)
+        mq, sm = _quant(m_pre, "mq", ties, out)
         out["mq"], out["sm"] = mq, sm
         y_pre = _w8a8(cfg, inp, "w_down", layer, mq, sm)
     else:
@@ -153,12 +162,12 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     return out
 
 
-def run_qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int = 0, decide=None) -> Dict[str, np.ndarray]:
+def run_qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int = 0, ties=None) -> Dict[str, np.ndarray]:
     """Single-layer workload: returns the layer outputs and the updated caches (decoded)."""
     k_cache = bf16_bits_to_f64(inp["k_cache"][layer])
     v_cache = bf16_bits_to_f64(inp["v_cache"][layer])
     out = qwen3_layer(cfg, inp, layer, bf16_bits_to_f64(inp["x"]), inp["r_in"].astype(np.float64),
-                      k_cache, v_cache, decide)
+                      k_cache, v_cache, ties)
     out["k_cache"], out["v_cache"] = k_cache, v_cache
     return out
 
@@ -176,7 +185,8 @@ def run_qwen3_step(cfg, inp: Dict[str, np.ndarray], keep_layers: bool = False) -
         if keep_layers:
             res["layers"].append(o)
         else:
-            res["layers"].append({k2: o[k2] for k2 in ("y_pre", "y", "r2", "slot_page", "slot_off", "k", "v")})
+            res["layers"].append({k2: o[k2] for k2 in ("y_pre", "y", "r2", "slot_page", "slot_off", "k", "v",
+                                                            "k_pre", "v_pre")})
         x, r = o["y"], o["r2"]
     r_f = ops.add_residual(x, r)
     hf_pre = ops.rmsnorm(r_f, bf16_bits_to_f64(inp["g_final"]), cfg.rms_eps)
@@ -188,8 +198,8 @@ def run_qwen3_step(cfg, inp: Dict[str, np.ndarray], keep_layers: bool = False) -
     return res
 
 
-def run_indexer_front(cfg, inp: Dict[str, np.ndarray], decide=None) -> Dict[str, np.ndarray]:
-    """decide: optional FP8 codes and scales {"hq", "qaq", "kq": (codes, s)} (see ``_quant``)."""
+def run_indexer_front(cfg, inp: Dict[str, np.ndarray], ties=None) -> Dict[str, np.ndarray]:
+    """ties: optional resolution of ambiguous FP8 decisions at "hq", "qaq", "kq" (``_quant``)."""
     H, qr, nh, hd = cfg.hidden, cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
     R, T = cfg.n_requests, cfg.tokens_per_request
     M = R * T
@@ -203,12 +213,12 @@ def run_indexer_front(cfg, inp: Dict[str, np.ndarray], decide=None) -> Dict[str,
 
     r1 = ops.add_residual(bf16_bits_to_f64(inp["x"]), inp["r_in"].astype(np.float64))
     h_pre = ops.rmsnorm(r1, bf16_bits_to_f64(inp["g_norm"]), cfg.rms_eps)
-    hq, sh = _quant(h_pre, "hq", decide)
+    hq, sh = _quant(h_pre, "hq", ties, out)
     out.update(r1=r1, h_pre=h_pre, hq=hq, sh=sh)
     # B0
     qa = w8a8("w_qa", hq, sh)
     qa_n = ops.rmsnorm(qa, bf16_bits_to_f64(inp["g_qa"]), cfg.rms_eps)
-    qaq, sqa = _quant(qa_n, "qaq", decide)
+    qaq, sqa = _quant(qa_n, "qaq", ties, out)
     out.update(qa=qa, qa_n=qa_n, qaq=qaq, sqa=sqa)
     # C0
     w_pre = w8a8("w_w", hq, sh)
@@ -217,7 +227,7 @@ def run_indexer_front(cfg, inp: Dict[str, np.ndarray], decide=None) -> Dict[str,
     # B1
     k_lin = w8a8("w_k", hq, sh)
     k_pre = ops.rope_neox(k_lin, pos, cfg.rope_theta)
-    kq, sk = _quant(k_pre, "kq", decide)
+    kq, sk = _quant(k_pre, "kq", ties, out)
     out.update(k_lin=k_lin, k_pre=k_pre, kq=kq, sk=sk)
     page, off = ops.cache_slots(inp["block_table"], pos, req, cfg.page_size)
     key_cache = inp["key_cache"].copy()

@@ -140,3 +140,46 @@ def dequant_weight_blocks(codes: np.ndarray, s: np.ndarray, block: int = 128) ->
     n, k = v.shape
     sf = np.repeat(np.repeat(np.asarray(s, dtype=np.float64), block, axis=0), block, axis=1)[:n, :k]
     return v * sf
+
+
+# ---------------------------------------------------------------------------------------------
+# Rounding margins.  A value that an fp32 evaluation reproduces only to within delta may round
+# to either code of the pair enclosing it when it lies within delta of that pair's midpoint;
+# everywhere else round-to-nearest-even fixes the code.  These helpers give the oracle's own
+# measure of that: they are the format definition (the grid, its midpoints) and nothing else.
+
+_E4M3_GRID = np.unique(np.abs(_E4M3_VALUES[~np.isnan(_E4M3_VALUES)]))  # 0, 2^-9, ..., 448 ascending
+
+
+def e4m3_enclosing(v: np.ndarray):
+    """(lo, hi): the adjacent e4m3 magnitudes with lo <= |v| < hi; lo = hi = 448 from 448 up."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    i = np.searchsorted(_E4M3_GRID, a, side="right")
+    top = len(_E4M3_GRID) - 1
+    lo = _E4M3_GRID[np.clip(i - 1, 0, top)]
+    hi = _E4M3_GRID[np.clip(i, 0, top)]
+    return lo, hi
+
+
+def e4m3_midpoint_margin(v: np.ndarray) -> np.ndarray:
+    """Distance from |v| to the midpoint of its enclosing pair (the point where round-to-nearest
+    changes its choice); infinite from 448 up, where the satfinite clamp decides."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    lo, hi = e4m3_enclosing(a)
+    return np.where(a >= E4M3_MAX, np.inf, np.abs(a - 0.5 * (lo + hi)))
+
+
+def e4m3_ambiguous(v: np.ndarray, delta_rel: float, delta_abs: float) -> np.ndarray:
+    """True where |v| lies within delta_rel |v| + delta_abs of a rounding midpoint."""
+    v = np.asarray(v, dtype=np.float64)
+    return e4m3_midpoint_margin(v) <= delta_rel * np.abs(v) + delta_abs
+
+
+def e4m3_other_code(v: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """The code of the other member of the pair enclosing v (same sign as v): the code a rounding
+    on the other side of the midpoint gives.  From 448 up the pair is (448, 448)."""
+    v = np.asarray(v, dtype=np.float64)
+    lo, hi = e4m3_enclosing(v)
+    chosen = np.abs(e4m3_decode(codes))
+    other = np.where(chosen == lo, hi, lo)
+    return e4m3_encode(np.where(np.signbit(v), -other, other))

@@ -80,11 +80,17 @@ def cache_slots(block_table: np.ndarray, positions: np.ndarray, request_of_row: 
     return page, pos % page_size
 
 
-def gather_tokens(cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int, page_size: int) -> np.ndarray:
-    """Tokens 0..n_tokens-1 of one request from a paged cache [pages, P, ...] via its page list."""
+def token_slots(block_table_row: np.ndarray, n_tokens: int, page_size: int) -> np.ndarray:
+    """The page walk: physical slot page * P + offset of tokens 0..n_tokens-1 of one request, with
+    page = block_table_row[t // P] and offset = t % P (the block table maps logical to physical pages)."""
     t = np.arange(n_tokens)
-    pages = np.asarray(block_table_row, np.int64)[t // page_size]
-    return cache[pages, t % page_size]
+    return np.asarray(block_table_row, np.int64)[t // page_size] * page_size + t % page_size
+
+
+def gather_tokens(cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int, page_size: int) -> np.ndarray:
+    """Tokens 0..n_tokens-1 of one request from a paged cache [pages, P, ...] via its page walk."""
+    slots = token_slots(block_table_row, n_tokens, page_size)
+    return cache[slots // page_size, slots % page_size]
 
 
 def softmax(s: np.ndarray) -> np.ndarray:

@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MK_OK, MK_ERR_INVALID, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_NOMEM, MK_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
 MK_QWEN3_LAYER, MK_QWEN3_STEP, MK_INDEXER_FRONT = 0, 1, 2
-MK_FLAG_NO_PREFETCH, MK_FLAG_NOOP_ONLY, MK_FLAG_TRACE = 1, 2, 4
+MK_FLAG_NO_PREFETCH, MK_FLAG_NOOP_ONLY, MK_FLAG_TRACE, MK_FLAG_DEBUG_GATHER = 1, 2, 4, 8
 MK_MAX_TENSORS = 32
 QWEN3_TENSORS = ["w_qkv", "w_o", "w_gu", "w_down", "g_attn", "g_mlp", "g_q", "g_k", "k_cache", "v_cache",
                  "block_table", "context_lens", "x", "r_in", "y_out", "r2_out", "workspace",
@@ -63,10 +63,12 @@ _lib.mk_run_layer.argtypes = [_P, ctypes.POINTER(MkTensors), _P]
 _lib.mk_run_graph_baseline.argtypes = [_P, ctypes.POINTER(MkTensors), ctypes.c_int32, _P]
 _lib.mk_sync.argtypes = [_P, _P]
 _lib.mk_read_trace.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t]
+_lib.mk_read_gather.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), ctypes.c_size_t]
 _lib.mk_plan_destroy.argtypes = [_P]
 _lib.mk_plan_destroy.restype = None
 for _f in ("mk_build_queue", "mk_plan_queue", "mk_plan_events", "mk_plan_info", "mk_plan_workspace_bytes",
-           "mk_plan_workspace_region", "mk_run_layer", "mk_run_graph_baseline", "mk_sync", "mk_read_trace"):
+           "mk_plan_workspace_region", "mk_run_layer", "mk_run_graph_baseline", "mk_sync", "mk_read_trace",
+           "mk_read_gather"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -176,6 +178,20 @@ class Plan:
         out = np.zeros((W, L, 16), dtype=np.uint32)
         _check(_lib.mk_read_trace(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), out.size),
                "mk_read_trace")
+        return out
+
+
+    def read_gather(self) -> np.ndarray:
+        """The gather record of the last run (MK_FLAG_DEBUG_GATHER), shaped as mk_read_gather lays it out."""
+        c = self.cfg
+        tokens = int(c.pages_per_request) * int(c.page_size)
+        if c.workload == "indexer_front":
+            shape = (c.n_requests, tokens)
+        else:
+            shape = (c.num_layers, c.n_requests, c.n_kv_heads, 2, tokens)
+        out = np.zeros(shape, dtype=np.int32)
+        _check(_lib.mk_read_gather(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size),
+               "mk_read_gather")
         return out
 
 

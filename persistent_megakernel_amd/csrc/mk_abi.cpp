@@ -48,6 +48,8 @@ struct mk_plan {
   float* d_rope = nullptr;   // per row: (cos, sin) at the row's position, [M][head_dim / 2][2]
   int32_t* d_pos = nullptr;  // per row: position of the row's token
   uint32_t* d_trace = nullptr;
+  int32_t* d_gather = nullptr;  // MK_FLAG_DEBUG_GATHER: physical slots of the gathered rows
+  size_t gather_words = 0;
   size_t events_bytes = 0, arrivals_bytes = 0;
   uint32_t epoch = 0;  // megakernel runs so far; never reset (record tags must not repeat)
   uint32_t cruns = 0;  // megakernel runs since the event counters were last zeroed
@@ -354,6 +356,7 @@ mk::KArgs base_args(const mk_plan* p, const uint64_t* table) {
   a.arrivals = p->d_arrivals;
   a.err = p->d_err;
   a.trace = p->d_trace;
+  a.gather = p->d_gather;
   a.tag0 = p->salt + p->epoch * 1024u;
   a.run = p->cruns;
   a.flags = p->hp.cfg.flags;
@@ -439,6 +442,13 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
     HIP_TRY(hipMalloc(&p->d_trace, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
     HIP_TRY(hipMemset(p->d_trace, 0, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
   }
+  if (c.flags & MK_FLAG_DEBUG_GATHER) {  // one slot per (layer, request, kv head, K|V, token) or (request, key)
+    const size_t tokens = (size_t)c.max_pages_per_req * c.page_size;
+    p->gather_words = c.workload == MK_INDEXER_FRONT ? (size_t)c.n_requests * tokens
+                                                     : (size_t)c.num_layers * c.n_requests * c.n_kv_heads * 2 * tokens;
+    HIP_TRY(hipMalloc(&p->d_gather, p->gather_words * 4));
+    HIP_TRY(hipMemset(p->d_gather, 0xFF, p->gather_words * 4));
+  }
   *out = p.release();
   return MK_OK;
 }
@@ -493,6 +503,7 @@ mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
   if ((st = get_table(p, t, &table)) != MK_OK) return st;
   if (new_set)  // a workspace first seen by this plan: no stale record may carry one of its tags
     HIP_TRY(hipMemsetAsync((void*)t->ptr[ws_index(p->hp.cfg)], 0, p->hp.workspace_bytes, (hipStream_t)stream));
+  if (p->d_gather) HIP_TRY(hipMemsetAsync(p->d_gather, 0xFF, p->gather_words * 4, (hipStream_t)stream));
   mk::KArgs a = base_args(p, table);
   a.instrs = p->d_queue;
   a.L = p->hp.L;
@@ -579,6 +590,7 @@ mk_status mk_run_graph_baseline(mk_plan* p, const mk_tensors* t, int32_t multist
     HIP_TRY(hipGraphInstantiate(&ge.exec, ge.graph, nullptr, nullptr, 0));
     it = p->graphs.emplace(key, ge).first;
   }
+  if (p->d_gather) HIP_TRY(hipMemsetAsync(p->d_gather, 0xFF, p->gather_words * 4, stream));  // outside the graph
   HIP_TRY(hipGraphLaunch(it->second.exec, stream));
   return MK_OK;
 }
@@ -610,6 +622,13 @@ mk_status mk_read_trace(const mk_plan* p, uint32_t* out, size_t n_words) {
   return MK_OK;
 }
 
+mk_status mk_read_gather(const mk_plan* p, int32_t* out, size_t n_words) {
+  if (!p || !out) return fail(MK_ERR_INVALID, "null argument");
+  if (!p->d_gather) return fail(MK_ERR_INVALID, "plan was not built with MK_FLAG_DEBUG_GATHER");
+  HIP_TRY(hipMemcpy(out, p->d_gather, std::min(p->gather_words, n_words) * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
 void mk_plan_destroy(mk_plan* p) {
   if (!p) return;
   for (auto& kv : p->graphs) {
@@ -627,6 +646,7 @@ void mk_plan_destroy(mk_plan* p) {
   (void)hipFree(p->d_rope);
   (void)hipFree(p->d_pos);
   if (p->d_trace) (void)hipFree(p->d_trace);
+  if (p->d_gather) (void)hipFree(p->d_gather);
   delete p;
 }
 

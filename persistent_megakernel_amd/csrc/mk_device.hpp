@@ -25,6 +25,7 @@ struct KArgs {
   uint32_t* arrivals;      // [A], kSubStride words apart, self re-arming
   uint32_t* err;           // device error record: flag, worker, task, event, value, target
   uint32_t* trace;         // [W, L, kTraceWords] or null
+  int32_t* gather;         // MK_FLAG_DEBUG_GATHER: the physical cache slot of every gathered K / V row or key, or null
   uint32_t tag0;           // megakernel: this run's record tag base (plan salt + runs so far * 1024)
   uint32_t run;            // megakernel: runs since the event counters were zeroed (targets (run + 1) * threshold)
   uint32_t flags;          // MK_FLAG_* | kModeGraph

@@ -394,7 +394,14 @@ struct Pf : PfFrag<S> {
   uint32_t mode;
   const int32_t* bt;  // attention: block-table row of the request
   int t0, nk, hk;
+  uint64_t gout;  // MK_FLAG_DEBUG_GATHER: address of the gathered rows' physical slots (token t0 first), or 0
 };
+// one word of the gather record (MK_FLAG_DEBUG_GATHER only): a plain vector store issued as assembly, so
+// that the compiler's lowering of the surrounding LDS-pointer arithmetic is left as it is without the flag
+// (read by the host after the run; nothing in the kernel reads it back)
+DEV void gather_put(uint64_t addr, uint32_t v) {
+  asm volatile("global_store_dword %0, %1, off" ::"v"(addr), "v"(v) : "memory");
+}
 DEV uint32_t blocks_of(uint32_t bytes) { return (bytes + 1023u) >> 10; }
 
 // span k of the descriptor (k is a compile-time constant at every call: no indexed registers)
@@ -436,6 +443,7 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
   pf.blk[0] = 0;
   pf.n = 0;
   pf.total = 0;
+  pf.gout = 0;
   pf.mode = op == OP_ATTN ? PF_ATTN : PF_SPANS;
   if constexpr (S == 1) if (op == OP_GEMM) {
     // 64 KiB: block b = 16 nb + q holds 64 bytes of each of the tile rows [16 nb, 16 nb + 16) (K
@@ -472,6 +480,7 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
     const uint32_t lim = min(t1, ctx - T), nko = lim > t0 ? lim - t0 : 0u;
     pf.mode = PF_KEYS;
     pf.bt = (const int32_t*)s_ld64(row + SC_BT) + (size_t)r * sh.maxp;
+    if (a.gather) pf.gout = (uint64_t)(uintptr_t)(a.gather + (size_t)r * (uint32_t)(sh.maxp * sh.P) + t0);  // [request][token]
     pf.t0 = (int)t0;
     pf.nk = (int)nko;
     pf_set<0>(pf, (const void*)s_ld64(row + SC_CACHE), nko * 128u);
@@ -484,6 +493,9 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
     const int t0 = in.w[W_P4], t1 = in.w[W_P5];
     const bool last = s == attn_splits<S>(in) - 1;
     pf.bt = (const int32_t*)s_ld64(row + ATT_BT) + (size_t)r * sh.maxp;
+    if (a.gather)  // [layer][request][kv head][K, V][token]
+      pf.gout = (uint64_t)(uintptr_t)(a.gather + ((((size_t)in.w[W_LAYER] * (uint32_t)(sh.M / sh.T) + (uint32_t)r) *
+                                                       (uint32_t)sh.Hkv + (uint32_t)hk) * 2u) * (uint32_t)(sh.maxp * sh.P) + t0);
     pf.t0 = t0;
     pf.hk = hk;
     pf.nk = (last ? t1 - 1 : t1) - t0;
@@ -561,6 +573,8 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
             lds_dma16(pf.src[1] + (size_t)slot * 4u + ln * 16u, sdst);
           lds_dma16(base + (size_t)slot * 128u + off, ring + ring_off(lease, b * 1024u));
           issued += 2u;
+          if (pf.gout != 0u && (ln & 7u) == 0u && 8u * b + (ln >> 3) < (uint32_t)pf.nk)
+            gather_put(pf.gout + 4u * (8u * b + (ln >> 3)), slot + (ln >> 3));
         }
         continue;
       }
@@ -575,19 +589,25 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
       uint32_t bb = b0 - pf.blk[k];
       const uint32_t tok = (uint32_t)pf.t0 + 4u * bb;
       uint32_t pidx = tok / P, pos = tok - pidx * P;
-      auto page_base = [&](uint32_t pi) {  // the span's head in page pi
-        return base + ((size_t)(uint32_t)s_ld32(pf.bt + pi) * P * (uint32_t)a.sh.Hkv + (uint32_t)pf.hk) * 256u;
+      uint32_t pg = (uint32_t)s_ld32(pf.bt + pidx);  // physical page of block-table entry pidx
+      auto page_base = [&](uint32_t page) {  // the span's head in physical page `page`
+        return base + ((size_t)page * P * (uint32_t)a.sh.Hkv + (uint32_t)pf.hk) * 256u;
       };
-      const char* pb = page_base(pidx);
+      const char* pb = page_base(pg);
+      const uint64_t go = pf.gout ? pf.gout + 4u * (k ? (uint32_t)(a.sh.maxp * a.sh.P) : 0u) : 0u;  // K or V slots
       for (uint32_t b = b0; b < b1; ++b, ++bb) {
         const uint32_t u = 4u * bb + r16;
         const uint32_t rp = u < (uint32_t)pf.nk ? pos + r16 : pos;  // beyond the tile: reload the block's first row
         lds_dma16(pb + rp * rowb + ((c16 ^ (u & 15u)) << 4), ring + ring_off(lease, b * 1024u));
         ++issued;
+        // the slot this lane fetched, recorded by all 16 lanes of its row (one word); a row past the split's
+        // tokens (the last block of the last split) re-fetches the block's first row and records that
+        if (go != 0u) gather_put(go + 4u * u, pg * P + rp);
         pos += 4u;
         if (pos == P && b + 1u < b1) {  // the next block starts the next page
           pos = 0;
-          pb = page_base(++pidx);
+          pg = (uint32_t)s_ld32(pf.bt + ++pidx);
+          pb = page_base(pg);
         }
       }
       continue;

@@ -25,18 +25,6 @@ def bf16_excess(gpu: np.ndarray, pre: np.ndarray, tol: float) -> float:
     return float(np.max(np.abs(gpu - pre) - allow)) if gpu.size else 0.0
 
 
-def e4m3_codes_ok(codes: np.ndarray, s: np.ndarray, pre: np.ndarray) -> bool:
-    """Each per-token e4m3 code is one of the two codes enclosing pre / s (either may be taken at a
-    rounding boundary): |decode - v| <= the code spacing at |v| (2^(e-3) in binade [2^e, 2^(e+1)),
-    2^-9 below 2^-6), v = pre / s."""
-    from oracle.numerics import e4m3_decode
-    s = np.asarray(s, dtype=np.float64)[:, None]
-    v = np.asarray(pre, dtype=np.float64) / s
-    a = np.abs(v)
-    step = np.where(a >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3), 2.0 ** -9)
-    return bool(np.all(np.abs(e4m3_decode(codes) - v) <= step * (1 + 1e-6)))
-
-
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     b = t.detach().cpu().numpy().view(np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)

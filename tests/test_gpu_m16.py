@@ -6,14 +6,16 @@ y and r2 and on the intermediates, against the oracle value before its output ro
 the layer materialises in bf16 passes when it is the bf16 rounding of a value within that error
 (bf16 spacing alone exceeds 2e-2 from |v| >= 8).  Cache writes: the written slot set is exact
 (every other byte of both caches is unchanged bit for bit).
-FP8 quantisation is a decision: a value within rounding of a code boundary may be coded either way
-by an evaluation that sums in another order, and one code step at the top binade (1/14 of the row's
-largest value) reaches every output of the next projection.  So each of the GPU's per-token codes
-is checked to be one of the two codes enclosing the oracle's value (its scale the oracle's), and the
-oracle then continues from the GPU's codes; everything after is compared for the same decisions.
-At the full sizes the oracle runs on a sample of the requests: the rows of the layer are
+FP8 decisions (tests/fp8_check.py): at each of the four per-token quantisation points the GPU's
+code equals the oracle's round-to-nearest-even code except inside the ambiguity set the oracle
+computes from its own values (within delta of a rounding midpoint); there it is one of the two
+enclosing codes, and the oracle continues with that choice -- nowhere else.  The fully
+independent oracle (no choice taken from the GPU) is run too: r2 is compared with it at the
+tolerance, and its y error is reported (a code taken the other way at an ambiguous point of o
+moves the next projection's inputs and cascades; measured in the design notes).
+At the full sizes the oracle runs request by request in chunks: the rows of the layer are
 independent requests, so a request's outputs depend only on its own row, its own cache pages and
-the shared weights; the sample's pages are copied into a compact pool with a remapped block table.
+the shared weights; a chunk's pages are copied into a compact pool with a remapped block table.
 """
 import dataclasses
 import sys
@@ -23,7 +25,7 @@ import pytest
 import torch
 
 from oracle import model
-from oracle.numerics import bf16_bits_to_f64, quant_per_token
+from oracle.numerics import bf16_bits_to_f64, e4m3_decode
 from workloads import get_config, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -74,36 +76,39 @@ def _decisions(run, rows):
 
 
 def _oracle(cfg, inp, run, rows):
-    """The oracle's layer for the given rows (inputs already restricted to them).  On the FP8 path it
-    continues from the GPU's codes, each checked against the oracle's value at that point."""
-    from gpu_helpers import e4m3_codes_ok
+    """(resolved, independent) oracle layers for the given rows (inputs already restricted to them).
+    bf16: both are the plain oracle.  FP8: ``resolved`` checks every GPU code against the oracle's
+    own at each quantisation point and continues with the GPU's choice only inside the oracle's
+    ambiguity set; ``independent`` takes no choice from the GPU."""
+    from fp8_check import KernelTies
     if not cfg.act_fp8:
-        return model.run_qwen3_layer(cfg, inp)
-    dec = _decisions(run, rows)
-    ref = model.run_qwen3_layer(cfg, inp, decide=dec)
-    for key, pre in (("h1q", "h1_pre"), ("oq", "o_pre"), ("h2q", "h2_pre"), ("mq", "m_pre")):
-        codes, s = dec[key]
-        own, s_own = quant_per_token(ref[pre])
-        assert np.allclose(s, s_own, rtol=1e-4), f"{key} scales"
-        assert e4m3_codes_ok(codes, s, ref[pre]), f"{key}: a code is not one enclosing the oracle's value"
-        _say(f"  {key}: {int(np.sum(codes != own))} of {codes.size} codes on the other side of a boundary")
-    return ref
+        ref = model.run_qwen3_layer(cfg, inp)
+        return ref, ref
+    ties = KernelTies(_decisions(run, rows))
+    ref = model.run_qwen3_layer(cfg, inp, ties=ties)
+    _say(f"  FP8 decisions: {ties.summary()}")
+    ind = model.run_qwen3_layer(cfg, inp) if ties.any_flip else ref
+    return ref, ind
 
 
-def _check_outputs(run, ref, rows, tag):
-    """y, r2 of the given GPU rows against the oracle rows 0.. of ref."""
+def _check_outputs(run, ref, ind, rows, tag):
+    """y, r2 of the given GPU rows against the oracle rows 0.. of ref (and r2 against the
+    independent oracle)."""
     from gpu_helpers import bf16_excess, bf16_to_f64
     cfg, tol = run.cfg, _tol(run.cfg)
     y = bf16_to_f64(run.t["y_out"]).reshape(cfg.m, cfg.hidden)[rows]
     r2 = run.t["r2_out"].cpu().numpy().astype(np.float64).reshape(cfg.m, cfg.hidden)[rows]
     ey, er = np.max(np.abs(y - ref["y_pre"])), np.max(np.abs(r2 - ref["r2"]))
-    _say(f"  {tag}: y err {ey:.3e} (max |y| {np.abs(ref['y_pre']).max():.3g}) r2 err {er:.3e}")
+    eyi, eri = np.max(np.abs(y - ind["y_pre"])), np.max(np.abs(r2 - ind["r2"]))
+    _say(f"  {tag}: y err {ey:.3e} (max |y| {np.abs(ref['y_pre']).max():.3g}) r2 err {er:.3e}; "
+         f"independent oracle: y err {eyi:.3e} r2 err {eri:.3e}")
     assert bf16_excess(y, ref["y_pre"], tol) <= 0 and er <= tol, f"{tag}: y err {ey}, r2 err {er}"
+    assert eri <= tol, f"{tag}: r2 err {eri} against the independent oracle"
 
 
-def _check_cache(run, inp, ref, rows, k_before, v_before, tag):
-    """The written slots are exactly the oracle's; their rows match; nothing else changed."""
-    cfg, tol = run.cfg, _tol(run.cfg)
+def _check_slot_set(run, inp, k_before, v_before, tag):
+    """Only the slots of the new tokens changed: every other byte of both caches is unchanged."""
+    cfg = run.cfg
     kc = run.t["k_cache"].cpu().numpy().view(np.uint16)[0]
     vc = run.t["v_cache"].cpu().numpy().view(np.uint16)[0]
     mask = np.ones(kc.shape[:2], dtype=bool)
@@ -112,12 +117,25 @@ def _check_cache(run, inp, ref, rows, k_before, v_before, tag):
         p = int(ctx[r]) - 1
         mask[inp["block_table"][r][p // cfg.page_size], p % cfg.page_size] = False
     assert np.array_equal(kc[mask], k_before[mask]) and np.array_equal(vc[mask], v_before[mask]), tag
+    return kc, vc
+
+
+def _check_written_rows(run, kc, vc, inp, ref, rows, tag):
+    """The rows written at the new tokens' slots match the oracle's k and v (before rounding)."""
+    cfg, tol = run.cfg, _tol(run.cfg)
     from gpu_helpers import bf16_excess
+    ctx = inp["context_lens"]
     for i, r in enumerate(rows):
         p = int(ctx[r]) - 1
         page, off = inp["block_table"][r][p // cfg.page_size], p % cfg.page_size
         assert bf16_excess(bf16_bits_to_f64(kc[page, off]), ref["k_pre"][i], tol) <= 0, tag
         assert bf16_excess(bf16_bits_to_f64(vc[page, off]), ref["v_pre"][i], tol) <= 0, tag
+
+
+def _check_cache(run, inp, ref, rows, k_before, v_before, tag):
+    """The written slots are exactly the oracle's; their rows match; nothing else changed."""
+    kc, vc = _check_slot_set(run, inp, k_before, v_before, tag)
+    _check_written_rows(run, kc, vc, inp, ref, rows, tag)
 
 
 def _check_intermediates(run, ref, tag):
@@ -131,19 +149,19 @@ def _check_intermediates(run, ref, tag):
     r2 = _ws(run, "r2").view(np.float32).astype(np.float64)[:M * H].reshape(M, H)
     assert np.max(np.abs(r2 - ref["r2"])) <= tol, tag
     if cfg.act_fp8:
-        from gpu_helpers import e4m3_codes_ok
-        for name, K, key in (("h1", H, "h1_pre"), ("h2", H, "h2_pre")):
-            s = _ws(run, "s" + name[1]).view(np.float32)[:M].astype(np.float64)
-            assert np.allclose(s, ref["s" + name[1]], rtol=1e-5), f"{tag} {name} scales"
-            assert e4m3_codes_ok(opnd_fp8_rows(_ws(run, name), K)[:M], s, ref[key]), f"{tag} {name}"
+        from fp8_check import SCALE_RTOL
+        # codes: exactly the resolved oracle's (its own RNE codes, the GPU's choice only at ambiguous
+        # points of the first run: every later mode must reproduce them); scales within SCALE_RTOL
+        for name, K, key, skey in (("h1", H, "h1q", "s1"), ("h2", H, "h2q", "s2"), ("oq", q, "oq", "so"),
+                                   ("mq", I, "mq", "sm")):
+            s = _ws(run, skey).view(np.float32)[:M].astype(np.float64)
+            assert np.max(np.abs(s / ref[skey] - 1)) <= SCALE_RTOL, f"{tag} {skey}"
+            codes = opnd_fp8_rows(_ws(run, name), K)[:M]
+            assert np.array_equal(e4m3_decode(codes), e4m3_decode(ref[key])), f"{tag} {name}"
         o = _ws(run, "o").view(np.float32)[:M * q].astype(np.float64).reshape(M, q)
         assert np.max(np.abs(o - ref["o_pre"])) <= tol, tag
         m = _ws(run, "m").view(np.float32)[:M * I].astype(np.float64).reshape(M, I)
         assert np.max(np.abs(m - ref["m_pre"])) <= tol, tag
-        for name, K, key, skey in (("oq", q, "o_pre", "so"), ("mq", I, "m_pre", "sm")):
-            s = _ws(run, skey).view(np.float32)[:M].astype(np.float64)
-            assert np.allclose(s, ref[skey], rtol=1e-4), f"{tag} {skey}"
-            assert e4m3_codes_ok(opnd_fp8_rows(_ws(run, name), K)[:M], s, ref[key]), f"{tag} {name}"
         pad = [opnd_fp8_rows(_ws(run, n), K)[M:] for n, K in (("h1", H), ("h2", H), ("oq", q), ("mq", I))]
     else:
         from gpu_helpers import bf16_excess
@@ -179,8 +197,8 @@ def test_m16_reduced_layer_all_modes(fp8):
             run.t["r2_out"].zero_()
             run.run(mode, ms)
             if ref is None:  # every mode gives the same bits (checked below)
-                ref = _oracle(cfg, inp, run, rows)
-            _check_outputs(run, ref, rows, f"{mode}/{ms}")
+                ref, ind = _oracle(cfg, inp, run, rows)
+            _check_outputs(run, ref, ind, rows, f"{mode}/{ms}")
             _check_cache(run, inp, ref, rows, k0, v0, f"{mode}/{ms}")
             _check_intermediates(run, ref, f"W={W} {mode}/{ms}")
             outs.append((run.t["y_out"].clone(), run.t["r2_out"].clone()))
@@ -204,8 +222,10 @@ def _sample_inputs(cfg, inp, rows):
     return scfg, sub
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["qwen3_8b_layer", "qwen3_8b_layer_fp8"])
-def test_m16_full_size_sampled_rows(name):
+def test_m16_full_size_all_requests(name):
+    """Every one of the 16 requests at full size, the oracle run on chunks of four requests."""
     cfg = get_config(name)
     _say(f"case: {name} full size, inputs")
     inp = make_inputs(cfg, seed=0)
@@ -213,14 +233,17 @@ def test_m16_full_size_sampled_rows(name):
     run = _run(cfg, inp)
     _say(f"case: {name} megakernel W=all")
     run.run("mk")
-    rows = [0, 9, 15]
-    scfg, sub = _sample_inputs(cfg, inp, rows)
-    _say(f"case: {name} oracle on rows {rows}")
-    ref = _oracle(scfg, sub, run, rows)
-    _check_outputs(run, ref, rows, f"{name} mk")
-    _check_cache(run, inp, ref, rows, k0, v0, f"{name} mk")
-    y_mk = run.t["y_out"].clone()
-    _say(f"case: {name} graph multistream")
-    run.t["y_out"].zero_()
-    run.run("graph", True)
-    assert torch.equal(run.t["y_out"], y_mk)
+    kc, vc = _check_slot_set(run, inp, k0, v0, f"{name} mk")
+    for rows in ([0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11], [12, 13, 14, 15]):
+        scfg, sub = _sample_inputs(cfg, inp, rows)
+        _say(f"case: {name} oracle on requests {rows}")
+        ref, ind = _oracle(scfg, sub, run, rows)
+        _check_outputs(run, ref, ind, rows, f"{name} mk requests {rows}")
+        _check_written_rows(run, kc, vc, inp, ref, rows, f"{name} mk")
+    y_mk, r2_mk = run.t["y_out"].clone(), run.t["r2_out"].clone()
+    for ms in (False, True):
+        _say(f"case: {name} graph multistream={ms}")
+        run.t["y_out"].zero_()
+        run.t["r2_out"].zero_()
+        run.run("graph", ms)
+        assert torch.equal(run.t["y_out"], y_mk) and torch.equal(run.t["r2_out"], r2_mk)

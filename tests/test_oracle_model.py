@@ -114,24 +114,40 @@ def test_indexer_front_consistency():
     assert abs(o["score"][mi, o["pos"][mi]] - ref) < 1e-3 * max(1, abs(ref))
 
 
-def test_fp8_decisions_taken_from_the_caller():
-    """The FP8 layer continues from codes a caller supplies: its own codes reproduce it exactly, and
-    one code moved to its neighbour changes y by that step times the dequantised down-projection
-    column (the layer is linear in the down projection's input)."""
+class _Ties:
+    """Takes the other enclosing code at the listed elements of the listed points (and nowhere else)."""
+
+    def __init__(self, flips, delta=(0.0, 1e9)):
+        self.flips, self._delta = flips, delta
+
+    def delta(self, key):
+        return self._delta
+
+    def choose(self, key, v, codes, s, amb):
+        take = np.zeros(codes.shape, bool)
+        for (r, c) in self.flips.get(key, ()):
+            take[r, c] = True
+        return take
+
+
+def test_fp8_ambiguity_resolution_is_exact_and_linear():
+    """The FP8 layer with a resolution that takes no choice is the independent layer bit for bit;
+    taking the other code of one mq element changes y by that code step times the dequantised
+    down-projection column (the layer is linear in the down projection's input), and nothing else."""
     cfg = dataclasses.replace(_small_cfg(), weight_fp8=True, act_fp8=True, hidden=256, inter=512)
     inp = make_inputs(cfg, seed=9)
     own = model.run_qwen3_layer(cfg, inp)
-    dec = {k: (own[k], own["s" + n]) for k, n in (("h1q", "1"), ("oq", "o"), ("h2q", "2"), ("mq", "m"))}
-    same = model.run_qwen3_layer(cfg, inp, decide=dec)
-    for key in ("y_pre", "r2", "o_pre", "m_pre", "qkv"):
+    same = model.run_qwen3_layer(cfg, inp, ties=_Ties({}))
+    for key in ("y_pre", "r2", "o_pre", "m_pre", "qkv", "h1q", "oq", "h2q", "mq"):
         assert np.array_equal(same[key], own[key]), key
-    mq = own["mq"].copy()
-    row, col = 1, int(np.argmax(np.abs(nu.e4m3_decode(own["mq"][1]))))
-    code = int(mq[row, col])
-    mq[row, col] = code - 1 if code & 0x7F else code + 1  # the neighbouring code toward zero (or away from it)
-    dec["mq"] = (mq, own["sm"])
-    moved = model.run_qwen3_layer(cfg, inp, decide=dec)
-    step = (nu.e4m3_decode(np.array([mq[row, col]], np.uint8))[0] - nu.e4m3_decode(np.array([code], np.uint8))[0])
+    row, col = 1, int(np.argmax(np.abs(nu.e4m3_decode(own["mq"][1]) * (np.abs(nu.e4m3_decode(own["mq"][1])) < 448))))
+    moved = model.run_qwen3_layer(cfg, inp, ties=_Ties({"mq": [(row, col)]}))
+    code, new = int(own["mq"][row, col]), int(moved["mq"][row, col])
+    assert new != code and np.sum(moved["mq"] != own["mq"]) == 1
+    step = nu.e4m3_decode(np.array([new], np.uint8))[0] - nu.e4m3_decode(np.array([code], np.uint8))[0]
+    v = own["m_pre"][row, col] / own["sm"][row]
+    lo, hi = nu.e4m3_enclosing(np.array([v]))
+    assert abs(step) == hi[0] - lo[0]  # the other member of the enclosing pair
     w_col = nu.dequant_weight_blocks(inp["w_down"][0], inp["s_down"][0])[:, col]
     want = own["y_pre"].copy()
     want[row] += step * own["sm"][row] * w_col

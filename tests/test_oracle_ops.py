@@ -115,6 +115,17 @@ def test_cache_slots_bit_exact():
     cache = np.arange(64 * 16).reshape(64, 16)
     tok = ops.gather_tokens(cache, bt[2], 40, 16)
     assert [int(t) for t in tok] == [int(bt[2][t // 16]) * 16 + t % 16 for t in range(40)]
+    # the page walk: one physical slot per logical token, brute force; with a permutation table the
+    # walks of all requests over their full page lists visit every physical slot exactly once
+    walk = ops.token_slots(bt[1], 37, 16)
+    for t in range(37):
+        page = None
+        for logical, phys in enumerate(bt[1]):
+            if logical == t // 16:
+                page = int(phys)
+        assert walk[t] == page * 16 + (t - (t // 16) * 16)
+    every = np.concatenate([ops.token_slots(bt[r], 256, 16) for r in range(4)])
+    assert np.array_equal(np.sort(every), np.arange(64 * 16))
 
 
 def test_argmax_ties_smallest_index():
