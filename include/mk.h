@@ -165,6 +165,23 @@ mk_status mk_plan_workspace_region(const mk_plan* plan, const char* name, size_t
  * issued on one stream. */
 mk_status mk_run_layer(mk_plan* plan, const mk_tensors* tensors, void* hip_stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc: the same run as mk_run_layer (same kernels, same results
+ * bit for bit) with its scratch in a statically allocated device array instead of the caller's
+ * workspace.  The MK_T_WORKSPACE / MK_TI_WORKSPACE entry of `tensors` is ignored (it may be 0); every
+ * other tensor is the caller's, as for mk_run_layer.
+ * The array is MK_SCRATCH_MAX_BYTES per GPU, allocated with the library's code object on each GPU
+ * the library runs on and held until the process ends; it holds the plan's workspace
+ * (mk_plan_workspace_bytes, rounded up to 256) followed by its operand pointer table (16 x 8 bytes per
+ * op).  A plan that needs more returns MK_ERR_INVALID and launches nothing.  The call allocates
+ * nothing: its address is looked up once per device at plan set-up (mk_build_queue), the table is
+ * written into the array by a small kernel on `hip_stream`, and the workspace is cleared (an
+ * asynchronous memset on `hip_stream`) whenever another plan used the array last.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must not be issued; calls in one stream order are safe.  Asynchronous. */
+#define MK_SCRATCH_MAX_BYTES (40u << 20)
+mk_status mk_run_layer_noalloc(mk_plan* plan, const mk_tensors* tensors, void* hip_stream);
+
 /* Run the same op bodies as one standalone kernel per op (one tile per block) inside a
  * hipGraph captured on first use per tensor set; multistream = 0: one stream in topological
  * order; 1: independent branches on forked streams joined by events.  Asynchronous. */

@@ -28,6 +28,7 @@ MK_OK, MK_ERR_INVALID, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_NOMEM, MK_ERR_TIME
 MK_QWEN3_LAYER, MK_QWEN3_STEP, MK_INDEXER_FRONT = 0, 1, 2
 MK_FLAG_NO_PREFETCH, MK_FLAG_NOOP_ONLY, MK_FLAG_TRACE, MK_FLAG_DEBUG_GATHER = 1, 2, 4, 8
 MK_MAX_TENSORS = 32
+MK_SCRATCH_MAX_BYTES = 40 << 20
 QWEN3_TENSORS = ["w_qkv", "w_o", "w_gu", "w_down", "g_attn", "g_mlp", "g_q", "g_k", "k_cache", "v_cache",
                  "block_table", "context_lens", "x", "r_in", "y_out", "r2_out", "workspace",
                  "g_final", "w_lm", "logits_out", "token_out",
@@ -60,6 +61,7 @@ _lib.mk_plan_info.argtypes = [_P] + [ctypes.POINTER(ctypes.c_int32)] * 3
 _lib.mk_plan_workspace_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
 _lib.mk_plan_workspace_region.argtypes = [_P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
 _lib.mk_run_layer.argtypes = [_P, ctypes.POINTER(MkTensors), _P]
+_lib.mk_run_layer_noalloc.argtypes = [_P, ctypes.POINTER(MkTensors), _P]
 _lib.mk_run_graph_baseline.argtypes = [_P, ctypes.POINTER(MkTensors), ctypes.c_int32, _P]
 _lib.mk_sync.argtypes = [_P, _P]
 _lib.mk_read_trace.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t]
@@ -67,8 +69,8 @@ _lib.mk_read_gather.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), ctypes.c_siz
 _lib.mk_plan_destroy.argtypes = [_P]
 _lib.mk_plan_destroy.restype = None
 for _f in ("mk_build_queue", "mk_plan_queue", "mk_plan_events", "mk_plan_info", "mk_plan_workspace_bytes",
-           "mk_plan_workspace_region", "mk_run_layer", "mk_run_graph_baseline", "mk_sync", "mk_read_trace",
-           "mk_read_gather"):
+           "mk_plan_workspace_region", "mk_run_layer", "mk_run_layer_noalloc", "mk_run_graph_baseline", "mk_sync",
+           "mk_read_trace", "mk_read_gather"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -164,6 +166,11 @@ class Plan:
 
     def run(self, tensors: MkTensors, stream=None) -> None:
         _check(_lib.mk_run_layer(self._h, ctypes.byref(tensors), _P(_stream_handle(stream))), "mk_run_layer")
+
+    def run_noalloc(self, tensors: MkTensors, stream=None) -> None:
+        """mk_run_layer_noalloc: the same run with the library's static device scratch as workspace."""
+        _check(_lib.mk_run_layer_noalloc(self._h, ctypes.byref(tensors), _P(_stream_handle(stream))),
+               "mk_run_layer_noalloc")
 
     def run_graph(self, tensors: MkTensors, multistream: bool = False, stream=None) -> None:
         _check(_lib.mk_run_graph_baseline(self._h, ctypes.byref(tensors), int(bool(multistream)),

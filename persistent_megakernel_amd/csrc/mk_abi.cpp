@@ -50,6 +50,10 @@ struct mk_plan {
   uint32_t* d_trace = nullptr;
   int32_t* d_gather = nullptr;  // MK_FLAG_DEBUG_GATHER: physical slots of the gathered rows
   size_t gather_words = 0;
+  mk::TableReloc* d_reloc = nullptr;  // the operand pointer table as (tensor, offset) pairs (no-allocation runs)
+  int n_reloc = 0;
+  uint64_t uid = 0;                   // identifies the plan to the per-device scratch
+  mk::TensorPtrs noalloc_last{};      // tensor set whose table the scratch holds for this plan
   size_t events_bytes = 0, arrivals_bytes = 0;
   uint32_t epoch = 0;  // megakernel runs so far; never reset (record tags must not repeat)
   uint32_t cruns = 0;  // megakernel runs since the event counters were last zeroed
@@ -63,6 +67,10 @@ struct mk_plan {
 };
 
 namespace {
+
+// per device: the plan whose workspace and table the no-allocation scratch holds (0: none)
+std::atomic<uint64_t> g_scratch_owner[64];
+std::atomic<uint64_t> g_plan_uid{0};
 
 bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 
@@ -442,6 +450,25 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
     HIP_TRY(hipMalloc(&p->d_trace, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
     HIP_TRY(hipMemset(p->d_trace, 0, (size_t)hp.W * hp.L * mk::kTraceWords * 4));
   }
+  {  // no-allocation runs: the scratch address of this device, and the table as a relocation list (the
+     // table of a tensor set whose entry i is (i + 1) << 48: every slot is 0, a library address below 2^48,
+     // or tensor i plus an offset)
+    HIP_TRY(mk::scratch_init(p->device));
+    mk_tensors tag{};
+    tag.n = MK_MAX_TENSORS;
+    for (int i = 0; i < MK_MAX_TENSORS; ++i) tag.ptr[i] = (uint64_t)(i + 1) << 48;
+    std::vector<uint64_t> tab;
+    fill_table(p.get(), &tag, tab);
+    std::vector<mk::TableReloc> rel(tab.size());
+    for (size_t k = 0; k < tab.size(); ++k) {
+      const uint64_t v = tab[k], hi = v >> 48;
+      rel[k] = hi == 0 ? mk::TableReloc{v, mk::kRelocAbs, 0} : mk::TableReloc{v & ((1ull << 48) - 1), (uint32_t)(hi - 1), 0};
+    }
+    p->n_reloc = (int)rel.size();
+    HIP_TRY(hipMalloc(&p->d_reloc, std::max<size_t>(1, rel.size()) * sizeof(mk::TableReloc)));
+    if (!rel.empty()) HIP_TRY(hipMemcpy(p->d_reloc, rel.data(), rel.size() * sizeof(mk::TableReloc), hipMemcpyHostToDevice));
+    p->uid = ++g_plan_uid;
+  }
   if (c.flags & MK_FLAG_DEBUG_GATHER) {  // one slot per (layer, request, kv head, K|V, token) or (request, key)
     const size_t tokens = (size_t)c.max_pages_per_req * c.page_size;
     p->gather_words = c.workload == MK_INDEXER_FRONT ? (size_t)c.n_requests * tokens
@@ -509,6 +536,48 @@ mk_status mk_run_layer(mk_plan* p, const mk_tensors* t, void* stream) {
   a.L = p->hp.L;
   a.first_task = 0;
   HIP_TRY(mk::launch_worker(a, p->hp.W, (hipStream_t)stream, p->hp.tp.spec, use_loaders(p)));
+  p->epoch++;
+  p->cruns++;
+  return MK_OK;
+}
+
+mk_status mk_run_layer_noalloc(mk_plan* p, const mk_tensors* t, void* stream) {
+  if (!p || !t) return fail(MK_ERR_INVALID, "null argument");
+  const size_t tab_off = (p->hp.workspace_bytes + 255) & ~(size_t)255;
+  const size_t tab_bytes = p->hp.ops.size() * mk::kTableSlots * sizeof(uint64_t);
+  if (tab_off + tab_bytes > mk::kScratchBytes)
+    return fail(MK_ERR_INVALID, "workspace of " + std::to_string(p->hp.workspace_bytes) + " bytes and a pointer table of " +
+                                    std::to_string(tab_bytes) + " bytes exceed the no-allocation scratch of " +
+                                    std::to_string(mk::kScratchBytes) + " bytes");
+  if (p->host_only) return fail(MK_ERR_INVALID, "plan was built without a device");
+  char* base = (char*)mk::scratch_base(p->device);
+  if (!base) return fail(MK_ERR_INVALID, "no-allocation scratch not set up on this device");
+  mk::TensorPtrs tp{};
+  const int n = std::min<int>(t->n, MK_MAX_TENSORS);
+  for (int i = 0; i < n; ++i) tp.ptr[i] = t->ptr[i];
+  const int wsi = ws_index(p->hp.cfg);
+  tp.ptr[wsi] = (uint64_t)(uintptr_t)base;  // the workspace is the scratch, whatever the caller passed
+  mk_tensors chk = *t;
+  chk.ptr[wsi] = tp.ptr[wsi];
+  mk_status st = check_tensors(p, &chk);
+  if (st != MK_OK) return st;
+  if ((st = check_runnable(p)) != MK_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* table = (uint64_t*)(base + tab_off);
+  const bool owner = g_scratch_owner[p->device].load() == p->uid;
+  if (!owner)  // another plan's (or no) contents: start from a zeroed workspace, as a new workspace does
+    HIP_TRY(hipMemsetAsync(base, 0, p->hp.workspace_bytes, s));
+  if (!owner || std::memcmp(&tp, &p->noalloc_last, sizeof(tp)) != 0) {
+    HIP_TRY(mk::launch_fill_table(p->d_reloc, p->n_reloc, tp, table, s));
+    p->noalloc_last = tp;
+    g_scratch_owner[p->device].store(p->uid);
+  }
+  if (p->d_gather) HIP_TRY(hipMemsetAsync(p->d_gather, 0xFF, p->gather_words * 4, s));
+  mk::KArgs a = base_args(p, table);
+  a.instrs = p->d_queue;
+  a.L = p->hp.L;
+  a.first_task = 0;
+  HIP_TRY(mk::launch_worker(a, p->hp.W, s, p->hp.tp.spec, use_loaders(p)));
   p->epoch++;
   p->cruns++;
   return MK_OK;
@@ -647,6 +716,11 @@ void mk_plan_destroy(mk_plan* p) {
   (void)hipFree(p->d_pos);
   if (p->d_trace) (void)hipFree(p->d_trace);
   if (p->d_gather) (void)hipFree(p->d_gather);
+  (void)hipFree(p->d_reloc);
+  if (p->device >= 0 && p->device < 64) {  // the scratch no longer holds a live plan's table
+    uint64_t mine = p->uid;
+    g_scratch_owner[p->device].compare_exchange_strong(mine, 0);
+  }
   delete p;
 }
 

@@ -107,6 +107,24 @@ static_assert(kLdsBytes == 163840, "LDS budget");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 }  // namespace dev
 
+// No-allocation runs: one statically allocated device array per GPU holds the workspace and the
+// operand pointer table of the run (mk_run_layer_noalloc).  The table is written on the device from a
+// relocation list the plan builds once: entry = (tensor index, byte offset), or an absolute library
+// address when the index is kRelocAbs.
+constexpr size_t kScratchBytes = (size_t)40 << 20;
+constexpr uint32_t kRelocAbs = 0xFFFFFFFFu;
+struct TableReloc {
+  uint64_t off;  // byte offset from tensor `idx`, or the absolute address (or 0) when idx == kRelocAbs
+  uint32_t idx;
+  uint32_t pad;
+};
+struct TensorPtrs {
+  uint64_t ptr[MK_MAX_TENSORS];
+};
+hipError_t scratch_init(int device);  // once per device, with that device current: the array's address
+void* scratch_base(int device);       // null until scratch_init succeeded on that device
+hipError_t launch_fill_table(const TableReloc* reloc, int n, const TensorPtrs& t, uint64_t* out, hipStream_t stream);
+
 // spec: the plan's op family (0 single-token bodies, 1 multi-row bodies), one kernel instance each
 // loaders: the multi-row kernel with its loader waves (kThreadsM threads) rather than the eight
 // waves prefetching for themselves (kThreads)

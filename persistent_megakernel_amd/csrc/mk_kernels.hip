@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mk_device.hpp"
 
 namespace mk {
@@ -2484,6 +2486,53 @@ hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec,
     hipLaunchKernelGGL((mk_worker<1, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
   else
     hipLaunchKernelGGL((mk_worker<0, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// the no-allocation scratch: a file-scope device array, one copy per GPU, kept until the process ends.
+// Host code never passes `scratch` itself (its host-side name is only a stand-in for the symbol): it
+// looks the device address up once per device and hands that address to the kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[device]) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != device) return hipErrorInvalidDevice;  // the caller makes the device current
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch[device] = ptr;
+  return hipSuccess;
+}
+
+void* scratch_base(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch[device];
+}
+
+// the operand pointer table from the plan's relocation list and the run's tensor addresses
+__global__ void __launch_bounds__(256) mk_fill_table(const TableReloc* reloc, int n, TensorPtrs t, uint64_t* out) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const TableReloc r = reloc[i];
+    out[i] = r.idx == kRelocAbs ? r.off : t.ptr[r.idx] + r.off;
+  }
+}
+
+hipError_t launch_fill_table(const TableReloc* reloc, int n, const TensorPtrs& t, uint64_t* out, hipStream_t stream) {
+  const int grid = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+  hipLaunchKernelGGL(mk_fill_table, dim3(grid > 0 ? grid : 1), dim3(256), 0, stream, reloc, n, t, out);
   return hipGetLastError();
 }
 

@@ -41,3 +41,21 @@ def test_invalid_shapes_rejected():
     except mk.MkError as e:
         ok = e.status == mk.MK_ERR_INVALID
     assert ok
+
+
+def test_noalloc_run_rejects_a_workspace_beyond_the_scratch():
+    """mk_run_layer_noalloc refuses, before anything else, a plan whose workspace and pointer table
+    exceed the static scratch (here a 16-request layer at context 16384: 57.6 MiB > 40 MiB)."""
+    import dataclasses
+    import persistent_megakernel_amd as mk
+    from workloads import get_config
+    cfg = dataclasses.replace(get_config("qwen3_8b_layer"), context=16384)
+    plan = mk.Plan(cfg, num_workers=256)
+    assert plan.workspace_bytes() > mk.MK_SCRATCH_MAX_BYTES
+    try:
+        plan.run_noalloc(mk.Plan.tensors([256] * 17), stream=0)
+        status = None
+    except mk.MkError as e:
+        status, msg = e.status, str(e)
+    assert status == mk.MK_ERR_INVALID and "exceed the no-allocation scratch" in msg
+    plan.close()
