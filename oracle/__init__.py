@@ -13,6 +13,8 @@ Modules
             indexer score)
   model     the workloads: one Qwen3-shaped layer, the full decode step, the indexer front
   queue     the host tile-instruction queue builder (tiles -> events -> round-robin queues)
+  taskgraph the generic op-graph lowering (tile regions -> pairing rules -> events -> queues),
+            pinned by the MegaRTP page's worked attention-pre plan
   bytes     the decode byte / gap estimate model of the handbook
 
 Pages cited: "Kernel-Mega-PDL" (MegaRTP; qingkeai.online), the handbook chapter on

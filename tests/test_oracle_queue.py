@@ -86,9 +86,7 @@ def test_page_packing_example():
     assert q.shape == (148, 5, 32)
     live = (q[:, :, 0] != 0).sum(axis=1)
     assert (live == 5).sum() == 140 and (live == 4).sum() == 8
-    # the page's 70 events: 16, 16, 16, 48, 64 x 2 (D0 -> D2 pairs), 32, 1
-    thr = [16, 16, 16, 48] + [2] * 64 + [32, 1]
-    assert len(thr) == 70 and sum(1 for t in thr if t == 2) == 128 // 2
+    # the page's events are derived from its graph by the lowering in tests/test_oracle_taskgraph.py
 
 
 def _tasks(plan):
