@@ -50,8 +50,10 @@ enum {
   MK_FLAG_NOOP_ONLY = 1u << 1,   /* megakernel: run the queue with every op body skipped: the waits,
                                     stagings and output stores remain, weights are not read */
   MK_FLAG_TRACE = 1u << 2,       /* megakernel: record per-instruction timestamps */
-  MK_FLAG_DEBUG_GATHER = 1u << 3 /* both modes: record the physical cache slot of every K / V row and indexer
+  MK_FLAG_DEBUG_GATHER = 1u << 3, /* both modes: record the physical cache slot of every K / V row and indexer
                                     key the run gathers through the block table (mk_read_gather) */
+  MK_FLAG_DEBUG_SHORT_WATCHDOG = 1u << 4 /* megakernel: a wait that is not met at its first check expires
+                                    (10 ns instead of 2 s), to exercise the watchdog and abort path */
 };
 
 /* Plain data, caller-owned, copied by mk_build_queue. */
@@ -188,7 +190,10 @@ mk_status mk_run_layer_noalloc(mk_plan* plan, const mk_tensors* tensors, void* h
 mk_status mk_run_graph_baseline(mk_plan* plan, const mk_tensors* tensors, int32_t multistream, void* hip_stream);
 
 /* Wait for the plan's last run on its stream and report the device error record:
- * MK_ERR_TIMEOUT if a worker's watchdog expired (counters are then reset). */
+ * MK_ERR_TIMEOUT if a worker's watchdog expired; MK_ERR_INVALID if a block-table entry was outside
+ * [0, num_phys_pages) (it was read as page 0, so no access left the cache pool, and the run's outputs
+ * are not valid).  On either error the other workers abandon their waits, and the plan's counters
+ * are reset so that the next run starts clean. */
 mk_status mk_sync(mk_plan* plan, void* hip_stream);
 
 /* Copy the trace of the last MK_FLAG_TRACE megakernel run into host memory: uint32 [W, L, 16]

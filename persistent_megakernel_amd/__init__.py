@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MK_OK, MK_ERR_INVALID, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_NOMEM, MK_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
 MK_QWEN3_LAYER, MK_QWEN3_STEP, MK_INDEXER_FRONT = 0, 1, 2
-MK_FLAG_NO_PREFETCH, MK_FLAG_NOOP_ONLY, MK_FLAG_TRACE, MK_FLAG_DEBUG_GATHER = 1, 2, 4, 8
+MK_FLAG_NO_PREFETCH, MK_FLAG_NOOP_ONLY, MK_FLAG_TRACE, MK_FLAG_DEBUG_GATHER, MK_FLAG_DEBUG_SHORT_WATCHDOG = 1, 2, 4, 8, 16
 MK_MAX_TENSORS = 32
 MK_SCRATCH_MAX_BYTES = 40 << 20
 QWEN3_TENSORS = ["w_qkv", "w_o", "w_gu", "w_down", "g_attn", "g_mlp", "g_q", "g_k", "k_cache", "v_cache",

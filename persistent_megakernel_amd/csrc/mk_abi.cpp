@@ -416,6 +416,7 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
                      c.n_requests * c.tokens_per_request, hp.tp.kc, c.act_fp8 ? 1 : 0, c.num_layers,
                      c.idx_q_rank, c.idx_heads, c.tokens_per_request, 0};
   for (int r = 0; r < c.n_requests; ++r) p->sh.smax = std::max(p->sh.smax, (int)host_context_lens[r]);
+  p->sh.npages = c.num_phys_pages;
   HIP_TRY(hipMalloc(&p->d_queue, hp.queue.size() * 4));
   HIP_TRY(hipMemcpy(p->d_queue, hp.queue.data(), hp.queue.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipMalloc(&p->d_tasks, hp.tasks.size() * 4));
@@ -676,6 +677,10 @@ mk_status mk_sync(mk_plan* p, void* stream) {
     HIP_TRY(hipMemset(p->d_arrivals, 0, p->arrivals_bytes));
     HIP_TRY(hipMemset(p->d_err, 0, 64));
     HIP_TRY(hipDeviceSynchronize());
+    if (e[0] == mk::kErrBlockTable)
+      return fail(MK_ERR_INVALID, "block table entry " + std::to_string((int32_t)e[4]) + " of request " + std::to_string(e[3]) +
+                                      " is outside the pool of " + std::to_string(p->hp.cfg.num_phys_pages) +
+                                      " pages (read as page 0; the run's outputs are not valid)");
     return fail(MK_ERR_TIMEOUT, "watchdog: worker " + std::to_string(e[1]) + " task " + std::to_string(e[2]) +
                                     " waited for tag " + std::to_string(e[3]) + " over " + std::to_string(e[4]) +
                                     " polls");

@@ -14,6 +14,7 @@ struct Shapes {
   float eps, inv_sqrt_d;
   int M, kc, fp8, layers;  // multi-row plans: rows, K chunk of a projection tile, W8A8, layers
   int qr, nh, T, smax;     // indexer front: q rank, heads, tokens per request, score row stride
+  int npages;              // physical pages of the cache pool: every block-table entry must be below it
 };
 
 struct KArgs {
@@ -37,6 +38,7 @@ constexpr int kTraceWords = 16;  // per instruction: visible, ready, prologue, A
 constexpr int kNSub = 16;                  // sub-counters per event (spreads the atomics)
 constexpr int kSubStride = 32;             // words between sub-counters (128 bytes)
 constexpr int kEvStride = kNSub * kSubStride;
+constexpr uint32_t kErrWatchdog = 1u, kErrBlockTable = 2u;  // error record word 0
 constexpr unsigned long long kWatchdogTicks = 200000000ull;  // 2 s of the 100 MHz clock
 
 namespace dev {

@@ -415,6 +415,21 @@ DEV void pf_set(Pf<S>& pf, const void* src, uint32_t bytes) {
   pf.total = pf.blk[K + 1];
 }
 
+// A block-table entry of request r, checked against the page pool: an entry outside [0, pages) is
+// written to the error record (mk_sync reports it) and read as page 0, so that no cache access leaves
+// the pool whatever the table holds.  `entry` is the table row of request r plus the logical page.
+DEV uint32_t bt_check(const KArgs& a, uint32_t v, uint32_t r) {
+  if (v < (uint32_t)a.sh.npages) return v;
+  uint32_t z = 0;
+  if (__hip_atomic_compare_exchange_strong(a.err, &z, kErrBlockTable, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(a.err + 3, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.err + 4, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return 0u;
+}
+DEV uint32_t bt_page(const KArgs& a, const int32_t* entry, uint32_t r) { return bt_check(a, (uint32_t)s_ld32(entry), r); }
+
 // K of a projection kind
 DEV uint32_t proj_k(const Shapes& sh, uint32_t kind) {
   switch (kind) {
@@ -566,7 +581,7 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
           const uint32_t tok = (uint32_t)pf.t0 + 8u * b;
           if (tok / P != pidx) {
             pidx = tok / P;
-            page = (uint32_t)s_ld32(pf.bt + pidx);
+            page = bt_page(a, pf.bt + pidx, kNone);
           }
           const uint32_t slot = page * P + tok % P;
           const uint32_t off = 8u * b + (ln >> 3) < (uint32_t)pf.nk ? ln * 16u : 0u;  // past the split: reload the block start
@@ -591,7 +606,7 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
       uint32_t bb = b0 - pf.blk[k];
       const uint32_t tok = (uint32_t)pf.t0 + 4u * bb;
       uint32_t pidx = tok / P, pos = tok - pidx * P;
-      uint32_t pg = (uint32_t)s_ld32(pf.bt + pidx);  // physical page of block-table entry pidx
+      uint32_t pg = bt_page(a, pf.bt + pidx, kNone);  // physical page of block-table entry pidx
       auto page_base = [&](uint32_t page) {  // the span's head in physical page `page`
         return base + ((size_t)page * P * (uint32_t)a.sh.Hkv + (uint32_t)pf.hk) * 256u;
       };
@@ -608,7 +623,7 @@ DEV void pf_issue(const KArgs& a, const Pf<S>& pf, uint32_t lease, int cw, uint3
         pos += 4u;
         if (pos == P && b + 1u < b1) {  // the next block starts the next page
           pos = 0;
-          pg = (uint32_t)s_ld32(pf.bt + ++pidx);
+          pg = bt_page(a, pf.bt + ++pidx, kNone);
           pb = page_base(pg);
         }
       }
@@ -659,6 +674,11 @@ struct LlRegion {
   const char* src;
   uint32_t bytes, dst, tag;
 };
+
+// how long a wait may take: 2 s of the 100 MHz clock, or one tick under MK_FLAG_DEBUG_SHORT_WATCHDOG
+DEV unsigned long long watchdog_ticks(const KArgs& a) {
+  return (a.flags & MK_FLAG_DEBUG_SHORT_WATCHDOG) ? 1ull : kWatchdogTicks;
+}
 
 DEV void record_timeout(const KArgs& a, const Instr& in, uint32_t what, uint32_t value) {
   if (lane() != 0) return;
@@ -718,7 +738,7 @@ DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, 
     if (done) return true;
     ++polls;
     if ((it & 15u) == 0 && __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
-    if (rtc() - t0 > kWatchdogTicks) {
+    if (rtc() - t0 > watchdog_ticks(a)) {
       record_timeout(a, in, rg[0].tag, polls);
       return false;
     }
@@ -1253,7 +1273,7 @@ DEV bool wait_events(const KArgs& a, const Instr& in, uint32_t& polls, WaitCache
       if ((int32_t)(sum - target) >= 0) break;
       ++polls;
       if ((it & 31u) == 0 && __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
-      if (rtc() - t0 > kWatchdogTicks) {
+      if (rtc() - t0 > watchdog_ticks(a)) {
         record_timeout(a, in, e, sum);
         return false;
       }
@@ -1713,7 +1733,7 @@ DEV void kcache(const KArgs& a, const Instr& in, int wv) {
     const float amax = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
     const float sc = amax > 0.f ? amax / 448.f : 1.f;
     const uint32_t p = (uint32_t)c_ld<int32_t>(pos + m), r = m / (uint32_t)sh.T;
-    const uint32_t page = (uint32_t)c_ld<int32_t>(bt + (size_t)r * sh.maxp + p / P);
+    const uint32_t page = bt_check(a, (uint32_t)c_ld<int32_t>(bt + (size_t)r * sh.maxp + p / P), r);
     const uint32_t slot = page * P + p % P;
     __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(e4m3x4(y0 / sc, 0.f, 0.f, 0.f) & 0xffu), rc, slot * 128u + i, 0, SC1);
     __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(e4m3x4(y1 / sc, 0.f, 0.f, 0.f) & 0xffu), rc, slot * 128u + i + 64u, 0, SC1);
@@ -1740,7 +1760,7 @@ DEV void score_stage(const KArgs& a, const Instr& in, char* act) {
   // the new tokens may straddle a page boundary)
   const uint32_t ln = lane();
   const uint32_t tk = ctx - T + min(ln >> 3, T - 1u), ts = ctx - T + min(ln, T - 1u);
-  const uint32_t sk_slot = (uint32_t)bt[tk / P] * P + tk % P, ss_slot = (uint32_t)bt[ts / P] * P + ts % P;
+  const uint32_t sk_slot = bt_check(a, (uint32_t)bt[tk / P], r) * P + tk % P, ss_slot = bt_check(a, (uint32_t)bt[ts / P], r) * P + ts % P;
   const float sj = __uint_as_float(ld32(rsrc(scale), ss_slot * 4u));
   if (ln < 8u * T) lds_dma16_sc1(cache + (size_t)sk_slot * 128u + (ln & 7u) * 16u, (uint32_t)(uintptr_t)(lds_void*)(act + kScoreNewK));
   wait_vm0();
@@ -1921,7 +1941,7 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
   if (s == ns - 1) {  // the split holding the new token writes its K / V row into the paged caches
     const int p = (int)in.w[W_P5] - 1;
     const int32_t* bt = (const int32_t*)s_ld64(row + ATT_BT) + (size_t)r * sh.maxp;
-    const int page = (int)s_ld32(bt + p / sh.P);
+    const int page = (int)bt_page(a, bt + p / sh.P, (uint32_t)r);
     const size_t rowi = ((size_t)page * sh.P + (p % sh.P)) * sh.Hkv + hk;
     const uint32_t* kl = (const uint32_t*)(smem + kActOff + kActK);
     const uint32_t* vl = (const uint32_t*)(smem + kActOff + kActV);
