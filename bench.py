@@ -68,6 +68,7 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=0, help="copies of weights/caches cycled per run (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-diagnostics", action="store_true", help="skip the traced pass and the stream-peak copy")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes instead (calibrates the "
                          "HBM byte counters of a profiler run)")
@@ -134,27 +135,40 @@ def main() -> int:
         tensor_sets.append(mk.qwen3_pointers(s, step))
     torch.cuda.synchronize()
 
-    def timed(fn, p, steps, warmup):
+    def timed(fn, p, steps, warmup, per_step=None, sets=None):
+        sets = sets or tensor_sets
         for i in range(warmup):
-            fn(p, tensor_sets[i % rotate])
+            fn(p, sets[i % len(sets)])
         p.sync(stream)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        # one event before every step and one after the last, all on the launch stream: the bracket
+        # gives the mean, consecutive events each step's own duration
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
         for i in range(steps):
-            fn(p, tensor_sets[i % rotate])
-        e1.record(stream)
+            fn(p, sets[i % len(sets)])
+            ev[i + 1].record(stream)
         p.sync(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps  # ms per run
+        if per_step is not None:
+            per_step.extend(ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps))
+        return ev[0].elapsed_time(ev[steps]) / steps  # ms per run
 
     run_mk = lambda p, t: p.run(t, stream)
     run_g1 = lambda p, t: p.run_graph(t, False, stream)
     run_gm = lambda p, t: p.run_graph(t, True, stream)
 
     _log("bench: megakernel")
+    env_before = _gpu_state()
+    per_step = []
     with torch.cuda.stream(stream):
-        ms = timed(run_mk, p0, args.steps, args.warmup)
+        ms = timed(run_mk, p0, args.steps, args.warmup, per_step)
+    env_after = _gpu_state()
+    hot_ms = None
+    if rotate > 1:  # the same work on one resident copy: the cache-resident (MALL / L2) figure
+        _log("bench: megakernel, one resident copy")
+        with torch.cuda.stream(stream):
+            hot_ms = timed(run_mk, p0, max(10, args.steps // 2), 3, sets=tensor_sets[:1])
     variants = {}
     if not args.no_variants:
         for name, fn, flags in (("graph_single_stream", run_g1, 0), ("graph_multi_stream", run_gm, 0),
@@ -196,6 +210,10 @@ def main() -> int:
                      "kernel": "mk_worker<%s> (persistent megakernel, one launch per step)" % (
                          "0, false" if cfg.m == 1 else "1, false" if indexer else "1, true")},
         "variants_us_per_step": variants,
+        "step_us_stats": _stats(per_step),
+        "hot_step_us": round(hot_ms * 1000.0, 3) if hot_ms is not None else
+                       ("same as step_us: one copy, larger than the 256 MiB last-level cache" if step else None),
+        "gpu_state": {"before": env_before, "after": env_after},
     }
     if variants:
         out["gain_split_us"] = {
@@ -203,6 +221,12 @@ def main() -> int:
             "in_kernel_scheduling": round(variants["graph_multi_stream"] - step_us, 3),
             "prefetch": round(variants["megakernel_no_prefetch"] - step_us, 3),
         }
+    if not args.no_diagnostics:
+        out["diagnostics"] = _diagnostics(cfg, mk, plans, tensor_sets[0], stream, torch, step, step_us)
+        if step and "tail_us" in out["diagnostics"]:
+            tail = out["diagnostics"]["tail_us"] * step_us / out["diagnostics"]["traced_step_us"]
+            out["us_per_layer_excluding_tail"] = round((step_us - tail) / layers, 3)
+        out["stream_peak"] = _stream_peak(torch)
     if not args.no_cpu_baseline:
         _log("bench: CPU oracle baseline")
         from oracle import model as omodel
@@ -211,22 +235,123 @@ def main() -> int:
             threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         except Exception:
             threads = os.cpu_count() or 1
-        t0 = time.perf_counter()
-        if step:
-            omodel.run_qwen3_step(cfg, inp)
-        elif indexer:
-            omodel.run_indexer_front(cfg, inp)
-        else:
-            omodel.run_qwen3_layer(cfg, inp)
-        dt = time.perf_counter() - t0
+        def one_pass():
+            t0 = time.perf_counter()
+            if step:
+                omodel.run_qwen3_step(cfg, inp)
+            elif indexer:
+                omodel.run_indexer_front(cfg, inp)
+            else:
+                omodel.run_qwen3_layer(cfg, inp)
+            return time.perf_counter() - t0
+
+        runs = sorted(one_pass() for _ in range(3))
+        dt = runs[1]
+        one_thread = None
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one_thread = one_pass()
+        except Exception:
+            pass
         out["cpu_baseline"] = {"value": round(dt * 1e6 / layers, 1), "unit": "us/layer-step", "cores": threads,
                                "kind": "oracle",
-                               "sample": f"one full pass of {cfg.name} ({layers} layer(s){' + lm_head' if step else ''}) "
-                                         f"in float64 NumPy, {dt:.1f} s wall, host cpu_count {os.cpu_count()}"}
+                               "one_thread_value": round(one_thread * 1e6 / layers, 1) if one_thread else None,
+                               "sample": f"full passes of {cfg.name} ({layers} layer(s){' + lm_head' if step else ''}) "
+                                         f"in float64 NumPy: median of 3 ({', '.join(f'{r:.2f}' for r in runs)} s) with "
+                                         f"{threads} BLAS threads, then one pass on 1 thread "
+                                         f"({one_thread or float('nan'):.2f} s); host cpu_count {os.cpu_count()}"}
     print(json.dumps(out), flush=True)
     for p in plans.values():
         p.close()
     return 0
+
+
+def _stats(us):
+    if not us:
+        return None
+    v = sorted(us)
+    pick = lambda q: v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
+    return {"median": round(pick(0.5), 3), "p10": round(pick(0.1), 3), "p90": round(pick(0.9), 3),
+            "min": round(v[0], 3), "max": round(v[-1], 3), "steps": len(v)}
+
+
+def _gpu_state():
+    """Shader / memory clocks, power and performance level as rocm-smi reports them (None if unavailable,
+    and not asked for under a profiler, whose preloaded library would follow rocm-smi's re-exec)."""
+    import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showperflevel", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next(iter(d.values())) if d else {}
+    keep = {}
+    for k, v in card.items():
+        kl = k.lower()
+        if any(t in kl for t in ("sclk", "mclk", "fclk", "power", "perf")):
+            keep[k] = v
+    return keep or None
+
+
+def _diagnostics(cfg, mk, plans, tensors, stream, torch, step, step_us):
+    """A traced pass after the timed region (perturbs timing, so reported apart): the share of
+    instruction time the controllers spent polling for inputs and, for the decode step, the tail
+    (final norm, lm_head, argmax) from the end of the last layer to the end of the step."""
+    import numpy as np
+    p = mk.Plan(cfg, flags=mk.MK_FLAG_TRACE)
+    plans[-1] = p
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            p.run(tensors, stream)
+        p.sync(stream)
+    torch.cuda.synchronize()
+    tr = p.read_trace().astype(np.int64)
+    q = p.queue()
+    live = q[:, :, 0] != 0
+    dur = (tr[:, :, 7] - tr[:, :, 0])[live]
+    wait = (tr[:, :, 1] - tr[:, :, 0])[live]
+    out = {"input_wait_share": round(float(wait.sum() / max(1, dur.sum())), 4),
+           "repolls_per_instruction": round(float(tr[:, :, 8][live].mean()), 3),
+           "traced_step_us": round(float((tr[:, :, 7][live].max() - tr[:, :, 0][live].min()) / 100.0), 2),
+           "note": "from an MK_FLAG_TRACE pass: the time from a controller reaching an instruction to its inputs "
+                   "being staged and current (waiting on producers, polling, staging), over the summed time of "
+                   "every instruction; and the staging rounds repeated because a tag was stale"}
+    if step:
+        lm = live & (q[:, :, 0] == 6)
+        layers_end = tr[:, :, 7][live & ~lm].max()
+        out["tail_us"] = round(float((tr[:, :, 7][lm].max() - layers_end) / 100.0), 2)
+    return out
+
+
+def _stream_peak(torch):
+    """Measured HBM rates of plain torch kernels over 2 GiB: a device-to-device copy (read + write
+    bytes) and a sum (read bytes), best of 5."""
+    n = 1 << 29  # 2 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+
+    def best(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e-3)
+        return round(nbytes / min(t) / 1e9, 1)
+
+    res = {"copy_GBps_read_plus_write": best(lambda: b.copy_(a), 2 * 4 * n),
+           "sum_GBps_read": best(lambda: a.sum(), 4 * n), "bytes": 4 * n}
+    del a, b
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(args, torch) -> int:

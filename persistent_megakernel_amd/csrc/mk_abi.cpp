@@ -599,17 +599,22 @@ mk_status mk_run_graph_baseline(mk_plan* p, const mk_tensors* t, int32_t multist
     const auto& ops = p->hp.ops;
     // stream per op: an op continues the stream of its first dependency unless another
     // consumer already continued it (independent branches then fork onto new streams)
+    // at most kMaxBranchStreams streams: a branch beyond them shares one round-robin (every edge between
+    // streams is an event, so any assignment keeps the order the graph needs; more streams than the
+    // graph's real branch width only add cross-queue waits)
+    constexpr int kMaxBranchStreams = 2;
     std::vector<int> op_stream(ops.size(), 0);
     std::vector<bool> continued(ops.size(), false);
-    int n_streams = 1;
+    int n_streams = 1, forks = 0;
     if (multistream) {
       for (size_t k = 0; k < ops.size(); ++k) {
         const auto& deps = ops[k].deps;
         if (!deps.empty() && !continued[deps[0]]) {
           op_stream[k] = op_stream[deps[0]];
           continued[deps[0]] = true;
-        } else if (!deps.empty() || k > 0) {
-          op_stream[k] = deps.empty() ? 0 : n_streams++;
+        } else if (!deps.empty()) {
+          op_stream[k] = 1 + (forks++ % (kMaxBranchStreams - 1));
+          n_streams = std::max(n_streams, op_stream[k] + 1);
         }
       }
     }
@@ -647,7 +652,9 @@ mk_status mk_run_graph_baseline(mk_plan* p, const mk_tensors* t, int32_t multist
       a.first_task = ops[k].first_task;
       a.L = ops[k].n_tasks;
       const int grid = std::min(ops[k].n_tasks, p->hp.W);
-      HIP_TRY(mk::launch_worker(a, grid, s, p->hp.tp.spec, use_loaders(p)));
+      // a node's blocks run one task each (more tasks than workers: a few each), so the loader waves,
+      // which stream leases ahead across a worker's queue, have nothing to run ahead of
+      HIP_TRY(mk::launch_worker(a, grid, s, p->hp.tp.spec, false));
       HIP_TRY(hipEventRecord(p->events[k], s));
     }
     for (int i = 1; i < n_streams; ++i) {  // join every forked stream back
