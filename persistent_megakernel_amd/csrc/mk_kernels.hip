@@ -124,6 +124,16 @@ DEV float rows_max(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+DEV uint32_t wave_or_u32(uint32_t v) {
+  int x = (int)v;
+  x |= dppi<0xB1>(x);
+  x |= dppi<0x4E>(x);
+  x |= dppi<0x141>(x);
+  x |= dppi<0x140>(x);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
 DEV uint32_t wave_sum_u32(uint32_t v) {
   int x = (int)v;
   x += dppi<0xB1>(x);
@@ -691,6 +701,33 @@ DEV void record_timeout(const KArgs& a, const Instr& in, uint32_t what, uint32_t
   }
 }
 
+// The 1 KiB blocks of a staged run of records (bit b: block b) holding a record whose tag is not
+// `tag`: every lane checks its two records of every block (four blocks' reads in flight at a
+// time), then one wave-wide OR of the per-lane masks.  Kept out of line: its registers stay out of
+// the allocation of the kernel's hot loops.
+__device__ __attribute__((noinline)) uint32_t stale_blocks(const char* base, uint32_t bytes, uint32_t tag) {
+  const uint32_t ln = lane(), nb = blocks_of(bytes);
+  uint32_t stale = 0u;
+  for (uint32_t b0 = 0; b0 < nb; b0 += 4u) {
+    u32x4 v[4];
+    uint32_t off[4], b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      b[q] = min(b0 + (uint32_t)q, nb - 1u);  // past the last block: check it again
+      off[q] = b[q] * 1024u + ln * 16u;
+      if (off[q] >= bytes) off[q] = b[q] * 1024u;  // lanes past the end look at the block's first records
+      v[q] = *(const u32x4*)(base + off[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // nonzero when a tag differs; the second record counts only when it lies inside the run
+      const uint32_t inside = (uint32_t)((int32_t)(off[q] + 8u - bytes) >> 31);
+      stale |= min((v[q].y ^ tag) | ((v[q].w ^ tag) & inside), 1u) << b[q];
+    }
+  }
+  return wave_or_u32(stale);
+}
+
 // The wait of an instruction: stage every block of its regions in one round trip; with `verify`
 // (the megakernel), stage again the blocks holding a record whose tag is not current, until all
 // are.  False when the watchdog expired or another worker aborted.
@@ -723,17 +760,9 @@ DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, 
     bool done = true;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      for (uint32_t m = j < nrg ? pend[j] : 0u; m; m &= m - 1u) {
-        const uint32_t b = (uint32_t)__builtin_ctz(m);
-        const uint32_t off = b * 1024u + ln * 16u;
-        bool ok = true;
-        if (off < rg[j].bytes) {
-          const u32x4 v = *(const u32x4*)(act + rg[j].dst + off);
-          ok = v.y == rg[j].tag && (off + 8u >= rg[j].bytes || v.w == rg[j].tag);
-        }
-        if (__builtin_amdgcn_ballot_w64(!ok) == 0) pend[j] &= ~(1u << b);
-        else done = false;
-      }
+      if (j >= nrg || pend[j] == 0u) continue;
+      pend[j] &= uni(stale_blocks(act + rg[j].dst, rg[j].bytes, rg[j].tag));
+      if (pend[j]) done = false;
     }
     if (done) return true;
     ++polls;
