@@ -123,16 +123,19 @@ enum {
 typedef struct mk_plan mk_plan; /* opaque, library-owned */
 
 /* Lower a workload into tile tasks, events and per-worker queues, and upload the queue,
- * zeroed counters and tables to the current device.  host_context_lens: n_requests
+ * zeroed counters and tables to the current device (MegaRTP page, section 4: the host lowering
+ * OpGraph -> tile expansion -> TaskGraph -> KernelPlan).  host_context_lens: n_requests
  * entries (context length per request including the new token).  The plan fixes tile
  * counts and thresholds, so a new plan is needed only when shapes, context lengths or the
- * worker count change (MegaRTP page, section 4: "only M/KV changes need a new plan").
+ * worker count change; the same section rebuilds its plan only when the row count or the KV
+ * lengths change, and rebinds tensors through the pointer table otherwise.
  * Without a HIP device the plan is built on the host only (num_workers must then be > 0):
  * its queue, events and info can be read, and the run entry points return MK_ERR_INVALID.
  * Errors: MK_ERR_INVALID for inconsistent shapes; MK_ERR_UNSUPPORTED for variants not built. */
 mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens, mk_plan** out);
 
-/* Host view of the queue: uint32 [W, L, 32], 32 words per instruction:
+/* Host view of the queue (MegaRTP page, section 4: the KernelPlan's instruction tensor, tasks dealt
+ * round-robin onto W worker queues padded with NoOp): uint32 [W, L, 32], 32 words per instruction:
  *   w0 opcode, w1 wait count, w2 signal count, w3 operand row, w4 spec id, w5 task id,
  *   w6..w13 four (event id, threshold) waits, w14..w19 two (event id, increment,
  *   publication id) signals, w20..w31 payload (layer, tile coordinates, arrival group id,
@@ -140,31 +143,42 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
  * The pointer stays valid until mk_plan_destroy. */
 mk_status mk_plan_queue(const mk_plan* plan, const uint32_t** host_instr, int32_t* W, int32_t* L);
 
-/* Event thresholds: uint32 [num_events]; each equals the increments its producers issue per run. */
+/* Event thresholds (MegaRTP page, section 4: the TaskGraph's counter events, a consumer waiting for
+ * counter >= threshold): uint32 [num_events]; each equals the increments its producers issue per run. */
 mk_status mk_plan_events(const mk_plan* plan, const uint32_t** host_thresholds, int32_t* num_events);
 
-/* Plan facts: n_tasks, n_ops (rows of the operand pointer table), n_arrivals. */
+/* Plan facts (MegaRTP page, section 4: tasks, and one operand-table row per op instance): n_tasks,
+ * n_ops (rows of the operand pointer table, 16 addresses each), n_arrivals (arrival groups). */
 mk_status mk_plan_info(const mk_plan* plan, int32_t* n_tasks, int32_t* n_ops, int32_t* n_arrivals);
 
-/* Bytes of scratch the caller passes as MK_T_WORKSPACE. */
+/* Bytes of scratch the caller passes as MK_T_WORKSPACE / MK_TI_WORKSPACE: the intermediates the
+ * MegaRTP page's operand table points at (section 4), owned by the caller. */
 mk_status mk_plan_workspace_bytes(const mk_plan* plan, size_t* bytes);
 
-/* Byte offset and size of a named intermediate inside the workspace, for inspection.  Vectors
- * written inside a run are tagged records of 8 bytes {uint32 payload, uint32 tag}, the tag being
- * epoch * 1024 + layer + 1 of the run and layer that wrote them (epoch = runs of this plan
- * before): "qkv" fp32 [M, N_qkv], "o" bf16 pairs [M, Hq d / 2], "m" bf16 pairs [M, I / 2],
- * "r2" fp32 [M, H] (residual after attention), "r1" fp32 [M, H] (r2 + y, the next layer's
- * residual input).  "part" holds the split-KV partials as plain fp32, "lm_part" the lm_head
- * tile maxima. */
+/* Byte offset and size of a named intermediate inside the workspace, for inspection.  In
+ * single-token plans the vectors written inside a run are tagged records of 8 bytes
+ * {uint32 payload, uint32 tag}, the tag being salt + epoch * 1024 + layer + 1 of the run and layer
+ * that wrote them (salt: a per-plan multiple of 1024; epoch: runs of this plan before): "qkv" fp32
+ * [M, N_qkv], "o" bf16 pairs [M, Hq d / 2], "m" bf16 pairs [M, I / 2], "r2" fp32 [M, H]
+ * (residual after attention), "r1" fp32 [M, H] (r2 + y, the next layer's residual input).
+ * "part" holds the split-KV partials as plain fp32 (kernel prologue/epilogue page, section 4: per
+ * split its normalised output and log-sum-exp), "lm_part" the lm_head tile maxima.  Multi-row
+ * plans keep "qkv" as records and everything else plain (projection inputs in the matrix-core
+ * operand order, fp32 partial sums per tile and K chunk).  Errors: MK_ERR_INVALID for an unknown name. */
 mk_status mk_plan_workspace_region(const mk_plan* plan, const char* name, size_t* offset, size_t* bytes);
 
-/* Run the plan once as ONE persistent kernel launch on `hip_stream` (asynchronous).
- * An instruction's waits are realised on the data: producers store tagged records (see
+/* Run the plan once as ONE persistent kernel launch on `hip_stream` (asynchronous): one worker
+ * block per compute unit walks its queue (MegaRTP page, section 4: the persistent kernel reading
+ * its instruction tensor, waiting on events before a tile's first read and signalling after its
+ * last write).  Single-token plans realise the waits on the data: producers store tagged records (see
  * mk_plan_workspace_region), and a consumer stages the records it needs until all carry the
  * run's tag -- the event reaches its threshold when every producer tile's records are current.
- * Polls are bounded by a watchdog.  The split-KV combine and the argmax use arrival counters.
- * Not capturable into a graph (the run epoch is a launch argument).  Runs on one plan must be
- * issued on one stream. */
+ * The split-KV combine and the argmax use arrival counters.  Multi-row plans and the indexer
+ * front wait on the queue's event counters, as the page does, with device-scope data accesses.
+ * Polls are bounded by a watchdog (see mk_sync).  Not capturable into a graph (the run epoch is a
+ * launch argument).  Runs on one plan must be issued on one stream.  Errors: MK_ERR_INVALID for a
+ * missing or misaligned tensor, a host-only plan or a launch failure (nothing is launched); device
+ * errors are reported by mk_sync. */
 mk_status mk_run_layer(mk_plan* plan, const mk_tensors* tensors, void* hip_stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
@@ -184,19 +198,26 @@ mk_status mk_run_layer(mk_plan* plan, const mk_tensors* tensors, void* hip_strea
 #define MK_SCRATCH_MAX_BYTES (40u << 20)
 mk_status mk_run_layer_noalloc(mk_plan* plan, const mk_tensors* tensors, void* hip_stream);
 
-/* Run the same op bodies as one standalone kernel per op (one tile per block) inside a
- * hipGraph captured on first use per tensor set; multistream = 0: one stream in topological
- * order; 1: independent branches on forked streams joined by events.  Asynchronous. */
+/* The graph baseline the megakernel is measured against (MegaRTP page, section 8: the same ops as
+ * separate kernels in a graph, on one stream and with branches on several): the same op bodies as
+ * one kernel per op (an op's tasks dealt over min(tasks, workers) blocks of the eight-wave worker,
+ * no waits, signals or tag checks: stream order orders the ops) inside a hipGraph captured on first
+ * use per tensor set; multistream = 0: one stream in topological order; 1: an op with no edge to
+ * the op before it goes on a second stream (at most two streams), joined by events.  Same results
+ * as mk_run_layer bit for bit.  Asynchronous.  Errors as mk_run_layer. */
 mk_status mk_run_graph_baseline(mk_plan* plan, const mk_tensors* tensors, int32_t multistream, void* hip_stream);
 
-/* Wait for the plan's last run on its stream and report the device error record:
+/* Wait for the plan's last run on its stream and report the device error record (the watchdog
+ * bounds the MegaRTP page's section-4 wait for counter >= threshold, which has no bound of its own):
  * MK_ERR_TIMEOUT if a worker's watchdog expired; MK_ERR_INVALID if a block-table entry was outside
  * [0, num_phys_pages) (it was read as page 0, so no access left the cache pool, and the run's outputs
  * are not valid).  On either error the other workers abandon their waits, and the plan's counters
  * are reset so that the next run starts clean. */
 mk_status mk_sync(mk_plan* plan, void* hip_stream);
 
-/* Copy the trace of the last MK_FLAG_TRACE megakernel run into host memory: uint32 [W, L, 16]
+/* Copy the trace of the last MK_FLAG_TRACE megakernel run into host memory (MegaRTP page,
+ * sections 4 and 5: per-task timestamps from which its timeline and empty-framework time are
+ * read; synchronous): uint32 [W, L, 16]
  * per instruction: low 32 bits of the 100 MHz realtime clock when the controller saw it, when
  * its waits were met, when its activations were staged, after the compute start / end
  * barriers, when its outputs were acknowledged, when its arrival resolved (0 if none), when it
@@ -215,6 +236,9 @@ mk_status mk_read_trace(const mk_plan* plan, uint32_t* host_out, size_t n_words)
  * Errors: MK_ERR_INVALID when the plan was built without the flag. */
 mk_status mk_read_gather(const mk_plan* plan, int32_t* host_out, size_t n_words);
 
+/* Plumbing, defined by no page: the calling thread's message for its last failed call (never
+ * NULL), and freeing a plan with everything it allocated (NULL is ignored; the plan's runs must
+ * have completed). */
 const char* mk_last_error(void);
 void mk_plan_destroy(mk_plan* plan);
 
