@@ -198,8 +198,9 @@ mk_status mk_run_layer(mk_plan* plan, const mk_tensors* tensors, void* hip_strea
 #define MK_SCRATCH_MAX_BYTES (40u << 20)
 mk_status mk_run_layer_noalloc(mk_plan* plan, const mk_tensors* tensors, void* hip_stream);
 
-/* The graph baseline the megakernel is measured against (MegaRTP page, section 8: the same ops as
- * separate kernels in a graph, on one stream and with branches on several): the same op bodies as
+/* The graph baseline the megakernel is measured against (MegaRTP page, sections 5 and 6: the same
+ * ops as standalone kernels composed in a graph, independent branches on streams of their own):
+ * the same op bodies as
  * one kernel per op (an op's tasks dealt over min(tasks, workers) blocks of the eight-wave worker,
  * no waits, signals or tag checks: stream order orders the ops) inside a hipGraph captured on first
  * use per tensor set; multistream = 0: one stream in topological order; 1: an op with no edge to
