@@ -42,7 +42,8 @@ typedef enum {
 typedef enum {
   MK_QWEN3_LAYER = 0,   /* one Qwen3-shaped decode layer, returns (y, r2) */
   MK_QWEN3_STEP = 1,    /* num_layers chained layers + final RMSNorm + lm_head + greedy argmax */
-  MK_INDEXER_FRONT = 2  /* A0 -> {B0, C0, B1} -> D1 -> E1 indexer front (MegaRTP page, section 4) */
+  MK_INDEXER_FRONT = 2  /* A0 -> {B0, C0, B1} -> D1 -> E1 indexer front (MegaRTP page, section 4),
+                           optionally followed by the per-token top-k of the scores (mk_config.topk) */
 } mk_workload;
 
 enum {
@@ -67,6 +68,8 @@ typedef struct {
   float rms_eps, rope_theta;
   int32_t num_workers; /* 0 => one worker per compute unit of the current device */
   uint32_t flags;      /* MK_FLAG_* */
+  int32_t topk;        /* MK_INDEXER_FRONT: positions each token selects after the score (0: none,
+                          else 1 .. 8192 keys per row); 0 for the other workloads */
 } mk_config;
 
 /* Device addresses in a fixed order per workload (MK_T_* below); n = number used. */
@@ -112,11 +115,15 @@ enum {
  *   X [M, H] bf16;  R_IN [M, H] fp32
  *   SCORE_OUT [M, S] fp32 with S = the largest context length: row m gets the scores of keys
  *     t < ctx_r (-inf for t > its position); entries t >= ctx_r are not written
- *   WORKSPACE  mk_plan_workspace_bytes() bytes, 256-byte aligned */
+ *   WORKSPACE  mk_plan_workspace_bytes() bytes, 256-byte aligned
+ *   TOPK_OUT [M, topk] int32, only when mk_config.topk > 0 (else the entry may be 0 or absent): row m
+ *     gets the positions of the topk largest scores among its keys t <= its position (MegaRTP page:
+ *     the Top-2048 that follows the paged indexer score), ties to the smaller position, listed in
+ *     ascending order; -1 fills the row past the number of keys when a token has fewer than topk */
 enum {
   MK_TI_W_QA = 0, MK_TI_S_QA, MK_TI_W_W, MK_TI_S_W, MK_TI_W_K, MK_TI_S_K, MK_TI_W_QI, MK_TI_S_QI,
   MK_TI_G_NORM, MK_TI_G_QA, MK_TI_KEY_CACHE, MK_TI_KEY_SCALE, MK_TI_BLOCK_TABLE, MK_TI_CONTEXT_LENS,
-  MK_TI_X, MK_TI_R_IN, MK_TI_SCORE_OUT, MK_TI_WORKSPACE,
+  MK_TI_X, MK_TI_R_IN, MK_TI_SCORE_OUT, MK_TI_WORKSPACE, MK_TI_TOPK_OUT,
   MK_TI_COUNT
 };
 

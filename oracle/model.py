@@ -20,6 +20,7 @@ Indexer front (MegaRTP page, section 4, the A0 -> {B0, C0, B1} -> D1 -> E1 DAG):
         (bt[r][pos // P], pos % P)
     D1: qi = bf16(RoPE(W8A8(qaq, W_qi) as [M, heads, d], pos))
     E1: score[m, t] = sum_h w[m, h] ReLU(sk[t] (qi[m, h] . kq[t])) for t <= pos(m), else -inf
+    top-k (optional, the step after E1): the positions of the k largest fp32 scores t <= pos(m)
 
 Every materialised tensor is returned both before (``*_pre``) and after its storage
 rounding; the next step consumes the rounded value.
@@ -250,6 +251,9 @@ def run_indexer_front(cfg, inp: Dict[str, np.ndarray], ties=None) -> Dict[str, n
         score_pre[mi, :ctx[r]] = ops.indexer_score(qi[mi], w[mi], K, S, int(pos[mi]))
     out["score_pre"] = score_pre
     out["score"] = round_f32(score_pre)
+    # top-k over each token's keys t <= pos, on the scores as stored (fp32)
+    if getattr(cfg, "topk", 0):
+        out["topk"] = np.stack([ops.topk_positions(out["score"][mi], int(pos[mi]) + 1, cfg.topk) for mi in range(M)])
     return out
 
 

@@ -150,3 +150,17 @@ def indexer_score(qi: np.ndarray, w: np.ndarray, kq: np.ndarray, sk: np.ndarray,
     score = np.asarray(w, np.float64) @ relu
     score = np.where(np.arange(T) <= pos, score, -np.inf)
     return score
+
+
+def topk_positions(scores: np.ndarray, n_valid: int, k: int) -> np.ndarray:
+    """Top-k selection after the indexer score (MegaRTP page: the Top-2048 that follows the paged
+    indexer score): the positions of the k largest of scores[:n_valid], ties to the smaller
+    position, listed in ascending order; -1 fills the k entries past n_valid.  (The pages fix
+    neither the tie rule nor the output order; these are the plainest.)"""
+    s = np.asarray(scores[:n_valid], np.float64)
+    pos = np.arange(n_valid)
+    order = np.lexsort((pos, -s))  # by score descending, then by position ascending
+    out = np.full(k, -1, np.int64)
+    sel = np.sort(order[:k])
+    out[:len(sel)] = sel
+    return out

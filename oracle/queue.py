@@ -38,6 +38,7 @@ OP_NORM, OP_GEMM, OP_FIN, OP_QUANT = 7, 8, 9, 10
 OP_COMB = 11  # multi-row: combine the split-KV partials of one (request, kv head)
 # indexer front
 OP_KCACHE, OP_SCORE = 12, 13  # key RoPE + per-token e4m3 + cache write; paged indexer score
+OP_TOPK = 14  # one token row: the positions of its top-k scores
 K_QA, K_W, K_KI, K_QI = 4, 5, 6, 7  # projection kinds: q_a, head weights, indexer key, indexer q
 SCORE_TOK = 128  # keys per indexer-score task
 K_QKV, K_O, K_GU, K_DOWN = 0, 1, 2, 3  # projection kinds
@@ -334,9 +335,11 @@ def _indexer(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
       D1: projection tiles of q_a; one finalize per head (its two 64-row tiles, so that RoPE pairs
         dimensions i and i + 64)
       E1: one score task per (request, SCORE_TOK keys)
+      top-k (when cfg.topk > 0): one task per token row
     Waits: B0 / C0 / B1 tiles on A0 ("tile_cover"); finalizes on their tiles' chunks
     ("tile_reduce"); the q_a norms on B0's finalizes; D1 tiles on the q_a norms; the key-cache
-    task on B1's finalizes; E1 on D1's finalizes, C0's finalize and the key-cache task."""
+    task on B1's finalizes; E1 on D1's finalizes, C0's finalize and the key-cache task; a top-k
+    task on every score task of its request ("whole" per request)."""
     H, qr, nh, hd = cfg.hidden, cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
     R, T = cfg.n_requests, cfg.tokens_per_request
     M = R * T
@@ -397,13 +400,20 @@ def _indexer(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
     for h in range(nh):
         b.task(OP_FIN, row_f, spec, [(ev_head[h], per_head * nk_q)], [(ev_qi, 1)],
                [l, K_QI, h, h * hd, hd, nk_q, kcq])
-    # E1: scores
+    # E1: scores; with a top-k, one event per request counts its score tasks
     row_e = b.op_row()
+    nsc = [-(-int(ctx_lens[r]) // st) for r in range(R)]
+    ev_e1 = [b.event(nsc[r]) for r in range(R)] if cfg.topk else []
     for r in range(R):
         ctx = int(ctx_lens[r])
-        for s in range(-(-ctx // st)):
-            b.task(OP_SCORE, row_e, spec, [(ev_qi, nh), (ev_w, nt_w), (ev_kc, 1)], [],
+        for s in range(nsc[r]):
+            b.task(OP_SCORE, row_e, spec, [(ev_qi, nh), (ev_w, nt_w), (ev_kc, 1)], [(ev_e1[r], 1)] if cfg.topk else [],
                    [l, r, s, s * st, min(ctx, (s + 1) * st)])
+    # top-k: one task per token row, after every score task of its request
+    if cfg.topk:
+        row_tk = b.op_row()
+        for m in range(M):
+            b.task(OP_TOPK, row_tk, spec, [(ev_e1[m // T], nsc[m // T])], [], [l, m])
 
 
 def build_queue(cfg, W: int, ctx_lens=None) -> Dict[str, np.ndarray]:

@@ -80,8 +80,9 @@ mk_status check_tensors(const mk_plan* p, const mk_tensors* t) {
   if (!t) return fail(MK_ERR_INVALID, "null tensors");
   const mk_config& c = p->hp.cfg;
   if (c.workload == MK_INDEXER_FRONT) {
-    if (t->n < MK_TI_COUNT) return fail(MK_ERR_INVALID, "too few tensors for the indexer front");
-    for (int i = 0; i < MK_TI_COUNT; ++i) {
+    const int need = c.topk > 0 ? MK_TI_COUNT : MK_TI_TOPK_OUT;  // the top-k output only with a top-k
+    if (t->n < need) return fail(MK_ERR_INVALID, "too few tensors for the indexer front");
+    for (int i = 0; i < need; ++i) {
       if (t->ptr[i] == 0) return fail(MK_ERR_INVALID, "null tensor at index " + std::to_string(i));
       if (!aligned16(t->ptr[i])) return fail(MK_ERR_INVALID, "tensor " + std::to_string(i) + " is not 16-byte aligned");
     }
@@ -158,6 +159,11 @@ void fill_table_indexer(const mk_plan* p, const mk_tensors* t, std::vector<uint6
         s[SC_BT] = t->ptr[MK_TI_BLOCK_TABLE];
         s[SC_OUT] = t->ptr[MK_TI_SCORE_OUT];
         s[SC_POS] = (uint64_t)p->d_pos;
+        break;
+      case OP_TOPK:
+        s[TK_SCORE] = t->ptr[MK_TI_SCORE_OUT];
+        s[TK_POS] = (uint64_t)p->d_pos;
+        s[TK_OUT] = t->ptr[MK_TI_TOPK_OUT];
         break;
       default: break;
     }
@@ -417,6 +423,7 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
                      c.idx_q_rank, c.idx_heads, c.tokens_per_request, 0};
   for (int r = 0; r < c.n_requests; ++r) p->sh.smax = std::max(p->sh.smax, (int)host_context_lens[r]);
   p->sh.npages = c.num_phys_pages;
+  p->sh.topk = c.topk;
   HIP_TRY(hipMalloc(&p->d_queue, hp.queue.size() * 4));
   HIP_TRY(hipMemcpy(p->d_queue, hp.queue.data(), hp.queue.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipMalloc(&p->d_tasks, hp.tasks.size() * 4));

@@ -15,6 +15,7 @@ struct Shapes {
   int M, kc, fp8, layers;  // multi-row plans: rows, K chunk of a projection tile, W8A8, layers
   int qr, nh, T, smax;     // indexer front: q rank, heads, tokens per request, score row stride
   int npages;              // physical pages of the cache pool: every block-table entry must be below it
+  int topk;                // indexer front: positions each token row selects (0: no top-k)
 };
 
 struct KArgs {

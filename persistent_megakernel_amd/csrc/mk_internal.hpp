@@ -25,7 +25,8 @@ enum Opcode : uint32_t {
   OP_COMB = 11,   // one (request, kv head): combine the split-KV partials into o
   // indexer front
   OP_KCACHE = 12, // the new tokens' keys: RoPE, per-token e4m3, key-cache write
-  OP_SCORE = 13   // one (request, key split): paged indexer score
+  OP_SCORE = 13,  // one (request, key split): paged indexer score
+  OP_TOPK = 14    // one token row: the positions of its top-k scores
 };
 enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_QA = 4, K_W = 5, K_KI = 6, K_QI = 7 };
 constexpr int kScoreTok = 128;  // keys per indexer-score task
@@ -83,6 +84,9 @@ enum KcSlot { KC_K = 0, KC_ROPE, KC_CACHE, KC_SCALE, KC_BT, KC_POS };
 // SCORE: q (bf16, score operand order), head weights (fp32 [M][heads]), key cache, key scales,
 // block table, scores out (fp32 [M][max context]), row positions
 enum ScSlot { SC_Q = 0, SC_W, SC_CACHE, SC_SCALE, SC_BT, SC_OUT, SC_POS };
+// TOPK: scores (fp32 [M][max context]), row positions, selected positions out (int32 [M][topk])
+enum TkSlot { TK_SCORE = 0, TK_POS, TK_OUT };
+constexpr int kTopkMaxKeys = 8192;  // keys a top-k row holds in registers (16 per lane of 512)
 
 struct TileParams {
   int r_qkv = 0, r_o = 0, r_gu = 0, r_down = 0, r_lm = 0, s_tok = 0, spec = 0;

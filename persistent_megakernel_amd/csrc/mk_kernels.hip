@@ -124,6 +124,33 @@ DEV float rows_max(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// inclusive prefix sum over the lanes (row_shr steps inside rows of 16, then the row totals
+// broadcast forward), and over lanes 0 .. 15 only
+DEV uint32_t row16_incl_scan(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  return (uint32_t)x;
+}
+DEV uint32_t wave_incl_scan(uint32_t v) {
+  int x = (int)row16_incl_scan(v);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return (uint32_t)x;
+}
+DEV uint32_t wave_min_u32(uint32_t v) {
+  int x = (int)v;
+  x = min((uint32_t)x, (uint32_t)dppi<0xB1>(x));
+  x = min((uint32_t)x, (uint32_t)dppi<0x4E>(x));
+  x = min((uint32_t)x, (uint32_t)dppi<0x141>(x));
+  x = min((uint32_t)x, (uint32_t)dppi<0x140>(x));
+  x = min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));
+  x = min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+DEV uint32_t wave_max_u32(uint32_t v) { return ~wave_min_u32(~v); }
 DEV uint32_t wave_or_u32(uint32_t v) {
   int x = (int)v;
   x |= dppi<0xB1>(x);
@@ -514,7 +541,8 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
     pf_set<1>(pf, (const void*)s_ld64(row + SC_SCALE), nko ? 1024u : 0u);
     return;
   }
-  if (S == 1 && (op == OP_FIN || op == OP_QUANT || op == OP_KCACHE)) return;  // nothing to prefetch: inputs are produced in the run
+  if (S == 1 && (op == OP_FIN || op == OP_QUANT || op == OP_KCACHE || op == OP_TOPK))
+    return;  // nothing to prefetch: inputs are produced in the run
   if (pf.mode == PF_ATTN) {
     const int r = in.w[W_P1], hk = in.w[W_P2], s = in.w[W_P3];
     const int t0 = in.w[W_P4], t1 = in.w[W_P5];
@@ -1870,6 +1898,209 @@ DEV void score_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease,
 }
 
 // the multi-row op body of one instruction on one of the eight waves (ATTN aside)
+// Top-k of one token row (the Top-2048 that follows the paged indexer score on the MegaRTP page;
+// k is a plan parameter): the positions of the k largest scores among the keys t <= the token's
+// position, ties to the smaller position, in ascending order, -1 past the number of keys.
+// The eight waves hold the row in registers as order-preserving integer keys, lane g of the 512
+// holding positions g, g + 512, ... (coalesced loads).  The bits all keys share (from a block-wide
+// minimum and maximum) are fixed first; radix selection then fixes the k-th largest key 8 bits at a
+// time from the highest differing bit: each wave counts the keys matching the bits fixed so far in
+// its own 256-bin histogram (LDS atomics), and wave 0 sums the eight and walks the bins from the top.
+// The selected positions are written in ascending order with wave ballots and two tables of
+// per-(position block, wave) counts: first how many keys equal to the threshold come earlier (the
+// first ones are taken), then where each selected position goes.
+DEV uint32_t order_key(float f) {  // unsigned order of the keys = float order of the scores (-0 as +0)
+  const uint32_t u = __float_as_uint(f) == 0x80000000u ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+DEV float key_value(uint32_t kk) { return __uint_as_float((kk & 0x80000000u) ? (kk ^ 0x80000000u) : ~kk); }
+
+// One selection pass of the top-k: every counted key (count(j)) adds 1 to bin(j) (0..255) of this
+// wave's histogram; wave 0 sums the eight histograms and walks the bins from the top.  Returns the
+// bin that holds the krem-th largest counted key and sets krem to that key's rank inside the bin.
+template <int J, class Bin, class Count>
+DEV uint32_t topk_pass(uint32_t* hist, uint32_t* ctl, int wv, uint32_t& krem, Bin bin, Count count) {
+  const uint32_t ln = lane();
+  uint32_t* mine = hist + wv * 256;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mine[q * 64 + (int)ln] = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (count(j)) __hip_atomic_fetch_add(mine + bin(j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  lds_barrier();
+  if (wv == 0) {  // lane l holds bins 255 - 4 l - q (q = 0..3): counts from the top
+    u32x4 hv[kNW];  // the eight waves' counts of bins 252 - 4 l .. 255 - 4 l, read together
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) hv[w] = *(const u32x4*)(hist + w * 256 + 252 - 4 * (int)ln);
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      c[0] += hv[w].w;
+      c[1] += hv[w].z;
+      c[2] += hv[w].y;
+      c[3] += hv[w].x;
+    }
+    const uint32_t s4 = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan(s4);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl >= krem);  // the bins hold at least krem keys
+    if (ln == (uint32_t)__builtin_ctzll(hit)) {
+      uint32_t above = incl - s4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (above + c[q] >= krem) {
+          ctl[0] = 255u - 4u * ln - (uint32_t)q;
+          ctl[1] = krem - above;
+          break;
+        }
+        above += c[q];
+      }
+    }
+  }
+  lds_barrier();
+  krem = ctl[1];
+  return ctl[0];
+}
+
+// block-wide minimum and maximum of the keys with count(j); `ctl`: 16 LDS words of its own, 16-byte aligned
+template <int J, class Count>
+DEV void topk_range(const uint32_t* key, uint32_t* ctl, int wv, Count count, uint32_t& lo, uint32_t& hi) {
+  lo = 0xFFFFFFFFu;
+  hi = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (count(j)) {
+      lo = min(lo, key[j]);
+      hi = max(hi, key[j]);
+    }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane() == 0u) {
+    ctl[wv] = lo;
+    ctl[8 + wv] = hi;
+  }
+  lds_barrier();
+  const u32x4 l0 = *(const u32x4*)ctl, l1 = *(const u32x4*)(ctl + 4);  // four loads for the sixteen words
+  const u32x4 h0 = *(const u32x4*)(ctl + 8), h1 = *(const u32x4*)(ctl + 12);
+  lo = min(min(min(l0.x, l0.y), min(l0.z, l0.w)), min(min(l1.x, l1.y), min(l1.z, l1.w)));
+  hi = max(max(max(h0.x, h0.y), max(h0.z, h0.w)), max(max(h1.x, h1.y), max(h1.z, h1.w)));
+}
+DEV uint32_t lanes_below(uint64_t b) {  // set bits of b in the lanes below this one
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+// Block-wide ordering of flagged keys over (position block j, wave, lane): `bits` holds, per lane,
+// a flag for each of its kTopkMaxKeys / 512 keys (bit j: position 512 j + 64 wave + lane).  Returns,
+// in lane j, how many flagged keys come before position block j's part of this wave (all earlier
+// blocks, then this block's earlier waves); `total`: all flagged keys.  `tab`: [J][8] LDS words.
+DEV uint32_t pos_prefix(uint32_t bits, int wv, uint32_t* tab, uint32_t& total) {
+  constexpr int J = kTopkMaxKeys / (kNW * 64);
+  const uint32_t ln = lane();
+  uint32_t mine = 0u;  // lane j: this wave's count in block j
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t c = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((bits >> j) & 1u));
+    mine = ln == (uint32_t)j ? c : mine;
+  }
+  if (ln < (uint32_t)J) tab[ln * kNW + wv] = mine;
+  lds_barrier();
+  uint32_t blk = 0u, earlier = 0u;  // lane j: block j's count over all waves, and over the waves before this one
+  if (ln < (uint32_t)J) {
+    const u32x4 a0 = *(const u32x4*)(tab + ln * kNW), a1 = *(const u32x4*)(tab + ln * kNW + 4);
+    const uint32_t c[kNW] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      blk += c[w];
+      earlier += w < wv ? c[w] : 0u;
+    }
+  }
+  static_assert(J == 16, "the block prefix runs over one row of 16 lanes");
+  const uint32_t incl = row16_incl_scan(blk);  // inclusive prefix over the J blocks (lanes 0 .. J-1)
+  total = (uint32_t)__builtin_amdgcn_readlane((int)incl, J - 1);
+  return incl - blk + earlier;
+}
+DEV void topk_row(const KArgs& a, const Instr& in, int wv) {
+  constexpr int J = kTopkMaxKeys / (kNW * 64);  // keys per lane
+  const Shapes& sh = a.sh;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t m = in.w[W_LAYER + 1], k = (uint32_t)sh.topk, ln = lane();
+  const uint32_t g = (uint32_t)wv * 64u + ln;
+  const uint32_t nvalid = (uint32_t)c_ld<int32_t>((const int32_t*)s_ld64(row + TK_POS) + m) + 1u;
+  __amdgpu_buffer_rsrc_t rs = rsrc((const float*)s_ld64(row + TK_SCORE) + (size_t)m * (uint32_t)sh.smax);
+  uint32_t key[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j)  // every load unconditional (past the row's keys: its last key again), so
+    key[j] = ld32(rs, min((uint32_t)j * 512u + g, nvalid - 1u) * 4u);  // that they are in flight together
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    key[j] = (uint32_t)j * 512u + g < nvalid ? order_key(__uint_as_float(key[j])) : 0u;  // 0: not a key of the row
+  uint32_t* hist = (uint32_t*)(mk_lds + kActOff);  // [8 waves][256] bins
+  uint32_t* ctl = hist + kNW * 256;                 // [2] bin, remainder; at 4 and 20 two min / max tables
+  uint32_t* tab = ctl + 64;                         // [2][J][8 waves] counts per (position block, wave)
+  uint32_t thr = 0u, krem = 0u;  // with k >= the keys, every key (all above 0) is taken
+  if (nvalid > k) {
+    auto valid = [&](int j) { return (uint32_t)j * 512u + g < nvalid; };
+    uint32_t lo, hi;
+    topk_range<J>(key, ctl + 4, wv, valid, lo, hi);
+    krem = k;
+    thr = hi;  // all keys equal: the first k of them
+    if (lo != hi) {
+      // first pass: 256 bins linear in the score between the smallest and the largest (a bin is a
+      // non-decreasing function of the score, so the bins order the keys), which spreads the keys
+      // over the bins whatever their exponents; the keys of the chosen bin remain
+      const float flo = key_value(lo), scale = 256.f / (key_value(hi) - flo);
+      auto vbin = [&](int j) { return min(255u, (uint32_t)((key_value(key[j]) - flo) * scale)); };
+      const uint32_t d0 = topk_pass<J>(hist, ctl, wv, krem, vbin, valid);
+      uint32_t clo, chi;
+      topk_range<J>(key, ctl + 20, wv, [&](int j) { return valid(j) && vbin(j) == d0; }, clo, chi);
+      thr = chi;
+      if (clo != chi) {
+        // then the order keys of the remaining ones, 8 bits at a time from the highest bit in which
+        // they differ (keys in [clo, chi] are exactly the chosen bin's)
+        const int hb = 31 - __builtin_clz(clo ^ chi);
+        uint32_t pmask = hb == 31 ? 0u : ~((2u << hb) - 1u), prefix = chi & pmask;
+        for (int s = hb - 7;; s -= 8) {
+          const uint32_t sft = (uint32_t)max(s, 0), dmask = (1u << (s > 0 ? 8 : 8 + s)) - 1u;
+          const uint32_t d = topk_pass<J>(
+              hist, ctl, wv, krem, [&](int j) { return (key[j] >> sft) & dmask; },
+              [&](int j) { return valid(j) && key[j] >= clo && key[j] <= chi && (key[j] & pmask) == prefix; });
+          prefix |= d << sft;
+          pmask |= dmask << sft;
+          if (s <= 0) break;
+        }
+        thr = prefix;
+      }
+    }
+  }
+  // ties: the krem first keys equal to thr in position order; then each selected key's output slot
+  // (per-lane bit masks over the lane's J keys, so that no lane mask per key stays live)
+  uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const bool v = (uint32_t)j * 512u + g < nvalid;
+    gtm |= v && key[j] > thr ? 1u << j : 0u;
+    eqm |= v && key[j] == thr ? 1u << j : 0u;
+  }
+  uint32_t tot;
+  const uint32_t eq_pos = pos_prefix(eqm, wv, tab, tot);
+  uint32_t selm = gtm;
+#pragma unroll
+  for (int j = 0; j < J; ++j)  // this lane's equal keys in position order: take those before the krem-th
+    selm |= ((eqm >> j) & 1u) && __builtin_amdgcn_readlane(eq_pos, j) + lanes_below(__builtin_amdgcn_ballot_w64((eqm >> j) & 1u)) < krem
+                ? 1u << j : 0u;
+  uint32_t run;
+  const uint32_t sel_pos = pos_prefix(selm, wv, tab + J * kNW, run);
+  __amdgpu_buffer_rsrc_t ro = rsrc((const int32_t*)s_ld64(row + TK_OUT) + (size_t)m * k);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t o = __builtin_amdgcn_readlane(sel_pos, j) + lanes_below(__builtin_amdgcn_ballot_w64((selm >> j) & 1u));
+    if ((selm >> j) & 1u) st32(ro, o * 4u, (uint32_t)j * 512u + g);
+  }
+  for (uint32_t i = run + g; i < k; i += (uint32_t)kNW * 64u) st32(ro, i * 4u, 0xFFFFFFFFu);
+  wait_vm0();
+}
+
+// LD: the instance with loader waves (the Qwen3 layers), which never runs the indexer's top-k: its
+// code stays out of that instance's register allocation
+template <bool LD>
 DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const uint32_t op = in.w[W_OPCODE];
   if (op == OP_GEMM) {
@@ -1893,6 +2124,8 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
     kcache(a, in, wv);
   } else if (op == OP_SCORE) {
     score_tile(a, in, smem, lease, wv);
+  } else if (op == OP_TOPK) {
+    if constexpr (!LD) topk_row(a, in, wv);
   }
 }
 
@@ -2379,7 +2612,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       if (op == OP_ATTN)
         attn_compute<S>(a, in, smem, act, lease, kNW - 1);
       else if constexpr (m16)
-        m16_body(a, in, smem, lease, kNW - 1);
+        m16_body<LD>(a, in, smem, lease, kNW - 1);
       else
         proj_body(a, in, smem, lease, fused_norm, kNW - 1);
     }
@@ -2489,7 +2722,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       if (op == OP_ATTN) {
         attn_compute<S>(a, in, smem, act, lease, cw);
       } else if constexpr (S == 1) {
-        m16_body(a, in, smem, lease, cw);
+        m16_body<LD>(a, in, smem, lease, cw);
       } else {
         proj_body(a, in, smem, lease, fused_norm, cw);
       }

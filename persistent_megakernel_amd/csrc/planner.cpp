@@ -317,12 +317,27 @@ void build_indexer(const mk_config& c, const int32_t* ctx, const TileParams& p, 
   for (int h = 0; h < nh; ++h)
     b.task(OP_FIN, row_d1f, spec, {{ev_head[h], (uint32_t)(per_head * nk_q)}}, {{ev_qi, 1u}},
            {l, K_QI, h, h * hd, hd, nk_q, kcq});
-  // E1
+  // E1; with a top-k, one event per request counts its score tasks
   const int row_e = b.op_row(OP_SCORE, l, {row_d1f, row_c0f, row_kc});
+  const int T = c.tokens_per_request;
+  std::vector<int> ev_e1;
+  if (c.topk > 0)
+    for (int r = 0; r < R; ++r) ev_e1.push_back(b.event((uint32_t)((ctx[r] + st - 1) / st)));
   for (int r = 0; r < R; ++r)
-    for (int s2 = 0; s2 < (ctx[r] + st - 1) / st; ++s2)
-      b.task(OP_SCORE, row_e, spec, {{ev_qi, (uint32_t)nh}, {ev_w, (uint32_t)nt_w}, {ev_kc, 1u}}, {},
-             {l, r, s2, s2 * st, std::min((int)ctx[r], (s2 + 1) * st)});
+    for (int s2 = 0; s2 < (ctx[r] + st - 1) / st; ++s2) {
+      const int t0 = s2 * st, t1 = std::min((int)ctx[r], (s2 + 1) * st);
+      if (c.topk > 0)
+        b.task(OP_SCORE, row_e, spec, {{ev_qi, (uint32_t)nh}, {ev_w, (uint32_t)nt_w}, {ev_kc, 1u}}, {{ev_e1[r], 1u}},
+               {l, r, s2, t0, t1});
+      else
+        b.task(OP_SCORE, row_e, spec, {{ev_qi, (uint32_t)nh}, {ev_w, (uint32_t)nt_w}, {ev_kc, 1u}}, {}, {l, r, s2, t0, t1});
+    }
+  // top-k: one task per token row, after every score task of its request
+  if (c.topk > 0) {
+    const int row_tk = b.op_row(OP_TOPK, l, {row_e});
+    for (int m = 0; m < M; ++m)
+      b.task(OP_TOPK, row_tk, spec, {{ev_e1[m / T], (uint32_t)((ctx[m / T] + st - 1) / st)}}, {}, {l, m});
+  }
 }
 
 // deal the tasks round-robin onto W queues padded with NoOp; move the builder's tables into the plan
@@ -403,6 +418,16 @@ mk_status plan_indexer(const mk_config& c, const int32_t* ctx, int W, HostPlan& 
       err = "context length out of range (at least the request's new tokens, at most its block table)";
       return MK_ERR_INVALID;
     }
+  if (c.topk < 0) {
+    err = "negative top-k";
+    return MK_ERR_INVALID;
+  }
+  if (c.topk > 0)
+    for (int r = 0; r < R; ++r)
+      if (ctx[r] > kTopkMaxKeys) {
+        err = "a top-k over more than 8192 keys per token is not built";
+        return MK_ERR_UNSUPPORTED;
+      }
   out = HostPlan{};
   out.cfg = c;
   out.ctx.assign(ctx, ctx + R);
@@ -437,6 +462,10 @@ mk_status plan_indexer(const mk_config& c, const int32_t* ctx, int W, HostPlan& 
 
 mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& out, std::string& err) {
   if (c.workload == MK_INDEXER_FRONT) return plan_indexer(c, ctx, W, out, err);
+  if (c.topk != 0) {
+    err = "top-k belongs to the indexer front";
+    return MK_ERR_INVALID;
+  }
   if (c.workload != MK_QWEN3_LAYER && c.workload != MK_QWEN3_STEP) {
     err = "workload not built in this library";
     return MK_ERR_UNSUPPORTED;

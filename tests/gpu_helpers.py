@@ -86,6 +86,8 @@ class IndexerRun:
         self.smax = max(ctx)
         t["score_out"] = torch.full((cfg.m * self.smax,), float("nan"), dtype=torch.float32, device="cuda")
         t["workspace"] = torch.zeros(self.plan.workspace_bytes() + 256, dtype=torch.uint8, device="cuda")
+        if getattr(cfg, "topk", 0):
+            t["topk_out"] = torch.full((cfg.m * cfg.topk,), -7, dtype=torch.int32, device="cuda")
         self.t = t
         self.tensors = mk.indexer_pointers(t)
 

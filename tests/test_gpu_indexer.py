@@ -9,6 +9,14 @@ round-to-nearest-even code except inside the ambiguity set the oracle computes f
 where it is one of the two enclosing codes.  Key-cache writes: the written slot set is exact (every
 other byte of the cache and its scales is unchanged).  Scores: -inf exactly for keys after a token's
 position; all modes give the same bits.
+
+Top-k (plans with cfg.topk): a selection decided in floating point, so two checks.  Validity on the
+kernel's own fp32 scores, exactly: min(k, keys) distinct positions <= the token's position in
+ascending order, -1 after them, and every selected key beats every unselected one (a larger score,
+or an equal score and a smaller position).  Against the independent oracle: the kernel's set and
+the oracle's (computed on the oracle's own scores) may differ only in keys whose oracle score lies
+within 2 x TOL of the oracle's k-th largest score (a key outside that window is above or below the
+kernel's own threshold too, since every kernel score is within TOL of the oracle's).
 """
 import dataclasses
 import sys
@@ -124,6 +132,39 @@ def _check_cache(run, inp, ref, kc0, ks0, tag):
     assert np.array_equal(e4m3_decode(kc[page, off]), e4m3_decode(ref["kq"])), tag
 
 
+def _check_topk(run, ind, tag):
+    cfg = run.cfg
+    M, k = cfg.m, cfg.topk
+    got = run.t["topk_out"].cpu().numpy().astype(np.int64).reshape(M, k)
+    score = run.t["score_out"].cpu().numpy().astype(np.float64).reshape(M, run.smax)
+    window = 0
+    for m in range(M):
+        nv = int(ind["pos"][m]) + 1
+        n = min(k, nv)
+        sel = got[m, :n]
+        assert np.all(got[m, n:] == -1), f"{tag}: row {m} padding"
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < nv, f"{tag}: row {m} positions"
+        s = score[m, :nv]
+        chosen = np.zeros(nv, bool)
+        chosen[sel] = True
+        if n < nv:  # every selected key beats every unselected one
+            lo = s[chosen].min()
+            assert s[~chosen].max() <= lo, f"{tag}: row {m} an unselected score above the selection"
+            tie_sel = np.flatnonzero(chosen & (s == lo))
+            tie_out = np.flatnonzero(~chosen & (s == lo))
+            assert tie_out.size == 0 or tie_out.min() > tie_sel.max(), f"{tag}: row {m} ties not to the smaller position"
+        # against the independent oracle: differences only near its k-th largest score
+        os_ = ind["score"][m, :nv]
+        kth = np.sort(os_)[::-1][n - 1]
+        ref = np.zeros(nv, bool)
+        ref[ind["topk"][m, :n]] = True
+        diff = np.flatnonzero(ref != chosen)
+        assert np.all(np.abs(os_[diff] - kth) <= 2 * TOL), f"{tag}: row {m} differs from the oracle away from its threshold"
+        window += int(np.sum(np.abs(os_ - kth) <= 2 * TOL))
+        assert len(diff) <= 2 * np.sum(np.abs(os_ - kth) <= 2 * TOL)
+    _say(f"  {tag}: top-{k} valid on the kernel's scores; {window} keys of {M} rows within the oracle's threshold window")
+
+
 def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True), ("mk", False)),
           W=0, intermediates=True):
     from gpu_helpers import IndexerRun
@@ -131,7 +172,7 @@ def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True
     inp["context_lens"] = np.array(ctx, dtype=np.int32)
     kc0, ks0 = inp["key_cache"].copy(), inp["key_scale"].astype(np.float64).copy()
     run = IndexerRun(cfg, inp, num_workers=W)
-    outs = []
+    outs, outs_k = [], []
     ref = None
     for mode, ms in modes:
         _say(f"case: {cfg.name} R={cfg.n_requests} T={cfg.tokens_per_request} ctx={ctx} W={W} {mode} ms={ms}")
@@ -142,8 +183,14 @@ def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True
         _check(run, inp, ref, ind, f"{mode}/{ms}", intermediates)
         _check_cache(run, inp, ref, kc0, ks0, f"{mode}/{ms}")
         outs.append(run.t["score_out"].clone())
+        if cfg.topk:
+            _check_topk(run, ind, f"{mode}/{ms}")
+            outs_k.append(run.t["topk_out"].clone())
+            run.t["topk_out"].fill_(-7)
     for o in outs[1:]:
         assert torch.equal(torch.nan_to_num(o), torch.nan_to_num(outs[0]))
+    for o in outs_k[1:]:
+        assert torch.equal(o, outs_k[0])
 
 
 @pytest.mark.parametrize("R,T,ctx,W", [(2, 8, [300, 133], 0), (3, 5, [64, 196, 5], 37)])
@@ -157,3 +204,17 @@ def test_indexer_reduced(R, T, ctx, W):
 def test_indexer_full_size():
     cfg = get_config("indexer_front")
     _case(cfg, [cfg.context] * cfg.n_requests, seed=0, modes=(("mk", False), ("graph", False), ("graph", True)))
+
+
+@pytest.mark.parametrize("R,T,ctx,W,k", [(2, 8, [300, 133], 0, 64), (3, 5, [64, 196, 5], 37, 100)])
+def test_indexer_topk_reduced(R, T, ctx, W, k):
+    """Top-k after the score, with rows that have more keys than k and rows that have fewer."""
+    cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, n_requests=R,
+                              tokens_per_request=T, context=max(ctx), topk=k)
+    _case(cfg, ctx, seed=12, W=W, intermediates=False)
+
+
+@pytest.mark.timeout(600)
+def test_indexer_topk_full_size():
+    cfg = get_config("indexer_front_topk")  # Top-2048 of 8192 keys per token, 16 tokens
+    _case(cfg, [cfg.context] * cfg.n_requests, seed=0, modes=(("mk", False), ("graph", False)), intermediates=False)

@@ -148,3 +148,44 @@ def test_indexer_score_brute_force_and_reductions():
     onehot = np.array([0.0, 1.0, 0.0])
     s1 = ops.indexer_score(qi, onehot, kq, sk, T)
     assert np.allclose(s1, sk * np.maximum(0, kq @ qi[1]), atol=1e-14)
+
+
+def _topk_valid(scores, n_valid, k, got):
+    """The defining property, checked pair by pair: min(k, n_valid) distinct positions < n_valid in
+    ascending order, -1 after them, and every selected position beats every unselected one (a
+    larger score, or an equal score and a smaller position)."""
+    n = min(k, n_valid)
+    sel = [int(v) for v in got[:n]]
+    assert all(v == -1 for v in got[n:])
+    assert sel == sorted(set(sel)) and all(0 <= v < n_valid for v in sel)
+    rest = [t for t in range(n_valid) if t not in set(sel)]
+    for i in sel:
+        for j in rest:
+            assert scores[i] > scores[j] or (scores[i] == scores[j] and i < j), (i, j)
+
+
+def test_topk_brute_force_and_special_cases():
+    rng = np.random.default_rng(3)
+    for trial in range(200):  # small rows with many ties (values from a set of 4)
+        n = int(rng.integers(1, 12))
+        s = rng.integers(0, 4, n).astype(np.float64) - 1.5
+        nv = int(rng.integers(0, n + 1))
+        k = int(rng.integers(1, n + 2))
+        got = ops.topk_positions(s, nv, k)
+        assert got.shape == (k,)
+        _topk_valid(s, nv, k, got)
+        # brute force: the selected set is the unique one of its size with that property
+        if nv <= 8:
+            from itertools import combinations
+            m = min(k, nv)
+            good = [c for c in combinations(range(nv), m)
+                    if all(s[i] > s[j] or (s[i] == s[j] and i < j) for i in c for j in range(nv) if j not in c)]
+            assert len(good) == 1 and list(good[0]) == [int(v) for v in got[:m]]
+    # fewer keys than k: every key, then -1
+    assert list(ops.topk_positions(np.array([5.0, -1.0, 2.0]), 3, 5)) == [0, 1, 2, -1, -1]
+    # all equal: the first k positions
+    assert list(ops.topk_positions(np.zeros(10), 10, 4)) == [0, 1, 2, 3]
+    # increasing scores: the last k positions; keys past n_valid are ignored
+    assert list(ops.topk_positions(np.arange(10.0), 7, 3)) == [4, 5, 6]
+    # -inf and negative scores order below everything finite
+    assert list(ops.topk_positions(np.array([-np.inf, -3.0, 0.0, -np.inf]), 4, 2)) == [1, 2]

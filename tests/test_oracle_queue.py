@@ -10,7 +10,7 @@ from workloads import get_config
 
 
 @pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
-                                  "indexer_front"])
+                                  "indexer_front", "indexer_front_topk"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_invariants(name, W):
     cfg = get_config(name)
@@ -154,8 +154,9 @@ def test_indexer_front_counts_and_no_deadlock():
     assert ops.count(oq.OP_KCACHE) == 1 and ops.count(oq.OP_SCORE) == 2 * 8192 // 128
     assert plan["n_tasks"] == 670
     small = dataclasses.replace(cfg, hidden=1024, idx_q_rank=512, context=300)
-    for W in (3, 64):
-        p = oq.build_queue(small, W)
-        oq.check_invariants(p)
-        for seed in range(2):
-            simulate(p, seed)
+    for topk in (0, 64):
+        for W in (3, 64):
+            p = oq.build_queue(dataclasses.replace(small, topk=topk), W)
+            oq.check_invariants(p)
+            for seed in range(2):
+                simulate(p, seed)

@@ -17,7 +17,7 @@ def _both(cfg, W, ctx=None):
 
 
 @pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
-                                  "indexer_front"])
+                                  "indexer_front", "indexer_front_topk"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_queue_bit_exact(name, W):
     cfg = get_config(name)
@@ -51,9 +51,10 @@ def test_small_shapes_bit_exact():
         plan.close()
 
 
-def test_indexer_ragged_bit_exact():
+@pytest.mark.parametrize("topk", [0, 64])
+def test_indexer_ragged_bit_exact(topk):
     cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, idx_heads=64,
-                              n_requests=2, tokens_per_request=3, context=300)
+                              n_requests=2, tokens_per_request=3, context=300, topk=topk)
     for ctx in ([300, 3], [129, 256]):
         for W in (5, 64, 256):
             plan, ref = _both(cfg, W, ctx)
@@ -120,3 +121,21 @@ def test_multi_row_attention_chain_lengths(name):
         s = [int(t[23]) for t in att]
         assert s == list(range(s[0], s[0] + ns // 2)) and s[0] % (ns // 2) == 0
         assert [int(t[30]) for t in att] == [0] + [1] * (ns // 2 - 2) + [3] and len({int(t[31]) for t in att}) == 1
+
+
+def test_topk_plan_shape_and_limits():
+    """The top-k adds one task per token row after its request's score tasks and leaves the rest of
+    the plan as without it; more than 8192 keys per row is refused."""
+    import persistent_megakernel_amd as mk
+    base = get_config("indexer_front")
+    with_k = get_config("indexer_front_topk")
+    a, b = oq.build_queue(base, 256), oq.build_queue(with_k, 256)
+    assert b["n_tasks"] == a["n_tasks"] + with_k.m
+    tasks = b["queue"].reshape(-1, 32)
+    topk = tasks[tasks[:, 0] == oq.OP_TOPK]
+    assert sorted(int(t[21]) for t in topk) == list(range(with_k.m))
+    assert all(int(t[7]) == 8192 // 128 for t in topk)
+    with pytest.raises(mk.MkError, match="8192 keys"):
+        mk.Plan(dataclasses.replace(with_k, context=8200), num_workers=256)
+    with pytest.raises(mk.MkError, match="indexer front"):
+        mk.Plan(dataclasses.replace(get_config("qwen3_0p6b_layer"), topk=4), num_workers=256)

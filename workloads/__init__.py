@@ -52,6 +52,7 @@ class Config:
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     residual_zero: bool = False  # r_in == 0 (full decode step)
+    topk: int = 0  # indexer front: positions each token selects after the score (0: no top-k)
 
     @property
     def m(self) -> int:
@@ -88,6 +89,12 @@ CONFIGS: Dict[str, Config] = {
                             tokens_per_request=8, context=8192, page_size=64, random_pages=True,
                             weight_fp8=True, act_fp8=True, idx_q_rank=1536, idx_heads=64,
                             idx_head_dim=128),
+    # The same front followed by the per-token Top-2048 over its 8192 scores (the MegaRTP page's
+    # next step after the paged indexer score).
+    "indexer_front_topk": Config("indexer_front_topk", "indexer_front", hidden=6144, n_requests=2,
+                                 tokens_per_request=8, context=8192, page_size=64, random_pages=True,
+                                 weight_fp8=True, act_fp8=True, idx_q_rank=1536, idx_heads=64,
+                                 idx_head_dim=128, topk=2048),
 }
 
 
@@ -269,5 +276,7 @@ def algorithmic_bytes(cfg) -> Dict[str, int]:
         parts["keys_write"] = M * (hd + 4)
         parts["act_in"] = M * H * (2 + 4)
         parts["score_out"] = M * cfg.context * 4
+        if cfg.topk:
+            parts["topk_out"] = M * cfg.topk * 4  # the scores it reads are this workload's own output
     parts["total"] = sum(parts.values())
     return parts
