@@ -64,7 +64,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_0p6b_step",
                     choices=["qwen3_0p6b_step", "qwen3_0p6b_layer", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
-                             "indexer_front", "indexer_front_topk"])
+                             "indexer_front", "indexer_front_topk", "attention_pre"])
     ap.add_argument("--rotate", type=int, default=0, help="copies of weights/caches cycled per run (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
@@ -126,6 +126,8 @@ def main() -> int:
             s["workspace"] = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
             if cfg.topk:
                 s["topk_out"] = torch.zeros(M * cfg.topk, dtype=torch.int32, device="cuda")
+            if cfg.mla_heads:
+                s["qlat_out"] = torch.zeros(M * cfg.mla_heads * 512, dtype=torch.int16, device="cuda")
             tensor_sets.append(mk.indexer_pointers(s))
             continue
         s["y_out"] = torch.zeros(M * H, dtype=torch.int16, device="cuda")
@@ -197,7 +199,8 @@ def main() -> int:
         "data": "synthetic (seeded random weights and KV caches of the workload's shapes)",
         "config": ({"workload": cfg.name, "hidden": cfg.hidden, "q_rank": cfg.idx_q_rank, "heads": cfg.idx_heads,
                     "head_dim": cfg.idx_head_dim, "requests": cfg.n_requests, "tokens_per_request": cfg.tokens_per_request,
-                    "context": cfg.context, "page_size": cfg.page_size, "topk": cfg.topk, "rotation_copies": rotate,
+                    "context": cfg.context, "page_size": cfg.page_size, "topk": cfg.topk, "mla_heads": cfg.mla_heads,
+                    "rotation_copies": rotate,
                     "workers": int(p0.queue().shape[0])} if indexer else
                    {"workload": cfg.name, "layers": layers, "hidden": cfg.hidden, "inter": cfg.inter,
                     "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,

@@ -43,7 +43,8 @@ typedef enum {
   MK_QWEN3_LAYER = 0,   /* one Qwen3-shaped decode layer, returns (y, r2) */
   MK_QWEN3_STEP = 1,    /* num_layers chained layers + final RMSNorm + lm_head + greedy argmax */
   MK_INDEXER_FRONT = 2  /* A0 -> {B0, C0, B1} -> D1 -> E1 indexer front (MegaRTP page, section 4),
-                           optionally followed by the per-token top-k of the scores (mk_config.topk) */
+                           optionally with the main-MLA query half D0 -> D2 (mk_config.mla_heads) and
+                           the per-token top-k of the scores (mk_config.topk) */
 } mk_workload;
 
 enum {
@@ -70,6 +71,8 @@ typedef struct {
   uint32_t flags;      /* MK_FLAG_* */
   int32_t topk;        /* MK_INDEXER_FRONT: positions each token selects after the score (0: none,
                           else 1 .. 8192 keys per row); 0 for the other workloads */
+  int32_t mla_heads;   /* MK_INDEXER_FRONT: heads of the main-MLA query half (D0 Main-Q -> D2 Q-BMM,
+                          128 no-RoPE dims and a 512-wide latent per head); 0: the indexer half only */
 } mk_config;
 
 /* Device addresses in a fixed order per workload (MK_T_* below); n = number used. */
@@ -116,6 +119,12 @@ enum {
  *   SCORE_OUT [M, S] fp32 with S = the largest context length: row m gets the scores of keys
  *     t < ctx_r (-inf for t > its position); entries t >= ctx_r are not written
  *   WORKSPACE  mk_plan_workspace_bytes() bytes, 256-byte aligned
+ *   main-MLA half, only when mk_config.mla_heads = nm > 0 (else the entries may be 0 or absent):
+ *     W_QB [nm 128, qr] e4m3 + S_QB (D0 Main-Q: rows h 128 .. h 128 + 127 are head h's no-RoPE query
+ *     from the normalised q_a); W_UK [nm 512, 128] bf16 (D2 Q-BMM: rows h 512 .. h 512 + 511 are head
+ *     h's [512, 128] up-projection of keys, absorbed into the query); QLAT_OUT [M, nm, 512] bf16:
+ *     q_lat[m][h] = W_UK[h] q_nope[m][h], q_nope[m][h] = bf16(W_QB[h] q_a(m)) (MegaRTP page, section 4:
+ *     the D0 -> D2 edge of the attention-pre graph)
  *   TOPK_OUT [M, topk] int32, only when mk_config.topk > 0 (else the entry may be 0 or absent): row m
  *     gets the positions of the topk largest scores among its keys t <= its position (MegaRTP page:
  *     the Top-2048 that follows the paged indexer score), ties to the smaller position, listed in
@@ -124,6 +133,7 @@ enum {
   MK_TI_W_QA = 0, MK_TI_S_QA, MK_TI_W_W, MK_TI_S_W, MK_TI_W_K, MK_TI_S_K, MK_TI_W_QI, MK_TI_S_QI,
   MK_TI_G_NORM, MK_TI_G_QA, MK_TI_KEY_CACHE, MK_TI_KEY_SCALE, MK_TI_BLOCK_TABLE, MK_TI_CONTEXT_LENS,
   MK_TI_X, MK_TI_R_IN, MK_TI_SCORE_OUT, MK_TI_WORKSPACE, MK_TI_TOPK_OUT,
+  MK_TI_W_QB, MK_TI_S_QB, MK_TI_W_UK, MK_TI_QLAT_OUT,
   MK_TI_COUNT
 };
 

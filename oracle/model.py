@@ -21,6 +21,8 @@ Indexer front (MegaRTP page, section 4, the A0 -> {B0, C0, B1} -> D1 -> E1 DAG):
     D1: qi = bf16(RoPE(W8A8(qaq, W_qi) as [M, heads, d], pos))
     E1: score[m, t] = sum_h w[m, h] ReLU(sk[t] (qi[m, h] . kq[t])) for t <= pos(m), else -inf
     top-k (optional, the step after E1): the positions of the k largest fp32 scores t <= pos(m)
+    D0 / D2 (optional, the main-MLA query half): q_nope = bf16(W8A8(qaq, W_qb)) per head, then
+        q_lat[m, h] = bf16(W_uk[h] q_nope[m, h])
 
 Every materialised tensor is returned both before (``*_pre``) and after its storage
 rounding; the next step consumes the rounded value.
@@ -251,6 +253,15 @@ def run_indexer_front(cfg, inp: Dict[str, np.ndarray], ties=None) -> Dict[str, n
         score_pre[mi, :ctx[r]] = ops.indexer_score(qi[mi], w[mi], K, S, int(pos[mi]))
     out["score_pre"] = score_pre
     out["score"] = round_f32(score_pre)
+    # main-MLA query half (the D0 -> D2 edge of the MegaRTP page's attention-pre graph, section 4):
+    # D0 q_nope[h] = bf16(W8A8(qaq, W_qb) rows h 128 .. h 128 + 127); D2 q_lat[h] = bf16(q_nope[h] W_uk[h]^T)
+    nm = getattr(cfg, "mla_heads", 0)
+    if nm:
+        qn_pre = w8a8("w_qb", qaq, sqa).reshape(M, nm, 128)
+        qn = round_bf16(qn_pre)
+        w_uk = bf16_bits_to_f64(inp["w_uk"]).reshape(nm, 512, 128)
+        ql_pre = np.einsum("mhk,hnk->mhn", qn, w_uk)
+        out.update(qn_pre=qn_pre, qn=qn, qlat_pre=ql_pre, qlat=round_bf16(ql_pre))
     # top-k over each token's keys t <= pos, on the scores as stored (fp32)
     if getattr(cfg, "topk", 0):
         out["topk"] = np.stack([ops.topk_positions(out["score"][mi], int(pos[mi]) + 1, cfg.topk) for mi in range(M)])

@@ -40,6 +40,8 @@ OP_COMB = 11  # multi-row: combine the split-KV partials of one (request, kv hea
 OP_KCACHE, OP_SCORE = 12, 13  # key RoPE + per-token e4m3 + cache write; paged indexer score
 OP_TOPK = 14  # one token row: the positions of its top-k scores
 K_QA, K_W, K_KI, K_QI = 4, 5, 6, 7  # projection kinds: q_a, head weights, indexer key, indexer q
+K_QB, K_UK = 8, 9  # main-MLA query (D0, finalized per head) and query BMM (D2, one chunk)
+MLA_NOPE, MLA_LATENT = 128, 512  # per main-MLA head: D0 output, D2 output
 SCORE_TOK = 128  # keys per indexer-score task
 K_QKV, K_O, K_GU, K_DOWN = 0, 1, 2, 3  # projection kinds
 NONE = 0xFFFFFFFF
@@ -336,10 +338,13 @@ def _indexer(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
         dimensions i and i + 64)
       E1: one score task per (request, SCORE_TOK keys)
       top-k (when cfg.topk > 0): one task per token row
+      D0 / D2 (when cfg.mla_heads > 0): D0 projection tiles (as D1) with a finalize per head, then
+        per head 8 tiles of 64 latent rows of D2 over that head's 128 columns
     Waits: B0 / C0 / B1 tiles on A0 ("tile_cover"); finalizes on their tiles' chunks
     ("tile_reduce"); the q_a norms on B0's finalizes; D1 tiles on the q_a norms; the key-cache
     task on B1's finalizes; E1 on D1's finalizes, C0's finalize and the key-cache task; a top-k
-    task on every score task of its request ("whole" per request)."""
+    task on every score task of its request ("whole" per request); D0 tiles on the q_a norms, a
+    D0 finalize on its head's tiles, D2 tiles on their head's finalize ("tile_cover" per head)."""
     H, qr, nh, hd = cfg.hidden, cfg.idx_q_rank, cfg.idx_heads, cfg.idx_head_dim
     R, T = cfg.n_requests, cfg.tokens_per_request
     M = R * T
@@ -400,6 +405,24 @@ def _indexer(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
     for h in range(nh):
         b.task(OP_FIN, row_f, spec, [(ev_head[h], per_head * nk_q)], [(ev_qi, 1)],
                [l, K_QI, h, h * hd, hd, nk_q, kcq])
+    # main-MLA query half, dealt after D1 and before E1 as in the page's tile list: D0 tiles over the
+    # normalised q_a (as D1), one finalize per head, then D2's tiles of a head once that head is
+    # finalized (an event per head: the page's per-head tile_cover of D0 -> D2)
+    nm = getattr(cfg, "mla_heads", 0)
+    if nm:
+        per_head_qb = MLA_NOPE // rt
+        ev_qb = [b.event(per_head_qb * nk_q) for _ in range(nm)]
+        tiles(K_QB, nm * MLA_NOPE, qr, kcq, (ev_qn, M), lambda j: ev_qb[j // per_head_qb])
+        row_d0f = b.op_row()
+        ev_qn_h = [b.event(1) for _ in range(nm)]
+        for h in range(nm):
+            b.task(OP_FIN, row_d0f, spec, [(ev_qb[h], per_head_qb * nk_q)], [(ev_qn_h[h], 1)],
+                   [l, K_QB, h, h * MLA_NOPE, MLA_NOPE, nk_q, kcq])
+        row_d2 = b.op_row()
+        for h in range(nm):
+            for j in range(MLA_LATENT // rt):
+                b.task(OP_GEMM, row_d2, spec, [(ev_qn_h[h], 1)], [],
+                       [l, K_UK, h * (MLA_LATENT // rt) + j, h * MLA_LATENT + j * rt, rt, 0, MLA_NOPE, h * MLA_NOPE])
     # E1: scores; with a top-k, one event per request counts its score tasks
     row_e = b.op_row()
     nsc = [-(-int(ctx_lens[r]) // st) for r in range(R)]

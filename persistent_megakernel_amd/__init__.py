@@ -34,7 +34,8 @@ QWEN3_TENSORS = ["w_qkv", "w_o", "w_gu", "w_down", "g_attn", "g_mlp", "g_q", "g_
                  "g_final", "w_lm", "logits_out", "token_out",
                  "s_qkv", "s_o", "s_gu", "s_down"]
 INDEXER_TENSORS = ["w_qa", "s_qa", "w_w", "s_w", "w_k", "s_k", "w_qi", "s_qi", "g_norm", "g_qa", "key_cache",
-                   "key_scale", "block_table", "context_lens", "x", "r_in", "score_out", "workspace", "topk_out"]
+                   "key_scale", "block_table", "context_lens", "x", "r_in", "score_out", "workspace", "topk_out",
+                   "w_qb", "s_qb", "w_uk", "qlat_out"]
 _WORKLOADS = {"qwen3_layer": MK_QWEN3_LAYER, "qwen3_step": MK_QWEN3_STEP, "indexer_front": MK_INDEXER_FRONT}
 
 
@@ -44,7 +45,7 @@ class MkConfig(ctypes.Structure):
         "num_layers", "vocab", "n_requests", "tokens_per_request", "page_size", "max_pages_per_req",
         "num_phys_pages", "idx_q_rank", "idx_heads", "idx_head_dim")] + [
         ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("num_workers", ctypes.c_int32),
-        ("flags", ctypes.c_uint32), ("topk", ctypes.c_int32)]
+        ("flags", ctypes.c_uint32), ("topk", ctypes.c_int32), ("mla_heads", ctypes.c_int32)]
 
 
 class MkTensors(ctypes.Structure):
@@ -98,6 +99,7 @@ def make_config(cfg, num_workers: int = 0, flags: int = 0) -> MkConfig:
     c.rms_eps, c.rope_theta = float(cfg.rms_eps), float(cfg.rope_theta)
     c.num_workers, c.flags = int(num_workers), int(flags)
     c.topk = int(getattr(cfg, "topk", 0))
+    c.mla_heads = int(getattr(cfg, "mla_heads", 0))
     return c
 
 
@@ -217,5 +219,5 @@ def exported_symbols():
 
 def indexer_pointers(t: Dict[str, "object"]) -> MkTensors:
     """mk_tensors in the indexer front's ABI order from a dict of device tensors keyed by INDEXER_TENSORS
-    ("topk_out" only for plans with a top-k: 0 when absent)."""
+    ("topk_out" only for plans with a top-k, the main-MLA tensors only with that half: 0 when absent)."""
     return Plan.tensors([t[n].data_ptr() if n in t else 0 for n in INDEXER_TENSORS])

@@ -80,9 +80,11 @@ mk_status check_tensors(const mk_plan* p, const mk_tensors* t) {
   if (!t) return fail(MK_ERR_INVALID, "null tensors");
   const mk_config& c = p->hp.cfg;
   if (c.workload == MK_INDEXER_FRONT) {
-    const int need = c.topk > 0 ? MK_TI_COUNT : MK_TI_TOPK_OUT;  // the top-k output only with a top-k
+    // the top-k output only with a top-k, the main-MLA tensors only with the main-MLA half
+    const int need = c.mla_heads > 0 ? MK_TI_COUNT : c.topk > 0 ? MK_TI_TOPK_OUT + 1 : MK_TI_TOPK_OUT;
     if (t->n < need) return fail(MK_ERR_INVALID, "too few tensors for the indexer front");
     for (int i = 0; i < need; ++i) {
+      if (i == MK_TI_TOPK_OUT && c.topk == 0) continue;
       if (t->ptr[i] == 0) return fail(MK_ERR_INVALID, "null tensor at index " + std::to_string(i));
       if (!aligned16(t->ptr[i])) return fail(MK_ERR_INVALID, "tensor " + std::to_string(i) + " is not 16-byte aligned");
     }
@@ -114,10 +116,13 @@ void fill_table_indexer(const mk_plan* p, const mk_tensors* t, std::vector<uint6
   const mk::HostPlan& hp = p->hp;
   const uint64_t ws = t->ptr[MK_TI_WORKSPACE];
   auto rg = [&](const char* n) { return ws + region_off(hp, n); };
-  const uint64_t wt[8] = {0, 0, 0, 0, t->ptr[MK_TI_W_QA], t->ptr[MK_TI_W_W], t->ptr[MK_TI_W_K], t->ptr[MK_TI_W_QI]};
-  const uint64_t st[8] = {0, 0, 0, 0, t->ptr[MK_TI_S_QA], t->ptr[MK_TI_S_W], t->ptr[MK_TI_S_K], t->ptr[MK_TI_S_QI]};
-  const char* gp[8] = {"", "", "", "", "gp_qa", "gp_w", "gp_k", "gp_qi"};
-  const char* out[8] = {"", "", "", "", "qa", "w", "k", "qi"};
+  const bool mla = hp.cfg.mla_heads > 0;
+  const uint64_t wt[10] = {0, 0, 0, 0, t->ptr[MK_TI_W_QA], t->ptr[MK_TI_W_W], t->ptr[MK_TI_W_K], t->ptr[MK_TI_W_QI],
+                           mla ? t->ptr[MK_TI_W_QB] : 0, mla ? t->ptr[MK_TI_W_UK] : 0};
+  const uint64_t st[10] = {0, 0, 0, 0, t->ptr[MK_TI_S_QA], t->ptr[MK_TI_S_W], t->ptr[MK_TI_S_K], t->ptr[MK_TI_S_QI],
+                           mla ? t->ptr[MK_TI_S_QB] : 0, 0};
+  const char* gp[10] = {"", "", "", "", "gp_qa", "gp_w", "gp_k", "gp_qi", "gp_qb", ""};
+  const char* out[10] = {"", "", "", "", "qa", "w", "k", "qi", "qn", ""};
   tab.assign(hp.ops.size() * kTableSlots, 0);
   for (size_t row = 0; row < hp.ops.size(); ++row) {
     uint64_t* s = &tab[row * kTableSlots];
@@ -133,13 +138,13 @@ void fill_table_indexer(const mk_plan* p, const mk_tensors* t, std::vector<uint6
         break;
       case OP_GEMM:
         s[GM_W] = wt[sub];
-        s[GM_ACT] = rg(sub == K_QI ? "qaq" : "hq");
-        s[GM_PART] = rg(gp[sub]);
+        s[GM_ACT] = rg(sub == K_UK ? "qn" : sub == K_QI || sub == K_QB ? "qaq" : "hq");
+        s[GM_PART] = sub == K_UK ? t->ptr[MK_TI_QLAT_OUT] : rg(gp[sub]);  // D2 writes its output directly
         s[GM_SW] = st[sub];
         break;
       case OP_FIN:
         s[FN_PART] = rg(gp[sub]);
-        s[FN_SA] = rg(sub == K_QI ? "sqa" : "sh");
+        s[FN_SA] = rg(sub == K_QI || sub == K_QB ? "sqa" : "sh");
         s[FN_OUT] = rg(out[sub]);
         s[FN_R1] = (uint64_t)p->d_rope;  // D1's RoPE
         break;
@@ -424,6 +429,7 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
   for (int r = 0; r < c.n_requests; ++r) p->sh.smax = std::max(p->sh.smax, (int)host_context_lens[r]);
   p->sh.npages = c.num_phys_pages;
   p->sh.topk = c.topk;
+  p->sh.mla = c.mla_heads;
   HIP_TRY(hipMalloc(&p->d_queue, hp.queue.size() * 4));
   HIP_TRY(hipMemcpy(p->d_queue, hp.queue.data(), hp.queue.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipMalloc(&p->d_tasks, hp.tasks.size() * 4));

@@ -16,6 +16,7 @@ struct Shapes {
   int qr, nh, T, smax;     // indexer front: q rank, heads, tokens per request, score row stride
   int npages;              // physical pages of the cache pool: every block-table entry must be below it
   int topk;                // indexer front: positions each token row selects (0: no top-k)
+  int mla;                 // indexer front: heads of the main-MLA query half (0: none)
 };
 
 struct KArgs {

@@ -28,7 +28,10 @@ enum Opcode : uint32_t {
   OP_SCORE = 13,  // one (request, key split): paged indexer score
   OP_TOPK = 14    // one token row: the positions of its top-k scores
 };
-enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_QA = 4, K_W = 5, K_KI = 6, K_QI = 7 };
+enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_QA = 4, K_W = 5, K_KI = 6, K_QI = 7,
+                           K_QB = 8,    // main-MLA query (D0): e4m3, K = q rank, finalized per head
+                           K_UK = 9 };  // main-MLA query BMM (D2): bf16, K = 128 (one head), one chunk
+constexpr int kMlaNope = 128, kMlaLatent = 512;  // per main-MLA head: D0 output, D2 output
 constexpr int kScoreTok = 128;  // keys per indexer-score task
 constexpr int kM16Rows = 64;  // weight rows of a multi-row projection tile (gate/up: 32 + 32)
 constexpr int kMaxChunks = 24;  // K chunks a multi-row finalize task adds

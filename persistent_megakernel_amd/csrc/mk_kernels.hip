@@ -473,6 +473,8 @@ DEV uint32_t proj_k(const Shapes& sh, uint32_t kind) {
     case K_O: return (uint32_t)sh.Hq * 128u;
     case K_DOWN: return (uint32_t)sh.I;
     case K_QI: return (uint32_t)sh.qr;
+    case K_QB: return (uint32_t)sh.qr;
+    case K_UK: return (uint32_t)kMlaNope;
     default: return (uint32_t)sh.H;
   }
 }
@@ -504,8 +506,9 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
     // step q: 32 bf16 or 64 e4m3 weights), lane l taking row 16 nb + l % 16, bytes 16 (l / 16) ...
     const uint32_t kind = in.w[W_LAYER + 1], n0 = in.w[W_LAYER + 3], k0 = in.w[W_LAYER + 5], kc = in.w[W_LAYER + 6];
     const uint32_t K = proj_k(sh, kind);
-    const uint32_t el = sh.fp8 ? 1u : 2u;
-    pf.mode = sh.fp8 ? PF_W_FP8 : PF_W_BF16;
+    const bool f8 = sh.fp8 && kind != K_UK;  // the main-MLA query BMM has bf16 weights in an e4m3 plan
+    const uint32_t el = f8 ? 1u : 2u;
+    pf.mode = f8 ? PF_W_FP8 : PF_W_BF16;
     pf.rowb = K * el;
     pf.k0b = k0 * el;
     pf.base0 = n0;
@@ -1388,12 +1391,14 @@ DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, 
   const char* ring = smem + kRingOff;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const uint32_t kc = in.w[W_LAYER + 6];
-  if (!FP8) {  // K chunk 512: 16 steps of 32
+  if (!FP8) {  // K chunk of kc / 32 steps of 32 (512 for the Qwen3 layers, 128 for the main-MLA BMM)
+    const uint32_t nq = kc >> 6, bpn = kc >> 5;  // steps per half, steps per 16-row block
 #pragma unroll
     for (uint32_t i = 0; i < 8; ++i) {
-      const uint32_t q = kh * 8u + i;
+      if (i >= nq) break;
+      const uint32_t q = kh * nq + i;
       const bf16x8 av = *(const bf16x8*)(act + q * 1024u + ln * 16u);
-      const bf16x8 bv = *(const bf16x8*)(ring + ring_off(lease, (nb * 16u + q) * 1024u + ln * 16u));
+      const bf16x8 bv = *(const bf16x8*)(ring + ring_off(lease, (nb * bpn + q) * 1024u + ln * 16u));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
     }
   } else {
@@ -1429,10 +1434,26 @@ DEV void gemm_epilogue(const KArgs& a, const Instr& in, const char* smem) {
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const uint32_t kind = in.w[W_LAYER + 1], j = in.w[W_LAYER + 2], k0 = in.w[W_LAYER + 5];
   const uint32_t kc = in.w[W_LAYER + 6], nk = proj_k(a.sh, kind) / kc;
-  float* part = (float*)s_ld64(row + GM_PART) + ((size_t)j * nk + k0 / kc) * 1024;
-  __amdgpu_buffer_rsrc_t rp = rsrc(part);
   const char* D = smem + kActOff + kActD;
   const uint32_t ln = lane();
+  if (kind == K_UK) {  // the main-MLA query BMM is one chunk: its tile is final, bf16 q_lat [M][heads][512]
+    const uint32_t n0 = in.w[W_LAYER + 3], h = n0 / (uint32_t)kMlaLatent, c0 = n0 % (uint32_t)kMlaLatent;
+    __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + GM_PART));
+#pragma unroll
+    for (uint32_t nb = 0; nb < 4; ++nb) {
+      const f32x4 v = *(const f32x4*)(D + (nb * 64u + ln) * 16u) + *(const f32x4*)(D + ((nb + 4u) * 64u + ln) * 16u);
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t m = 4u * (ln >> 4) + q, c = c0 + nb * 16u + (ln & 15u);
+        if (m < (uint32_t)a.sh.M)
+          st16(ro, ((m * (uint32_t)a.sh.mla + h) * (uint32_t)kMlaLatent + c) * 2u, bf16_bits(e[q]));
+      }
+    }
+    return;
+  }
+  float* part = (float*)s_ld64(row + GM_PART) + ((size_t)j * nk + k0 / kc) * 1024;
+  __amdgpu_buffer_rsrc_t rp = rsrc(part);
 #pragma unroll
   for (uint32_t nb = 0; nb < 4; ++nb) {
     const f32x4 v = *(const f32x4*)(D + (nb * 64u + ln) * 16u) + *(const f32x4*)(D + ((nb + 4u) * 64u + ln) * 16u);
@@ -1775,6 +1796,47 @@ DEV void fin_qi(const KArgs& a, const Instr& in, int wv) {
 // The step's keys on the eight waves (rows m = wave and wave + 8): RoPE at the row's position (lane i:
 // the pair (i, i + 64)), per-token e4m3 with scale amax / 448, codes and scale into the key cache at
 // (block_table[r][pos / P], pos % P)
+// D0's finalize of one main-MLA head: its two 64-row tiles' K chunks added in order, times the
+// per-token scale of the normalised q_a, rounded to bf16 into D2's A-operand order (16 rows,
+// K = heads x 128); thread t takes columns t % 64 of both tiles for rows t / 64 and t / 64 + 8
+DEV void fin_qb(const KArgs& a, const Instr& in, int wv) {
+  const Shapes& sh = a.sh;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t h = in.w[W_LAYER + 2], nk = in.w[W_LAYER + 5];
+  const uint32_t t = (uint32_t)wv * 64u + lane(), i = t & 63u, M = (uint32_t)sh.M;
+  const uint32_t ms[2] = {t >> 6, (t >> 6) + 8u};
+  __amdgpu_buffer_rsrc_t rp = rsrc((const float*)s_ld64(row + FN_PART) + (size_t)2u * h * nk * 1024);
+  __amdgpu_buffer_rsrc_t rs = rsrc((const void*)s_ld64(row + FN_SA));
+  float x[2][2][4], sa[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t m = min(ms[q], M - 1u);
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t kk = min((uint32_t)k, nk - 1u);
+        x[q][tl][k] = __uint_as_float(ld32(rp, (((uint32_t)tl * nk + kk) * 1024u + part_idx(m, i)) * 4u));
+      }
+    sa[q] = __uint_as_float(ld32(rs, m * 4u));
+  }
+  wait_vm0();
+  __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + FN_OUT));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (ms[q] >= M) continue;
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+      float acc = x[q][tl][0];
+#pragma unroll
+      for (uint32_t k = 1; k < 4; ++k)
+        if (k < nk) acc += x[q][tl][k];
+      st16(ro, opnd_bf16(ms[q], h * (uint32_t)kMlaNope + (uint32_t)tl * 64u + i), bf16_bits(acc * sa[q]));
+    }
+  }
+  wait_vm0();
+}
+
 DEV void kcache(const KArgs& a, const Instr& in, int wv) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
@@ -2111,7 +2173,7 @@ template <bool LD>
 DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const uint32_t op = in.w[W_OPCODE];
   if (op == OP_GEMM) {
-    if (a.sh.fp8) gemm_tile<true>(a, in, smem, lease, wv);
+    if (a.sh.fp8 && in.w[W_LAYER + 1] != K_UK) gemm_tile<true>(a, in, smem, lease, wv);
     else gemm_tile<false>(a, in, smem, lease, wv);
   } else if (op == OP_NORM) {
     if (a.sh.fp8) norm_row<true>(a, in, smem, lease, wv);
@@ -2119,6 +2181,7 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
   } else if (op == OP_FIN) {
     const uint32_t nk = in.w[W_LAYER + 5];
     if (in.w[W_LAYER + 1] == K_QI) fin_qi(a, in, wv);
+    else if (in.w[W_LAYER + 1] == K_QB) fin_qb(a, in, wv);
     else if (nk <= 4) fin_tile<4>(a, in, wv);
     else if (nk <= 8) fin_tile<8>(a, in, wv);
     else if (nk <= 12) fin_tile<12>(a, in, wv);
@@ -2140,9 +2203,12 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
 // instruction staged the same chunk and nothing has written the area since)
 DEV void gemm_stage(const KArgs& a, const Instr& in, char* act, uint64_t& staged) {
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
-  const uint32_t k0 = in.w[W_LAYER + 5], kc = in.w[W_LAYER + 6];
-  const uint32_t off = a.sh.fp8 ? (k0 >> 6) * 1024u : (k0 >> 5) * 1024u;
-  const uint32_t bytes = a.sh.fp8 ? (kc >> 6) * 1024u : (kc >> 5) * 1024u;  // at most kActABytes
+  const uint32_t kind = in.w[W_LAYER + 1], kc = in.w[W_LAYER + 6];
+  // the main-MLA query BMM reads its head's 128 columns of the D0 output (payload word 7), in bf16
+  const uint32_t k0 = kind == K_UK ? in.w[W_LAYER + 7] : in.w[W_LAYER + 5];
+  const bool f8 = a.sh.fp8 && kind != K_UK;
+  const uint32_t off = f8 ? (k0 >> 6) * 1024u : (k0 >> 5) * 1024u;
+  const uint32_t bytes = f8 ? (kc >> 6) * 1024u : (kc >> 5) * 1024u;  // at most kActABytes
   const char* src = (const char*)s_ld64(row + GM_ACT) + off;
   if ((uint64_t)src == staged) return;
   stage(src, bytes, act + kActA);

@@ -317,6 +317,27 @@ void build_indexer(const mk_config& c, const int32_t* ctx, const TileParams& p, 
   for (int h = 0; h < nh; ++h)
     b.task(OP_FIN, row_d1f, spec, {{ev_head[h], (uint32_t)(per_head * nk_q)}}, {{ev_qi, 1u}},
            {l, K_QI, h, h * hd, hd, nk_q, kcq});
+  // main-MLA query half, dealt after D1 and before E1 as in the page's tile list: D0 tiles of the
+  // normalised q_a (as D1), a finalize per head, and D2's tiles of each head as soon as that head is
+  // finalized (one event per head: the page's per-head tile_cover of D0 -> D2)
+  if (c.mla_heads > 0) {
+    const int nm = c.mla_heads, per_head_qb = kMlaNope / rt;
+    std::vector<int> ev_qb(nm);
+    for (int h = 0; h < nm; ++h) ev_qb[h] = b.event((uint32_t)(per_head_qb * nk_q));
+    const int row_d0 = tiles(K_QB, nm * kMlaNope, qr, kcq, {ev_qn, (uint32_t)M}, row_qn,
+                             [&](int j) { return ev_qb[j / per_head_qb]; });
+    const int row_d0f = b.op_row(OP_FIN, l, {row_d0}, K_QB);
+    std::vector<int> ev_qn_h(nm);
+    for (int h = 0; h < nm; ++h) ev_qn_h[h] = b.event(1u);
+    for (int h = 0; h < nm; ++h)
+      b.task(OP_FIN, row_d0f, spec, {{ev_qb[h], (uint32_t)(per_head_qb * nk_q)}}, {{ev_qn_h[h], 1u}},
+             {l, K_QB, h, h * kMlaNope, kMlaNope, nk_q, kcq});
+    const int row_d2 = b.op_row(OP_GEMM, l, {row_d0f}, K_UK);
+    for (int h = 0; h < nm; ++h)
+      for (int j = 0; j < kMlaLatent / rt; ++j)
+        b.task(OP_GEMM, row_d2, spec, {{ev_qn_h[h], 1u}}, {},
+               {l, K_UK, h * (kMlaLatent / rt) + j, h * kMlaLatent + j * rt, rt, 0, kMlaNope, h * kMlaNope});
+  }
   // E1; with a top-k, one event per request counts its score tasks
   const int row_e = b.op_row(OP_SCORE, l, {row_d1f, row_c0f, row_kc});
   const int T = c.tokens_per_request;
@@ -418,8 +439,8 @@ mk_status plan_indexer(const mk_config& c, const int32_t* ctx, int W, HostPlan& 
       err = "context length out of range (at least the request's new tokens, at most its block table)";
       return MK_ERR_INVALID;
     }
-  if (c.topk < 0) {
-    err = "negative top-k";
+  if (c.topk < 0 || c.mla_heads < 0) {
+    err = "negative top-k or main-MLA head count";
     return MK_ERR_INVALID;
   }
   if (c.topk > 0)
@@ -454,6 +475,10 @@ mk_status plan_indexer(const mk_config& c, const int32_t* ctx, int W, HostPlan& 
   region("gp_w", (size_t)(nh / kM16Rows) * (H / kc) * 4096);
   region("gp_k", (size_t)(hd / kM16Rows) * (H / kc) * 4096);
   region("gp_qi", (size_t)(nh * hd / kM16Rows) * (qr / kcq) * 4096);
+  if (c.mla_heads > 0) {
+    region("gp_qb", (size_t)(c.mla_heads * kMlaNope / kM16Rows) * (qr / kcq) * 4096);
+    region("qn", (size_t)16 * c.mla_heads * kMlaNope * 2);  // D0 output, bf16 in D2's operand order
+  }
   out.workspace_bytes = off;
   return check_events(out, err);
 }
@@ -462,8 +487,8 @@ mk_status plan_indexer(const mk_config& c, const int32_t* ctx, int W, HostPlan& 
 
 mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& out, std::string& err) {
   if (c.workload == MK_INDEXER_FRONT) return plan_indexer(c, ctx, W, out, err);
-  if (c.topk != 0) {
-    err = "top-k belongs to the indexer front";
+  if (c.topk != 0 || c.mla_heads != 0) {
+    err = "top-k and the main-MLA half belong to the indexer front";
     return MK_ERR_INVALID;
   }
   if (c.workload != MK_QWEN3_LAYER && c.workload != MK_QWEN3_STEP) {

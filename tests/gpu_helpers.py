@@ -88,6 +88,8 @@ class IndexerRun:
         t["workspace"] = torch.zeros(self.plan.workspace_bytes() + 256, dtype=torch.uint8, device="cuda")
         if getattr(cfg, "topk", 0):
             t["topk_out"] = torch.full((cfg.m * cfg.topk,), -7, dtype=torch.int32, device="cuda")
+        if getattr(cfg, "mla_heads", 0):
+            t["qlat_out"] = torch.full((cfg.m * cfg.mla_heads * 512,), -1, dtype=torch.int16, device="cuda")
         self.t = t
         self.tensors = mk.indexer_pointers(t)
 

@@ -165,6 +165,28 @@ def _check_topk(run, ind, tag):
     _say(f"  {tag}: top-{k} valid on the kernel's scores; {window} keys of {M} rows within the oracle's threshold window")
 
 
+def _check_mla(run, ref, ind, tag):
+    """The main-MLA half: D0's q_nope (bf16, D2's operand order in the workspace) and D2's q_lat
+    (bf16 output) against the oracle before their roundings, with the FP8 tolerance; q_lat against
+    the independent oracle too."""
+    from gpu_helpers import bf16_excess, bf16_to_f64
+    cfg = run.cfg
+    M, nm = cfg.m, cfg.mla_heads
+    qn_buf = _ws(run, "qn").view(np.uint16)[:16 * nm * 128]
+    k = np.arange(nm * 128)
+    rows = []
+    for m in range(M):  # operand order: step k // 32 of 1 KiB, lane m + 16 ((k % 32) // 8), element k % 8
+        idx = (k // 32) * 512 + (m + 16 * ((k % 32) // 8)) * 8 + k % 8
+        rows.append(qn_buf[idx])
+    qn = (np.array(rows).astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(M, nm, 128)
+    assert bf16_excess(qn, ref["qn_pre"], TOL) <= 0, f"{tag}: q_nope"
+    ql = bf16_to_f64(run.t["qlat_out"]).reshape(M, nm, 512)
+    assert bf16_excess(ql, ref["qlat_pre"], TOL) <= 0, f"{tag}: q_lat against the resolved oracle"
+    err = float(np.max(np.abs(ql - ind["qlat_pre"])))
+    _say(f"  {tag}: q_lat err {err:.3e} against the independent oracle (max |q_lat| {np.max(np.abs(ind['qlat_pre'])):.3g})")
+    assert bf16_excess(ql, ind["qlat_pre"], TOL) <= 0, f"{tag}: q_lat against the independent oracle"
+
+
 def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True), ("mk", False)),
           W=0, intermediates=True):
     from gpu_helpers import IndexerRun
@@ -187,10 +209,15 @@ def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True
             _check_topk(run, ind, f"{mode}/{ms}")
             outs_k.append(run.t["topk_out"].clone())
             run.t["topk_out"].fill_(-7)
+        if cfg.mla_heads:
+            _check_mla(run, ref, ind, f"{mode}/{ms}")
+            outs_k.append(run.t["qlat_out"].clone())
+            run.t["qlat_out"].fill_(-1)
     for o in outs[1:]:
         assert torch.equal(torch.nan_to_num(o), torch.nan_to_num(outs[0]))
-    for o in outs_k[1:]:
-        assert torch.equal(o, outs_k[0])
+    nk = len(outs_k) // len(modes)  # per mode: [top-k], [q_lat]
+    for i in range(nk, len(outs_k)):
+        assert torch.equal(outs_k[i], outs_k[i % nk])
 
 
 @pytest.mark.parametrize("R,T,ctx,W", [(2, 8, [300, 133], 0), (3, 5, [64, 196, 5], 37)])
@@ -218,3 +245,19 @@ def test_indexer_topk_reduced(R, T, ctx, W, k):
 def test_indexer_topk_full_size():
     cfg = get_config("indexer_front_topk")  # Top-2048 of 8192 keys per token, 16 tokens
     _case(cfg, [cfg.context] * cfg.n_requests, seed=0, modes=(("mk", False), ("graph", False)), intermediates=False)
+
+
+@pytest.mark.parametrize("R,T,ctx,W,nm", [(2, 8, [300, 133], 0, 3), (3, 5, [64, 196, 5], 37, 2)])
+def test_attention_pre_reduced(R, T, ctx, W, nm):
+    """The indexer front with the main-MLA query half (D0 -> D2): all of the indexer's checks, plus
+    q_nope and q_lat."""
+    cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, n_requests=R,
+                              tokens_per_request=T, context=max(ctx), mla_heads=nm)
+    _case(cfg, ctx, seed=13, W=W)
+
+
+@pytest.mark.timeout(600)
+def test_attention_pre_full_size():
+    cfg = get_config("attention_pre")  # 64 main-MLA heads: D0 over q rank 1536, D2 into a 512 latent
+    _case(cfg, [cfg.context] * cfg.n_requests, seed=0, modes=(("mk", False), ("graph", False), ("graph", True)),
+          intermediates=False)

@@ -184,12 +184,19 @@ def _torch_indexer(cfg, inp):
         t = torch.arange(int(pos[m]) + 1)
         K = keys[bt[req[m], t // P], t % P]  # [t, hd]
         score[m, :len(t)] = (w[m][:, None] * torch.relu(qi[m] @ K.T)).sum(0)
-    return {"hq": hq, "qaq": qaq, "kq": kq, "score_pre": score.numpy()}
+    out = {"hq": hq, "qaq": qaq, "kq": kq, "score_pre": score.numpy()}
+    if cfg.mla_heads:  # D0 Main-Q per head from the normalised q_a, then D2's per-head BMM into the latent
+        nm = cfg.mla_heads
+        qn = torch.from_numpy(nu.round_bf16((qa @ _t_weight(inp, "w_qb").T).view(M, nm, 128).numpy()))
+        w_uk = torch.from_numpy(nu.bf16_bits_to_f64(inp["w_uk"])).view(nm, 512, 128)
+        out["qlat_pre"] = torch.bmm(qn.transpose(0, 1), w_uk.transpose(1, 2).contiguous()).transpose(0, 1).numpy()
+        out["qn"] = qn.numpy()
+    return out
 
 
 def test_indexer_front_matches_torch_formulation():
     cfg = dataclasses.replace(get_config("indexer_front"), hidden=512, idx_q_rank=256, idx_heads=4,
-                              idx_head_dim=64, context=200, page_size=64)
+                              idx_head_dim=64, context=200, page_size=64, mla_heads=3)
     for seed, ctx in ((5, [200, 200]), (6, [9, 131])):  # 9 keys: a request of new keys and one older
         inp = make_inputs(cfg, seed=seed)
         inp["context_lens"] = np.array(ctx, dtype=np.int32)
@@ -201,6 +208,9 @@ def test_indexer_front_matches_torch_formulation():
         assert np.array_equal(fin, np.isfinite(o["score_pre"]))
         ref = t["score_pre"][fin]
         assert np.max(np.abs(o["score_pre"][fin] - ref)) < 1e-9 * max(1.0, np.max(np.abs(ref)))
+        # the main-MLA half: D0's bf16 q_nope bit for bit, D2's latent to rounding
+        assert np.array_equal(o["qn"], t["qn"]), seed
+        assert np.max(np.abs(o["qlat_pre"] - t["qlat_pre"])) < 1e-9 * max(1.0, np.max(np.abs(t["qlat_pre"])))
 
 
 def test_step_chains_layers():

@@ -10,7 +10,8 @@ from workloads import get_config
 
 
 @pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
-                                  "indexer_front", "indexer_front_topk"])
+                                  "indexer_front", "indexer_front_topk",
+                                  "attention_pre"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_invariants(name, W):
     cfg = get_config(name)

@@ -17,7 +17,8 @@ def _both(cfg, W, ctx=None):
 
 
 @pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
-                                  "indexer_front", "indexer_front_topk"])
+                                  "indexer_front", "indexer_front_topk",
+                                  "attention_pre"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_queue_bit_exact(name, W):
     cfg = get_config(name)
@@ -51,10 +52,10 @@ def test_small_shapes_bit_exact():
         plan.close()
 
 
-@pytest.mark.parametrize("topk", [0, 64])
-def test_indexer_ragged_bit_exact(topk):
+@pytest.mark.parametrize("topk,mla", [(0, 0), (64, 0), (0, 3), (64, 2)])
+def test_indexer_ragged_bit_exact(topk, mla):
     cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, idx_heads=64,
-                              n_requests=2, tokens_per_request=3, context=300, topk=topk)
+                              n_requests=2, tokens_per_request=3, context=300, topk=topk, mla_heads=mla)
     for ctx in ([300, 3], [129, 256]):
         for W in (5, 64, 256):
             plan, ref = _both(cfg, W, ctx)
@@ -139,3 +140,46 @@ def test_topk_plan_shape_and_limits():
         mk.Plan(dataclasses.replace(with_k, context=8200), num_workers=256)
     with pytest.raises(mk.MkError, match="indexer front"):
         mk.Plan(dataclasses.replace(get_config("qwen3_0p6b_layer"), topk=4), num_workers=256)
+
+
+def test_main_mla_half_plan():
+    """D0: 2 tiles of 64 rows per head x the q-rank K chunks, a finalize per head waiting for all
+    of them; D2: 8 tiles of 64 latent rows per head, each waiting only for its own head's finalize
+    (one event of threshold 1 per head), reading that head's 128 columns.  The half is one run of
+    tasks between D1's finalizes and E1; without it the plan is the indexer front's, task for task,
+    up to a renumbering of ids, operand rows and events that keeps which tasks share an event."""
+    base, cfg = get_config("indexer_front"), get_config("attention_pre")
+    a, b = oq.build_queue(base, 256), oq.build_queue(cfg, 256)
+    ta, tb = oq_tasks(a), oq_tasks(b)
+    mla = ((tb[:, 0] == oq.OP_GEMM) | (tb[:, 0] == oq.OP_FIN)) & np.isin(tb[:, 21], [oq.K_QB, oq.K_UK])
+    at = np.flatnonzero(mla)
+    assert np.array_equal(at, np.arange(at[0], at[0] + len(at)))
+    assert tb[at[0] - 1, 0] == oq.OP_FIN and tb[at[-1] + 1, 0] == oq.OP_SCORE
+    extra, rest = tb[mla], tb[~mla]
+    assert rest.shape == ta.shape
+    same = [0, 1, 2, 4, 7, 9, 11, 13, 15, 18] + list(range(20, 32))
+    assert np.array_equal(rest[:, same], ta[:, same])
+    emap = {}
+    for x, y in zip(ta, rest):
+        for k in range(int(x[1])):
+            assert emap.setdefault(int(x[6 + 2 * k]), int(y[6 + 2 * k])) == int(y[6 + 2 * k])
+        for k in range(int(x[2])):
+            assert emap.setdefault(int(x[14 + 3 * k]), int(y[14 + 3 * k])) == int(y[14 + 3 * k])
+    assert len(set(emap.values())) == len(emap)
+    nk = cfg.idx_q_rank // b["params"]["kc_q"]
+    d0 = extra[(extra[:, 0] == oq.OP_GEMM) & (extra[:, 21] == oq.K_QB)]
+    fin = extra[extra[:, 0] == oq.OP_FIN]
+    d2 = extra[(extra[:, 0] == oq.OP_GEMM) & (extra[:, 21] == oq.K_UK)]
+    assert len(d0) == 64 * 2 * nk and len(fin) == 64 and len(d2) == 64 * 8
+    thr = b["thresholds"]
+    for h in range(64):
+        f = fin[fin[:, 22] == h][0]
+        assert thr[f[6]] == 2 * nk and f[2] == 1 and thr[f[14]] == 1
+        heads = d2[(d2[:, 23] // 512) == h]
+        assert len(heads) == 8 and all(t[6] == f[14] and t[7] == 1 and t[27] == 128 * h for t in heads)
+
+
+def oq_tasks(plan):
+    t = plan["queue"].reshape(-1, 32)
+    t = t[t[:, 0] != 0]
+    return t[np.argsort(t[:, 5])]

@@ -53,6 +53,7 @@ class Config:
     rope_theta: float = 1e6
     residual_zero: bool = False  # r_in == 0 (full decode step)
     topk: int = 0  # indexer front: positions each token selects after the score (0: no top-k)
+    mla_heads: int = 0  # indexer front: heads of the main-MLA query half D0 -> D2 (0: none)
 
     @property
     def m(self) -> int:
@@ -95,6 +96,13 @@ CONFIGS: Dict[str, Config] = {
                                  tokens_per_request=8, context=8192, page_size=64, random_pages=True,
                                  weight_fp8=True, act_fp8=True, idx_q_rank=1536, idx_heads=64,
                                  idx_head_dim=128, topk=2048),
+    # The page's whole attention-pre graph: the indexer front plus the main-MLA query half,
+    # D0 Main-Q (64 heads x 128 no-RoPE dims from the normalised q_a) -> D2 Q-BMM (per head, into
+    # a 512-wide latent).
+    "attention_pre": Config("attention_pre", "indexer_front", hidden=6144, n_requests=2,
+                            tokens_per_request=8, context=8192, page_size=64, random_pages=True,
+                            weight_fp8=True, act_fp8=True, idx_q_rank=1536, idx_heads=64,
+                            idx_head_dim=128, mla_heads=64),
 }
 
 
@@ -187,6 +195,8 @@ def make_inputs(cfg: Config, seed: int = 0, layers: Optional[int] = None) -> Dic
       w_qa [1536, H], w_w [64, H], w_k [128, H], w_qi [64*128, 1536]: e4m3 codes + block scales
       g_norm [H], g_qa [1536] bf16 bits; x [16, H] bf16 bits; r_in [16, H] f32
       key_cache [pages, 64, 128] e4m3 codes, key_scale [pages, 64] f32; block_table, context_lens
+      main-MLA half (mla_heads = nm > 0), drawn last: w_qb [nm 128, 1536] e4m3 codes + s_qb,
+      w_uk [nm 512, 128] bf16 bits ~ N(0, 0.05)
     """
     rng = np.random.default_rng(seed)
     out: Dict[str, np.ndarray] = {}
@@ -235,6 +245,11 @@ def make_inputs(cfg: Config, seed: int = 0, layers: Optional[int] = None) -> Dic
         out["key_scale"] = (rng.uniform(0.8, 1.25, (cfg.num_phys_pages, cfg.page_size)) * _FP8_K_SCALE).astype(np.float32)
         out["x"] = _bf16_normal(rng, (cfg.m, H), 1.0)
         out["r_in"] = rng.standard_normal((cfg.m, H), dtype=np.float32)
+        if cfg.mla_heads:  # drawn last: the indexer's inputs are the same with or without this half
+            n = cfg.mla_heads * 128
+            out["w_qb"] = _fp8_codes(rng, (n, qr), _FP8_W_SIGMA)
+            out["s_qb"] = (rng.uniform(0.8, 1.25, (-(-n // 128), -(-qr // 128))) * _FP8_W_SCALE).astype(np.float32)
+            out["w_uk"] = _bf16_normal(rng, (cfg.mla_heads * 512, 128), 0.05)
     else:
         raise ValueError(cfg.workload)
     return out
@@ -278,5 +293,9 @@ def algorithmic_bytes(cfg) -> Dict[str, int]:
         parts["score_out"] = M * cfg.context * 4
         if cfg.topk:
             parts["topk_out"] = M * cfg.topk * 4  # the scores it reads are this workload's own output
+        if cfg.mla_heads:
+            n = cfg.mla_heads * 128
+            parts["mla_weights"] = n * qr + (-(-n // 128)) * (-(-qr // 128)) * 4 + cfg.mla_heads * 512 * 128 * 2
+            parts["qlat_out"] = M * cfg.mla_heads * 512 * 2
     parts["total"] = sum(parts.values())
     return parts
