@@ -63,7 +63,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_0p6b_step",
-                    choices=["qwen3_0p6b_step", "qwen3_0p6b_layer", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
+                    choices=["qwen3_0p6b_step", "qwen3_0p6b_layer", "qwen3_8b_layer", "qwen3_8b_layer_fp8", "qwen3_8b_layer_m64",
                              "indexer_front", "indexer_front_topk", "attention_pre"])
     ap.add_argument("--rotate", type=int, default=0, help="copies of weights/caches cycled per run (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -206,20 +206,23 @@ def _qwen3(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
 
 
 def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
-    """Multi-row (M = R x T rows, M <= 16) layer: row-task norms, projections as
-    (output-row tile, K chunk) tasks writing partial sums, one finalize task per row tile that
-    adds the chunks in K order and applies the epilogue; FP8 plans quantise o and m per row.
+    """Multi-row (M = R x T rows, M <= 256) layer: row-task norms, projections as
+    (output-row tile, K chunk) tasks writing partial sums for every 16-row group of M (one read
+    of the weights), one finalize task per (row tile, row group) that adds the chunks in K order
+    and applies the epilogue; FP8 plans quantise o and m per row.
 
-    Waits (all "whole" unless stated): NORM_A on the previous layer's down finalizes; QKV tiles
-    on NORM_A; QKV finalize on its tile's chunks ("tile_reduce"); attention on the QKV finalizes of
-    its kv group ("tile_cover"); a combine on its group's chain partials ("tile_reduce"); [QUANT_O on every
-    combine]; O tiles on the combines [or QUANT_O];
-    NORM_B on the O finalizes; gate/up tiles on NORM_B; [QUANT_M on the gate/up finalizes]; down
-    tiles on the gate/up finalizes [or QUANT_M]."""
+    Waits (all "whole" unless stated): NORM_A of a row on the previous layer's down finalizes of
+    its row group; QKV tiles on NORM_A; QKV finalize on its tile's chunks ("tile_reduce");
+    attention on the QKV finalizes of its kv group and row group ("tile_cover"); a combine on its
+    group's chain partials ("tile_reduce"); [QUANT_O on every combine]; O tiles on the combines
+    [or QUANT_O]; NORM_B of a row on its row group's O finalizes; gate/up tiles on NORM_B;
+    [QUANT_M of a row on its row group's gate/up finalizes]; down tiles on the gate/up finalizes
+    [or QUANT_M]."""
     H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
     Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
     g = Hq // Hkv
-    R, M = cfg.n_requests, cfg.m
+    R, M, T = cfg.n_requests, cfg.m, cfg.tokens_per_request
+    G = -(-M // 16)  # 16-row groups
     spec, kc, st = p["spec"], p["kc"], p["s_tok"]
     n_qkv = (Hq + 2 * Hkv) * d
     fp8 = bool(cfg.act_fp8)
@@ -233,17 +236,20 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
             for c in range(nk):
                 b.task(OP_GEMM, row_g, spec, [wait], [(parts[j], 1)], [l, kind, j, j * rows, rows, c * kc, kc])
         for j in range(nt):
-            b.task(OP_FIN, row_f, spec, [(parts[j], nk)], [fin_signal(j)], [l, kind, j, j * rows, rows, nk, kc])
+            for gi in range(G):
+                b.task(OP_FIN, row_f, spec, [(parts[j], nk)], [fin_signal(j, gi)],
+                       [l, kind, j, j * rows, rows, nk, kc, 0, 0, gi])  # the group in word 29
 
-    prev = None
+    prev = None  # per row group: the previous layer's down finalizes
     for l in range(cfg.num_layers):
         row_na = b.op_row()
         ev_na = b.event(M)
         for m in range(M):
-            b.task(OP_NORM, row_na, spec, [] if prev is None else [prev], [(ev_na, 1)], [l, 0, m])
-        # QKV: a 64-row tile lies inside one head; its finalize counts for the head's kv group
+            b.task(OP_NORM, row_na, spec, [] if prev is None else [prev[m // 16]], [(ev_na, 1)], [l, 0, m])
+        # QKV: a 64-row tile lies inside one head; its finalize of a row group counts for the
+        # head's kv group and that row group
         tiles_per_group = (g + 2) * d // rt
-        ev_qkv = [b.event(tiles_per_group) for _ in range(Hkv)]
+        ev_qkv = [b.event(tiles_per_group) for _ in range(Hkv * G)]
 
         def qkv_group(j):
             n0 = j * rt
@@ -253,7 +259,7 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
                 return (n0 - Hq * d) // d
             return (n0 - (Hq + Hkv) * d) // d
 
-        proj(K_QKV, l, n_qkv, H, rt, (ev_na, M), lambda j: (ev_qkv[qkv_group(j)], 1))
+        proj(K_QKV, l, n_qkv, H, rt, (ev_na, M), lambda j, gi: (ev_qkv[qkv_group(j) * G + gi], 1))
         # split-KV attention: the (request, kv head, split) tasks are laid out so that dealing them
         # round-robin hands each worker a run of consecutive splits of one (request, kv head) -- a
         # chain, which the worker folds into one running softmax state and writes as one partial.
@@ -290,7 +296,7 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
                 r, hk, s = seq[i]
                 flags, slot = chain[i]
                 t0, t1 = s * st, min(int(ctx_lens[r]), (s + 1) * st)
-                b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk], tiles_per_group)],
+                b.task(OP_ATTN, row_attn, spec, [(ev_qkv[hk * G + r * T // 16], tiles_per_group)],
                        [(ev_att[r * Hkv + hk], 1)] if flags & 2 else [],
                        [l, r, hk, s, t0, t1, 0, 0, 0, nsplit[r], flags, slot])
         row_comb = b.op_row()
@@ -306,25 +312,27 @@ def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
             for m in range(M):
                 b.task(OP_QUANT, row_qo, spec, [o_wait], [(ev_oq, 1)], [l, 0, m])
             o_wait = (ev_oq, M)
-        ev_o = b.event(H // rt)
-        proj(K_O, l, H, Hq * d, rt, o_wait, lambda j: (ev_o, 1))
+        ev_o = [b.event(H // rt) for _ in range(G)]
+        proj(K_O, l, H, Hq * d, rt, o_wait, lambda j, gi: (ev_o[gi], 1))
         row_nb = b.op_row()
         ev_nb = b.event(M)
         for m in range(M):
-            b.task(OP_NORM, row_nb, spec, [(ev_o, H // rt)], [(ev_nb, 1)], [l, 1, m])
-        # gate/up: a tile holds rt/2 gate rows and the matching rt/2 up rows
-        ev_gu = b.event(I // (rt // 2))
-        proj(K_GU, l, I, H, rt // 2, (ev_nb, M), lambda j: (ev_gu, 1))
-        m_wait = (ev_gu, I // (rt // 2))
+            b.task(OP_NORM, row_nb, spec, [(ev_o[m // 16], H // rt)], [(ev_nb, 1)], [l, 1, m])
+        # gate/up: a tile holds rt/2 gate rows and the matching rt/2 up rows.  W8A8: the per-row
+        # quantisation waits for its row group's finalizes; bf16: the down tiles read every group
+        n_gu = I // (rt // 2)
+        ev_gu = [b.event(n_gu) for _ in range(G)] if fp8 else [b.event(n_gu * G)]
+        proj(K_GU, l, I, H, rt // 2, (ev_nb, M), lambda j, gi: (ev_gu[gi if fp8 else 0], 1))
+        m_wait = (ev_gu[0], n_gu * G)
         if fp8:
             row_qm = b.op_row()
             ev_mq = b.event(M)
             for m in range(M):
-                b.task(OP_QUANT, row_qm, spec, [m_wait], [(ev_mq, 1)], [l, 1, m])
+                b.task(OP_QUANT, row_qm, spec, [(ev_gu[m // 16], n_gu)], [(ev_mq, 1)], [l, 1, m])
             m_wait = (ev_mq, M)
-        ev_down = b.event(H // rt)
-        proj(K_DOWN, l, H, I, rt, m_wait, lambda j: (ev_down, 1))
-        prev = (ev_down, H // rt)
+        ev_down = [b.event(H // rt) for _ in range(G)]
+        proj(K_DOWN, l, H, I, rt, m_wait, lambda j, gi: (ev_down[gi], 1))
+        prev = [(e, H // rt) for e in ev_down]
 
 
 def _indexer(cfg, W: int, ctx_lens, b: _Builder, p) -> None:

@@ -430,6 +430,7 @@ mk_status mk_build_queue(const mk_config* cfg, const int32_t* host_context_lens,
   p->sh.npages = c.num_phys_pages;
   p->sh.topk = c.topk;
   p->sh.mla = c.mla_heads;
+  p->sh.rg = (p->sh.M + 15) / 16;
   HIP_TRY(hipMalloc(&p->d_queue, hp.queue.size() * 4));
   HIP_TRY(hipMemcpy(p->d_queue, hp.queue.data(), hp.queue.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipMalloc(&p->d_tasks, hp.tasks.size() * 4));

@@ -17,6 +17,7 @@ struct Shapes {
   int npages;              // physical pages of the cache pool: every block-table entry must be below it
   int topk;                // indexer front: positions each token row selects (0: no top-k)
   int mla;                 // indexer front: heads of the main-MLA query half (0: none)
+  int rg;                  // multi-row plans: 16-row groups of M (operand order, partial sums, finalizes)
 };
 
 struct KArgs {

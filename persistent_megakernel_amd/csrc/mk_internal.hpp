@@ -33,6 +33,7 @@ enum ProjKind : uint32_t { K_QKV = 0, K_O = 1, K_GU = 2, K_DOWN = 3, K_QA = 4, K
                            K_UK = 9 };  // main-MLA query BMM (D2): bf16, K = 128 (one head), one chunk
 constexpr int kMlaNope = 128, kMlaLatent = 512;  // per main-MLA head: D0 output, D2 output
 constexpr int kScoreTok = 128;  // keys per indexer-score task
+constexpr int kMaxRows = 256;  // multi-row plans: at most 16 groups of 16 rows
 constexpr int kM16Rows = 64;  // weight rows of a multi-row projection tile (gate/up: 32 + 32)
 constexpr int kMaxChunks = 24;  // K chunks a multi-row finalize task adds
 
@@ -55,6 +56,7 @@ enum Word : int {
   W_ARR_N = 27,   // arrival group size (0: no arrival group)
   W_ARR_RANK = 28, // rank of this task in its group
   W_NSPLIT = 29,  // multi-row attention: splits of the (request, kv head)
+  W_GROUP = 29,   // multi-row finalize: the 16-row group of M it finalizes
   W_CHAIN = 30,   // multi-row attention: bit 0 continues the worker's previous task's chain, bit 1 ends it
   W_PSLOT = 31    // multi-row attention: the chain's partial slot in its (request, kv head)
 };

@@ -1349,13 +1349,14 @@ DEV bool wait_events(const KArgs& a, const Instr& in, uint32_t& polls, WaitCache
   return true;
 }
 
-// byte offset of element (m, k) of a 16-row operand-order matrix: 1 KiB per K step (32 bf16 or 64
-// e4m3), lane l = m + 16 g holding the step's 16-byte group g of row m
-DEV uint32_t opnd_bf16(uint32_t m, uint32_t k) {
-  return (k >> 5) * 1024u + (m + 16u * ((k & 31u) >> 3)) * 16u + (k & 7u) * 2u;
+// byte offset of element (m, k) of an operand-order matrix with K columns: rows in groups of 16,
+// one group after the other; inside a group 1 KiB per K step (32 bf16 or 64 e4m3), lane
+// l = (m mod 16) + 16 g holding the step's 16-byte group g of row m
+DEV uint32_t opnd_bf16(uint32_t m, uint32_t k, uint32_t K) {
+  return (m >> 4) * K * 32u + (k >> 5) * 1024u + ((m & 15u) + 16u * ((k & 31u) >> 3)) * 16u + (k & 7u) * 2u;
 }
-DEV uint32_t opnd_fp8(uint32_t m, uint32_t k) {
-  return (k >> 6) * 1024u + (m + 16u * ((k & 63u) >> 4)) * 16u + (k & 15u);
+DEV uint32_t opnd_fp8(uint32_t m, uint32_t k, uint32_t K) {
+  return (m >> 4) * K * 16u + (k >> 6) * 1024u + ((m & 15u) + 16u * ((k & 63u) >> 4)) * 16u + (k & 15u);
 }
 // eight e4m3 codes (bytes of w0, w1) as bf16: every e4m3 value is a bf16 value, so this is exact
 DEV bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
@@ -1427,9 +1428,67 @@ DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, 
   *(f32x4*)(smem + kActOff + kActD + ((uint32_t)wv * 64u + ln) * 16u) = acc;
 }
 
+// Plans of more than 16 rows: the same tile for every 16-row group of M, the weights read once from
+// the lease.  Wave w takes row block nb = w & 3 and the row groups w >> 2, w >> 2 + 2, ...; it reads
+// each group's input chunk straight from the workspace (operand order, device-scope loads: the
+// chunk would not fit the activation area for all groups), sums the whole K chunk and stores the
+// group's 16 x 16 partial sums itself, [tile][chunk][group][row block][lane][4].
+template <bool FP8>
+DEV void gemm_tile_groups(const KArgs& a, const Instr& in, const char* smem, uint32_t lease, int wv) {
+  const uint32_t ln = lane(), nb = (uint32_t)wv & 3u;
+  const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+  const uint32_t kind = in.w[W_LAYER + 1], j = in.w[W_LAYER + 2], n0 = in.w[W_LAYER + 3], k0 = in.w[W_LAYER + 5];
+  const uint32_t kc = in.w[W_LAYER + 6], K = proj_k(a.sh, kind), G = (uint32_t)a.sh.rg;
+  const uint32_t nst = FP8 ? kc >> 6 : kc >> 5;  // 1 KiB steps of the chunk: 16 (512 bf16, 1024 e4m3) or 12
+  const uint32_t gstride = FP8 ? K * 16u : K * 32u;
+  const char* ring = smem + kRingOff;
+  __amdgpu_buffer_rsrc_t ra = rsrc((const char*)s_ld64(row + GM_ACT) + (FP8 ? k0 >> 6 : k0 >> 5) * 1024u);
+  __amdgpu_buffer_rsrc_t rp = rsrc((float*)s_ld64(row + GM_PART) + ((size_t)j * (K / kc) + k0 / kc) * G * 1024);
+  const float* sw = nullptr;
+  if (FP8) {
+    const uint32_t tr0 = nb * 16u;
+    const uint32_t grow = kind == K_GU && tr0 >= 32u ? (uint32_t)a.sh.I + n0 + tr0 - 32u : n0 + tr0;
+    sw = (const float*)s_ld64(row + GM_SW) + (size_t)(grow >> 7) * (K >> 7) + (k0 >> 7);
+  }
+  for (uint32_t gi = (uint32_t)wv >> 2; gi < G; gi += 2u) {
+    u32x4 av[16];
+#pragma unroll
+    for (uint32_t q = 0; q < 16; ++q) av[q] = ld128(ra, gi * gstride + min(q, nst - 1u) * 1024u + ln * 16u);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!FP8) {
+#pragma unroll
+      for (uint32_t q = 0; q < 16; ++q) {  // guarded, not cut short: av stays in registers
+        if (q < nst) {
+          const bf16x8 bv = *(const bf16x8*)(ring + ring_off(lease, (nb * nst + q) * 1024u + ln * 16u));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8)av[q], bv, acc, 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (uint32_t kb = 0; kb < 8; ++kb) {  // 128-wide scale blocks, two 64-k steps each
+        if (2u * kb < nst) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t q = 2u * kb + h;
+            const u32x4 bv = *(const u32x4*)(ring + ring_off(lease, (nb * nst + q) * 1024u + ln * 16u));
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av[q].x, av[q].y), e4m3x8_bf16(bv.x, bv.y), t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av[q].z, av[q].w), e4m3x8_bf16(bv.z, bv.w), t, 0, 0, 0);
+          }
+          acc += c_ld<float>(sw + kb) * t;
+        }
+      }
+    }
+    st128(rp, gi * 4096u + (nb * 64u + ln) * 16u,
+          u32x4{__float_as_uint(acc.x), __float_as_uint(acc.y), __float_as_uint(acc.z), __float_as_uint(acc.w)});
+  }
+  wait_vm0();  // the signals follow barrier B
+}
+
 // controller: add the two K halves of each row block and store the tile's partial sums
 // [chunk][row block][lane][4] (element (m, c) of the 16 x 64 tile at lane c % 16 + 16 (m / 4) of
 // block c / 16, position m % 4), then signal
+template <bool RG>
 DEV void gemm_epilogue(const KArgs& a, const Instr& in, const char* smem) {
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const uint32_t kind = in.w[W_LAYER + 1], j = in.w[W_LAYER + 2], k0 = in.w[W_LAYER + 5];
@@ -1452,6 +1511,7 @@ DEV void gemm_epilogue(const KArgs& a, const Instr& in, const char* smem) {
     }
     return;
   }
+  if (RG) return;  // the waves stored every group's partial sums
   float* part = (float*)s_ld64(row + GM_PART) + ((size_t)j * nk + k0 / kc) * 1024;
   __amdgpu_buffer_rsrc_t rp = rsrc(part);
 #pragma unroll
@@ -1470,23 +1530,25 @@ DEV uint32_t part_idx(uint32_t m, uint32_t c) { return ((c >> 4) * 64u + (c & 15
 //   QKV: fp32 q | k | v as tagged records (the attention staging reads records)
 //   O: r2 = r1 + bf16(a)                    GATE_UP: m = silu(g) u (bf16 operand order, or fp32 rows)
 //   DOWN: y = bf16(.)                        W8A8: sums times the token's input scale first
-template <int NK>
+template <int NK, bool RG>
 DEV void fin_tile(const KArgs& a, const Instr& in, int wv) {
   const Shapes& sh = a.sh;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const uint32_t kind = in.w[W_LAYER + 1], j = in.w[W_LAYER + 2], n0 = in.w[W_LAYER + 3], nk = in.w[W_LAYER + 5];
+  const uint32_t gi = RG ? in.w[W_GROUP] : 0u, G = RG ? (uint32_t)sh.rg : 1u;  // the 16-row group it finalizes
   const uint32_t t = (uint32_t)wv * 64u + lane();
   const bool gu = kind == K_GU;
-  const uint32_t m0 = gu ? t >> 5 : t >> 6, c = gu ? t & 31u : t & 63u;
-  const uint32_t m1 = gu ? m0 : m0 + 8u, c1 = gu ? c + 32u : c;
-  __amdgpu_buffer_rsrc_t rp = rsrc((const float*)s_ld64(row + FN_PART) + (size_t)j * nk * 1024);
-  const uint32_t i0 = part_idx(m0, c), i1 = part_idx(m1, c1);
+  const uint32_t l0 = gu ? t >> 5 : t >> 6, c = gu ? t & 31u : t & 63u;
+  const uint32_t l1 = gu ? l0 : l0 + 8u, c1 = gu ? c + 32u : c;
+  const uint32_t m0 = 16u * gi + l0, m1 = 16u * gi + l1;
+  __amdgpu_buffer_rsrc_t rp = rsrc((const float*)s_ld64(row + FN_PART) + ((size_t)j * nk * G + gi) * 1024);
+  const uint32_t i0 = part_idx(l0, c), i1 = part_idx(l1, c1);
   float v0[NK], v1[NK];
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
     const uint32_t kk = min((uint32_t)k, nk - 1u);
-    v0[k] = __uint_as_float(ld32(rp, (kk * 1024u + i0) * 4u));
-    v1[k] = __uint_as_float(ld32(rp, (kk * 1024u + i1) * 4u));
+    v0[k] = __uint_as_float(ld32(rp, (kk * G * 1024u + i0) * 4u));
+    v1[k] = __uint_as_float(ld32(rp, (kk * G * 1024u + i1) * 4u));
   }
   const uint64_t out = s_ld64(row + FN_OUT), out2 = s_ld64(row + FN_OUT2);
   const uint32_t H = (uint32_t)sh.H, M = (uint32_t)sh.M;
@@ -1520,7 +1582,7 @@ DEV void fin_tile(const KArgs& a, const Instr& in, int wv) {
       if (sh.fp8)
         st32(ro, (m0 * (uint32_t)sh.I + n0 + c) * 4u, __float_as_uint(mv));
       else
-        st16(ro, opnd_bf16(m0, n0 + c), bf16_bits(mv));
+        st16(ro, opnd_bf16(m0, n0 + c, (uint32_t)sh.I), bf16_bits(mv));
     }
   } else if (kind >= K_QA) {  // indexer q_a, head weights, key: fp32 rows
     const uint32_t w = kind == K_QA ? (uint32_t)sh.qr : kind == K_W ? (uint32_t)sh.nh : 128u;
@@ -1632,10 +1694,10 @@ DEV void norm_row(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
       st128(r1o, e * 4u + 16u, u32x4{__float_as_uint(v[i][4]), __float_as_uint(v[i][5]), __float_as_uint(v[i][6]), __float_as_uint(v[i][7])});
     }
     if (FP8) {
-      st64(rh, opnd_fp8(m, e), u32x2{e4m3x4(h[i][0] / s, h[i][1] / s, h[i][2] / s, h[i][3] / s),
+      st64(rh, opnd_fp8(m, e, H), u32x2{e4m3x4(h[i][0] / s, h[i][1] / s, h[i][2] / s, h[i][3] / s),
                                      e4m3x4(h[i][4] / s, h[i][5] / s, h[i][6] / s, h[i][7] / s)});
     } else {
-      st128(rh, opnd_bf16(m, e), u32x4{pack_bf2(h[i][0], h[i][1]), pack_bf2(h[i][2], h[i][3]), pack_bf2(h[i][4], h[i][5]),
+      st128(rh, opnd_bf16(m, e, H), u32x4{pack_bf2(h[i][0], h[i][1]), pack_bf2(h[i][2], h[i][3]), pack_bf2(h[i][4], h[i][5]),
                                        pack_bf2(h[i][6], h[i][7])});
     }
   }
@@ -1675,7 +1737,7 @@ DEV void quant_row(const KArgs& a, const Instr& in, char* smem, int wv) {
   for (int i = 0; i < kQuantIt; ++i) {
     const uint32_t gi = t + 512u * i;
     if (gi < ng)
-      st32(ro, opnd_fp8(m, gi * 4u), e4m3x4(__uint_as_float(v[i].x) / s, __uint_as_float(v[i].y) / s,
+      st32(ro, opnd_fp8(m, gi * 4u, K), e4m3x4(__uint_as_float(v[i].x) / s, __uint_as_float(v[i].y) / s,
                                             __uint_as_float(v[i].z) / s, __uint_as_float(v[i].w) / s));
   }
   if (t == 0) st32(rsrc((const void*)s_ld64(row + QT_S)), m * 4u, __float_as_uint(s));
@@ -1728,7 +1790,7 @@ DEV void comb_group(const KArgs& a, const Instr& in, int wv) {
     if (sh.fp8)
       st32(ro, (r * (uint32_t)sh.Hq * 128u + k) * 4u, __float_as_uint(v));
     else
-      st16(ro, opnd_bf16(r, k), bf16_bits(v));
+      st16(ro, opnd_bf16(r, k, (uint32_t)sh.Hq * 128u), bf16_bits(v));
   }
   wait_vm0();
 }
@@ -1831,7 +1893,8 @@ DEV void fin_qb(const KArgs& a, const Instr& in, int wv) {
 #pragma unroll
       for (uint32_t k = 1; k < 4; ++k)
         if (k < nk) acc += x[q][tl][k];
-      st16(ro, opnd_bf16(ms[q], h * (uint32_t)kMlaNope + (uint32_t)tl * 64u + i), bf16_bits(acc * sa[q]));
+      st16(ro, opnd_bf16(ms[q], h * (uint32_t)kMlaNope + (uint32_t)tl * 64u + i, (uint32_t)sh.mla * kMlaNope),
+           bf16_bits(acc * sa[q]));
     }
   }
   wait_vm0();
@@ -2169,12 +2232,18 @@ DEV void topk_row(const KArgs& a, const Instr& in, int wv) {
 
 // LD: the instance with loader waves (the Qwen3 layers), which never runs the indexer's top-k: its
 // code stays out of that instance's register allocation
-template <bool LD>
+template <bool LD, bool RG>
 DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const uint32_t op = in.w[W_OPCODE];
   if (op == OP_GEMM) {
-    if (a.sh.fp8 && in.w[W_LAYER + 1] != K_UK) gemm_tile<true>(a, in, smem, lease, wv);
-    else gemm_tile<false>(a, in, smem, lease, wv);
+    if constexpr (RG) {  // plans of more than 16 rows: their own kernel instance
+      if (a.sh.fp8) gemm_tile_groups<true>(a, in, smem, lease, wv);
+      else gemm_tile_groups<false>(a, in, smem, lease, wv);
+    } else if (a.sh.fp8 && in.w[W_LAYER + 1] != K_UK) {
+      gemm_tile<true>(a, in, smem, lease, wv);
+    } else {
+      gemm_tile<false>(a, in, smem, lease, wv);
+    }
   } else if (op == OP_NORM) {
     if (a.sh.fp8) norm_row<true>(a, in, smem, lease, wv);
     else norm_row<false>(a, in, smem, lease, wv);
@@ -2182,10 +2251,10 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
     const uint32_t nk = in.w[W_LAYER + 5];
     if (in.w[W_LAYER + 1] == K_QI) fin_qi(a, in, wv);
     else if (in.w[W_LAYER + 1] == K_QB) fin_qb(a, in, wv);
-    else if (nk <= 4) fin_tile<4>(a, in, wv);
-    else if (nk <= 8) fin_tile<8>(a, in, wv);
-    else if (nk <= 12) fin_tile<12>(a, in, wv);
-    else fin_tile<kMaxChunks>(a, in, wv);
+    else if (nk <= 4) fin_tile<4, RG>(a, in, wv);
+    else if (nk <= 8) fin_tile<8, RG>(a, in, wv);
+    else if (nk <= 12) fin_tile<12, RG>(a, in, wv);
+    else fin_tile<kMaxChunks, RG>(a, in, wv);
   } else if (op == OP_QUANT) {
     quant_row(a, in, smem, wv);
   } else if (op == OP_COMB) {
@@ -2201,11 +2270,13 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
 
 // controller: a projection tile's input chunk into the activation area (skipped when the previous
 // instruction staged the same chunk and nothing has written the area since)
+template <bool RG>
 DEV void gemm_stage(const KArgs& a, const Instr& in, char* act, uint64_t& staged) {
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const uint32_t kind = in.w[W_LAYER + 1], kc = in.w[W_LAYER + 6];
   // the main-MLA query BMM reads its head's 128 columns of the D0 output (payload word 7), in bf16
   const uint32_t k0 = kind == K_UK ? in.w[W_LAYER + 7] : in.w[W_LAYER + 5];
+  if (RG) return;  // more than 16 rows: the waves read their groups' chunks themselves
   const bool f8 = a.sh.fp8 && kind != K_UK;
   const uint32_t off = f8 ? (k0 >> 6) * 1024u : (k0 >> 5) * 1024u;
   const uint32_t bytes = f8 ? (kc >> 6) * 1024u : (kc >> 5) * 1024u;  // at most kActABytes
@@ -2246,7 +2317,7 @@ DEV void o_store(const KArgs& a, const Instr& in, __amdgpu_buffer_rsrc_t ro, uin
   if (S == 0)
     ll_put2(ro, (r * w + k) / 2u, pack_bf2(v.x, v.y), pack_bf2(v.z, v.w), tag);
   else if (!a.sh.fp8)
-    st64(ro, opnd_bf16(r, k), u32x2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)});
+    st64(ro, opnd_bf16(r, k, w), u32x2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)});
   else
     st128(ro, (r * w + k) * 4u, u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
 }
@@ -2596,7 +2667,7 @@ DEV bool wait_loaders(const char* smem, int i) {
   }
 }
 
-template <int S, bool LD>
+template <int S, bool LD, bool RG>
 DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride, char* smem) {
   uint32_t* ctrl = (uint32_t*)(smem + kCtrlOff);  // LDS; read and written only across barriers
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
@@ -2646,7 +2717,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       ok = graph || wait_events(a, in, poll, wc);
       if (tracing) t_ev = rtc();
       if (ok && op == OP_ATTN && (in.w[W_CHAIN] & 1u) == 0u) ok = attn_stage(a, in, act, false, poll, sst);  // a chain's first split
-      if (ok && op == OP_GEMM) gemm_stage(a, in, act, staged);
+      if (ok && op == OP_GEMM) gemm_stage<RG>(a, in, act, staged);
       if (ok && op == OP_SCORE) score_stage(a, in, act);
       if (op != OP_GEMM) staged = 0;
       if (tracing) t_ld = rtc();
@@ -2685,7 +2756,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       if (op == OP_ATTN)
         attn_compute<S>(a, in, smem, act, lease, kNW - 1);
       else if constexpr (m16)
-        m16_body<LD>(a, in, smem, lease, kNW - 1);
+        m16_body<LD, RG>(a, in, smem, lease, kNW - 1);
       else
         proj_body(a, in, smem, lease, fused_norm, kNW - 1);
     }
@@ -2699,7 +2770,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       if (op == OP_ATTN)
         attn_epilogue<S>(a, in, smem, st);
       else if (op == OP_GEMM)
-        gemm_epilogue(a, in, smem);
+        gemm_epilogue<RG>(a, in, smem);
       pend = sig_of(in);
       pending = true;
     } else if (op == OP_ATTN) {
@@ -2738,7 +2809,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
   }
 }
 
-template <int S, bool LD>
+template <int S, bool LD, bool RG>
 DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, int cw, char* smem) {
   const uint32_t* ctrl = (const uint32_t*)(smem + kCtrlOff);  // LDS abort flag
   constexpr bool loaders = LD;  // loader waves stream the leases
@@ -2800,7 +2871,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
       if (op == OP_ATTN) {
         attn_compute<S>(a, in, smem, act, lease, cw);
       } else if constexpr (S == 1) {
-        m16_body<LD>(a, in, smem, lease, cw);
+        m16_body<LD, RG>(a, in, smem, lease, cw);
       } else {
         proj_body(a, in, smem, lease, fused_norm, cw);
       }
@@ -2843,7 +2914,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
 // one kernel per op family: the single-token plans' bodies (S = 0) and the multi-row plans' (S = 1)
 // are compiled separately, so neither family's register allocation carries the other's code; the
 // multi-row family comes with loader waves (LD) or with the eight waves prefetching for themselves
-template <int S, bool LD>
+template <int S, bool LD, bool RG>
 __global__ void __launch_bounds__(LD ? dev::kThreadsM : dev::kThreads, 1) mk_worker(KArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2862,17 +2933,22 @@ __global__ void __launch_bounds__(LD ? dev::kThreadsM : dev::kThreads, 1) mk_wor
   if (threadIdx.x < 8) ((uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff))[threadIdx.x] = 0u;  // instruction ring tags
   __syncthreads();
   if (LD && wave >= dev::kNW) dev::loader<S>(a, base, count, stride, wave - dev::kNW, smem);
-  else if (wave == 0) dev::controller<S, LD>(a, base, count, stride, smem);
-  else dev::compute<S, LD>(a, base, count, stride, wave - 1, smem);
+  else if (wave == 0) dev::controller<S, LD, RG>(a, base, count, stride, smem);
+  else dev::compute<S, LD, RG>(a, base, count, stride, wave - 1, smem);
 }
 
 hipError_t launch_worker(const KArgs& a, int grid, hipStream_t stream, int spec, bool loaders) {
-  if (spec == 1 && loaders)
-    hipLaunchKernelGGL((mk_worker<1, true>), dim3(grid), dim3(dev::kThreadsM), dev::kLdsBytes, stream, a);
+  const bool groups = spec == 1 && a.sh.rg > 1;  // more than 16 rows: the row-group GEMM tiles
+  if (groups && loaders)
+    hipLaunchKernelGGL((mk_worker<1, true, true>), dim3(grid), dim3(dev::kThreadsM), dev::kLdsBytes, stream, a);
+  else if (groups)
+    hipLaunchKernelGGL((mk_worker<1, false, true>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+  else if (spec == 1 && loaders)
+    hipLaunchKernelGGL((mk_worker<1, true, false>), dim3(grid), dim3(dev::kThreadsM), dev::kLdsBytes, stream, a);
   else if (spec == 1)
-    hipLaunchKernelGGL((mk_worker<1, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+    hipLaunchKernelGGL((mk_worker<1, false, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
   else
-    hipLaunchKernelGGL((mk_worker<0, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
+    hipLaunchKernelGGL((mk_worker<0, false, false>), dim3(grid), dim3(dev::kThreads), dev::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
@@ -2925,12 +3001,15 @@ hipError_t launch_fill_table(const TableReloc* reloc, int n, const TensorPtrs& t
 
 hipError_t worker_occupancy(int* blocks_per_cu, int spec) {
   // the multi-row family's larger block (with loader waves) bounds both of its instances
-  const void* f = spec == 1 ? (const void*)mk_worker<1, true> : (const void*)mk_worker<0, false>;
+  const void* f = spec == 1 ? (const void*)mk_worker<1, true, false> : (const void*)mk_worker<0, false, false>;
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
   if (e != hipSuccess) return e;
   if (spec == 1) {
-    e = hipFuncSetAttribute((const void*)mk_worker<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
-    if (e != hipSuccess) return e;
+    for (const void* g : {(const void*)mk_worker<1, false, false>, (const void*)mk_worker<1, true, true>,
+                          (const void*)mk_worker<1, false, true>}) {
+      e = hipFuncSetAttribute(g, hipFuncAttributeMaxDynamicSharedMemorySize, dev::kLdsBytes);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, spec == 1 ? dev::kThreadsM : dev::kThreads,
                                                       dev::kLdsBytes);

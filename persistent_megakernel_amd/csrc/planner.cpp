@@ -123,12 +123,14 @@ bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, s
   return true;
 }
 
-// Multi-row (M = R x T <= 16) layer: row-task norms, projections as (64-row tile, K chunk) tasks
-// writing partial sums, one finalize task per row tile adding the chunks in K order and applying
-// the epilogue; FP8 plans quantise o and m per row.  The same rules as the oracle's builder.
+// Multi-row (M = R x T <= 256) layer: row-task norms, projections as (64-row tile, K chunk) tasks
+// writing partial sums for every 16-row group of M (the weights are read once), one finalize task
+// per (row tile, row group) adding the chunks in K order and applying the epilogue; FP8 plans
+// quantise o and m per row.  Row-level consumers wait for their own group's finalizes only.  The
+// same rules as the oracle's builder.
 void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, int W, Builder& b, int& max_splits) {
   const int H = c.hidden, I = c.inter, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
-  const int g = Hq / Hkv, R = c.n_requests, M = R * c.tokens_per_request;
+  const int g = Hq / Hkv, R = c.n_requests, T = c.tokens_per_request, M = R * T, G = (M + 15) / 16;
   const int spec = p.spec, kc = p.kc, st = p.s_tok, rt = kM16Rows;
   const int n_qkv = (Hq + 2 * Hkv) * d;
   const bool fp8 = c.act_fp8 != 0;
@@ -143,24 +145,28 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, int 
         b.task(OP_GEMM, row_g, spec, {wait}, {{parts[j], 1u}}, {l, kind, j, j * rows, rows, ck * kc, kc});
     const int row_f = b.op_row(OP_FIN, l, {row_g}, kind);
     for (int j = 0; j < nt; ++j)
-      b.task(OP_FIN, row_f, spec, {{parts[j], (uint32_t)nk}}, {{fin_event(j), 1u}}, {l, kind, j, j * rows, rows, nk, kc});
+      for (int gi = 0; gi < G; ++gi)
+        b.task(OP_FIN, row_f, spec, {{parts[j], (uint32_t)nk}}, {{fin_event(j, gi), 1u}},
+               {l, kind, j, j * rows, rows, nk, kc, 0, 0, gi});  // gi at W_GROUP
     return row_f;
   };
-  int prev = -1, prev_row = -1;
+  std::vector<int> prev;  // per row group: the previous layer's down finalizes
+  int prev_row = -1;
   uint32_t prev_thr = 0;
   for (int l = 0; l < c.num_layers; ++l) {
     const int row_na = b.op_row(OP_NORM, l, prev_row >= 0 ? std::vector<int>{prev_row} : std::vector<int>{}, 0);
     const int ev_na = b.event((uint32_t)M);
     for (int m = 0; m < M; ++m) {
-      if (prev < 0)
+      if (prev.empty())
         b.task(OP_NORM, row_na, spec, {}, {{ev_na, 1u}}, {l, 0, m});
       else
-        b.task(OP_NORM, row_na, spec, {{prev, prev_thr}}, {{ev_na, 1u}}, {l, 0, m});
+        b.task(OP_NORM, row_na, spec, {{prev[m / 16], prev_thr}}, {{ev_na, 1u}}, {l, 0, m});
     }
-    // QKV: a 64-row tile lies inside one head; its finalize counts for the head's kv group
+    // QKV: a 64-row tile lies inside one head; its finalize of a row group counts for the head's
+    // kv group and that row group
     const uint32_t tiles_per_group = (uint32_t)((g + 2) * d / rt);
-    std::vector<int> ev_qkv(Hkv);
-    for (int hk = 0; hk < Hkv; ++hk) ev_qkv[hk] = b.event(tiles_per_group);
+    std::vector<int> ev_qkv((size_t)Hkv * G);
+    for (int q = 0; q < Hkv * G; ++q) ev_qkv[q] = b.event(tiles_per_group);
     auto qkv_group = [&](int j) {
       const int n0 = j * rt;
       if (n0 < Hq * d) return (n0 / d) / g;
@@ -168,7 +174,7 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, int 
       return (n0 - (Hq + Hkv) * d) / d;
     };
     const int row_qf = proj(K_QKV, l, n_qkv, H, rt, {ev_na, (uint32_t)M}, row_na,
-                            [&](int j) { return ev_qkv[qkv_group(j)]; });
+                            [&](int j, int gi) { return ev_qkv[qkv_group(j) * G + gi]; });
     // split-KV attention: the (request, kv head, split) tasks are laid out so that dealing them
     // round-robin hands each worker a run of consecutive splits of one (request, kv head) -- a
     // chain, folded into one running softmax state on chip and written as one partial.  The
@@ -209,12 +215,12 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, int 
       for (int j = 0; j < C && k < len[j]; ++j) {
         const int i = start[j] + k, r = seq[i].pair / Hkv, hk = seq[i].pair % Hkv, s = seq[i].s;
         const int t0 = s * st, t1 = std::min((int)ctx[r], (s + 1) * st);
+        const std::pair<int, uint32_t> qkv_wait{ev_qkv[hk * G + r * T / 16], tiles_per_group};
         if (flags[i] & 2)
-          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {{ev_att[seq[i].pair], 1u}},
+          b.task(OP_ATTN, row_attn, spec, {qkv_wait}, {{ev_att[seq[i].pair], 1u}},
                  {l, r, hk, s, t0, t1, 0, 0, 0, nsplit[r], flags[i], slot[i]});
         else
-          b.task(OP_ATTN, row_attn, spec, {{ev_qkv[hk], tiles_per_group}}, {},
-                 {l, r, hk, s, t0, t1, 0, 0, 0, nsplit[r], flags[i], slot[i]});
+          b.task(OP_ATTN, row_attn, spec, {qkv_wait}, {}, {l, r, hk, s, t0, t1, 0, 0, 0, nsplit[r], flags[i], slot[i]});
       }
     const int row_comb = b.op_row(OP_COMB, l, {row_attn});
     const int ev_oready = b.event((uint32_t)(R * Hkv));
@@ -230,25 +236,32 @@ void build_m16(const mk_config& c, const int32_t* ctx, const TileParams& p, int 
       o_wait = {ev_oq, (uint32_t)M};
       o_dep = row_qo;
     }
-    const int ev_o = b.event((uint32_t)(H / rt));
-    const int row_of = proj(K_O, l, H, Hq * d, rt, o_wait, o_dep, [&](int) { return ev_o; });
+    std::vector<int> ev_o(G);
+    for (int gi = 0; gi < G; ++gi) ev_o[gi] = b.event((uint32_t)(H / rt));
+    const int row_of = proj(K_O, l, H, Hq * d, rt, o_wait, o_dep, [&](int, int gi) { return ev_o[gi]; });
     const int row_nb = b.op_row(OP_NORM, l, {row_of}, 1);
     const int ev_nb = b.event((uint32_t)M);
-    for (int m = 0; m < M; ++m) b.task(OP_NORM, row_nb, spec, {{ev_o, (uint32_t)(H / rt)}}, {{ev_nb, 1u}}, {l, 1, m});
-    // gate/up: a tile holds rt/2 gate rows and the matching rt/2 up rows
-    const int ev_gu = b.event((uint32_t)(I / (rt / 2)));
-    const int row_gf = proj(K_GU, l, I, H, rt / 2, {ev_nb, (uint32_t)M}, row_nb, [&](int) { return ev_gu; });
-    std::pair<int, uint32_t> m_wait{ev_gu, (uint32_t)(I / (rt / 2))};
+    for (int m = 0; m < M; ++m)
+      b.task(OP_NORM, row_nb, spec, {{ev_o[m / 16], (uint32_t)(H / rt)}}, {{ev_nb, 1u}}, {l, 1, m});
+    // gate/up: a tile holds rt/2 gate rows and the matching rt/2 up rows.  W8A8: the per-row
+    // quantisation waits for its row group's finalizes; bf16: the down tiles read every group
+    const uint32_t n_gu = (uint32_t)(I / (rt / 2));
+    std::vector<int> ev_gu(fp8 ? G : 1);
+    for (auto& e : ev_gu) e = b.event(fp8 ? n_gu : n_gu * (uint32_t)G);
+    const int row_gf = proj(K_GU, l, I, H, rt / 2, {ev_nb, (uint32_t)M}, row_nb,
+                            [&](int, int gi) { return ev_gu[fp8 ? gi : 0]; });
+    std::pair<int, uint32_t> m_wait{ev_gu[0], n_gu * (uint32_t)G};
     int m_dep = row_gf;
     if (fp8) {
       const int row_qm = b.op_row(OP_QUANT, l, {row_gf}, 1);
       const int ev_mq = b.event((uint32_t)M);
-      for (int m = 0; m < M; ++m) b.task(OP_QUANT, row_qm, spec, {m_wait}, {{ev_mq, 1u}}, {l, 1, m});
+      for (int m = 0; m < M; ++m) b.task(OP_QUANT, row_qm, spec, {{ev_gu[m / 16], n_gu}}, {{ev_mq, 1u}}, {l, 1, m});
       m_wait = {ev_mq, (uint32_t)M};
       m_dep = row_qm;
     }
-    const int ev_down = b.event((uint32_t)(H / rt));
-    prev_row = proj(K_DOWN, l, H, I, rt, m_wait, m_dep, [&](int) { return ev_down; });
+    std::vector<int> ev_down(G);
+    for (int gi = 0; gi < G; ++gi) ev_down[gi] = b.event((uint32_t)(H / rt));
+    prev_row = proj(K_DOWN, l, H, I, rt, m_wait, m_dep, [&](int, int gi) { return ev_down[gi]; });
     prev = ev_down;
     prev_thr = (uint32_t)(H / rt);
   }
@@ -540,9 +553,9 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
       return MK_ERR_UNSUPPORTED;
     }
     if ((Hq + 2 * Hkv) * d % kM16Rows || H % kM16Rows || I % (kM16Rows / 2) || H % p.kc || I % p.kc ||
-        (Hq * d) % p.kc || R * c.tokens_per_request > 16) {
+        (Hq * d) % p.kc || R * c.tokens_per_request > kMaxRows) {
       err = "unsupported multi-row shape: projection sizes must be multiples of the 64-row tile and of the K chunk, "
-            "and at most 16 rows";
+            "and at most 256 rows";
       return MK_ERR_UNSUPPORTED;
     }
     build_m16(c, ctx, p, W, b, max_splits);
@@ -619,28 +632,29 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
     // plain; projection inputs in the matrix-core operand order over 16 row slots
     const size_t el = c.act_fp8 ? 1 : 2;
     const size_t kc = (size_t)p.kc;
+    const size_t G = (size_t)(M + 15) / 16, rows = 16 * G;  // 16-row groups of the operand order
     region("qkv", (size_t)M * n_qkv * 8);
     region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);
     region("r1", (size_t)M * H * 4);
     region("r2", (size_t)M * H * 4);
     region("y", (size_t)M * H * 2);
-    region("h1", (size_t)16 * H * el);
-    region("h2", (size_t)16 * H * el);
+    region("h1", rows * H * el);
+    region("h2", rows * H * el);
     if (c.act_fp8) {  // attention output and m in fp32 rows, quantised per token into oq / mq
       region("o", (size_t)M * Hq * d * 4);
       region("m", (size_t)M * I * 4);
-      region("oq", (size_t)16 * Hq * d);
-      region("mq", (size_t)16 * I);
-      for (const char* s : {"s1", "s2", "so", "sm"}) region(s, 16 * 4);
+      region("oq", rows * Hq * d);
+      region("mq", rows * I);
+      for (const char* s : {"s1", "s2", "so", "sm"}) region(s, rows * 4);
     } else {
-      region("o", (size_t)16 * Hq * d * 2);
-      region("m", (size_t)16 * I * 2);
+      region("o", rows * Hq * d * 2);
+      region("m", rows * I * 2);
     }
-    // fp32 partial sums of the projection tiles: [tile][K chunk][16 x 64]
-    region("gp_qkv", (size_t)(n_qkv / kM16Rows) * (H / kc) * 4096);
-    region("gp_o", (size_t)(H / kM16Rows) * (Hq * d / kc) * 4096);
-    region("gp_gu", (size_t)(I / (kM16Rows / 2)) * (H / kc) * 4096);
-    region("gp_down", (size_t)(H / kM16Rows) * (I / kc) * 4096);
+    // fp32 partial sums of the projection tiles: [tile][K chunk][row group][16 x 64]
+    region("gp_qkv", (size_t)(n_qkv / kM16Rows) * (H / kc) * G * 4096);
+    region("gp_o", (size_t)(H / kM16Rows) * (Hq * d / kc) * G * 4096);
+    region("gp_gu", (size_t)(I / (kM16Rows / 2)) * (H / kc) * G * 4096);
+    region("gp_down", (size_t)(H / kM16Rows) * (I / kc) * G * 4096);
   } else {
     // vectors written inside a run are tagged 8-byte records: fp32 or a bf16 pair per record
     region("qkv", (size_t)M * n_qkv * 8);

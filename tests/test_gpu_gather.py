@@ -77,9 +77,10 @@ def test_gather_full_step():
     _qwen_case(cfg, [cfg.context], 0, seed=0, modes=(("mk", False),))
 
 
+@pytest.mark.parametrize("R", [6, 35])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_gather_multi_row_reduced_random_pages(fp8):
-    ctx = [1, 37, 300, 513, 64, 6]
+def test_gather_multi_row_reduced_random_pages(fp8, R):
+    ctx = [1, 37, 300, 513, 64, 6] if R == 6 else [int(c) for c in np.random.default_rng(35).integers(1, 514, R)]
     base = get_config("qwen3_8b_layer_fp8" if fp8 else "qwen3_8b_layer")
     cfg = dataclasses.replace(base, hidden=1024, inter=2048 if fp8 else 1536, n_q_heads=8, n_kv_heads=2,
                               n_requests=len(ctx), context=max(ctx), page_size=16, random_pages=True)

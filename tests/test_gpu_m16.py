@@ -40,16 +40,21 @@ def _tol(cfg):
 
 
 def opnd_bf16_rows(buf: np.ndarray, K: int) -> np.ndarray:
-    """[16, K] float64 from the bf16 matrix-core operand order: per K step of 32, lane
-    m + 16 * ((k % 32) // 8) holds 8 consecutive k of row m."""
-    a = buf.view(np.uint16)[:16 * K].reshape(K // 32, 4, 16, 8).transpose(2, 0, 1, 3).reshape(16, K)
+    """[16 G, K] float64 from the bf16 matrix-core operand order: 16-row groups one after the
+    other; inside a group, per K step of 32, lane m + 16 * ((k % 32) // 8) holds 8 consecutive k of
+    row m of the group."""
+    u = buf.view(np.uint16)
+    G = len(u) // (16 * K)
+    a = u[:G * 16 * K].reshape(G, K // 32, 4, 16, 8).transpose(0, 3, 1, 2, 4).reshape(16 * G, K)
     return bf16_bits_to_f64(a)
 
 
 def opnd_fp8_rows(buf: np.ndarray, K: int) -> np.ndarray:
-    """[16, K] e4m3 codes from the FP8 operand order: per K step of 64, lane
-    m + 16 * ((k % 64) // 16) holds 16 consecutive k of row m."""
-    return buf.view(np.uint8)[:16 * K].reshape(K // 64, 4, 16, 16).transpose(2, 0, 1, 3).reshape(16, K)
+    """[16 G, K] e4m3 codes from the FP8 operand order: 16-row groups one after the other; inside
+    a group, per K step of 64, lane m + 16 * ((k % 64) // 16) holds 16 consecutive k of row m."""
+    u = buf.view(np.uint8)
+    G = len(u) // (16 * K)
+    return u[:G * 16 * K].reshape(G, K // 64, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(16 * G, K)
 
 
 def _run(cfg, inp, W=0):
@@ -178,9 +183,12 @@ def _reduced(fp8, R, ctx):
                                n_requests=R, context=max(ctx), page_size=16)
 
 
+@pytest.mark.parametrize("R", [5, 40])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_m16_reduced_layer_all_modes(fp8):
-    ctx = [1, 37, 300, 513, 64]
+def test_m16_reduced_layer_all_modes(fp8, R):
+    """Every intermediate and output at reduced shapes; 40 requests take three 16-row groups (the
+    last one ragged)."""
+    ctx = [1, 37, 300, 513, 64] if R == 5 else [int(c) for c in np.random.default_rng(40).integers(1, 514, R)]
     cfg = _reduced(fp8, len(ctx), ctx)
     inp = make_inputs(cfg, seed=3)
     inp["context_lens"] = np.array(ctx, dtype=np.int32)
@@ -220,6 +228,35 @@ def _sample_inputs(cfg, inp, rows):
     sub["k_cache"], sub["v_cache"] = inp["k_cache"][:, pages], inp["v_cache"][:, pages]
     scfg = dataclasses.replace(cfg, n_requests=len(rows))
     return scfg, sub
+
+
+@pytest.mark.timeout(900)
+def test_m64_full_size_sampled_requests():
+    """The 64-request layer (four 16-row groups, random page tables) at full size: the written slot
+    set exact, y / r2 and the written rows of eight requests spread over the four groups (both ends
+    of each) against the oracle; the graph modes bitwise equal to the megakernel."""
+    name = "qwen3_8b_layer_m64"
+    cfg = get_config(name)
+    _say(f"case: {name} full size, inputs")
+    inp = make_inputs(cfg, seed=0)
+    k0, v0 = inp["k_cache"][0].copy(), inp["v_cache"][0].copy()
+    run = _run(cfg, inp)
+    _say(f"case: {name} megakernel W=all")
+    run.run("mk")
+    kc, vc = _check_slot_set(run, inp, k0, v0, f"{name} mk")
+    for rows in ([0, 15, 16, 31], [32, 47, 48, 63]):
+        scfg, sub = _sample_inputs(cfg, inp, rows)
+        _say(f"case: {name} oracle on requests {rows}")
+        ref, ind = _oracle(scfg, sub, run, rows)
+        _check_outputs(run, ref, ind, rows, f"{name} mk requests {rows}")
+        _check_written_rows(run, kc, vc, inp, ref, rows, f"{name} mk")
+    y_mk, r2_mk = run.t["y_out"].clone(), run.t["r2_out"].clone()
+    for ms in (False, True):
+        _say(f"case: {name} graph multistream={ms}")
+        run.t["y_out"].zero_()
+        run.t["r2_out"].zero_()
+        run.run("graph", ms)
+        assert torch.equal(run.t["y_out"], y_mk) and torch.equal(run.t["r2_out"], r2_mk)
 
 
 @pytest.mark.timeout(900)

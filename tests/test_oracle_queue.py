@@ -10,7 +10,7 @@ from workloads import get_config
 
 
 @pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
-                                  "indexer_front", "indexer_front_topk",
+                                  "qwen3_8b_layer_m64", "indexer_front", "indexer_front_topk",
                                   "attention_pre"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_invariants(name, W):
@@ -95,10 +95,10 @@ def _tasks(plan):
     return [q[w, i] for i in range(q.shape[1]) for w in range(q.shape[0]) if q[w, i][0] != oq.OP_NOOP]
 
 
-@pytest.mark.parametrize("name", ["qwen3_8b_layer", "qwen3_8b_layer_fp8"])
+@pytest.mark.parametrize("name", ["qwen3_8b_layer", "qwen3_8b_layer_fp8", "qwen3_8b_layer_m64"])
 def test_multi_row_tiles_cover_each_projection_once(name):
     """Each projection's (row, K) grid is covered exactly once by its GEMM tiles, and its
-    rows exactly once by finalize tasks whose chunk count matches the tiles."""
+    (row, 16-row group) pairs exactly once by finalize tasks whose chunk count matches the tiles."""
     cfg = get_config(name)
     plan = oq.build_queue(cfg, 256)
     p = plan["params"]
@@ -111,8 +111,9 @@ def test_multi_row_tiles_cover_each_projection_once(name):
     assert set(ops) <= {oq.OP_NORM, oq.OP_GEMM, oq.OP_FIN, oq.OP_QUANT, oq.OP_ATTN, oq.OP_COMB}
     assert ops.count(oq.OP_COMB) == cfg.n_requests * cfg.n_kv_heads
     for kind, (N, K) in shapes.items():
+        G = -(-cfg.m // 16)
         grid = np.zeros((N, K // kc), dtype=np.int64)
-        fin = np.zeros(N, dtype=np.int64)
+        fin = np.zeros((N, G), dtype=np.int64)
         for t in _tasks(plan):
             pl = t[20:]  # payload words follow the header
             if t[0] == oq.OP_GEMM and pl[1] == kind:
@@ -120,9 +121,9 @@ def test_multi_row_tiles_cover_each_projection_once(name):
                 assert int(pl[6]) == kc and k0 % kc == 0
                 grid[n0:n0 + rows, k0 // kc] += 1
             if t[0] == oq.OP_FIN and pl[1] == kind:
-                n0, rows, nk = int(pl[3]), int(pl[4]), int(pl[5])
+                n0, rows, nk, gi = int(pl[3]), int(pl[4]), int(pl[5]), int(pl[9])
                 assert nk == K // kc
-                fin[n0:n0 + rows] += 1
+                fin[n0:n0 + rows, gi] += 1
         assert (grid == 1).all() and (fin == 1).all(), kind
     n_norm = ops.count(oq.OP_NORM)
     n_quant = ops.count(oq.OP_QUANT)
@@ -130,15 +131,43 @@ def test_multi_row_tiles_cover_each_projection_once(name):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-def test_multi_row_no_deadlock_random_speeds(fp8):
+@pytest.mark.parametrize("R", [3, 40])
+def test_multi_row_no_deadlock_random_speeds(fp8, R):
     cfg = dataclasses.replace(get_config("qwen3_8b_layer_fp8" if fp8 else "qwen3_8b_layer"),
-                              hidden=512, inter=1024, n_q_heads=4, n_kv_heads=2, n_requests=3,
+                              hidden=512, inter=1024, n_q_heads=4, n_kv_heads=2, n_requests=R,
                               context=200, num_layers=2)
     plan = oq.build_queue(cfg, 37)
     assert plan["params"]["spec"] == 1
     oq.check_invariants(plan)
     for seed in range(2):
         simulate(plan, seed)
+
+
+def test_row_groups_wait_for_their_own_group():
+    """Beyond 16 rows: an attention split waits for its request's 16-row group of its kv group's
+    QKV finalizes, a row's second norm for its group's O finalizes, the next layer's first norm
+    for its group's down finalizes; every finalize signals exactly one of those events."""
+    cfg = dataclasses.replace(get_config("qwen3_8b_layer"), hidden=512, inter=1024, n_q_heads=4,
+                              n_kv_heads=2, n_requests=40, context=100, num_layers=2)
+    plan = oq.build_queue(cfg, 37)
+    tasks = _tasks(plan)
+    fin_ev = {}
+    for t in tasks:
+        if t[0] == oq.OP_FIN:
+            fin_ev.setdefault((int(t[20]), int(t[21]), int(t[29])), set()).add(int(t[14]))
+    for (l, kind, gi), evs in fin_ev.items():
+        if kind != oq.K_QKV:
+            assert len(evs) == 1 or kind == oq.K_GU, (l, kind, gi)
+    for t in tasks:
+        if t[0] == oq.OP_ATTN:
+            l, r, hk = int(t[20]), int(t[21]), int(t[22])
+            assert int(t[6]) in fin_ev[(l, oq.K_QKV, r // 16)]
+        if t[0] == oq.OP_NORM and int(t[21]) == 1:
+            l, m = int(t[20]), int(t[22])
+            assert fin_ev[(l, oq.K_O, m // 16)] == {int(t[6])}
+        if t[0] == oq.OP_NORM and int(t[21]) == 0 and int(t[20]) > 0:
+            l, m = int(t[20]), int(t[22])
+            assert fin_ev[(l - 1, oq.K_DOWN, m // 16)] == {int(t[6])}
 
 
 def test_indexer_front_counts_and_no_deadlock():

@@ -17,7 +17,7 @@ def _both(cfg, W, ctx=None):
 
 
 @pytest.mark.parametrize("name", ["qwen3_0p6b_layer", "qwen3_0p6b_step", "qwen3_8b_layer", "qwen3_8b_layer_fp8",
-                                  "indexer_front", "indexer_front_topk",
+                                  "qwen3_8b_layer_m64", "indexer_front", "indexer_front_topk",
                                   "attention_pre"])
 @pytest.mark.parametrize("W", [1, 7, 148, 256])
 def test_queue_bit_exact(name, W):
@@ -50,6 +50,31 @@ def test_small_shapes_bit_exact():
         plan, ref = _both(cfg, W)
         assert np.array_equal(plan.queue(), ref["queue"])
         plan.close()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("R", [17, 40, 64, 256])
+def test_row_groups_bit_exact(fp8, R):
+    """Multi-row plans beyond 16 rows (16-row groups), ragged contexts, two layers."""
+    cfg = dataclasses.replace(get_config("qwen3_8b_layer_fp8" if fp8 else "qwen3_8b_layer"), hidden=1024,
+                              inter=2048, n_q_heads=8, n_kv_heads=2, n_requests=R, context=300, page_size=16,
+                              num_layers=2)
+    rng = np.random.default_rng(R)
+    ctx = [int(c) for c in rng.integers(1, 301, R)]
+    for W in (5, 37, 256):
+        plan, ref = _both(cfg, W, ctx)
+        assert np.array_equal(plan.queue(), ref["queue"])
+        assert np.array_equal(plan.thresholds(), ref["thresholds"])
+        oq.check_invariants(ref)
+        plan.close()
+
+
+def test_row_group_limits():
+    import persistent_megakernel_amd as mk
+    base = get_config("qwen3_8b_layer")
+    with pytest.raises(mk.MkError, match="at most 256 rows"):
+        mk.Plan(dataclasses.replace(base, n_requests=257), num_workers=256)
+    mk.Plan(dataclasses.replace(base, n_requests=256), num_workers=256).close()
 
 
 @pytest.mark.parametrize("topk,mla", [(0, 0), (64, 0), (0, 3), (64, 2)])

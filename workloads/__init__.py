@@ -85,6 +85,11 @@ CONFIGS: Dict[str, Config] = {
     "qwen3_8b_layer_fp8": Config("qwen3_8b_layer_fp8", "qwen3_layer", hidden=4096, inter=12288,
                                  n_q_heads=32, n_kv_heads=8, n_requests=16, context=8192,
                                  page_size=64, random_pages=True, weight_fp8=True, act_fp8=True),
+    # Qwen3-8B-shaped layer at a larger batch: 64 requests x 1 token (four 16-row groups), context
+    # 4096 in 64-token pages, randomised page tables.
+    "qwen3_8b_layer_m64": Config("qwen3_8b_layer_m64", "qwen3_layer", hidden=4096, inter=12288,
+                                 n_q_heads=32, n_kv_heads=8, n_requests=64, context=4096,
+                                 page_size=64, random_pages=True),
     # Indexer-style pre-attention front: 2 requests x 8 tokens, KV 8192, 64 heads x 128.
     "indexer_front": Config("indexer_front", "indexer_front", hidden=6144, n_requests=2,
                             tokens_per_request=8, context=8192, page_size=64, random_pages=True,
