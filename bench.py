@@ -177,7 +177,8 @@ def main() -> int:
     if not args.no_variants:
         for name, fn, flags in (("graph_single_stream", run_g1, 0), ("graph_multi_stream", run_gm, 0),
                                 ("megakernel_no_prefetch", run_mk, mk.MK_FLAG_NO_PREFETCH),
-                                ("megakernel_empty_framework", run_mk, mk.MK_FLAG_NOOP_ONLY)):
+                                ("megakernel_empty_framework", run_mk, mk.MK_FLAG_NOOP_ONLY),
+                                ("graph_empty_framework", run_g1, mk.MK_FLAG_NOOP_ONLY)):
             _log(f"bench: {name}")
             with torch.cuda.stream(stream):
                 variants[name] = round(timed(fn, plan(flags), max(10, args.steps // 2), 3) * 1000.0, 3)
@@ -213,7 +214,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _counter_traffic(cfg.name),
                      "kernel": "mk_worker<%s> (persistent megakernel, one launch per step)" % (
-                         "0, false" if cfg.m == 1 else "1, false" if indexer else "1, true")},
+                         "0, false, false" if cfg.m == 1 else "1, false, false" if indexer else
+                         "1, true, true" if cfg.m > 16 else "1, true, false")},
         "variants_us_per_step": variants,
         "step_us_stats": _stats(per_step),
         "hot_step_us": round(hot_ms * 1000.0, 3) if hot_ms is not None else
@@ -225,6 +227,10 @@ def main() -> int:
             "branch_parallelism": round(variants["graph_single_stream"] - variants["graph_multi_stream"], 3),
             "in_kernel_scheduling": round(variants["graph_multi_stream"] - step_us, 3),
             "prefetch": round(variants["megakernel_no_prefetch"] - step_us, 3),
+            # the same nodes with no op work (bodies skipped, loads of the leases not issued): what the
+            # graph's kernel boundaries and per-node set-up cost beyond the megakernel's own framework
+            "graph_fixed_cost_over_megakernel_framework": round(
+                variants["graph_empty_framework"] - variants["megakernel_empty_framework"], 3),
         }
     if not args.no_diagnostics:
         out["diagnostics"] = _diagnostics(cfg, mk, plans, tensor_sets[0], stream, torch, step, step_us)
