@@ -335,7 +335,31 @@ def _diagnostics(cfg, mk, plans, tensors, stream, torch, step, step_us):
         lm = live & (q[:, :, 0] == 6)
         layers_end = tr[:, :, 7][live & ~lm].max()
         out["tail_us"] = round(float((tr[:, :, 7][lm].max() - layers_end) / 100.0), 2)
+        out["cross_layer_prefetch"] = _cross_layer(q, tr, live, cfg.num_layers)
     return out
+
+
+def _cross_layer(q, tr, live, layers):
+    """Leases of the next layer issued during this one: for every worker and layer boundary, the
+    time from the issue of its first layer-(l+1) instruction's lease (trace word 9) to the end of its
+    last layer-l instruction, and to the end of layer l's last down tile on any worker."""
+    import numpy as np
+    layer = q[:, :, 20].astype(np.int64)
+    down_end = [tr[:, :, 7][live & (q[:, :, 0] == 5) & (layer == l)].max() for l in range(layers)]
+    own, glob = [], []
+    for w in range(q.shape[0]):
+        idx = np.flatnonzero(live[w] & (q[w, :, 0] != 6))
+        for a, b in zip(idx[:-1], idx[1:]):
+            if layer[w, b] == layer[w, a] + 1 and tr[w, b, 9] != 0:
+                own.append(tr[w, a, 7] - tr[w, b, 9])
+                glob.append(down_end[layer[w, a]] - tr[w, b, 9])
+    own, glob = np.array(own) / 100.0, np.array(glob) / 100.0
+    if not len(own):
+        return None
+    return {"boundaries": int(len(own)), "share_issued_before_own_layer_end": round(float((own > 0).mean()), 3),
+            "median_lead_over_own_layer_end_us": round(float(np.median(own)), 2),
+            "share_issued_before_layer_done": round(float((glob > 0).mean()), 3),
+            "median_lead_over_layer_done_us": round(float(np.median(glob)), 2)}
 
 
 def _stream_peak(torch):

@@ -239,8 +239,9 @@ mk_status mk_sync(mk_plan* plan, void* hip_stream);
  * per instruction: low 32 bits of the 100 MHz realtime clock when the controller saw it, when
  * its waits were met, when its activations were staged, after the compute start / end
  * barriers, when its outputs were acknowledged, when its arrival resolved (0 if none), when it
- * was done; word 8 counts the staging rounds repeated because an input was not yet current; words 9..15
- * hold per-family details (shader cycles between the two compute barriers in word 9). */
+ * was done; word 8 counts the staging rounds repeated because an input was not yet current; word 9:
+ * when the compute waves issued the instruction's lease (kernels with loader waves: shader cycles
+ * between the two compute barriers); words 10..15 hold per-family details. */
 mk_status mk_read_trace(const mk_plan* plan, uint32_t* host_out, size_t n_words);
 
 /* Copy the gather record of the last run of an MK_FLAG_DEBUG_GATHER plan into host memory (synchronous).

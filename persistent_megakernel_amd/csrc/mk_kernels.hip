@@ -765,8 +765,13 @@ __device__ __attribute__((noinline)) uint32_t stale_blocks(const char* base, uin
 // The wait of an instruction: stage every block of its regions in one round trip; with `verify`
 // (the megakernel), stage again the blocks holding a record whose tag is not current, until all
 // are.  False when the watchdog expired or another worker aborted.
-struct StageStamps {  // trace: when the first staging round was issued and when it landed
-  unsigned long long issue, landed;
+// One trace word of instruction i (MK_FLAG_TRACE runs): stored when it is taken, so that no stamp
+// stays live in registers across the instruction's body.
+DEV void tput(const KArgs& a, uint32_t i, int w, unsigned long long v) {
+  if (a.trace && lane() == 0) a.trace[((size_t)blockIdx.x * a.L + i) * kTraceWords + w] = (uint32_t)v;
+}
+struct StageStamps {  // trace: the instruction whose staging is stamped (words 12, 13: issued, landed)
+  uint32_t i;
 };
 
 DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, char* act, bool verify, uint32_t& polls,
@@ -777,7 +782,7 @@ DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, 
   for (int j = 0; j < 3; ++j)
     if (j < nrg) pend[j] = (1u << blocks_of(rg[j].bytes)) - 1u;  // at most 27 blocks
   const unsigned long long t0 = rtc();
-  if (a.flags & MK_FLAG_TRACE) ss.issue = t0;
+  if (a.flags & MK_FLAG_TRACE) tput(a, ss.i, 12, t0);
   for (uint32_t it = 1;; ++it) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -789,7 +794,7 @@ DEV bool ll_stage(const KArgs& a, const Instr& in, const LlRegion* rg, int nrg, 
       }
     }
     wait_vm0();
-    if ((a.flags & MK_FLAG_TRACE) && it == 1) ss.landed = rtc();
+    if ((a.flags & MK_FLAG_TRACE) && it == 1) tput(a, ss.i, 13, rtc());
     if (!verify) return true;
     bool done = true;
 #pragma unroll
@@ -1385,19 +1390,22 @@ DEV uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
 // fp32 sums keep full precision -- the e4m3 products of gfx950's fp8 instructions are summed at
 // lower internal precision, which the chain of per-token quantisations downstream amplifies.
 // Each 128-wide K block's sum is scaled by its weight block scale as it is added.
-template <bool FP8>
+// NQ, a compile-time bound so that the unrolled loop keeps its LDS reads ahead of the matrix-core
+// chain (a run-time bound cost the bf16 16-row layer 12 %): bf16, the K steps per half of the chunk
+// (8: chunk 512; 2: the main-MLA query BMM's 128); e4m3, the 128-wide scale blocks per half (4:
+// chunk 1024; 3: 768), or 0 for a bound read from the instruction
+template <bool FP8, int NQ>
 DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const uint32_t ln = lane(), nb = (uint32_t)wv & 3u, kh = (uint32_t)wv >> 2;
   const char* act = smem + kActOff + kActA;
   const char* ring = smem + kRingOff;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const uint32_t kc = in.w[W_LAYER + 6];
-  if (!FP8) {  // K chunk of kc / 32 steps of 32 (512 for the Qwen3 layers, 128 for the main-MLA BMM)
-    const uint32_t nq = kc >> 6, bpn = kc >> 5;  // steps per half, steps per 16-row block
+  if (!FP8) {  // K chunk of 2 NQ steps of 32
+    constexpr uint32_t bpn = 2u * NQ;  // steps per 16-row block
 #pragma unroll
-    for (uint32_t i = 0; i < 8; ++i) {
-      if (i >= nq) break;
-      const uint32_t q = kh * nq + i;
+    for (uint32_t i = 0; i < (uint32_t)NQ; ++i) {
+      const uint32_t q = kh * NQ + i;
       const bf16x8 av = *(const bf16x8*)(act + q * 1024u + ln * 16u);
       const bf16x8 bv = *(const bf16x8*)(ring + ring_off(lease, (nb * bpn + q) * 1024u + ln * 16u));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
@@ -1409,10 +1417,10 @@ DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, 
     const uint32_t tr0 = nb * 16u;
     const uint32_t grow = kind == K_GU && tr0 >= 32u ? (uint32_t)a.sh.I + n0 + tr0 - 32u : n0 + tr0;
     const float* sw = (const float*)s_ld64(row + GM_SW) + (size_t)(grow >> 7) * nkb + (k0 >> 7);
-    const uint32_t nkh = kc >> 8;  // 128-wide scale blocks per half of the chunk (kc 1024: 4, 768: 3)
+    const uint32_t nkh = NQ ? (uint32_t)NQ : kc >> 8;  // 128-wide scale blocks per half of the chunk
 #pragma unroll
-    for (uint32_t kb = 0; kb < 4; ++kb) {  // the wave's scale blocks, two 64-k steps each
-      if (kb >= nkh) break;
+    for (uint32_t kb = 0; kb < (NQ ? (uint32_t)NQ : 4u); ++kb) {  // the wave's scale blocks, two 64-k steps each
+      if (!NQ && kb >= nkh) break;
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (uint32_t h = 0; h < 2; ++h) {
@@ -1433,13 +1441,15 @@ DEV void gemm_tile(const KArgs& a, const Instr& in, char* smem, uint32_t lease, 
 // each group's input chunk straight from the workspace (operand order, device-scope loads: the
 // chunk would not fit the activation area for all groups), sums the whole K chunk and stores the
 // group's 16 x 16 partial sums itself, [tile][chunk][group][row block][lane][4].
-template <bool FP8>
+// NST: the chunk's 1 KiB steps (16: bf16 chunk 512, e4m3 chunk 1024)
+template <bool FP8, int NST>
 DEV void gemm_tile_groups(const KArgs& a, const Instr& in, const char* smem, uint32_t lease, int wv) {
   const uint32_t ln = lane(), nb = (uint32_t)wv & 3u;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const uint32_t kind = in.w[W_LAYER + 1], j = in.w[W_LAYER + 2], n0 = in.w[W_LAYER + 3], k0 = in.w[W_LAYER + 5];
   const uint32_t kc = in.w[W_LAYER + 6], K = proj_k(a.sh, kind), G = (uint32_t)a.sh.rg;
-  const uint32_t nst = FP8 ? kc >> 6 : kc >> 5;  // 1 KiB steps of the chunk: 16 (512 bf16, 1024 e4m3) or 12
+  constexpr uint32_t nst = NST;
+  static_assert(NST == 16, "two halves of 8 steps");
   const uint32_t gstride = FP8 ? K * 16u : K * 32u;
   const char* ring = smem + kRingOff;
   __amdgpu_buffer_rsrc_t ra = rsrc((const char*)s_ld64(row + GM_ACT) + (FP8 ? k0 >> 6 : k0 >> 5) * 1024u);
@@ -1451,33 +1461,33 @@ DEV void gemm_tile_groups(const KArgs& a, const Instr& in, const char* smem, uin
     sw = (const float*)s_ld64(row + GM_SW) + (size_t)(grow >> 7) * (K >> 7) + (k0 >> 7);
   }
   for (uint32_t gi = (uint32_t)wv >> 2; gi < G; gi += 2u) {
-    u32x4 av[16];
-#pragma unroll
-    for (uint32_t q = 0; q < 16; ++q) av[q] = ld128(ra, gi * gstride + min(q, nst - 1u) * 1024u + ln * 16u);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (!FP8) {
 #pragma unroll
-      for (uint32_t q = 0; q < 16; ++q) {  // guarded, not cut short: av stays in registers
-        if (q < nst) {
-          const bf16x8 bv = *(const bf16x8*)(ring + ring_off(lease, (nb * nst + q) * 1024u + ln * 16u));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8)av[q], bv, acc, 0, 0, 0);
+    for (uint32_t hh = 0; hh < 2; ++hh) {  // the chunk in two halves of 8 steps: 32 registers of input each
+      u32x4 av[8];
+#pragma unroll
+      for (uint32_t i = 0; i < 8; ++i) av[i] = ld128(ra, gi * gstride + (hh * 8u + i) * 1024u + ln * 16u);
+      if (!FP8) {
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+          const bf16x8 bv = *(const bf16x8*)(ring + ring_off(lease, (nb * nst + hh * 8u + i) * 1024u + ln * 16u));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8)av[i], bv, acc, 0, 0, 0);
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (uint32_t kb = 0; kb < 8; ++kb) {  // 128-wide scale blocks, two 64-k steps each
-        if (2u * kb < nst) {
+        for (uint32_t kb = 0; kb < 4; ++kb) {  // 128-wide scale blocks, two 64-k steps each
           f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (uint32_t h = 0; h < 2; ++h) {
-            const uint32_t q = 2u * kb + h;
-            const u32x4 bv = *(const u32x4*)(ring + ring_off(lease, (nb * nst + q) * 1024u + ln * 16u));
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av[q].x, av[q].y), e4m3x8_bf16(bv.x, bv.y), t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av[q].z, av[q].w), e4m3x8_bf16(bv.z, bv.w), t, 0, 0, 0);
+            const uint32_t i = 2u * kb + h;
+            const u32x4 bv = *(const u32x4*)(ring + ring_off(lease, (nb * nst + hh * 8u + i) * 1024u + ln * 16u));
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av[i].x, av[i].y), e4m3x8_bf16(bv.x, bv.y), t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(av[i].z, av[i].w), e4m3x8_bf16(bv.z, bv.w), t, 0, 0, 0);
           }
-          acc += c_ld<float>(sw + kb) * t;
+          acc += c_ld<float>(sw + hh * 4u + kb) * t;
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // the next half's loads after this half's products: bounded registers
     }
     st128(rp, gi * 4096u + (nb * 64u + ln) * 16u,
           u32x4{__float_as_uint(acc.x), __float_as_uint(acc.y), __float_as_uint(acc.z), __float_as_uint(acc.w)});
@@ -1488,14 +1498,14 @@ DEV void gemm_tile_groups(const KArgs& a, const Instr& in, const char* smem, uin
 // controller: add the two K halves of each row block and store the tile's partial sums
 // [chunk][row block][lane][4] (element (m, c) of the 16 x 64 tile at lane c % 16 + 16 (m / 4) of
 // block c / 16, position m % 4), then signal
-template <bool RG>
+template <bool LD, bool RG>
 DEV void gemm_epilogue(const KArgs& a, const Instr& in, const char* smem) {
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const uint32_t kind = in.w[W_LAYER + 1], j = in.w[W_LAYER + 2], k0 = in.w[W_LAYER + 5];
   const uint32_t kc = in.w[W_LAYER + 6], nk = proj_k(a.sh, kind) / kc;
   const char* D = smem + kActOff + kActD;
   const uint32_t ln = lane();
-  if (kind == K_UK) {  // the main-MLA query BMM is one chunk: its tile is final, bf16 q_lat [M][heads][512]
+  if (!LD && kind == K_UK) {  // the main-MLA query BMM is one chunk: its tile is final, bf16 q_lat [M][heads][512]
     const uint32_t n0 = in.w[W_LAYER + 3], h = n0 / (uint32_t)kMlaLatent, c0 = n0 % (uint32_t)kMlaLatent;
     __amdgpu_buffer_rsrc_t ro = rsrc((const void*)s_ld64(row + GM_PART));
 #pragma unroll
@@ -2230,27 +2240,36 @@ DEV void topk_row(const KArgs& a, const Instr& in, int wv) {
   wait_vm0();
 }
 
-// LD: the instance with loader waves (the Qwen3 layers), which never runs the indexer's top-k: its
-// code stays out of that instance's register allocation
+// LD: the instance with loader waves (the Qwen3 layers), which never runs the indexer's ops (key
+// cache, score, top-k, the D1 / D0 finalizes, the main-MLA BMM): their code stays out of that
+// instance's register allocation (with them in, it spilled 492 scalar registers instead of 298).
+// RG: plans of more than 16 rows (row-group GEMM tiles and finalizes).
 template <bool LD, bool RG>
 DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, int wv) {
   const uint32_t op = in.w[W_OPCODE];
   if (op == OP_GEMM) {
     if constexpr (RG) {  // plans of more than 16 rows: their own kernel instance
-      if (a.sh.fp8) gemm_tile_groups<true>(a, in, smem, lease, wv);
-      else gemm_tile_groups<false>(a, in, smem, lease, wv);
+      // 16 steps of 1 KiB: bf16 chunks are always 512 wide, and the planner takes e4m3 plans beyond
+      // 16 rows only with chunks of 1024
+      if (a.sh.fp8) gemm_tile_groups<true, 16>(a, in, smem, lease, wv);
+      else gemm_tile_groups<false, 16>(a, in, smem, lease, wv);
     } else if (a.sh.fp8 && in.w[W_LAYER + 1] != K_UK) {
-      gemm_tile<true>(a, in, smem, lease, wv);
+      const uint32_t kc = in.w[W_LAYER + 6];  // the layers' e4m3 chunks are 1024; the indexer's 1024 or 768
+      if (LD || kc == 1024u) gemm_tile<true, 4>(a, in, smem, lease, wv);
+      else if (kc == 768u) gemm_tile<true, 3>(a, in, smem, lease, wv);
+      else gemm_tile<true, 0>(a, in, smem, lease, wv);
+    } else if (!LD && in.w[W_LAYER + 1] == K_UK) {  // the main-MLA query BMM (indexer front only)
+      gemm_tile<false, kMlaNope / 64>(a, in, smem, lease, wv);
     } else {
-      gemm_tile<false>(a, in, smem, lease, wv);
+      gemm_tile<false, 8>(a, in, smem, lease, wv);
     }
   } else if (op == OP_NORM) {
     if (a.sh.fp8) norm_row<true>(a, in, smem, lease, wv);
     else norm_row<false>(a, in, smem, lease, wv);
   } else if (op == OP_FIN) {
     const uint32_t nk = in.w[W_LAYER + 5];
-    if (in.w[W_LAYER + 1] == K_QI) fin_qi(a, in, wv);
-    else if (in.w[W_LAYER + 1] == K_QB) fin_qb(a, in, wv);
+    if (!LD && in.w[W_LAYER + 1] == K_QI) fin_qi(a, in, wv);
+    else if (!LD && in.w[W_LAYER + 1] == K_QB) fin_qb(a, in, wv);
     else if (nk <= 4) fin_tile<4, RG>(a, in, wv);
     else if (nk <= 8) fin_tile<8, RG>(a, in, wv);
     else if (nk <= 12) fin_tile<12, RG>(a, in, wv);
@@ -2259,12 +2278,13 @@ DEV void m16_body(const KArgs& a, const Instr& in, char* smem, uint32_t lease, i
     quant_row(a, in, smem, wv);
   } else if (op == OP_COMB) {
     comb_group(a, in, wv);
+  } else if (LD) {  // the indexer's ops below never run in the Qwen3 layers' loader instance
   } else if (op == OP_KCACHE) {
     kcache(a, in, wv);
   } else if (op == OP_SCORE) {
     score_tile(a, in, smem, lease, wv);
   } else if (op == OP_TOPK) {
-    if constexpr (!LD) topk_row(a, in, wv);
+    topk_row(a, in, wv);
   }
 }
 
@@ -2302,9 +2322,12 @@ DEV bool arrive(const KArgs& a, const Instr& in) {
   return last;
 }
 
-// controller timestamps of one instruction (trace build)
+// controller timestamps of one instruction (trace runs of the kernels without loader waves, whose
+// loader 0 uses these words): 5, 6 when its stores were acknowledged and its arrival resolved, 10, 11
+// when a split combine was staged and computed
 struct Stamps {
-  unsigned long long ack, arr, c1, c2;  // c1 / c2: split combine staged / computed
+  uint32_t i;
+  bool on;
 };
 
 // four consecutive attention-output elements k .. k + 3 of row r: M = 1 plans as tagged records of
@@ -2327,7 +2350,7 @@ DEV void o_store(const KArgs& a, const Instr& in, __amdgpu_buffer_rsrc_t ro, uin
 // Multi-row plans: the last split of a chain stores the chain's partial and signals the group's
 // event; a combine task reduces the group's chains.
 template <int S>
-DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) {
+DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, const Stamps& st) {
   const Shapes& sh = a.sh;
   const int g = sh.g;
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
@@ -2356,9 +2379,9 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
   }
   if (S == 1) return false;  // multi-row plans: the controller completes the stores and signals later
   wait_vm0();
-  if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
+  if (st.on) tput(a, st.i, 5, rtc());
   const bool last = arrive(a, in);
-  if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
+  if (st.on) tput(a, st.i, 6, rtc());
   if (!last) return false;
   // combine the group's splits, o = sum_i exp(lse_i - lse) O_i with lse = log sum_i exp(lse_i)
   // o: tagged records of bf16 pairs, [request][Hq * 128 / 2]
@@ -2370,7 +2393,7 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
     // accumulate the outputs in split order
     stage(part + gbase, (uint32_t)ns * pstride * 4u, act);
     wait_vm0();
-    if (a.flags & MK_FLAG_TRACE) st.c1 = rtc();
+    if (st.on) tput(a, st.i, 10, rtc());
     const float* pl = (const float*)act;
     float* wts = (float*)(smem + kOutOff);  // [64][kMaxG] normalised weights
     const int ln = (int)lane();
@@ -2391,7 +2414,7 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
         o_store<S>(a, in, ro, (uint32_t)r, kbase + (uint32_t)oi, acc, otag);
       }
     }
-    if (a.flags & MK_FLAG_TRACE) st.c2 = rtc();
+    if (st.on) tput(a, st.i, 11, rtc());
     return true;
   }
   // many splits: online over chunks of splits staged into LDS: lanes over splits take the
@@ -2413,7 +2436,7 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
     const int nc = min((int)chunk, ns - t0);
     stage(part + gbase + (uint32_t)t0 * pstride, (uint32_t)nc * pstride * 4u, act);
     wait_vm0();
-    if ((a.flags & MK_FLAG_TRACE) && t0 == 0) st.c1 = rtc();
+    if (st.on && t0 == 0) tput(a, st.i, 10, rtc());
     const float* pl = (const float*)act;
     for (int j = 0; j < g; ++j) {
       const float lv = ln < nc ? pl[ln * pstride + g * 128 + j] : -INFINITY;
@@ -2450,7 +2473,7 @@ DEV bool attn_epilogue(const KArgs& a, const Instr& in, char* smem, Stamps& st) 
       }
     }
   }
-  if (a.flags & MK_FLAG_TRACE) st.c2 = rtc();
+  if (st.on) tput(a, st.i, 11, rtc());
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int unit = ln + 64 * u;
@@ -2481,7 +2504,7 @@ struct LmState {
   int idx;
 };
 
-DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmState& lm, Stamps& st) {
+DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmState& lm, const Stamps& st) {
   const uint32_t op = in.w[W_OPCODE];
   const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
   const int n0 = in.w[W_P1], nr = in.w[W_P2];
@@ -2543,9 +2566,9 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
       st32(rp, slot * 8u + 4u, (uint32_t)lm.idx);
     }
     wait_vm0();
-    if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
+    if (st.on) tput(a, st.i, 5, rtc());
     const bool last = arrive(a, in);
-    if (a.flags & MK_FLAG_TRACE) st.arr = rtc();
+    if (st.on) tput(a, st.i, 6, rtc());
     if (!last) return;
     const uint32_t n = in.w[W_ARR_N];
     best = -INFINITY;
@@ -2575,7 +2598,7 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
     wait_vm0();
     return;
   }
-  if (a.flags & MK_FLAG_TRACE) st.ack = rtc();
+  if (st.on) tput(a, st.i, 5, rtc());
 }
 
 // ---------------------------------------------------------------------------------------
@@ -2695,7 +2718,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     }
     constexpr bool m16 = S == 1;
     const bool tracing = a.flags & MK_FLAG_TRACE;
-    const unsigned long long t_vis = tracing ? rtc() : 0;
+    if (tracing) tput(a, (uint32_t)i, 0, rtc());
     const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
     const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
     const uint64_t row_touch = s_ld64(row);  // the pointer row into the scalar cache before the epilogue reads it
@@ -2704,8 +2727,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     // already guarantees them, so it stages without checking tags)
     uint32_t poll = 0;
     bool ok = true;
-    StageStamps sst{0, 0};
-    unsigned long long t_ev = 0, t_ld = 0;  // multi-row trace: events met, staging done
+    StageStamps sst{(uint32_t)i};
     if constexpr (m16) {
       // multi-row: wait for the event counters (the graph baseline's stream order guarantees them),
       // then stage what the op reads from LDS
@@ -2715,12 +2737,12 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
         pending = false;
       }
       ok = graph || wait_events(a, in, poll, wc);
-      if (tracing) t_ev = rtc();
+      if (tracing) tput(a, (uint32_t)i, 14, rtc());  // multi-row: events met
       if (ok && op == OP_ATTN && (in.w[W_CHAIN] & 1u) == 0u) ok = attn_stage(a, in, act, false, poll, sst);  // a chain's first split
       if (ok && op == OP_GEMM) gemm_stage<RG>(a, in, act, staged);
       if (ok && op == OP_SCORE) score_stage(a, in, act);
       if (op != OP_GEMM) staged = 0;
-      if (tracing) t_ld = rtc();
+      if (tracing) tput(a, (uint32_t)i, 15, rtc());  // multi-row: staging done
       if (LD && ok && !wait_loaders(smem, i)) {  // the loaders' shares of this lease
         record_timeout(a, in, 0xB0u, 0u);
         ok = false;
@@ -2739,13 +2761,15 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     else if (fused_norm)
       ok = norm_prologue(a, in, row, act, smem, !graph, noop_only, poll, sst);
     last_row = in.w[W_ROW];
-    const unsigned long long t_ready = tracing ? rtc() : 0;
-    Stamps st{0, 0, 0, 0};
+    if (tracing) {
+      const unsigned long long t_ready = rtc();
+      tput(a, (uint32_t)i, 1, t_ready);
+      tput(a, (uint32_t)i, 2, t_ready);
+    }
+    const Stamps st{(uint32_t)i, tracing && !LD};
     if (!ok && lane() == 0) ctrl[0] = 1u;
-    const unsigned long long t_pro = t_ready;
     lds_barrier();  // A: activations staged, prefetch of this instruction landed
-    const unsigned long long t_a = tracing ? rtc() : 0;
-    const unsigned long long c_a = tracing ? __builtin_readcyclecounter() : 0;
+    if (tracing) tput(a, (uint32_t)i, 3, rtc());
     if (!ok) break;
     if (m16 && uni(ctrl[0]) != 0u) {  // a barrier or a loader of this block gave up (watchdog)
       record_timeout(a, in, 0xBAu, 0u);
@@ -2762,15 +2786,14 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     }
     lds_barrier();  // B: compute done, results in the output area
     if (m16 && lane() == 0) *(volatile uint32_t*)(smem + kCtrlOff + kRetiredOff) = (uint32_t)i + 1u;  // its pages are free
-    const unsigned long long t_b = tracing ? rtc() : 0;
-    const unsigned long long c_b = tracing ? __builtin_readcyclecounter() : 0;
+    if (tracing) tput(a, (uint32_t)i, 4, rtc());
     if constexpr (m16) {
       // stores only; norm / finalize / quantise / combine / key-cache / score bodies completed theirs
       // in every wave before B
       if (op == OP_ATTN)
         attn_epilogue<S>(a, in, smem, st);
       else if (op == OP_GEMM)
-        gemm_epilogue<RG>(a, in, smem);
+        gemm_epilogue<LD, RG>(a, in, smem);
       pend = sig_of(in);
       pending = true;
     } else if (op == OP_ATTN) {
@@ -2779,28 +2802,9 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
       gemv_epilogue(a, in, smem, lm, st);
     }
     asm volatile("" ::"s"(row_touch));
-    if (tracing && a.trace && lane() == 0) {
-      uint32_t* tr = a.trace + ((size_t)blockIdx.x * a.L + i) * kTraceWords;
-      tr[0] = (uint32_t)t_vis;
-      tr[1] = (uint32_t)t_ready;
-      tr[2] = (uint32_t)t_pro;
-      tr[3] = (uint32_t)t_a;
-      tr[4] = (uint32_t)t_b;
-      if (!LD) {  // with loader waves: loader 0's issue and landing times of this lease
-        tr[5] = (uint32_t)st.ack;
-        tr[6] = (uint32_t)st.arr;
-      }
-      tr[7] = (uint32_t)rtc();
-      tr[8] = poll;
-      tr[9] = (uint32_t)(c_b - c_a);  // shader clock cycles between the two compute barriers
-      if (!LD) {  // with loader waves: loader 0's first look at this lease and when its pages were free
-        tr[10] = (uint32_t)st.c1;
-        tr[11] = (uint32_t)st.c2;
-      }
-      tr[12] = (uint32_t)sst.issue;
-      tr[13] = (uint32_t)sst.landed;
-      tr[14] = (uint32_t)t_ev;
-      tr[15] = (uint32_t)t_ld;
+    if (tracing) {
+      tput(a, (uint32_t)i, 7, rtc());
+      tput(a, (uint32_t)i, 8, poll);
     }
   }
   if (pending) {  // the last instruction's signals
@@ -2815,6 +2819,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
   constexpr bool loaders = LD;  // loader waves stream the leases
   uint32_t* lease_tab = (uint32_t*)(smem + kCtrlOff + kLeaseTabOff) + cw * 32;  // [16] lease, [16] issued_end
   const bool noop_only = a.flags & MK_FLAG_NOOP_ONLY;
+  const bool stamp = cw == 0 && (a.flags & MK_FLAG_TRACE) && a.trace;  // lease issue times into trace word 9
   const int lookahead = (a.flags & MK_FLAG_NO_PREFETCH) ? 0 : 15;
   uint32_t head = 0, issued = 0;
   uint32_t last_row = 0xFFFFFFFFu;  // as in the controller: the lm_head norm runs once per worker
@@ -2855,6 +2860,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
         // memory pipeline, so leases beyond kLookPages pages from instruction i's wait
         if (pf_i > i && head + npg - uni(lease_tab[i & 15]) > (uint32_t)kLookPages) break;
         pf_issue<S>(a, pf, head, cw, issued, smem);
+        if (stamp && lane() == 0) a.trace[((size_t)blockIdx.x * a.L + pf_i) * kTraceWords + 9] = (uint32_t)rtc();
         lease_tab[pf_i & 15] = head;
         lease_tab[16 + (pf_i & 15)] = issued;
         head += npg;
@@ -2899,6 +2905,7 @@ DEV void compute(const KArgs& a, const uint32_t* base, int count, int stride, in
         if (head + npg - freed > (uint32_t)kNPages) break;
         if (pf_i > i + 1 && head + npg - uni(lease_tab[(i + 1) & 15]) > (uint32_t)kLookPages) break;
         pf_issue<S>(a, pf, head, cw, issued, smem);
+        if (stamp && lane() == 0) a.trace[((size_t)blockIdx.x * a.L + pf_i) * kTraceWords + 9] = (uint32_t)rtc();
         lease_tab[pf_i & 15] = head;
         lease_tab[16 + (pf_i & 15)] = issued;
         head += npg;
