@@ -34,7 +34,7 @@ from typing import Dict
 import numpy as np
 
 from . import ops
-from .numerics import (bf16_bits_to_f64, dequant_per_token, dequant_weight_blocks, e4m3_ambiguous, e4m3_decode,
+from .numerics import (bf16_admissible, bf16_bits_to_f64, dequant_per_token, dequant_weight_blocks, e4m3_ambiguous, e4m3_decode,
                        e4m3_other_code, f64_to_bf16_bits, quant_per_token, round_bf16, round_f32)
 
 
@@ -69,6 +69,25 @@ def _quant(pre: np.ndarray, key: str, ties, out: Dict[str, np.ndarray]) -> tuple
     return np.where(other, e4m3_other_code(v, codes), codes), s
 
 
+def _round_bf16(pre: np.ndarray, key: str, ties) -> np.ndarray:
+    """bf16 materialisation of ``pre`` (round to nearest even).  Like ``_quant`` for the e4m3
+    codes: an evaluation that reproduces ``pre`` only to within delta may round it to any bf16
+    value that some value within delta of it rounds to, and one step of q, k or v moves that
+    head's logits and outputs.  ``ties`` (optional, with bf16 entries) gives delta from the
+    oracle's own values (``ties.bf16_delta(key, pre)``); where more than one bf16 value is
+    admissible the oracle takes the value ``ties.choose_bf16`` returns, and a value that is not
+    admissible, or differs where only one is, is an error."""
+    rne = round_bf16(pre)
+    if ties is None or not getattr(ties, "has_bf16", lambda k: False)(key):
+        return rne
+    lo, hi = bf16_admissible(pre, ties.bf16_delta(key, pre))
+    amb = lo != hi
+    chosen = np.asarray(ties.choose_bf16(key, pre, rne, amb), dtype=np.float64)
+    if np.any((chosen != rne) & ~amb) or np.any((chosen < lo) | (chosen > hi)):
+        raise ValueError(f"{key}: a bf16 value the oracle does not admit")
+    return chosen
+
+
 def _w8a8(cfg, inp, name, layer, codes, scale):
     return ops.linear_w8a8(e4m3_decode(codes), scale, e4m3_decode(inp[name][layer]), inp["s_" + name[2:]][layer])
 
@@ -78,7 +97,8 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     """One decode layer.  x: decoded bf16 values [M, H]; r_in: fp32 values [M, H].
     k_cache / v_cache: this layer's decoded caches [pages, P, Hkv, d] (updated in place
     with the new rows).  Rows are requests (one token per request).
-    ties: optional resolution of ambiguous FP8 decisions at "h1q", "oq", "h2q", "mq" (``_quant``)."""
+    ties: optional resolution of ambiguous FP8 decisions at "h1q", "oq", "h2q", "mq" (``_quant``) and
+    of the bf16 roundings of "q", "k", "v" (``_round_bf16``)."""
     H, d = cfg.hidden, cfg.head_dim
     Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
     g = Hq // Hkv
@@ -110,7 +130,7 @@ def qwen3_layer(cfg, inp: Dict[str, np.ndarray], layer: int, x: np.ndarray, r_in
     q_pre = ops.rope_neox(qn, pos[:, None], cfg.rope_theta)
     k_pre = ops.rope_neox(kn, pos[:, None], cfg.rope_theta)
     out["q_pre"], out["k_pre"], out["v_pre"] = q_pre, k_pre, v
-    qb, kb, vb = round_bf16(q_pre), round_bf16(k_pre), round_bf16(v)
+    qb, kb, vb = _round_bf16(q_pre, "q", ties), _round_bf16(k_pre, "k", ties), _round_bf16(v, "v", ties)
     out["q"], out["k"], out["v"] = qb, kb, vb
 
     page, off = ops.cache_slots(inp["block_table"], pos, req, cfg.page_size)

@@ -49,6 +49,42 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return np.where(np.abs(r) > bf16_max, np.sign(r) * np.inf, r)
 
 
+def bf16_enclosing(x: np.ndarray):
+    """(lo, hi): the adjacent bf16 magnitudes with lo <= |x| < hi (the finite range)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > a, e - 1, e)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= a, e + 1, e)
+    q = np.ldexp(1.0, (np.maximum(e, -126) - 7).astype(np.int64))  # the bf16 spacing at |x|
+    lo = np.floor(a / q) * q
+    return lo, lo + q
+
+
+def bf16_midpoint_margin(x: np.ndarray) -> np.ndarray:
+    """Distance from |x| to the midpoint of its enclosing bf16 pair, where round-to-nearest
+    changes its choice."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    lo, hi = bf16_enclosing(a)
+    return np.abs(a - 0.5 * (lo + hi))
+
+
+def bf16_other(x: np.ndarray, chosen: np.ndarray) -> np.ndarray:
+    """The other member of the bf16 pair enclosing x (with x's sign): the value a rounding on the
+    other side of the midpoint gives."""
+    x = np.asarray(x, dtype=np.float64)
+    lo, hi = bf16_enclosing(x)
+    other = np.where(np.abs(np.asarray(chosen, dtype=np.float64)) == lo, hi, lo)
+    return np.where(np.signbit(x), -other, other)
+
+
+def bf16_admissible(x: np.ndarray, delta: np.ndarray):
+    """(lo, hi): the least and greatest bf16 values that round-to-nearest gives for some value
+    within delta of x (rounding is monotone, so every bf16 value between them is one too)."""
+    x = np.asarray(x, dtype=np.float64)
+    return round_bf16(x - delta), round_bf16(x + delta)
+
+
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     r = round_bf16(x).astype(np.float32)  # exact: r has at most 8 significant bits
     return (r.view(np.uint32) >> 16).astype(np.uint16)

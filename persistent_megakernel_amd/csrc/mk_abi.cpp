@@ -242,6 +242,7 @@ void fill_table(const mk_plan* p, const mk_tensors* t, std::vector<uint64_t>& ta
         s[ATT_PART] = ws + region_off(hp, "part");
         s[ATT_O] = ob;
         s[ATT_ROPE] = (uint64_t)p->d_rope;
+        s[ATT_QB] = ws + region_off(hp, "qb");
         break;
       case OP_COMB:
         s[ATT_PART] = ws + region_off(hp, "part");

@@ -67,7 +67,8 @@ constexpr int kTableSlots = 16;
 // {payload, tag}; X / RIN are the caller's first-layer inputs, R2OUT / Y the caller's last-layer
 // outputs (0 on other layers).
 enum QkvSlot { QKV_W = 0, QKV_GAMMA, QKV_X, QKV_RIN, QKV_OUT, QKV_R1 };
-enum AttnSlot { ATT_QKV = 0, ATT_GQ, ATT_GK, ATT_KC, ATT_VC, ATT_BT, ATT_PART, ATT_O, ATT_ROPE };
+enum AttnSlot { ATT_QKV = 0, ATT_GQ, ATT_GK, ATT_KC, ATT_VC, ATT_BT, ATT_PART, ATT_O, ATT_ROPE,
+                ATT_QB };  // multi-row: the bf16 q heads after QK-norm and RoPE, [M][Hq][d] (read by the tests)
 enum OSlot { O_W = 0, O_IN, O_X, O_RIN, O_R2, O_R1, O_R2OUT };
 enum GuSlot { GU_W = 0, GU_GAMMA, GU_R2, GU_M };
 enum DownSlot { DN_W = 0, DN_M, DN_Y, DN_R2, DN_R1 };

@@ -1102,7 +1102,7 @@ DEV float rows4_sum(float v) {
 //   1. wave wv takes a contiguous block of at most 16 of the split's tokens and works on the matrix
 //      cores: S^T = K Q^T (16x16x32 bf16; token rows by key rows, head columns), the wave's maximum
 //      m_w and sum l_w per head over its tokens, P = exp(S - m_w) -- whose result layout is already
-//      the A operand of the next product -- and O_w = P V (16x16x16 bf16 on P's two bf16 parts);
+//      the A operand of the next product -- and O_w = P V (16x16x16 bf16 on P's three bf16 parts);
 //   2. the eight waves' (m_w, l_w, O_w) merge with weights exp(m_w - max m_w).
 // Output: the split's normalised O [G][128] and its lse [G] in the output area.
 // Multi-row plans deal a worker consecutive splits of one (request, kv head), a chain: step 0 runs
@@ -1128,6 +1128,14 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
   if (!cont) {
     if (wv < G) {
       qk_norm_rope(act + kAttQraw + wv * 1024, act + kAttGq, act + kAttRope, sh.eps, act + kActQ + wv * 256);
+      if (S == 1) {  // the q head as materialised in bf16, for the record (this lane wrote dims ln, ln + 64)
+        const uint16_t* qh = (const uint16_t*)(act + kActQ + wv * 256);
+        const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+        __amdgpu_buffer_rsrc_t rq = rsrc((const void*)s_ld64(row + ATT_QB));
+        const uint32_t h = in.w[W_LAYER + 1] * (uint32_t)sh.Hq + in.w[W_LAYER + 2] * (uint32_t)G + (uint32_t)wv;
+        st16(rq, (h * 128u + (uint32_t)ln) * 2u, qh[ln]);
+        st16(rq, (h * 128u + (uint32_t)ln + 64u) * 2u, qh[ln + 64]);
+      }
     } else if (wv == G) {
       qk_norm_rope(act + kAttKraw, act + kAttGk, act + kAttRope, sh.eps, act + kActK);
     } else if (wv == G + 1) {
@@ -1170,16 +1178,22 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
     lloc += p[e];
   }
   const float lw = rows4_sum(lloc);
-  // P V: A = P (lane: head sub, tokens 4 grp + e -- the layout the scores came in) as the sum of two
-  // bf16 parts, P = hi + lo, so the product keeps about 16 bits of P; B fragment c holds
+  // P V: A = P (lane: head sub, tokens 4 grp + e -- the layout the scores came in) as the sum of three
+  // bf16 parts, P = hi + lo + lo2 (each the nearest bf16 to what the parts before it leave, every
+  // remainder exact in fp32), so the product keeps about 24 bits of P, as an fp32 evaluation would
+  // (two parts carry 16 bits, and a sum of V rows of both signs cancels).  B fragment c holds
   // V[token 4 grp + e][dim 8 sub + c], taken from one 16-byte load per token (chunk sub of the row)
-  i16x4 pa, pl;
+  i16x4 pa, pl, pl2;
   {
     const u32x2 hw = {pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3])};
-    const u32x2 lw2 = {pack_bf2(p[0] - bf2f(hw[0] & 0xffffu), p[1] - bf2f(hw[0] >> 16)),
-                       pack_bf2(p[2] - bf2f(hw[1] & 0xffffu), p[3] - bf2f(hw[1] >> 16))};
+    const float r[4] = {p[0] - bf2f(hw[0] & 0xffffu), p[1] - bf2f(hw[0] >> 16), p[2] - bf2f(hw[1] & 0xffffu),
+                        p[3] - bf2f(hw[1] >> 16)};
+    const u32x2 lw2 = {pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3])};
+    const u32x2 lw3 = {pack_bf2(r[0] - bf2f(lw2[0] & 0xffffu), r[1] - bf2f(lw2[0] >> 16)),
+                       pack_bf2(r[2] - bf2f(lw2[1] & 0xffffu), r[3] - bf2f(lw2[1] >> 16))};
     __builtin_memcpy(&pa, &hw, 8);
     __builtin_memcpy(&pl, &lw2, 8);
+    __builtin_memcpy(&pl2, &lw3, 8);
   }
   u32x4 vv[4];
 #pragma unroll
@@ -1201,8 +1215,9 @@ DEV void attn_body(const KArgs& a, const Instr& in, const char* smem, char* act,
     }
     i16x4 b;
     __builtin_memcpy(&b, &bw, 8);
-    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl2, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, b, o[c], 0, 0, 0);
+    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, b, o[c], 0, 0, 0);
   }
   // O_w[head 4 grp + i][dim 8 sub + c] is element i of o[c]
   float* mrg = (float*)(act + kActMerge);  // [wave][G][128] partial P V, then [wave][G] (m_w, l_w)

@@ -635,6 +635,7 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
     const size_t G = (size_t)(M + 15) / 16, rows = 16 * G;  // 16-row groups of the operand order
     region("qkv", (size_t)M * n_qkv * 8);
     region("part", (size_t)R * Hkv * max_splits * (g * d + 8) * 4);
+    region("qb", (size_t)M * Hq * d * 2);  // the attention's bf16 q heads, as materialised
     region("r1", (size_t)M * H * 4);
     region("r2", (size_t)M * H * 4);
     region("y", (size_t)M * H * 2);

@@ -21,11 +21,9 @@ fp32 values (o, m) from the oracle's are quoted for comparison:
 * h1q, hq -- RMSNorm of inputs both sides hold bit for bit: an fp32 mean square over at most
   6144 terms summed in a tree (relative error <= (log2 n + 8) 2^-24, about 1.3e-6), one reciprocal
   square root and three roundings: relative 2^-16 leaves a margin of ten and more;
-* oq -- attention output: the kernel carries the softmax weights as two bf16 parts (16
-  significant bits, relative 2^-17 each) summed in fp32 over up to 8192 tokens, and q, k, v are
-  materialised in bf16 on both sides (a q value within fp32 error of a bf16 midpoint may round
-  either way, moving that head's logits): absolute 2^-8 code units (measured: largest deviation
-  3.1e-3, rms 2e-4 code units, ambiguous codes seen at <= 1.9e-4);
+* oq -- attention output: the kernel carries the softmax weights as three bf16 parts (24
+  significant bits) summed in fp32 over up to 8192 tokens: absolute 2^-8 code units (measured
+  before the bf16 decisions below were resolved: largest deviation 3.1e-3, rms 2e-4 code units);
 * h2q, mq, qaq, kq -- fp32 projection sums over <= 12288 products (per 128-block partials times
   the block scales), then RMSNorm, SiLU-mul or RoPE in fp32: relative 2^-14 plus absolute 2^-12
   code units (measured for m: largest deviation 8.9e-5, rms 4e-6).
@@ -36,7 +34,7 @@ from typing import Dict, Tuple
 
 import numpy as np
 
-from oracle.numerics import e4m3_decode, e4m3_other_code
+from oracle.numerics import bf16_admissible, e4m3_decode, e4m3_other_code
 
 DELTA: Dict[str, Tuple[float, float]] = {
     "h1q": (2.0 ** -16, 2.0 ** -20), "hq": (2.0 ** -16, 2.0 ** -20),
@@ -47,16 +45,58 @@ DELTA: Dict[str, Tuple[float, float]] = {
 SCALE_RTOL = 2e-6
 MAX_AMBIGUOUS = 0.02
 
+# bf16 decisions on the way to a quantisation point: q and k after QK-norm and RoPE, v as
+# projected, each materialised in bf16 on both sides.  A value within fp32 error of a bf16
+# midpoint may round either way (measured at 256 rows: one element in about 12,000 of k and v, and
+# a q element taken the other way moved a token's attention output by 1e-4 of its largest element,
+# fifty times SCALE_RTOL at oq).  The kernel's q (written to the workspace as it materialises it),
+# k and v (the written cache rows) are checked like the codes: its value must be the bf16 rounding
+# of some value within delta of the oracle's (the oracle's own round-to-nearest-even value wherever
+# that admits only one), and the oracle continues with the kernel's value where several are
+# admissible.  delta = delta_rel |x| + delta_abs rms(head).  The flip rate measured at 256 rows (one
+# value in about 12,000 of k and v rounded the other way) puts the kernel's error near 2^-23 of a
+# value: q, k (an RMSNorm over 128 dims and a rotation in fp32): 2^-18 relative and 2^-19 of the
+# head's rms for the rotation's cancellation, which leaves elements near zero with several
+# admissible values; v (an fp32 projection sum over the hidden size): 2^-17 and 2^-20.
+BF16_DELTA: Dict[str, Tuple[float, float]] = {"q": (2.0 ** -18, 2.0 ** -19), "k": (2.0 ** -18, 2.0 ** -19),
+                                              "v": (2.0 ** -17, 2.0 ** -20)}
+MAX_AMBIGUOUS_BF16 = 0.04
+
 
 class KernelTies:
     """The oracle's ``ties`` argument for one kernel run: at each quantisation point it checks
     the kernel's codes and scales (the rule above) and takes the kernel's choice inside the
     oracle's ambiguity set.  ``kernel``: {point: (codes [rows, K] uint8, scales [rows])}."""
 
-    def __init__(self, kernel: Dict[str, Tuple[np.ndarray, np.ndarray]], delta=None):
+    def __init__(self, kernel: Dict[str, Tuple[np.ndarray, np.ndarray]], delta=None,
+                 bf16: Dict[str, np.ndarray] = None):
         self.kernel = kernel
         self._delta = dict(DELTA if delta is None else delta)
+        self.bf16 = dict(bf16 or {})  # {"q" | "k" | "v": the kernel's bf16 values as float64}
         self.report: Dict[str, Dict[str, int]] = {}
+
+    def has_bf16(self, key: str) -> bool:
+        return key in self.bf16
+
+    def bf16_delta(self, key: str, pre: np.ndarray) -> np.ndarray:
+        rel, ab = BF16_DELTA[key]
+        rms = np.sqrt(np.mean(np.square(pre), axis=-1, keepdims=True))
+        return rel * np.abs(pre) + ab * rms
+
+    def choose_bf16(self, key, pre, rne, ambiguous):
+        kv = np.asarray(self.bf16[key], dtype=np.float64)
+        assert kv.shape == rne.shape, f"{key}: shapes {kv.shape} {rne.shape}"
+        differ = kv != rne
+        outside = int(np.sum(differ & ~ambiguous))
+        assert outside == 0, (f"{key}: {outside} of {rne.size} bf16 values differ from the oracle's "
+                              f"round-to-nearest-even value where it admits no other")
+        lo, hi = bf16_admissible(pre, self.bf16_delta(key, pre))
+        bad = int(np.sum(differ & ((kv < lo) | (kv > hi))))
+        assert bad == 0, f"{key}: {bad} values are not the rounding of any value within delta of the oracle's"
+        n_amb = int(np.sum(ambiguous))
+        self.report[key] = {"flipped": int(np.sum(differ)), "ambiguous": n_amb, "elements": int(rne.size)}
+        assert n_amb <= MAX_AMBIGUOUS_BF16 * rne.size, f"{key}: ambiguity set {n_amb} of {rne.size} is too large"
+        return np.where(differ, kv, rne)
 
     def delta(self, key: str) -> Tuple[float, float]:
         return self._delta[key]

@@ -113,3 +113,89 @@ def test_oracle_refuses_a_choice_outside_its_ambiguity_set():
 
     with pytest.raises(ValueError, match="outside the oracle's ambiguity set"):
         model._quant(pre, "mq", Greedy(), {})
+
+
+# --- bf16 decisions (q, k, v on the way to the oq quantisation) ---
+
+def test_bf16_enclosing_margin_and_other():
+    from oracle.numerics import bf16_enclosing, bf16_midpoint_margin, bf16_other, round_bf16
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 2.0 ** -9, -3.0, 255.5, 2.0 ** -130])
+    lo, hi = bf16_enclosing(x)
+    assert list(lo) == [1.0, 1.0, 1.0, 3.0, 255.0, 2.0 ** -130]
+    assert list(hi) == [1.0 + 2.0 ** -7, 1.0 + 2.0 ** -7, 1.0 + 2.0 ** -7, 3.0 + 2.0 ** -6, 256.0, 2.0 ** -130 + 2.0 ** -133]
+    assert list(bf16_midpoint_margin(x)) == [2.0 ** -8, 0.0, 2.0 ** -9, 2.0 ** -7, 0.0, 2.0 ** -134]
+    assert list(bf16_other(x, round_bf16(x))) == [1.0 + 2.0 ** -7, 1.0 + 2.0 ** -7, 1.0 + 2.0 ** -7, -(3.0 + 2.0 ** -6),
+                                                  255.0, 2.0 ** -130 + 2.0 ** -133]
+    rng = np.random.default_rng(4)
+    y = rng.standard_normal(10000) * 10.0 ** rng.uniform(-3, 3, 10000)
+    r = round_bf16(y)
+    lo, hi = bf16_enclosing(y)
+    assert np.all((np.abs(r) == lo) | (np.abs(r) == hi))  # RNE picks one of the pair
+    o = bf16_other(y, r)
+    assert np.all(np.abs(o) != np.abs(r)) and np.all(np.sign(o) == np.sign(y))
+    assert np.all(np.abs(np.abs(y) - np.abs(r)) <= np.abs(np.abs(y) - np.abs(o)))  # RNE is the nearer one
+
+
+def _bf16_run(pre, kernel_vals, key="q"):
+    ties = KernelTies({}, bf16={key: kernel_vals})
+    return ties, model._round_bf16(pre, key, ties)
+
+
+def test_bf16_rne_with_fp32_sized_errors_passes_and_is_followed():
+    from oracle.numerics import round_bf16
+    rng = np.random.default_rng(5)
+    pre = rng.standard_normal((16, 8, 128))
+    noisy = pre * (1.0 + rng.uniform(-2e-7, 2e-7, pre.shape))  # an fp32 evaluation of the same values
+    k = round_bf16(noisy)
+    ties, got = _bf16_run(pre, k)
+    assert np.array_equal(got, k)  # the kernel's choice where ambiguous, the oracle's own elsewhere (equal)
+    r = ties.report["q"]
+    assert r["flipped"] <= r["ambiguous"] <= 0.04 * pre.size
+
+
+def test_bf16_near_zero_admits_several_values():
+    """An element whose size is comparable to the absolute evaluation error admits more than the
+    enclosing pair: a value two bf16 steps from the oracle's there is accepted and followed."""
+    from oracle.numerics import bf16_admissible, round_bf16
+    rng = np.random.default_rng(8)
+    pre = rng.standard_normal((2, 2, 128))
+    pre[0, 0, 5] = 3e-7  # rms ~ 1: delta_abs 2^-18 ~ 3.8e-6 spans many bf16 steps here
+    ties = KernelTies({}, bf16={"q": round_bf16(pre)})
+    lo, hi = bf16_admissible(pre, ties.bf16_delta("q", pre))
+    k = round_bf16(pre)
+    k[0, 0, 5] = lo[0, 0, 5]  # several steps below the oracle's value, still admissible
+    assert k[0, 0, 5] != round_bf16(pre)[0, 0, 5]
+    ties = KernelTies({}, bf16={"q": k})
+    got = model._round_bf16(pre, "q", ties)
+    assert got[0, 0, 5] == lo[0, 0, 5] and np.array_equal(np.delete(got, 5), np.delete(round_bf16(pre), 5))
+
+
+@pytest.mark.parametrize("codec", ["truncate", "two_steps", "away"])
+def test_bf16_wrong_rounding_is_rejected(codec):
+    from oracle.numerics import bf16_enclosing, bf16_other, round_bf16
+    rng = np.random.default_rng(6)
+    pre = rng.standard_normal((16, 8, 128))
+    lo, hi = bf16_enclosing(pre)
+    if codec == "truncate":
+        k = np.sign(pre) * lo
+    elif codec == "away":
+        k = np.sign(pre) * hi
+    else:  # the RNE value moved by two spacings on one element far from any midpoint
+        k = round_bf16(pre)
+        k.flat[7] += 2 * (hi.flat[7] - lo.flat[7]) * np.sign(pre.flat[7])
+    with pytest.raises(AssertionError):
+        _bf16_run(pre, k)
+
+
+def test_bf16_choice_outside_the_ambiguity_set_is_refused():
+    from oracle.numerics import round_bf16
+
+    from oracle.numerics import bf16_other
+
+    class Rogue(KernelTies):
+        def choose_bf16(self, key, pre, rne, ambiguous):
+            return np.where(ambiguous, rne, bf16_other(pre, rne))  # every unambiguous element the other way
+
+    pre = np.random.default_rng(7).standard_normal((4, 2, 128))
+    with pytest.raises(ValueError):
+        model._round_bf16(pre, "k", Rogue({}, bf16={"k": round_bf16(pre)}))

@@ -188,10 +188,12 @@ def _check_mla(run, ref, ind, tag):
 
 
 def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True), ("mk", False)),
-          W=0, intermediates=True):
+          W=0, intermediates=True, edit=None):
     from gpu_helpers import IndexerRun
     inp = make_inputs(cfg, seed=seed)
     inp["context_lens"] = np.array(ctx, dtype=np.int32)
+    if edit is not None:
+        edit(inp)
     kc0, ks0 = inp["key_cache"].copy(), inp["key_scale"].astype(np.float64).copy()
     run = IndexerRun(cfg, inp, num_workers=W)
     outs, outs_k = [], []
@@ -218,6 +220,7 @@ def _case(cfg, ctx, seed, modes=(("mk", False), ("graph", False), ("graph", True
     nk = len(outs_k) // len(modes)  # per mode: [top-k], [q_lat]
     for i in range(nk, len(outs_k)):
         assert torch.equal(outs_k[i], outs_k[i % nk])
+    return outs_k[0] if cfg.topk else None
 
 
 @pytest.mark.parametrize("R,T,ctx,W", [(2, 8, [300, 133], 0), (3, 5, [64, 196, 5], 37)])
@@ -239,6 +242,30 @@ def test_indexer_topk_reduced(R, T, ctx, W, k):
     cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, n_requests=R,
                               tokens_per_request=T, context=max(ctx), topk=k)
     _case(cfg, ctx, seed=12, W=W, intermediates=False)
+
+
+@pytest.mark.parametrize("k", [64, 250])
+def test_indexer_topk_ties(k):
+    """Every prior key of every request identical (the same e4m3 codes and scale): each token's
+    scores over its prior keys are exactly equal, so its selection is decided by the tie rule --
+    the prior keys it takes are the first ones, positions 0, 1, ... -- besides its own request's
+    new keys, whichever of them score above the tie."""
+    R, T, ctx = 2, 8, [300, 133]
+    cfg = dataclasses.replace(get_config("indexer_front"), hidden=1024, idx_q_rank=512, n_requests=R,
+                              tokens_per_request=T, context=max(ctx), topk=k)
+
+    def same_keys(inp):
+        inp["key_cache"][:] = inp["key_cache"].reshape(-1, inp["key_cache"].shape[-1])[0]
+        inp["key_scale"][:] = inp["key_scale"].reshape(-1)[0]
+
+    got = _case(cfg, ctx, seed=14, intermediates=False, edit=same_keys, modes=(("mk", False), ("graph", False)))
+    sel = got.cpu().numpy().astype(np.int64).reshape(cfg.m, k)
+    for m in range(cfg.m):
+        r, j = divmod(m, T)
+        prior = int(ctx[r]) - T  # keys before the request's new tokens
+        p = sel[m][(sel[m] >= 0) & (sel[m] < prior)]
+        assert np.array_equal(p, np.arange(len(p))), f"row {m}: tied prior keys not taken from position 0"
+        assert len(p) == min(k, prior + j + 1) - np.sum((sel[m] >= prior)), f"row {m}: selection size"
 
 
 @pytest.mark.timeout(600)

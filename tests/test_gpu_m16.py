@@ -60,7 +60,9 @@ def opnd_fp8_rows(buf: np.ndarray, K: int) -> np.ndarray:
 def _run(cfg, inp, W=0):
     from gpu_helpers import QwenRun
     # the plan is built for the inputs' context lengths (tile counts and RoPE positions follow them)
-    return QwenRun(cfg, inp, num_workers=W, ctx=[int(c) for c in inp["context_lens"]])
+    run = QwenRun(cfg, inp, num_workers=W, ctx=[int(c) for c in inp["context_lens"]])
+    run.inp_block_table, run.inp_ctx = inp["block_table"], inp["context_lens"]
+    return run
 
 
 def _ws(run, name, dtype=torch.uint8):
@@ -80,6 +82,22 @@ def _decisions(run, rows):
     return dec
 
 
+def _bf16_decisions(run, rows):
+    """The kernel's bf16 q (as its attention materialised it, from the workspace), k and v (the
+    cache rows it wrote at the new tokens' slots), for the given rows: the oracle resolves its
+    ambiguous bf16 roundings of q, k, v from these (tests/fp8_check.py)."""
+    cfg = run.cfg
+    Hq, Hkv, d, P = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.page_size
+    qb = bf16_bits_to_f64(_ws(run, "qb").view(np.uint16)[:cfg.m * Hq * d]).reshape(cfg.m, Hq, d)[rows]
+    kc = run.t["k_cache"].cpu().numpy().view(np.uint16)[0]
+    vc = run.t["v_cache"].cpu().numpy().view(np.uint16)[0]
+    bt, ctx = run.inp_block_table, run.inp_ctx
+    slots = [(bt[r][(int(ctx[r]) - 1) // P], (int(ctx[r]) - 1) % P) for r in rows]
+    k = np.stack([bf16_bits_to_f64(kc[p, o]) for p, o in slots]).reshape(len(rows), Hkv, d)
+    v = np.stack([bf16_bits_to_f64(vc[p, o]) for p, o in slots]).reshape(len(rows), Hkv, d)
+    return {"q": qb, "k": k, "v": v}
+
+
 def _oracle(cfg, inp, run, rows):
     """(resolved, independent) oracle layers for the given rows (inputs already restricted to them).
     bf16: both are the plain oracle.  FP8: ``resolved`` checks every GPU code against the oracle's
@@ -89,7 +107,7 @@ def _oracle(cfg, inp, run, rows):
     if not cfg.act_fp8:
         ref = model.run_qwen3_layer(cfg, inp)
         return ref, ref
-    ties = KernelTies(_decisions(run, rows))
+    ties = KernelTies(_decisions(run, rows), bf16=_bf16_decisions(run, rows))
     ref = model.run_qwen3_layer(cfg, inp, ties=ties)
     _say(f"  FP8 decisions: {ties.summary()}")
     ind = model.run_qwen3_layer(cfg, inp) if ties.any_flip else ref
@@ -183,12 +201,12 @@ def _reduced(fp8, R, ctx):
                                n_requests=R, context=max(ctx), page_size=16)
 
 
-@pytest.mark.parametrize("R", [5, 40])
+@pytest.mark.parametrize("R", [5, 40, 256])
 @pytest.mark.parametrize("fp8", [False, True])
 def test_m16_reduced_layer_all_modes(fp8, R):
     """Every intermediate and output at reduced shapes; 40 requests take three 16-row groups (the
-    last one ragged)."""
-    ctx = [1, 37, 300, 513, 64] if R == 5 else [int(c) for c in np.random.default_rng(40).integers(1, 514, R)]
+    last one ragged), 256 the most a plan takes (sixteen groups)."""
+    ctx = [1, 37, 300, 513, 64] if R == 5 else [int(c) for c in np.random.default_rng(R).integers(1, 514, R)]
     cfg = _reduced(fp8, len(ctx), ctx)
     inp = make_inputs(cfg, seed=3)
     inp["context_lens"] = np.array(ctx, dtype=np.int32)
