@@ -74,7 +74,7 @@ def main() -> int:
                          "HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the decode chain on a single MI355X "
+        print("bench.py measures one GPU only: the library runs the decode chain on a single MI355X "
               "(no collectives); run with --gpus 1", file=sys.stderr)
         return 2
 
