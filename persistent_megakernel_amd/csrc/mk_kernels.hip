@@ -2074,9 +2074,10 @@ DEV float key_value(uint32_t kk) { return __uint_as_float((kk & 0x80000000u) ? (
 
 // One selection pass of the top-k: every counted key (count(j)) adds 1 to bin(j) (0..255) of this
 // wave's histogram; wave 0 sums the eight histograms and walks the bins from the top.  Returns the
-// bin that holds the krem-th largest counted key and sets krem to that key's rank inside the bin.
+// bin that holds the krem-th largest counted key, sets krem to that key's rank inside the bin and
+// nbin to the bin's count.
 template <int J, class Bin, class Count>
-DEV uint32_t topk_pass(uint32_t* hist, uint32_t* ctl, int wv, uint32_t& krem, Bin bin, Count count) {
+DEV uint32_t topk_pass(uint32_t* hist, uint32_t* ctl, int wv, uint32_t& krem, uint32_t& nbin, Bin bin, Count count) {
   const uint32_t ln = lane();
   uint32_t* mine = hist + wv * 256;
 #pragma unroll
@@ -2107,6 +2108,7 @@ DEV uint32_t topk_pass(uint32_t* hist, uint32_t* ctl, int wv, uint32_t& krem, Bi
         if (above + c[q] >= krem) {
           ctl[0] = 255u - 4u * ln - (uint32_t)q;
           ctl[1] = krem - above;
+          ctl[2] = c[q];
           break;
         }
         above += c[q];
@@ -2115,6 +2117,7 @@ DEV uint32_t topk_pass(uint32_t* hist, uint32_t* ctl, int wv, uint32_t& krem, Bi
   }
   lds_barrier();
   krem = ctl[1];
+  nbin = ctl[2];
   return ctl[0];
 }
 
@@ -2193,37 +2196,48 @@ DEV void topk_row(const KArgs& a, const Instr& in, int wv) {
   uint32_t* ctl = hist + kNW * 256;                 // [2] bin, remainder; at 4 and 20 two min / max tables
   uint32_t* tab = ctl + 64;                         // [2][J][8 waves] counts per (position block, wave)
   uint32_t thr = 0u, krem = 0u;  // with k >= the keys, every key (all above 0) is taken
+  uint32_t neq = 0u;             // keys equal to thr (when known without a count of its own)
   if (nvalid > k) {
     auto valid = [&](int j) { return (uint32_t)j * 512u + g < nvalid; };
     uint32_t lo, hi;
     topk_range<J>(key, ctl + 4, wv, valid, lo, hi);
     krem = k;
     thr = hi;  // all keys equal: the first k of them
+    neq = nvalid;
     if (lo != hi) {
-      // first pass: 256 bins linear in the score between the smallest and the largest (a bin is a
-      // non-decreasing function of the score, so the bins order the keys), which spreads the keys
-      // over the bins whatever their exponents; the keys of the chosen bin remain
+      // two passes of 256 bins linear in the score: first between the smallest and the largest key
+      // (a bin is a non-decreasing function of the score, so the bins order the keys, and they spread
+      // the keys whatever their exponents), then across the chosen bin's own interval; the chosen
+      // sub-bin almost always holds keys of one value
       const float flo = key_value(lo), scale = 256.f / (key_value(hi) - flo);
       auto vbin = [&](int j) { return min(255u, (uint32_t)((key_value(key[j]) - flo) * scale)); };
-      const uint32_t d0 = topk_pass<J>(hist, ctl, wv, krem, vbin, valid);
+      uint32_t nb;
+      const uint32_t d0 = topk_pass<J>(hist, ctl, wv, krem, nb, vbin, valid);
+      const float blo = flo + (float)d0 / scale, scale2 = fminf(256.f * scale, 3.0e38f);
+      auto vbin2 = [&](int j) { return min(255u, (uint32_t)fmaxf(0.f, (key_value(key[j]) - blo) * scale2)); };
+      auto in_d0 = [&](int j) { return valid(j) && vbin(j) == d0; };
+      const uint32_t d1 = topk_pass<J>(hist, ctl, wv, krem, nb, vbin2, in_d0);
+      auto in_d1 = [&](int j) { return in_d0(j) && vbin2(j) == d1; };
       uint32_t clo, chi;
-      topk_range<J>(key, ctl + 20, wv, [&](int j) { return valid(j) && vbin(j) == d0; }, clo, chi);
+      topk_range<J>(key, ctl + 20, wv, in_d1, clo, chi);
       thr = chi;
+      neq = nb;
       if (clo != chi) {
         // then the order keys of the remaining ones, 8 bits at a time from the highest bit in which
-        // they differ (keys in [clo, chi] are exactly the chosen bin's)
+        // they differ (keys in [clo, chi] are exactly the chosen sub-bin's)
         const int hb = 31 - __builtin_clz(clo ^ chi);
         uint32_t pmask = hb == 31 ? 0u : ~((2u << hb) - 1u), prefix = chi & pmask;
         for (int s = hb - 7;; s -= 8) {
           const uint32_t sft = (uint32_t)max(s, 0), dmask = (1u << (s > 0 ? 8 : 8 + s)) - 1u;
           const uint32_t d = topk_pass<J>(
-              hist, ctl, wv, krem, [&](int j) { return (key[j] >> sft) & dmask; },
+              hist, ctl, wv, krem, nb, [&](int j) { return (key[j] >> sft) & dmask; },
               [&](int j) { return valid(j) && key[j] >= clo && key[j] <= chi && (key[j] & pmask) == prefix; });
           prefix |= d << sft;
           pmask |= dmask << sft;
           if (s <= 0) break;
         }
         thr = prefix;
+        neq = nb;  // the last pass fixes every bit: its bin is the keys equal to thr
       }
     }
   }
@@ -2236,13 +2250,16 @@ DEV void topk_row(const KArgs& a, const Instr& in, int wv) {
     gtm |= v && key[j] > thr ? 1u << j : 0u;
     eqm |= v && key[j] == thr ? 1u << j : 0u;
   }
-  uint32_t tot;
-  const uint32_t eq_pos = pos_prefix(eqm, wv, tab, tot);
-  uint32_t selm = gtm;
+  uint32_t selm = gtm | eqm;
+  if (krem < neq) {  // only some of the equal keys: the krem first in position order
+    uint32_t tot;
+    const uint32_t eq_pos = pos_prefix(eqm, wv, tab, tot);
+    selm = gtm;
 #pragma unroll
-  for (int j = 0; j < J; ++j)  // this lane's equal keys in position order: take those before the krem-th
-    selm |= ((eqm >> j) & 1u) && __builtin_amdgcn_readlane(eq_pos, j) + lanes_below(__builtin_amdgcn_ballot_w64((eqm >> j) & 1u)) < krem
-                ? 1u << j : 0u;
+    for (int j = 0; j < J; ++j)  // this lane's equal keys in position order: take those before the krem-th
+      selm |= ((eqm >> j) & 1u) && __builtin_amdgcn_readlane(eq_pos, j) + lanes_below(__builtin_amdgcn_ballot_w64((eqm >> j) & 1u)) < krem
+                  ? 1u << j : 0u;
+  }
   uint32_t run;
   const uint32_t sel_pos = pos_prefix(selm, wv, tab + J * kNW, run);
   __amdgpu_buffer_rsrc_t ro = rsrc((const int32_t*)s_ld64(row + TK_OUT) + (size_t)m * k);
