@@ -9,6 +9,7 @@ indexer front without them):
   differences);
 - instances without loader waves stamp when the compute waves issued an instruction's lease
   (word 9), before that instruction's compute-start barrier;
+- the Perfetto export gives four slices per live instruction (every stamp pair is ordered);
 - on the single-token step the leases of a layer's first instructions are issued while the
   previous layer still runs on that worker (the queue-order lookahead crosses layer boundaries);
   the share is reported, and must be a majority.
@@ -21,6 +22,7 @@ import pytest
 import torch
 
 import persistent_megakernel_amd as mk
+from persistent_megakernel_amd import trace as tx
 from workloads import get_config, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -44,6 +46,8 @@ def _check_order(q, tr, tag):
         idx = np.flatnonzero(live[w])
         if len(idx) > 1:
             assert (_d(tr[w, idx[:-1], 7], tr[w, idx[1:], 0]) >= 0).all(), f"{tag}: worker {w} out of order"
+    ev = tx.events(q, tr)
+    assert sum(e["ph"] == "X" for e in ev) == 4 * int(live.sum()), f"{tag}: export lost slices"
     return live
 
 
