@@ -101,7 +101,7 @@ def tile_params(cfg, W: int, ctx_lens) -> Dict[str, int]:
     p["r_o"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(Hq * d, 1, 0)))
     p["r_gu"] = _largest_divisor_le(I, min(max(1, I // W), cap_rows(H, 2, gain + 1024)))
     p["r_down"] = _largest_divisor_le(H, min(max(1, H // W), cap_rows(I, 1, 0)))
-    p["r_lm"] = min(cfg.vocab, cap_rows(H, 1, gain), 64) if cfg.workload == "qwen3_step" else 0
+    p["r_lm"] = -(-cfg.vocab // W) if cfg.workload == "qwen3_step" else 0  # one lm_head task per worker
     ctx_max = int(max(ctx_lens))
     want = -(-(2 * R * ctx_max * Hkv) // W)  # about W/2 attention tasks
     p["s_tok"] = max(4, min(LEASE_BYTES // (4 * d), _pow2ceil(max(1, want))))
@@ -195,14 +195,13 @@ def _qwen3(cfg, W: int, ctx_lens, b: _Builder, p) -> None:
         rl = p["r_lm"]
         n_lm = -(-cfg.vocab // rl)
         grp = b.arrival_group()
-        # a worker keeps a running max over its lm_head tiles and publishes it with its last
-        # one: the last min(W, n_lm) tiles publish, each into its own slot of the group
+        # a worker keeps a running max over its lm_head tasks and publishes it with its last
+        # one: the last min(W, n_lm) tasks publish, each into its own slot of the group
         n_pub = min(W, n_lm)
-        for j in range(n_lm):
-            n0 = j * rl
+        for j in range(n_lm):  # task j takes rows j, j + n_lm, ... (interleaved)
             slot = j - (n_lm - n_pub) if j >= n_lm - n_pub else NONE
             b.task(OP_LMHEAD, row_lm, spec, [(prev_down, n_d_t)], [],
-                   [cfg.num_layers, n0, min(rl, cfg.vocab - n0), 0, H, 0, grp, n_pub, slot])
+                   [cfg.num_layers, j, -(-(cfg.vocab - j) // n_lm), n_lm, H, 0, grp, n_pub, slot])
 
 
 def _qwen3_m16(cfg, W: int, ctx_lens, b: _Builder, p) -> None:

@@ -42,6 +42,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // 16x16x32 bf16 mat
 typedef short i16x4 __attribute__((ext_vector_type(4)));    // 16x16x16 bf16 matrix-core operand
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const char lds_cchar;
 
 #define DEV __device__ __forceinline__
 
@@ -563,6 +564,10 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
     return;
   }
   if (S == 1 && op == OP_COMB) return;
+  if (op == OP_LMHEAD) {  // the rows stream from HBM inside the body; the lease holds the norm gain
+    pf_set<0>(pf, (const void*)s_ld64(row + LM_GAMMA), 2u * (uint32_t)sh.H);
+    return;
+  }
   const char* w = (const char*)s_ld64(row + 0);
   const uint32_t n0 = in.w[W_P1], nr = in.w[W_P2], K = in.w[W_P4];
   const uint32_t rowb = K * 2u;
@@ -570,8 +575,8 @@ DEV void pf_desc(const KArgs& a, const Instr& in, Pf<S>& pf) {
   if (op == OP_GATEUP) {
     pf_set<1>(pf, w + (size_t)(sh.I + n0) * rowb, nr * rowb);
     pf_set<2>(pf, (const void*)s_ld64(row + GU_GAMMA), 2u * (uint32_t)sh.H);
-  } else if (op == OP_QKV || op == OP_LMHEAD) {
-    pf_set<1>(pf, (const void*)s_ld64(row + (op == OP_QKV ? QKV_GAMMA : LM_GAMMA)), 2u * (uint32_t)sh.H);
+  } else if (op == OP_QKV) {
+    pf_set<1>(pf, (const void*)s_ld64(row + QKV_GAMMA), 2u * (uint32_t)sh.H);
   }
 }
 
@@ -1040,6 +1045,100 @@ DEV float row_sum(const float* part, int r, int KQ) {
   return s;
 }
 
+// lm_head rows n0 + st j (j < nr) of one instruction on one wave (all eight take part), streamed from
+// HBM into registers rather than through an LDS lease: one instruction per worker covers its whole
+// share of the vocabulary, so the per-instruction costs (staging, barriers, epilogue) are paid once
+// and the loads of four steps stay in flight while a step is summed.  h (bf16, K = 512 KQ) sits at
+// the start of the activation area; lane l holds its elements 512 kq + 8 l .. + 8 in registers for
+// the whole run.  A step is P = 4 / KQ consecutive rows (KQ = 3: one row and an empty fourth block),
+// i.e. four quads laid out as in the leased tile (lane l reads bytes 16 l .. + 16 of each quad),
+// summed by the same butterfly and cross-row swaps, and a row's quad sums are added in quad order:
+// the same arithmetic as the tiled GEMV.  The plan interleaves the workers' rows (stride = number of
+// tasks), so that at any time all compute units stream one narrow window of the matrix; the weights
+// are read once, with non-temporal loads.  Wave wv takes steps wv, wv + 8, ...; loads past a
+// wave's last step repeat the instruction's last step (cache hits, in bounds).  Logits go straight
+// to memory; the wave's (max, first index) lands in the output area for the epilogue.
+DEV void argmax_merge(float& best, int& bi);
+// Out of line: its load buffers stay out of the register allocation of the kernel's other bodies
+// (inlined, it raised the single-token kernel's spilled scalar registers from 163 to 200).
+typedef __attribute__((address_space(3))) float lds_float;
+template <int KQ>
+__device__ __attribute__((noinline)) void lm_rows(const char* wm, float* logits, int n0, int nr, int stride,
+                                                  lds_cchar* act, lds_float* out, int wv) {
+  constexpr int P = KQ == 3 ? 1 : 4 / KQ;
+  // the pointers arrive in vector registers: made wave-uniform (scalar) and typed as global memory, so
+  // that the loads are global loads whose counter the compiler tracks one by one (generic-pointer
+  // loads would wait for every load in flight before the first use)
+  typedef const __attribute__((address_space(1))) char gchar;
+  const uint64_t wa = (uint64_t)(uintptr_t)wm, la = (uint64_t)(uintptr_t)logits;
+  gchar* wg = (gchar*)(uintptr_t)(((uint64_t)uni((uint32_t)(wa >> 32)) << 32) | uni((uint32_t)wa));
+  __amdgpu_buffer_rsrc_t rl = rsrc((const void*)(uintptr_t)(((uint64_t)uni((uint32_t)(la >> 32)) << 32) | uni((uint32_t)la)));
+  n0 = (int)uni((uint32_t)n0);
+  nr = (int)uni((uint32_t)nr);
+  stride = (int)uni((uint32_t)stride);
+  wv = (int)uni((uint32_t)wv);
+  const int ln = (int)lane(), sub = ln & 15;
+  u32x4 xr[KQ];
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq) xr[kq] = *(const __attribute__((address_space(3))) u32x4*)(act + kq * 1024 + ln * 16);
+  const int nst = (nr + P - 1) / P;
+  const int my = nst > wv ? (nst - wv + kNW - 1) / kNW : 0;
+  const size_t rowb = (size_t)KQ * 1024u;
+  auto load = [&](u32x4 (&w)[4], int i) {
+    const int t = min(wv + kNW * i, nst - 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = min(t * P + (KQ == 3 ? 0 : m / KQ), nr - 1);
+      const int kq = KQ == 3 ? min(m, 2) : m % KQ;
+      w[m] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(
+          wg + (size_t)(n0 + r * stride) * rowb + (size_t)kq * 1024u + (size_t)ln * 16u));
+    }
+  };
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  auto consume = [&](const u32x4 (&w)[4], int i) {
+    if (i >= my) return;
+    const int t = wv + kNW * i;
+    float d[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      d[m] = (KQ == 3 && m == 3) ? 0.f : dot8(w[m], xr[KQ == 3 ? m : m % KQ], 0.f);
+    const float v = rows_sum(butterfly4(d[0], d[1], d[2], d[3], sub));  // lanes 4m .. 4m + 3: block m
+    const int blk = KQ == 3 ? 16 : 4 * KQ;  // lanes of one row's blocks
+    float sv = v;
+#pragma unroll
+    for (int k = 1; k < (KQ == 3 ? 3 : KQ); ++k) sv += __shfl(v, (ln & ~(blk - 1)) + 4 * k);
+    const int p = ln / blk, r = t * P + p;
+    if (ln < 16 && (ln & (blk - 1)) == 0 && p < P && r < nr) {
+      st32(rl, (uint32_t)(n0 + r * stride) * 4u, __float_as_uint(sv));
+      if (sv > best) {
+        best = sv;
+        bi = n0 + r * stride;
+      }
+    }
+  };
+  u32x4 b0[4], b1[4], b2[4], b3[4];
+  load(b0, 0);
+  load(b1, 1);
+  load(b2, 2);
+  load(b3, 3);
+  for (int i = 0; i < my; i += 4) {
+    consume(b0, i);
+    load(b0, i + 4);
+    consume(b1, i + 1);
+    load(b1, i + 5);
+    consume(b2, i + 2);
+    load(b2, i + 6);
+    consume(b3, i + 3);
+    load(b3, i + 7);
+  }
+  argmax_merge(best, bi);
+  if (ln == 0) {
+    out[2 * wv] = best;
+    out[2 * wv + 1] = __int_as_float(bi);
+  }
+}
+
 // the projection body of one instruction on one wave (wv 0..6 compute waves, 7 the controller):
 // the second half of a fused norm (then a barrier), then the tile's quad sums into the output area
 DEV void proj_body(const KArgs& a, const Instr& in, const char* smem, uint32_t lease, bool fused_norm, int wv) {
@@ -1048,14 +1147,27 @@ DEV void proj_body(const KArgs& a, const Instr& in, const char* smem, uint32_t l
   const uint32_t wblk = blocks_of((uint32_t)nr * K * 2u);
   float* out = (float*)(smem + kOutOff);
   if (fused_norm) {
-    const uint32_t goff = (op == OP_GATEUP ? 2u : 1u) * wblk * 1024u;
+    const uint32_t goff = op == OP_LMHEAD ? 0u : (op == OP_GATEUP ? 2u : 1u) * wblk * 1024u;
     if (op == OP_QKV && in.w[W_LAYER] == 0)
       norm_h<true>(smem, lease, goff, K, wv);
     else
       norm_h<false>(smem, lease, goff, K, wv);
     lds_barrier();
   }
-  if (op == OP_OPROJ || op == OP_DOWN)
+  if (op == OP_LMHEAD) {
+    const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
+    const char* wm = (const char*)s_ld64(row + LM_W);
+    float* lg = (float*)s_ld64(row + LM_LOGITS);
+    const int n0 = in.w[W_P1], st = in.w[W_P3];  // rows n0, n0 + st, ...
+    lds_cchar* act = (lds_cchar*)(smem + kActOff);
+    lds_float* lo = (lds_float*)(smem + kOutOff);
+    switch (K >> 9) {
+      case 1: lm_rows<1>(wm, lg, n0, nr, st, act, lo, wv); break;
+      case 2: lm_rows<2>(wm, lg, n0, nr, st, act, lo, wv); break;
+      case 3: lm_rows<3>(wm, lg, n0, nr, st, act, lo, wv); break;
+      default: lm_rows<4>(wm, lg, n0, nr, st, act, lo, wv); break;
+    }
+  } else if (op == OP_OPROJ || op == OP_DOWN)
     gemv<true>(smem, lease, nr, nr, 0u, K, wv, out);
   else
     gemv<false>(smem, lease, op == OP_GATEUP ? 2 * nr : nr, nr, wblk * 1024u, K, wv, out);
@@ -2574,18 +2686,10 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
       if (yout) st16(rsrc((const void*)yout), (uint32_t)(n0 + jj) * 2u, yb);
     }
   } else if (op == OP_LMHEAD) {
-    __amdgpu_buffer_rsrc_t rl = rsrc((const void*)s_ld64(row + LM_LOGITS));
+    // the body stored the logits; lane w < 8 takes wave w's (max, first index)
     __amdgpu_buffer_rsrc_t rp = rsrc((const void*)s_ld64(row + LM_PART));
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int jj = j; jj < nr; jj += 64) {
-      const float v = row_sum(part, jj, KB);
-      st32(rl, (uint32_t)(n0 + jj) * 4u, __float_as_uint(v));
-      if (v > best) {
-        best = v;
-        bi = n0 + jj;
-      }
-    }
+    float best = j < kNW ? part[2 * j] : -INFINITY;
+    int bi = j < kNW ? ((const int*)part)[2 * j + 1] : 0x7fffffff;
     argmax_merge(best, bi);
     if (best > lm.best || (best == lm.best && bi < lm.idx)) {
       lm.best = best;

@@ -111,7 +111,8 @@ bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, s
   p.r_o = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(Hq * d, 1, 0)));
   p.r_gu = largest_divisor_le(I, std::min(std::max(1, I / W), cap_rows(H, 2, gain + 1024)));
   p.r_down = largest_divisor_le(H, std::min(std::max(1, H / W), cap_rows(I, 1, 0)));
-  p.r_lm = c.workload == MK_QWEN3_STEP ? std::min({c.vocab, cap_rows(H, 1, gain), 64}) : 0;
+  // lm_head: one task per worker, its rows streamed from HBM inside the body (no weight lease)
+  p.r_lm = c.workload == MK_QWEN3_STEP ? (c.vocab + W - 1) / W : 0;
   int ctx_max = 0;
   for (int r = 0; r < R; ++r) ctx_max = std::max(ctx_max, (int)ctx[r]);
   // about W/2 attention tasks: fewer splits keep the combine short; the KV is prefetched anyway
@@ -608,14 +609,14 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
     int row_lm = b.op_row(OP_LMHEAD, c.num_layers, {prev_down_row});
     int rl = p.r_lm, n_lm = (c.vocab + rl - 1) / rl;
     int grp = b.n_arrivals++;
-    // each worker keeps a running max over its lm_head tiles and publishes it with its last
-    // one: the last min(W, n_lm) tiles publish, each into its own slot of the arrival group
+    // each worker keeps a running max over its lm_head tasks and publishes it with its last
+    // one: the last min(W, n_lm) tasks publish, each into its own slot of the arrival group
     const int n_pub = std::min(W, n_lm);
+    // task j takes rows j, j + n_lm, ... (the workers' rows interleaved)
     for (int j = 0; j < n_lm; ++j) {
-      int n0 = j * rl;
       int64_t slot = j >= n_lm - n_pub ? (int64_t)(j - (n_lm - n_pub)) : (int64_t)kNone;
       b.task(OP_LMHEAD, row_lm, p.spec, {{prev_down, (uint32_t)n_d_t}}, {},
-             {c.num_layers, n0, std::min(rl, c.vocab - n0), 0, H, 0, grp, n_pub, slot});
+             {c.num_layers, j, (c.vocab - j + n_lm - 1) / n_lm, n_lm, H, 0, grp, n_pub, slot});
     }
   }
   if (pack_plan(b, W, max_splits, out, err) != MK_OK) return MK_ERR_INVALID;
