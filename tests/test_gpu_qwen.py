@@ -144,6 +144,8 @@ def _check_step(run, res, tag):
     assert el <= TOL, f"{tag}: logits err {el}"
     tok = int(run.t["token_out"].cpu().numpy()[0])
     assert res["logits_pre"][0][tok] >= np.max(res["logits_pre"][0]) - TOL, tag
+    # the argmax over the kernel's own fp32 logits is exact: the first index of the largest value
+    assert tok == int(np.argmax(run.t["logits_out"].cpu().numpy())), f"{tag}: token {tok} is not the argmax"
 
 
 def test_reduced_step_all_modes():
@@ -158,6 +160,25 @@ def test_reduced_step_all_modes():
             run.run(mode, ms)
             _check_step(run, res, f"W={W} {mode}")
             _check_step_caches(run, inp, res, f"W={W} {mode}")
+
+
+@pytest.mark.parametrize("vocab,W", [(100, 0), (1001, 7), (4099, 37), (2 * 256 * 8 + 3, 0)])
+def test_step_lm_head_shapes(vocab, W):
+    """lm_head task shapes: fewer rows than workers (idle workers), ragged interleaved rows, a wave
+    with no rows, every worker with rows; logits against the oracle, the token against the argmax of
+    the kernel's own logits, the megakernel against the graph baseline bit for bit."""
+    cfg = dataclasses.replace(get_config("qwen3_0p6b_step"), num_layers=1, vocab=vocab, context=64)
+    inp = make_inputs(cfg, seed=11)
+    res = model.run_qwen3_step(cfg, inp)
+    from gpu_helpers import QwenRun
+    run = QwenRun(cfg, inp, num_workers=W)
+    got = {}
+    for mode in ("mk", "graph"):
+        _say(f"case: lm_head shapes vocab={vocab} W={W} {mode}")
+        run.run(mode)
+        _check_step(run, res, f"vocab={vocab} W={W} {mode}")
+        got[mode] = run.t["logits_out"].cpu().numpy().copy()
+    assert np.array_equal(got["mk"].view(np.uint32), got["graph"].view(np.uint32))
 
 
 def test_full_step_28_layers():
