@@ -234,6 +234,15 @@ DEV void put_instr8(char* smem, int j, const Instr& in) {
     *(volatile uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff + (j & 7) * 4) = (uint32_t)j + 1u;
   }
 }
+// the operand-table row of instruction i if compute wave 0 has copied it into the ring, else kNone
+template <int S>
+DEV uint32_t ring8_row(const char* smem, int i) {
+  if (__builtin_amdgcn_readfirstlane(*(const volatile uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff + (i & 7) * 4)) !=
+      (uint32_t)i + 1u)
+    return 0xFFFFFFFFu;
+  asm volatile("" ::: "memory");
+  return __builtin_amdgcn_readfirstlane(*(const uint32_t*)(ring8_slot<S>(smem, i) + 4 * W_ROW));
+}
 template <int S>
 DEV bool get_instr8(const char* smem, int i, Instr& in) {
   if (__builtin_amdgcn_readfirstlane(*(const volatile uint32_t*)(smem + dev::kCtrlOff + dev::kITagOff + (i & 7) * 4)) !=
@@ -2858,6 +2867,17 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     const bool fused_norm = op == OP_QKV || op == OP_GATEUP || (op == OP_LMHEAD && last_row != in.w[W_ROW]);
     const uint64_t* row = a.table + (size_t)in.w[W_ROW] * kTableSlots;
     const uint64_t row_touch = s_ld64(row);  // the pointer row into the scalar cache before the epilogue reads it
+    // single-token kernel: both cache lines of the next instruction's pointer row too, so that its
+    // prologue's pointer loads hit the scalar cache
+    uint64_t next_touch0 = 0, next_touch1 = 0;
+    if (!LD && !m16) {
+      const uint32_t nrow = ring8_row<S>(smem, i + 1);
+      if (nrow != 0xFFFFFFFFu) {
+        const uint64_t* nr = a.table + (size_t)nrow * kTableSlots;
+        next_touch0 = s_ld64(nr);
+        next_touch1 = s_ld64(nr + 8);
+      }
+    }
     char* act = smem + kActOff;
     // the instruction's wait: its tagged inputs staged into LDS (the graph baseline's stream order
     // already guarantees them, so it stages without checking tags)
@@ -2937,7 +2957,7 @@ DEV void controller(const KArgs& a, const uint32_t* base, int count, int stride,
     } else {
       gemv_epilogue(a, in, smem, lm, st);
     }
-    asm volatile("" ::"s"(row_touch));
+    asm volatile("" ::"s"(row_touch), "s"(next_touch0), "s"(next_touch1));
     if (tracing) {
       tput(a, (uint32_t)i, 7, rtc());
       tput(a, (uint32_t)i, 8, poll);
