@@ -190,3 +190,27 @@ def test_indexer_front_counts_and_no_deadlock():
             oq.check_invariants(p)
             for seed in range(2):
                 simulate(p, seed)
+
+
+@pytest.mark.parametrize("vocab,W", [(151936, 256), (3000, 9), (100, 256), (4099, 37), (7, 7)])
+def test_lm_head_tasks_cover_the_vocabulary_once(vocab, W):
+    """The step's lm_head tasks: at most one per worker, task j takes the rows j, j + n, j + 2n, ...
+    (n tasks), so every vocabulary row is computed exactly once; every task publishes its worker's
+    maximum into its own slot of one arrival group (the last arriver takes the argmax)."""
+    cfg = dataclasses.replace(get_config("qwen3_0p6b_step"), num_layers=1, vocab=vocab, context=64)
+    plan = oq.build_queue(cfg, W)
+    lm = [t for t in _tasks(plan) if t[0] == oq.OP_LMHEAD]
+    n = len(lm)
+    assert 1 <= n <= W
+    rows = []
+    for t in lm:
+        j, nr, stride = int(t[21]), int(t[22]), int(t[23])  # first row, row count, row stride
+        assert stride == n and int(t[24]) == cfg.hidden
+        rows.extend(range(j, j + nr * stride, stride))
+    assert sorted(rows) == list(range(vocab))
+    assert sorted(int(t[28]) for t in lm) == list(range(n))  # a slot each
+    assert {int(t[26]) for t in lm} == {int(lm[0][26])} and all(int(t[27]) == n for t in lm)
+    # every lm_head task sits on a worker of its own
+    q = plan["queue"]
+    per_worker = [(q[w, :, 0] == oq.OP_LMHEAD).sum() for w in range(W)]
+    assert max(per_worker) == 1
