@@ -179,7 +179,7 @@ mk_status mk_plan_workspace_bytes(const mk_plan* plan, size_t* bytes);
  * [M, N_qkv], "o" bf16 pairs [M, Hq d / 2], "m" bf16 pairs [M, I / 2], "r2" fp32 [M, H]
  * (residual after attention), "r1" fp32 [M, H] (r2 + y, the next layer's residual input).
  * "part" holds the split-KV partials as plain fp32 (kernel prologue/epilogue page, section 4: per
- * split its normalised output and log-sum-exp), "lm_part" the lm_head tile maxima.  Multi-row
+ * split its normalised output and log-sum-exp), "lm_part" the lm_head tasks' maxima (one slot per task).  Multi-row
  * plans keep "qkv" as records and everything else plain (projection inputs in the matrix-core
  * operand order, fp32 partial sums per tile and K chunk).  Errors: MK_ERR_INVALID for an unknown name. */
 mk_status mk_plan_workspace_region(const mk_plan* plan, const char* name, size_t* offset, size_t* bytes);

@@ -16,7 +16,7 @@ enum Opcode : uint32_t {
   OP_OPROJ = 3,   // O projection rows + residual add
   OP_GATEUP = 4,  // RMSNorm prologue, gate and up rows, SiLU-mul epilogue
   OP_DOWN = 5,    // down projection rows
-  OP_LMHEAD = 6,  // final add + RMSNorm prologue, lm_head rows, tile max; last arrival takes the argmax
+  OP_LMHEAD = 6,  // final add + RMSNorm prologue, a worker's lm_head rows streamed, their max; last arrival takes the argmax
   // multi-row (M = 16) plans
   OP_NORM = 7,    // one row: (add +) RMSNorm (+ FP8 quantisation) into the projection input layout
   OP_GEMM = 8,    // one (64-row tile, K chunk) of a projection: MFMA partial sums

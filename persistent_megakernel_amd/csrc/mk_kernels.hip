@@ -2705,7 +2705,7 @@ DEV void gemv_epilogue(const KArgs& a, const Instr& in, const char* smem, LmStat
       lm.idx = bi;
     }
     const uint32_t slot = in.w[W_ARR_RANK];
-    if (slot == kNone) return;  // not this worker's last lm_head tile
+    if (slot == kNone) return;  // not this worker's last lm_head task
     if (j == 0) {
       st32(rp, slot * 8u, __float_as_uint(lm.best));
       st32(rp, slot * 8u + 4u, (uint32_t)lm.idx);
