@@ -58,6 +58,16 @@ enum {
                                     (10 ns instead of 2 s), to exercise the watchdog and abort path */
 };
 
+/* mk_config.tile_params entries.  Rows per task of the single-token (M = 1) projections: QKV a power
+ * of two <= head_dim; O and down a divisor of hidden, <= 128; gate/up an even divisor of inter; each
+ * within one 64 KiB LDS lease with the norm gain.  lm_head (decode step): rows per task, >= 1 (task j
+ * takes the rows j, j + n, ... of n tasks).  Attention split: tokens per split-KV task, a power of two
+ * in 4 .. 128 (both op families).  The multi-row projections' 64-row tiles and the indexer front's
+ * tiles are fixed: their row entries and every entry of an indexer plan must be 0. */
+#define MK_TILE_PARAMS 8
+enum { MK_TP_ROWS_QKV = 0, MK_TP_ROWS_O = 1, MK_TP_ROWS_GATEUP = 2, MK_TP_ROWS_DOWN = 3, MK_TP_ROWS_LMHEAD = 4,
+       MK_TP_SPLIT_TOKENS = 5 /* 6, 7: reserved, 0 */ };
+
 /* Plain data, caller-owned, copied by mk_build_queue. */
 typedef struct {
   int32_t workload;            /* mk_workload */
@@ -73,6 +83,11 @@ typedef struct {
                           else 1 .. 8192 keys per row); 0 for the other workloads */
   int32_t mla_heads;   /* MK_INDEXER_FRONT: heads of the main-MLA query half (D0 Main-Q -> D2 Q-BMM,
                           128 no-RoPE dims and a 512-wide latent per head); 0: the indexer half only */
+  int32_t rotary_dim;  /* dims of a head the RoPE rotates: 0 or the head dim (head_dim, idx_head_dim):
+                          the whole head; any other value is refused with MK_ERR_UNSUPPORTED */
+  int32_t tile_params[MK_TILE_PARAMS]; /* tile sizes of the plan, MK_TP_* above; 0 lets the planner
+                          choose (its rules: the queue specification of the design notes); a value
+                          the op bodies cannot run is refused with MK_ERR_UNSUPPORTED */
 } mk_config;
 
 /* Device addresses in a fixed order per workload (MK_T_* below); n = number used. */

@@ -108,6 +108,12 @@ def tile_params(cfg, W: int, ctx_lens) -> Dict[str, int]:
     p["spec"] = 0 if cfg.m == 1 else 1
     # multi-row projection tiles: M16_ROWS weight rows x kc columns fill one lease
     p["kc"] = LEASE_BYTES // (M16_ROWS * elem) if p["spec"] == 1 else 0
+    # tile sizes the caller fixed (mk_config.tile_params; 0 keeps the rule above).  The library
+    # refuses values its op bodies cannot run; this builder only takes them over.
+    tp = tuple(getattr(cfg, "tile_params", ()) or ()) + (0,) * 8
+    for key, idx in (("r_qkv", 0), ("r_o", 1), ("r_gu", 2), ("r_down", 3), ("r_lm", 4), ("s_tok", 5)):
+        if tp[idx]:
+            p[key] = int(tp[idx])
     return p
 
 

@@ -28,6 +28,8 @@ MK_OK, MK_ERR_INVALID, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_NOMEM, MK_ERR_TIME
 MK_QWEN3_LAYER, MK_QWEN3_STEP, MK_INDEXER_FRONT = 0, 1, 2
 MK_FLAG_NO_PREFETCH, MK_FLAG_NOOP_ONLY, MK_FLAG_TRACE, MK_FLAG_DEBUG_GATHER, MK_FLAG_DEBUG_SHORT_WATCHDOG = 1, 2, 4, 8, 16
 MK_MAX_TENSORS = 32
+MK_TILE_PARAMS = 8
+MK_TP_ROWS_QKV, MK_TP_ROWS_O, MK_TP_ROWS_GATEUP, MK_TP_ROWS_DOWN, MK_TP_ROWS_LMHEAD, MK_TP_SPLIT_TOKENS = 0, 1, 2, 3, 4, 5
 MK_SCRATCH_MAX_BYTES = 40 << 20
 QWEN3_TENSORS = ["w_qkv", "w_o", "w_gu", "w_down", "g_attn", "g_mlp", "g_q", "g_k", "k_cache", "v_cache",
                  "block_table", "context_lens", "x", "r_in", "y_out", "r2_out", "workspace",
@@ -45,7 +47,8 @@ class MkConfig(ctypes.Structure):
         "num_layers", "vocab", "n_requests", "tokens_per_request", "page_size", "max_pages_per_req",
         "num_phys_pages", "idx_q_rank", "idx_heads", "idx_head_dim")] + [
         ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("num_workers", ctypes.c_int32),
-        ("flags", ctypes.c_uint32), ("topk", ctypes.c_int32), ("mla_heads", ctypes.c_int32)]
+        ("flags", ctypes.c_uint32), ("topk", ctypes.c_int32), ("mla_heads", ctypes.c_int32),
+        ("rotary_dim", ctypes.c_int32), ("tile_params", ctypes.c_int32 * MK_TILE_PARAMS)]
 
 
 class MkTensors(ctypes.Structure):
@@ -100,6 +103,12 @@ def make_config(cfg, num_workers: int = 0, flags: int = 0) -> MkConfig:
     c.num_workers, c.flags = int(num_workers), int(flags)
     c.topk = int(getattr(cfg, "topk", 0))
     c.mla_heads = int(getattr(cfg, "mla_heads", 0))
+    c.rotary_dim = int(getattr(cfg, "rotary_dim", 0))
+    tp = tuple(getattr(cfg, "tile_params", ()) or ())
+    if len(tp) > MK_TILE_PARAMS:
+        raise ValueError(f"tile_params holds at most {MK_TILE_PARAMS} entries")
+    for i, v in enumerate(tp):
+        c.tile_params[i] = int(v)
     return c
 
 

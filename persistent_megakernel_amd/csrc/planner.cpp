@@ -88,7 +88,17 @@ int kchunk(int K) {
 }
 
 bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, std::string& err) {
+  for (int k = 6; k < MK_TILE_PARAMS; ++k)
+    if (c.tile_params[k] != 0) {
+      err = "tile_params entries 6 and 7 are reserved and must be 0";
+      return false;
+    }
   if (c.workload == MK_INDEXER_FRONT) {
+    for (int k = 0; k < MK_TILE_PARAMS; ++k)
+      if (c.tile_params[k] != 0) {
+        err = "the indexer front's tiles are fixed: its tile_params must be 0";
+        return false;
+      }
     p.spec = 1;
     p.kc = kchunk(c.hidden);
     p.kc_q = kchunk(c.idx_q_rank);
@@ -120,7 +130,47 @@ bool tile_params(const mk_config& c, int W, const int32_t* ctx, TileParams& p, s
   p.s_tok = std::max(4, std::min(kLeaseBytes / (4 * d), pow2ceil((int)std::max(1ll, want))));
   p.spec = (R * c.tokens_per_request == 1) ? 0 : 1;
   p.kc = p.spec == 1 ? kLeaseBytes / (kM16Rows * elem) : 0;
-  (void)err;
+  // the caller's tile sizes, each checked against what the op bodies run
+  const int32_t* t = c.tile_params;
+  if (p.spec == 1 && (t[MK_TP_ROWS_QKV] || t[MK_TP_ROWS_O] || t[MK_TP_ROWS_GATEUP] || t[MK_TP_ROWS_DOWN] ||
+                      t[MK_TP_ROWS_LMHEAD])) {
+    err = "multi-row plans use fixed 64-row projection tiles: tile_params rows entries must be 0";
+    return false;
+  }
+  auto bad = [&](const char* m) {
+    err = m;
+    return false;
+  };
+  if (const int v = t[MK_TP_ROWS_QKV]) {
+    if (v < 1 || v > d || (v & (v - 1)) || v > cap_rows(H, 1, gain) || n_qkv % v)
+      return bad("tile_params QKV rows: a power of two <= head_dim whose weights and gain fit one lease");
+    p.r_qkv = v;
+  }
+  if (const int v = t[MK_TP_ROWS_O]) {
+    if (v < 1 || H % v || v > 128 || v > cap_rows(Hq * d, 1, 0))
+      return bad("tile_params O rows: a divisor of hidden, <= 128, whose weights fit one lease");
+    p.r_o = v;
+  }
+  if (const int v = t[MK_TP_ROWS_GATEUP]) {
+    if (v < 2 || v % 2 || I % v || v > cap_rows(H, 2, gain + 1024))
+      return bad("tile_params gate/up rows: an even divisor of inter whose gate, up and gain fit one lease");
+    p.r_gu = v;
+  }
+  if (const int v = t[MK_TP_ROWS_DOWN]) {
+    if (v < 1 || H % v || v > 128 || v > cap_rows(I, 1, 0))
+      return bad("tile_params down rows: a divisor of hidden, <= 128, whose weights fit one lease");
+    p.r_down = v;
+  }
+  if (const int v = t[MK_TP_ROWS_LMHEAD]) {
+    if (c.workload != MK_QWEN3_STEP || v < 1 || v > c.vocab)
+      return bad("tile_params lm_head rows: 1 .. vocab, decode step only");
+    p.r_lm = v;
+  }
+  if (const int v = t[MK_TP_SPLIT_TOKENS]) {
+    if (v < 4 || v > kLeaseBytes / (4 * d) || (v & (v - 1)))
+      return bad("tile_params split tokens: a power of two in 4 .. 128");
+    p.s_tok = v;
+  }
   return true;
 }
 
@@ -500,6 +550,10 @@ mk_status plan_indexer(const mk_config& c, const int32_t* ctx, int W, HostPlan& 
 }  // namespace
 
 mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& out, std::string& err) {
+  if (c.rotary_dim != 0 && c.rotary_dim != (c.workload == MK_INDEXER_FRONT ? c.idx_head_dim : c.head_dim)) {
+    err = "partial rotary embeddings are not built: rotary_dim must be 0 or the head dim";
+    return MK_ERR_UNSUPPORTED;
+  }
   if (c.workload == MK_INDEXER_FRONT) return plan_indexer(c, ctx, W, out, err);
   if (c.topk != 0 || c.mla_heads != 0) {
     err = "top-k and the main-MLA half belong to the indexer front";
@@ -538,7 +592,7 @@ mk_status plan_build(const mk_config& c, const int32_t* ctx, int W, HostPlan& ou
   out.ctx.assign(ctx, ctx + R);
   out.W = W;
   TileParams& p = out.tp;
-  if (!tile_params(c, W, ctx, p, err)) return MK_ERR_INVALID;
+  if (!tile_params(c, W, ctx, p, err)) return MK_ERR_UNSUPPORTED;
 
   Builder b;
   const int g = Hq / Hkv;

@@ -181,6 +181,44 @@ def test_step_lm_head_shapes(vocab, W):
     assert np.array_equal(got["mk"].view(np.uint32), got["graph"].view(np.uint32))
 
 
+@pytest.mark.parametrize("tp,W", [((8, 2, 6, 4, 0, 64), 0), ((16, 16, 2, 1, 0, 4), 37)])
+def test_layer_tile_params(tp, W):
+    """Caller-fixed tile sizes (mk_config.tile_params: QKV / O / gate-up / down rows, split tokens)
+    on the single-token layer: against the oracle, megakernel against graph bit for bit."""
+    from gpu_helpers import QwenRun, bf16_to_f64
+    cfg = dataclasses.replace(get_config("qwen3_0p6b_layer"), tile_params=tp)
+    inp = make_inputs(cfg, seed=5)
+    ref = model.run_qwen3_layer(cfg, inp)
+    run = QwenRun(cfg, inp, num_workers=W)
+    got = {}
+    for mode in ("mk", "graph"):
+        _say(f"case: layer tile_params {tp} W={W} {mode}")
+        run.run(mode)
+        y = bf16_to_f64(run.t["y_out"]).reshape(1, -1)
+        r2 = run.t["r2_out"].cpu().numpy().astype(np.float64).reshape(1, -1)
+        assert np.max(np.abs(y - ref["y_pre"])) <= TOL and np.max(np.abs(r2 - ref["r2"])) <= TOL, mode
+        got[mode] = (run.t["y_out"].cpu().numpy().copy(), run.t["r2_out"].cpu().numpy().copy())
+    assert np.array_equal(got["mk"][0], got["graph"][0])
+    assert np.array_equal(got["mk"][1].view(np.uint32), got["graph"][1].view(np.uint32))
+
+
+def test_step_tile_params_many_lm_tasks_per_worker():
+    """lm_head rows per task fixed at 7 on 9 workers (429 tasks, about 48 per worker: the final norm
+    once per worker, its running maximum over its tasks, published by its last one) and 32-token
+    attention splits, two layers."""
+    from gpu_helpers import QwenRun
+    cfg = dataclasses.replace(get_config("qwen3_0p6b_step"), num_layers=2, vocab=3000, context=300,
+                              tile_params=(0, 0, 0, 0, 7, 32))
+    inp = make_inputs(cfg, seed=13)
+    res = model.run_qwen3_step(cfg, inp)
+    run = QwenRun(cfg, inp, num_workers=9)
+    for mode in ("mk", "graph"):
+        _say(f"case: step tile_params {mode}")
+        run.run(mode)
+        _check_step(run, res, f"tile_params {mode}")
+        _check_step_caches(run, inp, res, f"tile_params {mode}")
+
+
 def test_full_step_28_layers():
     cfg = get_config("qwen3_0p6b_step")
     _say("case: full 28-layer step, oracle on host")

@@ -208,3 +208,61 @@ def oq_tasks(plan):
     t = plan["queue"].reshape(-1, 32)
     t = t[t[:, 0] != 0]
     return t[np.argsort(t[:, 5])]
+
+
+@pytest.mark.parametrize("name,tp,W", [
+    ("qwen3_0p6b_layer", (8, 2, 6, 4, 0, 64), 256),
+    ("qwen3_0p6b_layer", (16, 16, 2, 1, 0, 4), 37),
+    ("qwen3_0p6b_step", (0, 0, 0, 0, 1000, 128), 256),
+    ("qwen3_0p6b_step", (16, 8, 12, 8, 7, 32), 9),
+    ("qwen3_8b_layer", (0, 0, 0, 0, 0, 64), 256),
+    ("qwen3_8b_layer_m64", (0, 0, 0, 0, 0, 32), 148)])
+def test_tile_params_bit_exact(name, tp, W):
+    """Caller-fixed tile sizes (mk_config.tile_params) reach both builders alike."""
+    cfg = dataclasses.replace(get_config(name), tile_params=tp, num_layers=min(2, get_config(name).num_layers),
+                              vocab=min(5000, get_config(name).vocab))
+    plan, ref = _both(cfg, W)
+    assert np.array_equal(plan.queue(), ref["queue"])
+    assert np.array_equal(plan.thresholds(), ref["thresholds"])
+    p = ref["params"]
+    for key, idx in (("r_qkv", 0), ("r_o", 1), ("r_gu", 2), ("r_down", 3), ("r_lm", 4), ("s_tok", 5)):
+        if tp[idx]:
+            assert p[key] == tp[idx]
+    plan.close()
+
+
+@pytest.mark.parametrize("name,tp,field", [
+    ("qwen3_0p6b_layer", (3,), "QKV rows, not a power of two"),
+    ("qwen3_0p6b_layer", (256,), "QKV rows above head_dim"),
+    ("qwen3_0p6b_layer", (0, 3), "O rows not dividing hidden"),
+    ("qwen3_0p6b_layer", (0, 256), "O rows above 128"),
+    ("qwen3_0p6b_layer", (0, 0, 5), "odd gate/up rows"),
+    ("qwen3_0p6b_layer", (0, 0, 96), "gate/up rows beyond one lease"),
+    ("qwen3_0p6b_layer", (0, 0, 0, 7), "down rows not dividing hidden"),
+    ("qwen3_0p6b_layer", (0, 0, 0, 0, 10), "lm_head rows outside the decode step"),
+    ("qwen3_0p6b_layer", (0, 0, 0, 0, 0, 256), "split above 128 tokens"),
+    ("qwen3_0p6b_layer", (0, 0, 0, 0, 0, 48), "split not a power of two"),
+    ("qwen3_0p6b_layer", (0, 0, 0, 0, 0, 0, 1), "reserved entry"),
+    ("qwen3_8b_layer", (64,), "row tiles of a multi-row plan"),
+    ("indexer_front", (0, 0, 0, 0, 0, 128), "any entry of an indexer plan")])
+def test_tile_params_refused(name, tp, field):
+    import persistent_megakernel_amd as mk
+    cfg = dataclasses.replace(get_config(name), tile_params=tp)
+    with pytest.raises(mk.MkError) as e:
+        mk.Plan(cfg, num_workers=256)
+    assert e.value.status == mk.MK_ERR_UNSUPPORTED, field
+
+
+@pytest.mark.parametrize("name,rd,ok", [("qwen3_0p6b_layer", 0, True), ("qwen3_0p6b_layer", 128, True),
+                                        ("qwen3_0p6b_layer", 64, False), ("indexer_front", 128, True),
+                                        ("indexer_front", 32, False)])
+def test_rotary_dim(name, rd, ok):
+    """RoPE over the whole head only: rotary_dim 0 or the head dim; a partial rotary is refused."""
+    import persistent_megakernel_amd as mk
+    cfg = dataclasses.replace(get_config(name), rotary_dim=rd)
+    if ok:
+        mk.Plan(cfg, num_workers=256).close()
+    else:
+        with pytest.raises(mk.MkError) as e:
+            mk.Plan(cfg, num_workers=256)
+        assert e.value.status == mk.MK_ERR_UNSUPPORTED

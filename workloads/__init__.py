@@ -54,6 +54,8 @@ class Config:
     residual_zero: bool = False  # r_in == 0 (full decode step)
     topk: int = 0  # indexer front: positions each token selects after the score (0: no top-k)
     mla_heads: int = 0  # indexer front: heads of the main-MLA query half D0 -> D2 (0: none)
+    rotary_dim: int = 0  # dims of a head the RoPE rotates (0: all of them)
+    tile_params: tuple = ()  # the plan's tile sizes (rows per task, split tokens); () or 0: the planner's rule
 
     @property
     def m(self) -> int:
